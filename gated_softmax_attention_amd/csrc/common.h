@@ -1,0 +1,100 @@
+// Shared device-side definitions for the FiX attention kernels (gfx950 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fix {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Tiling constants shared by every kernel.
+constexpr int CH = 64;        // gate chunk: chunk-local cumsums restart every CH tokens of a sequence
+constexpr int QB = 128;       // forward query block (4 waves x 32 rows)
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+// Device plan written by k_plan: every sequence's place in the packed token
+// order, its first chunk, and the forward work list.
+struct Plan {
+  int *seq_start;   // [nseq] first token of each sequence
+  int *seq_len;     // [nseq]
+  int *chunk_base;  // [nseq + 1] prefix sum of ceil(len / CH)
+  int2 *qitems;     // [nqb_ub] (sequence, query block), longest rows first
+  int *counts;      // [0] query blocks, [1] chunks, [2] longest sequence
+  int nseq;
+};
+
+// Position of key j (0..63) inside a transposed V tile: the two middle
+// quads of every 16-key group trade places, so that the eight keys one MFMA
+// half-wave contributes (see the 32x32x16 operand layout) are contiguous.
+__device__ __host__ inline int key_pos(int j) {
+  int q = (j >> 2) & 3;
+  int nq = (q == 1) ? 2 : (q == 2) ? 1 : q;
+  return (j & ~15) | (nq << 2) | (j & 3);
+}
+
+__device__ inline f32x16 mma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ inline f32x16 mma32(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Maximum of x over lanes l and l ^ 32.  v_permlane32_swap with both
+// operands equal to x leaves the low half of x in both halves of one result
+// and the high half in both halves of the other, so their maximum is the
+// maximum across the two halves in every lane.
+__device__ inline float max_across_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+__device__ inline uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Load one scalar of an input tensor stored as bf16 (is_f32 = false) or fp32.
+__device__ inline float load_in(const void *p, int64_t idx, bool is_f32) {
+  return is_f32 ? ((const float *)p)[idx] : bf16_to_f32(((const uint16_t *)p)[idx]);
+}
+__device__ inline void store_out(void *p, int64_t idx, float v, bool is_f32) {
+  if (is_f32) ((float *)p)[idx] = v;
+  else ((uint16_t *)p)[idx] = f32_to_bf16_rne(v);
+}
+
+// Eight consecutive input elements as an MFMA operand.  bf16 inputs stay
+// bf16; fp32 inputs are rounded to fp16 (their exact products keep the
+// logits accurate where bf16 rounding would not).
+template <bool F32IN> struct InFrag;
+template <> struct InFrag<false> {
+  typedef bf16x8 type;
+  __device__ static type load(const void *base, int64_t idx) {
+    uint4 u = *(const uint4 *)((const uint16_t *)base + idx);
+    return __builtin_bit_cast(bf16x8, u);
+  }
+  __device__ static type zero() { return __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0)); }
+};
+template <> struct InFrag<true> {
+  typedef f16x8 type;
+  __device__ static type load(const void *base, int64_t idx) {
+    const float4 *p = (const float4 *)((const float *)base + idx);
+    float4 a = p[0], b = p[1];
+    f16x8 r;
+    r[0] = (_Float16)a.x; r[1] = (_Float16)a.y; r[2] = (_Float16)a.z; r[3] = (_Float16)a.w;
+    r[4] = (_Float16)b.x; r[5] = (_Float16)b.y; r[6] = (_Float16)b.z; r[7] = (_Float16)b.w;
+    return r;
+  }
+  __device__ static type zero() { return __builtin_bit_cast(f16x8, make_uint4(0, 0, 0, 0)); }
+};
+
+}  // namespace fix

@@ -1,0 +1,79 @@
+// Gate preprocess: chunk-local prefix sums of the log-space forget gate and
+// the decay-scaled value tiles the forward consumes.
+//
+// FiX multiplies a cumulative, per-channel decay onto the value vectors (FiX
+// ICML 2026 poster page, abstract; the gate is fp32 and shaped like v, FiX
+// README, "Quick Start").  Writing G for the per-sequence inclusive prefix
+// sum of g, the decay between key j and query i is exp(G_i - G_j).  Every
+// sequence is cut into chunks of CH tokens starting at its first token; for
+// a chunk n with local prefix sums Gl (restarting at the chunk), the factor
+// splits around chunk ends into pieces that are all <= 1 when g <= 0:
+//   exp(G_i - G_j) = exp(Gl_i) * prod_{chunks strictly between} Gam_n
+//                    * exp(Gl_end(j's chunk) - Gl_j)
+// This kernel writes, per (chunk, kv head, channel):
+//   Gl2 = log2(e) * Gl        fp32, [Ttot, Hkv, dv] (token-major like g)
+//   Gam = exp(Gl at the chunk's last token)   fp32, [chunk, Hkv, dv]
+//   VtT = exp(Gl_end - Gl_j) * v_j            fp16, [chunk, Hkv, dv, CH]
+// VtT is stored transposed (keys contiguous per channel) in the key_pos
+// order, zero past the end of the sequence, which is the operand layout of
+// the forward kernel's P.V product.
+#include "common.h"
+
+namespace fix {
+
+template <int DV>
+__global__ void __launch_bounds__(128) k_gate_prep(const float *__restrict__ g, const void *__restrict__ v,
+                                                   bool in_f32, Plan plan, int Hkv, float *__restrict__ Gl2,
+                                                   float *__restrict__ Gam, _Float16 *__restrict__ VtT) {
+  const int gc = blockIdx.x, c = blockIdx.y, d = threadIdx.x;
+  if (gc >= plan.counts[1] || d >= DV) return;
+  int lo = 0, hi = plan.nseq - 1;
+  while (lo < hi) {  // last sequence whose first chunk is <= gc (skips empty sequences)
+    int mid = (lo + hi + 1) >> 1;
+    if (plan.chunk_base[mid] <= gc) lo = mid; else hi = mid - 1;
+  }
+  const int s = lo;
+  const int t0 = (gc - plan.chunk_base[s]) * CH;
+  const int n = min(CH, plan.seq_len[s] - t0);
+  const int64_t tok0 = (int64_t)plan.seq_start[s] + t0;
+
+  float gl[CH];
+  float acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    if (j < n) {
+      int64_t idx = ((tok0 + j) * Hkv + c) * DV + d;
+      acc += g[idx] * LOG2E;
+      Gl2[idx] = acc;
+    }
+    gl[j] = acc;
+  }
+  const int64_t cidx = ((int64_t)gc * Hkv + c) * DV + d;
+  Gam[cidx] = fast_exp2(acc);
+
+  _Float16 row[CH];
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    float val = 0.f;
+    if (j < n) val = fast_exp2(acc - gl[j]) * load_in(v, ((tok0 + j) * Hkv + c) * DV + d, in_f32);
+    row[key_pos(j)] = (_Float16)val;
+  }
+  uint4 *dst = (uint4 *)(VtT + cidx * CH);
+#pragma unroll
+  for (int p = 0; p < CH / 8; ++p) dst[p] = *(const uint4 *)(row + 8 * p);
+}
+
+hipError_t launch_gate_prep(int dv, const float *g, const void *v, bool in_f32, const Plan &plan, int Hkv,
+                            int nch_ub, float *Gl2, float *Gam, _Float16 *VtT, hipStream_t st) {
+  dim3 grid(nch_ub, Hkv), block(128);
+  switch (dv) {
+    case 16: hipLaunchKernelGGL(k_gate_prep<16>, grid, block, 0, st, g, v, in_f32, plan, Hkv, Gl2, Gam, VtT); break;
+    case 32: hipLaunchKernelGGL(k_gate_prep<32>, grid, block, 0, st, g, v, in_f32, plan, Hkv, Gl2, Gam, VtT); break;
+    case 64: hipLaunchKernelGGL(k_gate_prep<64>, grid, block, 0, st, g, v, in_f32, plan, Hkv, Gl2, Gam, VtT); break;
+    case 128: hipLaunchKernelGGL(k_gate_prep<128>, grid, block, 0, st, g, v, in_f32, plan, Hkv, Gl2, Gam, VtT); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fix

@@ -1,0 +1,136 @@
+/*
+ * fixattn.h -- C ABI of the FiX parallel attention library for AMD MI355X
+ * (gfx950 / CDNA4).  Library: gated_softmax_attention_amd/libfixattn.so.
+ *
+ * The operation (FiX repository README, section "Quick Start"; FiX ICML 2026
+ * poster page, abstract).  Per sequence, for query head h with kv head
+ * c = h / (Hq / Hkv) (contiguous head groups, the FlashAttention convention):
+ *
+ *   s_ij = scale * <q_i, k_j>            for j <= i in the same sequence
+ *   m_i  = max_{j<=i} s_ij
+ *   x_i  = sum_{j<=i} exp(s_ij - m_i) * exp(G_i - G_j) (.) v_j,
+ *          with G_t = sum_{u<=t} g_u the inclusive per-channel prefix sum of
+ *          the log-space forget gate g over the sequence
+ *   o_i  = x_i * (mean_d x_i^2 + eps)^-1/2 (.) o_norm_weight   if o_norm
+ *        = x_i                                                   otherwise
+ *   o_i  = o_i (.) o_gate_i                                     if o_gate given
+ *
+ * The softmax denominator is not formed: the RMSNorm that follows removes
+ * any positive per-row scale (FiX ICML 2026 poster page, abstract), so the
+ * gate can act directly on v as an element-wise multiplication.  g is fp32
+ * and shaped like v; head dimensions are 16, 32, 64 or 128 (FiX README,
+ * "Quick Start", closing note).  Sequences may be packed with cu_seqlens
+ * offsets as in FlashAttention (same section).
+ *
+ * Conventions shared by every entry point
+ *  - Layout: every tensor is a contiguous row-major [B, T, H, D] device
+ *    buffer (packed: B = 1, T = total tokens), 16-byte aligned.
+ *  - Ownership: all buffers belong to the caller.  The library never
+ *    allocates or frees device memory and keeps no state between calls;
+ *    scratch memory is the caller's `ws` of at least the size the matching
+ *    *_workspace_size function returns.  Calls are reentrant.
+ *  - Asynchrony: work is enqueued on `hip_stream` (a hipStream_t, NULL for
+ *    the null stream); calls return after enqueueing, without a host sync.
+ *  - Outputs are fully overwritten, never accumulated into.
+ *  - Errors: validation runs on the host before anything is enqueued, so a
+ *    call that returns FIX_E_INVALID / FIX_E_UNSUPPORTED / FIX_E_WORKSPACE
+ *    wrote nothing.  FIX_E_HIP reports a failed launch; the HIP error code is
+ *    then available from fix_attn_last_hip_error() on the calling thread.
+ *  - Preconditions not checked (they would need a device scan): g <= 0
+ *    (a forget gate; results for positive g are only as accurate as fp32
+ *    range allows), cu_seqlens non-decreasing with cu[0] = 0 and
+ *    cu[num_seqs] = T.
+ */
+#ifndef FIXATTN_H
+#define FIXATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FIX_OK = 0,
+  FIX_E_INVALID = 1,     /* malformed descriptor or a required NULL pointer */
+  FIX_E_UNSUPPORTED = 2, /* well formed but outside what the kernels handle */
+  FIX_E_WORKSPACE = 3,   /* workspace smaller than required */
+  FIX_E_HIP = 4          /* a HIP launch failed */
+} fix_status;
+
+typedef enum {
+  FIX_BF16 = 0, /* bfloat16 */
+  FIX_F32 = 1   /* float32 */
+} fix_dtype;
+
+typedef struct {
+  int64_t B, T;        /* batch and sequence length; packed input: B = 1, T = total tokens */
+  int64_t Hq, Hkv;     /* query heads and key/value heads, Hq % Hkv == 0 */
+  int64_t dk, dv;      /* head dims of q/k and of v/g/o, each in {16, 32, 64, 128} */
+  const int64_t *cu_seqlens; /* device int64 [num_seqs + 1] offsets, or NULL (B dense rows) */
+  int64_t num_seqs;    /* number of packed sequences (host-known); ignored without cu_seqlens */
+  fix_dtype in_dtype;  /* q, k, v, o_norm_weight, o_gate and d_o */
+  fix_dtype out_dtype; /* o, dq, dk, dv and d_o_gate */
+  float scale;         /* logit scale; <= 0 selects dk^-1/2 */
+  float eps;           /* RMSNorm epsilon (used when o_norm != 0) */
+  int32_t o_norm;      /* nonzero: apply RMSNorm and o_norm_weight to the output */
+} fix_attn_desc;
+
+/* Checks a descriptor on the host; makes no HIP call (usable without a GPU).
+ * FIX_E_INVALID: B, T, Hq, Hkv, dk or dv < 1; Hq % Hkv != 0; cu_seqlens with
+ *   B != 1 or num_seqs < 1; unknown dtype; negative eps; NaN scale or eps.
+ * FIX_E_UNSUPPORTED: dk or dv not in {16, 32, 64, 128}; B*T*max(Hq, Hkv) *
+ *   max(dk, dv) >= 2^40 or B*T >= 2^31 (index ranges of the kernels). */
+fix_status fix_attn_validate(const fix_attn_desc *d);
+
+/* Bytes of device scratch fix_attn_fwd / fix_attn_bwd need for this
+ * descriptor (0 when the descriptor does not validate).  The size depends
+ * only on the descriptor, not on the contents of cu_seqlens. */
+size_t fix_attn_fwd_workspace_size(const fix_attn_desc *d);
+size_t fix_attn_bwd_workspace_size(const fix_attn_desc *d);
+
+/* Forward pass.
+ *   q [B,T,Hq,dk], k [B,T,Hkv,dk], v [B,T,Hkv,dv]       in_dtype
+ *   g [B,T,Hkv,dv]                                      fp32, log-space forget gate
+ *   o_norm_weight [dv] in_dtype or NULL (ones); read only when o_norm
+ *   o_gate [B,T,Hq,dv] in_dtype or NULL (no output gate)
+ * Outputs (all required except x):
+ *   o [B,T,Hq,dv] out_dtype
+ *   m [B,T,Hq] fp32: m_i = max_{j<=i} s_ij (natural-log units)
+ *   rstd [B,T,Hq] fp32: (mean_d x_i^2 + eps)^-1/2 (written also when o_norm == 0)
+ *   x [B,T,Hq,dv] fp32: the un-normalised x_i, or NULL when no backward follows
+ * m, rstd and x are the saved state fix_attn_bwd consumes.  Rows of a packed
+ * buffer past cu_seqlens[num_seqs] are left untouched. */
+fix_status fix_attn_fwd(const fix_attn_desc *d, const void *q, const void *k, const void *v,
+                        const float *g, const void *o_norm_weight, const void *o_gate, void *o,
+                        float *m, float *rstd, float *x, void *ws, size_t ws_bytes,
+                        void *hip_stream);
+
+/* Backward pass, with m held constant (as in FlashAttention-style backward
+ * passes; exact when eps = 0, where o does not depend on m).
+ *   q, k, v, g, o_norm_weight, o_gate: as given to fix_attn_fwd
+ *   m, rstd, x: as written by fix_attn_fwd for the same inputs
+ *   d_o [B,T,Hq,dv] in_dtype: gradient of the loss with respect to o
+ * Outputs:
+ *   dq [B,T,Hq,dk], dk [B,T,Hkv,dk], dv [B,T,Hkv,dv]   out_dtype (required)
+ *   dg [B,T,Hkv,dv] fp32 (required)
+ *   d_o_norm_weight [dv] fp32, or NULL to skip (written only when o_norm)
+ *   d_o_gate [B,T,Hq,dv] out_dtype, or NULL to skip (needs o_gate) */
+fix_status fix_attn_bwd(const fix_attn_desc *d, const void *q, const void *k, const void *v,
+                        const float *g, const void *o_norm_weight, const void *o_gate,
+                        const float *m, const float *rstd, const float *x, const void *d_o,
+                        void *dq, void *dk, void *dv, float *dg, float *d_o_norm_weight,
+                        void *d_o_gate, void *ws, size_t ws_bytes, void *hip_stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *fix_attn_status_string(fix_status s);
+
+/* hipError_t value of the last FIX_E_HIP returned on the calling thread (0 if none). */
+int fix_attn_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FIXATTN_H */

@@ -54,6 +54,7 @@ void carve_plan(Carve &cv, const fix_attn_desc *d, const Shape &s, fix::Plan &p)
   p.seq_start = cv.take<int>(s.nseq);
   p.seq_len = cv.take<int>(s.nseq);
   p.chunk_base = cv.take<int>(s.nseq + 1);
+  p.cb128 = cv.take<int>(s.nseq + 1);
   p.qitems = cv.take<int2>(s.nqb_ub);
   p.counts = cv.take<int>(4);
   p.nseq = (int)s.nseq;
@@ -65,6 +66,40 @@ size_t carve_fwd(Carve &cv, const fix_attn_desc *d, FwdWs &w) {
   w.Gl2 = cv.take<float>(s.Ttot * d->Hkv * d->dv);
   w.Gam = cv.take<float>(s.nch_ub * d->Hkv * d->dv);
   w.VtT = cv.take<_Float16>(s.nch_ub * d->Hkv * d->dv * fix::CH);
+  return cv.off;
+}
+
+struct BwdWs {
+  fix::Plan plan;
+  float *Gl2, *Gam;
+  _Float16 *Vr, *Qt, *Kt;
+  float *delta;
+  _Float16 *dh, *dht;
+  float *mb, *sig, *qside, *dG, *dq_i, *dk_i, *dv_i, *dw_part, *dg_tot, *dg_carry;
+};
+
+size_t carve_bwd(Carve &cv, const fix_attn_desc *d, BwdWs &w) {
+  Shape s = shape_of(d);
+  carve_plan(cv, d, s, w.plan);
+  const int64_t T = s.Ttot, ncb = s.nqb_ub, Hq = d->Hq, Hkv = d->Hkv, DK = d->dk, DV = d->dv;
+  w.Gl2 = cv.take<float>(T * Hkv * DV);
+  w.Gam = cv.take<float>(ncb * Hkv * DV);
+  w.Vr = cv.take<_Float16>(ncb * Hkv * fix::CB * DV);
+  w.Qt = cv.take<_Float16>(ncb * Hq * DK * fix::CB);
+  w.Kt = cv.take<_Float16>(ncb * Hkv * DK * fix::CB);
+  w.delta = cv.take<float>(T * Hq * DV);
+  w.dh = cv.take<_Float16>(T * Hq * DV);
+  w.dht = cv.take<_Float16>(ncb * Hq * DV * fix::CB);
+  w.mb = cv.take<float>(T * Hq);
+  w.sig = cv.take<float>(T * Hq);
+  w.qside = cv.take<float>(T * Hkv * DV);
+  w.dG = cv.take<float>(T * Hkv * DV);
+  w.dq_i = cv.take<float>(T * Hq * DK);
+  w.dk_i = cv.take<float>(T * Hkv * DK);
+  w.dv_i = cv.take<float>(T * Hkv * DV);
+  w.dw_part = cv.take<float>(ncb * Hkv * DV);
+  w.dg_tot = cv.take<float>(ncb * Hkv * DV);
+  w.dg_carry = cv.take<float>(ncb * Hkv * DV);
   return cv.off;
 }
 
@@ -146,14 +181,73 @@ fix_status fix_attn_fwd(const fix_attn_desc *d, const void *q, const void *k, co
 
 size_t fix_attn_bwd_workspace_size(const fix_attn_desc *d) {
   if (fix_attn_validate(d) != FIX_OK) return 0;
-  return 256;
+  Carve cv(nullptr);
+  BwdWs w;
+  return carve_bwd(cv, d, w);
 }
 
 fix_status fix_attn_bwd(const fix_attn_desc *d, const void *q, const void *k, const void *v, const float *g,
                         const void *o_norm_weight, const void *o_gate, const float *m, const float *rstd,
                         const float *x, const void *d_o, void *dq, void *dk, void *dv, float *dg,
                         float *d_o_norm_weight, void *d_o_gate, void *ws, size_t ws_bytes, void *hip_stream) {
-  return FIX_E_UNSUPPORTED;
+  fix_status stt = fix_attn_validate(d);
+  if (stt != FIX_OK) return stt;
+  if (!q || !k || !v || !g || !m || !rstd || !x || !d_o || !dq || !dk || !dv || !dg) return FIX_E_INVALID;
+  if (d_o_gate && !o_gate) return FIX_E_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(x) || !aligned16(d_o) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(dg) || (o_gate && !aligned16(o_gate)))
+    return FIX_E_INVALID;
+  const size_t need = fix_attn_bwd_workspace_size(d);
+  if (ws_bytes < need || (need && !ws)) return FIX_E_WORKSPACE;
+  if (!aligned16(ws)) return FIX_E_INVALID;
+  hipStream_t st = (hipStream_t)hip_stream;
+  Shape s = shape_of(d);
+  Carve cv(ws);
+  BwdWs w;
+  carve_bwd(cv, d, w);
+  const bool f32in = d->in_dtype == FIX_F32;
+  const int Hq = (int)d->Hq, Hkv = (int)d->Hkv, DK = (int)d->dk, DV = (int)d->dv, ncb = (int)s.nqb_ub;
+  const bool want_dw = d->o_norm && d_o_norm_weight;
+  hipError_t e;
+#define FIX_TRY(call)             \
+  e = (call);                     \
+  if (e != hipSuccess) return hip_fail(e);
+  FIX_TRY(fix::launch_plan(d->cu_seqlens, (int)s.nseq, (int)d->T, s.Ttot, w.plan, st));
+  FIX_TRY(fix::launch_gate_prep_rows(DV, g, v, f32in, w.plan, Hkv, ncb, w.Gl2, w.Gam, w.Vr, st));
+  FIX_TRY(fix::launch_tiles_t(DK, q, f32in, w.plan, Hq, ncb, w.Qt, st));
+  FIX_TRY(fix::launch_tiles_t(DK, k, f32in, w.plan, Hkv, ncb, w.Kt, st));
+  fix::PrepArgs pa;
+  pa.x = x; pa.rstd = rstd; pa.m = m; pa.Gl2 = w.Gl2;
+  pa.dO = d_o; pa.z = o_gate; pa.w = d->o_norm ? o_norm_weight : nullptr;
+  pa.plan = w.plan;
+  pa.Hq = Hq; pa.Hkv = Hkv;
+  pa.o_norm = d->o_norm ? 1 : 0;
+  pa.out_f32 = d->out_dtype == FIX_F32;
+  pa.in_f32 = f32in;
+  pa.delta = w.delta; pa.dh = w.dh; pa.dht = w.dht; pa.mb = w.mb; pa.sig = w.sig; pa.qside = w.qside;
+  pa.dz = d_o_gate;
+  pa.dw_part = want_dw ? w.dw_part : nullptr;
+  FIX_TRY(fix::launch_bwd_prep(DV, pa, ncb, st));
+  fix::BwdArgs a;
+  a.q = q; a.k = k; a.v = v;
+  a.Gl2 = w.Gl2; a.Gam = w.Gam; a.Vr = w.Vr; a.Qt = w.Qt; a.Kt = w.Kt;
+  a.delta = w.delta; a.dh = w.dh; a.dht = w.dht; a.mb = w.mb; a.sig = w.sig; a.qside = w.qside;
+  a.dq_i = w.dq_i; a.dk_i = w.dk_i; a.dv_i = w.dv_i;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dG = w.dG;
+  a.plan = w.plan;
+  a.Hq = Hq; a.Hkv = Hkv;
+  const float scale = d->scale > 0.f ? d->scale : 1.f / std::sqrt((float)d->dk);
+  a.sl2 = scale * fix::LOG2E;
+  a.scale = scale;
+  a.out_f32 = d->out_dtype == FIX_F32;
+  FIX_TRY(fix::launch_bwd(fix::BK_INTRA_DQ, DK, DV, f32in, a, dim3(ncb, Hq), st));
+  FIX_TRY(fix::launch_bwd(fix::BK_INTRA_DKV, DK, DV, f32in, a, dim3(ncb, Hkv), st));
+  FIX_TRY(fix::launch_bwd(fix::BK_DQ, DK, DV, f32in, a, dim3(ncb * Hq), st));
+  FIX_TRY(fix::launch_bwd(fix::BK_DKV, DK, DV, f32in, a, dim3(ncb * Hkv), st));
+  FIX_TRY(fix::launch_dg_scan(DV, w.dG, w.plan, Hkv, ncb, w.dg_tot, w.dg_carry, dg, st));
+  if (want_dw) FIX_TRY(fix::launch_dw_reduce(w.dw_part, w.plan.counts, Hkv, DV, d_o_norm_weight, st));
+#undef FIX_TRY
+  return FIX_OK;
 }
 
 const char *fix_attn_status_string(fix_status s) {

@@ -1,0 +1,8 @@
+// Backward kernel instances with dk = 64 (all dv and input types).
+#include "bwd_kernel.h"
+
+namespace fix {
+hipError_t launch_bwd_d64(BwdKernel kind, int dv, bool f32in, const BwdArgs &a, dim3 grid, hipStream_t st) {
+  return launch_bwd_dk<64>(kind, dv, f32in, a, grid, st);
+}
+}  // namespace fix

@@ -1,0 +1,305 @@
+// Backward preprocessing: gate chunks of CB = 128 tokens, operand tiles in
+// the layouts the backward MFMA kernels read, and the output-side backward.
+//
+// The backward of o = RMSNorm(x) (.) w (.) z with respect to x (FiX README,
+// "Quick Start": optional o_norm weight and o_gate), with r = rstd and
+// xh = x r:
+//   dz = dO (.) n  (n = xh (.) w under the norm, x without it),  dn = dO (.) z
+//   dw = sum over rows of dn (.) xh
+//   delta = r (dn (.) w - xh * mean_d(dn (.) w (.) xh))   (or dn without the norm)
+// delta is the gradient reaching x_i = sum_j P_ij D_ij (.) v_j.  For the
+// chunk-factored products the query side needs dhat_i = exp(Gl_i) delta_i
+// (Gl the 128-chunk-local prefix sum of g, so the factor is <= 1); it is
+// stored fp16 after a per-row power-of-two scale sigma_i = 2^-e_i with
+// max_d |sigma_i delta_i| about 1, which keeps it, and the within-chunk
+// operands exp(Gl_i - Gl_ref) sigma_i delta_i, inside fp16 range.  The kernels compute probabilities as
+// exp2(s log2e - (m log2e - e_i)) = P_ij / sigma_i, so every product of a
+// probability with a scaled dhat is unchanged.  The gate's own gradient
+// needs, per kv head, sum over the group's q heads of delta (.) x (the query
+// side of dG).
+#include "common.h"
+#include "launch.h"
+
+namespace fix {
+
+// Gl2 (log2 units, 128-chunk local), Gam per 128-chunk, and row-major fp16
+// V scaled to its chunk end: Vr[chunk][kvh][t][d] = exp(Gl_end - Gl_t) v_t.
+template <int DV>
+__global__ void __launch_bounds__(128) k_gate_prep_rows(const float *__restrict__ g, const void *__restrict__ v,
+                                                        bool in_f32, Plan plan, int Hkv, float *__restrict__ Gl2,
+                                                        float *__restrict__ Gam, _Float16 *__restrict__ Vr) {
+  const int gc = blockIdx.x, c = blockIdx.y, d = threadIdx.x;
+  if (gc >= plan.counts[0] || d >= DV) return;
+  const int s = seq_of_chunk(plan.cb128, plan.nseq, gc);
+  const int t0 = (gc - plan.cb128[s]) * CB;
+  const int n = min(CB, plan.seq_len[s] - t0);
+  const int64_t tok0 = (int64_t)plan.seq_start[s] + t0;
+  float acc = 0.f;
+  for (int j = 0; j < n; ++j) {
+    int64_t idx = ((tok0 + j) * Hkv + c) * DV + d;
+    acc += g[idx] * LOG2E;
+    Gl2[idx] = acc;
+  }
+  const int64_t cidx = ((int64_t)gc * Hkv + c);
+  Gam[cidx * DV + d] = fast_exp2(acc);
+  _Float16 *dst = Vr + cidx * CB * DV + d;
+  for (int j = 0; j < CB; ++j) {
+    float val = 0.f;
+    if (j < n) {
+      int64_t idx = ((tok0 + j) * Hkv + c) * DV + d;
+      val = fast_exp2(acc - Gl2[idx]) * load_in(v, idx, in_f32);
+    }
+    dst[(int64_t)j * DV] = (_Float16)val;
+  }
+}
+
+// Transposed fp16 tiles of a [Ttot, H, D] input: out[chunk][h][d][key_pos(t)]
+// for the CB tokens of each 128-chunk (zero past the end of the sequence).
+template <int D>
+__global__ void __launch_bounds__(256) k_tiles_t(const void *__restrict__ in, bool in_f32, Plan plan, int H,
+                                                 _Float16 *__restrict__ out) {
+  constexpr int STR = CB + 8;
+  __shared__ _Float16 tile[D * STR];
+  const int gc = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  if (gc >= plan.counts[0]) return;
+  const int s = seq_of_chunk(plan.cb128, plan.nseq, gc);
+  const int t0 = (gc - plan.cb128[s]) * CB;
+  const int n = min(CB, plan.seq_len[s] - t0);
+  const int64_t tok0 = (int64_t)plan.seq_start[s] + t0;
+  for (int e = tid; e < CB * D; e += 256) {
+    int t = e / D, d = e % D;
+    float val = t < n ? load_in(in, ((tok0 + t) * H + h) * D + d, in_f32) : 0.f;
+    tile[d * STR + key_pos(t)] = (_Float16)val;
+  }
+  __syncthreads();
+  uint4 *dst = (uint4 *)(out + ((int64_t)gc * H + h) * D * CB);
+  for (int e = tid; e < D * CB / 8; e += 256) {
+    int d = e / (CB / 8), p8 = e % (CB / 8);
+    dst[e] = *(const uint4 *)&tile[d * STR + 8 * p8];
+  }
+}
+
+template <int DV>
+__global__ void __launch_bounds__(256) k_bwd_prep(PrepArgs a) {
+  constexpr int STR = CB + 8;
+  constexpr int PER = (DV + 63) / 64;  // channels per lane
+  __shared__ _Float16 tile[DV * STR];
+  const int gc = blockIdx.x, c = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  if (gc >= a.plan.counts[0]) return;
+  const Plan &pl = a.plan;
+  const int s = seq_of_chunk(pl.cb128, pl.nseq, gc);
+  const int t0 = (gc - pl.cb128[s]) * CB;
+  const int n = min(CB, pl.seq_len[s] - t0);
+  const int64_t tok0 = (int64_t)pl.seq_start[s] + t0;
+  const int Hq = a.Hq, Hkv = a.Hkv, G = Hq / Hkv;
+  const bool in_f32 = a.in_f32;
+
+  float wv[PER], dwacc[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    int d = lane + 64 * k;
+    wv[k] = (a.o_norm && a.w && d < DV) ? load_in(a.w, d, in_f32) : 1.f;
+    dwacc[k] = 0.f;
+  }
+  for (int gq = 0; gq < G; ++gq) {
+    const int h = c * G + gq;
+#pragma unroll 1
+    for (int i = 0; i < CB / 4; ++i) {
+      const int t = wave + 4 * i;  // token within the chunk
+      if (t < n) {
+        const int64_t tok = tok0 + t;
+        const int64_t rb = (tok * Hq + h) * DV;
+        const float r = a.rstd[tok * Hq + h];
+        float xv[PER], dn[PER], del[PER];
+        float proj = 0.f;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+          int d = lane + 64 * k;
+          xv[k] = dn[k] = 0.f;
+          if (d < DV) {
+            xv[k] = a.x[rb + d];
+            float go = load_in(a.dO, rb + d, in_f32);
+            float zz = a.z ? load_in(a.z, rb + d, in_f32) : 1.f;
+            dn[k] = go * zz;
+            float nval = a.o_norm ? xv[k] * r * wv[k] : xv[k];
+            if (a.dz) store_out(a.dz, rb + d, go * nval, a.out_f32);
+            if (a.o_norm) {
+              dwacc[k] += dn[k] * xv[k] * r;
+              proj += dn[k] * wv[k] * xv[k] * r;
+            }
+          }
+        }
+        if (a.o_norm) {
+#pragma unroll
+          for (int off = 32; off > 0; off >>= 1) proj += __shfl_xor(proj, off);
+          proj *= 1.f / DV;
+        }
+        // sigma = 2^-e scales the row so that max |sigma delta| is about 1; every
+        // fp16 operand built from the row (here exp(Gl) sigma delta, within a
+        // chunk exp(Gl_i - Gl_ref) sigma delta, all factors <= 1) stays in range
+        float amax = 0.f;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+          del[k] = a.o_norm ? r * (dn[k] * wv[k] - xv[k] * r * proj) : dn[k];
+          if (lane + 64 * k < DV) amax = fmaxf(amax, fabsf(del[k]));
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+        int e = 0;
+        if (amax > 0.f) e = min(15, max(-15, (int)ceilf(__log2f(amax))));
+        const float sg = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+          int d = lane + 64 * k;
+          if (d < DV) {
+            a.delta[rb + d] = del[k];
+            // query side of dG, summed over the group; (token, channel) is
+            // owned by this thread for every head of the group
+            const int64_t qi = (tok * Hkv + c) * DV + d;
+            a.qside[qi] = (gq == 0 ? 0.f : a.qside[qi]) + del[k] * xv[k];
+            _Float16 hv = (_Float16)(fast_exp2(a.Gl2[(tok * Hkv + c) * DV + d]) * del[k] * sg);
+            a.dh[rb + d] = hv;
+            tile[d * STR + key_pos(t)] = hv;
+          }
+        }
+        if (lane == 0) {
+          a.mb[tok * Hq + h] = a.m[tok * Hq + h] * LOG2E - (float)e;
+          a.sig[tok * Hq + h] = sg;
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+          int d = lane + 64 * k;
+          if (d < DV) tile[d * STR + key_pos(t)] = (_Float16)0.f;
+        }
+      }
+    }
+    __syncthreads();
+    uint4 *dst = (uint4 *)(a.dht + ((int64_t)gc * Hq + h) * DV * CB);
+    for (int e = tid; e < DV * CB / 8; e += 256) {
+      int d = e / (CB / 8), p8 = e % (CB / 8);
+      dst[e] = *(const uint4 *)&tile[d * STR + 8 * p8];
+    }
+    __syncthreads();
+  }
+  if (a.dw_part) {
+    // per-block partials: reduce the four waves in LDS, then one row per block
+    __shared__ float red[4][DV];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      int d = lane + 64 * k;
+      if (d < DV) red[wave][d] = dwacc[k];
+    }
+    __syncthreads();
+    for (int d = tid; d < DV; d += 256)
+      a.dw_part[((int64_t)gc * Hkv + c) * DV + d] = red[0][d] + red[1][d] + red[2][d] + red[3][d];
+  }
+}
+
+// dw[d] = sum over blocks of the partials, in a fixed order.
+__global__ void __launch_bounds__(256) k_dw_reduce(const float *__restrict__ part, const int *__restrict__ counts,
+                                                   int Hkv, int dv, float *__restrict__ dw) {
+  const int d = blockIdx.x * 256 + threadIdx.x;
+  if (d >= dv) return;
+  const int nb = counts[0] * Hkv;
+  float acc = 0.f;
+  for (int b = 0; b < nb; ++b) acc += part[(int64_t)b * dv + d];
+  dw[d] = acc;
+}
+
+// dg_t = sum over t' >= t of the same sequence of dG_t' (the gate enters
+// through G_t = sum_{u<=t} g_u).  Three passes over 128-chunks: chunk
+// totals, exclusive suffix carries per sequence, then in-chunk suffix sums.
+template <int DV>
+__global__ void __launch_bounds__(128) k_dg_totals(const float *__restrict__ dG, Plan plan, int Hkv,
+                                                   float *__restrict__ tot) {
+  const int gc = blockIdx.x, c = blockIdx.y, d = threadIdx.x;
+  if (gc >= plan.counts[0] || d >= DV) return;
+  const int s = seq_of_chunk(plan.cb128, plan.nseq, gc);
+  const int t0 = (gc - plan.cb128[s]) * CB;
+  const int n = min(CB, plan.seq_len[s] - t0);
+  const int64_t tok0 = (int64_t)plan.seq_start[s] + t0;
+  float acc = 0.f;
+  for (int j = 0; j < n; ++j) acc += dG[((tok0 + j) * Hkv + c) * DV + d];
+  tot[((int64_t)gc * Hkv + c) * DV + d] = acc;
+}
+
+template <int DV>
+__global__ void __launch_bounds__(128) k_dg_carry(const float *__restrict__ tot, Plan plan, int Hkv,
+                                                  float *__restrict__ carry) {
+  const int s = blockIdx.x, c = blockIdx.y, d = threadIdx.x;
+  if (d >= DV) return;
+  float run = 0.f;
+  for (int gc = plan.cb128[s + 1] - 1; gc >= plan.cb128[s]; --gc) {
+    const int64_t idx = ((int64_t)gc * Hkv + c) * DV + d;
+    carry[idx] = run;
+    run += tot[idx];
+  }
+}
+
+template <int DV>
+__global__ void __launch_bounds__(128) k_dg_final(const float *__restrict__ dG, const float *__restrict__ carry,
+                                                  Plan plan, int Hkv, float *__restrict__ dg) {
+  const int gc = blockIdx.x, c = blockIdx.y, d = threadIdx.x;
+  if (gc >= plan.counts[0] || d >= DV) return;
+  const int s = seq_of_chunk(plan.cb128, plan.nseq, gc);
+  const int t0 = (gc - plan.cb128[s]) * CB;
+  const int n = min(CB, plan.seq_len[s] - t0);
+  const int64_t tok0 = (int64_t)plan.seq_start[s] + t0;
+  float run = carry[((int64_t)gc * Hkv + c) * DV + d];
+  for (int j = n - 1; j >= 0; --j) {
+    const int64_t idx = ((tok0 + j) * Hkv + c) * DV + d;
+    run += dG[idx];
+    dg[idx] = run;
+  }
+}
+
+#define FIX_DV_SWITCH(dv, ...)                         \
+  switch (dv) {                                        \
+    case 16: { constexpr int DVC = 16; __VA_ARGS__; } break;   \
+    case 32: { constexpr int DVC = 32; __VA_ARGS__; } break;   \
+    case 64: { constexpr int DVC = 64; __VA_ARGS__; } break;   \
+    case 128: { constexpr int DVC = 128; __VA_ARGS__; } break; \
+    default: return hipErrorInvalidValue;              \
+  }
+
+hipError_t launch_gate_prep_rows(int dv, const float *g, const void *v, bool in_f32, const Plan &plan, int Hkv,
+                                 int ncb_ub, float *Gl2, float *Gam, _Float16 *Vr, hipStream_t st) {
+  dim3 grid(ncb_ub, Hkv);
+  FIX_DV_SWITCH(dv, hipLaunchKernelGGL(k_gate_prep_rows<DVC>, grid, dim3(128), 0, st, g, v, in_f32, plan, Hkv,
+                                       Gl2, Gam, Vr));
+  return hipGetLastError();
+}
+
+hipError_t launch_tiles_t(int D, const void *in, bool in_f32, const Plan &plan, int H, int ncb_ub, _Float16 *out,
+                          hipStream_t st) {
+  dim3 grid(ncb_ub, H);
+  FIX_DV_SWITCH(D, hipLaunchKernelGGL(k_tiles_t<DVC>, grid, dim3(256), 0, st, in, in_f32, plan, H, out));
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_prep(int dv, const PrepArgs &a, int ncb_ub, hipStream_t st) {
+  dim3 grid(ncb_ub, a.Hkv);
+  FIX_DV_SWITCH(dv, hipLaunchKernelGGL(k_bwd_prep<DVC>, grid, dim3(256), 0, st, a));
+  return hipGetLastError();
+}
+
+hipError_t launch_dg_scan(int dv, const float *dG, const Plan &plan, int Hkv, int ncb_ub, float *tot, float *carry,
+                          float *dg, hipStream_t st) {
+  dim3 grid(ncb_ub, Hkv), gs(plan.nseq, Hkv);
+  FIX_DV_SWITCH(dv, hipLaunchKernelGGL(k_dg_totals<DVC>, grid, dim3(128), 0, st, dG, plan, Hkv, tot));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  FIX_DV_SWITCH(dv, hipLaunchKernelGGL(k_dg_carry<DVC>, gs, dim3(128), 0, st, tot, plan, Hkv, carry));
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  FIX_DV_SWITCH(dv, hipLaunchKernelGGL(k_dg_final<DVC>, grid, dim3(128), 0, st, dG, carry, plan, Hkv, dg));
+  return hipGetLastError();
+}
+
+hipError_t launch_dw_reduce(const float *part, const int *counts, int Hkv, int dv, float *dw, hipStream_t st) {
+  hipLaunchKernelGGL(k_dw_reduce, dim3((dv + 255) / 256), dim3(256), 0, st, part, counts, Hkv, dv, dw);
+  return hipGetLastError();
+}
+
+}  // namespace fix

@@ -13,8 +13,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Tiling constants shared by every kernel.
-constexpr int CH = 64;        // gate chunk: chunk-local cumsums restart every CH tokens of a sequence
+constexpr int CH = 64;        // forward gate chunk: chunk-local cumsums restart every CH tokens of a sequence
 constexpr int QB = 128;       // forward query block (4 waves x 32 rows)
+constexpr int CB = 128;       // backward gate chunk (= one backward workgroup's rows or keys)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
@@ -24,10 +25,21 @@ struct Plan {
   int *seq_start;   // [nseq] first token of each sequence
   int *seq_len;     // [nseq]
   int *chunk_base;  // [nseq + 1] prefix sum of ceil(len / CH)
-  int2 *qitems;     // [nqb_ub] (sequence, query block), longest rows first
-  int *counts;      // [0] query blocks, [1] chunks, [2] longest sequence
+  int *cb128;       // [nseq + 1] prefix sum of ceil(len / CB)
+  int2 *qitems;     // [nqb_ub] (sequence, 128-token block), latest blocks first
+  int *counts;      // [0] 128-token blocks, [1] 64-token chunks, [2] longest sequence
   int nseq;
 };
+
+// Last sequence whose first chunk (of the given table) is <= gc.
+__device__ inline int seq_of_chunk(const int *base, int nseq, int gc) {
+  int lo = 0, hi = nseq - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (base[mid] <= gc) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
 
 // Position of key j (0..63) inside a transposed V tile: the two middle
 // quads of every 16-key group trade places, so that the eight keys one MFMA
@@ -36,6 +48,30 @@ __device__ __host__ inline int key_pos(int j) {
   int q = (j >> 2) & 3;
   int nq = (q == 1) ? 2 : (q == 2) ? 1 : q;
   return (j & ~15) | (nq << 2) | (j & 3);
+}
+
+// Operand and result layout of the 32x32x16 MFMA (lane l = 32 * hh + n):
+//  * an operand element i of lane (hh, n) carries row/column n and k-index
+//    8 * hh + i of its 16-wide k-slab;
+//  * result register j of lane (hh, n) holds row acc_row(hh, j), column n.
+// A result can feed the next product directly when its rows become the
+// k-index: register j = 8 * u + i of a 32-row result then carries k-slab u,
+// element i, i.e. row slab_key(u, hh, i) of the 32-row block.
+__device__ inline int acc_row(int hh, int j) { return 8 * (j >> 2) + 4 * hh + (j & 3); }
+__device__ inline int slab_key(int u, int hh, int i) { return 16 * u + 8 * (i >> 2) + 4 * hh + (i & 3); }
+
+// x = hi + lo to about 16 significant bits, both parts bf16 (fp32 exponent range).
+__device__ inline void split_bf16(float x, bf16x8 &hi, bf16x8 &lo, int e) {
+  __bf16 h = (__bf16)x;
+  hi[e] = h;
+  lo[e] = (__bf16)(x - (float)h);
+}
+
+__device__ inline f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) z[j] = 0.f;
+  return z;
 }
 
 __device__ inline f32x16 mma32(bf16x8 a, bf16x8 b, f32x16 c) {

@@ -8,7 +8,7 @@
 //
 // Work decomposition.  A workgroup owns QB = 128 query rows of one q head
 // (4 waves x 32 rows); keys are visited in gate chunks of CH = 64.
-//  * Key chunks strictly before the wave's own chunk use the chunk
+//  * Key chunks at least two before the wave's own chunk use the chunk
 //    factoring of the decay (see gate_prep.hip): with A the accumulator
 //    relative to the end of the last visited chunk,
 //        A <- A (.) Gam_J + P_J . Vt_J
@@ -16,8 +16,12 @@
 //    the gate preprocess.  Tiles of K and Vt are staged through LDS (double
 //    buffered) and shared by the four waves; S = Q K^T is a bf16 MFMA and
 //    P.Vt an fp16 MFMA, both with fp32 accumulation.
-//  * The wave's own chunk is handled in registers: if the wave holds the
-//    second half of its chunk, the first 32 keys are one more factored step
+//  * The chunk before the wave's own chunk and the wave's own chunk are
+//    handled in registers, with P and V as bf16x3 (hi*hi + hi*lo + lo*hi):
+//    these nearest keys carry the largest decay weights, and their fp16
+//    rounding would dominate the error of x (and of the gate gradient built
+//    from it).  The previous chunk is one more factored step; if the wave
+//    holds the second half of its chunk, the first 32 keys are another one
 //    (decay taken to key 31 of the chunk); then the 32x32 diagonal block is
 //    factored around the token before the block, V'' = exp(Gl_ref - Gl_j) v_j
 //    (>= 1, up to 2^GUARD), which needs fp32 range: it is multiplied as
@@ -39,11 +43,6 @@ namespace fix {
 
 constexpr float TAU = 8.f;      // lazy max threshold (log2 units)
 constexpr float GUARD = 100.f;  // largest factored gate range of a diagonal block (log2 units)
-
-// k-slab u (16 keys) of a 32-key block: key carried by element i of a half-wave's operand.
-__device__ inline int slab_key(int u, int hh, int i) { return 16 * u + 8 * (i >> 2) + 4 * hh + (i & 3); }
-// Key of register j of a 32x32 MFMA result held by half-wave hh.
-__device__ inline int acc_row(int hh, int j) { return 8 * (j >> 2) + 4 * hh + (j & 3); }
 
 template <int DK, int DV, bool F32IN>
 __global__ void __launch_bounds__(256, 2) k_fix_fwd(FwdArgs a) {
@@ -83,7 +82,9 @@ __global__ void __launch_bounds__(256, 2) k_fix_fwd(FwdArgs a) {
   const int nrows = min(QB, L - q0);
   const bool active = wave * 32 < nrows;
   const int Iw = (q0 / CH) + (wave >> 1);          // chunk holding this wave's rows
-  const int nJ = (q0 / CH) + (nrows > CH ? 1 : 0);  // chunks staged through LDS
+  // Key chunks before Iw - 1 go through LDS; chunk Iw - 1 and the wave's own
+  // chunk are handled per wave from registers at higher precision.
+  const int nJ = (nrows > CH) ? (q0 / CH) : max(0, q0 / CH - 1);
   const float sl2 = a.sl2;
 
   // Q^T operand: lane (hh, n) holds row n of the wave, dims 16s + 8hh .. +7.
@@ -196,7 +197,7 @@ __global__ void __launch_bounds__(256, 2) k_fix_fwd(FwdArgs a) {
   for (int J = 0; J < nJ; ++J) {
     const int b = J & 1;
     if (J + 1 < nJ) load_tile(J + 1);
-    if (active && J < Iw) {
+    if (active && J < Iw - 1) {
       f32x16 sc[2];
 #pragma unroll
       for (int be = 0; be < 2; ++be) {
@@ -248,40 +249,63 @@ __global__ void __launch_bounds__(256, 2) k_fix_fwd(FwdArgs a) {
     int d = 32 * bb + n;
     glref[bb] = (wp == 1 && d < DV) ? gl_at(c0 + 31, d) : 0.f;
   }
-  if (wp == 1) {
-    // keys c0 .. c0+31 precede every row of this wave: one more factored step.
-    f32x16 s1;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) s1[j] = 0.f;
+  // 32 keys kb0 .. kb0+31 that precede every row of the wave, with the decay
+  // taken to the token whose chunk-local log2 prefix sum is gref (>= every
+  // key's, so each factor is <= 1).  P and V are multiplied as bf16x3: these
+  // nearest keys carry the largest decay weights.
+  auto near_block = [&](int kb0, const float *gref) {
+    f32x16 s1 = zero16();
 #pragma unroll
     for (int i = 0; i < NS; ++i)
-      s1 = mma32(IF::load(a.k, ((st + c0 + n) * Hkv + c) * DK + 16 * i + 8 * hh), qf[i], s1);
-    float mx = row_max(s1);
-    mx = max_across_halves(mx) * sl2;
-    update_max(mx);
-    f16x8 pf[2];
+      s1 = mma32(IF::load(a.k, ((st + kb0 + n) * Hkv + c) * DK + 16 * i + 8 * hh), qf[i], s1);
+    update_max(max_across_halves(row_max(s1)) * sl2);
+    bf16x8 ph[2], plo[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pf[u][i] = (_Float16)fast_exp2(s1[8 * u + i] * sl2 - m_used);
+      for (int i = 0; i < 8; ++i) split_bf16(fast_exp2(s1[8 * u + i] * sl2 - m_used), ph[u], plo[u], i);
 #pragma unroll
     for (int bb = 0; bb < NB; ++bb) {
       const int d = 32 * bb + n;
-      float gam = fast_exp2(glref[bb]);
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc[bb][j] *= gam;
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        f16x8 vf;
+        bf16x8 vh, vl;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          int tok = c0 + slab_key(u, hh, i);
-          float val = (d < DV) ? fast_exp2(glref[bb] - gl_at(tok, d)) * v_at(tok, d) : 0.f;
-          vf[i] = (_Float16)val;
+          const int tok = kb0 + slab_key(u, hh, i);
+          const float val = (d < DV) ? fast_exp2(gref[bb] - gl_at(tok, d)) * v_at(tok, d) : 0.f;
+          split_bf16(val, vh, vl, i);
         }
-        acc[bb] = mma32(pf[u], vf, acc[bb]);
+        acc[bb] = mma32(ph[u], vh, acc[bb]);
+        acc[bb] = mma32(ph[u], vl, acc[bb]);
+        acc[bb] = mma32(plo[u], vh, acc[bb]);
       }
     }
+  };
+  if (Iw >= 1) {
+    // previous chunk: A <- A (.) Gam + P V~ with V~ to the chunk end
+    const int jc = (Iw - 1) * CH;
+    float gend[NB];
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+      const int d = 32 * bb + n;
+      gend[bb] = d < DV ? gl_at(jc + CH - 1, d) : 0.f;
+      const float gam = fast_exp2(gend[bb]);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[bb][j] *= gam;
+    }
+    near_block(jc, gend);
+    near_block(jc + 32, gend);
+  }
+  if (wp == 1) {
+    // keys c0 .. c0+31 precede every row of this wave: decay to key 31 of the chunk
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+      const float gam = fast_exp2(glref[bb]);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[bb][j] *= gam;
+    }
+    near_block(c0, glref);
   }
 
   // Diagonal 32x32 block: keys kb .. kb+31 against rows kb .. kb+31.

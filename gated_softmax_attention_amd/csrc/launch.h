@@ -21,6 +21,40 @@ struct FwdArgs {
   int out_f32;
 };
 
+struct BwdArgs {
+  const void *q, *k, *v;
+  const float *Gl2, *Gam;      // 128-chunk local prefix sums of g (log2 units), chunk decays
+  const _Float16 *Vr;          // [chunk][Hkv][CB][DV] V scaled to its chunk end
+  const _Float16 *Qt, *Kt;     // [chunk][H][D][CB] transposed fp16 tiles (key_pos order)
+  const float *delta;          // [T, Hq, DV] gradient reaching x
+  const _Float16 *dh, *dht;    // sigma * exp(Gl) * delta, rows and transposed tiles
+  const float *mb, *sig;       // [T, Hq] m log2e - e, sigma = 2^-e
+  const float *qside;          // [T, Hkv, DV]
+  float *dq_i, *dk_i, *dv_i;   // within-chunk contributions (fp32)
+  void *dq, *dk, *dv;          // outputs (out dtype)
+  float *dG;                   // [T, Hkv, DV] gradient with respect to the prefix sums of g
+  Plan plan;
+  int Hq, Hkv;
+  float sl2, scale;
+  int out_f32;
+};
+
+struct PrepArgs {
+  const float *x, *rstd, *m, *Gl2;
+  const void *dO, *z, *w;
+  Plan plan;
+  int Hq, Hkv;
+  int o_norm, out_f32, in_f32;
+  float *delta;        // [Ttot, Hq, DV] fp32
+  _Float16 *dh;        // [Ttot, Hq, DV] fp16, sigma * exp(Gl) * delta
+  _Float16 *dht;       // [chunk][Hq][DV][CB] fp16, the same transposed (key_pos order)
+  float *mb;           // [Ttot, Hq] m log2e - e
+  float *sig;          // [Ttot, Hq] sigma = 2^-e
+  float *qside;        // [Ttot, Hkv, DV] sum over the group of delta (.) x
+  void *dz;            // [Ttot, Hq, DV] out dtype, or null
+  float *dw_part;      // [chunks * Hkv][DV] per-block partial sums of dn (.) xh, or null
+};
+
 hipError_t launch_plan(const int64_t *cu, int nseq, int T, int64_t Ttot, const Plan &plan, hipStream_t st);
 hipError_t launch_gate_prep(int dv, const float *g, const void *v, bool in_f32, const Plan &plan, int Hkv,
                             int nch_ub, float *Gl2, float *Gam, _Float16 *VtT, hipStream_t st);
@@ -35,6 +69,33 @@ inline hipError_t launch_fwd(int dk, int dv, bool f32in, const FwdArgs &a, int g
     case 32: return launch_fwd_d32(dv, f32in, a, grid, st);
     case 64: return launch_fwd_d64(dv, f32in, a, grid, st);
     case 128: return launch_fwd_d128(dv, f32in, a, grid, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gate_prep_rows(int dv, const float *g, const void *v, bool in_f32, const Plan &plan, int Hkv,
+                                 int ncb_ub, float *Gl2, float *Gam, _Float16 *Vr, hipStream_t st);
+hipError_t launch_tiles_t(int D, const void *in, bool in_f32, const Plan &plan, int H, int ncb_ub, _Float16 *out,
+                          hipStream_t st);
+hipError_t launch_bwd_prep(int dv, const PrepArgs &a, int ncb_ub, hipStream_t st);
+hipError_t launch_dw_reduce(const float *part, const int *counts, int Hkv, int dv, float *dw, hipStream_t st);
+hipError_t launch_dg_scan(int dv, const float *dG, const Plan &plan, int Hkv, int ncb_ub, float *tot, float *carry,
+                          float *dg, hipStream_t st);
+
+// Backward MFMA kernels, one translation unit per dk.
+enum BwdKernel { BK_INTRA_DQ = 0, BK_INTRA_DKV = 1, BK_DQ = 2, BK_DKV = 3 };
+hipError_t launch_bwd_d16(BwdKernel kind, int dv, bool f32in, const BwdArgs &a, dim3 grid, hipStream_t st);
+hipError_t launch_bwd_d32(BwdKernel kind, int dv, bool f32in, const BwdArgs &a, dim3 grid, hipStream_t st);
+hipError_t launch_bwd_d64(BwdKernel kind, int dv, bool f32in, const BwdArgs &a, dim3 grid, hipStream_t st);
+hipError_t launch_bwd_d128(BwdKernel kind, int dv, bool f32in, const BwdArgs &a, dim3 grid, hipStream_t st);
+
+inline hipError_t launch_bwd(BwdKernel kind, int dk, int dv, bool f32in, const BwdArgs &a, dim3 grid,
+                             hipStream_t st) {
+  switch (dk) {
+    case 16: return launch_bwd_d16(kind, dv, f32in, a, grid, st);
+    case 32: return launch_bwd_d32(kind, dv, f32in, a, grid, st);
+    case 64: return launch_bwd_d64(kind, dv, f32in, a, grid, st);
+    case 128: return launch_bwd_d128(kind, dv, f32in, a, grid, st);
   }
   return hipErrorInvalidValue;
 }

@@ -41,7 +41,7 @@ __global__ void __launch_bounds__(PLAN_THREADS) k_plan(const int64_t *cu, int ns
   // sequences nor exceed the token range or the planned grid sizes.
   __shared__ int64_t mx64[PLAN_THREADS];
   int64_t carry = cu ? min(max(cu[0], (int64_t)0), Ttot) : 0;
-  int run = 0, maxlen = 0;
+  int run = 0, run128 = 0, maxlen = 0;
   for (int base = 0; base < nseq; base += PLAN_THREADS) {
     int s = base + t;
     int64_t b = 0;
@@ -73,6 +73,10 @@ __global__ void __launch_bounds__(PLAN_THREADS) k_plan(const int64_t *cu, int ns
     int tot = block_scan(nch, tmp, excl);
     if (s < nseq) plan.chunk_base[s] = run + excl;
     run += tot;
+    int nb = (len + CB - 1) / CB;
+    tot = block_scan(nb, tmp, excl);
+    if (s < nseq) plan.cb128[s] = run128 + excl;
+    run128 += tot;
     maxlen = max(maxlen, len);
   }
   red[t] = maxlen;
@@ -84,6 +88,7 @@ __global__ void __launch_bounds__(PLAN_THREADS) k_plan(const int64_t *cu, int ns
   int longest = red[0];
   if (t == 0) {
     plan.chunk_base[nseq] = run;
+    plan.cb128[nseq] = run128;
     plan.counts[1] = run;
     plan.counts[2] = longest;
   }

@@ -1,0 +1,235 @@
+"""Benchmark of the FiX attention hot path (forward + backward) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step = fix_attn_fwd + fix_attn_bwd over the training-shape workload
+(B=4, T=8192, Hq=Hkv=16, dk=dv=128, bf16 inputs and outputs, gates
+logsigmoid(N(4, 2))), with inputs, outputs and workspaces resident in HBM
+before the timed region.  Before anything is timed the same inputs pass a
+parity check against the fp64 oracle on a sampled set of rows.  Prints one
+JSON line.  Throughput counts algorithmic flops (FlashAttention convention,
+causal pairs only): forward 2*(dk+dv) per pair and head, backward
+2*(3*dk+2*dv).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16/fp16 MFMA peak (AMD specification)
+METRIC = "FiX attn fwd+bwd TFLOP/s (and % MFMA peak) at T=8192 d=128 bf16, 1 GPU"
+WORKLOAD = "train"
+
+
+def pair_counts(lengths, cb=128):
+    """Causal pairs in total and split by 128-chunk distance (0, 1, >=1, >=2)."""
+    tot = same = adj = 0
+    for L in lengths:
+        tot += L * (L + 1) // 2
+        nch = (L + cb - 1) // cb
+        for I in range(nch):
+            rows = min(cb, L - I * cb)
+            same += rows * (rows + 1) // 2
+            if I >= 1:
+                adj += rows * cb
+    return {"all": tot, "same": same, "adj": adj, "inter": tot - same, "far": tot - same - adj}
+
+
+def hip():
+    lib = ctypes.CDLL("libamdhip64.so")
+    lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+    return lib
+
+
+def parity_gate(x, d, F, torch):
+    """Sampled parity against the oracle (last 64 rows of two (sequence, kv head) units)."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import oracle as O
+    from gpu_util import err_rms
+    o, m, rstd, xx = F.forward(d["q"], d["k"], d["v"], d["g"], o_norm=True, out_dtype=torch.float32)
+    dq, dk, dv, dg, _, _ = F.backward(d["q"], d["k"], d["v"], d["g"], m, rstd, xx, d["dO"], o_norm=True,
+                                      out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    wl = x["workload"]
+    mask = np.zeros((wl.B, wl.Hkv), np.uint8)
+    mask[0, 0] = mask[wl.B - 1, wl.Hkv - 1] = 1
+    rf = O.oracle_fwd(x["q"], x["k"], x["v"], x["g"], unit_mask=mask, window=64)
+    rb = O.oracle_bwd(x["q"], x["k"], x["v"], x["g"], x["dO"], unit_mask=mask, window=64)
+    errs = {"o": err_rms(o.cpu().numpy(), rf["o"])}
+    for n, t in (("dq", dq), ("dk", dk), ("dv", dv), ("dg", dg)):
+        errs[n] = err_rms(t.cpu().numpy(), rb[n])
+    ok = all(v <= (5e-3 if n == "dg" else 1e-2) for n, v in errs.items())
+    return ok, errs
+
+
+def cpu_baseline(x):
+    """The fp64 oracle, fwd + bwd, on four heads of one batch row of the same workload, full length."""
+    import oracle as O
+    NH = 4
+    sl = lambda a: np.ascontiguousarray(a[:1, :, :NH])
+    q, k, v, g, dO = (sl(x[n]) for n in ("q", "k", "v", "g", "dO"))
+    O.load()
+    t0 = time.perf_counter()
+    O.oracle_fwd(q, k, v, g)
+    t1 = time.perf_counter()
+    O.oracle_bwd(q, k, v, g, dO)
+    t2 = time.perf_counter()
+    wl = x["workload"]
+    pairs = wl.T * (wl.T + 1) // 2 * NH
+    flops = (2 * (wl.dk + wl.dv) + 2 * (3 * wl.dk + 2 * wl.dv)) * pairs
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": flops / (t2 - t0) / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"heads 0-{NH - 1} of batch row 0 of the workload: B=1 T={wl.T} H={NH} d={wl.dk}, "
+                      f"fwd {t1 - t0:.1f} s + "
+                      f"bwd {t2 - t1:.1f} s (the backward recomputes the forward)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build runs the kernel on one GPU's share and has no "
+              f"multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_softmax_attention_amd as F
+    from gated_softmax_attention_amd import synth
+
+    x = synth.make_inputs(WORKLOAD)
+    wl = x["workload"]
+    dev = lambda a, dt=torch.bfloat16: torch.from_numpy(np.ascontiguousarray(a)).to(dt).cuda()
+    d = {n: dev(x[n]) for n in ("q", "k", "v", "dO")}
+    d["g"] = dev(x["g"], torch.float32)
+    print(f"[bench] inputs resident: {wl}", file=sys.stderr, flush=True)
+
+    ok, errs = parity_gate(x, d, F, torch)
+    print(f"[bench] parity gate: {'pass' if ok else 'FAIL'} {errs}", file=sys.stderr, flush=True)
+    if not ok:
+        sys.exit(1)
+
+    B, T, Hq, dk = d["q"].shape
+    Hkv, dv = d["k"].shape[2], d["v"].shape[3]
+    bf = torch.bfloat16
+    o = torch.empty(B, T, Hq, dv, dtype=bf, device="cuda")
+    m = torch.empty(B, T, Hq, device="cuda")
+    rstd = torch.empty(B, T, Hq, device="cuda")
+    xx = torch.empty(B, T, Hq, dv, device="cuda")
+    dq, dkk, dvv = torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"])
+    dg = torch.empty_like(d["g"])
+    desc = F.make_desc(d["q"], d["k"], d["v"], o_norm=True)
+    wf, wb = F.fix_attn_fwd_workspace_size(desc), F.fix_attn_bwd_workspace_size(desc)
+    ws_f = torch.empty(wf, dtype=torch.uint8, device="cuda")
+    ws_b = torch.empty(wb, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    lib = F.library()
+    lib.fix_attn_set_event_trace.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    lib.fix_attn_event_trace_count.restype = ctypes.c_int
+    lib.fix_attn_event_trace_label.restype = ctypes.c_char_p
+    lib.fix_attn_event_trace_label.argtypes = [ctypes.c_int]
+
+    def step():
+        F.fix_attn_fwd(desc, d["q"], d["k"], d["v"], d["g"], None, None, o, m, rstd, xx, ws_f, wf, stream)
+        F.fix_attn_bwd(desc, d["q"], d["k"], d["v"], d["g"], None, None, m, rstd, xx, d["dO"], dq, dkk, dvv, dg,
+                       None, None, ws_b, wb, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Per-kernel events recorded by the library on its stream during the timed steps.
+    h = hip()
+    cap = 16
+    ev = [[(ctypes.c_void_p * cap)() for _ in range(2)] for _ in range(args.steps)]
+    for s in ev:
+        for arr in s:
+            for i in range(cap):
+                e = ctypes.c_void_p()
+                assert h.hipEventCreate(ctypes.byref(e)) == 0
+                arr[i] = e
+    labels = [None, None]
+    counts = [0, 0]
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        lib.fix_attn_set_event_trace(ctypes.cast(ev[k][0], ctypes.c_void_p), cap)
+        F.fix_attn_fwd(desc, d["q"], d["k"], d["v"], d["g"], None, None, o, m, rstd, xx, ws_f, wf, stream)
+        counts[0] = lib.fix_attn_event_trace_count()
+        if labels[0] is None:
+            labels[0] = [lib.fix_attn_event_trace_label(i).decode() for i in range(1, counts[0])]
+        lib.fix_attn_set_event_trace(ctypes.cast(ev[k][1], ctypes.c_void_p), cap)
+        F.fix_attn_bwd(desc, d["q"], d["k"], d["v"], d["g"], None, None, m, rstd, xx, d["dO"], dq, dkk, dvv, dg,
+                       None, None, ws_b, wb, stream)
+        counts[1] = lib.fix_attn_event_trace_count()
+        if labels[1] is None:
+            labels[1] = [lib.fix_attn_event_trace_label(i).decode() for i in range(1, counts[1])]
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    lib.fix_attn_set_event_trace(None, 0)
+    ms_step = (t1 - t0) * 1e3 / args.steps
+
+    per_kernel = {}
+    for k in range(args.steps):
+        for side in (0, 1):
+            for i in range(1, counts[side]):
+                t = ctypes.c_float()
+                assert h.hipEventElapsedTime(ctypes.byref(t), ev[k][side][i - 1], ev[k][side][i]) == 0
+                per_kernel.setdefault(labels[side][i - 1], []).append(t.value)
+    avg = {n: sum(v) / len(v) for n, v in per_kernel.items()}
+
+    pc = pair_counts([T] * B)
+    heads = Hq
+    fwd_flops = 2 * (dk + dv) * pc["all"] * heads
+    bwd_flops = 2 * (3 * dk + 2 * dv) * pc["all"] * heads
+    total = fwd_flops + bwd_flops
+    tflops = total / (ms_step * 1e-3) / 1e12
+    # Algorithmic flops of each kernel: its share of the 2 forward and 5 backward products.
+    alg = {
+        "fix_fwd": fwd_flops,
+        "bwd_dq": 2 * (2 * dk + dv) * pc["inter"] * heads,        # S, dP, dQ on pairs in different chunks
+        "bwd_dkv": 2 * (dk + dv) * pc["far"] * heads,             # dV, dK on pairs two or more chunks apart
+        "bwd_intra_dq": 2 * (2 * dk + dv) * pc["same"] * heads,
+        "bwd_intra_dkv": 2 * (dk + dv) * (pc["same"] + pc["adj"]) * heads,
+    }
+    dom = max(avg, key=avg.get)
+    roof = None
+    if dom in alg:
+        ach = alg[dom] / (avg[dom] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "avg_launch_ms": round(avg[dom], 4)}
+    out = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{WORKLOAD}: B={B} T={T} Hq={Hq} Hkv={Hkv} dk={dk} dv={dv} bf16 in/out, "
+                               f"g=logsigmoid(N({wl.gate_mu},{wl.gate_sd})), o_norm, fwd+bwd",
+                   "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+                   "fwd_flops": fwd_flops, "bwd_flops": bwd_flops,
+                   "kernel_ms": {n: round(v, 4) for n, v in sorted(avg.items(), key=lambda kv: -kv[1])}},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host ...", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(x)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -62,6 +62,12 @@ def _load():
     lib.fix_attn_status_string.restype = ctypes.c_char_p
     lib.fix_attn_last_hip_error.argtypes = []
     lib.fix_attn_last_hip_error.restype = ctypes.c_int
+    lib.fix_attn_set_event_trace.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    lib.fix_attn_set_event_trace.restype = None
+    lib.fix_attn_event_trace_count.argtypes = []
+    lib.fix_attn_event_trace_count.restype = ctypes.c_int
+    lib.fix_attn_event_trace_label.argtypes = [ctypes.c_int]
+    lib.fix_attn_event_trace_label.restype = ctypes.c_char_p
     _lib = lib
     return lib
 

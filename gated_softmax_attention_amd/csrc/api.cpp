@@ -15,6 +15,27 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
+// Opt-in event trace (see fix_attn_set_event_trace).
+struct Trace {
+  hipEvent_t *events = nullptr;
+  int capacity = 0, count = 0;
+  const char *labels[64] = {};
+};
+thread_local Trace g_trace;
+
+hipError_t trace_begin(hipStream_t st) {
+  g_trace.count = 0;
+  if (!g_trace.events || g_trace.capacity < 1) return hipSuccess;
+  g_trace.labels[0] = "begin";
+  g_trace.count = 1;
+  return hipEventRecord(g_trace.events[0], st);
+}
+hipError_t trace_mark(hipStream_t st, const char *label) {
+  if (!g_trace.events || g_trace.count >= g_trace.capacity || g_trace.count >= 64) return hipSuccess;
+  g_trace.labels[g_trace.count] = label;
+  return hipEventRecord(g_trace.events[g_trace.count++], st);
+}
+
 bool head_dim_ok(int64_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -158,9 +179,13 @@ fix_status fix_attn_fwd(const fix_attn_desc *d, const void *q, const void *k, co
   FwdWs w;
   carve_fwd(cv, d, w);
   const bool f32in = d->in_dtype == FIX_F32;
-  hipError_t e = fix::launch_plan(d->cu_seqlens, (int)s.nseq, (int)d->T, s.Ttot, w.plan, st);
+  hipError_t e = trace_begin(st);
+  if (e != hipSuccess) return hip_fail(e);
+  e = fix::launch_plan(d->cu_seqlens, (int)s.nseq, (int)d->T, s.Ttot, w.plan, st);
+  if (e == hipSuccess) e = trace_mark(st, "plan");
   if (e != hipSuccess) return hip_fail(e);
   e = fix::launch_gate_prep((int)d->dv, g, v, f32in, w.plan, (int)d->Hkv, (int)s.nch_ub, w.Gl2, w.Gam, w.VtT, st);
+  if (e == hipSuccess) e = trace_mark(st, "gate_prep");
   if (e != hipSuccess) return hip_fail(e);
   fix::FwdArgs a;
   a.q = q; a.k = k; a.v = v;
@@ -175,6 +200,7 @@ fix_status fix_attn_fwd(const fix_attn_desc *d, const void *q, const void *k, co
   a.o_norm = d->o_norm ? 1 : 0;
   a.out_f32 = d->out_dtype == FIX_F32;
   e = fix::launch_fwd((int)d->dk, (int)d->dv, f32in, a, (int)(s.nqb_ub * d->Hq), st);
+  if (e == hipSuccess) e = trace_mark(st, "fix_fwd");
   if (e != hipSuccess) return hip_fail(e);
   return FIX_OK;
 }
@@ -209,13 +235,16 @@ fix_status fix_attn_bwd(const fix_attn_desc *d, const void *q, const void *k, co
   const int Hq = (int)d->Hq, Hkv = (int)d->Hkv, DK = (int)d->dk, DV = (int)d->dv, ncb = (int)s.nqb_ub;
   const bool want_dw = d->o_norm && d_o_norm_weight;
   hipError_t e;
-#define FIX_TRY(call)             \
-  e = (call);                     \
+#define FIX_TRY(call, label)          \
+  e = (call);                         \
+  if (e == hipSuccess) e = trace_mark(st, label); \
   if (e != hipSuccess) return hip_fail(e);
-  FIX_TRY(fix::launch_plan(d->cu_seqlens, (int)s.nseq, (int)d->T, s.Ttot, w.plan, st));
-  FIX_TRY(fix::launch_gate_prep_rows(DV, g, v, f32in, w.plan, Hkv, ncb, w.Gl2, w.Gam, w.Vr, st));
-  FIX_TRY(fix::launch_tiles_t(DK, q, f32in, w.plan, Hq, ncb, w.Qt, st));
-  FIX_TRY(fix::launch_tiles_t(DK, k, f32in, w.plan, Hkv, ncb, w.Kt, st));
+  e = trace_begin(st);
+  if (e != hipSuccess) return hip_fail(e);
+  FIX_TRY(fix::launch_plan(d->cu_seqlens, (int)s.nseq, (int)d->T, s.Ttot, w.plan, st), "plan");
+  FIX_TRY(fix::launch_gate_prep_rows(DV, g, v, f32in, w.plan, Hkv, ncb, w.Gl2, w.Gam, w.Vr, st), "gate_prep_rows");
+  FIX_TRY(fix::launch_tiles_t(DK, q, f32in, w.plan, Hq, ncb, w.Qt, st), "tiles_q");
+  FIX_TRY(fix::launch_tiles_t(DK, k, f32in, w.plan, Hkv, ncb, w.Kt, st), "tiles_k");
   fix::PrepArgs pa;
   pa.x = x; pa.rstd = rstd; pa.m = m; pa.Gl2 = w.Gl2;
   pa.dO = d_o; pa.z = o_gate; pa.w = d->o_norm ? o_norm_weight : nullptr;
@@ -227,7 +256,7 @@ fix_status fix_attn_bwd(const fix_attn_desc *d, const void *q, const void *k, co
   pa.delta = w.delta; pa.dh = w.dh; pa.dht = w.dht; pa.mb = w.mb; pa.sig = w.sig; pa.qside = w.qside;
   pa.dz = d_o_gate;
   pa.dw_part = want_dw ? w.dw_part : nullptr;
-  FIX_TRY(fix::launch_bwd_prep(DV, pa, ncb, st));
+  FIX_TRY(fix::launch_bwd_prep(DV, pa, ncb, st), "bwd_prep");
   fix::BwdArgs a;
   a.q = q; a.k = k; a.v = v;
   a.Gl2 = w.Gl2; a.Gam = w.Gam; a.Vr = w.Vr; a.Qt = w.Qt; a.Kt = w.Kt;
@@ -240,12 +269,14 @@ fix_status fix_attn_bwd(const fix_attn_desc *d, const void *q, const void *k, co
   a.sl2 = scale * fix::LOG2E;
   a.scale = scale;
   a.out_f32 = d->out_dtype == FIX_F32;
-  FIX_TRY(fix::launch_bwd(fix::BK_INTRA_DQ, DK, DV, f32in, a, dim3(ncb, Hq), st));
-  FIX_TRY(fix::launch_bwd(fix::BK_INTRA_DKV, DK, DV, f32in, a, dim3(ncb, Hkv), st));
-  FIX_TRY(fix::launch_bwd(fix::BK_DQ, DK, DV, f32in, a, dim3(ncb * Hq), st));
-  FIX_TRY(fix::launch_bwd(fix::BK_DKV, DK, DV, f32in, a, dim3(ncb * Hkv), st));
-  FIX_TRY(fix::launch_dg_scan(DV, w.dG, w.plan, Hkv, ncb, w.dg_tot, w.dg_carry, dg, st));
-  if (want_dw) FIX_TRY(fix::launch_dw_reduce(w.dw_part, w.plan.counts, Hkv, DV, d_o_norm_weight, st));
+  FIX_TRY(fix::launch_bwd(fix::BK_INTRA_DQ, DK, DV, f32in, a, dim3(ncb, Hq), st), "bwd_intra_dq");
+  FIX_TRY(fix::launch_bwd(fix::BK_INTRA_DKV, DK, DV, f32in, a, dim3(ncb, Hkv), st), "bwd_intra_dkv");
+  FIX_TRY(fix::launch_bwd(fix::BK_DQ, DK, DV, f32in, a, dim3(ncb * Hq), st), "bwd_dq");
+  FIX_TRY(fix::launch_bwd(fix::BK_DKV, DK, DV, f32in, a, dim3(ncb * Hkv), st), "bwd_dkv");
+  FIX_TRY(fix::launch_dg_scan(DV, w.dG, w.plan, Hkv, ncb, w.dg_tot, w.dg_carry, dg, st), "dg_scan");
+  if (want_dw) {
+    FIX_TRY(fix::launch_dw_reduce(w.dw_part, w.plan.counts, Hkv, DV, d_o_norm_weight, st), "dw_reduce");
+  }
 #undef FIX_TRY
   return FIX_OK;
 }
@@ -262,5 +293,18 @@ const char *fix_attn_status_string(fix_status s) {
 }
 
 int fix_attn_last_hip_error(void) { return g_last_hip_error; }
+
+void fix_attn_set_event_trace(void **events, int capacity) {
+  g_trace.events = (hipEvent_t *)events;
+  g_trace.capacity = events ? capacity : 0;
+  g_trace.count = 0;
+}
+
+int fix_attn_event_trace_count(void) { return g_trace.count; }
+
+const char *fix_attn_event_trace_label(int i) {
+  if (i < 1 || i >= g_trace.count) return nullptr;
+  return g_trace.labels[i];
+}
 
 }  // extern "C"

@@ -26,7 +26,8 @@
  *  - Layout: every tensor is a contiguous row-major [B, T, H, D] device
  *    buffer (packed: B = 1, T = total tokens), 16-byte aligned.
  *  - Ownership: all buffers belong to the caller.  The library never
- *    allocates or frees device memory and keeps no state between calls;
+ *    allocates or frees device memory and keeps no state between calls
+ *    (apart from the opt-in, per-thread event trace setting below);
  *    scratch memory is the caller's `ws` of at least the size the matching
  *    *_workspace_size function returns.  Calls are reentrant.
  *  - Asynchrony: work is enqueued on `hip_stream` (a hipStream_t, NULL for
@@ -122,6 +123,19 @@ fix_status fix_attn_bwd(const fix_attn_desc *d, const void *q, const void *k, co
                         const float *m, const float *rstd, const float *x, const void *d_o,
                         void *dq, void *dk, void *dv, float *dg, float *d_o_norm_weight,
                         void *d_o_gate, void *ws, size_t ws_bytes, void *hip_stream);
+
+/* Opt-in launch timing for benchmarks (host side, per calling thread).
+ * With events non-NULL and capacity > 0, every later fix_attn_fwd /
+ * fix_attn_bwd call on this thread records events[0] on its stream before
+ * its first kernel and events[i] after its i-th launch, at most capacity
+ * events; the events are hipEvent_t created by the caller and stay the
+ * caller's.  fix_attn_event_trace_count() gives the number recorded by the
+ * last call, fix_attn_event_trace_label(i) (i >= 1) the name of the launch
+ * that events[i] closes (NULL out of range).  events == NULL turns it off.
+ * A failed hipEventRecord ends the call with FIX_E_HIP. */
+void fix_attn_set_event_trace(void **events, int capacity);
+int fix_attn_event_trace_count(void);
+const char *fix_attn_event_trace_label(int i);
 
 /* Static, NUL-terminated description of a status code. */
 const char *fix_attn_status_string(fix_status s);

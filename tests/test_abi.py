@@ -1,0 +1,111 @@
+"""The C ABI on the host: exported symbols, descriptor validation, workspace sizing,
+status strings (no GPU needed: validation makes no HIP call)."""
+import ctypes
+import re
+import os
+
+import pytest
+
+import gated_softmax_attention_amd as F
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "fixattn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fix_attn_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    lib = F.library()
+    names = declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in fixattn.h but not exported"
+
+
+def desc(**kw):
+    d = F.fix_attn_desc()
+    base = dict(B=2, T=100, Hq=4, Hkv=2, dk=64, dv=64, in_dtype=F.FIX_BF16, out_dtype=F.FIX_BF16, scale=0.0,
+                eps=1e-5, o_norm=1)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(d, k, v)
+    return d
+
+
+def test_valid_descriptor():
+    assert F.fix_attn_validate(desc()) == F.FIX_OK
+    for dk in (16, 32, 64, 128):
+        for dv in (16, 32, 64, 128):
+            assert F.fix_attn_validate(desc(dk=dk, dv=dv)) == F.FIX_OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"B": 0}, F.FIX_E_INVALID), ({"T": 0}, F.FIX_E_INVALID), ({"Hq": 0}, F.FIX_E_INVALID),
+    ({"Hkv": 0}, F.FIX_E_INVALID), ({"Hq": 6, "Hkv": 4}, F.FIX_E_INVALID),
+    ({"in_dtype": 7}, F.FIX_E_INVALID), ({"out_dtype": -1}, F.FIX_E_INVALID),
+    ({"eps": -1.0}, F.FIX_E_INVALID), ({"eps": float("nan")}, F.FIX_E_INVALID),
+    ({"scale": float("inf")}, F.FIX_E_INVALID),
+    ({"dk": 48}, F.FIX_E_UNSUPPORTED), ({"dv": 256}, F.FIX_E_UNSUPPORTED), ({"dk": 8}, F.FIX_E_UNSUPPORTED),
+    ({"B": 1, "T": 2 ** 31}, F.FIX_E_UNSUPPORTED),
+])
+def test_invalid_descriptors(kw, status):
+    assert F.fix_attn_validate(desc(**kw)) == status
+
+
+def test_packed_descriptor_rules():
+    d = desc(B=1)
+    d.cu_seqlens = 0x1000  # never dereferenced on the host
+    d.num_seqs = 3
+    assert F.fix_attn_validate(d) == F.FIX_OK
+    d.num_seqs = 0
+    assert F.fix_attn_validate(d) == F.FIX_E_INVALID
+    d = desc(B=2)
+    d.cu_seqlens = 0x1000
+    d.num_seqs = 3
+    assert F.fix_attn_validate(d) == F.FIX_E_INVALID
+
+
+def test_workspace_sizes():
+    assert F.fix_attn_fwd_workspace_size(desc(dk=48)) == 0
+    assert F.fix_attn_bwd_workspace_size(desc(B=0)) == 0
+    small, large = desc(T=100), desc(T=1000)
+    assert 0 < F.fix_attn_fwd_workspace_size(small) < F.fix_attn_fwd_workspace_size(large)
+    assert 0 < F.fix_attn_bwd_workspace_size(small) < F.fix_attn_bwd_workspace_size(large)
+    assert F.fix_attn_fwd_workspace_size(small) % 256 == 0
+
+
+def test_entry_points_reject_before_launching():
+    lib = F.library()
+    d = desc()
+    # missing required pointers: rejected on the host, nothing enqueued
+    assert lib.fix_attn_fwd(ctypes.byref(d), None, None, None, None, None, None, None, None, None, None, None,
+                            0, None) == F.FIX_E_INVALID
+    assert lib.fix_attn_bwd(ctypes.byref(d), *([None] * 17), 0, None) == F.FIX_E_INVALID
+    bad = desc(dk=48)
+    assert lib.fix_attn_fwd(ctypes.byref(bad), *([None] * 10), None, 0, None) == F.FIX_E_UNSUPPORTED
+    # a too-small workspace is reported as such (pointers are never dereferenced on the host)
+    fake = 0x10000
+    st = lib.fix_attn_fwd(ctypes.byref(d), fake, fake, fake, fake, None, None, fake, fake, fake, None, fake, 16, None)
+    assert st == F.FIX_E_WORKSPACE
+    # misaligned q
+    st = lib.fix_attn_fwd(ctypes.byref(d), fake + 2, fake, fake, fake, None, None, fake, fake, fake, None, fake,
+                          1 << 40, None)
+    assert st == F.FIX_E_INVALID
+
+
+def test_status_strings():
+    lib = F.library()
+    for s in range(5):
+        assert lib.fix_attn_status_string(s)
+    assert b"head dim" in lib.fix_attn_status_string(F.FIX_E_UNSUPPORTED)
+    assert lib.fix_attn_last_hip_error() == 0
+
+
+def test_event_trace_setting_is_host_only():
+    lib = F.library()
+    lib.fix_attn_set_event_trace(None, 0)
+    assert lib.fix_attn_event_trace_count() == 0
+    assert lib.fix_attn_event_trace_label(1) is None

@@ -93,6 +93,7 @@ size_t carve_fwd(Carve &cv, const fix_attn_desc *d, FwdWs &w) {
 struct BwdWs {
   fix::Plan plan;
   float *Gl2, *Gam;
+  double *Lam;
   _Float16 *Vr, *Qt, *Kt;
   float *delta;
   _Float16 *dh, *dht;
@@ -105,6 +106,7 @@ size_t carve_bwd(Carve &cv, const fix_attn_desc *d, BwdWs &w) {
   const int64_t T = s.Ttot, ncb = s.nqb_ub, Hq = d->Hq, Hkv = d->Hkv, DK = d->dk, DV = d->dv;
   w.Gl2 = cv.take<float>(T * Hkv * DV);
   w.Gam = cv.take<float>(ncb * Hkv * DV);
+  w.Lam = cv.take<double>(ncb * Hkv * DV);
   w.Vr = cv.take<_Float16>(ncb * Hkv * fix::CB * DV);
   w.Qt = cv.take<_Float16>(ncb * Hq * DK * fix::CB);
   w.Kt = cv.take<_Float16>(ncb * Hkv * DK * fix::CB);
@@ -243,6 +245,7 @@ fix_status fix_attn_bwd(const fix_attn_desc *d, const void *q, const void *k, co
   if (e != hipSuccess) return hip_fail(e);
   FIX_TRY(fix::launch_plan(d->cu_seqlens, (int)s.nseq, (int)d->T, s.Ttot, w.plan, st), "plan");
   FIX_TRY(fix::launch_gate_prep_rows(DV, g, v, f32in, w.plan, Hkv, ncb, w.Gl2, w.Gam, w.Vr, st), "gate_prep_rows");
+  FIX_TRY(fix::launch_chunk_logprefix(DV, w.Gl2, w.plan, Hkv, w.Lam, st), "chunk_logprefix");
   FIX_TRY(fix::launch_tiles_t(DK, q, f32in, w.plan, Hq, ncb, w.Qt, st), "tiles_q");
   FIX_TRY(fix::launch_tiles_t(DK, k, f32in, w.plan, Hkv, ncb, w.Kt, st), "tiles_k");
   fix::PrepArgs pa;
@@ -259,7 +262,7 @@ fix_status fix_attn_bwd(const fix_attn_desc *d, const void *q, const void *k, co
   FIX_TRY(fix::launch_bwd_prep(DV, pa, ncb, st), "bwd_prep");
   fix::BwdArgs a;
   a.q = q; a.k = k; a.v = v;
-  a.Gl2 = w.Gl2; a.Gam = w.Gam; a.Vr = w.Vr; a.Qt = w.Qt; a.Kt = w.Kt;
+  a.Gl2 = w.Gl2; a.Gam = w.Gam; a.Lam = w.Lam; a.Vr = w.Vr; a.Qt = w.Qt; a.Kt = w.Kt;
   a.delta = w.delta; a.dh = w.dh; a.dht = w.dht; a.mb = w.mb; a.sig = w.sig; a.qside = w.qside;
   a.dq_i = w.dq_i; a.dk_i = w.dk_i; a.dv_i = w.dv_i;
   a.dq = dq; a.dk = dk; a.dv = dv; a.dG = w.dG;

@@ -40,15 +40,49 @@ constexpr float BGUARD = 100.f;  // largest factored gate range of a 32-token bl
 
 template <int D> struct Pad32 { static constexpr int value = D < 32 ? 32 : D; };
 
+// Exact per-pair decays for a diagonal 32x32 block whose gate range exceeds
+// 2^BGUARD (rare): dP for the pairs held by this lane, evaluated directly.
+// Register j of lane (hh, n) holds the pair (row q0 + rowof(j, n), key k0 + keyof(j, n)).
+template <int DV, bool F32IN, bool ROW_IS_LANE>
+__device__ __noinline__ void direct_dp(const BwdArgs &a, int64_t st, int c, int h, int L, int q0, int k0, int hh,
+                                       int n, float *dp) {
+  const int Hq = a.Hq, Hkv = a.Hkv;
+  for (int j = 0; j < 16; ++j) {
+    const int r = ROW_IS_LANE ? n : acc_row(hh, j);
+    const int kk = ROW_IS_LANE ? acc_row(hh, j) : n;
+    const int qi = q0 + r, kj = k0 + kk;
+    float t = 0.f;
+    if (qi < L && kj <= qi) {
+      const float *dr = a.delta + ((st + qi) * Hq + h) * DV;
+      const float sg = a.sig[(st + qi) * Hq + h];
+      for (int d = 0; d < DV; ++d) {
+        const float gq = a.Gl2[((st + qi) * Hkv + c) * DV + d], gk = a.Gl2[((st + kj) * Hkv + c) * DV + d];
+        t += dr[d] * sg * fast_exp2(gq - gk) * load_in(a.v, ((st + kj) * Hkv + c) * DV + d, F32IN);
+      }
+    }
+    dp[j] = t;
+  }
+}
+
 // ---------------------------------------------------------------------------
-// Within-chunk contributions to dq: wave w of the workgroup owns query rows
-// c0 + 32w .. +31 of one 128-chunk and one q head.
+// Within-chunk contributions to dq.  Workgroup = one 128-chunk of one q head;
+// wave w owns query rows c0 + 32w .. +31.  Key blocks b = 0..3 are staged in
+// LDS once for all waves: K rows, transposed K, the key operand scaled to the
+// end of the block (for rows of later blocks, <= 1, fp16) and the key
+// operand scaled from the token before the block (for the diagonal block,
+// >= 1, bf16 hi/lo).
 // ---------------------------------------------------------------------------
 template <int DK, int DV, bool F32IN>
-__global__ void __launch_bounds__(256) k_bwd_intra_dq(BwdArgs a) {
+__global__ void __launch_bounds__(256, 1) k_bwd_intra_dq(BwdArgs a) {
   using IF = InFrag<F32IN>;
   using kfrag = typename IF::type;
-  constexpr int NS = DK / 16, NSV = DV / 16, NBK = Pad32<DK>::value / 32;
+  constexpr int NS = DK / 16, NSV = DV / 16, DKP = Pad32<DK>::value, NBK = DKP / 32;
+  constexpr int KSTR = DK + 8, VSTR = DV + 8, TSTR = 32 + 8;
+  __shared__ __align__(16) uint16_t Ks[32 * KSTR];
+  __shared__ __align__(16) _Float16 Kts[DKP * TSTR];
+  __shared__ __align__(16) _Float16 Vo[32 * VSTR];
+  __shared__ __align__(16) __bf16 Vdh[32 * VSTR];
+  __shared__ __align__(16) __bf16 Vdl[32 * VSTR];
   const Plan &pl = a.plan;
   const int gc = blockIdx.x, hq = blockIdx.y;
   if (gc >= pl.counts[0]) return;
@@ -58,100 +92,108 @@ __global__ void __launch_bounds__(256) k_bwd_intra_dq(BwdArgs a) {
   const int L = pl.seq_len[s];
   const int64_t st = pl.seq_start[s];
   const int Hq = a.Hq, Hkv = a.Hkv, c = hq / (Hq / Hkv);
+  const int nblk = min(4, (L - c0 + 31) / 32);  // query (and key) blocks present in the chunk
   const int r0 = c0 + 32 * wave;
-  if (r0 >= L) return;
   const int row = r0 + n;
-  const bool rv = row < L;
+  const bool active = wave < nblk;
+  const bool rv = active && row < L;
   const float sl2 = a.sl2;
-  auto gl = [&](int tok, int d) { return a.Gl2[((st + tok) * Hkv + c) * DV + d]; };
-  auto vv = [&](int tok, int d) { return load_in(a.v, ((st + tok) * Hkv + c) * DV + d, F32IN); };
+  auto gl = [&](int tok, int d) { return tok < c0 ? 0.f : a.Gl2[((st + tok) * Hkv + c) * DV + d]; };
 
+  if (DK < DKP)
+    for (int e = tid; e < (DKP - DK) * TSTR; e += 256) Kts[DK * TSTR + e] = (_Float16)0.f;
   kfrag qf[NS];
 #pragma unroll
   for (int i = 0; i < NS; ++i)
     qf[i] = rv ? IF::load(a.q, ((st + row) * Hq + hq) * DK + 16 * i + 8 * hh) : IF::zero();
   const float mbn = rv ? a.mb[(st + row) * Hq + hq] : INFINITY;
   const float sgn = rv ? a.sig[(st + row) * Hq + hq] : 0.f;
-  const float *drow = a.delta + ((st + row) * Hq + hq) * DV;
-
+  const float *drow = a.delta + ((st + (rv ? row : c0)) * Hq + hq) * DV;
   f32x16 acc[NBK];
 #pragma unroll
   for (int b = 0; b < NBK; ++b) acc[b] = zero16();
 
-  for (int b = 0; b <= wave; ++b) {
+  for (int b = 0; b < nblk; ++b) {
     const int kb = c0 + 32 * b;
-    const int key = kb + n;
-    const bool diag = b == wave;
-    const int ref = diag ? kb - 1 : kb + 31;  // token the decay is split at (c0 - 1: chunk start)
+    // ---- stage key block b ----
+    __syncthreads();
+    for (int p = tid; p < 32 * DK / 8; p += 256) {
+      const int r = p / (DK / 8), e8 = p % (DK / 8);
+      *(uint4 *)&Ks[r * KSTR + 8 * e8] =
+          kb + r < L ? __builtin_bit_cast(uint4, IF::load(a.k, ((st + kb + r) * Hkv + c) * DK + 8 * e8))
+                     : make_uint4(0, 0, 0, 0);
+    }
+    const _Float16 *ktile = a.Kt + ((int64_t)gc * Hkv + c) * DK * CB + 32 * b;
+    for (int p = tid; p < DK * 4; p += 256) *(uint4 *)&Kts[(p >> 2) * TSTR + 8 * (p & 3)] = *(const uint4 *)(ktile + (p >> 2) * CB + 8 * (p & 3));
+    for (int e = tid; e < 32 * DV; e += 256) {
+      const int r = e / DV, d = e % DV, tok = kb + r;
+      float vo = 0.f, vd = 0.f;
+      if (tok < L) {
+        const float gk = gl(tok, d), vvv = load_in(a.v, ((st + tok) * Hkv + c) * DV + d, F32IN);
+        vo = fast_exp2(gl(min(kb + 31, L - 1), d) - gk) * vvv;
+        vd = fast_exp2(gl(kb - 1, d) - gk) * vvv;
+      }
+      Vo[r * VSTR + d] = (_Float16)vo;
+      const __bf16 hi = (__bf16)vd;
+      Vdh[r * VSTR + d] = hi;
+      Vdl[r * VSTR + d] = (__bf16)(vd - (float)hi);
+    }
+    __syncthreads();
+    if (!active || wave < b) continue;
+    const bool diag = wave == b;
+    const int ref = diag ? kb - 1 : kb + 31;
     // S^T[key][row]
     f32x16 sc = zero16();
 #pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      kfrag kf = key < L ? IF::load(a.k, ((st + key) * Hkv + c) * DK + 16 * i + 8 * hh) : IF::zero();
-      sc = mma32(kf, qf[i], sc);
-    }
+    for (int i = 0; i < NS; ++i) sc = mma32(*(const kfrag *)&Ks[n * KSTR + 16 * i + 8 * hh], qf[i], sc);
     float p[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       p[j] = fast_exp2(sc[j] * sl2 - mbn);
       if (diag && acc_row(hh, j) > n) p[j] = 0.f;
     }
-    // dP^T[key][row] = sum_d Vx[key][d] dx[row][d]
     f32x16 dp = zero16();
-    bool direct = false;
     if (!diag) {
 #pragma unroll
       for (int sv = 0; sv < NSV; ++sv) {
-        f16x8 va, db;
+        f16x8 db;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int d = 16 * sv + 8 * hh + e;
-          const float gr = gl(ref, d);
-          va[e] = (_Float16)(fast_exp2(gr - gl(key, d)) * vv(key, d));
-          db[e] = (_Float16)(rv ? fast_exp2(gl(row, d) - gr) * drow[d] * sgn : 0.f);
+          db[e] = (_Float16)(rv ? fast_exp2(gl(row, d) - gl(ref, d)) * drow[d] * sgn : 0.f);
         }
-        dp = mma32(va, db, dp);
+        dp = mma32(*(const f16x8 *)&Vo[n * VSTR + 16 * sv + 8 * hh], db, dp);
       }
     } else {
-      const int klast = min(kb + 31, L - 1);
       float rng = 0.f;
+      const int klast = min(kb + 31, L - 1);
 #pragma unroll
       for (int sv = 0; sv < NSV; ++sv)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int d = 16 * sv + 8 * hh + e;
-          rng = fmaxf(rng, (ref >= c0 ? gl(ref, d) : 0.f) - gl(klast, d));
+          rng = fmaxf(rng, gl(ref, d) - gl(klast, d));
         }
-      direct = __any(rng > BGUARD);
-      if (!direct) {
+      if (!__any(rng > BGUARD)) {
 #pragma unroll
         for (int sv = 0; sv < NSV; ++sv) {
-          bf16x8 vh, vl, dh_, dl_;
+          bf16x8 dh_, dl_;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int d = 16 * sv + 8 * hh + e;
-            const float gr = ref >= c0 ? gl(ref, d) : 0.f;
-            const float vx = key < L ? fast_exp2(gr - gl(key, d)) * vv(key, d) : 0.f;
-            const float dx = rv ? fast_exp2(gl(row, d) - gr) * drow[d] * sgn : 0.f;
-            split_bf16(vx, vh, vl, e);
-            split_bf16(dx, dh_, dl_, e);
+            split_bf16(rv ? fast_exp2(gl(row, d) - gl(ref, d)) * drow[d] * sgn : 0.f, dh_, dl_, e);
           }
+          const bf16x8 vh = *(const bf16x8 *)&Vdh[n * VSTR + 16 * sv + 8 * hh];
+          const bf16x8 vl = *(const bf16x8 *)&Vdl[n * VSTR + 16 * sv + 8 * hh];
           dp = mma32(vh, dh_, dp);
           dp = mma32(vh, dl_, dp);
           dp = mma32(vl, dh_, dp);
         }
       } else {
-        // exact per-pair decays (rare: block gate range beyond 2^BGUARD)
+        float t[16];
+        direct_dp<DV, F32IN, true>(a, st, c, hq, L, r0, kb, hh, n, t);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int kj = kb + acc_row(hh, j);
-          float t = 0.f;
-          if (rv && kj <= row) {
-#pragma unroll 1
-            for (int d = 0; d < DV; ++d) t += drow[d] * sgn * fast_exp2(gl(row, d) - gl(kj, d)) * vv(kj, d);
-          }
-          dp[j] = t;
-        }
+        for (int j = 0; j < 16; ++j) dp[j] = t[j];
       }
     }
     f16x8 dsf[2];
@@ -159,22 +201,13 @@ __global__ void __launch_bounds__(256) k_bwd_intra_dq(BwdArgs a) {
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int i = 0; i < 8; ++i) dsf[u][i] = (_Float16)(p[8 * u + i] * dp[8 * u + i]);
-    // dQ[row][dk] += dS[row][key] K[key][dk]
 #pragma unroll
-    for (int bk = 0; bk < NBK; ++bk) {
-      const int col = 32 * bk + n;
+    for (int bk = 0; bk < NBK; ++bk)
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        f16x8 kt;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int kk = kb + slab_key(u, hh, i);
-          kt[i] = (_Float16)((col < DK && kk < L) ? load_in(a.k, ((st + kk) * Hkv + c) * DK + col, F32IN) : 0.f);
-        }
-        acc[bk] = mma32(dsf[u], kt, acc[bk]);
-      }
-    }
+      for (int u = 0; u < 2; ++u)
+        acc[bk] = mma32(dsf[u], *(const f16x8 *)&Kts[(32 * bk + n) * TSTR + 16 * u + 8 * hh], acc[bk]);
   }
+  if (!active) return;
 #pragma unroll
   for (int bk = 0; bk < NBK; ++bk) {
     const int col = 32 * bk + n;
@@ -188,18 +221,32 @@ __global__ void __launch_bounds__(256) k_bwd_intra_dq(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Near contributions to dk, dv: wave w owns keys c0 + 32w .. +31 of one
-// 128-chunk and one kv head, summed over the head group, against the queries
-// of the same chunk and of the next one (the pairs with the largest decay
-// weights).  dP is fp16 except on the diagonal block; P^T dhat for dv is
-// always bf16x3, because dv feeds the gate gradient, whose suffix sums
-// accumulate the rounding of every token.
+// Near contributions to dk, dv: workgroup = one 128-chunk of one kv head;
+// wave w owns keys c0 + 32w .. +31, against the queries of the same chunk
+// and of the next one (the pairs with the largest decay weights), summed over
+// the head group.  For each query block, the query-side operands are staged
+// in LDS once for all waves: Q rows, transposed Q, and dx = exp(Gl_q -
+// Gl_ref) sigma delta with the split at the token before the block (<= 1),
+// as fp16 rows (dP off the diagonal), bf16 hi/lo rows (dP on the diagonal)
+// and bf16 hi/lo transposed (dV, always bf16x3: dv feeds the gate gradient,
+// whose suffix sums accumulate the rounding of every token).
 // ---------------------------------------------------------------------------
 template <int DK, int DV, bool F32IN>
-__global__ void __launch_bounds__(256) k_bwd_intra_dkv(BwdArgs a) {
+__global__ void __launch_bounds__(256, 1) k_bwd_intra_dkv(BwdArgs a) {
   using IF = InFrag<F32IN>;
   using kfrag = typename IF::type;
-  constexpr int NS = DK / 16, NSV = DV / 16, NBK = Pad32<DK>::value / 32, NBV = Pad32<DV>::value / 32;
+  constexpr int NS = DK / 16, NSV = DV / 16, DKP = Pad32<DK>::value, DVP = Pad32<DV>::value;
+  constexpr int NBK = DKP / 32, NBV = DVP / 32;
+  constexpr int QSTR = DK + 8, DSTR = DV + 8, TSTR = 32 + 8;
+  __shared__ __align__(16) uint16_t Qs[32 * QSTR];
+  __shared__ __align__(16) _Float16 Qts[DKP * TSTR];
+  __shared__ __align__(16) _Float16 Dr[32 * DSTR];
+  __shared__ __align__(16) __bf16 Drh[32 * DSTR];
+  __shared__ __align__(16) __bf16 Drl[32 * DSTR];
+  __shared__ __align__(16) __bf16 Dth[DVP * TSTR];
+  __shared__ __align__(16) __bf16 Dtl[DVP * TSTR];
+  __shared__ __align__(16) float Ms[32];
+  __shared__ __align__(16) float Gr[DVP];
   const Plan &pl = a.plan;
   const int gc = blockIdx.x, c = blockIdx.y;
   if (gc >= pl.counts[0]) return;
@@ -210,7 +257,7 @@ __global__ void __launch_bounds__(256) k_bwd_intra_dkv(BwdArgs a) {
   const int64_t st = pl.seq_start[s];
   const int Hq = a.Hq, Hkv = a.Hkv, G = Hq / Hkv;
   const int kb = c0 + 32 * wave;
-  if (kb >= L) return;
+  const bool active = kb < L;
   const int key = kb + n;
   const bool kv = key < L;
   const float sl2 = a.sl2;
@@ -221,8 +268,14 @@ __global__ void __launch_bounds__(256) k_bwd_intra_dkv(BwdArgs a) {
     if (tok >= c0 + CB) gv += a.Gl2[((st + c0 + CB - 1) * Hkv + c) * DV + d];
     return gv;
   };
-  auto vv = [&](int tok, int d) { return load_in(a.v, ((st + tok) * Hkv + c) * DV + d, F32IN); };
 
+  if (DK < DKP)
+    for (int e = tid; e < (DKP - DK) * TSTR; e += 256) Qts[DK * TSTR + e] = (_Float16)0.f;
+  if (DV < DVP)
+    for (int e = tid; e < (DVP - DV) * TSTR; e += 256) {
+      Dth[DV * TSTR + e] = (__bf16)0.f;
+      Dtl[DV * TSTR + e] = (__bf16)0.f;
+    }
   kfrag kf[NS];
 #pragma unroll
   for (int i = 0; i < NS; ++i)
@@ -232,141 +285,158 @@ __global__ void __launch_bounds__(256) k_bwd_intra_dkv(BwdArgs a) {
   for (int b = 0; b < NBK; ++b) accK[b] = zero16();
 #pragma unroll
   for (int b = 0; b < NBV; ++b) accV[b] = zero16();
+  const int nqb = min(8, (L - c0 + 31) / 32);  // query blocks in this chunk and the next
 
   for (int gq = 0; gq < G; ++gq) {
     const int h = c * G + gq;
-    for (int qa = wave; qa < 2 * CB / 32; ++qa) {
+    for (int qa = 0; qa < nqb; ++qa) {
       const int q0 = c0 + 32 * qa;
-      if (q0 >= L) break;
-      const bool diag = qa == wave;
       const int ref = q0 - 1;  // token the decay is split at
-      const int qrow = q0 + n;
-      const bool qv = qrow < L;
-      // S[q][key]
+      // ---- stage query block qa ----
+      __syncthreads();
+      for (int p = tid; p < 32 * DK / 8; p += 256) {
+        const int r = p / (DK / 8), e8 = p % (DK / 8);
+        *(uint4 *)&Qs[r * QSTR + 8 * e8] =
+            q0 + r < L ? __builtin_bit_cast(uint4, IF::load(a.q, ((st + q0 + r) * Hq + h) * DK + 8 * e8))
+                       : make_uint4(0, 0, 0, 0);
+      }
+      const _Float16 *qtile = a.Qt + ((int64_t)(gc + (qa >> 2)) * Hq + h) * DK * CB + 32 * (qa & 3);
+      for (int p = tid; p < DK * 4; p += 256)
+        *(uint4 *)&Qts[(p >> 2) * TSTR + 8 * (p & 3)] = *(const uint4 *)(qtile + (p >> 2) * CB + 8 * (p & 3));
+      if (tid < 32) Ms[tid] = q0 + tid < L ? a.mb[(st + q0 + tid) * Hq + h] : INFINITY;
+      for (int d = tid; d < DV; d += 256) Gr[d] = glx(ref, d);
+      for (int e = tid; e < 32 * DV; e += 256) {
+        const int r = e / DV, d = e % DV, tok = q0 + r;
+        float dx = 0.f;
+        if (tok < L)
+          dx = fast_exp2(glx(tok, d) - glx(ref, d)) * a.delta[((st + tok) * Hq + h) * DV + d] *
+               a.sig[(st + tok) * Hq + h];
+        Dr[r * DSTR + d] = (_Float16)dx;
+        const __bf16 hi = (__bf16)dx, lo = (__bf16)(dx - (float)hi);
+        Drh[r * DSTR + d] = hi;
+        Drl[r * DSTR + d] = lo;
+        Dth[d * TSTR + key_pos(r)] = hi;
+        Dtl[d * TSTR + key_pos(r)] = lo;
+      }
+      __syncthreads();
+      if (!active || wave > qa) continue;
+      const bool diag = qa == wave;
+      // S[q][key]: lane = key, register j = query acc_row(hh, j)
       f32x16 sc = zero16();
 #pragma unroll
-      for (int i = 0; i < NS; ++i) {
-        kfrag qf = qv ? IF::load(a.q, ((st + qrow) * Hq + h) * DK + 16 * i + 8 * hh) : IF::zero();
-        sc = mma32(qf, kf[i], sc);
-      }
+      for (int i = 0; i < NS; ++i) sc = mma32(*(const kfrag *)&Qs[n * QSTR + 16 * i + 8 * hh], kf[i], sc);
       float p[16];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int qj = q0 + acc_row(hh, j);
-        const float mbq = qj < L ? a.mb[(st + qj) * Hq + h] : INFINITY;
-        p[j] = fast_exp2(sc[j] * sl2 - mbq);
-        if (diag && acc_row(hh, j) < n) p[j] = 0.f;
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 mq = *(const float4 *)&Ms[8 * q4 + 4 * hh];
+        const float mv[4] = {mq.x, mq.y, mq.z, mq.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = 4 * q4 + e;
+          p[j] = fast_exp2(sc[j] * sl2 - mv[e]);
+          if (diag && acc_row(hh, j) < n) p[j] = 0.f;
+        }
       }
-      const float *dq_row = a.delta + ((st + qrow) * Hq + h) * DV;
-      const float sgq = qv ? a.sig[(st + qrow) * Hq + h] : 0.f;
       // dP[q][key] = sum_d dx[q][d] Vx[key][d]
       f32x16 dp = zero16();
       bool direct = false;
       if (!diag) {
 #pragma unroll
         for (int sv = 0; sv < NSV; ++sv) {
-          f16x8 da, vb;
+          f16x8 vb;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int d = 16 * sv + 8 * hh + e;
-            const float gr = glx(ref, d);
-            da[e] = (_Float16)(qv ? fast_exp2(glx(qrow, d) - gr) * dq_row[d] * sgq : 0.f);
-            vb[e] = (_Float16)(fast_exp2(gr - glx(key, d)) * vv(key, d));
+            vb[e] = (_Float16)(kv ? fast_exp2(Gr[d] - glx(key, d)) * load_in(a.v, ((st + key) * Hkv + c) * DV + d, F32IN) : 0.f);
           }
-          dp = mma32(da, vb, dp);
+          dp = mma32(*(const f16x8 *)&Dr[n * DSTR + 16 * sv + 8 * hh], vb, dp);
         }
       } else {
-        const int klast = min(kb + 31, L - 1);
         float rng = 0.f;
+        const int klast = min(kb + 31, L - 1);
 #pragma unroll
         for (int sv = 0; sv < NSV; ++sv)
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int d = 16 * sv + 8 * hh + e;
-            rng = fmaxf(rng, glx(ref, d) - glx(klast, d));
+            rng = fmaxf(rng, Gr[d] - glx(klast, d));
           }
         direct = __any(rng > BGUARD);
         if (!direct) {
 #pragma unroll
           for (int sv = 0; sv < NSV; ++sv) {
-            bf16x8 dh_, dl_, vh, vl;
+            bf16x8 vh, vl;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
               const int d = 16 * sv + 8 * hh + e;
-              const float gr = glx(ref, d);
-              const float dx = qv ? fast_exp2(glx(qrow, d) - gr) * dq_row[d] * sgq : 0.f;
-              const float vx = kv ? fast_exp2(gr - glx(key, d)) * vv(key, d) : 0.f;
-              split_bf16(dx, dh_, dl_, e);
-              split_bf16(vx, vh, vl, e);
+              split_bf16(kv ? fast_exp2(Gr[d] - glx(key, d)) * load_in(a.v, ((st + key) * Hkv + c) * DV + d, F32IN) : 0.f,
+                         vh, vl, e);
             }
+            const bf16x8 dh_ = *(const bf16x8 *)&Drh[n * DSTR + 16 * sv + 8 * hh];
+            const bf16x8 dl_ = *(const bf16x8 *)&Drl[n * DSTR + 16 * sv + 8 * hh];
             dp = mma32(dh_, vh, dp);
             dp = mma32(dl_, vh, dp);
             dp = mma32(dh_, vl, dp);
           }
         } else {
+          float t[16];
+          direct_dp<DV, F32IN, false>(a, st, c, h, L, q0, kb, hh, n, t);
 #pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int qj = q0 + acc_row(hh, j);
-            float t = 0.f;
-            if (kv && qj < L && qj >= key) {
-              const float *dr = a.delta + ((st + qj) * Hq + h) * DV;
-              const float sgj = a.sig[(st + qj) * Hq + h];
-#pragma unroll 1
-              for (int d = 0; d < DV; ++d) t += dr[d] * sgj * fast_exp2(glx(qj, d) - glx(key, d)) * vv(key, d);
-            }
-            dp[j] = t;
-          }
+          for (int j = 0; j < 16; ++j) dp[j] = t[j];
         }
       }
       f16x8 dsf[2];
+      bf16x8 ph[2], plo[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) dsf[u][i] = (_Float16)(p[8 * u + i] * dp[8 * u + i]);
-      // dV[key][dv] += F[key][dv] * sum_q P[q][key] dx[q][dv], with F = exp(Gl_ref - Gl_key)
-      // the key side of the split decay (<= 1 off the diagonal block, >= 1 on it)
+        for (int i = 0; i < 8; ++i) {
+          dsf[u][i] = (_Float16)(p[8 * u + i] * dp[8 * u + i]);
+          split_bf16(p[8 * u + i], ph[u], plo[u], i);
+        }
+      // dV[key][dv] += F[key][dv] * sum_q P[q][key] dx[q][dv], F = exp(Gl_ref - Gl_key) the key
+      // side of the split decay (<= 1 off the diagonal block, >= 1 on it)
+      if (!direct) {
 #pragma unroll
-      for (int bv = 0; bv < NBV; ++bv) {
-        const int col = 32 * bv + n;
-        const bool cv = col < DV;
-        const float grc = cv ? glx(ref, col) : 0.f;
-        if (!direct) {
+        for (int bv = 0; bv < NBV; ++bv) {
+          const int col = 32 * bv + n;
           f32x16 tmp = zero16();
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
-            bf16x8 ph, plo, th, tl;
+            const bf16x8 th = *(const bf16x8 *)&Dth[col * TSTR + 16 * u + 8 * hh];
+            const bf16x8 tl = *(const bf16x8 *)&Dtl[col * TSTR + 16 * u + 8 * hh];
+            tmp = mma32(ph[u], th, tmp);
+            tmp = mma32(ph[u], tl, tmp);
+            tmp = mma32(plo[u], th, tmp);
+          }
+          if (col < DV) {
+            const float grc = Gr[col];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              split_bf16(p[8 * u + i], ph, plo, i);
-              const int qk = q0 + slab_key(u, hh, i);
-              float val = 0.f;
-              if (cv && qk < L)
-                val = fast_exp2(glx(qk, col) - grc) * a.delta[((st + qk) * Hq + h) * DV + col] *
-                      a.sig[(st + qk) * Hq + h];
-              split_bf16(val, th, tl, i);
+            for (int j = 0; j < 16; ++j) {
+              const int kj = kb + acc_row(hh, j);
+              const float f = kj < L ? fast_exp2(grc - glx(kj, col)) : 0.f;
+              accV[bv][j] += f * tmp[j];
             }
-            tmp = mma32(ph, th, tmp);
-            tmp = mma32(ph, tl, tmp);
-            tmp = mma32(plo, th, tmp);
           }
+        }
+      } else {
+        // exact per-pair decays: P[q][kj] lives in lane kj, register of q
+#pragma unroll 1
+        for (int qq = 0; qq < 32; ++qq) {
+          const int qk = q0 + qq;
+          const int jsrc = (qq >> 3) * 4 + (qq & 3), hsrc = (qq >> 2) & 1;
+          float pj = 0.f;
 #pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int kj = kb + acc_row(hh, j);
-            const float f = (cv && kj < L) ? fast_exp2(grc - glx(kj, col)) : 0.f;
-            accV[bv][j] += f * tmp[j];
-          }
-        } else {
-          // exact per-pair decays: P[q][kj] lives in lane kj, register of q
+          for (int j = 0; j < 16; ++j) pj = (j == jsrc) ? p[j] : pj;
 #pragma unroll
-          for (int qq = 0; qq < 32; ++qq) {
-            const int jsrc = (qq >> 3) * 4 + (qq & 3), hsrc = (qq >> 2) & 1;
-            const int qk = q0 + qq;
+          for (int bv = 0; bv < NBV; ++bv) {
+            const int col = 32 * bv + n;
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
               const int kl = acc_row(hh, j);
-              const float pv = __shfl(p[jsrc], kl + 32 * hsrc);
+              const float pv = __shfl(pj, kl + 32 * hsrc);
               const int kj = kb + kl;
-              if (cv && qk < L && kj <= qk)
+              if (col < DV && qk < L && kj <= qk)
                 accV[bv][j] += pv * fast_exp2(glx(qk, col) - glx(kj, col)) *
                                a.delta[((st + qk) * Hq + h) * DV + col] * a.sig[(st + qk) * Hq + h];
             }
@@ -375,21 +445,13 @@ __global__ void __launch_bounds__(256) k_bwd_intra_dkv(BwdArgs a) {
       }
       // dK[key][dk] += dS[q][key] Q[q][dk]
 #pragma unroll
-      for (int bk = 0; bk < NBK; ++bk) {
-        const int col = 32 * bk + n;
+      for (int bk = 0; bk < NBK; ++bk)
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          f16x8 qt;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int qk = q0 + slab_key(u, hh, i);
-            qt[i] = (_Float16)((col < DK && qk < L) ? load_in(a.q, ((st + qk) * Hq + h) * DK + col, F32IN) : 0.f);
-          }
-          accK[bk] = mma32(dsf[u], qt, accK[bk]);
-        }
-      }
+        for (int u = 0; u < 2; ++u)
+          accK[bk] = mma32(dsf[u], *(const f16x8 *)&Qts[(32 * bk + n) * TSTR + 16 * u + 8 * hh], accK[bk]);
     }
   }
+  if (!active) return;
 #pragma unroll
   for (int bk = 0; bk < NBK; ++bk) {
     const int col = 32 * bk + n;
@@ -414,21 +476,25 @@ __global__ void __launch_bounds__(256) k_bwd_intra_dkv(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // dq from key chunks before the query chunk.  Workgroup = 128 query rows of
-// one q head (4 waves x 32 rows); steps of 32 keys staged through LDS
-// (double buffered): K rows (bf16) for S^T, transposed K (fp16) for dS.K,
-// and V scaled to the query chunk start (fp16) for dP^T.
+// one q head (4 waves x 32 rows); key chunks are visited from the last to the
+// first, 32 keys per step copied straight into LDS (double buffered): K rows
+// (bf16) for S^T, transposed K (fp16) for dS.K, and V scaled to its chunk
+// end (fp16) for dP^T.  The decay product between the chunks, gamma_IJ =
+// exp2(Lam[I-1] - Lam[J]), multiplies the query-side operand (the scaled
+// dhat rows), rebuilt once per key chunk.
 // ---------------------------------------------------------------------------
 template <int DK, int DV, bool F32IN>
 __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdArgs a) {
   using IF = InFrag<F32IN>;
   using kfrag = typename IF::type;
   constexpr int NS = DK / 16, NSV = DV / 16, DKP = Pad32<DK>::value, NBK = DKP / 32;
-  constexpr int KSTR = DK + 8, TSTR = 32 + 8, VSTR = DV + 8;
-  constexpr int KP = 32 * DK / 8, TP = DK * 32 / 8, VP = 32 * DV / 8;  // 16-byte pieces per step
-  constexpr int KPT = (KP + 255) / 256, TPT = (TP + 255) / 256, VPT = (VP + 255) / 256;
-  __shared__ __align__(16) uint16_t Ks[2][32 * KSTR];
-  __shared__ __align__(16) _Float16 Kts[2][DKP * TSTR];
-  __shared__ __align__(16) _Float16 Vs[2][32 * VSTR];
+  using KT = LdsTile<32, DK * 2>;   // K rows of the step
+  using TT = LdsTile<DKP, 64>;     // transposed K (dk rows x 32 keys), rows padded to DKP
+  using TTD = LdsTile<DK, 64>;
+  using VT = LdsTile<32, DV * 2>;  // V rows of the step (scaled to their chunk end)
+  __shared__ __align__(1024) char Ks[2][KT::BYTES];
+  __shared__ __align__(1024) char Kts[2][TT::BYTES];
+  __shared__ __align__(1024) char Vs[2][VT::BYTES];
 
   const Plan &pl = a.plan;
   const int Hq = a.Hq, Hkv = a.Hkv, G = Hq / Hkv;
@@ -455,101 +521,63 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdArgs a) {
   for (int i = 0; i < NS; ++i)
     qf[i] = rv ? IF::load(a.q, ((st + row) * Hq + hq) * DK + 16 * i + 8 * hh) : IF::zero();
   const float mbn = rv ? a.mb[(st + row) * Hq + hq] : INFINITY;
+  // Rows past the end of the sequence read the last row; their mbn = +inf
+  // zeroes their probabilities.
+  const _Float16 *dhrow = a.dh + ((st + min(row, L - 1)) * Hq + hq) * DV;
   f16x8 dhf[NSV];
-#pragma unroll
-  for (int i = 0; i < NSV; ++i)
-    dhf[i] = rv ? *(const f16x8 *)(a.dh + ((st + row) * Hq + hq) * DV + 16 * i + 8 * hh)
-                : __builtin_bit_cast(f16x8, make_uint4(0, 0, 0, 0));
-  if (DK < DKP) {
-    for (int e = tid; e < (DKP - DK) * TSTR; e += 256) {
-      Kts[0][DK * TSTR + e] = (_Float16)0.f;
-      Kts[1][DK * TSTR + e] = (_Float16)0.f;
+  if (DK < DKP)
+    for (int e = tid; e < (DKP - DK) * 64 / 4; e += 256) {
+      ((uint32_t *)(Kts[0] + DK * 64))[e] = 0u;
+      ((uint32_t *)(Kts[1] + DK * 64))[e] = 0u;
     }
-  }
   f32x16 acc[NBK];
 #pragma unroll
   for (int b = 0; b < NBK; ++b) acc[b] = zero16();
 
-  // staging state: this thread's V pieces always cover channels 8*d8 .. +7
-  const int d8 = tid % (DV / 8);
-  float gam[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) gam[e] = 1.f;
-  uint4 kreg[KPT], treg[TPT], vreg[VPT];
   const int nsteps = 4 * I;
-  auto load_tile = [&](int k) {
+  auto stage_tile = [&](int k, int b) {
     const int J = I - 1 - (k >> 2), u = k & 3;
-    if (k > 0 && (k & 3) == 0) {  // entered chunk J: gamma_IJ = gamma_I,J+1 * Gam_J+1
-      const float *gp = a.Gam + ((int64_t)(cbs + J + 1) * Hkv + c) * DV + 8 * d8;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) gam[e] *= gp[e];
-    }
     const int kt0 = J * CB + 32 * u;
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int p = tid + 256 * i;
-      if (p < KP) {
-        const int kr = p / (DK / 8), e8 = p % (DK / 8);
-        kreg[i] = __builtin_bit_cast(uint4, IF::load(a.k, ((st + kt0 + kr) * Hkv + c) * DK + 8 * e8));
+    if constexpr (!F32IN) {
+      KT::dma(Ks[b], [&](int r) { return (const uint16_t *)a.k + ((st + kt0 + r) * Hkv + c) * DK; }, wave, lane);
+    } else {
+      for (int p = tid; p < KT::NCH; p += 256) {
+        const int r = p / KT::CPR, cc = p % KT::CPR;
+        *(f16x8 *)(Ks[b] + KT::off(r, cc)) = IF::load(a.k, ((st + kt0 + r) * Hkv + c) * DK + 8 * cc);
       }
     }
     const _Float16 *ktile = a.Kt + ((int64_t)(cbs + J) * Hkv + c) * DK * CB + 32 * u;
-#pragma unroll
-    for (int i = 0; i < TPT; ++i) {
-      const int p = tid + 256 * i;
-      if (p < TP) {
-        const int dr = p >> 2, q8 = p & 3;
-        treg[i] = *(const uint4 *)(ktile + dr * CB + 8 * q8);
-      }
-    }
+    TTD::dma(Kts[b], [&](int r) { return ktile + r * CB; }, wave, lane);
     const _Float16 *vtile = a.Vr + ((int64_t)(cbs + J) * Hkv + c) * CB * DV + (32 * u) * DV;
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int p = tid + 256 * i;
-      if (p < VP) {
-        const int vr = p / (DV / 8);
-        f16x8 x = *(const f16x8 *)(vtile + vr * DV + 8 * d8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = (_Float16)((float)x[e] * gam[e]);
-        vreg[i] = __builtin_bit_cast(uint4, x);
-      }
-    }
-  };
-  auto store_tile = [&](int b) {
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int p = tid + 256 * i;
-      if (p < KP) {
-        const int kr = p / (DK / 8), e8 = p % (DK / 8);
-        *(uint4 *)&Ks[b][kr * KSTR + 8 * e8] = kreg[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < TPT; ++i) {
-      const int p = tid + 256 * i;
-      if (p < TP) *(uint4 *)&Kts[b][(p >> 2) * TSTR + 8 * (p & 3)] = treg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int p = tid + 256 * i;
-      if (p < VP) *(uint4 *)&Vs[b][(p / (DV / 8)) * VSTR + 8 * d8] = vreg[i];
-    }
+    VT::dma(Vs[b], [&](int r) { return vtile + r * DV; }, wave, lane);
   };
 
-  if (nsteps > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
+  if (nsteps > 0) stage_tile(0, 0);
+  wait_all();
   __syncthreads();
   for (int k = 0; k < nsteps; ++k) {
     const int b = k & 1;
-    if (k + 1 < nsteps) load_tile(k + 1);
+    if (k + 1 < nsteps) stage_tile(k + 1, b ^ 1);
+    if ((k & 3) == 0) {  // entered key chunk J: dhat operand times gamma_IJ
+      const int J = I - 1 - (k >> 2);
+      const double *l1 = a.Lam + ((int64_t)(cbs + I - 1) * Hkv + c) * DV;
+      const double *l0 = a.Lam + ((int64_t)(cbs + J) * Hkv + c) * DV;
+#pragma unroll
+      for (int i = 0; i < NSV; ++i) {
+        const f16x8 raw = *(const f16x8 *)(dhrow + 16 * i + 8 * hh);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int d = 16 * i + 8 * hh + e;
+          dhf[i][e] = (_Float16)((float)raw[e] * fast_exp2((float)(l1[d] - l0[d])));
+        }
+      }
+    }
     {
       f32x16 sc = zero16(), dp = zero16();
 #pragma unroll
-      for (int i = 0; i < NS; ++i) sc = mma32(*(const kfrag *)&Ks[b][n * KSTR + 16 * i + 8 * hh], qf[i], sc);
+      for (int i = 0; i < NS; ++i) sc = mma32(*(const kfrag *)(Ks[b] + KT::off(n, 2 * i + hh)), qf[i], sc);
 #pragma unroll
-      for (int i = 0; i < NSV; ++i) dp = mma32(*(const f16x8 *)&Vs[b][n * VSTR + 16 * i + 8 * hh], dhf[i], dp);
+      for (int i = 0; i < NSV; ++i) dp = mma32(*(const f16x8 *)(Vs[b] + VT::off(n, 2 * i + hh)), dhf[i], dp);
       f16x8 dsf[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u)
@@ -562,9 +590,9 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdArgs a) {
       for (int bk = 0; bk < NBK; ++bk)
 #pragma unroll
         for (int u = 0; u < 2; ++u)
-          acc[bk] = mma32(dsf[u], *(const f16x8 *)&Kts[b][(32 * bk + n) * TSTR + 16 * u + 8 * hh], acc[bk]);
+          acc[bk] = mma32(dsf[u], *(const f16x8 *)(Kts[b] + TT::off(32 * bk + n, 2 * u + hh)), acc[bk]);
     }
-    if (k + 1 < nsteps) store_tile(b ^ 1);
+    wait_all();
     __syncthreads();
   }
 #pragma unroll
@@ -583,25 +611,33 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dk, dv from query chunks after the key chunk.  Workgroup = 128 keys of one
-// kv head (4 waves x 32 keys); steps of 32 queries of one head of the group
-// staged through LDS (double buffered): Q rows (bf16) for S, transposed Q
-// (fp16) for dK, the scaled dhat (fp16, times gamma) as rows for dP and
-// transposed for dV, and the per-row exponent offsets.
+// dk, dv from query chunks two or more after the key chunk.  Workgroup = 128
+// keys of one kv head (4 waves x 32 keys).  Query chunks are visited from the
+// last to the first (and within a chunk every head of the group), 32 queries
+// per step staged through LDS (double buffered): Q rows (bf16) for S,
+// transposed Q (fp16) for dK, the scaled dhat (relative to its chunk start)
+// as rows for dP and transposed for dV, and the per-row exponent offsets.
+// With the chunks visited backwards, the decay products between the chunks
+// enter dV as a Horner recurrence, dV <- dV (.) Gam_I + P^T dhat_I, and enter
+// dP through the key-side operand V (.) gamma_IJ, rebuilt once per chunk with
+// gamma_IJ = exp2(Lam[I-1] - Lam[J]).  The staged tiles are plain copies.
 // ---------------------------------------------------------------------------
 template <int DK, int DV, bool F32IN>
-__global__ void __launch_bounds__(256, 2) k_bwd_dkv(BwdArgs a) {
+__global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
   using IF = InFrag<F32IN>;
   using kfrag = typename IF::type;
   constexpr int NS = DK / 16, NSV = DV / 16, DKP = Pad32<DK>::value, DVP = Pad32<DV>::value;
   constexpr int NBK = DKP / 32, NBV = DVP / 32;
-  constexpr int QSTR = DK + 8, TSTR = 32 + 8, DSTR = DV + 8;
-  constexpr int QP = 32 * DK / 8, QTP = DK * 4, DP_ = 32 * DV / 8, DTP = DV * 4;
-  constexpr int QPT = (QP + 255) / 256, QTPT = (QTP + 255) / 256, DPT = (DP_ + 255) / 256, DTPT = (DTP + 255) / 256;
-  __shared__ __align__(16) uint16_t Qs[2][32 * QSTR];
-  __shared__ __align__(16) _Float16 Qts[2][DKP * TSTR];
-  __shared__ __align__(16) _Float16 Ds[2][32 * DSTR];
-  __shared__ __align__(16) _Float16 Dts[2][DVP * TSTR];
+  using QT = LdsTile<32, DK * 2>;   // Q rows of the step
+  using QTT = LdsTile<DKP, 64>;     // transposed Q (dk rows x 32 queries)
+  using QTTD = LdsTile<DK, 64>;
+  using DR = LdsTile<32, DV * 2>;   // scaled dhat rows
+  using DTT = LdsTile<DVP, 64>;     // scaled dhat, transposed
+  using DTTD = LdsTile<DV, 64>;
+  __shared__ __align__(1024) char Qs[2][QT::BYTES];
+  __shared__ __align__(1024) char Qts[2][QTT::BYTES];
+  __shared__ __align__(1024) char Ds[2][DR::BYTES];
+  __shared__ __align__(1024) char Dts[2][DTT::BYTES];
   __shared__ __align__(16) float Ms[2][32];
 
   const Plan &pl = a.plan;
@@ -624,138 +660,103 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dkv(BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < NS; ++i)
     kf[i] = kv ? IF::load(a.k, ((st + key) * Hkv + c) * DK + 16 * i + 8 * hh) : IF::zero();
-  f16x8 vf[NSV];
   const _Float16 *vrow = a.Vr + (((int64_t)(cbs + J) * Hkv + c) * CB + 32 * wave + n) * DV;
-#pragma unroll
-  for (int i = 0; i < NSV; ++i) vf[i] = *(const f16x8 *)(vrow + 16 * i + 8 * hh);
-  if (DK < DKP || DV < DVP) {
-    for (int e = tid; e < (DKP - DK) * TSTR; e += 256) {
-      Qts[0][DK * TSTR + e] = (_Float16)0.f;
-      Qts[1][DK * TSTR + e] = (_Float16)0.f;
+  if (DK < DKP)
+    for (int e = tid; e < (DKP - DK) * 64 / 4; e += 256) {
+      ((uint32_t *)(Qts[0] + DK * 64))[e] = 0u;
+      ((uint32_t *)(Qts[1] + DK * 64))[e] = 0u;
     }
-    for (int e = tid; e < (DVP - DV) * TSTR; e += 256) {
-      Dts[0][DV * TSTR + e] = (_Float16)0.f;
-      Dts[1][DV * TSTR + e] = (_Float16)0.f;
+  if (DV < DVP)
+    for (int e = tid; e < (DVP - DV) * 64 / 4; e += 256) {
+      ((uint32_t *)(Dts[0] + DV * 64))[e] = 0u;
+      ((uint32_t *)(Dts[1] + DV * 64))[e] = 0u;
     }
-  }
   f32x16 accK[NBK], accV[NBV];
 #pragma unroll
   for (int b = 0; b < NBK; ++b) accK[b] = zero16();
 #pragma unroll
   for (int b = 0; b < NBV; ++b) accV[b] = zero16();
 
-  const int after = L - (J + 2) * CB;                // queries two chunks or more after the key chunk
-  const int nsph = after > 0 ? (after + 31) / 32 : 0;  // 32-query steps per head
-  const int nsteps = G * nsph;
-  // staging state: row pieces cover channels 8*d8 .. +7; transposed pieces
-  // cover channel rows (tid >> 2) + 64 i
-  const int d8 = tid % (DV / 8);
-  float gr[8], gt[DTPT];
-  uint4 qreg[QPT], qtreg[QTPT], dreg[DPT], dtreg[DTPT];
-  float mreg = INFINITY;
-  auto load_tile = [&](int k) {
-    const int gq = k / nsph, kk = k % nsph;
-    const int h = c * G + gq;
-    const int I = J + 2 + (kk >> 2), u = kk & 3;
-    if (kk == 0 || (kk & 3) == 0) {  // entered chunk I: gamma_IJ = gamma_I-1,J * Gam_I-1 (gamma_J+1,J = 1)
-      if (kk == 0) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) gr[e] = 1.f;
-#pragma unroll
-        for (int i = 0; i < DTPT; ++i) gt[i] = 1.f;
-      }
-      const float *gp = a.Gam + ((int64_t)(cbs + I - 1) * Hkv + c) * DV;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) gr[e] *= gp[8 * d8 + e];
-#pragma unroll
-      for (int i = 0; i < DTPT; ++i) {
-        const int dr = (tid >> 2) + 64 * i;
-        if (dr < DV) gt[i] *= gp[dr];
-      }
+  const int nch = (L + CB - 1) / CB;
+  const int I0 = J + 2, I1 = nch - 1;                  // query chunks visited: I1 down to I0
+  const int ns1 = (L - I1 * CB + 31) / 32;              // steps of the last (possibly partial) chunk
+  const int nsteps = I0 <= I1 ? G * ns1 + 4 * G * (I1 - I0) : 0;
+  auto step_of = [&](int k, int &I, int &gq, int &u) {
+    if (k < G * ns1) {
+      I = I1; gq = k / ns1; u = k % ns1;
+    } else {
+      const int r = k - G * ns1;
+      I = I1 - 1 - r / (4 * G); gq = (r % (4 * G)) >> 2; u = r & 3;
     }
+  };
+  // Rows past the end of the sequence are copied from its last row (finite
+  // values); their probabilities are masked to zero when the step is computed.
+  auto stage_tile = [&](int k, int b) {
+    int I, gq, u;
+    step_of(k, I, gq, u);
+    const int h = c * G + gq;
     const int qt0 = I * CB + 32 * u;
-#pragma unroll
-    for (int i = 0; i < QPT; ++i) {
-      const int p = tid + 256 * i;
-      if (p < QP) {
-        const int qr = p / (DK / 8), e8 = p % (DK / 8);
-        qreg[i] = (qt0 + qr < L)
-                      ? __builtin_bit_cast(uint4, IF::load(a.q, ((st + qt0 + qr) * Hq + h) * DK + 8 * e8))
-                      : make_uint4(0, 0, 0, 0);
+    auto qrow = [&](int r) { return st + min(qt0 + r, L - 1); };
+    if constexpr (!F32IN) {
+      QT::dma(Qs[b], [&](int r) { return (const uint16_t *)a.q + (qrow(r) * Hq + h) * DK; }, wave, lane);
+    } else {
+      for (int p = tid; p < QT::NCH; p += 256) {
+        const int r = p / QT::CPR, cc = p % QT::CPR;
+        *(f16x8 *)(Qs[b] + QT::off(r, cc)) = IF::load(a.q, (qrow(r) * Hq + h) * DK + 8 * cc);
       }
     }
     const _Float16 *qtile = a.Qt + ((int64_t)(cbs + I) * Hq + h) * DK * CB + 32 * u;
-#pragma unroll
-    for (int i = 0; i < QTPT; ++i) {
-      const int p = tid + 256 * i;
-      if (p < QTP) qtreg[i] = *(const uint4 *)(qtile + (p >> 2) * CB + 8 * (p & 3));
-    }
-#pragma unroll
-    for (int i = 0; i < DPT; ++i) {
-      const int p = tid + 256 * i;
-      if (p < DP_) {
-        const int qr = p / (DV / 8);
-        f16x8 x = __builtin_bit_cast(f16x8, make_uint4(0, 0, 0, 0));
-        if (qt0 + qr < L) {
-          x = *(const f16x8 *)(a.dh + ((st + qt0 + qr) * Hq + h) * DV + 8 * d8);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = (_Float16)((float)x[e] * gr[e]);
-        }
-        dreg[i] = __builtin_bit_cast(uint4, x);
-      }
-    }
+    QTTD::dma(Qts[b], [&](int r) { return qtile + r * CB; }, wave, lane);
+    DR::dma(Ds[b], [&](int r) { return a.dh + (qrow(r) * Hq + h) * DV; }, wave, lane);
     const _Float16 *dtile = a.dht + ((int64_t)(cbs + I) * Hq + h) * DV * CB + 32 * u;
-#pragma unroll
-    for (int i = 0; i < DTPT; ++i) {
-      const int p = tid + 256 * i;
-      if (p < DTP) {
-        f16x8 x = *(const f16x8 *)(dtile + (p >> 2) * CB + 8 * (p & 3));
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = (_Float16)((float)x[e] * gt[i]);
-        dtreg[i] = __builtin_bit_cast(uint4, x);
-      }
-    }
-    if (tid < 32) mreg = (qt0 + tid < L) ? a.mb[(st + qt0 + tid) * Hq + h] : INFINITY;
-  };
-  auto store_tile = [&](int b) {
-#pragma unroll
-    for (int i = 0; i < QPT; ++i) {
-      const int p = tid + 256 * i;
-      if (p < QP) *(uint4 *)&Qs[b][(p / (DK / 8)) * QSTR + 8 * (p % (DK / 8))] = qreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < QTPT; ++i) {
-      const int p = tid + 256 * i;
-      if (p < QTP) *(uint4 *)&Qts[b][(p >> 2) * TSTR + 8 * (p & 3)] = qtreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < DPT; ++i) {
-      const int p = tid + 256 * i;
-      if (p < DP_) *(uint4 *)&Ds[b][(p / (DV / 8)) * DSTR + 8 * d8] = dreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < DTPT; ++i) {
-      const int p = tid + 256 * i;
-      if (p < DTP) *(uint4 *)&Dts[b][(p >> 2) * TSTR + 8 * (p & 3)] = dtreg[i];
-    }
-    if (tid < 32) Ms[b][tid] = mreg;
+    DTTD::dma(Dts[b], [&](int r) { return dtile + r * CB; }, wave, lane);
+    if (tid < 32)  // one dword per lane: lane r fills Ms[b][r]
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1))) *)(a.mb + (qrow(tid) * Hq + h)),
+          (void __attribute__((address_space(3))) *)Ms[b], 4, 0, 0);
   };
 
-  if (nsteps > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
+  f16x8 vf[NSV];  // key-side dP operand V (.) gamma_IJ, rebuilt per query chunk
+  int curI = -1;
+  if (nsteps > 0) stage_tile(0, 0);
+  wait_all();
   __syncthreads();
   for (int k = 0; k < nsteps; ++k) {
     const int b = k & 1;
-    if (k + 1 < nsteps) load_tile(k + 1);
+    if (k + 1 < nsteps) stage_tile(k + 1, b ^ 1);
     {
+      int I, gq, u;
+      step_of(k, I, gq, u);
+      const int qt0 = I * CB + 32 * u;
+      if (I != curI) {
+        if (curI >= 0) {  // left chunk I + 1: dV <- dV (.) Gam_I before adding chunk I
+#pragma unroll
+          for (int bv = 0; bv < NBV; ++bv) {
+            const int col = 32 * bv + n;
+            const float gm = col < DV ? a.Gam[((int64_t)(cbs + I) * Hkv + c) * DV + col] : 1.f;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) accV[bv][j] *= gm;
+          }
+        }
+        curI = I;
+        const double *l1 = a.Lam + ((int64_t)(cbs + I - 1) * Hkv + c) * DV;
+        const double *l0 = a.Lam + ((int64_t)(cbs + J) * Hkv + c) * DV;
+#pragma unroll
+        for (int i = 0; i < NSV; ++i) {
+          const f16x8 raw = *(const f16x8 *)(vrow + 16 * i + 8 * hh);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int d = 16 * i + 8 * hh + e;
+            vf[i][e] = (_Float16)((float)raw[e] * fast_exp2((float)(l1[d] - l0[d])));
+          }
+        }
+      }
       // S[q][key] and dP[q][key]: lane = key, register j = query acc_row(hh, j)
       f32x16 sc = zero16(), dp = zero16();
 #pragma unroll
-      for (int i = 0; i < NS; ++i) sc = mma32(*(const kfrag *)&Qs[b][n * QSTR + 16 * i + 8 * hh], kf[i], sc);
+      for (int i = 0; i < NS; ++i) sc = mma32(*(const kfrag *)(Qs[b] + QT::off(n, 2 * i + hh)), kf[i], sc);
 #pragma unroll
-      for (int i = 0; i < NSV; ++i) dp = mma32(*(const f16x8 *)&Ds[b][n * DSTR + 16 * i + 8 * hh], vf[i], dp);
+      for (int i = 0; i < NSV; ++i) dp = mma32(*(const f16x8 *)(Ds[b] + DR::off(n, 2 * i + hh)), vf[i], dp);
       f16x8 pf[2], dsf[2];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
@@ -764,7 +765,7 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dkv(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int j = 4 * q4 + e;
-          const float pv = fast_exp2(sc[j] * sl2 - mv[e]);
+          const float pv = qt0 + acc_row(hh, j) < L ? fast_exp2(sc[j] * sl2 - mv[e]) : 0.f;
           pf[j >> 3][j & 7] = (_Float16)pv;
           dsf[j >> 3][j & 7] = (_Float16)(pv * dp[j]);
         }
@@ -772,18 +773,28 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dkv(BwdArgs a) {
 #pragma unroll
       for (int bv = 0; bv < NBV; ++bv)
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-          accV[bv] = mma32(pf[u], *(const f16x8 *)&Dts[b][(32 * bv + n) * TSTR + 16 * u + 8 * hh], accV[bv]);
+        for (int uu = 0; uu < 2; ++uu)
+          accV[bv] = mma32(pf[uu], *(const f16x8 *)(Dts[b] + DTT::off(32 * bv + n, 2 * uu + hh)), accV[bv]);
 #pragma unroll
       for (int bk = 0; bk < NBK; ++bk)
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-          accK[bk] = mma32(dsf[u], *(const f16x8 *)&Qts[b][(32 * bk + n) * TSTR + 16 * u + 8 * hh], accK[bk]);
+        for (int uu = 0; uu < 2; ++uu)
+          accK[bk] = mma32(dsf[uu], *(const f16x8 *)(Qts[b] + QTT::off(32 * bk + n, 2 * uu + hh)), accK[bk]);
     }
-    if (k + 1 < nsteps) store_tile(b ^ 1);
+    wait_all();
     __syncthreads();
   }
   if (kb >= L) return;
+  // dV so far is relative to the start of chunk J + 2; the chunk J + 1 between adds Gam_J+1
+  if (nsteps > 0) {
+#pragma unroll
+    for (int bv = 0; bv < NBV; ++bv) {
+      const int col = 32 * bv + n;
+      const float gm = col < DV ? a.Gam[((int64_t)(cbs + J + 1) * Hkv + c) * DV + col] : 1.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) accV[bv][j] *= gm;
+    }
+  }
   // epilogue: dk, dv (inter part scaled to the key: exp(Gl_end(J) - Gl_key)), dG = qside - v (.) dv
   const int tend = min((J + 1) * CB, L) - 1;
 #pragma unroll

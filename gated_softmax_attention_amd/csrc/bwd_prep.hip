@@ -53,6 +53,25 @@ __global__ void __launch_bounds__(128) k_gate_prep_rows(const float *__restrict_
   }
 }
 
+// Lam[chunk][kvh][d] = sum over the sequence's chunks n <= chunk of the chunk
+// total of the log2 gate (fp64, so that differences of far-apart prefixes keep
+// their precision): the decay product of the chunks strictly between J and I
+// is exp2(Lam[I-1] - Lam[J]).
+template <int DV>
+__global__ void __launch_bounds__(128) k_chunk_logprefix(const float *__restrict__ Gl2, Plan plan, int Hkv,
+                                                         double *__restrict__ Lam) {
+  const int s = blockIdx.x, c = blockIdx.y, d = threadIdx.x;
+  if (d >= DV) return;
+  const int L = plan.seq_len[s];
+  const int64_t st = plan.seq_start[s];
+  double run = 0.0;
+  for (int gc = plan.cb128[s]; gc < plan.cb128[s + 1]; ++gc) {
+    const int tend = min((gc - plan.cb128[s] + 1) * CB, L) - 1;
+    run += (double)Gl2[((st + tend) * Hkv + c) * DV + d];
+    Lam[((int64_t)gc * Hkv + c) * DV + d] = run;
+  }
+}
+
 // Transposed fp16 tiles of a [Ttot, H, D] input: out[chunk][h][d][key_pos(t)]
 // for the CB tokens of each 128-chunk (zero past the end of the sequence).
 template <int D>
@@ -268,6 +287,12 @@ hipError_t launch_gate_prep_rows(int dv, const float *g, const void *v, bool in_
   dim3 grid(ncb_ub, Hkv);
   FIX_DV_SWITCH(dv, hipLaunchKernelGGL(k_gate_prep_rows<DVC>, grid, dim3(128), 0, st, g, v, in_f32, plan, Hkv,
                                        Gl2, Gam, Vr));
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_logprefix(int dv, const float *Gl2, const Plan &plan, int Hkv, double *Lam, hipStream_t st) {
+  dim3 grid(plan.nseq, Hkv);
+  FIX_DV_SWITCH(dv, hipLaunchKernelGGL(k_chunk_logprefix<DVC>, grid, dim3(128), 0, st, Gl2, plan, Hkv, Lam));
   return hipGetLastError();
 }
 

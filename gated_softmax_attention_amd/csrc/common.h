@@ -99,6 +99,37 @@ __device__ inline uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// ---- LDS tiles filled by direct global->LDS copies ----
+// gfx950's global_load_lds_dwordx4 moves 16 bytes per lane from global memory
+// straight into LDS, the wave's 64 pieces landing contiguously (1 KB) at the
+// wave-uniform base, piece of lane l at base + 16 l.  Tiles are therefore
+// unpadded, [ROWS][RB bytes], and the 16-byte chunk c of row r is stored at
+// chunk position c ^ swz(r): for the MFMA operand reads (32 lanes reading the
+// same chunk of 32 consecutive rows) every 16 lanes then hit 16 distinct
+// 16-byte bank groups, with no padding.
+template <int ROWS, int RB> struct LdsTile {
+  static constexpr int CPR = RB / 16;     // 16-byte chunks per row (2..16)
+  static constexpr int NCH = ROWS * CPR;  // chunks per tile
+  static constexpr int BYTES = ROWS * RB;
+  static_assert(CPR >= 2 && CPR <= 16 && NCH % 64 == 0, "tile shape");
+  __device__ static int swz(int r) { return (r / (16 / CPR)) % CPR; }
+  __device__ static int off(int r, int c) { return r * RB + ((c ^ swz(r)) << 4); }
+  // Copy the tile: rowptr(r) gives the global address of row r (RB contiguous bytes).
+  template <class RowPtr>
+  __device__ static void dma(char *lds, RowPtr rowptr, int wave, int lane) {
+#pragma unroll
+    for (int idx = wave; idx < NCH / 64; idx += 4) {
+      const int p = idx * 64 + lane, r = p / CPR, pc = p % CPR;
+      const char *src = (const char *)rowptr(r) + ((pc ^ swz(r)) << 4);
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)src,
+                                       (void __attribute__((address_space(3))) *)(lds + idx * 1024), 16, 0, 0);
+    }
+  }
+};
+
+// Wait for every outstanding memory operation of the wave (direct LDS copies included).
+__device__ inline void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
+
 // Load one scalar of an input tensor stored as bf16 (is_f32 = false) or fp32.
 __device__ inline float load_in(const void *p, int64_t idx, bool is_f32) {
   return is_f32 ? ((const float *)p)[idx] : bf16_to_f32(((const uint16_t *)p)[idx]);

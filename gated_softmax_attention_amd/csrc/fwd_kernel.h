@@ -51,15 +51,12 @@ __global__ void __launch_bounds__(256, 2) k_fix_fwd(FwdArgs a) {
   constexpr int DVP = DV < 32 ? 32 : DV;  // output columns padded to whole 32-wide MFMA blocks
   constexpr int NB = DVP / 32;
   constexpr int NS = DK / 16;
-  constexpr int KSTR = DK + 8;  // LDS row strides (elements), padded against bank conflicts
-  constexpr int VSTR = CH + 8;
-  constexpr int KCH = CH * DK / 8;  // 16-byte pieces per K tile
-  constexpr int KPT = (KCH + 255) / 256;
-  constexpr int VCH = DV * CH / 8;  // 16-byte pieces per Vt tile
-  constexpr int VPT = (VCH + 255) / 256;
+  using KT = LdsTile<CH, DK * 2>;   // K rows of a key chunk (bf16, or fp16 for fp32 inputs)
+  using VT = LdsTile<DVP, CH * 2>;  // transposed V tile, rows padded to DVP (zero rows)
+  using VTD = LdsTile<DV, CH * 2>;  // the rows a copy fills
 
-  __shared__ __align__(16) uint16_t Ks[2][CH * KSTR];
-  __shared__ __align__(16) _Float16 Vs[2][DVP * VSTR];
+  __shared__ __align__(1024) char Ks[2][KT::BYTES];
+  __shared__ __align__(1024) char Vs[2][VT::BYTES];
   __shared__ __align__(16) float Gs[2][DVP];
   __shared__ __align__(16) float Asc[4][32];
 
@@ -96,53 +93,31 @@ __global__ void __launch_bounds__(256, 2) k_fix_fwd(FwdArgs a) {
 
   // Padding rows of narrow Vt tiles stay zero; their Gam entries stay one.
   if (DV < DVP) {
-    for (int e = tid; e < (DVP - DV) * VSTR; e += 256) {
-      Vs[0][DV * VSTR + e] = (_Float16)0.f;
-      Vs[1][DV * VSTR + e] = (_Float16)0.f;
+    for (int e = tid; e < (DVP - DV) * CH * 2 / 4; e += 256) {
+      ((uint32_t *)(Vs[0] + DV * CH * 2))[e] = 0u;
+      ((uint32_t *)(Vs[1] + DV * CH * 2))[e] = 0u;
     }
     for (int e = tid; e < DVP - DV; e += 256) { Gs[0][DV + e] = 1.f; Gs[1][DV + e] = 1.f; }
   }
 
-  uint4 kreg[KPT], vreg[VPT];
-  float4 greg = make_float4(1.f, 1.f, 1.f, 1.f);
-  auto load_tile = [&](int J) {
+  // Stage key chunk J into LDS buffer b: direct copies for bf16 inputs; fp32
+  // inputs are converted to fp16 through registers into the same layout.
+  auto stage_tile = [&](int J, int b) {
     const int64_t gcJ = cb + J;
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      int idx = tid + 256 * i;
-      if (idx < KCH) {
-        int key = idx / (DK / 8), e8 = idx % (DK / 8);
-        int tok = J * CH + key;
-        if (tok < L) kreg[i] = __builtin_bit_cast(uint4, IF::load(a.k, ((st + tok) * Hkv + c) * DK + 8 * e8));
-        else kreg[i] = make_uint4(0, 0, 0, 0);
+    if constexpr (!F32IN) {
+      KT::dma(Ks[b], [&](int r) { return (const uint16_t *)a.k + ((st + J * CH + r) * Hkv + c) * DK; }, wave, lane);
+    } else {
+      for (int p = tid; p < KT::NCH; p += 256) {
+        const int r = p / KT::CPR, cc = p % KT::CPR;
+        *(f16x8 *)(Ks[b] + KT::off(r, cc)) = IF::load(a.k, ((st + J * CH + r) * Hkv + c) * DK + 8 * cc);
       }
     }
-    const uint4 *vsrc = (const uint4 *)(a.VtT + (gcJ * Hkv + c) * DV * CH);
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      int idx = tid + 256 * i;
-      if (idx < VCH) vreg[i] = vsrc[idx];
-    }
-    if (tid < DV / 4) greg = ((const float4 *)(a.Gam + (gcJ * Hkv + c) * DV))[tid];
-  };
-  auto store_tile = [&](int b) {
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      int idx = tid + 256 * i;
-      if (idx < KCH) {
-        int key = idx / (DK / 8), e8 = idx % (DK / 8);
-        *(uint4 *)&Ks[b][key * KSTR + 8 * e8] = kreg[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      int idx = tid + 256 * i;
-      if (idx < VCH) {
-        int row = idx / (CH / 8), c8 = idx % (CH / 8);
-        *(uint4 *)&Vs[b][row * VSTR + 8 * c8] = vreg[i];
-      }
-    }
-    if (tid < DV / 4) *(float4 *)&Gs[b][4 * tid] = greg;
+    const _Float16 *vt = a.VtT + (gcJ * Hkv + c) * DV * CH;
+    VTD::dma(Vs[b], [&](int r) { return vt + r * CH; }, wave, lane);
+    if (tid < DV / 4)
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1))) *)(a.Gam + (gcJ * Hkv + c) * DV + 4 * tid),
+          (void __attribute__((address_space(3))) *)Gs[b], 16, 0, 0);
   };
 
   f32x16 acc[NB];
@@ -189,25 +164,20 @@ __global__ void __launch_bounds__(256, 2) k_fix_fwd(FwdArgs a) {
   };
 
   // ---------------- inter-chunk loop ----------------
-  if (nJ > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
+  if (nJ > 0) stage_tile(0, 0);
+  wait_all();
   __syncthreads();
   for (int J = 0; J < nJ; ++J) {
     const int b = J & 1;
-    if (J + 1 < nJ) load_tile(J + 1);
+    if (J + 1 < nJ) stage_tile(J + 1, b ^ 1);
     if (active && J < Iw - 1) {
       f32x16 sc[2];
 #pragma unroll
       for (int be = 0; be < 2; ++be) {
+        sc[be] = zero16();
 #pragma unroll
-        for (int j = 0; j < 16; ++j) sc[be][j] = 0.f;
-#pragma unroll
-        for (int i = 0; i < NS; ++i) {
-          kfrag kf = *(const kfrag *)&Ks[b][(32 * be + n) * KSTR + 16 * i + 8 * hh];
-          sc[be] = mma32(kf, qf[i], sc[be]);
-        }
+        for (int i = 0; i < NS; ++i)
+          sc[be] = mma32(*(const kfrag *)(Ks[b] + KT::off(32 * be + n, 2 * i + hh)), qf[i], sc[be]);
       }
       float mx = fmaxf(row_max(sc[0]), row_max(sc[1]));
       mx = max_across_halves(mx) * sl2;
@@ -225,13 +195,11 @@ __global__ void __launch_bounds__(256, 2) k_fix_fwd(FwdArgs a) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) acc[bb][j] *= gam;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          f16x8 vf = *(const f16x8 *)&Vs[b][(32 * bb + n) * VSTR + 16 * t + 8 * hh];
-          acc[bb] = mma32(pf[t], vf, acc[bb]);
-        }
+        for (int t = 0; t < 4; ++t)
+          acc[bb] = mma32(pf[t], *(const f16x8 *)(Vs[b] + VT::off(32 * bb + n, 2 * t + hh)), acc[bb]);
       }
     }
-    if (J + 1 < nJ) store_tile(b ^ 1);
+    wait_all();
     __syncthreads();
   }
   if (!active) return;

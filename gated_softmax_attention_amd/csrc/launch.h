@@ -24,6 +24,7 @@ struct FwdArgs {
 struct BwdArgs {
   const void *q, *k, *v;
   const float *Gl2, *Gam;      // 128-chunk local prefix sums of g (log2 units), chunk decays
+  const double *Lam;           // [chunk][Hkv][DV] prefix over chunks of the chunk log2 totals
   const _Float16 *Vr;          // [chunk][Hkv][CB][DV] V scaled to its chunk end
   const _Float16 *Qt, *Kt;     // [chunk][H][D][CB] transposed fp16 tiles (key_pos order)
   const float *delta;          // [T, Hq, DV] gradient reaching x
@@ -75,6 +76,7 @@ inline hipError_t launch_fwd(int dk, int dv, bool f32in, const FwdArgs &a, int g
 
 hipError_t launch_gate_prep_rows(int dv, const float *g, const void *v, bool in_f32, const Plan &plan, int Hkv,
                                  int ncb_ub, float *Gl2, float *Gam, _Float16 *Vr, hipStream_t st);
+hipError_t launch_chunk_logprefix(int dv, const float *Gl2, const Plan &plan, int Hkv, double *Lam, hipStream_t st);
 hipError_t launch_tiles_t(int D, const void *in, bool in_f32, const Plan &plan, int H, int ncb_ub, _Float16 *out,
                           hipStream_t st);
 hipError_t launch_bwd_prep(int dv, const PrepArgs &a, int ncb_ub, hipStream_t st);

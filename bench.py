@@ -95,12 +95,28 @@ def cpu_baseline(x):
                       f"bwd {t2 - t1:.1f} s (the backward recomputes the forward)"}
 
 
+COPY_BYTES = 1 << 30
+
+
+def copy_probe(torch):
+    """A plain copy of known size: each dispatch reads and writes COPY_BYTES of HBM, which
+    calibrates the FETCH_SIZE / WRITE_SIZE counters against true bytes."""
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": COPY_BYTES, "dispatches": 3}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 3 times (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build runs the kernel on one GPU's share and has no "
@@ -108,6 +124,9 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_probe:
+        copy_probe(torch)
+        return
     import gated_softmax_attention_amd as F
     from gated_softmax_attention_amd import synth
 

@@ -481,7 +481,8 @@ __global__ void __launch_bounds__(256, 1) k_bwd_intra_dkv(BwdArgs a) {
 // (bf16) for S^T, transposed K (fp16) for dS.K, and V scaled to its chunk
 // end (fp16) for dP^T.  The decay product between the chunks, gamma_IJ =
 // exp2(Lam[I-1] - Lam[J]), multiplies the query-side operand (the scaled
-// dhat rows), rebuilt once per key chunk.
+// dhat rows), rebuilt once per key chunk; gamma_IJ itself is computed into
+// LDS during the step before the chunk starts, from a Lam row loaded then.
 // ---------------------------------------------------------------------------
 template <int DK, int DV, bool F32IN>
 __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdArgs a) {
@@ -492,9 +493,13 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdArgs a) {
   using TT = LdsTile<DKP, 64>;     // transposed K (dk rows x 32 keys), rows padded to DKP
   using TTD = LdsTile<DK, 64>;
   using VT = LdsTile<32, DV * 2>;  // V rows of the step (scaled to their chunk end)
-  __shared__ __align__(1024) char Ks[2][KT::BYTES];
-  __shared__ __align__(1024) char Kts[2][TT::BYTES];
-  __shared__ __align__(1024) char Vs[2][VT::BYTES];
+  // One LDS object for every tile (see the forward kernel).
+  constexpr int O_K = 0, O_T = O_K + 2 * KT::BYTES, O_V = O_T + 2 * TT::BYTES, O_G = O_V + 2 * VT::BYTES;
+  __shared__ __align__(1024) char smem[O_G + 2 * DV * 4];
+  auto Ks = [&](int b) { return smem + O_K + b * KT::BYTES; };
+  auto Kts = [&](int b) { return smem + O_T + b * TT::BYTES; };
+  auto Vs = [&](int b) { return smem + O_V + b * VT::BYTES; };
+  auto gam = [&](int b) { return (float *)(smem + O_G) + b * DV; };
 
   const Plan &pl = a.plan;
   const int Hq = a.Hq, Hkv = a.Hkv, G = Hq / Hkv;
@@ -510,7 +515,8 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdArgs a) {
   const int64_t st = pl.seq_start[s];
   const int L = pl.seq_len[s];
   const int cbs = pl.cb128[s];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hh = lane >> 5, n = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, n = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r0 = I * CB + 32 * wave;
   const int row = r0 + n;
   const bool rv = row < L;
@@ -527,57 +533,73 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdArgs a) {
   f16x8 dhf[NSV];
   if (DK < DKP)
     for (int e = tid; e < (DKP - DK) * 64 / 4; e += 256) {
-      ((uint32_t *)(Kts[0] + DK * 64))[e] = 0u;
-      ((uint32_t *)(Kts[1] + DK * 64))[e] = 0u;
+      ((uint32_t *)(Kts(0) + DK * 64))[e] = 0u;
+      ((uint32_t *)(Kts(1) + DK * 64))[e] = 0u;
     }
   f32x16 acc[NBK];
 #pragma unroll
   for (int b = 0; b < NBK; ++b) acc[b] = zero16();
+
+  // gamma_IJ[d] for d = tid (threads tid < DV): Lam[I-1] is fixed, Lam[J] is
+  // loaded one step ahead of the chunk that uses it.
+  const int dt = min(tid, DV - 1);
+  const double lamI = I > 0 ? a.Lam[((int64_t)(cbs + I - 1) * Hkv + c) * DV + dt] : 0.0;
+  auto lam_of = [&](int J) { return a.Lam[((int64_t)(cbs + J) * Hkv + c) * DV + dt]; };
 
   const int nsteps = 4 * I;
   auto stage_tile = [&](int k, int b) {
     const int J = I - 1 - (k >> 2), u = k & 3;
     const int kt0 = J * CB + 32 * u;
     if constexpr (!F32IN) {
-      KT::dma(Ks[b], [&](int r) { return (const uint16_t *)a.k + ((st + kt0 + r) * Hkv + c) * DK; }, wave, lane);
+      KT::dma(Ks(b), [&](int r) { return (const uint16_t *)a.k + ((st + kt0 + r) * Hkv + c) * DK; }, wave, lane);
     } else {
       for (int p = tid; p < KT::NCH; p += 256) {
         const int r = p / KT::CPR, cc = p % KT::CPR;
-        *(f16x8 *)(Ks[b] + KT::off(r, cc)) = IF::load(a.k, ((st + kt0 + r) * Hkv + c) * DK + 8 * cc);
+        *(f16x8 *)(Ks(b) + KT::off(r, cc)) = IF::load(a.k, ((st + kt0 + r) * Hkv + c) * DK + 8 * cc);
       }
     }
     const _Float16 *ktile = a.Kt + ((int64_t)(cbs + J) * Hkv + c) * DK * CB + 32 * u;
-    TTD::dma(Kts[b], [&](int r) { return ktile + r * CB; }, wave, lane);
+    TTD::dma(Kts(b), [&](int r) { return ktile + r * CB; }, wave, lane);
     const _Float16 *vtile = a.Vr + ((int64_t)(cbs + J) * Hkv + c) * CB * DV + (32 * u) * DV;
-    VT::dma(Vs[b], [&](int r) { return vtile + r * DV; }, wave, lane);
+    VT::dma(Vs(b), [&](int r) { return vtile + r * DV; }, wave, lane);
   };
 
-  if (nsteps > 0) stage_tile(0, 0);
+  // The unscaled dhat rows are loaded at the end of the step before each key
+  // chunk (so their wait is the step's final wait) and scaled at the top of
+  // the chunk's first step, before that step issues any copy: LDS reads that
+  // follow a copy issue in the same step can make the compiler wait for it.
+  f16x8 raw[NSV];
+  if (nsteps > 0) {
+    stage_tile(0, 0);
+    if (tid < DV) gam(0)[tid] = fast_exp2((float)(lamI - lam_of(I - 1)));
+#pragma unroll
+    for (int i = 0; i < NSV; ++i) raw[i] = *(const f16x8 *)(dhrow + 16 * i + 8 * hh);
+  }
   wait_all();
   __syncthreads();
   for (int k = 0; k < nsteps; ++k) {
     const int b = k & 1;
-    if (k + 1 < nsteps) stage_tile(k + 1, b ^ 1);
+    const bool next_chunk = (k & 3) == 3 && k + 1 < nsteps;
     if ((k & 3) == 0) {  // entered key chunk J: dhat operand times gamma_IJ
-      const int J = I - 1 - (k >> 2);
-      const double *l1 = a.Lam + ((int64_t)(cbs + I - 1) * Hkv + c) * DV;
-      const double *l0 = a.Lam + ((int64_t)(cbs + J) * Hkv + c) * DV;
+      const float *gm = gam((k >> 2) & 1);
 #pragma unroll
       for (int i = 0; i < NSV; ++i) {
-        const f16x8 raw = *(const f16x8 *)(dhrow + 16 * i + 8 * hh);
+        const float4 g0 = *(const float4 *)(gm + 16 * i + 8 * hh), g1 = *(const float4 *)(gm + 16 * i + 8 * hh + 4);
+        const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int d = 16 * i + 8 * hh + e;
-          dhf[i][e] = (_Float16)((float)raw[e] * fast_exp2((float)(l1[d] - l0[d])));
-        }
+        for (int e = 0; e < 8; ++e) dhf[i][e] = (_Float16)((float)raw[i][e] * gv[e]);
       }
     }
+    // Same copies and loads on every step (the last step re-copies its own
+    // tile into the idle buffer; the Lam row index is kept valid).
+    stage_tile(min(k + 1, nsteps - 1), b ^ 1);
+    const double lamJ = lam_of(max(I - 2 - (k >> 2), 0));
     {
       f32x16 sc = zero16(), dp = zero16();
 #pragma unroll
-      for (int i = 0; i < NS; ++i) sc = mma32(*(const kfrag *)(Ks[b] + KT::off(n, 2 * i + hh)), qf[i], sc);
+      for (int i = 0; i < NS; ++i) sc = mma32(*(const kfrag *)(Ks(b) + KT::off(n, 2 * i + hh)), qf[i], sc);
 #pragma unroll
-      for (int i = 0; i < NSV; ++i) dp = mma32(*(const f16x8 *)(Vs[b] + VT::off(n, 2 * i + hh)), dhf[i], dp);
+      for (int i = 0; i < NSV; ++i) dp = mma32(*(const f16x8 *)(Vs(b) + VT::off(n, 2 * i + hh)), dhf[i], dp);
       f16x8 dsf[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u)
@@ -590,7 +612,14 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdArgs a) {
       for (int bk = 0; bk < NBK; ++bk)
 #pragma unroll
         for (int u = 0; u < 2; ++u)
-          acc[bk] = mma32(dsf[u], *(const f16x8 *)(Kts[b] + TT::off(32 * bk + n, 2 * u + hh)), acc[bk]);
+          acc[bk] = mma32(dsf[u], *(const f16x8 *)(Kts(b) + TT::off(32 * bk + n, 2 * u + hh)), acc[bk]);
+    }
+    // gamma of the next chunk, into the other buffer (its last readers passed
+    // the barrier that began this chunk).
+    if (next_chunk) {
+      if (tid < DV) gam(((k >> 2) + 1) & 1)[tid] = fast_exp2((float)(lamI - lamJ));
+#pragma unroll
+      for (int i = 0; i < NSV; ++i) raw[i] = *(const f16x8 *)(dhrow + 16 * i + 8 * hh);
     }
     wait_all();
     __syncthreads();
@@ -611,16 +640,17 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dk, dv from query chunks two or more after the key chunk.  Workgroup = 128
-// keys of one kv head (4 waves x 32 keys).  Query chunks are visited from the
-// last to the first (and within a chunk every head of the group), 32 queries
-// per step staged through LDS (double buffered): Q rows (bf16) for S,
-// transposed Q (fp16) for dK, the scaled dhat (relative to its chunk start)
-// as rows for dP and transposed for dV, and the per-row exponent offsets.
-// With the chunks visited backwards, the decay products between the chunks
-// enter dV as a Horner recurrence, dV <- dV (.) Gam_I + P^T dhat_I, and enter
-// dP through the key-side operand V (.) gamma_IJ, rebuilt once per chunk with
-// gamma_IJ = exp2(Lam[I-1] - Lam[J]).  The staged tiles are plain copies.
+// dk, dv from query chunks two or more after the key chunk.  Workgroup = the
+// 128 keys of one key chunk J and kv head (4 waves x 32 keys), visiting the
+// query chunks from the last to J + 2 and, within each, the G query heads of
+// the group, 32 query rows per step copied straight into LDS (double
+// buffered): Q rows, transposed Q, scaled dhat rows and transposed scaled
+// dhat.  The decay product between the chunks, gamma_IJ = exp2(Lam[I-1] -
+// Lam[J]), enters both products through per-chunk operands: V (.) gamma_IJ
+// (rebuilt per query chunk from an LDS copy of the chunk's V rows) for dP,
+// and the transposed dhat times gamma_IJ[d] (a per-lane factor, d being the
+// lane's output column) for dV, so the accumulators are only ever touched by
+// MFMAs.  gamma_IJ is computed into LDS during the step before its chunk.
 // ---------------------------------------------------------------------------
 template <int DK, int DV, bool F32IN>
 __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
@@ -634,11 +664,17 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
   using DR = LdsTile<32, DV * 2>;   // scaled dhat rows
   using DTT = LdsTile<DVP, 64>;     // scaled dhat, transposed
   using DTTD = LdsTile<DV, 64>;
-  __shared__ __align__(1024) char Qs[2][QT::BYTES];
-  __shared__ __align__(1024) char Qts[2][QTT::BYTES];
-  __shared__ __align__(1024) char Ds[2][DR::BYTES];
-  __shared__ __align__(1024) char Dts[2][DTT::BYTES];
-  __shared__ __align__(16) float Ms[2][32];
+  using VRT = LdsTile<CB, DV * 2>;  // the key chunk's V rows, scaled to the chunk end
+  // One LDS object for every tile (see the forward kernel).
+  constexpr int O_Q = 0, O_QT = O_Q + 2 * QT::BYTES, O_D = O_QT + 2 * QTT::BYTES, O_DT = O_D + 2 * DR::BYTES;
+  constexpr int O_V = O_DT + 2 * DTT::BYTES, O_M = O_V + VRT::BYTES, O_G = O_M + 2 * 256;
+  __shared__ __align__(1024) char smem[O_G + 2 * DVP * 4];
+  auto Qs = [&](int b) { return smem + O_Q + b * QT::BYTES; };
+  auto Qts = [&](int b) { return smem + O_QT + b * QTT::BYTES; };
+  auto Ds = [&](int b) { return smem + O_D + b * DR::BYTES; };
+  auto Dts = [&](int b) { return smem + O_DT + b * DTT::BYTES; };
+  auto Ms = [&](int b) { return (float *)(smem + O_M + b * 256); };  // 64 floats, 32 used
+  auto gam = [&](int b) { return (float *)(smem + O_G) + b * DVP; };
 
   const Plan &pl = a.plan;
   const int Hq = a.Hq, Hkv = a.Hkv, G = Hq / Hkv;
@@ -650,26 +686,30 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
   const int64_t st = pl.seq_start[s];
   const int L = pl.seq_len[s];
   const int cbs = pl.cb128[s];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hh = lane >> 5, n = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, n = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kb = J * CB + 32 * wave;
   const int key = kb + n;
   const bool kv = key < L;
   const float sl2 = a.sl2;
 
+  const int nch = (L + CB - 1) / CB;
+  const int I0 = J + 2, I1 = nch - 1;                  // query chunks visited: I1 down to I0
+  const int ns1 = (L - I1 * CB + 31) / 32;              // steps of the last (possibly partial) chunk
+  const int nsteps = I0 <= I1 ? G * ns1 + 4 * G * (I1 - I0) : 0;
   kfrag kf[NS];
 #pragma unroll
   for (int i = 0; i < NS; ++i)
     kf[i] = kv ? IF::load(a.k, ((st + key) * Hkv + c) * DK + 16 * i + 8 * hh) : IF::zero();
-  const _Float16 *vrow = a.Vr + (((int64_t)(cbs + J) * Hkv + c) * CB + 32 * wave + n) * DV;
   if (DK < DKP)
     for (int e = tid; e < (DKP - DK) * 64 / 4; e += 256) {
-      ((uint32_t *)(Qts[0] + DK * 64))[e] = 0u;
-      ((uint32_t *)(Qts[1] + DK * 64))[e] = 0u;
+      ((uint32_t *)(Qts(0) + DK * 64))[e] = 0u;
+      ((uint32_t *)(Qts(1) + DK * 64))[e] = 0u;
     }
   if (DV < DVP)
     for (int e = tid; e < (DVP - DV) * 64 / 4; e += 256) {
-      ((uint32_t *)(Dts[0] + DV * 64))[e] = 0u;
-      ((uint32_t *)(Dts[1] + DV * 64))[e] = 0u;
+      ((uint32_t *)(Dts(0) + DV * 64))[e] = 0u;
+      ((uint32_t *)(Dts(1) + DV * 64))[e] = 0u;
     }
   f32x16 accK[NBK], accV[NBV];
 #pragma unroll
@@ -677,10 +717,8 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
 #pragma unroll
   for (int b = 0; b < NBV; ++b) accV[b] = zero16();
 
-  const int nch = (L + CB - 1) / CB;
-  const int I0 = J + 2, I1 = nch - 1;                  // query chunks visited: I1 down to I0
-  const int ns1 = (L - I1 * CB + 31) / 32;              // steps of the last (possibly partial) chunk
-  const int nsteps = I0 <= I1 ? G * ns1 + 4 * G * (I1 - I0) : 0;
+  // Step k -> query chunk I, query head of the group gq, 32-row slice u; and
+  // the ordinal of its chunk among the visited ones (0 for I1).
   auto step_of = [&](int k, int &I, int &gq, int &u) {
     if (k < G * ns1) {
       I = I1; gq = k / ns1; u = k % ns1;
@@ -689,6 +727,7 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
       I = I1 - 1 - r / (4 * G); gq = (r % (4 * G)) >> 2; u = r & 3;
     }
   };
+  auto ord_of = [&](int k) { return k < G * ns1 ? 0 : 1 + (k - G * ns1) / (4 * G); };
   // Rows past the end of the sequence are copied from its last row (finite
   // values); their probabilities are masked to zero when the step is computed.
   auto stage_tile = [&](int k, int b) {
@@ -698,70 +737,78 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
     const int qt0 = I * CB + 32 * u;
     auto qrow = [&](int r) { return st + min(qt0 + r, L - 1); };
     if constexpr (!F32IN) {
-      QT::dma(Qs[b], [&](int r) { return (const uint16_t *)a.q + (qrow(r) * Hq + h) * DK; }, wave, lane);
+      QT::dma(Qs(b), [&](int r) { return (const uint16_t *)a.q + (qrow(r) * Hq + h) * DK; }, wave, lane);
     } else {
       for (int p = tid; p < QT::NCH; p += 256) {
         const int r = p / QT::CPR, cc = p % QT::CPR;
-        *(f16x8 *)(Qs[b] + QT::off(r, cc)) = IF::load(a.q, (qrow(r) * Hq + h) * DK + 8 * cc);
+        *(f16x8 *)(Qs(b) + QT::off(r, cc)) = IF::load(a.q, (qrow(r) * Hq + h) * DK + 8 * cc);
       }
     }
     const _Float16 *qtile = a.Qt + ((int64_t)(cbs + I) * Hq + h) * DK * CB + 32 * u;
-    QTTD::dma(Qts[b], [&](int r) { return qtile + r * CB; }, wave, lane);
-    DR::dma(Ds[b], [&](int r) { return a.dh + (qrow(r) * Hq + h) * DV; }, wave, lane);
+    QTTD::dma(Qts(b), [&](int r) { return qtile + r * CB; }, wave, lane);
+    DR::dma(Ds(b), [&](int r) { return a.dh + (qrow(r) * Hq + h) * DV; }, wave, lane);
     const _Float16 *dtile = a.dht + ((int64_t)(cbs + I) * Hq + h) * DV * CB + 32 * u;
-    DTTD::dma(Dts[b], [&](int r) { return dtile + r * CB; }, wave, lane);
-    if (tid < 32)  // one dword per lane: lane r fills Ms[b][r]
-      __builtin_amdgcn_global_load_lds(
-          (const void __attribute__((address_space(1))) *)(a.mb + (qrow(tid) * Hq + h)),
-          (void __attribute__((address_space(3))) *)Ms[b], 4, 0, 0);
+    DTTD::dma(Dts(b), [&](int r) { return dtile + r * CB; }, wave, lane);
+    dma4(Ms(b), a.mb + qrow(lane) * Hq + h);  // lane r fills Ms[r] (every wave, the same bytes)
   };
 
-  f16x8 vf[NSV];  // key-side dP operand V (.) gamma_IJ, rebuilt per query chunk
-  int curI = -1;
-  if (nsteps > 0) stage_tile(0, 0);
+  // gamma_IJ[d] for d = tid (threads tid < DV).
+  const int dt = min(tid, DV - 1);
+  const double lamJ = a.Lam[((int64_t)(cbs + J) * Hkv + c) * DV + dt];
+  auto lam_of = [&](int I) { return a.Lam[((int64_t)(cbs + I - 1) * Hkv + c) * DV + dt]; };
+
+  if (nsteps > 0) {
+    VRT::dma(smem + O_V, [&](int r) { return a.Vr + (((int64_t)(cbs + J) * Hkv + c) * CB + r) * DV; }, wave, lane);
+    stage_tile(0, 0);
+    if (tid < DV) gam(0)[tid] = fast_exp2((float)(lam_of(I1) - lamJ));
+  }
   wait_all();
   __syncthreads();
+
+  f16x8 vf[NSV];        // key-side dP operand V (.) gamma_IJ, rebuilt per query chunk
+  _Float16 gh[NBV];     // gamma_IJ of the lane's dV output columns
   for (int k = 0; k < nsteps; ++k) {
     const int b = k & 1;
-    if (k + 1 < nsteps) stage_tile(k + 1, b ^ 1);
-    {
-      int I, gq, u;
-      step_of(k, I, gq, u);
-      const int qt0 = I * CB + 32 * u;
-      if (I != curI) {
-        if (curI >= 0) {  // left chunk I + 1: dV <- dV (.) Gam_I before adding chunk I
+    int I, gq, u;
+    step_of(k, I, gq, u);
+    const int ord = ord_of(k);
+    const bool first = k == 0 || ord != ord_of(k - 1);
+    const bool next_chunk = k + 1 < nsteps && ord_of(k + 1) != ord;
+    if (first) {  // before this step issues copies (see the dq kernel)
+      const float *gm = gam(ord & 1);
 #pragma unroll
-          for (int bv = 0; bv < NBV; ++bv) {
-            const int col = 32 * bv + n;
-            const float gm = col < DV ? a.Gam[((int64_t)(cbs + I) * Hkv + c) * DV + col] : 1.f;
+      for (int i = 0; i < NSV; ++i) {
+        const f16x8 raw = *(const f16x8 *)(smem + O_V + VRT::off(32 * wave + n, 2 * i + hh));
+        const float4 g0 = *(const float4 *)(gm + 16 * i + 8 * hh), g1 = *(const float4 *)(gm + 16 * i + 8 * hh + 4);
+        const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
 #pragma unroll
-            for (int j = 0; j < 16; ++j) accV[bv][j] *= gm;
-          }
-        }
-        curI = I;
-        const double *l1 = a.Lam + ((int64_t)(cbs + I - 1) * Hkv + c) * DV;
-        const double *l0 = a.Lam + ((int64_t)(cbs + J) * Hkv + c) * DV;
-#pragma unroll
-        for (int i = 0; i < NSV; ++i) {
-          const f16x8 raw = *(const f16x8 *)(vrow + 16 * i + 8 * hh);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int d = 16 * i + 8 * hh + e;
-            vf[i][e] = (_Float16)((float)raw[e] * fast_exp2((float)(l1[d] - l0[d])));
-          }
-        }
+        for (int e = 0; e < 8; ++e) vf[i][e] = (_Float16)((float)raw[e] * gv[e]);
       }
+#pragma unroll
+      for (int bv = 0; bv < NBV; ++bv) gh[bv] = 32 * bv + n < DV ? (_Float16)gm[32 * bv + n] : (_Float16)0.f;
+    }
+    float4 mq[4];  // exponent offsets of the step's rows, read before the copies are issued
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) mq[q4] = *(const float4 *)&Ms(b)[8 * q4 + 4 * hh];
+    // Same copies and loads on every step (the last step re-copies its own
+    // tile into the idle buffer; the Lam row index is kept valid).
+    const int kn = min(k + 1, nsteps - 1);
+    int In, gn, un;
+    step_of(kn, In, gn, un);
+    const double lamI = lam_of(In);
+    stage_tile(kn, b ^ 1);
+    const int qt0 = I * CB + 32 * u;
+    {
       // S[q][key] and dP[q][key]: lane = key, register j = query acc_row(hh, j)
       f32x16 sc = zero16(), dp = zero16();
 #pragma unroll
-      for (int i = 0; i < NS; ++i) sc = mma32(*(const kfrag *)(Qs[b] + QT::off(n, 2 * i + hh)), kf[i], sc);
+      for (int i = 0; i < NS; ++i) sc = mma32(*(const kfrag *)(Qs(b) + QT::off(n, 2 * i + hh)), kf[i], sc);
 #pragma unroll
-      for (int i = 0; i < NSV; ++i) dp = mma32(*(const f16x8 *)(Ds[b] + DR::off(n, 2 * i + hh)), vf[i], dp);
+      for (int i = 0; i < NSV; ++i) dp = mma32(*(const f16x8 *)(Ds(b) + DR::off(n, 2 * i + hh)), vf[i], dp);
       f16x8 pf[2], dsf[2];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 mq = *(const float4 *)&Ms[b][8 * q4 + 4 * hh];
-        const float mv[4] = {mq.x, mq.y, mq.z, mq.w};
+        const float mv[4] = {mq[q4].x, mq[q4].y, mq[q4].z, mq[q4].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int j = 4 * q4 + e;
@@ -774,27 +821,20 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
       for (int bv = 0; bv < NBV; ++bv)
 #pragma unroll
         for (int uu = 0; uu < 2; ++uu)
-          accV[bv] = mma32(pf[uu], *(const f16x8 *)(Dts[b] + DTT::off(32 * bv + n, 2 * uu + hh)), accV[bv]);
+          accV[bv] = mma32(pf[uu], *(const f16x8 *)(Dts(b) + DTT::off(32 * bv + n, 2 * uu + hh)) * gh[bv], accV[bv]);
 #pragma unroll
       for (int bk = 0; bk < NBK; ++bk)
 #pragma unroll
         for (int uu = 0; uu < 2; ++uu)
-          accK[bk] = mma32(dsf[uu], *(const f16x8 *)(Qts[b] + QTT::off(32 * bk + n, 2 * uu + hh)), accK[bk]);
+          accK[bk] = mma32(dsf[uu], *(const f16x8 *)(Qts(b) + QTT::off(32 * bk + n, 2 * uu + hh)), accK[bk]);
     }
+    // gamma of the next chunk, into the other buffer (its last readers passed
+    // the barrier that ended the first step of the previous chunk).
+    if (next_chunk && tid < DV) gam((ord + 1) & 1)[tid] = fast_exp2((float)(lamI - lamJ));
     wait_all();
     __syncthreads();
   }
   if (kb >= L) return;
-  // dV so far is relative to the start of chunk J + 2; the chunk J + 1 between adds Gam_J+1
-  if (nsteps > 0) {
-#pragma unroll
-    for (int bv = 0; bv < NBV; ++bv) {
-      const int col = 32 * bv + n;
-      const float gm = col < DV ? a.Gam[((int64_t)(cbs + J + 1) * Hkv + c) * DV + col] : 1.f;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) accV[bv][j] *= gm;
-    }
-  }
   // epilogue: dk, dv (inter part scaled to the key: exp(Gl_end(J) - Gl_key)), dG = qside - v (.) dv
   const int tend = min((J + 1) * CB, L) - 1;
 #pragma unroll

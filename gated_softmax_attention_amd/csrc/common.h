@@ -106,7 +106,8 @@ __device__ inline uint16_t f32_to_bf16_rne(float f) {
 // unpadded, [ROWS][RB bytes], and the 16-byte chunk c of row r is stored at
 // chunk position c ^ swz(r): for the MFMA operand reads (32 lanes reading the
 // same chunk of 32 consecutive rows) every 16 lanes then hit 16 distinct
-// 16-byte bank groups, with no padding.
+// 16-byte bank groups, with no padding.  `wave` must be wave-uniform (an
+// SGPR value) so that the copies are issued under uniform control flow.
 template <int ROWS, int RB> struct LdsTile {
   static constexpr int CPR = RB / 16;     // 16-byte chunks per row (2..16)
   static constexpr int NCH = ROWS * CPR;  // chunks per tile
@@ -114,11 +115,19 @@ template <int ROWS, int RB> struct LdsTile {
   static_assert(CPR >= 2 && CPR <= 16 && NCH % 64 == 0, "tile shape");
   __device__ static int swz(int r) { return (r / (16 / CPR)) % CPR; }
   __device__ static int off(int r, int c) { return r * RB + ((c ^ swz(r)) << 4); }
-  // Copy the tile: rowptr(r) gives the global address of row r (RB contiguous bytes).
+  // Copy the tile: rowptr(r) gives the global address of row r (RB contiguous
+  // bytes).  Every wave issues the same number of copies, NW (a wave with
+  // nothing left repeats a piece another wave copies, same bytes to the same
+  // place), so that the number of loads in flight never depends on the path
+  // taken: the compiler's wait counts stay exact instead of falling back to
+  // waiting for everything.
+  static constexpr int NI = NCH / 64;             // 1 KB wave copies per tile
+  static constexpr int NW = NI < 4 ? 1 : (NI + 3) / 4;
   template <class RowPtr>
   __device__ static void dma(char *lds, RowPtr rowptr, int wave, int lane) {
 #pragma unroll
-    for (int idx = wave; idx < NCH / 64; idx += 4) {
+    for (int t = 0; t < NW; ++t) {
+      const int idx = NI < 4 ? wave % NI : min(wave + 4 * t, NI - 1);
       const int p = idx * 64 + lane, r = p / CPR, pc = p % CPR;
       const char *src = (const char *)rowptr(r) + ((pc ^ swz(r)) << 4);
       __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)src,
@@ -126,6 +135,18 @@ template <int ROWS, int RB> struct LdsTile {
     }
   }
 };
+
+// One direct copy of 16 bytes per lane; lane l's piece lands at lds + 16 l.
+// Issue it under wave-uniform control flow only.
+__device__ inline void dma16(void *lds, const void *src) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)src,
+                                   (void __attribute__((address_space(3))) *)lds, 16, 0, 0);
+}
+// The same with 4 bytes per lane, landing at lds + 4 l.
+__device__ inline void dma4(void *lds, const void *src) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)src,
+                                   (void __attribute__((address_space(3))) *)lds, 4, 0, 0);
+}
 
 // Wait for every outstanding memory operation of the wave (direct LDS copies included).
 __device__ inline void wait_all() { __builtin_amdgcn_s_waitcnt(0); }

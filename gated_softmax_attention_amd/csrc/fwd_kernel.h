@@ -55,12 +55,17 @@ __global__ void __launch_bounds__(256, 2) k_fix_fwd(FwdArgs a) {
   using VT = LdsTile<DVP, CH * 2>;  // transposed V tile, rows padded to DVP (zero rows)
   using VTD = LdsTile<DV, CH * 2>;  // the rows a copy fills
 
-  __shared__ __align__(1024) char Ks[2][KT::BYTES];
-  __shared__ __align__(1024) char Vs[2][VT::BYTES];
-  __shared__ __align__(16) float Gs[2][DVP];
-  __shared__ __align__(16) float Asc[4][32];
+  // One LDS object for every tile: with a single object the compiler does not
+  // make LDS reads wait for copies in flight into the other buffer.
+  constexpr int O_K = 0, O_V = O_K + 2 * KT::BYTES, O_G = O_V + 2 * VT::BYTES, O_A = O_G + 2 * 1024;
+  __shared__ __align__(1024) char smem[O_A + 4 * 32 * 4];
+  auto Ks = [&](int b) { return smem + O_K + b * KT::BYTES; };
+  auto Vs = [&](int b) { return smem + O_V + b * VT::BYTES; };
+  auto Gs = [&](int b) { return (float *)(smem + O_G + b * 1024); };  // 256 floats, DV used
+  float(*Asc)[32] = (float(*)[32])(smem + O_A);
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hh = lane >> 5, n = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, n = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const Plan &pl = a.plan;
   const int Hq = a.Hq, Hkv = a.Hkv, G = Hq / Hkv;
   int bid = blockIdx.x;
@@ -92,12 +97,12 @@ __global__ void __launch_bounds__(256, 2) k_fix_fwd(FwdArgs a) {
     qf[i] = (active && qrow < L) ? IF::load(a.q, ((st + qrow) * Hq + hq) * DK + 16 * i + 8 * hh) : IF::zero();
 
   // Padding rows of narrow Vt tiles stay zero; their Gam entries stay one.
+  // (Their Gam entries only scale accumulator columns that stay zero.)
   if (DV < DVP) {
     for (int e = tid; e < (DVP - DV) * CH * 2 / 4; e += 256) {
-      ((uint32_t *)(Vs[0] + DV * CH * 2))[e] = 0u;
-      ((uint32_t *)(Vs[1] + DV * CH * 2))[e] = 0u;
+      ((uint32_t *)(Vs(0) + DV * CH * 2))[e] = 0u;
+      ((uint32_t *)(Vs(1) + DV * CH * 2))[e] = 0u;
     }
-    for (int e = tid; e < DVP - DV; e += 256) { Gs[0][DV + e] = 1.f; Gs[1][DV + e] = 1.f; }
   }
 
   // Stage key chunk J into LDS buffer b: direct copies for bf16 inputs; fp32
@@ -105,19 +110,17 @@ __global__ void __launch_bounds__(256, 2) k_fix_fwd(FwdArgs a) {
   auto stage_tile = [&](int J, int b) {
     const int64_t gcJ = cb + J;
     if constexpr (!F32IN) {
-      KT::dma(Ks[b], [&](int r) { return (const uint16_t *)a.k + ((st + J * CH + r) * Hkv + c) * DK; }, wave, lane);
+      KT::dma(Ks(b), [&](int r) { return (const uint16_t *)a.k + ((st + J * CH + r) * Hkv + c) * DK; }, wave, lane);
     } else {
       for (int p = tid; p < KT::NCH; p += 256) {
         const int r = p / KT::CPR, cc = p % KT::CPR;
-        *(f16x8 *)(Ks[b] + KT::off(r, cc)) = IF::load(a.k, ((st + J * CH + r) * Hkv + c) * DK + 8 * cc);
+        *(f16x8 *)(Ks(b) + KT::off(r, cc)) = IF::load(a.k, ((st + J * CH + r) * Hkv + c) * DK + 8 * cc);
       }
     }
     const _Float16 *vt = a.VtT + (gcJ * Hkv + c) * DV * CH;
-    VTD::dma(Vs[b], [&](int r) { return vt + r * CH; }, wave, lane);
-    if (tid < DV / 4)
-      __builtin_amdgcn_global_load_lds(
-          (const void __attribute__((address_space(1))) *)(a.Gam + (gcJ * Hkv + c) * DV + 4 * tid),
-          (void __attribute__((address_space(3))) *)Gs[b], 16, 0, 0);
+    VTD::dma(Vs(b), [&](int r) { return vt + r * CH; }, wave, lane);
+    // every wave (the same bytes); lanes past DV / 4 repeat the last piece
+    dma16(Gs(b), a.Gam + (gcJ * Hkv + c) * DV + 4 * min(lane, DV / 4 - 1));
   };
 
   f32x16 acc[NB];
@@ -169,7 +172,9 @@ __global__ void __launch_bounds__(256, 2) k_fix_fwd(FwdArgs a) {
   __syncthreads();
   for (int J = 0; J < nJ; ++J) {
     const int b = J & 1;
-    if (J + 1 < nJ) stage_tile(J + 1, b ^ 1);
+    // The last step copies its own tile again into the idle buffer, so that
+    // every step issues the same copies.
+    stage_tile(min(J + 1, nJ - 1), b ^ 1);
     if (active && J < Iw - 1) {
       f32x16 sc[2];
 #pragma unroll
@@ -177,7 +182,7 @@ __global__ void __launch_bounds__(256, 2) k_fix_fwd(FwdArgs a) {
         sc[be] = zero16();
 #pragma unroll
         for (int i = 0; i < NS; ++i)
-          sc[be] = mma32(*(const kfrag *)(Ks[b] + KT::off(32 * be + n, 2 * i + hh)), qf[i], sc[be]);
+          sc[be] = mma32(*(const kfrag *)(Ks(b) + KT::off(32 * be + n, 2 * i + hh)), qf[i], sc[be]);
       }
       float mx = fmaxf(row_max(sc[0]), row_max(sc[1]));
       mx = max_across_halves(mx) * sl2;
@@ -191,12 +196,12 @@ __global__ void __launch_bounds__(256, 2) k_fix_fwd(FwdArgs a) {
           for (int i = 0; i < 8; ++i) pf[2 * be + u][i] = (_Float16)fast_exp2(sc[be][8 * u + i] * sl2 - m_used);
 #pragma unroll
       for (int bb = 0; bb < NB; ++bb) {
-        float gam = Gs[b][32 * bb + n];
+        float gam = Gs(b)[32 * bb + n];
 #pragma unroll
         for (int j = 0; j < 16; ++j) acc[bb][j] *= gam;
 #pragma unroll
         for (int t = 0; t < 4; ++t)
-          acc[bb] = mma32(pf[t], *(const f16x8 *)(Vs[b] + VT::off(32 * bb + n, 2 * t + hh)), acc[bb]);
+          acc[bb] = mma32(pf[t], *(const f16x8 *)(Vs(b) + VT::off(32 * bb + n, 2 * t + hh)), acc[bb]);
       }
     }
     wait_all();

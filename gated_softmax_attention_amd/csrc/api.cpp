@@ -94,9 +94,10 @@ struct BwdWs {
   fix::Plan plan;
   float *Gl2, *Gam;
   double *Lam;
-  _Float16 *Vr, *Qt, *Kt;
+  _Float16 *Vr, *Qt, *Kt, *VE;
   float *delta;
-  _Float16 *dh, *dht;
+  _Float16 *dh, *dht, *X16;
+  __bf16 *XH, *XL, *XTH, *XTL;
   float *mb, *sig, *qside, *dG, *dq_i, *dk_i, *dv_i, *dw_part, *dg_tot, *dg_carry;
 };
 
@@ -113,6 +114,12 @@ size_t carve_bwd(Carve &cv, const fix_attn_desc *d, BwdWs &w) {
   w.delta = cv.take<float>(T * Hq * DV);
   w.dh = cv.take<_Float16>(T * Hq * DV);
   w.dht = cv.take<_Float16>(ncb * Hq * DV * fix::CB);
+  w.VE = cv.take<_Float16>(T * Hkv * DV);
+  w.X16 = cv.take<_Float16>(T * Hq * DV);
+  w.XH = cv.take<__bf16>(T * Hq * DV);
+  w.XL = cv.take<__bf16>(T * Hq * DV);
+  w.XTH = cv.take<__bf16>(ncb * Hq * DV * fix::CB);
+  w.XTL = cv.take<__bf16>(ncb * Hq * DV * fix::CB);
   w.mb = cv.take<float>(T * Hq);
   w.sig = cv.take<float>(T * Hq);
   w.qside = cv.take<float>(T * Hkv * DV);
@@ -244,7 +251,7 @@ fix_status fix_attn_bwd(const fix_attn_desc *d, const void *q, const void *k, co
   e = trace_begin(st);
   if (e != hipSuccess) return hip_fail(e);
   FIX_TRY(fix::launch_plan(d->cu_seqlens, (int)s.nseq, (int)d->T, s.Ttot, w.plan, st), "plan");
-  FIX_TRY(fix::launch_gate_prep_rows(DV, g, v, f32in, w.plan, Hkv, ncb, w.Gl2, w.Gam, w.Vr, st), "gate_prep_rows");
+  FIX_TRY(fix::launch_gate_prep_rows(DV, g, v, f32in, w.plan, Hkv, ncb, w.Gl2, w.Gam, w.Vr, w.VE, st), "gate_prep_rows");
   FIX_TRY(fix::launch_chunk_logprefix(DV, w.Gl2, w.plan, Hkv, w.Lam, st), "chunk_logprefix");
   FIX_TRY(fix::launch_tiles_t(DK, q, f32in, w.plan, Hq, ncb, w.Qt, st), "tiles_q");
   FIX_TRY(fix::launch_tiles_t(DK, k, f32in, w.plan, Hkv, ncb, w.Kt, st), "tiles_k");
@@ -258,12 +265,14 @@ fix_status fix_attn_bwd(const fix_attn_desc *d, const void *q, const void *k, co
   pa.in_f32 = f32in;
   pa.delta = w.delta; pa.dh = w.dh; pa.dht = w.dht; pa.mb = w.mb; pa.sig = w.sig; pa.qside = w.qside;
   pa.dz = d_o_gate;
+  pa.X16 = w.X16; pa.XH = w.XH; pa.XL = w.XL; pa.XTH = w.XTH; pa.XTL = w.XTL;
   pa.dw_part = want_dw ? w.dw_part : nullptr;
   FIX_TRY(fix::launch_bwd_prep(DV, pa, ncb, st), "bwd_prep");
   fix::BwdArgs a;
   a.q = q; a.k = k; a.v = v;
   a.Gl2 = w.Gl2; a.Gam = w.Gam; a.Lam = w.Lam; a.Vr = w.Vr; a.Qt = w.Qt; a.Kt = w.Kt;
   a.delta = w.delta; a.dh = w.dh; a.dht = w.dht; a.mb = w.mb; a.sig = w.sig; a.qside = w.qside;
+  a.VE = w.VE; a.X16 = w.X16; a.XH = w.XH; a.XL = w.XL; a.XTH = w.XTH; a.XTL = w.XTL;
   a.dq_i = w.dq_i; a.dk_i = w.dk_i; a.dv_i = w.dv_i;
   a.dq = dq; a.dk = dk; a.dv = dv; a.dG = w.dG;
   a.plan = w.plan;

@@ -43,21 +43,23 @@ template <int D> struct Pad32 { static constexpr int value = D < 32 ? 32 : D; };
 // Exact per-pair decays for a diagonal 32x32 block whose gate range exceeds
 // 2^BGUARD (rare): dP for the pairs held by this lane, evaluated directly.
 // Register j of lane (hh, n) holds the pair (row q0 + rowof(j, n), key k0 + keyof(j, n)).
+// (Arguments by value: passing the kernel's argument struct by reference
+// would force a stack copy of it in every kernel that can call this.)
 template <int DV, bool F32IN, bool ROW_IS_LANE>
-__device__ __noinline__ void direct_dp(const BwdArgs &a, int64_t st, int c, int h, int L, int q0, int k0, int hh,
-                                       int n, float *dp) {
-  const int Hq = a.Hq, Hkv = a.Hkv;
+__device__ __noinline__ void direct_dp(const float *delta, const float *sig, const float *Gl2, const void *v, int Hq,
+                                       int Hkv, int64_t st, int c, int h, int L, int q0, int k0, int hh, int n,
+                                       float *dp) {
   for (int j = 0; j < 16; ++j) {
     const int r = ROW_IS_LANE ? n : acc_row(hh, j);
     const int kk = ROW_IS_LANE ? acc_row(hh, j) : n;
     const int qi = q0 + r, kj = k0 + kk;
     float t = 0.f;
     if (qi < L && kj <= qi) {
-      const float *dr = a.delta + ((st + qi) * Hq + h) * DV;
-      const float sg = a.sig[(st + qi) * Hq + h];
+      const float *dr = delta + ((st + qi) * Hq + h) * DV;
+      const float sg = sig[(st + qi) * Hq + h];
       for (int d = 0; d < DV; ++d) {
-        const float gq = a.Gl2[((st + qi) * Hkv + c) * DV + d], gk = a.Gl2[((st + kj) * Hkv + c) * DV + d];
-        t += dr[d] * sg * fast_exp2(gq - gk) * load_in(a.v, ((st + kj) * Hkv + c) * DV + d, F32IN);
+        const float gq = Gl2[((st + qi) * Hkv + c) * DV + d], gk = Gl2[((st + kj) * Hkv + c) * DV + d];
+        t += dr[d] * sg * fast_exp2(gq - gk) * load_in(v, ((st + kj) * Hkv + c) * DV + d, F32IN);
       }
     }
     dp[j] = t;
@@ -66,31 +68,45 @@ __device__ __noinline__ void direct_dp(const BwdArgs &a, int64_t st, int c, int 
 
 // ---------------------------------------------------------------------------
 // Within-chunk contributions to dq.  Workgroup = one 128-chunk of one q head;
-// wave w owns query rows c0 + 32w .. +31.  Key blocks b = 0..3 are staged in
-// LDS once for all waves: K rows, transposed K, the key operand scaled to the
-// end of the block (for rows of later blocks, <= 1, fp16) and the key
-// operand scaled from the token before the block (for the diagonal block,
-// >= 1, bf16 hi/lo).
+// wave w owns query rows c0 + 32w .. +31 (query block w).  Key blocks b are
+// copied into LDS one per step (double buffered): K rows, transposed K, and
+// V scaled to the end of its block (VE).  With E(b) the chunk-local log2
+// gate prefix at the end of block b (E(-1) = 0), the decay of a pair in
+// query block a > b splits as
+//     exp2(Gl_i - E(a-1)) * exp2(E(a-1) - E(b)) * exp2(E(b) - Gl_j),
+// all three <= 1: the first is the prepared block-relative dhat (X16), the
+// middle one gamma_ab multiplies the wave's dhat operand per channel, the
+// last is VE.  On the diagonal block the split is at the token before it:
+// the key side exp2(E(a-1) - Gl_j) >= 1 needs fp32 range and is multiplied
+// as bf16x3 (hi*hi + hi*lo + lo*hi); a block whose gate range exceeds
+// 2^BGUARD is evaluated with direct per-pair decays.
 // ---------------------------------------------------------------------------
 template <int DK, int DV, bool F32IN>
 __global__ void __launch_bounds__(256, 1) k_bwd_intra_dq(BwdArgs a) {
   using IF = InFrag<F32IN>;
   using kfrag = typename IF::type;
   constexpr int NS = DK / 16, NSV = DV / 16, DKP = Pad32<DK>::value, NBK = DKP / 32;
-  constexpr int KSTR = DK + 8, VSTR = DV + 8, TSTR = 32 + 8;
-  __shared__ __align__(16) uint16_t Ks[32 * KSTR];
-  __shared__ __align__(16) _Float16 Kts[DKP * TSTR];
-  __shared__ __align__(16) _Float16 Vo[32 * VSTR];
-  __shared__ __align__(16) __bf16 Vdh[32 * VSTR];
-  __shared__ __align__(16) __bf16 Vdl[32 * VSTR];
+  using KT = LdsTile<32, DK * 2>;   // K rows of the key block
+  using TT = LdsTile<DKP, 64>;     // transposed K, rows padded to DKP
+  using TTD = LdsTile<DK, 64>;
+  using VT = LdsTile<32, DV * 2>;  // VE rows of the key block
+  // One LDS object for every tile (see the forward kernel).
+  constexpr int O_K = 0, O_T = O_K + 2 * KT::BYTES, O_V = O_T + 2 * TT::BYTES, O_E = O_V + 2 * VT::BYTES;
+  __shared__ __align__(1024) char smem[O_E + 5 * DV * 4];
+  auto Ks = [&](int b) { return smem + O_K + b * KT::BYTES; };
+  auto Kts = [&](int b) { return smem + O_T + b * TT::BYTES; };
+  auto Vs = [&](int b) { return smem + O_V + b * VT::BYTES; };
+  float(*BE)[DV] = (float(*)[DV])(smem + O_E);  // BE[b + 1] = E(b), BE[0] = 0
+
   const Plan &pl = a.plan;
   const int gc = blockIdx.x, hq = blockIdx.y;
   if (gc >= pl.counts[0]) return;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hh = lane >> 5, n = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, n = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int s = seq_of_chunk(pl.cb128, pl.nseq, gc);
-  const int c0 = (gc - pl.cb128[s]) * CB;
-  const int L = pl.seq_len[s];
-  const int64_t st = pl.seq_start[s];
+  const int c0 = uniform((gc - pl.cb128[s]) * CB);
+  const int L = uniform(pl.seq_len[s]);
+  const int64_t st = uniform((int64_t)pl.seq_start[s]);
   const int Hq = a.Hq, Hkv = a.Hkv, c = hq / (Hq / Hkv);
   const int nblk = min(4, (L - c0 + 31) / 32);  // query (and key) blocks present in the chunk
   const int r0 = c0 + 32 * wave;
@@ -98,116 +114,154 @@ __global__ void __launch_bounds__(256, 1) k_bwd_intra_dq(BwdArgs a) {
   const bool active = wave < nblk;
   const bool rv = active && row < L;
   const float sl2 = a.sl2;
-  auto gl = [&](int tok, int d) { return tok < c0 ? 0.f : a.Gl2[((st + tok) * Hkv + c) * DV + d]; };
+  auto gl_at = [&](int tok, int d) { return a.Gl2[((st + tok) * Hkv + c) * DV + d]; };
 
+  for (int e = tid; e < 5 * DV; e += 256) {
+    const int b = e / DV - 1, d = e % DV;
+    BE[b + 1][d] = b < 0 ? 0.f : gl_at(min(c0 + 32 * b + 31, L - 1), d);
+  }
   if (DK < DKP)
-    for (int e = tid; e < (DKP - DK) * TSTR; e += 256) Kts[DK * TSTR + e] = (_Float16)0.f;
+    for (int e = tid; e < (DKP - DK) * 64 / 4; e += 256) {
+      ((uint32_t *)(Kts(0) + DK * 64))[e] = 0u;
+      ((uint32_t *)(Kts(1) + DK * 64))[e] = 0u;
+    }
   kfrag qf[NS];
+  f16x8 xr[NSV];  // the row's block-relative dhat, B operand of dP^T (k = channel)
 #pragma unroll
   for (int i = 0; i < NS; ++i)
     qf[i] = rv ? IF::load(a.q, ((st + row) * Hq + hq) * DK + 16 * i + 8 * hh) : IF::zero();
+#pragma unroll
+  for (int i = 0; i < NSV; ++i)
+    xr[i] = rv ? *(const f16x8 *)(a.X16 + ((st + row) * Hq + hq) * DV + 16 * i + 8 * hh)
+               : __builtin_bit_cast(f16x8, make_uint4(0, 0, 0, 0));
   const float mbn = rv ? a.mb[(st + row) * Hq + hq] : INFINITY;
-  const float sgn = rv ? a.sig[(st + row) * Hq + hq] : 0.f;
-  const float *drow = a.delta + ((st + (rv ? row : c0)) * Hq + hq) * DV;
   f32x16 acc[NBK];
 #pragma unroll
   for (int b = 0; b < NBK; ++b) acc[b] = zero16();
 
-  for (int b = 0; b < nblk; ++b) {
+  // Off-diagonal key blocks lie wholly before a valid query row: every key is valid.
+  uint32_t ok[KT::NW], ot[TTD::NW], ov[VT::NW];
+  KT::lane_offsets(Hkv * DK * 2, wave, lane, ok);
+  TTD::lane_offsets(CB * 2, wave, lane, ot);
+  VT::lane_offsets(Hkv * DV * 2, wave, lane, ov);
+  auto stage_tile = [&](int b, int buf) {
     const int kb = c0 + 32 * b;
-    // ---- stage key block b ----
-    __syncthreads();
-    for (int p = tid; p < 32 * DK / 8; p += 256) {
-      const int r = p / (DK / 8), e8 = p % (DK / 8);
-      *(uint4 *)&Ks[r * KSTR + 8 * e8] =
-          kb + r < L ? __builtin_bit_cast(uint4, IF::load(a.k, ((st + kb + r) * Hkv + c) * DK + 8 * e8))
-                     : make_uint4(0, 0, 0, 0);
-    }
-    const _Float16 *ktile = a.Kt + ((int64_t)gc * Hkv + c) * DK * CB + 32 * b;
-    for (int p = tid; p < DK * 4; p += 256) *(uint4 *)&Kts[(p >> 2) * TSTR + 8 * (p & 3)] = *(const uint4 *)(ktile + (p >> 2) * CB + 8 * (p & 3));
-    for (int e = tid; e < 32 * DV; e += 256) {
-      const int r = e / DV, d = e % DV, tok = kb + r;
-      float vo = 0.f, vd = 0.f;
-      if (tok < L) {
-        const float gk = gl(tok, d), vvv = load_in(a.v, ((st + tok) * Hkv + c) * DV + d, F32IN);
-        vo = fast_exp2(gl(min(kb + 31, L - 1), d) - gk) * vvv;
-        vd = fast_exp2(gl(kb - 1, d) - gk) * vvv;
+    const int64_t kr = (st + kb) * Hkv + c;
+    if constexpr (!F32IN) {
+      KT::dma(Ks(buf), make_rsrc((const uint16_t *)a.k + kr * DK, (int64_t)32 * Hkv * DK * 2), ok, wave);
+    } else {
+      for (int p = tid; p < KT::NCH; p += 256) {
+        const int r = p / KT::CPR, cc = p % KT::CPR;
+        *(f16x8 *)(Ks(buf) + KT::off(r, cc)) = IF::load(a.k, ((st + kb + r) * Hkv + c) * DK + 8 * cc);
       }
-      Vo[r * VSTR + d] = (_Float16)vo;
-      const __bf16 hi = (__bf16)vd;
-      Vdh[r * VSTR + d] = hi;
-      Vdl[r * VSTR + d] = (__bf16)(vd - (float)hi);
     }
-    __syncthreads();
-    if (!active || wave < b) continue;
-    const bool diag = wave == b;
-    const int ref = diag ? kb - 1 : kb + 31;
-    // S^T[key][row]
-    f32x16 sc = zero16();
+    TTD::dma(Kts(buf), make_rsrc(a.Kt + ((int64_t)gc * Hkv + c) * DK * CB + 32 * b, (int64_t)DK * CB * 2), ot, wave);
+    VT::dma(Vs(buf), make_rsrc(a.VE + kr * DV, (int64_t)32 * Hkv * DV * 2), ov, wave);
+  };
+
+  // Off-diagonal key blocks b < wave through LDS; block nblk - 1 is only
+  // ever diagonal, so it is not staged.
+  const int nsteps = nblk - 1;
+  if (nsteps > 0) stage_tile(0, 0);
+  wait_all();
+  __syncthreads();
+  for (int b = 0; b < nsteps; ++b) {
+    const int buf = b & 1;
+    const bool act = active && wave > b;
+    // gamma_ab (an LDS table) is applied before the next copies are issued:
+    // LDS reads that follow a copy issue in the same step can make the
+    // compiler wait for it.
+    f16x8 xg[NSV];
+    if (act) {
 #pragma unroll
-    for (int i = 0; i < NS; ++i) sc = mma32(*(const kfrag *)&Ks[n * KSTR + 16 * i + 8 * hh], qf[i], sc);
-    float p[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      p[j] = fast_exp2(sc[j] * sl2 - mbn);
-      if (diag && acc_row(hh, j) > n) p[j] = 0.f;
-    }
-    f32x16 dp = zero16();
-    if (!diag) {
-#pragma unroll
-      for (int sv = 0; sv < NSV; ++sv) {
-        f16x8 db;
+      for (int i = 0; i < NSV; ++i)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int d = 16 * sv + 8 * hh + e;
-          db[e] = (_Float16)(rv ? fast_exp2(gl(row, d) - gl(ref, d)) * drow[d] * sgn : 0.f);
+          const int d = 16 * i + 8 * hh + e;
+          xg[i][e] = (_Float16)((float)xr[i][e] * fast_exp2(BE[wave][d] - BE[b + 1][d]));
         }
-        dp = mma32(*(const f16x8 *)&Vo[n * VSTR + 16 * sv + 8 * hh], db, dp);
+    }
+    stage_tile(min(b + 1, nsteps - 1), buf ^ 1);
+    if (act) {
+      // S^T[key][row]: lane = row, register j = key acc_row(hh, j)
+      f32x16 sc = zero16(), dp = zero16();
+#pragma unroll
+      for (int i = 0; i < NS; ++i) sc = mma32(*(const kfrag *)(Ks(buf) + KT::off(n, 2 * i + hh)), qf[i], sc);
+#pragma unroll
+      for (int i = 0; i < NSV; ++i) dp = mma32(*(const f16x8 *)(Vs(buf) + VT::off(n, 2 * i + hh)), xg[i], dp);
+      f16x8 dsf[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dsf[u][i] = (_Float16)(fast_exp2(sc[8 * u + i] * sl2 - mbn) * dp[8 * u + i]);
+#pragma unroll
+      for (int bk = 0; bk < NBK; ++bk)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          acc[bk] = mma32(dsf[u], *(const f16x8 *)(Kts(buf) + TT::off(32 * bk + n, 2 * u + hh)), acc[bk]);
+    }
+    wait_all();
+    __syncthreads();
+  }
+  if (!active) return;
+  // Diagonal block, per wave from global memory (L2): keys kb .. kb + 31 of
+  // the wave's own block, split at the token before it (bf16x3).
+  {
+    const int kb = r0;
+    const int key = min(kb + n, L - 1);
+    float rng = 0.f;
+#pragma unroll
+    for (int i = 0; i < NSV; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int d = 16 * i + 8 * hh + e;
+        rng = fmaxf(rng, BE[wave][d] - BE[wave + 1][d]);
+      }
+    const bool direct = __any(rng > BGUARD);
+    f32x16 sc = zero16(), dp = zero16();
+#pragma unroll
+    for (int i = 0; i < NS; ++i)
+      sc = mma32(IF::load(a.k, ((st + key) * Hkv + c) * DK + 16 * i + 8 * hh), qf[i], sc);
+    if (!direct) {
+      const int64_t kr = ((st + key) * Hkv + c) * DV, xrw = ((st + min(row, L - 1)) * Hq + hq) * DV;
+#pragma unroll
+      for (int i = 0; i < NSV; ++i) {
+        bf16x8 vh, vl;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int d = 16 * i + 8 * hh + e;
+          const float val = kb + n < L ? fast_exp2(BE[wave][d] - a.Gl2[kr + d]) * load_in(a.v, kr + d, F32IN) : 0.f;
+          split_bf16(val, vh, vl, e);
+        }
+        const bf16x8 xh = *(const bf16x8 *)(a.XH + xrw + 16 * i + 8 * hh);
+        const bf16x8 xl = *(const bf16x8 *)(a.XL + xrw + 16 * i + 8 * hh);
+        dp = mma32(vh, xh, dp);
+        dp = mma32(vh, xl, dp);
+        dp = mma32(vl, xh, dp);
       }
     } else {
-      float rng = 0.f;
-      const int klast = min(kb + 31, L - 1);
+      float t[16];
+      direct_dp<DV, F32IN, true>(a.delta, a.sig, a.Gl2, a.v, Hq, Hkv, st, c, hq, L, r0, kb, hh, n, t);
 #pragma unroll
-      for (int sv = 0; sv < NSV; ++sv)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int d = 16 * sv + 8 * hh + e;
-          rng = fmaxf(rng, gl(ref, d) - gl(klast, d));
-        }
-      if (!__any(rng > BGUARD)) {
-#pragma unroll
-        for (int sv = 0; sv < NSV; ++sv) {
-          bf16x8 dh_, dl_;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int d = 16 * sv + 8 * hh + e;
-            split_bf16(rv ? fast_exp2(gl(row, d) - gl(ref, d)) * drow[d] * sgn : 0.f, dh_, dl_, e);
-          }
-          const bf16x8 vh = *(const bf16x8 *)&Vdh[n * VSTR + 16 * sv + 8 * hh];
-          const bf16x8 vl = *(const bf16x8 *)&Vdl[n * VSTR + 16 * sv + 8 * hh];
-          dp = mma32(vh, dh_, dp);
-          dp = mma32(vh, dl_, dp);
-          dp = mma32(vl, dh_, dp);
-        }
-      } else {
-        float t[16];
-        direct_dp<DV, F32IN, true>(a, st, c, hq, L, r0, kb, hh, n, t);
-#pragma unroll
-        for (int j = 0; j < 16; ++j) dp[j] = t[j];
-      }
+      for (int j = 0; j < 16; ++j) dp[j] = t[j];
     }
     f16x8 dsf[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) dsf[u][i] = (_Float16)(p[8 * u + i] * dp[8 * u + i]);
+      for (int i = 0; i < 8; ++i) {
+        const int j = 8 * u + i;
+        dsf[u][i] = (_Float16)(acc_row(hh, j) > n ? 0.f : fast_exp2(sc[j] * sl2 - mbn) * dp[j]);
+      }
+    const _Float16 *ktile = a.Kt + ((int64_t)gc * Hkv + c) * DK * CB + 32 * wave;
 #pragma unroll
-    for (int bk = 0; bk < NBK; ++bk)
+    for (int bk = 0; bk < NBK; ++bk) {
+      const int col = min(32 * bk + n, DK - 1);  // padded columns are never stored
 #pragma unroll
       for (int u = 0; u < 2; ++u)
-        acc[bk] = mma32(dsf[u], *(const f16x8 *)&Kts[(32 * bk + n) * TSTR + 16 * u + 8 * hh], acc[bk]);
+        acc[bk] = mma32(dsf[u], *(const f16x8 *)(ktile + (int64_t)col * CB + 16 * u + 8 * hh), acc[bk]);
+    }
   }
-  if (!active) return;
 #pragma unroll
   for (int bk = 0; bk < NBK; ++bk) {
     const int col = 32 * bk + n;
@@ -221,15 +275,22 @@ __global__ void __launch_bounds__(256, 1) k_bwd_intra_dq(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Near contributions to dk, dv: workgroup = one 128-chunk of one kv head;
-// wave w owns keys c0 + 32w .. +31, against the queries of the same chunk
-// and of the next one (the pairs with the largest decay weights), summed over
-// the head group.  For each query block, the query-side operands are staged
-// in LDS once for all waves: Q rows, transposed Q, and dx = exp(Gl_q -
-// Gl_ref) sigma delta with the split at the token before the block (<= 1),
-// as fp16 rows (dP off the diagonal), bf16 hi/lo rows (dP on the diagonal)
-// and bf16 hi/lo transposed (dV, always bf16x3: dv feeds the gate gradient,
-// whose suffix sums accumulate the rounding of every token).
+// Near contributions to dk, dv: workgroup = one 128-chunk J of one kv head;
+// wave w owns keys c0 + 32w .. +31 (key block w), against the query blocks
+// qa = 0..7 of chunk J and of the next chunk (the pairs with the largest
+// decay weights), summed over the head group.  Each step copies one query
+// block into LDS (double buffered): Q rows, transposed Q, the block-relative
+// dhat as fp16 rows (dP off the diagonal), bf16 hi/lo rows (dP on the
+// diagonal) and bf16 hi/lo transposed (dV, always bf16x3: dv feeds the gate
+// gradient, whose suffix sums accumulate the rounding of every token).  With
+// E(b) the log2 gate prefix at the end of block b, continued into the next
+// chunk, the decay of a pair in query block qa > w splits as
+//     exp2(Gl_i - E(qa-1)) * exp2(E(qa-1) - E(w)) * exp2(E(w) - Gl_j):
+// the first factor is in the staged dhat, the middle one gamma multiplies
+// the wave's V-to-block-end operand (dP) and each dV step's result per
+// channel, and the last one scales dV in the epilogue.  The diagonal block
+// uses gamma = exp2(E(w-1) - E(w)) >= 1 and V from the token before the
+// block, as in the dq kernel; past 2^BGUARD its pairs are evaluated directly.
 // ---------------------------------------------------------------------------
 template <int DK, int DV, bool F32IN>
 __global__ void __launch_bounds__(256, 1) k_bwd_intra_dkv(BwdArgs a) {
@@ -237,153 +298,252 @@ __global__ void __launch_bounds__(256, 1) k_bwd_intra_dkv(BwdArgs a) {
   using kfrag = typename IF::type;
   constexpr int NS = DK / 16, NSV = DV / 16, DKP = Pad32<DK>::value, DVP = Pad32<DV>::value;
   constexpr int NBK = DKP / 32, NBV = DVP / 32;
-  constexpr int QSTR = DK + 8, DSTR = DV + 8, TSTR = 32 + 8;
-  __shared__ __align__(16) uint16_t Qs[32 * QSTR];
-  __shared__ __align__(16) _Float16 Qts[DKP * TSTR];
-  __shared__ __align__(16) _Float16 Dr[32 * DSTR];
-  __shared__ __align__(16) __bf16 Drh[32 * DSTR];
-  __shared__ __align__(16) __bf16 Drl[32 * DSTR];
-  __shared__ __align__(16) __bf16 Dth[DVP * TSTR];
-  __shared__ __align__(16) __bf16 Dtl[DVP * TSTR];
-  __shared__ __align__(16) float Ms[32];
-  __shared__ __align__(16) float Gr[DVP];
+  using QT = LdsTile<32, DK * 2>;   // Q rows of the step
+  using QTT = LdsTile<DKP, 64>;     // transposed Q (dk rows x 32 queries)
+  using QTTD = LdsTile<DK, 64>;
+  using XR = LdsTile<32, DV * 2>;   // block-relative dhat rows (fp16)
+  using XTT = LdsTile<DVP, 64>;     // the same transposed (bf16 hi, lo), rows padded to DVP
+  using XTTD = LdsTile<DV, 64>;
+  // One LDS object for every tile (see the forward kernel).
+  constexpr int O_Q = 0, O_QT = O_Q + 2 * QT::BYTES, O_X = O_QT + 2 * QTT::BYTES;
+  constexpr int O_TH = O_X + 2 * XR::BYTES, O_TL = O_TH + 2 * XTT::BYTES;
+  constexpr int O_M = O_TL + 2 * XTT::BYTES, O_E = O_M + 2 * 256;
+  __shared__ __align__(1024) char smem[O_E + 9 * DV * 4];
+  auto Qs = [&](int b) { return smem + O_Q + b * QT::BYTES; };
+  auto Qts = [&](int b) { return smem + O_QT + b * QTT::BYTES; };
+  auto Xs = [&](int b) { return smem + O_X + b * XR::BYTES; };
+  auto Ths = [&](int b) { return smem + O_TH + b * XTT::BYTES; };
+  auto Tls = [&](int b) { return smem + O_TL + b * XTT::BYTES; };
+  auto Ms = [&](int b) { return (float *)(smem + O_M + b * 256); };  // 64 floats, 32 used
+  float(*BE)[DV] = (float(*)[DV])(smem + O_E);  // BE[b + 1] = E(b), b = -1..7
+
   const Plan &pl = a.plan;
   const int gc = blockIdx.x, c = blockIdx.y;
   if (gc >= pl.counts[0]) return;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hh = lane >> 5, n = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, n = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int s = seq_of_chunk(pl.cb128, pl.nseq, gc);
-  const int c0 = (gc - pl.cb128[s]) * CB;
-  const int L = pl.seq_len[s];
-  const int64_t st = pl.seq_start[s];
+  const int c0 = uniform((gc - pl.cb128[s]) * CB);
+  const int L = uniform(pl.seq_len[s]);
+  const int64_t st = uniform((int64_t)pl.seq_start[s]);
   const int Hq = a.Hq, Hkv = a.Hkv, G = Hq / Hkv;
   const int kb = c0 + 32 * wave;
   const bool active = kb < L;
   const int key = kb + n;
   const bool kv = key < L;
   const float sl2 = a.sl2;
-  // log2 prefix sums relative to the start of this chunk, continued into the next chunk
-  auto glx = [&](int tok, int d) {
-    if (tok < c0) return 0.f;
-    float gv = a.Gl2[((st + tok) * Hkv + c) * DV + d];
-    if (tok >= c0 + CB) gv += a.Gl2[((st + c0 + CB - 1) * Hkv + c) * DV + d];
-    return gv;
-  };
+  const int nqb = min(8, (L - c0 + 31) / 32);  // query blocks in this chunk and the next
+  auto gl_at = [&](int tok, int d) { return a.Gl2[((st + tok) * Hkv + c) * DV + d]; };
 
+  for (int e = tid; e < 9 * DV; e += 256) {
+    const int b = e / DV - 1, d = e % DV;
+    float v = 0.f;
+    if (b >= 0 && b < 4) v = gl_at(min(c0 + 32 * b + 31, L - 1), d);
+    if (b >= 4) {
+      v = gl_at(min(c0 + CB - 1, L - 1), d);
+      if (c0 + CB < L) v += gl_at(min(c0 + CB + 32 * (b - 4) + 31, L - 1), d);
+    }
+    BE[b + 1][d] = v;
+  }
   if (DK < DKP)
-    for (int e = tid; e < (DKP - DK) * TSTR; e += 256) Qts[DK * TSTR + e] = (_Float16)0.f;
+    for (int e = tid; e < (DKP - DK) * 64 / 4; e += 256) {
+      ((uint32_t *)(Qts(0) + DK * 64))[e] = 0u;
+      ((uint32_t *)(Qts(1) + DK * 64))[e] = 0u;
+    }
   if (DV < DVP)
-    for (int e = tid; e < (DVP - DV) * TSTR; e += 256) {
-      Dth[DV * TSTR + e] = (__bf16)0.f;
-      Dtl[DV * TSTR + e] = (__bf16)0.f;
+    for (int e = tid; e < (DVP - DV) * 64 / 4; e += 256) {
+      ((uint32_t *)(Ths(0) + DV * 64))[e] = 0u;
+      ((uint32_t *)(Ths(1) + DV * 64))[e] = 0u;
+      ((uint32_t *)(Tls(0) + DV * 64))[e] = 0u;
+      ((uint32_t *)(Tls(1) + DV * 64))[e] = 0u;
     }
   kfrag kf[NS];
+  f16x8 ve[NSV];  // the key's V to the end of its block, B operand of dP (k = channel)
 #pragma unroll
   for (int i = 0; i < NS; ++i)
     kf[i] = kv ? IF::load(a.k, ((st + key) * Hkv + c) * DK + 16 * i + 8 * hh) : IF::zero();
+#pragma unroll
+  for (int i = 0; i < NSV; ++i)
+    ve[i] = kv ? *(const f16x8 *)(a.VE + ((st + key) * Hkv + c) * DV + 16 * i + 8 * hh)
+               : __builtin_bit_cast(f16x8, make_uint4(0, 0, 0, 0));
   f32x16 accK[NBK], accV[NBV];
 #pragma unroll
   for (int b = 0; b < NBK; ++b) accK[b] = zero16();
 #pragma unroll
   for (int b = 0; b < NBV; ++b) accV[b] = zero16();
-  const int nqb = min(8, (L - c0 + 31) / 32);  // query blocks in this chunk and the next
 
-  for (int gq = 0; gq < G; ++gq) {
+  // Off-diagonal query blocks qa = 1 .. nqb - 1 of every head through LDS
+  // (block 0 is only ever diagonal); the diagonal blocks follow per wave.
+  const int nqo = nqb - 1;
+  const int nsteps = G * nqo;
+  // Rows past the end of the sequence read as zeros; their probabilities are
+  // masked to zero when the step is computed.
+  uint32_t oq[QT::NW], oqt[QTTD::NW], ox[XR::NW], oxt[XTTD::NW];
+  QT::lane_offsets(Hq * DK * 2, wave, lane, oq);
+  QTTD::lane_offsets(CB * 2, wave, lane, oqt);
+  XR::lane_offsets(Hq * DV * 2, wave, lane, ox);
+  XTTD::lane_offsets(CB * 2, wave, lane, oxt);
+  auto stage_tile = [&](int k, int buf) {
+    const int gq = k / nqo, qa = 1 + k % nqo;
     const int h = c * G + gq;
-    for (int qa = 0; qa < nqb; ++qa) {
-      const int q0 = c0 + 32 * qa;
-      const int ref = q0 - 1;  // token the decay is split at
-      // ---- stage query block qa ----
-      __syncthreads();
-      for (int p = tid; p < 32 * DK / 8; p += 256) {
-        const int r = p / (DK / 8), e8 = p % (DK / 8);
-        *(uint4 *)&Qs[r * QSTR + 8 * e8] =
-            q0 + r < L ? __builtin_bit_cast(uint4, IF::load(a.q, ((st + q0 + r) * Hq + h) * DK + 8 * e8))
-                       : make_uint4(0, 0, 0, 0);
+    const int q0 = c0 + 32 * qa;
+    const int64_t qr = (st + q0) * Hq + h;
+    const int nrow = L - q0;
+    if constexpr (!F32IN) {
+      QT::dma(Qs(buf), make_rsrc((const uint16_t *)a.q + qr * DK, (int64_t)nrow * Hq * DK * 2), oq, wave);
+    } else {
+      for (int p = tid; p < QT::NCH; p += 256) {
+        const int r = p / QT::CPR, cc = p % QT::CPR;
+        *(f16x8 *)(Qs(buf) + QT::off(r, cc)) = IF::load(a.q, ((st + min(q0 + r, L - 1)) * Hq + h) * DK + 8 * cc);
       }
-      const _Float16 *qtile = a.Qt + ((int64_t)(gc + (qa >> 2)) * Hq + h) * DK * CB + 32 * (qa & 3);
-      for (int p = tid; p < DK * 4; p += 256)
-        *(uint4 *)&Qts[(p >> 2) * TSTR + 8 * (p & 3)] = *(const uint4 *)(qtile + (p >> 2) * CB + 8 * (p & 3));
-      if (tid < 32) Ms[tid] = q0 + tid < L ? a.mb[(st + q0 + tid) * Hq + h] : INFINITY;
-      for (int d = tid; d < DV; d += 256) Gr[d] = glx(ref, d);
-      for (int e = tid; e < 32 * DV; e += 256) {
-        const int r = e / DV, d = e % DV, tok = q0 + r;
-        float dx = 0.f;
-        if (tok < L)
-          dx = fast_exp2(glx(tok, d) - glx(ref, d)) * a.delta[((st + tok) * Hq + h) * DV + d] *
-               a.sig[(st + tok) * Hq + h];
-        Dr[r * DSTR + d] = (_Float16)dx;
-        const __bf16 hi = (__bf16)dx, lo = (__bf16)(dx - (float)hi);
-        Drh[r * DSTR + d] = hi;
-        Drl[r * DSTR + d] = lo;
-        Dth[d * TSTR + key_pos(r)] = hi;
-        Dtl[d * TSTR + key_pos(r)] = lo;
-      }
-      __syncthreads();
-      if (!active || wave > qa) continue;
-      const bool diag = qa == wave;
-      // S[q][key]: lane = key, register j = query acc_row(hh, j)
-      f32x16 sc = zero16();
+    }
+    const int64_t ch = (int64_t)(gc + (qa >> 2)) * Hq + h;
+    QTTD::dma(Qts(buf), make_rsrc(a.Qt + ch * DK * CB + 32 * (qa & 3), (int64_t)DK * CB * 2), oqt, wave);
+    XR::dma(Xs(buf), make_rsrc(a.X16 + qr * DV, (int64_t)nrow * Hq * DV * 2), ox, wave);
+    XTTD::dma(Ths(buf), make_rsrc(a.XTH + ch * DV * CB + 32 * (qa & 3), (int64_t)DV * CB * 2), oxt, wave);
+    XTTD::dma(Tls(buf), make_rsrc(a.XTL + ch * DV * CB + 32 * (qa & 3), (int64_t)DV * CB * 2), oxt, wave);
+    // lane r fills Ms[r] (every wave, the same bytes)
+    dma4(Ms(buf), make_rsrc(a.mb + qr, (int64_t)nrow * Hq * 4), (uint32_t)lane * Hq * 4);
+  };
+
+  if (nsteps > 0) stage_tile(0, 0);
+  wait_all();
+  __syncthreads();
+  for (int k = 0; k < nsteps; ++k) {
+    const int buf = k & 1;
+    const int qa = 1 + k % nqo;
+    const int q0 = c0 + 32 * qa;
+    const bool act = active && qa > wave;
+    // LDS tables are read, and gamma applied, before the next copies are
+    // issued (LDS reads that follow a copy issue in the same step can make
+    // the compiler wait for it).
+    float4 mq[4];
 #pragma unroll
-      for (int i = 0; i < NS; ++i) sc = mma32(*(const kfrag *)&Qs[n * QSTR + 16 * i + 8 * hh], kf[i], sc);
-      float p[16];
+    for (int q4 = 0; q4 < 4; ++q4) mq[q4] = *(const float4 *)&Ms(buf)[8 * q4 + 4 * hh];
+    float gcol[NBV];  // gamma of the lane's dV output columns
+    f16x8 kop[NSV];   // V to block end (.) gamma, B operand of dP
+    if (act) {
+#pragma unroll
+      for (int bv = 0; bv < NBV; ++bv) {
+        const int d = min(32 * bv + n, DV - 1);
+        gcol[bv] = fast_exp2(BE[qa][d] - BE[wave + 1][d]);
+      }
+#pragma unroll
+      for (int i = 0; i < NSV; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int d = 16 * i + 8 * hh + e;
+          kop[i][e] = (_Float16)((float)ve[i][e] * fast_exp2(BE[qa][d] - BE[wave + 1][d]));
+        }
+    }
+    stage_tile(min(k + 1, nsteps - 1), buf ^ 1);
+    if (act) {
+      // S[q][key] and dP[q][key]: lane = key, register j = query acc_row(hh, j)
+      f32x16 sc = zero16(), dp = zero16();
+#pragma unroll
+      for (int i = 0; i < NS; ++i) sc = mma32(*(const kfrag *)(Qs(buf) + QT::off(n, 2 * i + hh)), kf[i], sc);
+#pragma unroll
+      for (int i = 0; i < NSV; ++i) dp = mma32(*(const f16x8 *)(Xs(buf) + XR::off(n, 2 * i + hh)), kop[i], dp);
+      f16x8 dsf[2];
+      bf16x8 ph[2], plo[2];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 mq = *(const float4 *)&Ms[8 * q4 + 4 * hh];
-        const float mv[4] = {mq.x, mq.y, mq.z, mq.w};
+        const float mv[4] = {mq[q4].x, mq[q4].y, mq[q4].z, mq[q4].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int j = 4 * q4 + e;
-          p[j] = fast_exp2(sc[j] * sl2 - mv[e]);
-          if (diag && acc_row(hh, j) < n) p[j] = 0.f;
+          const float pv = q0 + acc_row(hh, j) < L ? fast_exp2(sc[j] * sl2 - mv[e]) : 0.f;
+          dsf[j >> 3][j & 7] = (_Float16)(pv * dp[j]);
+          split_bf16(pv, ph[j >> 3], plo[j >> 3], j & 7);
         }
       }
-      // dP[q][key] = sum_d dx[q][d] Vx[key][d]
-      f32x16 dp = zero16();
-      bool direct = false;
-      if (!diag) {
+      // dV[key][d] += gamma[d] * sum_q P[q][key] dhat[q][d]  (bf16x3)
 #pragma unroll
-        for (int sv = 0; sv < NSV; ++sv) {
-          f16x8 vb;
+      for (int bv = 0; bv < NBV; ++bv) {
+        f32x16 tmp = zero16();
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int d = 16 * sv + 8 * hh + e;
-            vb[e] = (_Float16)(kv ? fast_exp2(Gr[d] - glx(key, d)) * load_in(a.v, ((st + key) * Hkv + c) * DV + d, F32IN) : 0.f);
-          }
-          dp = mma32(*(const f16x8 *)&Dr[n * DSTR + 16 * sv + 8 * hh], vb, dp);
+        for (int u = 0; u < 2; ++u) {
+          const bf16x8 th = *(const bf16x8 *)(Ths(buf) + XTT::off(32 * bv + n, 2 * u + hh));
+          const bf16x8 tl = *(const bf16x8 *)(Tls(buf) + XTT::off(32 * bv + n, 2 * u + hh));
+          tmp = mma32(ph[u], th, tmp);
+          tmp = mma32(ph[u], tl, tmp);
+          tmp = mma32(plo[u], th, tmp);
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) accV[bv][j] += gcol[bv] * tmp[j];
+      }
+      // dK[key][dk] += dS[q][key] Q[q][dk]
+#pragma unroll
+      for (int bk = 0; bk < NBK; ++bk)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          accK[bk] = mma32(dsf[u], *(const f16x8 *)(Qts(buf) + QTT::off(32 * bk + n, 2 * u + hh)), accK[bk]);
+    }
+    wait_all();
+    __syncthreads();
+  }
+  if (!active) return;
+
+  // Diagonal block (queries of the wave's own block), per head, from global
+  // memory (L2): the split is at the token before the block, gamma =
+  // exp2(E(w-1) - E(w)) >= 1, V from the token before the block as bf16x3.
+  bool dflag = false;  // exact diagonal contributions written to dv_i
+  {
+    float rng = 0.f, gd[NBV];
+#pragma unroll
+    for (int i = 0; i < NSV; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int d = 16 * i + 8 * hh + e;
+        rng = fmaxf(rng, BE[wave][d] - BE[wave + 1][d]);
+      }
+#pragma unroll
+    for (int bv = 0; bv < NBV; ++bv) {
+      const int d = min(32 * bv + n, DV - 1);
+      gd[bv] = fast_exp2(BE[wave][d] - BE[wave + 1][d]);
+    }
+    const bool direct = __any(rng > BGUARD);
+    bf16x8 vh[NSV], vl[NSV];
+    if (!direct) {
+      const int64_t kr = ((st + min(key, L - 1)) * Hkv + c) * DV;
+#pragma unroll
+      for (int i = 0; i < NSV; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int d = 16 * i + 8 * hh + e;
+          const float val = kv ? fast_exp2(BE[wave][d] - a.Gl2[kr + d]) * load_in(a.v, kr + d, F32IN) : 0.f;
+          split_bf16(val, vh[i], vl[i], e);
+        }
+    }
+    const int q0 = kb;
+    const int qrow = min(q0 + n, L - 1);  // A-operand row of this lane
+    for (int gq = 0; gq < G; ++gq) {
+      const int h = c * G + gq;
+      f32x16 sc = zero16(), dp = zero16();
+#pragma unroll
+      for (int i = 0; i < NS; ++i)
+        sc = mma32(IF::load(a.q, ((st + qrow) * Hq + h) * DK + 16 * i + 8 * hh), kf[i], sc);
+      float p[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int r = acc_row(hh, j);
+        p[j] = (q0 + r < L && r >= n) ? fast_exp2(sc[j] * sl2 - a.mb[(st + q0 + r) * Hq + h]) : 0.f;
+      }
+      if (!direct) {
+        const int64_t xrw = ((st + qrow) * Hq + h) * DV;
+#pragma unroll
+        for (int i = 0; i < NSV; ++i) {
+          const bf16x8 xh = *(const bf16x8 *)(a.XH + xrw + 16 * i + 8 * hh);
+          const bf16x8 xl = *(const bf16x8 *)(a.XL + xrw + 16 * i + 8 * hh);
+          dp = mma32(xh, vh[i], dp);
+          dp = mma32(xl, vh[i], dp);
+          dp = mma32(xh, vl[i], dp);
         }
       } else {
-        float rng = 0.f;
-        const int klast = min(kb + 31, L - 1);
+        float t[16];
+        direct_dp<DV, F32IN, false>(a.delta, a.sig, a.Gl2, a.v, Hq, Hkv, st, c, h, L, q0, kb, hh, n, t);
 #pragma unroll
-        for (int sv = 0; sv < NSV; ++sv)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int d = 16 * sv + 8 * hh + e;
-            rng = fmaxf(rng, Gr[d] - glx(klast, d));
-          }
-        direct = __any(rng > BGUARD);
-        if (!direct) {
-#pragma unroll
-          for (int sv = 0; sv < NSV; ++sv) {
-            bf16x8 vh, vl;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int d = 16 * sv + 8 * hh + e;
-              split_bf16(kv ? fast_exp2(Gr[d] - glx(key, d)) * load_in(a.v, ((st + key) * Hkv + c) * DV + d, F32IN) : 0.f,
-                         vh, vl, e);
-            }
-            const bf16x8 dh_ = *(const bf16x8 *)&Drh[n * DSTR + 16 * sv + 8 * hh];
-            const bf16x8 dl_ = *(const bf16x8 *)&Drl[n * DSTR + 16 * sv + 8 * hh];
-            dp = mma32(dh_, vh, dp);
-            dp = mma32(dl_, vh, dp);
-            dp = mma32(dh_, vl, dp);
-          }
-        } else {
-          float t[16];
-          direct_dp<DV, F32IN, false>(a, st, c, h, L, q0, kb, hh, n, t);
-#pragma unroll
-          for (int j = 0; j < 16; ++j) dp[j] = t[j];
-        }
+        for (int j = 0; j < 16; ++j) dp[j] = t[j];
       }
       f16x8 dsf[2];
       bf16x8 ph[2], plo[2];
@@ -394,64 +554,70 @@ __global__ void __launch_bounds__(256, 1) k_bwd_intra_dkv(BwdArgs a) {
           dsf[u][i] = (_Float16)(p[8 * u + i] * dp[8 * u + i]);
           split_bf16(p[8 * u + i], ph[u], plo[u], i);
         }
-      // dV[key][dv] += F[key][dv] * sum_q P[q][key] dx[q][dv], F = exp(Gl_ref - Gl_key) the key
-      // side of the split decay (<= 1 off the diagonal block, >= 1 on it)
+      const int64_t qtb = ((int64_t)gc * Hq + h) * DK * CB + 32 * wave;
+      const int64_t xtb = ((int64_t)gc * Hq + h) * DV * CB + 32 * wave;
       if (!direct) {
 #pragma unroll
         for (int bv = 0; bv < NBV; ++bv) {
-          const int col = 32 * bv + n;
+          const int col = min(32 * bv + n, DV - 1);  // padded columns are never stored
           f32x16 tmp = zero16();
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
-            const bf16x8 th = *(const bf16x8 *)&Dth[col * TSTR + 16 * u + 8 * hh];
-            const bf16x8 tl = *(const bf16x8 *)&Dtl[col * TSTR + 16 * u + 8 * hh];
+            const bf16x8 th = *(const bf16x8 *)(a.XTH + xtb + (int64_t)col * CB + 16 * u + 8 * hh);
+            const bf16x8 tl = *(const bf16x8 *)(a.XTL + xtb + (int64_t)col * CB + 16 * u + 8 * hh);
             tmp = mma32(ph[u], th, tmp);
             tmp = mma32(ph[u], tl, tmp);
             tmp = mma32(plo[u], th, tmp);
           }
-          if (col < DV) {
-            const float grc = Gr[col];
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-              const int kj = kb + acc_row(hh, j);
-              const float f = kj < L ? fast_exp2(grc - glx(kj, col)) : 0.f;
-              accV[bv][j] += f * tmp[j];
-            }
-          }
+          for (int j = 0; j < 16; ++j) accV[bv][j] += gd[bv] * tmp[j];
         }
       } else {
-        // exact per-pair decays: P[q][kj] lives in lane kj, register of q
+        // exact per-pair decays, written straight to the within-chunk partial
+        // (this wave owns these keys): P[q][kj] lives in lane kj, register of q
+#pragma unroll
+        for (int bv = 0; bv < NBV; ++bv) {
+          const int col = 32 * bv + n;
+          float t[16];
+#pragma unroll
+          for (int j = 0; j < 16; ++j) t[j] = 0.f;
 #pragma unroll 1
-        for (int qq = 0; qq < 32; ++qq) {
-          const int qk = q0 + qq;
-          const int jsrc = (qq >> 3) * 4 + (qq & 3), hsrc = (qq >> 2) & 1;
-          float pj = 0.f;
+          for (int qq = 0; qq < 32; ++qq) {
+            const int qk = q0 + qq;
+            const int jsrc = (qq >> 3) * 4 + (qq & 3), hsrc = (qq >> 2) & 1;
+            float pj = 0.f;
 #pragma unroll
-          for (int j = 0; j < 16; ++j) pj = (j == jsrc) ? p[j] : pj;
-#pragma unroll
-          for (int bv = 0; bv < NBV; ++bv) {
-            const int col = 32 * bv + n;
+            for (int j = 0; j < 16; ++j) pj = (j == jsrc) ? p[j] : pj;
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
               const int kl = acc_row(hh, j);
               const float pv = __shfl(pj, kl + 32 * hsrc);
               const int kj = kb + kl;
               if (col < DV && qk < L && kj <= qk)
-                accV[bv][j] += pv * fast_exp2(glx(qk, col) - glx(kj, col)) *
-                               a.delta[((st + qk) * Hq + h) * DV + col] * a.sig[(st + qk) * Hq + h];
+                t[j] += pv * fast_exp2(gl_at(qk, col) - gl_at(kj, col)) * a.delta[((st + qk) * Hq + h) * DV + col] *
+                        a.sig[(st + qk) * Hq + h];
+            }
+          }
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int kj = kb + acc_row(hh, j);
+            if (col < DV && kj < L) {
+              const int64_t idx = ((st + kj) * Hkv + c) * DV + col;
+              a.dv_i[idx] = (dflag ? a.dv_i[idx] : 0.f) + t[j];
             }
           }
         }
+        dflag = true;
       }
-      // dK[key][dk] += dS[q][key] Q[q][dk]
 #pragma unroll
-      for (int bk = 0; bk < NBK; ++bk)
+      for (int bk = 0; bk < NBK; ++bk) {
+        const int col = min(32 * bk + n, DK - 1);
 #pragma unroll
         for (int u = 0; u < 2; ++u)
-          accK[bk] = mma32(dsf[u], *(const f16x8 *)&Qts[(32 * bk + n) * TSTR + 16 * u + 8 * hh], accK[bk]);
+          accK[bk] = mma32(dsf[u], *(const f16x8 *)(a.Qt + qtb + (int64_t)col * CB + 16 * u + 8 * hh), accK[bk]);
+      }
     }
   }
-  if (!active) return;
 #pragma unroll
   for (int bk = 0; bk < NBK; ++bk) {
     const int col = 32 * bk + n;
@@ -462,22 +628,29 @@ __global__ void __launch_bounds__(256, 1) k_bwd_intra_dkv(BwdArgs a) {
       if (kj < L) a.dk_i[((st + kj) * Hkv + c) * DK + col] = a.scale * accK[bk][j];
     }
   }
+  // dv relative to the end of the key's block: exp2(E(w) - Gl_j)
 #pragma unroll
   for (int bv = 0; bv < NBV; ++bv) {
     const int col = 32 * bv + n;
     if (col >= DV) continue;
+    const float ew = BE[wave + 1][col];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int kj = kb + acc_row(hh, j);
-      if (kj < L) a.dv_i[((st + kj) * Hkv + c) * DV + col] = accV[bv][j];
+      if (kj < L) {
+        const int64_t idx = ((st + kj) * Hkv + c) * DV + col;
+        a.dv_i[idx] = fast_exp2(ew - a.Gl2[idx]) * accV[bv][j] + (dflag ? a.dv_i[idx] : 0.f);
+      }
     }
   }
 }
 
 // ---------------------------------------------------------------------------
 // dq from key chunks before the query chunk.  Workgroup = 128 query rows of
-// one q head (4 waves x 32 rows); key chunks are visited from the last to the
-// first, 32 keys per step copied straight into LDS (double buffered): K rows
+// one q head (4 waves x 32 rows); key chunks are visited from the first on
+// (so the workgroups of a head, started together, read the same key chunk at
+// the same time and share it in L2), 32 keys per step copied straight into
+// LDS (double buffered): K rows
 // (bf16) for S^T, transposed K (fp16) for dS.K, and V scaled to its chunk
 // end (fp16) for dP^T.  The decay product between the chunks, gamma_IJ =
 // exp2(Lam[I-1] - Lam[J]), multiplies the query-side operand (the scaled
@@ -547,21 +720,25 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdArgs a) {
   auto lam_of = [&](int J) { return a.Lam[((int64_t)(cbs + J) * Hkv + c) * DV + dt]; };
 
   const int nsteps = 4 * I;
+  uint32_t ok[KT::NW], ot[TTD::NW], ov[VT::NW];
+  KT::lane_offsets(Hkv * DK * 2, wave, lane, ok);
+  TTD::lane_offsets(CB * 2, wave, lane, ot);
+  VT::lane_offsets(DV * 2, wave, lane, ov);
   auto stage_tile = [&](int k, int b) {
-    const int J = I - 1 - (k >> 2), u = k & 3;
+    const int J = k >> 2, u = k & 3;
     const int kt0 = J * CB + 32 * u;
     if constexpr (!F32IN) {
-      KT::dma(Ks(b), [&](int r) { return (const uint16_t *)a.k + ((st + kt0 + r) * Hkv + c) * DK; }, wave, lane);
+      KT::dma(Ks(b), make_rsrc((const uint16_t *)a.k + ((st + kt0) * Hkv + c) * DK, (int64_t)32 * Hkv * DK * 2), ok,
+              wave);
     } else {
       for (int p = tid; p < KT::NCH; p += 256) {
         const int r = p / KT::CPR, cc = p % KT::CPR;
         *(f16x8 *)(Ks(b) + KT::off(r, cc)) = IF::load(a.k, ((st + kt0 + r) * Hkv + c) * DK + 8 * cc);
       }
     }
-    const _Float16 *ktile = a.Kt + ((int64_t)(cbs + J) * Hkv + c) * DK * CB + 32 * u;
-    TTD::dma(Kts(b), [&](int r) { return ktile + r * CB; }, wave, lane);
-    const _Float16 *vtile = a.Vr + ((int64_t)(cbs + J) * Hkv + c) * CB * DV + (32 * u) * DV;
-    VT::dma(Vs(b), [&](int r) { return vtile + r * DV; }, wave, lane);
+    const int64_t ch = (int64_t)(cbs + J) * Hkv + c;
+    TTD::dma(Kts(b), make_rsrc(a.Kt + ch * DK * CB + 32 * u, (int64_t)DK * CB * 2), ot, wave);
+    VT::dma(Vs(b), make_rsrc(a.Vr + (ch * CB + 32 * u) * DV, 32 * DV * 2), ov, wave);
   };
 
   // The unscaled dhat rows are loaded at the end of the step before each key
@@ -571,7 +748,7 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdArgs a) {
   f16x8 raw[NSV];
   if (nsteps > 0) {
     stage_tile(0, 0);
-    if (tid < DV) gam(0)[tid] = fast_exp2((float)(lamI - lam_of(I - 1)));
+    if (tid < DV) gam(0)[tid] = fast_exp2((float)(lamI - lam_of(0)));
 #pragma unroll
     for (int i = 0; i < NSV; ++i) raw[i] = *(const f16x8 *)(dhrow + 16 * i + 8 * hh);
   }
@@ -593,7 +770,7 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdArgs a) {
     // Same copies and loads on every step (the last step re-copies its own
     // tile into the idle buffer; the Lam row index is kept valid).
     stage_tile(min(k + 1, nsteps - 1), b ^ 1);
-    const double lamJ = lam_of(max(I - 2 - (k >> 2), 0));
+    const double lamJ = lam_of(min((k >> 2) + 1, I - 1));
     {
       f32x16 sc = zero16(), dp = zero16();
 #pragma unroll
@@ -728,28 +905,34 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
     }
   };
   auto ord_of = [&](int k) { return k < G * ns1 ? 0 : 1 + (k - G * ns1) / (4 * G); };
-  // Rows past the end of the sequence are copied from its last row (finite
-  // values); their probabilities are masked to zero when the step is computed.
+  // Rows past the end of the sequence read as zeros; their probabilities are
+  // masked to zero when the step is computed.
+  uint32_t oq[QT::NW], oqt[QTTD::NW], od[DR::NW], odt[DTTD::NW];
+  QT::lane_offsets(Hq * DK * 2, wave, lane, oq);
+  QTTD::lane_offsets(CB * 2, wave, lane, oqt);
+  DR::lane_offsets(Hq * DV * 2, wave, lane, od);
+  DTTD::lane_offsets(CB * 2, wave, lane, odt);
   auto stage_tile = [&](int k, int b) {
     int I, gq, u;
     step_of(k, I, gq, u);
     const int h = c * G + gq;
     const int qt0 = I * CB + 32 * u;
-    auto qrow = [&](int r) { return st + min(qt0 + r, L - 1); };
+    const int64_t qr = (st + qt0) * Hq + h;
+    const int nrow = L - qt0;
     if constexpr (!F32IN) {
-      QT::dma(Qs(b), [&](int r) { return (const uint16_t *)a.q + (qrow(r) * Hq + h) * DK; }, wave, lane);
+      QT::dma(Qs(b), make_rsrc((const uint16_t *)a.q + qr * DK, (int64_t)nrow * Hq * DK * 2), oq, wave);
     } else {
       for (int p = tid; p < QT::NCH; p += 256) {
         const int r = p / QT::CPR, cc = p % QT::CPR;
-        *(f16x8 *)(Qs(b) + QT::off(r, cc)) = IF::load(a.q, (qrow(r) * Hq + h) * DK + 8 * cc);
+        *(f16x8 *)(Qs(b) + QT::off(r, cc)) = IF::load(a.q, ((st + min(qt0 + r, L - 1)) * Hq + h) * DK + 8 * cc);
       }
     }
-    const _Float16 *qtile = a.Qt + ((int64_t)(cbs + I) * Hq + h) * DK * CB + 32 * u;
-    QTTD::dma(Qts(b), [&](int r) { return qtile + r * CB; }, wave, lane);
-    DR::dma(Ds(b), [&](int r) { return a.dh + (qrow(r) * Hq + h) * DV; }, wave, lane);
-    const _Float16 *dtile = a.dht + ((int64_t)(cbs + I) * Hq + h) * DV * CB + 32 * u;
-    DTTD::dma(Dts(b), [&](int r) { return dtile + r * CB; }, wave, lane);
-    dma4(Ms(b), a.mb + qrow(lane) * Hq + h);  // lane r fills Ms[r] (every wave, the same bytes)
+    const int64_t ch = (int64_t)(cbs + I) * Hq + h;
+    QTTD::dma(Qts(b), make_rsrc(a.Qt + ch * DK * CB + 32 * u, (int64_t)DK * CB * 2), oqt, wave);
+    DR::dma(Ds(b), make_rsrc(a.dh + qr * DV, (int64_t)nrow * Hq * DV * 2), od, wave);
+    DTTD::dma(Dts(b), make_rsrc(a.dht + ch * DV * CB + 32 * u, (int64_t)DV * CB * 2), odt, wave);
+    // lane r fills Ms[r] (every wave, the same bytes)
+    dma4(Ms(b), make_rsrc(a.mb + qr, (int64_t)nrow * Hq * 4), (uint32_t)lane * Hq * 4);
   };
 
   // gamma_IJ[d] for d = tid (threads tid < DV).
@@ -758,7 +941,9 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
   auto lam_of = [&](int I) { return a.Lam[((int64_t)(cbs + I - 1) * Hkv + c) * DV + dt]; };
 
   if (nsteps > 0) {
-    VRT::dma(smem + O_V, [&](int r) { return a.Vr + (((int64_t)(cbs + J) * Hkv + c) * CB + r) * DV; }, wave, lane);
+    uint32_t ovr[VRT::NW];
+    VRT::lane_offsets(DV * 2, wave, lane, ovr);
+    VRT::dma(smem + O_V, make_rsrc(a.Vr + ((int64_t)(cbs + J) * Hkv + c) * CB * DV, (int64_t)CB * DV * 2), ovr, wave);
     stage_tile(0, 0);
     if (tid < DV) gam(0)[tid] = fast_exp2((float)(lam_of(I1) - lamJ));
   }

@@ -22,12 +22,15 @@
 
 namespace fix {
 
-// Gl2 (log2 units, 128-chunk local), Gam per 128-chunk, and row-major fp16
-// V scaled to its chunk end: Vr[chunk][kvh][t][d] = exp(Gl_end - Gl_t) v_t.
+// Gl2 (log2 units, 128-chunk local), Gam per 128-chunk, row-major fp16 V
+// scaled to its chunk end, Vr[chunk][kvh][t][d] = exp(Gl_end - Gl_t) v_t, and
+// V scaled to the end of its 32-token block, VE[t][kvh][d] (the block end
+// clamped to the sequence end).
 template <int DV>
 __global__ void __launch_bounds__(128) k_gate_prep_rows(const float *__restrict__ g, const void *__restrict__ v,
                                                         bool in_f32, Plan plan, int Hkv, float *__restrict__ Gl2,
-                                                        float *__restrict__ Gam, _Float16 *__restrict__ Vr) {
+                                                        float *__restrict__ Gam, _Float16 *__restrict__ Vr,
+                                                        _Float16 *__restrict__ VE) {
   const int gc = blockIdx.x, c = blockIdx.y, d = threadIdx.x;
   if (gc >= plan.counts[0] || d >= DV) return;
   const int s = seq_of_chunk(plan.cb128, plan.nseq, gc);
@@ -47,7 +50,10 @@ __global__ void __launch_bounds__(128) k_gate_prep_rows(const float *__restrict_
     float val = 0.f;
     if (j < n) {
       int64_t idx = ((tok0 + j) * Hkv + c) * DV + d;
-      val = fast_exp2(acc - Gl2[idx]) * load_in(v, idx, in_f32);
+      const float gj = Gl2[idx], vj = load_in(v, idx, in_f32);
+      val = fast_exp2(acc - gj) * vj;
+      const float gbe = Gl2[((tok0 + min((j | 31), n - 1)) * Hkv + c) * DV + d];
+      VE[idx] = (_Float16)(fast_exp2(gbe - gj) * vj);
     }
     dst[(int64_t)j * DV] = (_Float16)val;
   }
@@ -103,6 +109,7 @@ __global__ void __launch_bounds__(256) k_bwd_prep(PrepArgs a) {
   constexpr int STR = CB + 8;
   constexpr int PER = (DV + 63) / 64;  // channels per lane
   __shared__ _Float16 tile[DV * STR];
+  __shared__ __bf16 tileh[DV * STR], tilel[DV * STR];
   const int gc = blockIdx.x, c = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   if (gc >= a.plan.counts[0]) return;
   const Plan &pl = a.plan;
@@ -176,9 +183,19 @@ __global__ void __launch_bounds__(256) k_bwd_prep(PrepArgs a) {
             // owned by this thread for every head of the group
             const int64_t qi = (tok * Hkv + c) * DV + d;
             a.qside[qi] = (gq == 0 ? 0.f : a.qside[qi]) + del[k] * xv[k];
-            _Float16 hv = (_Float16)(fast_exp2(a.Gl2[(tok * Hkv + c) * DV + d]) * del[k] * sg);
+            const float gl = a.Gl2[(tok * Hkv + c) * DV + d];
+            _Float16 hv = (_Float16)(fast_exp2(gl) * del[k] * sg);
             a.dh[rb + d] = hv;
             tile[d * STR + key_pos(t)] = hv;
+            // relative to the token before the row's 32-token block (<= 1)
+            const float gbs = (t & ~31) ? a.Gl2[((tok0 + (t & ~31) - 1) * Hkv + c) * DV + d] : 0.f;
+            const float xb = fast_exp2(gl - gbs) * del[k] * sg;
+            const __bf16 xh = (__bf16)xb, xl = (__bf16)(xb - (float)xh);
+            a.X16[rb + d] = (_Float16)xb;
+            a.XH[rb + d] = xh;
+            a.XL[rb + d] = xl;
+            tileh[d * STR + key_pos(t)] = xh;
+            tilel[d * STR + key_pos(t)] = xl;
           }
         }
         if (lane == 0) {
@@ -189,15 +206,22 @@ __global__ void __launch_bounds__(256) k_bwd_prep(PrepArgs a) {
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
           int d = lane + 64 * k;
-          if (d < DV) tile[d * STR + key_pos(t)] = (_Float16)0.f;
+          if (d < DV) {
+            tile[d * STR + key_pos(t)] = (_Float16)0.f;
+            tileh[d * STR + key_pos(t)] = (__bf16)0.f;
+            tilel[d * STR + key_pos(t)] = (__bf16)0.f;
+          }
         }
       }
     }
     __syncthreads();
-    uint4 *dst = (uint4 *)(a.dht + ((int64_t)gc * Hq + h) * DV * CB);
+    const int64_t tb = ((int64_t)gc * Hq + h) * DV * CB;
+    uint4 *dst = (uint4 *)(a.dht + tb), *dsth = (uint4 *)(a.XTH + tb), *dstl = (uint4 *)(a.XTL + tb);
     for (int e = tid; e < DV * CB / 8; e += 256) {
       int d = e / (CB / 8), p8 = e % (CB / 8);
       dst[e] = *(const uint4 *)&tile[d * STR + 8 * p8];
+      dsth[e] = *(const uint4 *)&tileh[d * STR + 8 * p8];
+      dstl[e] = *(const uint4 *)&tilel[d * STR + 8 * p8];
     }
     __syncthreads();
   }
@@ -283,10 +307,10 @@ __global__ void __launch_bounds__(128) k_dg_final(const float *__restrict__ dG, 
   }
 
 hipError_t launch_gate_prep_rows(int dv, const float *g, const void *v, bool in_f32, const Plan &plan, int Hkv,
-                                 int ncb_ub, float *Gl2, float *Gam, _Float16 *Vr, hipStream_t st) {
+                                 int ncb_ub, float *Gl2, float *Gam, _Float16 *Vr, _Float16 *VE, hipStream_t st) {
   dim3 grid(ncb_ub, Hkv);
   FIX_DV_SWITCH(dv, hipLaunchKernelGGL(k_gate_prep_rows<DVC>, grid, dim3(128), 0, st, g, v, in_f32, plan, Hkv,
-                                       Gl2, Gam, Vr));
+                                       Gl2, Gam, Vr, VE));
   return hipGetLastError();
 }
 

@@ -38,7 +38,15 @@ __device__ inline int seq_of_chunk(const int *base, int nseq, int gc) {
     int mid = (lo + hi + 1) >> 1;
     if (base[mid] <= gc) lo = mid; else hi = mid - 1;
   }
-  return lo;
+  return __builtin_amdgcn_readfirstlane(lo);  // the same in every lane (gc is per workgroup)
+}
+
+// Values that are the same in every lane, marked so for the compiler (they
+// then live in SGPRs, as buffer resources built from them must).
+__device__ inline int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ inline int64_t uniform(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x), hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
 // Position of key j (0..63) inside a transposed V tile: the two middle
@@ -100,52 +108,71 @@ __device__ inline uint16_t f32_to_bf16_rne(float f) {
 }
 
 // ---- LDS tiles filled by direct global->LDS copies ----
-// gfx950's global_load_lds_dwordx4 moves 16 bytes per lane from global memory
-// straight into LDS, the wave's 64 pieces landing contiguously (1 KB) at the
-// wave-uniform base, piece of lane l at base + 16 l.  Tiles are therefore
-// unpadded, [ROWS][RB bytes], and the 16-byte chunk c of row r is stored at
-// chunk position c ^ swz(r): for the MFMA operand reads (32 lanes reading the
-// same chunk of 32 consecutive rows) every 16 lanes then hit 16 distinct
-// 16-byte bank groups, with no padding.  `wave` must be wave-uniform (an
-// SGPR value) so that the copies are issued under uniform control flow.
+// gfx950's buffer_load_dwordx4 ... lds moves 16 bytes per lane from global
+// memory straight into LDS, the wave's 64 pieces landing contiguously (1 KB)
+// at the wave-uniform base, piece of lane l at base + 16 l.  The source is a
+// buffer resource (base and byte count in SGPRs) plus a 32-bit per-lane
+// offset: a tile's per-lane offsets are fixed for a kernel (computed once),
+// the per-step base goes into the resource, and offsets at or past the
+// resource's byte count read as zeros (rows past the end of a sequence).
+//
+// Tiles are unpadded, [ROWS][RB bytes], and the 16-byte chunk c of row r is
+// stored at chunk position c ^ swz(r): for the MFMA operand reads (32 lanes
+// reading the same chunk of 32 consecutive rows) every 16 lanes then hit 16
+// distinct 16-byte bank groups, with no padding.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Buffer resource over [base, base + bytes) (raw, stride 0).  Both are the
+// same in every lane wherever it is used; that is asserted to the compiler
+// so that the resource lives in SGPRs.
+__device__ inline rsrc_t make_rsrc(const void *base, int64_t bytes) {
+  const int nrec = (int)(bytes < 0 ? 0 : bytes > 0x7fffffffLL ? 0x7fffffffLL : bytes);
+  const uint64_t b = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b), hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc((void *)(((uint64_t)hi << 32) | lo), (short)0,
+                                           __builtin_amdgcn_readfirstlane(nrec), 0x00020000);
+}
+
 template <int ROWS, int RB> struct LdsTile {
   static constexpr int CPR = RB / 16;     // 16-byte chunks per row (2..16)
   static constexpr int NCH = ROWS * CPR;  // chunks per tile
   static constexpr int BYTES = ROWS * RB;
   static_assert(CPR >= 2 && CPR <= 16 && NCH % 64 == 0, "tile shape");
-  __device__ static int swz(int r) { return (r / (16 / CPR)) % CPR; }
-  __device__ static int off(int r, int c) { return r * RB + ((c ^ swz(r)) << 4); }
-  // Copy the tile: rowptr(r) gives the global address of row r (RB contiguous
-  // bytes).  Every wave issues the same number of copies, NW (a wave with
-  // nothing left repeats a piece another wave copies, same bytes to the same
-  // place), so that the number of loads in flight never depends on the path
-  // taken: the compiler's wait counts stay exact instead of falling back to
-  // waiting for everything.
+  // Every wave issues the same number of copies, NW (a wave with nothing left
+  // repeats a piece another wave copies, same bytes to the same place), so
+  // that the number of loads in flight never depends on the path taken: the
+  // compiler's wait counts stay exact instead of falling back to waiting for
+  // everything.
   static constexpr int NI = NCH / 64;             // 1 KB wave copies per tile
   static constexpr int NW = NI < 4 ? 1 : (NI + 3) / 4;
-  template <class RowPtr>
-  __device__ static void dma(char *lds, RowPtr rowptr, int wave, int lane) {
+  __device__ static int swz(int r) { return (r / (16 / CPR)) % CPR; }
+  __device__ static int off(int r, int c) { return r * RB + ((c ^ swz(r)) << 4); }
+  __device__ static int piece(int t, int wave) { return NI < 4 ? wave % NI : min(wave + 4 * t, NI - 1); }
+  // This lane's source offsets in a global tile whose rows are `stride` bytes apart.
+  __device__ static void lane_offsets(uint32_t stride, int wave, int lane, uint32_t (&o)[NW]) {
 #pragma unroll
     for (int t = 0; t < NW; ++t) {
-      const int idx = NI < 4 ? wave % NI : min(wave + 4 * t, NI - 1);
-      const int p = idx * 64 + lane, r = p / CPR, pc = p % CPR;
-      const char *src = (const char *)rowptr(r) + ((pc ^ swz(r)) << 4);
-      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)src,
-                                       (void __attribute__((address_space(3))) *)(lds + idx * 1024), 16, 0, 0);
+      const int p = piece(t, wave) * 64 + lane, r = p / CPR, pc = p % CPR;
+      o[t] = (uint32_t)r * stride + (uint32_t)((pc ^ swz(r)) << 4);
     }
+  }
+  // Copy the tile.  `wave` must be wave-uniform (an SGPR value).
+  __device__ static void dma(char *lds, rsrc_t src, const uint32_t (&o)[NW], int wave) {
+#pragma unroll
+    for (int t = 0; t < NW; ++t)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (void __attribute__((address_space(3))) *)(lds + piece(t, wave) * 1024),
+                                               16, o[t], 0, 0, 0);
   }
 };
 
-// One direct copy of 16 bytes per lane; lane l's piece lands at lds + 16 l.
-// Issue it under wave-uniform control flow only.
-__device__ inline void dma16(void *lds, const void *src) {
-  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)src,
-                                   (void __attribute__((address_space(3))) *)lds, 16, 0, 0);
+// One copy of 16 (or 4) bytes per lane from a buffer resource at byte offset
+// `o`; lane l's piece lands at lds + 16 l (lds + 4 l).  Wave-uniform control
+// flow only.
+__device__ inline void dma16(void *lds, rsrc_t src, uint32_t o) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (void __attribute__((address_space(3))) *)lds, 16, o, 0, 0, 0);
 }
-// The same with 4 bytes per lane, landing at lds + 4 l.
-__device__ inline void dma4(void *lds, const void *src) {
-  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)src,
-                                   (void __attribute__((address_space(3))) *)lds, 4, 0, 0);
+__device__ inline void dma4(void *lds, rsrc_t src, uint32_t o) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (void __attribute__((address_space(3))) *)lds, 4, o, 0, 0, 0);
 }
 
 // Wait for every outstanding memory operation of the wave (direct LDS copies included).

@@ -96,8 +96,8 @@ __global__ void __launch_bounds__(256, 2) k_fix_fwd(FwdArgs a) {
   for (int i = 0; i < NS; ++i)
     qf[i] = (active && qrow < L) ? IF::load(a.q, ((st + qrow) * Hq + hq) * DK + 16 * i + 8 * hh) : IF::zero();
 
-  // Padding rows of narrow Vt tiles stay zero; their Gam entries stay one.
-  // (Their Gam entries only scale accumulator columns that stay zero.)
+  // Padding rows of narrow Vt tiles stay zero (their Gam entries, zero too,
+  // only scale accumulator columns that stay zero).
   if (DV < DVP) {
     for (int e = tid; e < (DVP - DV) * CH * 2 / 4; e += 256) {
       ((uint32_t *)(Vs(0) + DV * CH * 2))[e] = 0u;
@@ -107,20 +107,23 @@ __global__ void __launch_bounds__(256, 2) k_fix_fwd(FwdArgs a) {
 
   // Stage key chunk J into LDS buffer b: direct copies for bf16 inputs; fp32
   // inputs are converted to fp16 through registers into the same layout.
+  uint32_t ok[KT::NW], ov[VTD::NW];
+  KT::lane_offsets(Hkv * DK * 2, wave, lane, ok);
+  VTD::lane_offsets(CH * 2, wave, lane, ov);
   auto stage_tile = [&](int J, int b) {
     const int64_t gcJ = cb + J;
     if constexpr (!F32IN) {
-      KT::dma(Ks(b), [&](int r) { return (const uint16_t *)a.k + ((st + J * CH + r) * Hkv + c) * DK; }, wave, lane);
+      const int64_t kr = (st + J * CH) * Hkv + c;
+      KT::dma(Ks(b), make_rsrc((const uint16_t *)a.k + kr * DK, (int64_t)(L - J * CH) * Hkv * DK * 2), ok, wave);
     } else {
       for (int p = tid; p < KT::NCH; p += 256) {
         const int r = p / KT::CPR, cc = p % KT::CPR;
         *(f16x8 *)(Ks(b) + KT::off(r, cc)) = IF::load(a.k, ((st + J * CH + r) * Hkv + c) * DK + 8 * cc);
       }
     }
-    const _Float16 *vt = a.VtT + (gcJ * Hkv + c) * DV * CH;
-    VTD::dma(Vs(b), [&](int r) { return vt + r * CH; }, wave, lane);
-    // every wave (the same bytes); lanes past DV / 4 repeat the last piece
-    dma16(Gs(b), a.Gam + (gcJ * Hkv + c) * DV + 4 * min(lane, DV / 4 - 1));
+    VTD::dma(Vs(b), make_rsrc(a.VtT + (gcJ * Hkv + c) * DV * CH, DV * CH * 2), ov, wave);
+    // every wave (the same bytes); lanes past DV / 4 read zeros
+    dma16(Gs(b), make_rsrc(a.Gam + (gcJ * Hkv + c) * DV, DV * 4), 16 * lane);
   };
 
   f32x16 acc[NB];

@@ -31,6 +31,12 @@ struct BwdArgs {
   const _Float16 *dh, *dht;    // sigma * exp(Gl) * delta, rows and transposed tiles
   const float *mb, *sig;       // [T, Hq] m log2e - e, sigma = 2^-e
   const float *qside;          // [T, Hkv, DV]
+  // Operands of the pairs in the same or the adjacent chunk, relative to
+  // 32-token blocks (blocks tile every 128-chunk):
+  const _Float16 *VE;          // [T, Hkv, DV] exp(Gl_blockend - Gl_j) v_j
+  const _Float16 *X16;         // [T, Hq, DV] exp(Gl_i - Gl_blockstart-1) sigma delta_i
+  const __bf16 *XH, *XL;       // the same, bf16 hi and lo parts
+  const __bf16 *XTH, *XTL;     // [chunk][Hq][DV][CB] transposed hi / lo tiles (key_pos order)
   float *dq_i, *dk_i, *dv_i;   // within-chunk contributions (fp32)
   void *dq, *dk, *dv;          // outputs (out dtype)
   float *dG;                   // [T, Hkv, DV] gradient with respect to the prefix sums of g
@@ -54,6 +60,9 @@ struct PrepArgs {
   float *qside;        // [Ttot, Hkv, DV] sum over the group of delta (.) x
   void *dz;            // [Ttot, Hq, DV] out dtype, or null
   float *dw_part;      // [chunks * Hkv][DV] per-block partial sums of dn (.) xh, or null
+  _Float16 *X16;       // [Ttot, Hq, DV] sigma * exp(Gl - Gl at the token before the 32-block) * delta
+  __bf16 *XH, *XL;     // the same as bf16 hi / lo parts
+  __bf16 *XTH, *XTL;   // [chunk][Hq][DV][CB] hi / lo transposed (key_pos order)
 };
 
 hipError_t launch_plan(const int64_t *cu, int nseq, int T, int64_t Ttot, const Plan &plan, hipStream_t st);
@@ -75,7 +84,7 @@ inline hipError_t launch_fwd(int dk, int dv, bool f32in, const FwdArgs &a, int g
 }
 
 hipError_t launch_gate_prep_rows(int dv, const float *g, const void *v, bool in_f32, const Plan &plan, int Hkv,
-                                 int ncb_ub, float *Gl2, float *Gam, _Float16 *Vr, hipStream_t st);
+                                 int ncb_ub, float *Gl2, float *Gam, _Float16 *Vr, _Float16 *VE, hipStream_t st);
 hipError_t launch_chunk_logprefix(int dv, const float *Gl2, const Plan &plan, int Hkv, double *Lam, hipStream_t st);
 hipError_t launch_tiles_t(int D, const void *in, bool in_f32, const Plan &plan, int H, int ncb_ub, _Float16 *out,
                           hipStream_t st);

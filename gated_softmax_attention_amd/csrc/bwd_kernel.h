@@ -772,11 +772,28 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdArgs a) {
     stage_tile(min(k + 1, nsteps - 1), b ^ 1);
     const double lamJ = lam_of(min((k >> 2) + 1, I - 1));
     {
+      // Operands of a group of products are read from LDS in one batch (one
+      // wait for all of them rather than one per product).
+      kfrag ka[NS];
+#pragma unroll
+      for (int i = 0; i < NS; ++i) ka[i] = *(const kfrag *)(Ks(b) + KT::off(n, 2 * i + hh));
+      __builtin_amdgcn_sched_barrier(0);
       f32x16 sc = zero16(), dp = zero16();
 #pragma unroll
-      for (int i = 0; i < NS; ++i) sc = mma32(*(const kfrag *)(Ks(b) + KT::off(n, 2 * i + hh)), qf[i], sc);
+      for (int i = 0; i < NS; ++i) sc = mma32(ka[i], qf[i], sc);
+      __builtin_amdgcn_sched_barrier(0);
+      f16x8 va[NSV];
 #pragma unroll
-      for (int i = 0; i < NSV; ++i) dp = mma32(*(const f16x8 *)(Vs(b) + VT::off(n, 2 * i + hh)), dhf[i], dp);
+      for (int i = 0; i < NSV; ++i) va[i] = *(const f16x8 *)(Vs(b) + VT::off(n, 2 * i + hh));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < NSV; ++i) dp = mma32(va[i], dhf[i], dp);
+      __builtin_amdgcn_sched_barrier(0);
+      f16x8 tk[NBK][2];
+#pragma unroll
+      for (int bk = 0; bk < NBK; ++bk)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) tk[bk][u] = *(const f16x8 *)(Kts(b) + TT::off(32 * bk + n, 2 * u + hh));
       f16x8 dsf[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u)
@@ -785,11 +802,11 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdArgs a) {
           const int j = 8 * u + i;
           dsf[u][i] = (_Float16)(fast_exp2(sc[j] * sl2 - mbn) * dp[j]);
         }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int bk = 0; bk < NBK; ++bk)
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-          acc[bk] = mma32(dsf[u], *(const f16x8 *)(Kts(b) + TT::off(32 * bk + n, 2 * u + hh)), acc[bk]);
+        for (int u = 0; u < 2; ++u) acc[bk] = mma32(dsf[u], tk[bk][u], acc[bk]);
     }
     // gamma of the next chunk, into the other buffer (its last readers passed
     // the barrier that began this chunk).
@@ -820,14 +837,14 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdArgs a) {
 // dk, dv from query chunks two or more after the key chunk.  Workgroup = the
 // 128 keys of one key chunk J and kv head (4 waves x 32 keys), visiting the
 // query chunks from the last to J + 2 and, within each, the G query heads of
-// the group, 32 query rows per step copied straight into LDS (double
-// buffered): Q rows, transposed Q, scaled dhat rows and transposed scaled
-// dhat.  The decay product between the chunks, gamma_IJ = exp2(Lam[I-1] -
-// Lam[J]), enters both products through per-chunk operands: V (.) gamma_IJ
-// (rebuilt per query chunk from an LDS copy of the chunk's V rows) for dP,
-// and the transposed dhat times gamma_IJ[d] (a per-lane factor, d being the
-// lane's output column) for dV, so the accumulators are only ever touched by
-// MFMAs.  gamma_IJ is computed into LDS during the step before its chunk.
+// the group, 32 query rows per step copied straight into LDS, three steps in
+// flight: Q rows, transposed Q, scaled dhat rows and transposed scaled dhat.
+// The decay product between the chunks, gamma_IJ = exp2(Lam[I-1] - Lam[J]),
+// enters both products through per-chunk operands: V (.) gamma_IJ (rebuilt
+// per query chunk from an LDS copy of the chunk's V rows) for dP, and the
+// transposed dhat times gamma_IJ[d] (a per-lane factor, d being the lane's
+// output column) for dV, so the accumulators are only ever touched by MFMAs.
+// gamma_IJ is computed into LDS during the step before its chunk.
 // ---------------------------------------------------------------------------
 template <int DK, int DV, bool F32IN>
 __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
@@ -835,6 +852,8 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
   using kfrag = typename IF::type;
   constexpr int NS = DK / 16, NSV = DV / 16, DKP = Pad32<DK>::value, DVP = Pad32<DV>::value;
   constexpr int NBK = DKP / 32, NBV = DVP / 32;
+  constexpr int NB = 2;             // LDS stages
+  constexpr int DIST = NB - 1;      // steps copied ahead of the one computed
   using QT = LdsTile<32, DK * 2>;   // Q rows of the step
   using QTT = LdsTile<DKP, 64>;     // transposed Q (dk rows x 32 queries)
   using QTTD = LdsTile<DK, 64>;
@@ -842,9 +861,13 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
   using DTT = LdsTile<DVP, 64>;     // scaled dhat, transposed
   using DTTD = LdsTile<DV, 64>;
   using VRT = LdsTile<CB, DV * 2>;  // the key chunk's V rows, scaled to the chunk end
+  // Loads a step issues after its copies' predecessors: the copies themselves
+  // (fixed per wave) and nothing else, so waiting for the next step's copies
+  // is waiting until this many are left in flight.
+  constexpr int NCOPY = F32IN ? QTTD::NW + DR::NW + DTTD::NW + 1 : QT::NW + QTTD::NW + DR::NW + DTTD::NW + 1;
   // One LDS object for every tile (see the forward kernel).
-  constexpr int O_Q = 0, O_QT = O_Q + 2 * QT::BYTES, O_D = O_QT + 2 * QTT::BYTES, O_DT = O_D + 2 * DR::BYTES;
-  constexpr int O_V = O_DT + 2 * DTT::BYTES, O_M = O_V + VRT::BYTES, O_G = O_M + 2 * 256;
+  constexpr int O_Q = 0, O_QT = O_Q + NB * QT::BYTES, O_D = O_QT + NB * QTT::BYTES, O_DT = O_D + NB * DR::BYTES;
+  constexpr int O_V = O_DT + NB * DTT::BYTES, O_M = O_V + VRT::BYTES, O_G = O_M + NB * 256;
   __shared__ __align__(1024) char smem[O_G + 2 * DVP * 4];
   auto Qs = [&](int b) { return smem + O_Q + b * QT::BYTES; };
   auto Qts = [&](int b) { return smem + O_QT + b * QTT::BYTES; };
@@ -859,10 +882,10 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
   const int rank = blockIdx.x / Hkv;
   if (rank >= pl.counts[0]) return;
   const int2 it = pl.qitems[pl.counts[0] - 1 - rank];  // earliest chunks (most queries after them) first
-  const int s = it.x, J = it.y;
-  const int64_t st = pl.seq_start[s];
-  const int L = pl.seq_len[s];
-  const int cbs = pl.cb128[s];
+  const int s = uniform(it.x), J = uniform(it.y);
+  const int64_t st = uniform((int64_t)pl.seq_start[s]);
+  const int L = uniform(pl.seq_len[s]);
+  const int cbs = uniform(pl.cb128[s]);
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, n = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kb = J * CB + 32 * wave;
@@ -872,39 +895,39 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
 
   const int nch = (L + CB - 1) / CB;
   const int I0 = J + 2, I1 = nch - 1;                  // query chunks visited: I1 down to I0
-  const int ns1 = (L - I1 * CB + 31) / 32;              // steps of the last (possibly partial) chunk
+  const int ns1 = (L - I1 * CB + 31) / 32;              // slices of the last (possibly partial) chunk
   const int nsteps = I0 <= I1 ? G * ns1 + 4 * G * (I1 - I0) : 0;
   kfrag kf[NS];
 #pragma unroll
   for (int i = 0; i < NS; ++i)
     kf[i] = kv ? IF::load(a.k, ((st + key) * Hkv + c) * DK + 16 * i + 8 * hh) : IF::zero();
-  if (DK < DKP)
-    for (int e = tid; e < (DKP - DK) * 64 / 4; e += 256) {
-      ((uint32_t *)(Qts(0) + DK * 64))[e] = 0u;
-      ((uint32_t *)(Qts(1) + DK * 64))[e] = 0u;
-    }
-  if (DV < DVP)
-    for (int e = tid; e < (DVP - DV) * 64 / 4; e += 256) {
-      ((uint32_t *)(Dts(0) + DV * 64))[e] = 0u;
-      ((uint32_t *)(Dts(1) + DV * 64))[e] = 0u;
-    }
+  for (int b = 0; b < NB; ++b) {
+    if (DK < DKP)
+      for (int e = tid; e < (DKP - DK) * 64 / 4; e += 256) ((uint32_t *)(Qts(b) + DK * 64))[e] = 0u;
+    if (DV < DVP)
+      for (int e = tid; e < (DVP - DV) * 64 / 4; e += 256) ((uint32_t *)(Dts(b) + DV * 64))[e] = 0u;
+  }
   f32x16 accK[NBK], accV[NBV];
 #pragma unroll
   for (int b = 0; b < NBK; ++b) accK[b] = zero16();
 #pragma unroll
   for (int b = 0; b < NBV; ++b) accV[b] = zero16();
 
-  // Step k -> query chunk I, query head of the group gq, 32-row slice u; and
-  // the ordinal of its chunk among the visited ones (0 for I1).
-  auto step_of = [&](int k, int &I, int &gq, int &u) {
-    if (k < G * ns1) {
-      I = I1; gq = k / ns1; u = k % ns1;
-    } else {
-      const int r = k - G * ns1;
-      I = I1 - 1 - r / (4 * G); gq = (r % (4 * G)) >> 2; u = r & 3;
+  // Step position: query chunk I, query head of the group gq, 32-row slice
+  // u, and the ordinal of the chunk among the visited ones (0 for I1).
+  struct Pos {
+    int I, gq, u, ord;
+  };
+  auto advance = [&](Pos &p) {
+    if (++p.u == (p.I == I1 ? ns1 : 4)) {
+      p.u = 0;
+      if (++p.gq == G) {
+        p.gq = 0;
+        --p.I;
+        ++p.ord;
+      }
     }
   };
-  auto ord_of = [&](int k) { return k < G * ns1 ? 0 : 1 + (k - G * ns1) / (4 * G); };
   // Rows past the end of the sequence read as zeros; their probabilities are
   // masked to zero when the step is computed.
   uint32_t oq[QT::NW], oqt[QTTD::NW], od[DR::NW], odt[DTTD::NW];
@@ -912,25 +935,23 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
   QTTD::lane_offsets(CB * 2, wave, lane, oqt);
   DR::lane_offsets(Hq * DV * 2, wave, lane, od);
   DTTD::lane_offsets(CB * 2, wave, lane, odt);
-  auto stage_tile = [&](int k, int b) {
-    int I, gq, u;
-    step_of(k, I, gq, u);
-    const int h = c * G + gq;
-    const int qt0 = I * CB + 32 * u;
+  auto stage_tile = [&](const Pos &p, int b) {
+    const int h = c * G + p.gq;
+    const int qt0 = p.I * CB + 32 * p.u;
     const int64_t qr = (st + qt0) * Hq + h;
     const int nrow = L - qt0;
     if constexpr (!F32IN) {
       QT::dma(Qs(b), make_rsrc((const uint16_t *)a.q + qr * DK, (int64_t)nrow * Hq * DK * 2), oq, wave);
     } else {
-      for (int p = tid; p < QT::NCH; p += 256) {
-        const int r = p / QT::CPR, cc = p % QT::CPR;
+      for (int e = tid; e < QT::NCH; e += 256) {
+        const int r = e / QT::CPR, cc = e % QT::CPR;
         *(f16x8 *)(Qs(b) + QT::off(r, cc)) = IF::load(a.q, ((st + min(qt0 + r, L - 1)) * Hq + h) * DK + 8 * cc);
       }
     }
-    const int64_t ch = (int64_t)(cbs + I) * Hq + h;
-    QTTD::dma(Qts(b), make_rsrc(a.Qt + ch * DK * CB + 32 * u, (int64_t)DK * CB * 2), oqt, wave);
+    const int64_t ch = (int64_t)(cbs + p.I) * Hq + h;
+    QTTD::dma(Qts(b), make_rsrc(a.Qt + ch * DK * CB + 32 * p.u, (int64_t)DK * CB * 2), oqt, wave);
     DR::dma(Ds(b), make_rsrc(a.dh + qr * DV, (int64_t)nrow * Hq * DV * 2), od, wave);
-    DTTD::dma(Dts(b), make_rsrc(a.dht + ch * DV * CB + 32 * u, (int64_t)DV * CB * 2), odt, wave);
+    DTTD::dma(Dts(b), make_rsrc(a.dht + ch * DV * CB + 32 * p.u, (int64_t)DV * CB * 2), odt, wave);
     // lane r fills Ms[r] (every wave, the same bytes)
     dma4(Ms(b), make_rsrc(a.mb + qr, (int64_t)nrow * Hq * 4), (uint32_t)lane * Hq * 4);
   };
@@ -940,56 +961,89 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
   const double lamJ = a.Lam[((int64_t)(cbs + J) * Hkv + c) * DV + dt];
   auto lam_of = [&](int I) { return a.Lam[((int64_t)(cbs + I - 1) * Hkv + c) * DV + dt]; };
 
+  Pos cur{I1, 0, 0, 0}, ahead{I1, 0, 0, 0};  // the step computed, the step being copied
   if (nsteps > 0) {
     uint32_t ovr[VRT::NW];
     VRT::lane_offsets(DV * 2, wave, lane, ovr);
     VRT::dma(smem + O_V, make_rsrc(a.Vr + ((int64_t)(cbs + J) * Hkv + c) * CB * DV, (int64_t)CB * DV * 2), ovr, wave);
-    stage_tile(0, 0);
     if (tid < DV) gam(0)[tid] = fast_exp2((float)(lam_of(I1) - lamJ));
+    for (int k = 0; k < DIST; ++k) {  // steps 0 .. DIST - 1 (the last step again past the end)
+      stage_tile(ahead, k);
+      if (k + 1 < nsteps) advance(ahead);
+    }
+    // `ahead` is now step DIST (or the last step)
   }
   wait_all();
   __syncthreads();
 
   f16x8 vf[NSV];        // key-side dP operand V (.) gamma_IJ, rebuilt per query chunk
   _Float16 gh[NBV];     // gamma_IJ of the lane's dV output columns
+  int prev_ord = -1;
   for (int k = 0; k < nsteps; ++k) {
-    const int b = k & 1;
-    int I, gq, u;
-    step_of(k, I, gq, u);
-    const int ord = ord_of(k);
-    const bool first = k == 0 || ord != ord_of(k - 1);
-    const bool next_chunk = k + 1 < nsteps && ord_of(k + 1) != ord;
-    if (first) {  // before this step issues copies (see the dq kernel)
-      const float *gm = gam(ord & 1);
+    const int b = k % NB;
+    const int I = cur.I, qt0 = I * CB + 32 * cur.u;
+    if (cur.ord != prev_ord) {  // first step of a query chunk
+      prev_ord = cur.ord;
+      const float *gm = gam(cur.ord & 1);
 #pragma unroll
       for (int i = 0; i < NSV; ++i) {
-        const f16x8 raw = *(const f16x8 *)(smem + O_V + VRT::off(32 * wave + n, 2 * i + hh));
-        const float4 g0 = *(const float4 *)(gm + 16 * i + 8 * hh), g1 = *(const float4 *)(gm + 16 * i + 8 * hh + 4);
-        const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+        uint4 r, g0, g1, gc;
+        lds_read4(r, g0, g1, gc, smem + O_V + VRT::off(32 * wave + n, 2 * i + hh), gm + 16 * i + 8 * hh,
+                  gm + 16 * i + 8 * hh + 4, gm + min(32 * (i & (NBV - 1)) + n, DV - 1));
+        const f16x8 raw = __builtin_bit_cast(f16x8, r);
+        const float4 a0 = __builtin_bit_cast(float4, g0), a1 = __builtin_bit_cast(float4, g1);
+        const float gv[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) vf[i][e] = (_Float16)((float)raw[e] * gv[e]);
+        // gamma of the lane's dV column 32 bv + n (bv = i for the first NBV i)
+        if (i < NBV) gh[i] = 32 * i + n < DV ? (_Float16)__uint_as_float(gc.x) : (_Float16)0.f;
       }
-#pragma unroll
-      for (int bv = 0; bv < NBV; ++bv) gh[bv] = 32 * bv + n < DV ? (_Float16)gm[32 * bv + n] : (_Float16)0.f;
     }
-    float4 mq[4];  // exponent offsets of the step's rows, read before the copies are issued
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) mq[q4] = *(const float4 *)&Ms(b)[8 * q4 + 4 * hh];
-    // Same copies and loads on every step (the last step re-copies its own
-    // tile into the idle buffer; the Lam row index is kept valid).
-    const int kn = min(k + 1, nsteps - 1);
-    int In, gn, un;
-    step_of(kn, In, gn, un);
-    const double lamI = lam_of(In);
-    stage_tile(kn, b ^ 1);
-    const int qt0 = I * CB + 32 * u;
+    float4 mq[4];  // exponent offsets of the step's rows
     {
-      // S[q][key] and dP[q][key]: lane = key, register j = query acc_row(hh, j)
+      uint4 m0, m1, m2, m3;
+      lds_read4(m0, m1, m2, m3, &Ms(b)[4 * hh], &Ms(b)[8 + 4 * hh], &Ms(b)[16 + 4 * hh], &Ms(b)[24 + 4 * hh]);
+      mq[0] = __builtin_bit_cast(float4, m0);
+      mq[1] = __builtin_bit_cast(float4, m1);
+      mq[2] = __builtin_bit_cast(float4, m2);
+      mq[3] = __builtin_bit_cast(float4, m3);
+    }
+    // The position after this step: its chunk's gamma is due at the end of
+    // this step if the chunk changes.
+    Pos nxt = cur;
+    if (k + 1 < nsteps) advance(nxt);
+    const bool next_chunk = nxt.ord != cur.ord;
+    const double lamI = lam_of(nxt.I);
+    // Copies of step k + DIST (the last step again near the end, so that
+    // every step issues the same copies); `ahead` is that step's position.
+    stage_tile(ahead, (k + DIST) % NB);
+    if (k + DIST + 1 < nsteps) advance(ahead);
+    {
+      // S[q][key] and dP[q][key]: lane = key, register j = query acc_row(hh, j).
+      // Operands of a group of products are read from LDS in one batch (one
+      // wait for all of them rather than one per product).
+      kfrag qa[NS];
+      f16x8 da[NSV];
+#pragma unroll
+      for (int i = 0; i < NS; ++i) qa[i] = *(const kfrag *)(Qs(b) + QT::off(n, 2 * i + hh));
+#pragma unroll
+      for (int i = 0; i < NSV; ++i) da[i] = *(const f16x8 *)(Ds(b) + DR::off(n, 2 * i + hh));
+      __builtin_amdgcn_sched_barrier(0);
       f32x16 sc = zero16(), dp = zero16();
 #pragma unroll
-      for (int i = 0; i < NS; ++i) sc = mma32(*(const kfrag *)(Qs(b) + QT::off(n, 2 * i + hh)), kf[i], sc);
+      for (int i = 0; i < NS; ++i) sc = mma32(qa[i], kf[i], sc);
 #pragma unroll
-      for (int i = 0; i < NSV; ++i) dp = mma32(*(const f16x8 *)(Ds(b) + DR::off(n, 2 * i + hh)), vf[i], dp);
+      for (int i = 0; i < NSV; ++i) dp = mma32(da[i], vf[i], dp);
+      __builtin_amdgcn_sched_barrier(0);
+      f16x8 ta[NBV][2], tq[NBK][2];
+#pragma unroll
+      for (int bv = 0; bv < NBV; ++bv)
+#pragma unroll
+        for (int uu = 0; uu < 2; ++uu) ta[bv][uu] = *(const f16x8 *)(Dts(b) + DTT::off(32 * bv + n, 2 * uu + hh));
+#pragma unroll
+      for (int bk = 0; bk < NBK; ++bk)
+#pragma unroll
+        for (int uu = 0; uu < 2; ++uu) tq[bk][uu] = *(const f16x8 *)(Qts(b) + QTT::off(32 * bk + n, 2 * uu + hh));
       f16x8 pf[2], dsf[2];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
@@ -1002,22 +1056,22 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
           dsf[j >> 3][j & 7] = (_Float16)(pv * dp[j]);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int bv = 0; bv < NBV; ++bv)
 #pragma unroll
-        for (int uu = 0; uu < 2; ++uu)
-          accV[bv] = mma32(pf[uu], *(const f16x8 *)(Dts(b) + DTT::off(32 * bv + n, 2 * uu + hh)) * gh[bv], accV[bv]);
+        for (int uu = 0; uu < 2; ++uu) accV[bv] = mma32(pf[uu], ta[bv][uu] * gh[bv], accV[bv]);
 #pragma unroll
       for (int bk = 0; bk < NBK; ++bk)
 #pragma unroll
-        for (int uu = 0; uu < 2; ++uu)
-          accK[bk] = mma32(dsf[uu], *(const f16x8 *)(Qts(b) + QTT::off(32 * bk + n, 2 * uu + hh)), accK[bk]);
+        for (int uu = 0; uu < 2; ++uu) accK[bk] = mma32(dsf[uu], tq[bk][uu], accK[bk]);
     }
     // gamma of the next chunk, into the other buffer (its last readers passed
     // the barrier that ended the first step of the previous chunk).
-    if (next_chunk && tid < DV) gam((ord + 1) & 1)[tid] = fast_exp2((float)(lamI - lamJ));
-    wait_all();
-    __syncthreads();
+    if (next_chunk && tid < DV) gam(nxt.ord & 1)[tid] = fast_exp2((float)(lamI - lamJ));
+    cur = nxt;
+    wait_vm<(DIST - 1) * NCOPY>();  // the copies of step k + 1 have landed
+    lds_barrier();
   }
   if (kb >= L) return;
   // epilogue: dk, dv (inter part scaled to the key: exp(Gl_end(J) - Gl_key)), dG = qside - v (.) dv

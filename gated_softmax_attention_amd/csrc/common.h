@@ -175,6 +175,50 @@ __device__ inline void dma4(void *lds, rsrc_t src, uint32_t o) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (void __attribute__((address_space(3))) *)lds, 4, o, 0, 0, 0);
 }
 
+// Wait until at most N of the wave's vector-memory loads are in flight
+// (loads, direct LDS copies included, complete in issue order); LDS and
+// export counters are left alone.
+template <int N> __device__ inline void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// LDS byte address of a pointer into LDS.
+__device__ inline uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
+}
+// Four 16-byte LDS reads the compiler does not track: it would otherwise
+// make them wait for every direct copy in flight into LDS (it cannot tell
+// that they touch other regions).  The block waits for its own reads before
+// it ends, so its outputs are complete when it returns.
+__device__ inline void lds_read4(uint4 &r0, uint4 &r1, uint4 &r2, uint4 &r3, const void *p0, const void *p1,
+                                 const void *p2, const void *p3) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_b128 %2, %6\n\t"
+      "ds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+      : "v"(lds_addr(p0)), "v"(lds_addr(p1)), "v"(lds_addr(p2)), "v"(lds_addr(p3))
+      : "memory");
+}
+
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() is a
+// release/acquire for every address space, which makes each wave wait for
+// all its vector-memory loads before the barrier, direct LDS copies issued for
+// later steps included; the copies a step needs are waited for explicitly
+// (each wave its own, with wait_vm) before this barrier.
+__device__ inline void lds_barrier() {
+  // this wave's LDS stores are done (lgkmcnt 0; vmcnt and expcnt at their
+  // maxima, i.e. not waited for), then the barrier; the empty asm statements
+  // keep the compiler from moving memory accesses across it
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Wait for every outstanding memory operation of the wave (direct LDS copies included).
 __device__ inline void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
 

@@ -179,13 +179,19 @@ __global__ void __launch_bounds__(256, 2) k_fix_fwd(FwdArgs a) {
     // every step issues the same copies.
     stage_tile(min(J + 1, nJ - 1), b ^ 1);
     if (active && J < Iw - 1) {
+      // Operands of a group of products are read from LDS in one batch (one
+      // wait for all of them rather than one per product).
       f32x16 sc[2];
 #pragma unroll
       for (int be = 0; be < 2; ++be) {
+        kfrag ka[NS];
+#pragma unroll
+        for (int i = 0; i < NS; ++i) ka[i] = *(const kfrag *)(Ks(b) + KT::off(32 * be + n, 2 * i + hh));
+        __builtin_amdgcn_sched_barrier(0);
         sc[be] = zero16();
 #pragma unroll
-        for (int i = 0; i < NS; ++i)
-          sc[be] = mma32(*(const kfrag *)(Ks(b) + KT::off(32 * be + n, 2 * i + hh)), qf[i], sc[be]);
+        for (int i = 0; i < NS; ++i) sc[be] = mma32(ka[i], qf[i], sc[be]);
+        __builtin_amdgcn_sched_barrier(0);
       }
       float mx = fmaxf(row_max(sc[0]), row_max(sc[1]));
       mx = max_across_halves(mx) * sl2;
@@ -199,12 +205,16 @@ __global__ void __launch_bounds__(256, 2) k_fix_fwd(FwdArgs a) {
           for (int i = 0; i < 8; ++i) pf[2 * be + u][i] = (_Float16)fast_exp2(sc[be][8 * u + i] * sl2 - m_used);
 #pragma unroll
       for (int bb = 0; bb < NB; ++bb) {
+        f16x8 vb[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) vb[t] = *(const f16x8 *)(Vs(b) + VT::off(32 * bb + n, 2 * t + hh));
         float gam = Gs(b)[32 * bb + n];
 #pragma unroll
         for (int j = 0; j < 16; ++j) acc[bb][j] *= gam;
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-          acc[bb] = mma32(pf[t], *(const f16x8 *)(Vs(b) + VT::off(32 * bb + n, 2 * t + hh)), acc[bb]);
+        for (int t = 0; t < 4; ++t) acc[bb] = mma32(pf[t], vb[t], acc[bb]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     wait_all();

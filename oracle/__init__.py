@@ -113,6 +113,8 @@ def oracle_bwd(q, k, v, g, dO, cu_seqlens=None, *, scale=None, eps=1e-5, o_norm=
                m_in=None, unit_mask=None, window=0, lib=None):
     """Backward of FiX attention in fp64 (row max m held constant).
 
+    window > 0: the last `window` rows and keys of every selected unit; window < 0: dq of the
+    first -window rows and dk, dv of the first -window keys (dg not computed).
     Returns dict dq, dk, dv, dg, dw ([dv]; zeros without o_norm), dz (NaN where not computed).
     """
     lib = lib or load()

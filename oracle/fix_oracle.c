@@ -48,6 +48,11 @@
  * sequence to its last `window` rows.  Forward rows depend only on earlier
  * rows, and dk/dv/dg of a suffix depend only on rows inside that suffix, so
  * the suffix results are exact.  dq is exact for every computed row too.
+ * window < 0 (backward only) selects the first -window rows and keys
+ * instead: the rows' forward and gradient reaching x are computed for the
+ * whole sequence (every later query takes part in the keys' dk and dv),
+ * then dq of the first rows and dk, dv of the first keys; dg, a suffix sum
+ * over the whole sequence, is not computed in that mode.
  * Outputs outside the computed set are left untouched.
  */
 #include <math.h>
@@ -80,6 +85,13 @@ static int64_t row_lo(const octx *c, int64_t s) {
   int64_t L = seq_len(c, s);
   if (c->window > 0 && c->window < L) return L - c->window;
   return 0;
+}
+/* Rows whose dq, and keys whose dk and dv, are reported: [out_lo, out_hi). */
+static int64_t out_lo(const octx *c, int64_t s) { return row_lo(c, s); }
+static int64_t out_hi(const octx *c, int64_t s) {
+  int64_t L = seq_len(c, s);
+  if (c->window < 0 && -c->window < L) return -c->window;
+  return L;
 }
 static int unit_on(const octx *c, int64_t s, int64_t kvh) {
   return c->mask == NULL || c->mask[s * c->Hkv + kvh] != 0;
@@ -296,6 +308,7 @@ int fix_oracle_bwd(int64_t nseq, const int64_t *cu, int64_t Hq, int64_t Hkv, int
 #pragma omp for schedule(dynamic, 8)
     for (int64_t e = 0; e < n; ++e) {
       int64_t s = it[e].s, h = it[e].h, i = it[e].i, t = cu[s] + i, base = cu[s], kh = h / c.G;
+      if (i < out_lo(&c, s) || i >= out_hi(&c, s)) continue;
       size_t ro = (size_t)(t * Hq + h);
       (void)row_scores(&c, s, h, i, sc);
       double m = M[ro];
@@ -321,14 +334,14 @@ int fix_oracle_bwd(int64_t nseq, const int64_t *cu, int64_t Hq, int64_t Hkv, int
   int64_t nk = 0;
   for (int64_t s = 0; s < nseq; ++s)
     for (int64_t kh = 0; kh < Hkv; ++kh)
-      if (unit_on(&c, s, kh)) nk += seq_len(&c, s) - row_lo(&c, s);
+      if (unit_on(&c, s, kh)) nk += out_hi(&c, s) - out_lo(&c, s);
   item *kit = (item *)malloc(sizeof(item) * (size_t)(nk > 0 ? nk : 1));
   {
     int64_t p = 0;
     for (int64_t s = 0; s < nseq; ++s)
       for (int64_t kh = 0; kh < Hkv; ++kh)
         if (unit_on(&c, s, kh))
-          for (int64_t j = row_lo(&c, s); j < seq_len(&c, s); ++j) { kit[p].s = s; kit[p].h = kh; kit[p].i = j; ++p; }
+          for (int64_t j = out_lo(&c, s); j < out_hi(&c, s); ++j) { kit[p].s = s; kit[p].h = kh; kit[p].i = j; ++p; }
   }
 #pragma omp parallel
   {
@@ -374,7 +387,7 @@ int fix_oracle_bwd(int64_t nseq, const int64_t *cu, int64_t Hq, int64_t Hkv, int
 #pragma omp parallel for collapse(2) schedule(static)
   for (int64_t s = 0; s < nseq; ++s)
     for (int64_t kh = 0; kh < Hkv; ++kh) {
-      if (!unit_on(&c, s, kh)) continue;
+      if (!unit_on(&c, s, kh) || c.window < 0) continue;
       int64_t base = cu[s], L = seq_len(&c, s), lo = row_lo(&c, s);
       for (int64_t d = 0; d < dv; ++d) {
         double run = 0.0;

@@ -324,6 +324,29 @@ def pin_suffix_window(lib, rng):
     return worst
 
 
+def pin_prefix_window(lib, rng):
+    """The prefix mode (window < 0) reproduces the full dq of the first rows and dk, dv of the
+    first keys of the selected units, and computes nothing else."""
+    lengths = [30, 45]
+    q, k, v, g, cu = rand_case(rng, 1, 75, 4, 2, 8, 8, lengths=lengths)
+    dO = rng.standard_normal((1, 75, 4, 8))
+    full_b = O.oracle_bwd(q, k, v, g, dO, cu, lib=lib)
+    mask = np.array([[0, 1], [1, 0]], np.uint8)
+    pre = O.oracle_bwd(q, k, v, g, dO, cu, unit_mask=mask, window=-7, lib=lib)
+    sel = np.zeros((75, 4), bool)
+    sel[0:7, 2:4] = True       # sequence 0, kv head 1
+    sel[30:37, 0:2] = True     # sequence 1, kv head 0
+    selk = np.zeros((75, 2), bool)
+    selk[0:7, 1] = True
+    selk[30:37, 0] = True
+    worst = rel(pre["dq"][0][sel], full_b["dq"][0][sel])
+    for n in ("dk", "dv"):
+        worst = max(worst, rel(pre[n][0][selk], full_b[n][0][selk]))
+    assert np.isnan(pre["dq"][0][~sel]).all() and np.isnan(pre["dk"][0][~selk]).all()
+    assert np.isnan(pre["dg"]).all()
+    return worst
+
+
 ALL_PINS = {
     "no_gate_softmax": (pin_no_gate_is_softmax_attention, 1e-12),
     "no_gate_unnormalised": (pin_no_gate_unnormalised, 1e-12),
@@ -340,4 +363,5 @@ ALL_PINS = {
     "dense_reference": (pin_dense_reference, 1e-10),
     "dense_reference_unnormed": (lambda lib, rng: pin_dense_reference(lib, rng, False), 1e-10),
     "suffix_window": (pin_suffix_window, 0.0),
+    "prefix_window": (pin_prefix_window, 0.0),
 }

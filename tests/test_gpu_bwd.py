@@ -61,6 +61,11 @@ EDGES = [
     (1, 257, 2, 2, 32, 16, {"in_dtype": "f32"}),
     (1, 384, 2, 2, 16, 16, {}),
     (3, 170, 2, 2, 128, 64, {"o_gate": True, "gate": (1.0, 2.0)}),
+    # long memory (g about -3e-4 per token): pairs two or more chunks apart carry most of
+    # the weight, so the inter-chunk kernels decide the result
+    (1, 1100, 4, 2, 64, 64, {"gate": (8.0, 1.0)}),
+    (2, 640, 2, 1, 128, 128, {"gate": (10.0, 0.5), "o_gate": True}),
+    (1, 1024, 4, 4, 32, 128, {"gate": (8.0, 1.0), "lengths": (384, 129, 511)}),
 ]
 
 
@@ -167,3 +172,17 @@ def test_bwd_full_size_sampled(name, units):
     got = run_bwd(x)
     ref = oracle_bwd_for(x, unit_mask=_unit_mask(x["workload"], units), window=256)
     check_bwd(got, ref, check_dw=False)
+
+
+def test_bwd_full_size_first_keys():
+    """Training shape as the benchmark runs it: dq of the first 256 rows and dk, dv of the first
+    256 keys of two units, whose gradients gather every later query (the inter-chunk kernels'
+    work); the oracle computes the units' whole forward for them."""
+    announce("bwd full-size train, first keys")
+    x = synth.make_inputs("train")
+    got = run_bwd(x)
+    ref = oracle_bwd_for(x, unit_mask=_unit_mask(x["workload"], [(0, 5), (2, 11)]), window=-256)
+    e = {n: err_rms(got[n], ref[n]) for n in ("dq", "dk", "dv")}
+    print("errors:", {k: f"{v:.2e}" for k, v in e.items()}, flush=True)
+    for n, v in e.items():
+        assert v <= TOL, f"{n}: {v:.3e}"

@@ -66,6 +66,9 @@ EDGES = [
     (1, 257, 2, 2, 32, 16, {"in_dtype": "f32"}),
     (1, 384, 2, 2, 16, 16, {}),
     (3, 170, 2, 2, 128, 64, {"o_gate": True, "gate": (1.0, 2.0)}),
+    # long memory (g about -3e-4 per token): far-apart chunks carry most of the weight
+    (1, 1100, 4, 2, 64, 64, {"gate": (8.0, 1.0)}),
+    (2, 640, 2, 1, 128, 128, {"gate": (10.0, 0.5), "o_gate": True}),
 ]
 
 

@@ -76,7 +76,6 @@ void carve_plan(Carve &cv, const fix_attn_desc *d, const Shape &s, fix::Plan &p)
   p.seq_len = cv.take<int>(s.nseq);
   p.chunk_base = cv.take<int>(s.nseq + 1);
   p.cb128 = cv.take<int>(s.nseq + 1);
-  p.qitems = cv.take<int2>(s.nqb_ub);
   p.counts = cv.take<int>(4);
   p.nseq = (int)s.nseq;
 }
@@ -134,6 +133,9 @@ size_t carve_bwd(Carve &cv, const fix_attn_desc *d, BwdWs &w) {
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+
+// Grids of kernels that order their work per XCD hold a multiple of 8 workgroups.
+int64_t round8(int64_t n) { return (n + 7) / 8 * 8; }
 
 fix_status hip_fail(hipError_t e) {
   g_last_hip_error = (int)e;
@@ -208,7 +210,7 @@ fix_status fix_attn_fwd(const fix_attn_desc *d, const void *q, const void *k, co
   a.eps = d->eps;
   a.o_norm = d->o_norm ? 1 : 0;
   a.out_f32 = d->out_dtype == FIX_F32;
-  e = fix::launch_fwd((int)d->dk, (int)d->dv, f32in, a, (int)(s.nqb_ub * d->Hq), st);
+  e = fix::launch_fwd((int)d->dk, (int)d->dv, f32in, a, (int)round8(s.nqb_ub * d->Hq), st);
   if (e == hipSuccess) e = trace_mark(st, "fix_fwd");
   if (e != hipSuccess) return hip_fail(e);
   return FIX_OK;
@@ -283,8 +285,8 @@ fix_status fix_attn_bwd(const fix_attn_desc *d, const void *q, const void *k, co
   a.out_f32 = d->out_dtype == FIX_F32;
   FIX_TRY(fix::launch_bwd(fix::BK_INTRA_DQ, DK, DV, f32in, a, dim3(ncb, Hq), st), "bwd_intra_dq");
   FIX_TRY(fix::launch_bwd(fix::BK_INTRA_DKV, DK, DV, f32in, a, dim3(ncb, Hkv), st), "bwd_intra_dkv");
-  FIX_TRY(fix::launch_bwd(fix::BK_DQ, DK, DV, f32in, a, dim3(ncb * Hq), st), "bwd_dq");
-  FIX_TRY(fix::launch_bwd(fix::BK_DKV, DK, DV, f32in, a, dim3(ncb * Hkv), st), "bwd_dkv");
+  FIX_TRY(fix::launch_bwd(fix::BK_DQ, DK, DV, f32in, a, dim3(round8(ncb * Hq)), st), "bwd_dq");
+  FIX_TRY(fix::launch_bwd(fix::BK_DKV, DK, DV, f32in, a, dim3(round8(ncb * Hkv)), st), "bwd_dkv");
   FIX_TRY(fix::launch_dg_scan(DV, w.dG, w.plan, Hkv, ncb, w.dg_tot, w.dg_carry, dg, st), "dg_scan");
   if (want_dw) {
     FIX_TRY(fix::launch_dw_reduce(w.dw_part, w.plan.counts, Hkv, DV, d_o_norm_weight, st), "dw_reduce");

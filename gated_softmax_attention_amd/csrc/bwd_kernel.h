@@ -676,18 +676,21 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdArgs a) {
 
   const Plan &pl = a.plan;
   const int Hq = a.Hq, Hkv = a.Hkv, G = Hq / Hkv;
-  int bid = blockIdx.x;
-  const int c = bid % Hkv;
-  bid /= Hkv;
-  const int gq = bid % G;
-  const int item = bid / G;
-  if (item >= pl.counts[0]) return;
+  // Items ordered (kv head, sequence, query chunk from the last, q head of
+  // the group): the workgroups of one (sequence, kv head) run together on an
+  // XCD and walk the same key chunks upward in step, sharing them in L2.
+  const int nchunk = pl.counts[0];
+  const int idx = xcd_item(nchunk * Hq);
+  if (idx < 0) return;
+  const int c = uniform(idx / (nchunk * G)), rem = uniform(idx % (nchunk * G));
+  const int gci = rem / G, gq = rem % G;
+  const int s = seq_of_chunk(pl.cb128, pl.nseq, gci);
+  const int cbs = uniform(pl.cb128[s]);
+  const int64_t st = uniform((int64_t)pl.seq_start[s]);
+  const int L = uniform(pl.seq_len[s]);
+  const int nchs = (L + CB - 1) / CB;
+  const int I = nchs - 1 - (gci - cbs);  // longest first within the sequence
   const int hq = c * G + gq;
-  const int2 it = pl.qitems[item];
-  const int s = it.x, I = it.y;
-  const int64_t st = pl.seq_start[s];
-  const int L = pl.seq_len[s];
-  const int cbs = pl.cb128[s];
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, n = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r0 = I * CB + 32 * wave;
@@ -772,28 +775,13 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdArgs a) {
     stage_tile(min(k + 1, nsteps - 1), b ^ 1);
     const double lamJ = lam_of(min((k >> 2) + 1, I - 1));
     {
-      // Operands of a group of products are read from LDS in one batch (one
-      // wait for all of them rather than one per product).
-      kfrag ka[NS];
-#pragma unroll
-      for (int i = 0; i < NS; ++i) ka[i] = *(const kfrag *)(Ks(b) + KT::off(n, 2 * i + hh));
-      __builtin_amdgcn_sched_barrier(0);
+      // (Operands are read from LDS per product: batching them needs more
+      // registers than this kernel has at two workgroups per CU.)
       f32x16 sc = zero16(), dp = zero16();
 #pragma unroll
-      for (int i = 0; i < NS; ++i) sc = mma32(ka[i], qf[i], sc);
-      __builtin_amdgcn_sched_barrier(0);
-      f16x8 va[NSV];
+      for (int i = 0; i < NS; ++i) sc = mma32(*(const kfrag *)(Ks(b) + KT::off(n, 2 * i + hh)), qf[i], sc);
 #pragma unroll
-      for (int i = 0; i < NSV; ++i) va[i] = *(const f16x8 *)(Vs(b) + VT::off(n, 2 * i + hh));
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < NSV; ++i) dp = mma32(va[i], dhf[i], dp);
-      __builtin_amdgcn_sched_barrier(0);
-      f16x8 tk[NBK][2];
-#pragma unroll
-      for (int bk = 0; bk < NBK; ++bk)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) tk[bk][u] = *(const f16x8 *)(Kts(b) + TT::off(32 * bk + n, 2 * u + hh));
+      for (int i = 0; i < NSV; ++i) dp = mma32(*(const f16x8 *)(Vs(b) + VT::off(n, 2 * i + hh)), dhf[i], dp);
       f16x8 dsf[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u)
@@ -802,11 +790,11 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdArgs a) {
           const int j = 8 * u + i;
           dsf[u][i] = (_Float16)(fast_exp2(sc[j] * sl2 - mbn) * dp[j]);
         }
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int bk = 0; bk < NBK; ++bk)
 #pragma unroll
-        for (int u = 0; u < 2; ++u) acc[bk] = mma32(dsf[u], tk[bk][u], acc[bk]);
+        for (int u = 0; u < 2; ++u)
+          acc[bk] = mma32(dsf[u], *(const f16x8 *)(Kts(b) + TT::off(32 * bk + n, 2 * u + hh)), acc[bk]);
     }
     // gamma of the next chunk, into the other buffer (its last readers passed
     // the barrier that began this chunk).
@@ -818,16 +806,22 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdArgs a) {
     wait_all();
     __syncthreads();
   }
+  // The block's inputs are loaded before any of its stores (the compiler
+  // cannot tell dq and dq_i apart, so interleaving would serialize them).
 #pragma unroll
   for (int bk = 0; bk < NBK; ++bk) {
     const int col = 32 * bk + n;
     if (col >= DK) continue;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int r = r0 + acc_row(hh, j);
-      if (r < L) {
-        const int64_t idx = ((st + r) * Hq + hq) * DK + col;
-        store_out(a.dq, idx, a.scale * acc[bk][j] + a.dq_i[idx], a.out_f32);
+    for (int h8 = 0; h8 < 16; h8 += 8) {
+      float part[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        part[j] = a.dq_i[((st + min(r0 + acc_row(hh, h8 + j), L - 1)) * Hq + hq) * DK + col];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int r = r0 + acc_row(hh, h8 + j);
+        if (r < L) store_out(a.dq, ((st + r) * Hq + hq) * DK + col, a.scale * acc[bk][h8 + j] + part[j], a.out_f32);
       }
     }
   }
@@ -878,14 +872,18 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
 
   const Plan &pl = a.plan;
   const int Hq = a.Hq, Hkv = a.Hkv, G = Hq / Hkv;
-  const int c = blockIdx.x % Hkv;
-  const int rank = blockIdx.x / Hkv;
-  if (rank >= pl.counts[0]) return;
-  const int2 it = pl.qitems[pl.counts[0] - 1 - rank];  // earliest chunks (most queries after them) first
-  const int s = uniform(it.x), J = uniform(it.y);
+  // Items ordered (kv head, sequence, key chunk): the workgroups of one
+  // (sequence, kv head) run together on an XCD and walk the same query
+  // chunks downward in step, sharing them in L2.
+  const int nchunk = pl.counts[0];
+  const int idx = xcd_item(nchunk * Hkv);
+  if (idx < 0) return;
+  const int c = uniform(idx / nchunk), gci = uniform(idx % nchunk);
+  const int s = seq_of_chunk(pl.cb128, pl.nseq, gci);
+  const int cbs = uniform(pl.cb128[s]);
+  const int J = gci - cbs;
   const int64_t st = uniform((int64_t)pl.seq_start[s]);
   const int L = uniform(pl.seq_len[s]);
-  const int cbs = uniform(pl.cb128[s]);
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, n = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kb = J * CB + 32 * wave;
@@ -1074,19 +1072,25 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
     lds_barrier();
   }
   if (kb >= L) return;
-  // epilogue: dk, dv (inter part scaled to the key: exp(Gl_end(J) - Gl_key)), dG = qside - v (.) dv
+  // epilogue: dk, dv (inter part scaled to the key: exp(Gl_end(J) - Gl_key)), dG = qside - v (.) dv.
+  // Each block's inputs are loaded before any of its stores: the compiler
+  // cannot tell the output and input buffers apart, so interleaved loads
+  // and stores would each wait for the previous store's load.
   const int tend = min((J + 1) * CB, L) - 1;
 #pragma unroll
   for (int bk = 0; bk < NBK; ++bk) {
     const int col = 32 * bk + n;
     if (col >= DK) continue;
+    float part[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int kj = min(kb + acc_row(hh, j), L - 1);
+      part[j] = a.dk_i[((st + kj) * Hkv + c) * DK + col];
+    }
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int kj = kb + acc_row(hh, j);
-      if (kj < L) {
-        const int64_t idx = ((st + kj) * Hkv + c) * DK + col;
-        store_out(a.dk, idx, a.scale * accK[bk][j] + a.dk_i[idx], a.out_f32);
-      }
+      if (kj < L) store_out(a.dk, ((st + kj) * Hkv + c) * DK + col, a.scale * accK[bk][j] + part[j], a.out_f32);
     }
   }
 #pragma unroll
@@ -1094,14 +1098,23 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
     const int col = 32 * bv + n;
     if (col >= DV) continue;
     const float gend = a.Gl2[((st + tend) * Hkv + c) * DV + col];
+    float gl[16], part[16], qs[16], vv[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int64_t idx = ((st + min(kb + acc_row(hh, j), L - 1)) * Hkv + c) * DV + col;
+      gl[j] = a.Gl2[idx];
+      part[j] = a.dv_i[idx];
+      qs[j] = a.qside[idx];
+      vv[j] = load_in(a.v, idx, F32IN);
+    }
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int kj = kb + acc_row(hh, j);
       if (kj < L) {
         const int64_t idx = ((st + kj) * Hkv + c) * DV + col;
-        const float dvv = fast_exp2(gend - a.Gl2[idx]) * accV[bv][j] + a.dv_i[idx];
+        const float dvv = fast_exp2(gend - gl[j]) * accV[bv][j] + part[j];
         store_out(a.dv, idx, dvv, a.out_f32);
-        a.dG[idx] = a.qside[idx] - load_in(a.v, idx, F32IN) * dvv;
+        a.dG[idx] = qs[j] - vv[j] * dvv;
       }
     }
   }

@@ -91,10 +91,25 @@ __global__ void __launch_bounds__(256) k_tiles_t(const void *__restrict__ in, bo
   const int t0 = (gc - plan.cb128[s]) * CB;
   const int n = min(CB, plan.seq_len[s] - t0);
   const int64_t tok0 = (int64_t)plan.seq_start[s] + t0;
-  for (int e = tid; e < CB * D; e += 256) {
-    int t = e / D, d = e % D;
-    float val = t < n ? load_in(in, ((tok0 + t) * H + h) * D + d, in_f32) : 0.f;
-    tile[d * STR + key_pos(t)] = (_Float16)val;
+  // 8 consecutive channels of one token per thread and pass (16-byte loads for bf16)
+  for (int e = tid; e < CB * D / 8; e += 256) {
+    const int t = e / (D / 8), d8 = 8 * (e % (D / 8));
+    const int64_t base = ((tok0 + min(t, n - 1)) * H + h) * D + d8;
+    float val[8];
+    if (in_f32) {
+      const float4 lo = *(const float4 *)((const float *)in + base), hi = *(const float4 *)((const float *)in + base + 4);
+      val[0] = lo.x; val[1] = lo.y; val[2] = lo.z; val[3] = lo.w; val[4] = hi.x; val[5] = hi.y; val[6] = hi.z; val[7] = hi.w;
+    } else {
+      const uint4 r = *(const uint4 *)((const uint16_t *)in + base);
+      const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        val[2 * i] = __uint_as_float(w[i] << 16);
+        val[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tile[(d8 + i) * STR + key_pos(t)] = (_Float16)(t < n ? val[i] : 0.f);
   }
   __syncthreads();
   uint4 *dst = (uint4 *)(out + ((int64_t)gc * H + h) * D * CB);
@@ -129,87 +144,108 @@ __global__ void __launch_bounds__(256) k_bwd_prep(PrepArgs a) {
   }
   for (int gq = 0; gq < G; ++gq) {
     const int h = c * G + gq;
+    // U tokens per wave at a time: every input of the U rows is loaded
+    // before any output is stored (the compiler cannot tell the buffers
+    // apart, so interleaving would make each row wait for the previous
+    // row's stores).
+    constexpr int U = 4;
 #pragma unroll 1
-    for (int i = 0; i < CB / 4; ++i) {
-      const int t = wave + 4 * i;  // token within the chunk
-      if (t < n) {
+    for (int i0 = 0; i0 < CB / 4; i0 += U) {
+      float r[U], mrow[U], xv[U][PER], go[U][PER], zz[U][PER], gl[U][PER], gbs[U][PER], qo[U][PER];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int t = min(wave + 4 * (i0 + u), n - 1);  // rows past the end repeat the last (not stored)
         const int64_t tok = tok0 + t;
         const int64_t rb = (tok * Hq + h) * DV;
-        const float r = a.rstd[tok * Hq + h];
-        float xv[PER], dn[PER], del[PER];
-        float proj = 0.f;
+        r[u] = a.rstd[tok * Hq + h];
+        mrow[u] = a.m[tok * Hq + h];
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
-          int d = lane + 64 * k;
-          xv[k] = dn[k] = 0.f;
-          if (d < DV) {
-            xv[k] = a.x[rb + d];
-            float go = load_in(a.dO, rb + d, in_f32);
-            float zz = a.z ? load_in(a.z, rb + d, in_f32) : 1.f;
-            dn[k] = go * zz;
-            float nval = a.o_norm ? xv[k] * r * wv[k] : xv[k];
-            if (a.dz) store_out(a.dz, rb + d, go * nval, a.out_f32);
-            if (a.o_norm) {
-              dwacc[k] += dn[k] * xv[k] * r;
-              proj += dn[k] * wv[k] * xv[k] * r;
+          const int d = min(lane + 64 * k, DV - 1);
+          const int64_t gi = (tok * Hkv + c) * DV + d;
+          xv[u][k] = a.x[rb + d];
+          go[u][k] = load_in(a.dO, rb + d, in_f32);
+          zz[u][k] = a.z ? load_in(a.z, rb + d, in_f32) : 1.f;
+          gl[u][k] = a.Gl2[gi];
+          gbs[u][k] = (t & ~31) ? a.Gl2[((tok0 + (t & ~31) - 1) * Hkv + c) * DV + d] : 0.f;
+          qo[u][k] = gq == 0 ? 0.f : a.qside[gi];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int t = wave + 4 * (i0 + u);  // token within the chunk
+        if (t < n) {
+          const int64_t tok = tok0 + t;
+          const int64_t rb = (tok * Hq + h) * DV;
+          float dn[PER], del[PER];
+          float proj = 0.f;
+#pragma unroll
+          for (int k = 0; k < PER; ++k) {
+            const int d = lane + 64 * k;
+            dn[k] = 0.f;
+            if (d < DV) {
+              dn[k] = go[u][k] * zz[u][k];
+              const float nval = a.o_norm ? xv[u][k] * r[u] * wv[k] : xv[u][k];
+              if (a.dz) store_out(a.dz, rb + d, go[u][k] * nval, a.out_f32);
+              if (a.o_norm) {
+                dwacc[k] += dn[k] * xv[u][k] * r[u];
+                proj += dn[k] * wv[k] * xv[u][k] * r[u];
+              }
             }
           }
-        }
-        if (a.o_norm) {
+          if (a.o_norm) {
 #pragma unroll
-          for (int off = 32; off > 0; off >>= 1) proj += __shfl_xor(proj, off);
-          proj *= 1.f / DV;
-        }
-        // sigma = 2^-e scales the row so that max |sigma delta| is about 1; every
-        // fp16 operand built from the row (here exp(Gl) sigma delta, within a
-        // chunk exp(Gl_i - Gl_ref) sigma delta, all factors <= 1) stays in range
-        float amax = 0.f;
-#pragma unroll
-        for (int k = 0; k < PER; ++k) {
-          del[k] = a.o_norm ? r * (dn[k] * wv[k] - xv[k] * r * proj) : dn[k];
-          if (lane + 64 * k < DV) amax = fmaxf(amax, fabsf(del[k]));
-        }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-        int e = 0;
-        if (amax > 0.f) e = min(15, max(-15, (int)ceilf(__log2f(amax))));
-        const float sg = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e
-#pragma unroll
-        for (int k = 0; k < PER; ++k) {
-          int d = lane + 64 * k;
-          if (d < DV) {
-            a.delta[rb + d] = del[k];
-            // query side of dG, summed over the group; (token, channel) is
-            // owned by this thread for every head of the group
-            const int64_t qi = (tok * Hkv + c) * DV + d;
-            a.qside[qi] = (gq == 0 ? 0.f : a.qside[qi]) + del[k] * xv[k];
-            const float gl = a.Gl2[(tok * Hkv + c) * DV + d];
-            _Float16 hv = (_Float16)(fast_exp2(gl) * del[k] * sg);
-            a.dh[rb + d] = hv;
-            tile[d * STR + key_pos(t)] = hv;
-            // relative to the token before the row's 32-token block (<= 1)
-            const float gbs = (t & ~31) ? a.Gl2[((tok0 + (t & ~31) - 1) * Hkv + c) * DV + d] : 0.f;
-            const float xb = fast_exp2(gl - gbs) * del[k] * sg;
-            const __bf16 xh = (__bf16)xb, xl = (__bf16)(xb - (float)xh);
-            a.X16[rb + d] = (_Float16)xb;
-            a.XH[rb + d] = xh;
-            a.XL[rb + d] = xl;
-            tileh[d * STR + key_pos(t)] = xh;
-            tilel[d * STR + key_pos(t)] = xl;
+            for (int off = 32; off > 0; off >>= 1) proj += __shfl_xor(proj, off);
+            proj *= 1.f / DV;
           }
-        }
-        if (lane == 0) {
-          a.mb[tok * Hq + h] = a.m[tok * Hq + h] * LOG2E - (float)e;
-          a.sig[tok * Hq + h] = sg;
-        }
-      } else {
+          // sigma = 2^-e scales the row so that max |sigma delta| is about 1; every
+          // fp16 operand built from the row (here exp(Gl) sigma delta, within a
+          // block exp(Gl_i - Gl_ref) sigma delta, all factors <= 1) stays in range
+          float amax = 0.f;
 #pragma unroll
-        for (int k = 0; k < PER; ++k) {
-          int d = lane + 64 * k;
-          if (d < DV) {
-            tile[d * STR + key_pos(t)] = (_Float16)0.f;
-            tileh[d * STR + key_pos(t)] = (__bf16)0.f;
-            tilel[d * STR + key_pos(t)] = (__bf16)0.f;
+          for (int k = 0; k < PER; ++k) {
+            del[k] = a.o_norm ? r[u] * (dn[k] * wv[k] - xv[u][k] * r[u] * proj) : dn[k];
+            if (lane + 64 * k < DV) amax = fmaxf(amax, fabsf(del[k]));
+          }
+#pragma unroll
+          for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+          int e = 0;
+          if (amax > 0.f) e = min(15, max(-15, (int)ceilf(__log2f(amax))));
+          const float sg = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e
+#pragma unroll
+          for (int k = 0; k < PER; ++k) {
+            const int d = lane + 64 * k;
+            if (d < DV) {
+              a.delta[rb + d] = del[k];
+              // query side of dG, summed over the group; (token, channel) is
+              // owned by this thread for every head of the group
+              a.qside[(tok * Hkv + c) * DV + d] = qo[u][k] + del[k] * xv[u][k];
+              const _Float16 hv = (_Float16)(fast_exp2(gl[u][k]) * del[k] * sg);
+              a.dh[rb + d] = hv;
+              tile[d * STR + key_pos(t)] = hv;
+              // relative to the token before the row's 32-token block (<= 1)
+              const float xb = fast_exp2(gl[u][k] - gbs[u][k]) * del[k] * sg;
+              const __bf16 xh = (__bf16)xb, xl = (__bf16)(xb - (float)xh);
+              a.X16[rb + d] = (_Float16)xb;
+              a.XH[rb + d] = xh;
+              a.XL[rb + d] = xl;
+              tileh[d * STR + key_pos(t)] = xh;
+              tilel[d * STR + key_pos(t)] = xl;
+            }
+          }
+          if (lane == 0) {
+            a.mb[tok * Hq + h] = mrow[u] * LOG2E - (float)e;
+            a.sig[tok * Hq + h] = sg;
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < PER; ++k) {
+            const int d = lane + 64 * k;
+            if (d < DV) {
+              tile[d * STR + key_pos(t)] = (_Float16)0.f;
+              tileh[d * STR + key_pos(t)] = (__bf16)0.f;
+              tilel[d * STR + key_pos(t)] = (__bf16)0.f;
+            }
           }
         }
       }
@@ -262,8 +298,13 @@ __global__ void __launch_bounds__(128) k_dg_totals(const float *__restrict__ dG,
   const int t0 = (gc - plan.cb128[s]) * CB;
   const int n = min(CB, plan.seq_len[s] - t0);
   const int64_t tok0 = (int64_t)plan.seq_start[s] + t0;
+  // fixed trip count, masked, so that the loads are issued together
   float acc = 0.f;
-  for (int j = 0; j < n; ++j) acc += dG[((tok0 + j) * Hkv + c) * DV + d];
+#pragma unroll 32
+  for (int j = 0; j < CB; ++j) {
+    const float x = dG[((tok0 + min(j, n - 1)) * Hkv + c) * DV + d];
+    acc += j < n ? x : 0.f;
+  }
   tot[((int64_t)gc * Hkv + c) * DV + d] = acc;
 }
 
@@ -289,11 +330,21 @@ __global__ void __launch_bounds__(128) k_dg_final(const float *__restrict__ dG, 
   const int t0 = (gc - plan.cb128[s]) * CB;
   const int n = min(CB, plan.seq_len[s] - t0);
   const int64_t tok0 = (int64_t)plan.seq_start[s] + t0;
+  // 32-token blocks from the chunk end down, each block's loads issued together
   float run = carry[((int64_t)gc * Hkv + c) * DV + d];
-  for (int j = n - 1; j >= 0; --j) {
-    const int64_t idx = ((tok0 + j) * Hkv + c) * DV + d;
-    run += dG[idx];
-    dg[idx] = run;
+#pragma unroll 1
+  for (int b = CB / 32 - 1; b >= 0; --b) {
+    float x[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) x[j] = dG[((tok0 + min(32 * b + j, n - 1)) * Hkv + c) * DV + d];
+#pragma unroll
+    for (int j = 31; j >= 0; --j) {
+      const int t = 32 * b + j;
+      if (t < n) {
+        run += x[j];
+        dg[((tok0 + t) * Hkv + c) * DV + d] = run;
+      }
+    }
   }
 }
 

@@ -20,13 +20,12 @@ constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
 // Device plan written by k_plan: every sequence's place in the packed token
-// order, its first chunk, and the forward work list.
+// order, its first chunk, and the number of chunks.
 struct Plan {
   int *seq_start;   // [nseq] first token of each sequence
   int *seq_len;     // [nseq]
   int *chunk_base;  // [nseq + 1] prefix sum of ceil(len / CH)
   int *cb128;       // [nseq + 1] prefix sum of ceil(len / CB)
-  int2 *qitems;     // [nqb_ub] (sequence, 128-token block), latest blocks first
   int *counts;      // [0] 128-token blocks, [1] 64-token chunks, [2] longest sequence
   int nseq;
 };
@@ -39,6 +38,19 @@ __device__ inline int seq_of_chunk(const int *base, int nseq, int gc) {
     if (base[mid] <= gc) lo = mid; else hi = mid - 1;
   }
   return __builtin_amdgcn_readfirstlane(lo);  // the same in every lane (gc is per workgroup)
+}
+
+// XCD-aware work order.  Workgroups are dispatched round-robin over the 8
+// XCDs (blockIdx.x % 8 picks the XCD), each with its own L2.  Item idx =
+// xcd * per + slot gives every XCD a contiguous range of an ordered item
+// list, so the workgroups running together on one XCD are neighbours in the
+// list (the same sequence and head, reading the same tiles at about the same
+// time).  Returns -1 for workgroups past the end; the grid must hold at least
+// 8 * ceil(nitems / 8) workgroups.
+__device__ inline int xcd_item(int nitems) {
+  const int x = blockIdx.x & 7, slot = blockIdx.x >> 3, per = (nitems + 7) >> 3;
+  const int idx = x * per + slot;
+  return (slot < per && idx < nitems) ? idx : -1;
 }
 
 // Values that are the same in every lane, marked so for the compiler (they

@@ -68,18 +68,20 @@ __global__ void __launch_bounds__(256, 2) k_fix_fwd(FwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const Plan &pl = a.plan;
   const int Hq = a.Hq, Hkv = a.Hkv, G = Hq / Hkv;
-  int bid = blockIdx.x;
-  const int c = bid % Hkv;
-  bid /= Hkv;
-  const int gq = bid % G;
-  const int item = bid / G;
-  if (item >= pl.counts[0]) return;
+  // Items ordered (kv head, sequence, query block from the last, q head of
+  // the group): the workgroups of one (sequence, kv head) run together on an
+  // XCD and walk the same key chunks upward in step, sharing them in L2.
+  const int nblk = pl.counts[0];  // 128-row query blocks
+  const int idx = xcd_item(nblk * Hq);
+  if (idx < 0) return;
+  const int c = uniform(idx / (nblk * G)), rem = uniform(idx % (nblk * G));
+  const int bi = rem / G, gq = rem % G;
+  const int s = seq_of_chunk(pl.cb128, pl.nseq, bi);
+  const int64_t st = uniform((int64_t)pl.seq_start[s]);
+  const int L = uniform(pl.seq_len[s]);
+  const int cb = uniform(pl.chunk_base[s]);
+  const int qb = (L + QB - 1) / QB - 1 - (bi - uniform(pl.cb128[s]));  // longest first within the sequence
   const int hq = c * G + gq;
-  const int2 it = pl.qitems[item];
-  const int s = it.x, qb = it.y;
-  const int64_t st = pl.seq_start[s];
-  const int L = pl.seq_len[s];
-  const int cb = pl.chunk_base[s];
   const int q0 = qb * QB;
   const int nrows = min(QB, L - q0);
   const bool active = wave * 32 < nrows;

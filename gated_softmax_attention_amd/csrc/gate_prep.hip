@@ -37,27 +37,30 @@ __global__ void __launch_bounds__(128) k_gate_prep(const float *__restrict__ g, 
   const int n = min(CH, plan.seq_len[s] - t0);
   const int64_t tok0 = (int64_t)plan.seq_start[s] + t0;
 
-  float gl[CH];
+  // All loads first (rows past the end repeat the last row and are not
+  // used), so that they are in flight together.
+  float gl[CH], vv[CH];
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    const int64_t idx = ((tok0 + min(j, n - 1)) * Hkv + c) * DV + d;
+    gl[j] = g[idx];
+    vv[j] = load_in(v, idx, in_f32);
+  }
   float acc = 0.f;
 #pragma unroll
   for (int j = 0; j < CH; ++j) {
-    if (j < n) {
-      int64_t idx = ((tok0 + j) * Hkv + c) * DV + d;
-      acc += g[idx] * LOG2E;
-      Gl2[idx] = acc;
-    }
+    if (j < n) acc += gl[j] * LOG2E;
     gl[j] = acc;
   }
+#pragma unroll
+  for (int j = 0; j < CH; ++j)
+    if (j < n) Gl2[((tok0 + j) * Hkv + c) * DV + d] = gl[j];
   const int64_t cidx = ((int64_t)gc * Hkv + c) * DV + d;
   Gam[cidx] = fast_exp2(acc);
 
   _Float16 row[CH];
 #pragma unroll
-  for (int j = 0; j < CH; ++j) {
-    float val = 0.f;
-    if (j < n) val = fast_exp2(acc - gl[j]) * load_in(v, ((tok0 + j) * Hkv + c) * DV + d, in_f32);
-    row[key_pos(j)] = (_Float16)val;
-  }
+  for (int j = 0; j < CH; ++j) row[key_pos(j)] = (_Float16)(j < n ? fast_exp2(acc - gl[j]) * vv[j] : 0.f);
   uint4 *dst = (uint4 *)(VtT + cidx * CH);
 #pragma unroll
   for (int p = 0; p < CH / 8; ++p) dst[p] = *(const uint4 *)(row + 8 * p);

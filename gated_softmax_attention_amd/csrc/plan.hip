@@ -92,22 +92,7 @@ __global__ void __launch_bounds__(PLAN_THREADS) k_plan(const int64_t *cu, int ns
     plan.counts[1] = run;
     plan.counts[2] = longest;
   }
-  __syncthreads();
-  // Query block list, level by level from the last block position down.
-  int maxqb = (longest + QB - 1) / QB;
-  int pos = 0;
-  for (int lvl = maxqb - 1; lvl >= 0; --lvl) {
-    for (int base = 0; base < nseq; base += PLAN_THREADS) {
-      int s = base + t;
-      int flag = 0;
-      if (s < nseq) flag = ((plan.seq_len[s] + QB - 1) / QB) > lvl;
-      int excl;
-      int tot = block_scan(flag, tmp, excl);
-      if (flag) plan.qitems[pos + excl] = make_int2(s, lvl);
-      pos += tot;
-    }
-  }
-  if (t == 0) plan.counts[0] = pos;
+  if (t == 0) plan.counts[0] = run128;
 }
 
 hipError_t launch_plan(const int64_t *cu, int nseq, int T, int64_t Ttot, const Plan &plan, hipStream_t st) {

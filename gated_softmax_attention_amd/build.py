@@ -27,6 +27,19 @@ COMMON_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 
+# Backward kernels: MFMA results in the VGPR form.  These kernels run one wave
+# per SIMD with their dk/dv accumulators in AGPRs; with the compiler's default
+# choice every product then writes AGPRs, and the score and dP tiles (read by
+# vector code right after) displace accumulators into VGPRs and back on every
+# step.  In the VGPR form the allocator places each product's result where its
+# readers want it.
+EXTRA_FLAGS = {"bwd_d": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
+def flags_for(src: str) -> list:
+    name = os.path.basename(src)
+    return [f for key, fl in EXTRA_FLAGS.items() if name.startswith(key) for f in fl]
+
 
 def sources() -> list:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + [os.path.join(CSRC, "api.cpp")]
@@ -42,7 +55,7 @@ def _compile(src: str, force: bool) -> str:
     if not force and os.path.exists(obj):
         if os.path.getmtime(obj) >= max(os.path.getmtime(src), _headers_mtime()):
             return obj
-    cmd = [HIPCC, "-x", "hip", *COMMON_FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, "-x", "hip", *COMMON_FLAGS, *flags_for(src), "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{res.stderr}")

@@ -861,14 +861,15 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
   constexpr int NCOPY = F32IN ? QTTD::NW + DR::NW + DTTD::NW + 1 : QT::NW + QTTD::NW + DR::NW + DTTD::NW + 1;
   // One LDS object for every tile (see the forward kernel).
   constexpr int O_Q = 0, O_QT = O_Q + NB * QT::BYTES, O_D = O_QT + NB * QTT::BYTES, O_DT = O_D + NB * DR::BYTES;
-  constexpr int O_V = O_DT + NB * DTT::BYTES, O_M = O_V + VRT::BYTES, O_G = O_M + NB * 256;
-  __shared__ __align__(1024) char smem[O_G + 2 * DVP * 4];
+  constexpr int O_V = O_DT + NB * DTT::BYTES, O_M = O_V + VRT::BYTES, O_G = O_M + NB * 256, O_GH = O_G + 2 * DVP * 4;
+  __shared__ __align__(1024) char smem[O_GH + 2 * DVP * 2];
   auto Qs = [&](int b) { return smem + O_Q + b * QT::BYTES; };
   auto Qts = [&](int b) { return smem + O_QT + b * QTT::BYTES; };
   auto Ds = [&](int b) { return smem + O_D + b * DR::BYTES; };
   auto Dts = [&](int b) { return smem + O_DT + b * DTT::BYTES; };
   auto Ms = [&](int b) { return (float *)(smem + O_M + b * 256); };  // 64 floats, 32 used
   auto gam = [&](int b) { return (float *)(smem + O_G) + b * DVP; };
+  auto gamh = [&](int b) { return (_Float16 *)(smem + O_GH) + b * DVP; };  // the same, fp16
 
   const Plan &pl = a.plan;
   const int Hq = a.Hq, Hkv = a.Hkv, G = Hq / Hkv;
@@ -964,7 +965,11 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
     uint32_t ovr[VRT::NW];
     VRT::lane_offsets(DV * 2, wave, lane, ovr);
     VRT::dma(smem + O_V, make_rsrc(a.Vr + ((int64_t)(cbs + J) * Hkv + c) * CB * DV, (int64_t)CB * DV * 2), ovr, wave);
-    if (tid < DV) gam(0)[tid] = fast_exp2((float)(lam_of(I1) - lamJ));
+    if (tid < DV) {
+      const float g0 = fast_exp2((float)(lam_of(I1) - lamJ));
+      gam(0)[tid] = g0;
+      gamh(0)[tid] = (_Float16)g0;
+    }
     for (int k = 0; k < DIST; ++k) {  // steps 0 .. DIST - 1 (the last step again past the end)
       stage_tile(ahead, k);
       if (k + 1 < nsteps) advance(ahead);
@@ -983,16 +988,13 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
     if (cur.ord != prev_ord) {  // first step of a query chunk
       prev_ord = cur.ord;
       const float *gm = gam(cur.ord & 1);
+      const _Float16 *gmh = gamh(cur.ord & 1);
 #pragma unroll
       for (int i = 0; i < NSV; ++i) {
-        uint4 r, g0, g1, gc;
-        lds_read4(r, g0, g1, gc, smem + O_V + VRT::off(32 * wave + n, 2 * i + hh), gm + 16 * i + 8 * hh,
-                  gm + 16 * i + 8 * hh + 4, gm + min(32 * (i & (NBV - 1)) + n, DV - 1));
-        const f16x8 raw = __builtin_bit_cast(f16x8, r);
-        const float4 a0 = __builtin_bit_cast(float4, g0), a1 = __builtin_bit_cast(float4, g1);
-        const float gv[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) vf[i][e] = (_Float16)((float)raw[e] * gv[e]);
+        uint4 r, gv, gc;
+        lds_read3(r, gv, gc, smem + O_V + VRT::off(32 * wave + n, 2 * i + hh), gmh + 16 * i + 8 * hh,
+                  gm + min(32 * (i & (NBV - 1)) + n, DV - 1));
+        vf[i] = __builtin_bit_cast(f16x8, r) * __builtin_bit_cast(f16x8, gv);
         // gamma of the lane's dV column 32 bv + n (bv = i for the first NBV i)
         if (i < NBV) gh[i] = 32 * i + n < DV ? (_Float16)__uint_as_float(gc.x) : (_Float16)0.f;
       }
@@ -1005,6 +1007,15 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
       mq[1] = __builtin_bit_cast(float4, m1);
       mq[2] = __builtin_bit_cast(float4, m2);
       mq[3] = __builtin_bit_cast(float4, m3);
+    }
+    if (qt0 + 32 > L) {  // rows past the end of the sequence: probability exp2(-inf) = 0
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        if (qt0 + acc_row(hh, 4 * q4) >= L) mq[q4].x = __builtin_inff();
+        if (qt0 + acc_row(hh, 4 * q4 + 1) >= L) mq[q4].y = __builtin_inff();
+        if (qt0 + acc_row(hh, 4 * q4 + 2) >= L) mq[q4].z = __builtin_inff();
+        if (qt0 + acc_row(hh, 4 * q4 + 3) >= L) mq[q4].w = __builtin_inff();
+      }
     }
     // The position after this step: its chunk's gamma is due at the end of
     // this step if the chunk changes.
@@ -1049,7 +1060,7 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int j = 4 * q4 + e;
-          const float pv = qt0 + acc_row(hh, j) < L ? fast_exp2(sc[j] * sl2 - mv[e]) : 0.f;
+          const float pv = fast_exp2(sc[j] * sl2 - mv[e]);  // rows past the end: mv = inf
           pf[j >> 3][j & 7] = (_Float16)pv;
           dsf[j >> 3][j & 7] = (_Float16)(pv * dp[j]);
         }
@@ -1066,7 +1077,11 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
     }
     // gamma of the next chunk, into the other buffer (its last readers passed
     // the barrier that ended the first step of the previous chunk).
-    if (next_chunk && tid < DV) gam(nxt.ord & 1)[tid] = fast_exp2((float)(lamI - lamJ));
+    if (next_chunk && tid < DV) {
+      const float gn = fast_exp2((float)(lamI - lamJ));
+      gam(nxt.ord & 1)[tid] = gn;
+      gamh(nxt.ord & 1)[tid] = (_Float16)gn;
+    }
     cur = nxt;
     wait_vm<(DIST - 1) * NCOPY>();  // the copies of step k + 1 have landed
     lds_barrier();

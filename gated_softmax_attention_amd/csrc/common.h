@@ -216,6 +216,17 @@ __device__ inline void lds_read4(uint4 &r0, uint4 &r1, uint4 &r2, uint4 &r3, con
       : "memory");
 }
 
+__device__ inline void lds_read3(uint4 &r0, uint4 &r1, uint4 &r2, const void *p0, const void *p1, const void *p2) {
+  asm volatile(
+      "ds_read_b128 %0, %3\n\t"
+      "ds_read_b128 %1, %4\n\t"
+      "ds_read_b128 %2, %5\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2)
+      : "v"(lds_addr(p0)), "v"(lds_addr(p1)), "v"(lds_addr(p2))
+      : "memory");
+}
+
 // Workgroup barrier that orders LDS accesses only.  __syncthreads() is a
 // release/acquire for every address space, which makes each wave wait for
 // all its vector-memory loads before the barrier, direct LDS copies issued for

@@ -119,13 +119,59 @@ __global__ void __launch_bounds__(256) k_tiles_t(const void *__restrict__ in, bo
   }
 }
 
+// Eight consecutive elements of a row, as fp32.
+__device__ inline void load8(const void *p, int64_t idx, bool is_f32, float (&v)[8]) {
+  if (is_f32) {
+    const float4 lo = *(const float4 *)((const float *)p + idx), hi = *(const float4 *)((const float *)p + idx + 4);
+    v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w; v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+  } else {
+    const uint4 r = *(const uint4 *)((const uint16_t *)p + idx);
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+}
+__device__ inline void load8f(const float *p, int64_t idx, float (&v)[8]) { load8(p, idx, true, v); }
+__device__ inline void store8f(float *p, int64_t idx, const float (&v)[8]) {
+  *(float4 *)(p + idx) = make_float4(v[0], v[1], v[2], v[3]);
+  *(float4 *)(p + idx + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+__device__ inline void store8(void *p, int64_t idx, const float (&v)[8], bool is_f32) {
+  if (is_f32) {
+    store8f((float *)p, idx, v);
+  } else {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f32_to_bf16_rne(v[2 * i]) | ((uint32_t)f32_to_bf16_rne(v[2 * i + 1]) << 16);
+    *(uint4 *)((uint16_t *)p + idx) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+template <class T> __device__ inline void store8h(T *p, int64_t idx, const T (&v)[8]) {
+  uint16_t u[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) u[i] = __builtin_bit_cast(uint16_t, v[i]);
+  *(uint4 *)((uint16_t *)p + idx) = make_uint4(u[0] | (u[1] << 16), u[2] | (u[3] << 16), u[4] | (u[5] << 16), u[6] | (u[7] << 16));
+}
+
+// One workgroup per 128-token chunk and kv head, each query head of the group
+// in turn.  A thread owns eight consecutive channels of a token row (16-byte
+// loads and stores; DV / 8 threads per row, row reductions by lane shuffles
+// inside that group).  The transposed tiles are built in LDS one 32-token
+// segment at a time and written out as 16-byte row pieces.
 template <int DV>
 __global__ void __launch_bounds__(256) k_bwd_prep(PrepArgs a) {
-  constexpr int STR = CB + 8;
-  constexpr int PER = (DV + 63) / 64;  // channels per lane
-  __shared__ _Float16 tile[DV * STR];
-  __shared__ __bf16 tileh[DV * STR], tilel[DV * STR];
-  const int gc = blockIdx.x, c = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  constexpr int TPR = DV / 8;        // threads per token row
+  constexpr int RPP = 256 / TPR;     // rows per pass of the workgroup
+  constexpr int SEG = 32;            // tokens per tile segment
+  constexpr int STR = SEG + 8;       // LDS tile row stride (elements; rows 16-byte aligned)
+  constexpr int TILE = DV * STR * 2, RED = RPP * DV * 4;
+  __shared__ __align__(16) char smem[3 * TILE > RED ? 3 * TILE : RED];
+  _Float16 *tile = (_Float16 *)smem;
+  __bf16 *tileh = (__bf16 *)(smem + TILE), *tilel = (__bf16 *)(smem + 2 * TILE);
+  const int gc = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
   if (gc >= a.plan.counts[0]) return;
   const Plan &pl = a.plan;
   const int s = seq_of_chunk(pl.cb128, pl.nseq, gc);
@@ -133,145 +179,139 @@ __global__ void __launch_bounds__(256) k_bwd_prep(PrepArgs a) {
   const int n = min(CB, pl.seq_len[s] - t0);
   const int64_t tok0 = (int64_t)pl.seq_start[s] + t0;
   const int Hq = a.Hq, Hkv = a.Hkv, G = Hq / Hkv;
-  const bool in_f32 = a.in_f32;
+  const bool in_f32 = a.in_f32, o_norm = a.o_norm;
+  const int sub = tid % TPR, d0 = 8 * sub, rr = tid / TPR;  // channels d0 .. d0 + 7 of row rr (+ RPP k)
 
-  float wv[PER], dwacc[PER];
+  float wv[8], dwacc[8];
+  if (o_norm && a.w) load8(a.w, d0, in_f32, wv);
+  else
 #pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    int d = lane + 64 * k;
-    wv[k] = (a.o_norm && a.w && d < DV) ? load_in(a.w, d, in_f32) : 1.f;
-    dwacc[k] = 0.f;
-  }
+    for (int i = 0; i < 8; ++i) wv[i] = 1.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) dwacc[i] = 0.f;
+
   for (int gq = 0; gq < G; ++gq) {
     const int h = c * G + gq;
-    // U tokens per wave at a time: every input of the U rows is loaded
-    // before any output is stored (the compiler cannot tell the buffers
-    // apart, so interleaving would make each row wait for the previous
-    // row's stores).
-    constexpr int U = 4;
+    for (int hf = 0; hf < CB / SEG; ++hf) {
 #pragma unroll 1
-    for (int i0 = 0; i0 < CB / 4; i0 += U) {
-      float r[U], mrow[U], xv[U][PER], go[U][PER], zz[U][PER], gl[U][PER], gbs[U][PER], qo[U][PER];
+      for (int r = rr; r < SEG; r += RPP) {
+        const int t = SEG * hf + r;  // token within the chunk
+        const int tc = min(t, n - 1);  // rows past the end repeat the last (nothing stored)
+        const int64_t tok = tok0 + tc;
+        const int64_t rb = (tok * Hq + h) * DV + d0, gi = (tok * Hkv + c) * DV + d0;
+        // every input of the row first (see the note on stores below)
+        float xv[8], go[8], zz[8], gl[8], gbs[8], qo[8];
+        load8f(a.x, rb, xv);
+        load8(a.dO, rb, in_f32, go);
+        if (a.z) load8(a.z, rb, in_f32, zz);
+        load8f(a.Gl2, gi, gl);
+        if (tc & ~31) load8f(a.Gl2, ((tok0 + (tc & ~31) - 1) * Hkv + c) * DV + d0, gbs);
+        if (gq > 0) load8f(a.qside, gi, qo);
+        const float rs = a.rstd[tok * Hq + h], mrow = a.m[tok * Hq + h];
+        if (!a.z)
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int t = min(wave + 4 * (i0 + u), n - 1);  // rows past the end repeat the last (not stored)
-        const int64_t tok = tok0 + t;
-        const int64_t rb = (tok * Hq + h) * DV;
-        r[u] = a.rstd[tok * Hq + h];
-        mrow[u] = a.m[tok * Hq + h];
+          for (int i = 0; i < 8; ++i) zz[i] = 1.f;
+        if (!(tc & ~31))
 #pragma unroll
-        for (int k = 0; k < PER; ++k) {
-          const int d = min(lane + 64 * k, DV - 1);
-          const int64_t gi = (tok * Hkv + c) * DV + d;
-          xv[u][k] = a.x[rb + d];
-          go[u][k] = load_in(a.dO, rb + d, in_f32);
-          zz[u][k] = a.z ? load_in(a.z, rb + d, in_f32) : 1.f;
-          gl[u][k] = a.Gl2[gi];
-          gbs[u][k] = (t & ~31) ? a.Gl2[((tok0 + (t & ~31) - 1) * Hkv + c) * DV + d] : 0.f;
-          qo[u][k] = gq == 0 ? 0.f : a.qside[gi];
+          for (int i = 0; i < 8; ++i) gbs[i] = 0.f;
+        if (gq == 0)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) qo[i] = 0.f;
+
+        float dn[8], nval[8], proj = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          dn[i] = go[i] * zz[i];
+          nval[i] = o_norm ? xv[i] * rs * wv[i] : xv[i];
+          proj += dn[i] * wv[i] * xv[i] * rs;
         }
-      }
+        if (o_norm) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int t = wave + 4 * (i0 + u);  // token within the chunk
-        if (t < n) {
-          const int64_t tok = tok0 + t;
-          const int64_t rb = (tok * Hq + h) * DV;
-          float dn[PER], del[PER];
-          float proj = 0.f;
+          for (int off = TPR / 2; off > 0; off >>= 1) proj += __shfl_xor(proj, off);
+          proj *= 1.f / DV;
+        }
+        // sigma = 2^-e scales the row so that max |sigma delta| is about 1; every
+        // fp16 operand built from the row (exp(Gl) sigma delta, within a block
+        // exp(Gl_i - Gl_ref) sigma delta, all factors <= 1) stays in range
+        float del[8], amax = 0.f;
 #pragma unroll
-          for (int k = 0; k < PER; ++k) {
-            const int d = lane + 64 * k;
-            dn[k] = 0.f;
-            if (d < DV) {
-              dn[k] = go[u][k] * zz[u][k];
-              const float nval = a.o_norm ? xv[u][k] * r[u] * wv[k] : xv[u][k];
-              if (a.dz) store_out(a.dz, rb + d, go[u][k] * nval, a.out_f32);
-              if (a.o_norm) {
-                dwacc[k] += dn[k] * xv[u][k] * r[u];
-                proj += dn[k] * wv[k] * xv[u][k] * r[u];
-              }
-            }
-          }
-          if (a.o_norm) {
+        for (int i = 0; i < 8; ++i) {
+          del[i] = o_norm ? rs * (dn[i] * wv[i] - xv[i] * rs * proj) : dn[i];
+          amax = fmaxf(amax, fabsf(del[i]));
+        }
 #pragma unroll
-            for (int off = 32; off > 0; off >>= 1) proj += __shfl_xor(proj, off);
-            proj *= 1.f / DV;
-          }
-          // sigma = 2^-e scales the row so that max |sigma delta| is about 1; every
-          // fp16 operand built from the row (here exp(Gl) sigma delta, within a
-          // block exp(Gl_i - Gl_ref) sigma delta, all factors <= 1) stays in range
-          float amax = 0.f;
+        for (int off = TPR / 2; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+        int e = 0;
+        if (amax > 0.f) e = min(15, max(-15, (int)ceilf(__log2f(amax))));
+        const float sg = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e
+        _Float16 hv[8], x16[8];
+        __bf16 xh[8], xl[8];
+        float qs[8], dzv[8];
 #pragma unroll
-          for (int k = 0; k < PER; ++k) {
-            del[k] = a.o_norm ? r[u] * (dn[k] * wv[k] - xv[u][k] * r[u] * proj) : dn[k];
-            if (lane + 64 * k < DV) amax = fmaxf(amax, fabsf(del[k]));
-          }
+        for (int i = 0; i < 8; ++i) {
+          // query side of dG, summed over the group ((token, channel) is owned by
+          // this thread for every head of the group)
+          qs[i] = qo[i] + del[i] * xv[i];
+          dzv[i] = go[i] * nval[i];
+          hv[i] = (_Float16)(fast_exp2(gl[i]) * del[i] * sg);
+          // relative to the token before the row's 32-token block (<= 1)
+          const float xb = fast_exp2(gl[i] - gbs[i]) * del[i] * sg;
+          x16[i] = (_Float16)xb;
+          xh[i] = (__bf16)xb;
+          xl[i] = (__bf16)(xb - (float)xh[i]);
+        }
+        const bool valid = t < n;
+        const int pos = key_pos(r);
 #pragma unroll
-          for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-          int e = 0;
-          if (amax > 0.f) e = min(15, max(-15, (int)ceilf(__log2f(amax))));
-          const float sg = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e
+        for (int i = 0; i < 8; ++i) {
+          tile[(d0 + i) * STR + pos] = valid ? hv[i] : (_Float16)0.f;
+          tileh[(d0 + i) * STR + pos] = valid ? xh[i] : (__bf16)0.f;
+          tilel[(d0 + i) * STR + pos] = valid ? xl[i] : (__bf16)0.f;
+        }
+        if (valid) {
+          if (o_norm)
 #pragma unroll
-          for (int k = 0; k < PER; ++k) {
-            const int d = lane + 64 * k;
-            if (d < DV) {
-              a.delta[rb + d] = del[k];
-              // query side of dG, summed over the group; (token, channel) is
-              // owned by this thread for every head of the group
-              a.qside[(tok * Hkv + c) * DV + d] = qo[u][k] + del[k] * xv[u][k];
-              const _Float16 hv = (_Float16)(fast_exp2(gl[u][k]) * del[k] * sg);
-              a.dh[rb + d] = hv;
-              tile[d * STR + key_pos(t)] = hv;
-              // relative to the token before the row's 32-token block (<= 1)
-              const float xb = fast_exp2(gl[u][k] - gbs[u][k]) * del[k] * sg;
-              const __bf16 xh = (__bf16)xb, xl = (__bf16)(xb - (float)xh);
-              a.X16[rb + d] = (_Float16)xb;
-              a.XH[rb + d] = xh;
-              a.XL[rb + d] = xl;
-              tileh[d * STR + key_pos(t)] = xh;
-              tilel[d * STR + key_pos(t)] = xl;
-            }
-          }
-          if (lane == 0) {
-            a.mb[tok * Hq + h] = mrow[u] * LOG2E - (float)e;
+            for (int i = 0; i < 8; ++i) dwacc[i] += dn[i] * xv[i] * rs;
+          // The row's outputs after all of its inputs: the compiler cannot tell
+          // the buffers apart, so a load placed after a store would wait for it.
+          if (a.dz) store8(a.dz, rb, dzv, a.out_f32);
+          store8f(a.delta, rb, del);
+          store8f(a.qside, gi, qs);
+          store8h(a.dh, rb, hv);
+          store8h(a.X16, rb, x16);
+          store8h(a.XH, rb, xh);
+          store8h(a.XL, rb, xl);
+          if (sub == 0) {
+            a.mb[tok * Hq + h] = mrow * LOG2E - (float)e;
             a.sig[tok * Hq + h] = sg;
           }
-        } else {
-#pragma unroll
-          for (int k = 0; k < PER; ++k) {
-            const int d = lane + 64 * k;
-            if (d < DV) {
-              tile[d * STR + key_pos(t)] = (_Float16)0.f;
-              tileh[d * STR + key_pos(t)] = (__bf16)0.f;
-              tilel[d * STR + key_pos(t)] = (__bf16)0.f;
-            }
-          }
         }
       }
+      __syncthreads();
+      // the segment's tile rows: DV rows of SEG keys, 16-byte pieces
+      const int64_t tb = ((int64_t)gc * Hq + h) * DV * CB + SEG * hf;
+      for (int e = tid; e < DV * SEG / 8; e += 256) {
+        const int d = e / (SEG / 8), p8 = e % (SEG / 8);
+        const int64_t o = tb + (int64_t)d * CB + 8 * p8;
+        *(uint4 *)(a.dht + o) = *(const uint4 *)&tile[d * STR + 8 * p8];
+        *(uint4 *)(a.XTH + o) = *(const uint4 *)&tileh[d * STR + 8 * p8];
+        *(uint4 *)(a.XTL + o) = *(const uint4 *)&tilel[d * STR + 8 * p8];
+      }
+      __syncthreads();
     }
-    __syncthreads();
-    const int64_t tb = ((int64_t)gc * Hq + h) * DV * CB;
-    uint4 *dst = (uint4 *)(a.dht + tb), *dsth = (uint4 *)(a.XTH + tb), *dstl = (uint4 *)(a.XTL + tb);
-    for (int e = tid; e < DV * CB / 8; e += 256) {
-      int d = e / (CB / 8), p8 = e % (CB / 8);
-      dst[e] = *(const uint4 *)&tile[d * STR + 8 * p8];
-      dsth[e] = *(const uint4 *)&tileh[d * STR + 8 * p8];
-      dstl[e] = *(const uint4 *)&tilel[d * STR + 8 * p8];
-    }
-    __syncthreads();
   }
   if (a.dw_part) {
-    // per-block partials: reduce the four waves in LDS, then one row per block
-    __shared__ float red[4][DV];
+    // per-block partials: the rows of the block's threads summed in LDS (the
+    // tile memory, free after the last barrier), then one row per block
+    float *red = (float *)smem;  // [RPP][DV]
 #pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      int d = lane + 64 * k;
-      if (d < DV) red[wave][d] = dwacc[k];
-    }
+    for (int i = 0; i < 8; ++i) red[rr * DV + d0 + i] = dwacc[i];
     __syncthreads();
-    for (int d = tid; d < DV; d += 256)
-      a.dw_part[((int64_t)gc * Hkv + c) * DV + d] = red[0][d] + red[1][d] + red[2][d] + red[3][d];
+    for (int d = tid; d < DV; d += 256) {
+      float acc = 0.f;
+      for (int q = 0; q < RPP; ++q) acc += red[q * DV + d];
+      a.dw_part[((int64_t)gc * Hkv + c) * DV + d] = acc;
+    }
   }
 }
 

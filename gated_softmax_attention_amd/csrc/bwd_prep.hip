@@ -27,35 +27,62 @@ namespace fix {
 // V scaled to the end of its 32-token block, VE[t][kvh][d] (the block end
 // clamped to the sequence end).
 template <int DV>
-__global__ void __launch_bounds__(128) k_gate_prep_rows(const float *__restrict__ g, const void *__restrict__ v,
-                                                        bool in_f32, Plan plan, int Hkv, float *__restrict__ Gl2,
-                                                        float *__restrict__ Gam, _Float16 *__restrict__ Vr,
-                                                        _Float16 *__restrict__ VE) {
-  const int gc = blockIdx.x, c = blockIdx.y, d = threadIdx.x;
-  if (gc >= plan.counts[0] || d >= DV) return;
+__global__ void __launch_bounds__(8 * DV) k_gate_prep_rows(const float *__restrict__ g, const void *__restrict__ v,
+                                                           bool in_f32, Plan plan, int Hkv, float *__restrict__ Gl2,
+                                                           float *__restrict__ Gam, _Float16 *__restrict__ Vr,
+                                                           _Float16 *__restrict__ VE) {
+  // Thread (blk, d): channel d of the chunk's 16-token piece blk.  Each piece's
+  // local prefix sums, then the totals of the pieces before it (through LDS).
+  constexpr int NP = CB / 16;
+  __shared__ float tot[NP][DV];
+  const int gc = blockIdx.x, c = blockIdx.y, d = threadIdx.x % DV, blk = threadIdx.x / DV;
+  if (gc >= plan.counts[0]) return;
   const int s = seq_of_chunk(plan.cb128, plan.nseq, gc);
   const int t0 = (gc - plan.cb128[s]) * CB;
   const int n = min(CB, plan.seq_len[s] - t0);
   const int64_t tok0 = (int64_t)plan.seq_start[s] + t0;
+  const int j0 = 16 * blk;
+  // every load of the piece first (rows past the end repeat the last row, unused)
+  float gl[16], vv[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int64_t idx = ((tok0 + min(j0 + j, n - 1)) * Hkv + c) * DV + d;
+    gl[j] = g[idx];
+    vv[j] = load_in(v, idx, in_f32);
+  }
   float acc = 0.f;
-  for (int j = 0; j < n; ++j) {
-    int64_t idx = ((tok0 + j) * Hkv + c) * DV + d;
-    acc += g[idx] * LOG2E;
-    Gl2[idx] = acc;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (j0 + j < n) acc += gl[j] * LOG2E;
+    gl[j] = acc;  // past the end the prefix stops growing
+  }
+  tot[blk][d] = acc;
+  __syncthreads();
+  // totals of the pieces before this one, and of the pieces of this one's
+  // 32-token block (for the block end) and of the whole chunk
+  float before = 0.f, all = 0.f, blkend = 0.f;
+#pragma unroll
+  for (int q = 0; q < NP; ++q) {
+    const float tq = tot[q][d];
+    before += q < blk ? tq : 0.f;
+    blkend += q <= (blk | 1) ? tq : 0.f;
+    all += tq;
   }
   const int64_t cidx = ((int64_t)gc * Hkv + c);
-  Gam[cidx * DV + d] = fast_exp2(acc);
+  if (blk == 0) Gam[cidx * DV + d] = fast_exp2(all);
   _Float16 *dst = Vr + cidx * CB * DV + d;
-  for (int j = 0; j < CB; ++j) {
+  const float gbe = blkend - before;  // 32-token block end (clamped to the sequence end), piece-local
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int t = j0 + j;
     float val = 0.f;
-    if (j < n) {
-      int64_t idx = ((tok0 + j) * Hkv + c) * DV + d;
-      const float gj = Gl2[idx], vj = load_in(v, idx, in_f32);
-      val = fast_exp2(acc - gj) * vj;
-      const float gbe = Gl2[((tok0 + min((j | 31), n - 1)) * Hkv + c) * DV + d];
-      VE[idx] = (_Float16)(fast_exp2(gbe - gj) * vj);
+    if (t < n) {
+      const int64_t idx = ((tok0 + t) * Hkv + c) * DV + d;
+      Gl2[idx] = before + gl[j];
+      val = fast_exp2(all - before - gl[j]) * vv[j];
+      VE[idx] = (_Float16)(fast_exp2(gbe - gl[j]) * vv[j]);
     }
-    dst[(int64_t)j * DV] = (_Float16)val;
+    dst[(int64_t)t * DV] = (_Float16)val;
   }
 }
 
@@ -400,7 +427,7 @@ __global__ void __launch_bounds__(128) k_dg_final(const float *__restrict__ dG, 
 hipError_t launch_gate_prep_rows(int dv, const float *g, const void *v, bool in_f32, const Plan &plan, int Hkv,
                                  int ncb_ub, float *Gl2, float *Gam, _Float16 *Vr, _Float16 *VE, hipStream_t st) {
   dim3 grid(ncb_ub, Hkv);
-  FIX_DV_SWITCH(dv, hipLaunchKernelGGL(k_gate_prep_rows<DVC>, grid, dim3(128), 0, st, g, v, in_f32, plan, Hkv,
+  FIX_DV_SWITCH(dv, hipLaunchKernelGGL(k_gate_prep_rows<DVC>, grid, dim3(8 * DVC), 0, st, g, v, in_f32, plan, Hkv,
                                        Gl2, Gam, Vr, VE));
   return hipGetLastError();
 }

@@ -22,11 +22,16 @@
 namespace fix {
 
 template <int DV>
-__global__ void __launch_bounds__(128) k_gate_prep(const float *__restrict__ g, const void *__restrict__ v,
-                                                   bool in_f32, Plan plan, int Hkv, float *__restrict__ Gl2,
-                                                   float *__restrict__ Gam, _Float16 *__restrict__ VtT) {
-  const int gc = blockIdx.x, c = blockIdx.y, d = threadIdx.x;
-  if (gc >= plan.counts[1] || d >= DV) return;
+__global__ void __launch_bounds__(4 * DV) k_gate_prep(const float *__restrict__ g, const void *__restrict__ v,
+                                                      bool in_f32, Plan plan, int Hkv, float *__restrict__ Gl2,
+                                                      float *__restrict__ Gam, _Float16 *__restrict__ VtT) {
+  // Thread (blk, d): channel d of the chunk's 16-token piece blk: piece-local
+  // prefix sums, then the totals of the pieces before it (through LDS).
+  constexpr int STR = CH + 8, NP = CH / 16;
+  __shared__ float tot[NP][DV];
+  __shared__ __align__(16) _Float16 tile[DV * STR];
+  const int gc = blockIdx.x, c = blockIdx.y, d = threadIdx.x % DV, blk = threadIdx.x / DV;
+  if (gc >= plan.counts[1]) return;
   int lo = 0, hi = plan.nseq - 1;
   while (lo < hi) {  // last sequence whose first chunk is <= gc (skips empty sequences)
     int mid = (lo + hi + 1) >> 1;
@@ -36,44 +41,61 @@ __global__ void __launch_bounds__(128) k_gate_prep(const float *__restrict__ g, 
   const int t0 = (gc - plan.chunk_base[s]) * CH;
   const int n = min(CH, plan.seq_len[s] - t0);
   const int64_t tok0 = (int64_t)plan.seq_start[s] + t0;
+  const int j0 = 16 * blk;
 
   // All loads first (rows past the end repeat the last row and are not
   // used), so that they are in flight together.
-  float gl[CH], vv[CH];
+  float gl[16], vv[16];
 #pragma unroll
-  for (int j = 0; j < CH; ++j) {
-    const int64_t idx = ((tok0 + min(j, n - 1)) * Hkv + c) * DV + d;
+  for (int j = 0; j < 16; ++j) {
+    const int64_t idx = ((tok0 + min(j0 + j, n - 1)) * Hkv + c) * DV + d;
     gl[j] = g[idx];
     vv[j] = load_in(v, idx, in_f32);
   }
   float acc = 0.f;
 #pragma unroll
-  for (int j = 0; j < CH; ++j) {
-    if (j < n) acc += gl[j] * LOG2E;
-    gl[j] = acc;
+  for (int j = 0; j < 16; ++j) {
+    if (j0 + j < n) acc += gl[j] * LOG2E;
+    gl[j] = acc;  // past the end the prefix stops growing
+  }
+  tot[blk][d] = acc;
+  __syncthreads();
+  float before = 0.f, all = 0.f;
+#pragma unroll
+  for (int q = 0; q < NP; ++q) {
+    before += q < blk ? tot[q][d] : 0.f;
+    all += tot[q][d];
   }
 #pragma unroll
-  for (int j = 0; j < CH; ++j)
-    if (j < n) Gl2[((tok0 + j) * Hkv + c) * DV + d] = gl[j];
+  for (int j = 0; j < 16; ++j)
+    if (j0 + j < n) Gl2[((tok0 + j0 + j) * Hkv + c) * DV + d] = before + gl[j];
   const int64_t cidx = ((int64_t)gc * Hkv + c) * DV + d;
-  Gam[cidx] = fast_exp2(acc);
+  if (blk == 0) Gam[cidx] = fast_exp2(all);
 
-  _Float16 row[CH];
+  // The transposed tile goes through LDS (this thread's 16 keys, then the
+  // workgroup's DV x CH tile back out as consecutive 16-byte pieces, so that
+  // each store instruction writes whole cache lines).
+  _Float16 row[16];
 #pragma unroll
-  for (int j = 0; j < CH; ++j) row[key_pos(j)] = (_Float16)(j < n ? fast_exp2(acc - gl[j]) * vv[j] : 0.f);
-  uint4 *dst = (uint4 *)(VtT + cidx * CH);
+  for (int j = 0; j < 16; ++j)
+    row[key_pos(j)] = (_Float16)(j0 + j < n ? fast_exp2(all - before - gl[j]) * vv[j] : 0.f);
 #pragma unroll
-  for (int p = 0; p < CH / 8; ++p) dst[p] = *(const uint4 *)(row + 8 * p);
+  for (int p = 0; p < 2; ++p) *(uint4 *)&tile[d * STR + j0 + 8 * p] = *(const uint4 *)(row + 8 * p);
+  __syncthreads();
+  uint4 *dst = (uint4 *)(VtT + ((int64_t)gc * Hkv + c) * DV * CH);
+#pragma unroll
+  for (int e = threadIdx.x; e < DV * CH / 8; e += 4 * DV)
+    dst[e] = *(const uint4 *)&tile[(e / (CH / 8)) * STR + 8 * (e % (CH / 8))];
 }
 
 hipError_t launch_gate_prep(int dv, const float *g, const void *v, bool in_f32, const Plan &plan, int Hkv,
                             int nch_ub, float *Gl2, float *Gam, _Float16 *VtT, hipStream_t st) {
-  dim3 grid(nch_ub, Hkv), block(128);
+  dim3 grid(nch_ub, Hkv);
   switch (dv) {
-    case 16: hipLaunchKernelGGL(k_gate_prep<16>, grid, block, 0, st, g, v, in_f32, plan, Hkv, Gl2, Gam, VtT); break;
-    case 32: hipLaunchKernelGGL(k_gate_prep<32>, grid, block, 0, st, g, v, in_f32, plan, Hkv, Gl2, Gam, VtT); break;
-    case 64: hipLaunchKernelGGL(k_gate_prep<64>, grid, block, 0, st, g, v, in_f32, plan, Hkv, Gl2, Gam, VtT); break;
-    case 128: hipLaunchKernelGGL(k_gate_prep<128>, grid, block, 0, st, g, v, in_f32, plan, Hkv, Gl2, Gam, VtT); break;
+    case 16: hipLaunchKernelGGL(k_gate_prep<16>, grid, dim3(4 * 16), 0, st, g, v, in_f32, plan, Hkv, Gl2, Gam, VtT); break;
+    case 32: hipLaunchKernelGGL(k_gate_prep<32>, grid, dim3(4 * 32), 0, st, g, v, in_f32, plan, Hkv, Gl2, Gam, VtT); break;
+    case 64: hipLaunchKernelGGL(k_gate_prep<64>, grid, dim3(4 * 64), 0, st, g, v, in_f32, plan, Hkv, Gl2, Gam, VtT); break;
+    case 128: hipLaunchKernelGGL(k_gate_prep<128>, grid, dim3(4 * 128), 0, st, g, v, in_f32, plan, Hkv, Gl2, Gam, VtT); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -989,16 +989,29 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
       prev_ord = cur.ord;
       const float *gm = gam(cur.ord & 1);
       const _Float16 *gmh = gamh(cur.ord & 1);
+      // every read of the rebuild first (no copies are in flight here: the
+      // previous step waited for all of them)
+      f16x8 r[NSV], gv[NSV];
+      float gcol[NBV];
 #pragma unroll
       for (int i = 0; i < NSV; ++i) {
-        uint4 r, gv, gc;
-        lds_read3(r, gv, gc, smem + O_V + VRT::off(32 * wave + n, 2 * i + hh), gmh + 16 * i + 8 * hh,
-                  gm + min(32 * (i & (NBV - 1)) + n, DV - 1));
-        vf[i] = __builtin_bit_cast(f16x8, r) * __builtin_bit_cast(f16x8, gv);
-        // gamma of the lane's dV column 32 bv + n (bv = i for the first NBV i)
-        if (i < NBV) gh[i] = 32 * i + n < DV ? (_Float16)__uint_as_float(gc.x) : (_Float16)0.f;
+        r[i] = *(const f16x8 *)(smem + O_V + VRT::off(32 * wave + n, 2 * i + hh));
+        gv[i] = *(const f16x8 *)(gmh + 16 * i + 8 * hh);
       }
+#pragma unroll
+      for (int i = 0; i < NBV; ++i) gcol[i] = gm[min(32 * i + n, DV - 1)];
+#pragma unroll
+      for (int i = 0; i < NSV; ++i) vf[i] = r[i] * gv[i];
+      // gamma of the lane's dV column 32 bv + n
+#pragma unroll
+      for (int i = 0; i < NBV; ++i) gh[i] = 32 * i + n < DV ? (_Float16)gcol[i] : (_Float16)0.f;
     }
+    // The position after this step: its chunk's gamma is due at the end of
+    // this step if the chunk changes.
+    Pos nxt = cur;
+    if (k + 1 < nsteps) advance(nxt);
+    const bool next_chunk = nxt.ord != cur.ord;
+    double lamI;
     float4 mq[4];  // exponent offsets of the step's rows
     {
       uint4 m0, m1, m2, m3;
@@ -1008,25 +1021,6 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
       mq[2] = __builtin_bit_cast(float4, m2);
       mq[3] = __builtin_bit_cast(float4, m3);
     }
-    if (qt0 + 32 > L) {  // rows past the end of the sequence: probability exp2(-inf) = 0
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        if (qt0 + acc_row(hh, 4 * q4) >= L) mq[q4].x = __builtin_inff();
-        if (qt0 + acc_row(hh, 4 * q4 + 1) >= L) mq[q4].y = __builtin_inff();
-        if (qt0 + acc_row(hh, 4 * q4 + 2) >= L) mq[q4].z = __builtin_inff();
-        if (qt0 + acc_row(hh, 4 * q4 + 3) >= L) mq[q4].w = __builtin_inff();
-      }
-    }
-    // The position after this step: its chunk's gamma is due at the end of
-    // this step if the chunk changes.
-    Pos nxt = cur;
-    if (k + 1 < nsteps) advance(nxt);
-    const bool next_chunk = nxt.ord != cur.ord;
-    const double lamI = lam_of(nxt.I);
-    // Copies of step k + DIST (the last step again near the end, so that
-    // every step issues the same copies); `ahead` is that step's position.
-    stage_tile(ahead, (k + DIST) % NB);
-    if (k + DIST + 1 < nsteps) advance(ahead);
     {
       // S[q][key] and dP[q][key]: lane = key, register j = query acc_row(hh, j).
       // Operands of a group of products are read from LDS in one batch (one
@@ -1043,7 +1037,13 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
       for (int i = 0; i < NS; ++i) sc = mma32(qa[i], kf[i], sc);
 #pragma unroll
       for (int i = 0; i < NSV; ++i) dp = mma32(da[i], vf[i], dp);
-      __builtin_amdgcn_sched_barrier(0);
+      // While the products run, between them: the copies of step k + DIST
+      // (the last step again near the end, so that every step issues the
+      // same copies; `ahead` is that step's position), the next chunk's Lam
+      // row, the step's row offsets and the dV / dK operands.
+      stage_tile(ahead, (k + DIST) % NB);
+      if (k + DIST + 1 < nsteps) advance(ahead);
+      lamI = lam_of(nxt.I);
       f16x8 ta[NBV][2], tq[NBK][2];
 #pragma unroll
       for (int bv = 0; bv < NBV; ++bv)
@@ -1053,6 +1053,22 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
       for (int bk = 0; bk < NBK; ++bk)
 #pragma unroll
         for (int uu = 0; uu < 2; ++uu) tq[bk][uu] = *(const f16x8 *)(Qts(b) + QTT::off(32 * bk + n, 2 * uu + hh));
+#pragma unroll
+      for (int i = 0; i < NS + NSV; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one product
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one copy / global load
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (qt0 + 32 > L) {  // rows past the end of the sequence: probability exp2(-inf) = 0
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          if (qt0 + acc_row(hh, 4 * q4) >= L) mq[q4].x = __builtin_inff();
+          if (qt0 + acc_row(hh, 4 * q4 + 1) >= L) mq[q4].y = __builtin_inff();
+          if (qt0 + acc_row(hh, 4 * q4 + 2) >= L) mq[q4].z = __builtin_inff();
+          if (qt0 + acc_row(hh, 4 * q4 + 3) >= L) mq[q4].w = __builtin_inff();
+        }
+      }
       f16x8 pf[2], dsf[2];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {

@@ -138,9 +138,10 @@ __global__ void __launch_bounds__(256, 2) k_fix_fwd(FwdArgs a) {
   // Multiply accumulator row r by the row factor held in lane r of this half-wave pair.
   auto row_scale = [&](float f) {
     if (hh == 0) Asc[wave][n] = f;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    // A wave's LDS accesses complete in order: waiting for its own write is
+    // enough (a memory fence would also wait for the tile copies in flight).
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       float4 al = *(const float4 *)&Asc[wave][8 * q4 + 4 * hh];
@@ -177,13 +178,14 @@ __global__ void __launch_bounds__(256, 2) k_fix_fwd(FwdArgs a) {
   __syncthreads();
   for (int J = 0; J < nJ; ++J) {
     const int b = J & 1;
-    // The last step copies its own tile again into the idle buffer, so that
-    // every step issues the same copies.
-    stage_tile(min(J + 1, nJ - 1), b ^ 1);
-    if (active && J < Iw - 1) {
-      // Operands of a group of products are read from LDS in one batch (one
-      // wait for all of them rather than one per product).
-      f32x16 sc[2];
+    const bool comp = active && J < Iw - 1;
+    // Operands of a group of products are read from LDS in one batch (one
+    // wait for all of them rather than one per product).  The next tile's
+    // copies are issued between the first score products (the last step
+    // copies its own tile again into the idle buffer, so that every step
+    // issues the same copies).
+    f32x16 sc[2];
+    if (comp) {
 #pragma unroll
       for (int be = 0; be < 2; ++be) {
         kfrag ka[NS];
@@ -193,8 +195,20 @@ __global__ void __launch_bounds__(256, 2) k_fix_fwd(FwdArgs a) {
         sc[be] = zero16();
 #pragma unroll
         for (int i = 0; i < NS; ++i) sc[be] = mma32(ka[i], qf[i], sc[be]);
+        if (be == 0) {
+          stage_tile(min(J + 1, nJ - 1), b ^ 1);
+#pragma unroll
+          for (int i = 0; i < NS; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one product
+            __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // two copies
+          }
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
+    } else {
+      stage_tile(min(J + 1, nJ - 1), b ^ 1);
+    }
+    if (comp) {
       float mx = fmaxf(row_max(sc[0]), row_max(sc[1]));
       mx = max_across_halves(mx) * sl2;
       update_max(mx);

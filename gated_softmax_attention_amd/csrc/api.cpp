@@ -94,6 +94,7 @@ struct BwdWs {
   float *Gl2, *Gam;
   double *Lam;
   _Float16 *Vr, *Qt, *Kt, *VE;
+  __bf16 *VBH, *VBL;
   float *delta;
   _Float16 *dh, *dht, *X16;
   __bf16 *XH, *XL, *XTH, *XTL;
@@ -114,6 +115,8 @@ size_t carve_bwd(Carve &cv, const fix_attn_desc *d, BwdWs &w) {
   w.dh = cv.take<_Float16>(T * Hq * DV);
   w.dht = cv.take<_Float16>(ncb * Hq * DV * fix::CB);
   w.VE = cv.take<_Float16>(T * Hkv * DV);
+  w.VBH = cv.take<__bf16>(T * Hkv * DV);
+  w.VBL = cv.take<__bf16>(T * Hkv * DV);
   w.X16 = cv.take<_Float16>(T * Hq * DV);
   w.XH = cv.take<__bf16>(T * Hq * DV);
   w.XL = cv.take<__bf16>(T * Hq * DV);
@@ -253,7 +256,8 @@ fix_status fix_attn_bwd(const fix_attn_desc *d, const void *q, const void *k, co
   e = trace_begin(st);
   if (e != hipSuccess) return hip_fail(e);
   FIX_TRY(fix::launch_plan(d->cu_seqlens, (int)s.nseq, (int)d->T, s.Ttot, w.plan, st), "plan");
-  FIX_TRY(fix::launch_gate_prep_rows(DV, g, v, f32in, w.plan, Hkv, ncb, w.Gl2, w.Gam, w.Vr, w.VE, st), "gate_prep_rows");
+  FIX_TRY(fix::launch_gate_prep_rows(DV, g, v, f32in, w.plan, Hkv, ncb, w.Gl2, w.Gam, w.Vr, w.VE, w.VBH, w.VBL, st),
+          "gate_prep_rows");
   FIX_TRY(fix::launch_chunk_logprefix(DV, w.Gl2, w.plan, Hkv, w.Lam, st), "chunk_logprefix");
   FIX_TRY(fix::launch_tiles_t(DK, q, f32in, w.plan, Hq, ncb, w.Qt, st), "tiles_q");
   FIX_TRY(fix::launch_tiles_t(DK, k, f32in, w.plan, Hkv, ncb, w.Kt, st), "tiles_k");
@@ -274,7 +278,7 @@ fix_status fix_attn_bwd(const fix_attn_desc *d, const void *q, const void *k, co
   a.q = q; a.k = k; a.v = v;
   a.Gl2 = w.Gl2; a.Gam = w.Gam; a.Lam = w.Lam; a.Vr = w.Vr; a.Qt = w.Qt; a.Kt = w.Kt;
   a.delta = w.delta; a.dh = w.dh; a.dht = w.dht; a.mb = w.mb; a.sig = w.sig; a.qside = w.qside;
-  a.VE = w.VE; a.X16 = w.X16; a.XH = w.XH; a.XL = w.XL; a.XTH = w.XTH; a.XTL = w.XTL;
+  a.VE = w.VE; a.VBH = w.VBH; a.VBL = w.VBL; a.X16 = w.X16; a.XH = w.XH; a.XL = w.XL; a.XTH = w.XTH; a.XTL = w.XTL;
   a.dq_i = w.dq_i; a.dk_i = w.dk_i; a.dv_i = w.dv_i;
   a.dq = dq; a.dk = dk; a.dv = dv; a.dG = w.dG;
   a.plan = w.plan;

@@ -226,13 +226,10 @@ __global__ void __launch_bounds__(256, 1) k_bwd_intra_dq(BwdArgs a) {
       const int64_t kr = ((st + key) * Hkv + c) * DV, xrw = ((st + min(row, L - 1)) * Hq + hq) * DV;
 #pragma unroll
       for (int i = 0; i < NSV; ++i) {
-        bf16x8 vh, vl;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int d = 16 * i + 8 * hh + e;
-          const float val = kb + n < L ? fast_exp2(BE[wave][d] - a.Gl2[kr + d]) * load_in(a.v, kr + d, F32IN) : 0.f;
-          split_bf16(val, vh, vl, e);
-        }
+        // the key's V relative to the token before the block, bf16 hi / lo
+        const bf16x8 zero = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+        const bf16x8 vh = kb + n < L ? *(const bf16x8 *)(a.VBH + kr + 16 * i + 8 * hh) : zero;
+        const bf16x8 vl = kb + n < L ? *(const bf16x8 *)(a.VBL + kr + 16 * i + 8 * hh) : zero;
         const bf16x8 xh = *(const bf16x8 *)(a.XH + xrw + 16 * i + 8 * hh);
         const bf16x8 xl = *(const bf16x8 *)(a.XL + xrw + 16 * i + 8 * hh);
         dp = mma32(vh, xh, dp);
@@ -503,17 +500,15 @@ __global__ void __launch_bounds__(256, 1) k_bwd_intra_dkv(BwdArgs a) {
       gd[bv] = fast_exp2(BE[wave][d] - BE[wave + 1][d]);
     }
     const bool direct = __any(rng > BGUARD);
-    bf16x8 vh[NSV], vl[NSV];
+    bf16x8 vh[NSV], vl[NSV];  // the key's V relative to the token before the block, bf16 hi / lo
     if (!direct) {
       const int64_t kr = ((st + min(key, L - 1)) * Hkv + c) * DV;
+      const bf16x8 zero = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
 #pragma unroll
-      for (int i = 0; i < NSV; ++i)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int d = 16 * i + 8 * hh + e;
-          const float val = kv ? fast_exp2(BE[wave][d] - a.Gl2[kr + d]) * load_in(a.v, kr + d, F32IN) : 0.f;
-          split_bf16(val, vh[i], vl[i], e);
-        }
+      for (int i = 0; i < NSV; ++i) {
+        vh[i] = kv ? *(const bf16x8 *)(a.VBH + kr + 16 * i + 8 * hh) : zero;
+        vl[i] = kv ? *(const bf16x8 *)(a.VBL + kr + 16 * i + 8 * hh) : zero;
+      }
     }
     const int q0 = kb;
     const int qrow = min(q0 + n, L - 1);  // A-operand row of this lane

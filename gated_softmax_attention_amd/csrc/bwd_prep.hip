@@ -23,14 +23,17 @@
 namespace fix {
 
 // Gl2 (log2 units, 128-chunk local), Gam per 128-chunk, row-major fp16 V
-// scaled to its chunk end, Vr[chunk][kvh][t][d] = exp(Gl_end - Gl_t) v_t, and
-// V scaled to the end of its 32-token block, VE[t][kvh][d] (the block end
-// clamped to the sequence end).
+// scaled to its chunk end, Vr[chunk][kvh][t][d] = exp(Gl_end - Gl_t) v_t, V
+// scaled to the end of its 32-token block, VE[t][kvh][d] (the block end
+// clamped to the sequence end), and V relative to the token before its
+// 32-token block, VB = exp(Gl_blockstart-1 - Gl_t) v_t (>= |v_t|, fp32 range)
+// as bf16 hi / lo parts, the key operand of the diagonal blocks.
 template <int DV>
 __global__ void __launch_bounds__(8 * DV) k_gate_prep_rows(const float *__restrict__ g, const void *__restrict__ v,
                                                            bool in_f32, Plan plan, int Hkv, float *__restrict__ Gl2,
                                                            float *__restrict__ Gam, _Float16 *__restrict__ Vr,
-                                                           _Float16 *__restrict__ VE) {
+                                                           _Float16 *__restrict__ VE, __bf16 *__restrict__ VBH,
+                                                           __bf16 *__restrict__ VBL) {
   // Thread (blk, d): channel d of the chunk's 16-token piece blk.  Each piece's
   // local prefix sums, then the totals of the pieces before it (through LDS).
   constexpr int NP = CB / 16;
@@ -60,18 +63,20 @@ __global__ void __launch_bounds__(8 * DV) k_gate_prep_rows(const float *__restri
   __syncthreads();
   // totals of the pieces before this one, and of the pieces of this one's
   // 32-token block (for the block end) and of the whole chunk
-  float before = 0.f, all = 0.f, blkend = 0.f;
+  float before = 0.f, all = 0.f, blkend = 0.f, blkstart = 0.f;
 #pragma unroll
   for (int q = 0; q < NP; ++q) {
     const float tq = tot[q][d];
     before += q < blk ? tq : 0.f;
     blkend += q <= (blk | 1) ? tq : 0.f;
+    blkstart += q < (blk & ~1) ? tq : 0.f;
     all += tq;
   }
   const int64_t cidx = ((int64_t)gc * Hkv + c);
   if (blk == 0) Gam[cidx * DV + d] = fast_exp2(all);
   _Float16 *dst = Vr + cidx * CB * DV + d;
   const float gbe = blkend - before;  // 32-token block end (clamped to the sequence end), piece-local
+  const float gbs = blkstart - before;  // the token before the 32-token block, piece-local
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const int t = j0 + j;
@@ -81,6 +86,10 @@ __global__ void __launch_bounds__(8 * DV) k_gate_prep_rows(const float *__restri
       Gl2[idx] = before + gl[j];
       val = fast_exp2(all - before - gl[j]) * vv[j];
       VE[idx] = (_Float16)(fast_exp2(gbe - gl[j]) * vv[j]);
+      const float vb = fast_exp2(gbs - gl[j]) * vv[j];
+      const __bf16 vbh = (__bf16)vb;
+      VBH[idx] = vbh;
+      VBL[idx] = (__bf16)(vb - (float)vbh);
     }
     dst[(int64_t)t * DV] = (_Float16)val;
   }
@@ -425,10 +434,11 @@ __global__ void __launch_bounds__(128) k_dg_final(const float *__restrict__ dG, 
   }
 
 hipError_t launch_gate_prep_rows(int dv, const float *g, const void *v, bool in_f32, const Plan &plan, int Hkv,
-                                 int ncb_ub, float *Gl2, float *Gam, _Float16 *Vr, _Float16 *VE, hipStream_t st) {
+                                 int ncb_ub, float *Gl2, float *Gam, _Float16 *Vr, _Float16 *VE, __bf16 *VBH,
+                                 __bf16 *VBL, hipStream_t st) {
   dim3 grid(ncb_ub, Hkv);
   FIX_DV_SWITCH(dv, hipLaunchKernelGGL(k_gate_prep_rows<DVC>, grid, dim3(8 * DVC), 0, st, g, v, in_f32, plan, Hkv,
-                                       Gl2, Gam, Vr, VE));
+                                       Gl2, Gam, Vr, VE, VBH, VBL));
   return hipGetLastError();
 }
 

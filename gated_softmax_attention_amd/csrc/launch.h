@@ -34,6 +34,7 @@ struct BwdArgs {
   // Operands of the pairs in the same or the adjacent chunk, relative to
   // 32-token blocks (blocks tile every 128-chunk):
   const _Float16 *VE;          // [T, Hkv, DV] exp(Gl_blockend - Gl_j) v_j
+  const __bf16 *VBH, *VBL;     // [T, Hkv, DV] exp(Gl_blockstart-1 - Gl_j) v_j (>= |v_j|), bf16 hi / lo
   const _Float16 *X16;         // [T, Hq, DV] exp(Gl_i - Gl_blockstart-1) sigma delta_i
   const __bf16 *XH, *XL;       // the same, bf16 hi and lo parts
   const __bf16 *XTH, *XTL;     // [chunk][Hq][DV][CB] transposed hi / lo tiles (key_pos order)
@@ -84,7 +85,7 @@ inline hipError_t launch_fwd(int dk, int dv, bool f32in, const FwdArgs &a, int g
 }
 
 hipError_t launch_gate_prep_rows(int dv, const float *g, const void *v, bool in_f32, const Plan &plan, int Hkv,
-                                 int ncb_ub, float *Gl2, float *Gam, _Float16 *Vr, _Float16 *VE, hipStream_t st);
+                                 int ncb_ub, float *Gl2, float *Gam, _Float16 *Vr, _Float16 *VE, __bf16 *VBH, __bf16 *VBL, hipStream_t st);
 hipError_t launch_chunk_logprefix(int dv, const float *Gl2, const Plan &plan, int Hkv, double *Lam, hipStream_t st);
 hipError_t launch_tiles_t(int D, const void *in, bool in_f32, const Plan &plan, int H, int ncb_ub, _Float16 *out,
                           hipStream_t st);

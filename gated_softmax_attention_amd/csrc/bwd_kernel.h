@@ -613,6 +613,28 @@ __global__ void __launch_bounds__(256, 1) k_bwd_intra_dkv(BwdArgs a) {
       }
     }
   }
+  // dv relative to the end of the key's block: exp2(E(w) - Gl_j).  Each
+  // block's inputs are loaded before any of its stores (the compiler cannot
+  // tell the buffers apart, so a load after a store would wait for it).
+#pragma unroll
+  for (int bv = 0; bv < NBV; ++bv) {
+    const int col = 32 * bv + n;
+    if (col >= DV) continue;
+    const float ew = BE[wave + 1][col];
+    float gl[16], part[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int64_t idx = ((st + min(kb + acc_row(hh, j), L - 1)) * Hkv + c) * DV + col;
+      gl[j] = a.Gl2[idx];
+      part[j] = dflag ? a.dv_i[idx] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int kj = kb + acc_row(hh, j);
+      if (kj < L) a.dv_i[((st + kj) * Hkv + c) * DV + col] = fast_exp2(ew - gl[j]) * accV[bv][j] + part[j];
+    }
+  }
+  // dk after dv: the dv block loads then wait for no earlier stores
 #pragma unroll
   for (int bk = 0; bk < NBK; ++bk) {
     const int col = 32 * bk + n;
@@ -621,21 +643,6 @@ __global__ void __launch_bounds__(256, 1) k_bwd_intra_dkv(BwdArgs a) {
     for (int j = 0; j < 16; ++j) {
       const int kj = kb + acc_row(hh, j);
       if (kj < L) a.dk_i[((st + kj) * Hkv + c) * DK + col] = a.scale * accK[bk][j];
-    }
-  }
-  // dv relative to the end of the key's block: exp2(E(w) - Gl_j)
-#pragma unroll
-  for (int bv = 0; bv < NBV; ++bv) {
-    const int col = 32 * bv + n;
-    if (col >= DV) continue;
-    const float ew = BE[wave + 1][col];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int kj = kb + acc_row(hh, j);
-      if (kj < L) {
-        const int64_t idx = ((st + kj) * Hkv + c) * DV + col;
-        a.dv_i[idx] = fast_exp2(ew - a.Gl2[idx]) * accV[bv][j] + (dflag ? a.dv_i[idx] : 0.f);
-      }
     }
   }
 }

@@ -1106,50 +1106,61 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
   }
   if (kb >= L) return;
   // epilogue: dk, dv (inter part scaled to the key: exp(Gl_end(J) - Gl_key)), dG = qside - v (.) dv.
-  // Each block's inputs are loaded before any of its stores: the compiler
-  // cannot tell the output and input buffers apart, so interleaved loads
-  // and stores would each wait for the previous store's load.
+  // The compiler cannot tell the output and input buffers apart, so a load
+  // placed after a store waits for it: each block's inputs are loaded one
+  // block ahead, before the previous block's stores.
   const int tend = min((J + 1) * CB, L) - 1;
+  auto kidx = [&](int j) { return min(kb + acc_row(hh, j), L - 1); };
+  float pk[2][16];
+  auto load_dk = [&](int bk, float (&part)[16]) {
+    const int col = min(32 * bk + n, DK - 1);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) part[j] = a.dk_i[((st + kidx(j)) * Hkv + c) * DK + col];
+  };
+  load_dk(0, pk[0]);
 #pragma unroll
   for (int bk = 0; bk < NBK; ++bk) {
+    if (bk + 1 < NBK) load_dk(bk + 1, pk[(bk + 1) & 1]);
     const int col = 32 * bk + n;
-    if (col >= DK) continue;
-    float part[16];
+    if (col < DK)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int kj = min(kb + acc_row(hh, j), L - 1);
-      part[j] = a.dk_i[((st + kj) * Hkv + c) * DK + col];
-    }
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int kj = kb + acc_row(hh, j);
-      if (kj < L) store_out(a.dk, ((st + kj) * Hkv + c) * DK + col, a.scale * accK[bk][j] + part[j], a.out_f32);
-    }
+      for (int j = 0; j < 16; ++j) {
+        const int kj = kb + acc_row(hh, j);
+        if (kj < L) store_out(a.dk, ((st + kj) * Hkv + c) * DK + col, a.scale * accK[bk][j] + pk[bk & 1][j], a.out_f32);
+      }
   }
+  float in[2][4][16];  // [slot][prefix sum, partial, qside, v][row]
+  float gend[NBV];
+#pragma unroll
+  for (int bv = 0; bv < NBV; ++bv) gend[bv] = a.Gl2[((st + tend) * Hkv + c) * DV + min(32 * bv + n, DV - 1)];
+  auto load_dv = [&](int bv, float (&x)[4][16]) {
+    const int col = min(32 * bv + n, DV - 1);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int64_t idx = ((st + kidx(j)) * Hkv + c) * DV + col;
+      x[0][j] = a.Gl2[idx];
+      x[1][j] = a.dv_i[idx];
+      x[2][j] = a.qside[idx];
+      x[3][j] = load_in(a.v, idx, F32IN);
+    }
+  };
+  load_dv(0, in[0]);
 #pragma unroll
   for (int bv = 0; bv < NBV; ++bv) {
+    if (bv + 1 < NBV) load_dv(bv + 1, in[(bv + 1) & 1]);
     const int col = 32 * bv + n;
-    if (col >= DV) continue;
-    const float gend = a.Gl2[((st + tend) * Hkv + c) * DV + col];
-    float gl[16], part[16], qs[16], vv[16];
+    if (col < DV)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int64_t idx = ((st + min(kb + acc_row(hh, j), L - 1)) * Hkv + c) * DV + col;
-      gl[j] = a.Gl2[idx];
-      part[j] = a.dv_i[idx];
-      qs[j] = a.qside[idx];
-      vv[j] = load_in(a.v, idx, F32IN);
-    }
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int kj = kb + acc_row(hh, j);
-      if (kj < L) {
-        const int64_t idx = ((st + kj) * Hkv + c) * DV + col;
-        const float dvv = fast_exp2(gend - gl[j]) * accV[bv][j] + part[j];
-        store_out(a.dv, idx, dvv, a.out_f32);
-        a.dG[idx] = qs[j] - vv[j] * dvv;
+      for (int j = 0; j < 16; ++j) {
+        const int kj = kb + acc_row(hh, j);
+        if (kj < L) {
+          const int64_t idx = ((st + kj) * Hkv + c) * DV + col;
+          const float(&x)[4][16] = in[bv & 1];
+          const float dvv = fast_exp2(gend[bv] - x[0][j]) * accV[bv][j] + x[1][j];
+          store_out(a.dv, idx, dvv, a.out_f32);
+          a.dG[idx] = x[2][j] - x[3][j] * dvv;
+        }
       }
-    }
   }
 }
 

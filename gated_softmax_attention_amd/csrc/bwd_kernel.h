@@ -1014,15 +1014,12 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
     if (k + 1 < nsteps) advance(nxt);
     const bool next_chunk = nxt.ord != cur.ord;
     double lamI;
-    float4 mq[4];  // exponent offsets of the step's rows
-    {
-      uint4 m0, m1, m2, m3;
-      lds_read4(m0, m1, m2, m3, &Ms(b)[4 * hh], &Ms(b)[8 + 4 * hh], &Ms(b)[16 + 4 * hh], &Ms(b)[24 + 4 * hh]);
-      mq[0] = __builtin_bit_cast(float4, m0);
-      mq[1] = __builtin_bit_cast(float4, m1);
-      mq[2] = __builtin_bit_cast(float4, m2);
-      mq[3] = __builtin_bit_cast(float4, m3);
-    }
+    // Exponent offsets of the step's rows: read before the step's copies are
+    // issued (an LDS read after them can make the compiler wait for them) and
+    // used only after the products.
+    float4 mq[4];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) mq[q4] = *(const float4 *)&Ms(b)[8 * q4 + 4 * hh];
     {
       // S[q][key] and dP[q][key]: lane = key, register j = query acc_row(hh, j).
       // Operands of a group of products are read from LDS in one batch (one

@@ -75,20 +75,22 @@ def hip():
     return lib
 
 
-def parity_gate(x, d, F, torch):
+def parity_gate(x, d, F, torch, logits=False):
     """Sampled parity against the oracle (last 64 rows of two (sequence, kv head) units)."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     import oracle as O
     from gpu_util import err_rms
-    o, m, rstd, xx = F.forward(d["q"], d["k"], d["v"], d["g"], o_norm=True, out_dtype=torch.float32)
+    o, m, rstd, xx = F.forward(d["q"], d["k"], d["v"], d["g"], o_norm=True, out_dtype=torch.float32,
+                               gate_logits=logits)
     dq, dk, dv, dg, _, _ = F.backward(d["q"], d["k"], d["v"], d["g"], m, rstd, xx, d["dO"], o_norm=True,
-                                      out_dtype=torch.float32)
+                                      out_dtype=torch.float32, gate_logits=logits)
     torch.cuda.synchronize()
     wl = x["workload"]
     mask = np.zeros((wl.B, wl.Hkv), np.uint8)
     mask[0, 0] = mask[wl.B - 1, wl.Hkv - 1] = 1
-    rf = O.oracle_fwd(x["q"], x["k"], x["v"], x["g"], unit_mask=mask, window=64)
-    rb = O.oracle_bwd(x["q"], x["k"], x["v"], x["g"], x["dO"], unit_mask=mask, window=64)
+    g = x["g_logits"] if logits else x["g"]
+    rf = O.oracle_fwd(x["q"], x["k"], x["v"], g, unit_mask=mask, window=64, gate_logits=logits)
+    rb = O.oracle_bwd(x["q"], x["k"], x["v"], g, x["dO"], unit_mask=mask, window=64, gate_logits=logits)
     errs = {"o": err_rms(o.cpu().numpy(), rf["o"])}
     for n, t in (("dq", dq), ("dk", dk), ("dv", dv), ("dg", dg)):
         errs[n] = err_rms(t.cpu().numpy(), rb[n])
@@ -96,17 +98,17 @@ def parity_gate(x, d, F, torch):
     return ok, errs
 
 
-def cpu_baseline(x):
+def cpu_baseline(x, logits=False):
     """The fp64 oracle, fwd + bwd, on four heads of one batch row of the same workload, full length."""
     import oracle as O
     NH = 4
     sl = lambda a: np.ascontiguousarray(a[:1, :, :NH])
-    q, k, v, g, dO = (sl(x[n]) for n in ("q", "k", "v", "g", "dO"))
+    q, k, v, g, dO = (sl(x[n]) for n in ("q", "k", "v", "g_logits" if logits else "g", "dO"))
     O.load()
     t0 = time.perf_counter()
-    O.oracle_fwd(q, k, v, g)
+    O.oracle_fwd(q, k, v, g, gate_logits=logits)
     t1 = time.perf_counter()
-    O.oracle_bwd(q, k, v, g, dO)
+    O.oracle_bwd(q, k, v, g, dO, gate_logits=logits)
     t2 = time.perf_counter()
     wl = x["workload"]
     pairs = wl.T * (wl.T + 1) // 2 * NH
@@ -138,6 +140,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--gate-logits", action="store_true",
+                    help="pass the gate as raw logits (logsigmoid applied inside the kernels)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (HBM counter calibration)")
     args = ap.parse_args()
@@ -157,10 +161,11 @@ def main():
     wl = x["workload"]
     dev = lambda a, dt=torch.bfloat16: torch.from_numpy(np.ascontiguousarray(a)).to(dt).cuda()
     d = {n: dev(x[n]) for n in ("q", "k", "v", "dO")}
-    d["g"] = dev(x["g"], torch.float32)
-    print(f"[bench] inputs resident: {wl}", file=sys.stderr, flush=True)
+    d["g"] = dev(x["g_logits"] if args.gate_logits else x["g"], torch.float32)
+    print(f"[bench] inputs resident: {wl}{' (gate as logits)' if args.gate_logits else ''}", file=sys.stderr,
+          flush=True)
 
-    ok, errs = parity_gate(x, d, F, torch)
+    ok, errs = parity_gate(x, d, F, torch, logits=args.gate_logits)
     print(f"[bench] parity gate: {'pass' if ok else 'FAIL'} {errs}", file=sys.stderr, flush=True)
     if not ok:
         sys.exit(1)
@@ -174,7 +179,7 @@ def main():
     xx = torch.empty(B, T, Hq, dv, device="cuda")
     dq, dkk, dvv = torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"])
     dg = torch.empty_like(d["g"])
-    desc = F.make_desc(d["q"], d["k"], d["v"], o_norm=True)
+    desc = F.make_desc(d["q"], d["k"], d["v"], o_norm=True, gate_logits=args.gate_logits)
     wf, wb = F.fix_attn_fwd_workspace_size(desc), F.fix_attn_bwd_workspace_size(desc)
     ws_f = torch.empty(wf, dtype=torch.uint8, device="cuda")
     ws_b = torch.empty(wb, dtype=torch.uint8, device="cuda")
@@ -261,7 +266,9 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{WORKLOAD}: B={B} T={T} Hq={Hq} Hkv={Hkv} dk={dk} dv={dv} bf16 in/out, "
-                               f"g=logsigmoid(N({wl.gate_mu},{wl.gate_sd})), o_norm, fwd+bwd",
+                               f"g=logsigmoid(N({wl.gate_mu},{wl.gate_sd}))"
+                               f"{' passed as logits (logsigmoid in the kernels)' if args.gate_logits else ''}, "
+                               f"o_norm, fwd+bwd",
                    "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
                    "fwd_flops": fwd_flops, "bwd_flops": bwd_flops,
                    "kernel_ms": {n: round(v, 4) for n, v in sorted(avg.items(), key=lambda kv: -kv[1])}},
@@ -269,7 +276,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host ...", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(x)
+        out["cpu_baseline"] = cpu_baseline(x, logits=args.gate_logits)
     print(json.dumps(out), flush=True)
 
 

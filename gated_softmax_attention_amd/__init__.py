@@ -33,7 +33,7 @@ class fix_attn_desc(ctypes.Structure):
         ("cu_seqlens", ctypes.c_void_p), ("num_seqs", ctypes.c_int64),
         ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
         ("scale", ctypes.c_float), ("eps", ctypes.c_float),
-        ("o_norm", ctypes.c_int32),
+        ("o_norm", ctypes.c_int32), ("gate_logits", ctypes.c_int32),
     ]
 
 
@@ -130,7 +130,8 @@ def fix_attn_bwd(desc, q, k, v, g, o_norm_weight, o_gate, m, rstd, x, d_o, dq, d
     _check("fix_attn_bwd", st)
 
 
-def make_desc(q, k, v, cu_seqlens=None, *, o_norm=False, scale=None, eps=1e-5, out_dtype=None) -> fix_attn_desc:
+def make_desc(q, k, v, cu_seqlens=None, *, o_norm=False, scale=None, eps=1e-5, out_dtype=None,
+              gate_logits=False) -> fix_attn_desc:
     """Descriptor for torch tensors q [B,T,Hq,dk], k [B,T,Hkv,dk], v [B,T,Hkv,dv]."""
     import torch
     B, T, Hq, dk = q.shape
@@ -149,6 +150,7 @@ def make_desc(q, k, v, cu_seqlens=None, *, o_norm=False, scale=None, eps=1e-5, o
     d.scale = 0.0 if scale is None else float(scale)
     d.eps = float(eps)
     d.o_norm = 1 if o_norm else 0
+    d.gate_logits = 1 if gate_logits else 0
     return d
 
 
@@ -179,11 +181,12 @@ def _check_inputs(q, k, v, g, cu_seqlens, o_norm_weight, o_gate):
 
 
 def forward(q, k, v, g, cu_seqlens=None, *, o_norm=False, o_norm_weight=None, o_gate=None, scale=None,
-            eps=1e-5, out_dtype=None, save_x=True):
-    """One call of fix_attn_fwd; returns (o, m, rstd, x or None)."""
+            eps=1e-5, out_dtype=None, save_x=True, gate_logits=False):
+    """One call of fix_attn_fwd; returns (o, m, rstd, x or None).  gate_logits: g holds logits."""
     import torch
     _check_inputs(q, k, v, g, cu_seqlens, o_norm_weight, o_gate)
-    desc = make_desc(q, k, v, cu_seqlens, o_norm=o_norm, scale=scale, eps=eps, out_dtype=out_dtype)
+    desc = make_desc(q, k, v, cu_seqlens, o_norm=o_norm, scale=scale, eps=eps, out_dtype=out_dtype,
+                     gate_logits=gate_logits)
     B, T, Hq, _ = q.shape
     dv = v.shape[3]
     od = q.dtype if out_dtype is None else out_dtype
@@ -200,11 +203,13 @@ def forward(q, k, v, g, cu_seqlens=None, *, o_norm=False, o_norm_weight=None, o_
 
 
 def backward(q, k, v, g, m, rstd, x, d_o, cu_seqlens=None, *, o_norm=False, o_norm_weight=None, o_gate=None,
-             scale=None, eps=1e-5, out_dtype=None, need_dw=False, need_dz=False):
-    """One call of fix_attn_bwd; returns (dq, dk, dv, dg, d_o_norm_weight or None, d_o_gate or None)."""
+             scale=None, eps=1e-5, out_dtype=None, need_dw=False, need_dz=False, gate_logits=False):
+    """One call of fix_attn_bwd; returns (dq, dk, dv, dg, d_o_norm_weight or None, d_o_gate or None).
+    gate_logits: g holds logits and dg is the gradient with respect to them."""
     import torch
     _check_inputs(q, k, v, g, cu_seqlens, o_norm_weight, o_gate)
-    desc = make_desc(q, k, v, cu_seqlens, o_norm=o_norm, scale=scale, eps=eps, out_dtype=out_dtype)
+    desc = make_desc(q, k, v, cu_seqlens, o_norm=o_norm, scale=scale, eps=eps, out_dtype=out_dtype,
+                     gate_logits=gate_logits)
     od = q.dtype if out_dtype is None else out_dtype
     d_o = d_o.contiguous().to(q.dtype)
     dq = torch.empty(q.shape, dtype=od, device=q.device)

@@ -198,7 +198,8 @@ fix_status fix_attn_fwd(const fix_attn_desc *d, const void *q, const void *k, co
   e = fix::launch_plan(d->cu_seqlens, (int)s.nseq, (int)d->T, s.Ttot, w.plan, st);
   if (e == hipSuccess) e = trace_mark(st, "plan");
   if (e != hipSuccess) return hip_fail(e);
-  e = fix::launch_gate_prep((int)d->dv, g, v, f32in, w.plan, (int)d->Hkv, (int)s.nch_ub, w.Gl2, w.Gam, w.VtT, st);
+  e = fix::launch_gate_prep((int)d->dv, g, d->gate_logits != 0, v, f32in, w.plan, (int)d->Hkv, (int)s.nch_ub, w.Gl2,
+                            w.Gam, w.VtT, st);
   if (e == hipSuccess) e = trace_mark(st, "gate_prep");
   if (e != hipSuccess) return hip_fail(e);
   fix::FwdArgs a;
@@ -256,7 +257,8 @@ fix_status fix_attn_bwd(const fix_attn_desc *d, const void *q, const void *k, co
   e = trace_begin(st);
   if (e != hipSuccess) return hip_fail(e);
   FIX_TRY(fix::launch_plan(d->cu_seqlens, (int)s.nseq, (int)d->T, s.Ttot, w.plan, st), "plan");
-  FIX_TRY(fix::launch_gate_prep_rows(DV, g, v, f32in, w.plan, Hkv, ncb, w.Gl2, w.Gam, w.Vr, w.VE, w.VBH, w.VBL, st),
+  FIX_TRY(fix::launch_gate_prep_rows(DV, g, d->gate_logits != 0, v, f32in, w.plan, Hkv, ncb, w.Gl2, w.Gam, w.Vr,
+                                     w.VE, w.VBH, w.VBL, st),
           "gate_prep_rows");
   FIX_TRY(fix::launch_chunk_logprefix(DV, w.Gl2, w.plan, Hkv, w.Lam, st), "chunk_logprefix");
   FIX_TRY(fix::launch_tiles_t(DK, q, f32in, w.plan, Hq, ncb, w.Qt, st), "tiles_q");
@@ -291,7 +293,8 @@ fix_status fix_attn_bwd(const fix_attn_desc *d, const void *q, const void *k, co
   FIX_TRY(fix::launch_bwd(fix::BK_INTRA_DKV, DK, DV, f32in, a, dim3(ncb, Hkv), st), "bwd_intra_dkv");
   FIX_TRY(fix::launch_bwd(fix::BK_DQ, DK, DV, f32in, a, dim3(round8(ncb * Hq)), st), "bwd_dq");
   FIX_TRY(fix::launch_bwd(fix::BK_DKV, DK, DV, f32in, a, dim3(round8(ncb * Hkv)), st), "bwd_dkv");
-  FIX_TRY(fix::launch_dg_scan(DV, w.dG, w.plan, Hkv, ncb, w.dg_tot, w.dg_carry, dg, st), "dg_scan");
+  FIX_TRY(fix::launch_dg_scan(DV, w.dG, d->gate_logits ? g : nullptr, w.plan, Hkv, ncb, w.dg_tot, w.dg_carry, dg, st),
+          "dg_scan");
   if (want_dw) {
     FIX_TRY(fix::launch_dw_reduce(w.dw_part, w.plan.counts, Hkv, DV, d_o_norm_weight, st), "dw_reduce");
   }

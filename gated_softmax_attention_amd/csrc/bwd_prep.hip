@@ -28,7 +28,7 @@ namespace fix {
 // clamped to the sequence end), and V relative to the token before its
 // 32-token block, VB = exp(Gl_blockstart-1 - Gl_t) v_t (>= |v_t|, fp32 range)
 // as bf16 hi / lo parts, the key operand of the diagonal blocks.
-template <int DV>
+template <int DV, bool LOGITS>
 __global__ void __launch_bounds__(8 * DV) k_gate_prep_rows(const float *__restrict__ g, const void *__restrict__ v,
                                                            bool in_f32, Plan plan, int Hkv, float *__restrict__ Gl2,
                                                            float *__restrict__ Gam, _Float16 *__restrict__ Vr,
@@ -53,6 +53,9 @@ __global__ void __launch_bounds__(8 * DV) k_gate_prep_rows(const float *__restri
     gl[j] = g[idx];
     vv[j] = load_in(v, idx, in_f32);
   }
+  if constexpr (LOGITS)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) gl[j] = log_sigmoid(gl[j]);
   float acc = 0.f;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
@@ -397,9 +400,10 @@ __global__ void __launch_bounds__(128) k_dg_carry(const float *__restrict__ tot,
   }
 }
 
-template <int DV>
+template <int DV, bool LOGITS>
 __global__ void __launch_bounds__(128) k_dg_final(const float *__restrict__ dG, const float *__restrict__ carry,
-                                                  Plan plan, int Hkv, float *__restrict__ dg) {
+                                                  const float *__restrict__ logits, Plan plan, int Hkv,
+                                                  float *__restrict__ dg) {
   const int gc = blockIdx.x, c = blockIdx.y, d = threadIdx.x;
   if (gc >= plan.counts[0] || d >= DV) return;
   const int s = seq_of_chunk(plan.cb128, plan.nseq, gc);
@@ -407,18 +411,23 @@ __global__ void __launch_bounds__(128) k_dg_final(const float *__restrict__ dG, 
   const int n = min(CB, plan.seq_len[s] - t0);
   const int64_t tok0 = (int64_t)plan.seq_start[s] + t0;
   // 32-token blocks from the chunk end down, each block's loads issued together
+  // (with logits, times dg/dx = sigmoid(-x) of the token)
   float run = carry[((int64_t)gc * Hkv + c) * DV + d];
 #pragma unroll 1
   for (int b = CB / 32 - 1; b >= 0; --b) {
-    float x[32];
+    float x[32], f[32];
 #pragma unroll
-    for (int j = 0; j < 32; ++j) x[j] = dG[((tok0 + min(32 * b + j, n - 1)) * Hkv + c) * DV + d];
+    for (int j = 0; j < 32; ++j) {
+      const int64_t idx = ((tok0 + min(32 * b + j, n - 1)) * Hkv + c) * DV + d;
+      x[j] = dG[idx];
+      f[j] = LOGITS ? logits[idx] : 0.f;
+    }
 #pragma unroll
     for (int j = 31; j >= 0; --j) {
       const int t = 32 * b + j;
       if (t < n) {
         run += x[j];
-        dg[((tok0 + t) * Hkv + c) * DV + d] = run;
+        dg[((tok0 + t) * Hkv + c) * DV + d] = LOGITS ? run * sigmoid_neg(f[j]) : run;
       }
     }
   }
@@ -433,12 +442,16 @@ __global__ void __launch_bounds__(128) k_dg_final(const float *__restrict__ dG, 
     default: return hipErrorInvalidValue;              \
   }
 
-hipError_t launch_gate_prep_rows(int dv, const float *g, const void *v, bool in_f32, const Plan &plan, int Hkv,
-                                 int ncb_ub, float *Gl2, float *Gam, _Float16 *Vr, _Float16 *VE, __bf16 *VBH,
+hipError_t launch_gate_prep_rows(int dv, const float *g, bool logits, const void *v, bool in_f32, const Plan &plan,
+                                 int Hkv, int ncb_ub, float *Gl2, float *Gam, _Float16 *Vr, _Float16 *VE, __bf16 *VBH,
                                  __bf16 *VBL, hipStream_t st) {
   dim3 grid(ncb_ub, Hkv);
-  FIX_DV_SWITCH(dv, hipLaunchKernelGGL(k_gate_prep_rows<DVC>, grid, dim3(8 * DVC), 0, st, g, v, in_f32, plan, Hkv,
-                                       Gl2, Gam, Vr, VE, VBH, VBL));
+  if (logits)
+    FIX_DV_SWITCH(dv, hipLaunchKernelGGL((k_gate_prep_rows<DVC, true>), grid, dim3(8 * DVC), 0, st, g, v, in_f32,
+                                         plan, Hkv, Gl2, Gam, Vr, VE, VBH, VBL))
+  else
+    FIX_DV_SWITCH(dv, hipLaunchKernelGGL((k_gate_prep_rows<DVC, false>), grid, dim3(8 * DVC), 0, st, g, v, in_f32,
+                                         plan, Hkv, Gl2, Gam, Vr, VE, VBH, VBL));
   return hipGetLastError();
 }
 
@@ -461,8 +474,8 @@ hipError_t launch_bwd_prep(int dv, const PrepArgs &a, int ncb_ub, hipStream_t st
   return hipGetLastError();
 }
 
-hipError_t launch_dg_scan(int dv, const float *dG, const Plan &plan, int Hkv, int ncb_ub, float *tot, float *carry,
-                          float *dg, hipStream_t st) {
+hipError_t launch_dg_scan(int dv, const float *dG, const float *logits, const Plan &plan, int Hkv, int ncb_ub,
+                          float *tot, float *carry, float *dg, hipStream_t st) {
   dim3 grid(ncb_ub, Hkv), gs(plan.nseq, Hkv);
   FIX_DV_SWITCH(dv, hipLaunchKernelGGL(k_dg_totals<DVC>, grid, dim3(128), 0, st, dG, plan, Hkv, tot));
   hipError_t e = hipGetLastError();
@@ -470,7 +483,12 @@ hipError_t launch_dg_scan(int dv, const float *dG, const Plan &plan, int Hkv, in
   FIX_DV_SWITCH(dv, hipLaunchKernelGGL(k_dg_carry<DVC>, gs, dim3(128), 0, st, tot, plan, Hkv, carry));
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  FIX_DV_SWITCH(dv, hipLaunchKernelGGL(k_dg_final<DVC>, grid, dim3(128), 0, st, dG, carry, plan, Hkv, dg));
+  if (logits)
+    FIX_DV_SWITCH(dv, hipLaunchKernelGGL((k_dg_final<DVC, true>), grid, dim3(128), 0, st, dG, carry, logits, plan,
+                                         Hkv, dg))
+  else
+    FIX_DV_SWITCH(dv, hipLaunchKernelGGL((k_dg_final<DVC, false>), grid, dim3(128), 0, st, dG, carry, logits, plan,
+                                         Hkv, dg));
   return hipGetLastError();
 }
 

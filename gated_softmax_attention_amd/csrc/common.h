@@ -103,6 +103,17 @@ __device__ inline f32x16 mma32(f16x8 a, f16x8 b, f32x16 c) {
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Gate given as logits x: the forget gate logsigmoid(x) = min(x, 0) - log1p(exp(-|x|)) (no
+// overflow for either sign), and its derivative sigmoid(-x) = 1 / (1 + exp(x)).  log1p(t) for
+// t in (0, 1] is log(u) * t / (u - 1) with u = fl(1 + t), which cancels the rounding of u
+// (or t itself where u rounds to 1): a few ulp with the hardware log and exp.
+__device__ inline float log_sigmoid(float x) {
+  const float t = fast_exp2(-fabsf(x) * LOG2E), u = 1.f + t;
+  const float l1p = u == 1.f ? t : __logf(u) * __fdividef(t, u - 1.f);
+  return fminf(x, 0.f) - l1p;
+}
+__device__ inline float sigmoid_neg(float x) { return __frcp_rn(1.f + fast_exp2(x * LOG2E)); }
+
 // Maximum of x over lanes l and l ^ 32.  v_permlane32_swap with both
 // operands equal to x leaves the low half of x in both halves of one result
 // and the high half in both halves of the other, so their maximum is the

@@ -21,7 +21,7 @@
 
 namespace fix {
 
-template <int DV>
+template <int DV, bool LOGITS>
 __global__ void __launch_bounds__(4 * DV) k_gate_prep(const float *__restrict__ g, const void *__restrict__ v,
                                                       bool in_f32, Plan plan, int Hkv, float *__restrict__ Gl2,
                                                       float *__restrict__ Gam, _Float16 *__restrict__ VtT) {
@@ -52,6 +52,9 @@ __global__ void __launch_bounds__(4 * DV) k_gate_prep(const float *__restrict__ 
     gl[j] = g[idx];
     vv[j] = load_in(v, idx, in_f32);
   }
+  if constexpr (LOGITS)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) gl[j] = log_sigmoid(gl[j]);
   float acc = 0.f;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
@@ -88,14 +91,26 @@ __global__ void __launch_bounds__(4 * DV) k_gate_prep(const float *__restrict__ 
     dst[e] = *(const uint4 *)&tile[(e / (CH / 8)) * STR + 8 * (e % (CH / 8))];
 }
 
-hipError_t launch_gate_prep(int dv, const float *g, const void *v, bool in_f32, const Plan &plan, int Hkv,
-                            int nch_ub, float *Gl2, float *Gam, _Float16 *VtT, hipStream_t st) {
+hipError_t launch_gate_prep(int dv, const float *g, bool logits, const void *v, bool in_f32, const Plan &plan,
+                            int Hkv, int nch_ub, float *Gl2, float *Gam, _Float16 *VtT, hipStream_t st) {
   dim3 grid(nch_ub, Hkv);
   switch (dv) {
-    case 16: hipLaunchKernelGGL(k_gate_prep<16>, grid, dim3(4 * 16), 0, st, g, v, in_f32, plan, Hkv, Gl2, Gam, VtT); break;
-    case 32: hipLaunchKernelGGL(k_gate_prep<32>, grid, dim3(4 * 32), 0, st, g, v, in_f32, plan, Hkv, Gl2, Gam, VtT); break;
-    case 64: hipLaunchKernelGGL(k_gate_prep<64>, grid, dim3(4 * 64), 0, st, g, v, in_f32, plan, Hkv, Gl2, Gam, VtT); break;
-    case 128: hipLaunchKernelGGL(k_gate_prep<128>, grid, dim3(4 * 128), 0, st, g, v, in_f32, plan, Hkv, Gl2, Gam, VtT); break;
+    case 16:
+      if (logits) hipLaunchKernelGGL((k_gate_prep<16, true>), grid, dim3(4 * 16), 0, st, g, v, in_f32, plan, Hkv, Gl2, Gam, VtT);
+      else hipLaunchKernelGGL((k_gate_prep<16, false>), grid, dim3(4 * 16), 0, st, g, v, in_f32, plan, Hkv, Gl2, Gam, VtT);
+      break;
+    case 32:
+      if (logits) hipLaunchKernelGGL((k_gate_prep<32, true>), grid, dim3(4 * 32), 0, st, g, v, in_f32, plan, Hkv, Gl2, Gam, VtT);
+      else hipLaunchKernelGGL((k_gate_prep<32, false>), grid, dim3(4 * 32), 0, st, g, v, in_f32, plan, Hkv, Gl2, Gam, VtT);
+      break;
+    case 64:
+      if (logits) hipLaunchKernelGGL((k_gate_prep<64, true>), grid, dim3(4 * 64), 0, st, g, v, in_f32, plan, Hkv, Gl2, Gam, VtT);
+      else hipLaunchKernelGGL((k_gate_prep<64, false>), grid, dim3(4 * 64), 0, st, g, v, in_f32, plan, Hkv, Gl2, Gam, VtT);
+      break;
+    case 128:
+      if (logits) hipLaunchKernelGGL((k_gate_prep<128, true>), grid, dim3(4 * 128), 0, st, g, v, in_f32, plan, Hkv, Gl2, Gam, VtT);
+      else hipLaunchKernelGGL((k_gate_prep<128, false>), grid, dim3(4 * 128), 0, st, g, v, in_f32, plan, Hkv, Gl2, Gam, VtT);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

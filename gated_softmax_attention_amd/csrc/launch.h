@@ -67,8 +67,8 @@ struct PrepArgs {
 };
 
 hipError_t launch_plan(const int64_t *cu, int nseq, int T, int64_t Ttot, const Plan &plan, hipStream_t st);
-hipError_t launch_gate_prep(int dv, const float *g, const void *v, bool in_f32, const Plan &plan, int Hkv,
-                            int nch_ub, float *Gl2, float *Gam, _Float16 *VtT, hipStream_t st);
+hipError_t launch_gate_prep(int dv, const float *g, bool logits, const void *v, bool in_f32, const Plan &plan,
+                            int Hkv, int nch_ub, float *Gl2, float *Gam, _Float16 *VtT, hipStream_t st);
 hipError_t launch_fwd_d16(int dv, bool f32in, const FwdArgs &a, int grid, hipStream_t st);
 hipError_t launch_fwd_d32(int dv, bool f32in, const FwdArgs &a, int grid, hipStream_t st);
 hipError_t launch_fwd_d64(int dv, bool f32in, const FwdArgs &a, int grid, hipStream_t st);
@@ -84,15 +84,17 @@ inline hipError_t launch_fwd(int dk, int dv, bool f32in, const FwdArgs &a, int g
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_gate_prep_rows(int dv, const float *g, const void *v, bool in_f32, const Plan &plan, int Hkv,
-                                 int ncb_ub, float *Gl2, float *Gam, _Float16 *Vr, _Float16 *VE, __bf16 *VBH, __bf16 *VBL, hipStream_t st);
+hipError_t launch_gate_prep_rows(int dv, const float *g, bool logits, const void *v, bool in_f32, const Plan &plan,
+                                 int Hkv, int ncb_ub, float *Gl2, float *Gam, _Float16 *Vr, _Float16 *VE, __bf16 *VBH,
+                                 __bf16 *VBL, hipStream_t st);
 hipError_t launch_chunk_logprefix(int dv, const float *Gl2, const Plan &plan, int Hkv, double *Lam, hipStream_t st);
 hipError_t launch_tiles_t(int D, const void *in, bool in_f32, const Plan &plan, int H, int ncb_ub, _Float16 *out,
                           hipStream_t st);
 hipError_t launch_bwd_prep(int dv, const PrepArgs &a, int ncb_ub, hipStream_t st);
 hipError_t launch_dw_reduce(const float *part, const int *counts, int Hkv, int dv, float *dw, hipStream_t st);
-hipError_t launch_dg_scan(int dv, const float *dG, const Plan &plan, int Hkv, int ncb_ub, float *tot, float *carry,
-                          float *dg, hipStream_t st);
+// logits != null: the gate was given as logits x; dg is multiplied by dg/dx = sigmoid(-x).
+hipError_t launch_dg_scan(int dv, const float *dG, const float *logits, const Plan &plan, int Hkv, int ncb_ub,
+                          float *tot, float *carry, float *dg, hipStream_t st);
 
 // Backward MFMA kernels, one translation unit per dk.
 enum BwdKernel { BK_INTRA_DQ = 0, BK_INTRA_DKV = 1, BK_DQ = 2, BK_DKV = 3 };

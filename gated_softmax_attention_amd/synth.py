@@ -116,11 +116,14 @@ def make_inputs(wl: Workload | str, seed: int | None = None, **overrides) -> dic
     def normal(r, shape, mu=0.0, sd=1.0):
         return (r.standard_normal(shape, dtype=np.float64) * sd + mu).astype(np.float32)
 
+    logits = rg.standard_normal((B, T, Hkv, dv)) * wl.gate_sd + wl.gate_mu
     out = {
         "q": cast(normal(rq, (B, T, Hq, dk))),
         "k": cast(normal(rk, (B, T, Hkv, dk))),
         "v": cast(normal(rv, (B, T, Hkv, dv))),
-        "g": logsigmoid64(rg.standard_normal((B, T, Hkv, dv)) * wl.gate_sd + wl.gate_mu).astype(np.float32),
+        "g": logsigmoid64(logits).astype(np.float32),
+        # the same gate as raw logits (fp32), for callers that pass logits
+        "g_logits": logits.astype(np.float32),
     }
     out["w"] = cast(normal(rw, (dv,), 1.0, 0.1)) if wl.w_kind == "normal" else np.ones(dv, np.float32)
     out["z"] = cast(normal(rz, (B, T, Hq, dv))) if wl.o_gate else None

@@ -37,6 +37,12 @@
  *    call that returns FIX_E_INVALID / FIX_E_UNSUPPORTED / FIX_E_WORKSPACE
  *    wrote nothing.  FIX_E_HIP reports a failed launch; the HIP error code is
  *    then available from fix_attn_last_hip_error() on the calling thread.
+ *  - Gate as logits: with gate_logits set, the g argument holds raw
+ *    unconstrained logits x and the forget gate is g = logsigmoid(x) =
+ *    log(sigmoid(x)) <= 0, applied inside the kernels; dg is then the
+ *    gradient with respect to x (dg/dx = sigmoid(-x)).  The pages fix g as a
+ *    log-space gate shaped like v (FiX README, "Quick Start"); logsigmoid of
+ *    unconstrained logits is the usual way to produce one.
  *  - Preconditions not checked (they would need a device scan): g <= 0
  *    (a forget gate; results for positive g are only as accurate as fp32
  *    range allows), cu_seqlens non-decreasing with cu[0] = 0 and
@@ -76,6 +82,7 @@ typedef struct {
   float scale;         /* logit scale; <= 0 selects dk^-1/2 */
   float eps;           /* RMSNorm epsilon (used when o_norm != 0) */
   int32_t o_norm;      /* nonzero: apply RMSNorm and o_norm_weight to the output */
+  int32_t gate_logits; /* nonzero: g holds logits x, the gate is logsigmoid(x), dg is d/dx */
 } fix_attn_desc;
 
 /* Checks a descriptor on the host; makes no HIP call (usable without a GPU).
@@ -93,7 +100,7 @@ size_t fix_attn_bwd_workspace_size(const fix_attn_desc *d);
 
 /* Forward pass.
  *   q [B,T,Hq,dk], k [B,T,Hkv,dk], v [B,T,Hkv,dv]       in_dtype
- *   g [B,T,Hkv,dv]                                      fp32, log-space forget gate
+ *   g [B,T,Hkv,dv]                                      fp32, log-space forget gate (or its logits)
  *   o_norm_weight [dv] in_dtype or NULL (ones); read only when o_norm
  *   o_gate [B,T,Hq,dv] in_dtype or NULL (no output gate)
  * Outputs (all required except x):
@@ -115,7 +122,7 @@ fix_status fix_attn_fwd(const fix_attn_desc *d, const void *q, const void *k, co
  *   d_o [B,T,Hq,dv] in_dtype: gradient of the loss with respect to o
  * Outputs:
  *   dq [B,T,Hq,dk], dk [B,T,Hkv,dk], dv [B,T,Hkv,dv]   out_dtype (required)
- *   dg [B,T,Hkv,dv] fp32 (required)
+ *   dg [B,T,Hkv,dv] fp32 (required): gradient with respect to g (to the logits with gate_logits)
  *   d_o_norm_weight [dv] fp32, or NULL to skip (written only when o_norm)
  *   d_o_gate [B,T,Hq,dv] out_dtype, or NULL to skip (needs o_gate) */
 fix_status fix_attn_bwd(const fix_attn_desc *d, const void *q, const void *k, const void *v,

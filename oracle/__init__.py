@@ -41,10 +41,10 @@ def _bind(lib):
     i64, f64, i32 = ctypes.c_int64, ctypes.c_double, ctypes.c_int
     p = ctypes.c_void_p
     lib.fix_oracle_fwd.restype = i32
-    lib.fix_oracle_fwd.argtypes = [i64, p, i64, i64, i64, i64, f64, f64, i32,
+    lib.fix_oracle_fwd.argtypes = [i64, p, i64, i64, i64, i64, f64, f64, i32, i32,
                                    p, p, p, p, p, p, p, p, i64, p, p, p, p]
     lib.fix_oracle_bwd.restype = i32
-    lib.fix_oracle_bwd.argtypes = [i64, p, i64, i64, i64, i64, f64, f64, i32,
+    lib.fix_oracle_bwd.argtypes = [i64, p, i64, i64, i64, i64, f64, f64, i32, i32,
                                    p, p, p, p, p, p, p, p, p, i64, p, p, p, p, p, p]
     return lib
 
@@ -84,10 +84,11 @@ def _layout(q, k, v, g, cu_seqlens):
 
 
 def oracle_fwd(q, k, v, g, cu_seqlens=None, *, scale=None, eps=1e-5, o_norm=True, w=None, z=None,
-               m_in=None, unit_mask=None, window=0, lib=None):
+               m_in=None, unit_mask=None, window=0, gate_logits=False, lib=None):
     """Forward of FiX attention in fp64.
 
     q [B,T,Hq,dk], k [B,T,Hkv,dk], v, g [B,T,Hkv,dv], w [dv] or None, z [B,T,Hq,dv] or None.
+    gate_logits: g holds raw logits x and the gate is logsigmoid(x).
     Returns dict o, x [B,T,Hq,dv], m, rstd [B,T,Hq] (float64; NaN where not computed).
     """
     lib = lib or load()
@@ -101,7 +102,7 @@ def oracle_fwd(q, k, v, g, cu_seqlens=None, *, scale=None, eps=1e-5, o_norm=True
     r = np.full((B, T, Hq), np.nan)
     mi = None if m_in is None else np.ascontiguousarray(np.asarray(m_in, dtype=np.float64))
     um = None if unit_mask is None else np.ascontiguousarray(np.asarray(unit_mask, dtype=np.uint8))
-    st = lib.fix_oracle_fwd(nseq, _ptr(cu), Hq, Hkv, dk, dv, scale, float(eps), int(bool(o_norm)),
+    st = lib.fix_oracle_fwd(nseq, _ptr(cu), Hq, Hkv, dk, dv, scale, float(eps), int(bool(o_norm)), int(bool(gate_logits)),
                             _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(w), _ptr(z), _ptr(mi), _ptr(um),
                             int(window), _ptr(o), _ptr(x), _ptr(m), _ptr(r))
     if st != 0:
@@ -110,8 +111,11 @@ def oracle_fwd(q, k, v, g, cu_seqlens=None, *, scale=None, eps=1e-5, o_norm=True
 
 
 def oracle_bwd(q, k, v, g, dO, cu_seqlens=None, *, scale=None, eps=1e-5, o_norm=True, w=None, z=None,
-               m_in=None, unit_mask=None, window=0, lib=None):
+               m_in=None, unit_mask=None, window=0, gate_logits=False, lib=None):
     """Backward of FiX attention in fp64 (row max m held constant).
+
+    gate_logits: g holds raw logits x (the gate is logsigmoid(x)) and dg is the gradient with
+    respect to x.
 
     window > 0: the last `window` rows and keys of every selected unit; window < 0: dq of the
     first -window rows and dk, dv of the first -window keys (dg not computed).
@@ -130,7 +134,7 @@ def oracle_bwd(q, k, v, g, dO, cu_seqlens=None, *, scale=None, eps=1e-5, o_norm=
     dz = np.full((B, T, Hq, dv), np.nan)
     mi = None if m_in is None else np.ascontiguousarray(np.asarray(m_in, dtype=np.float64))
     um = None if unit_mask is None else np.ascontiguousarray(np.asarray(unit_mask, dtype=np.uint8))
-    st = lib.fix_oracle_bwd(nseq, _ptr(cu), Hq, Hkv, dk, dv, scale, float(eps), int(bool(o_norm)),
+    st = lib.fix_oracle_bwd(nseq, _ptr(cu), Hq, Hkv, dk, dv, scale, float(eps), int(bool(o_norm)), int(bool(gate_logits)),
                             _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(w), _ptr(z), _ptr(dO), _ptr(mi),
                             _ptr(um), int(window), _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(dg), _ptr(dw),
                             _ptr(dz))

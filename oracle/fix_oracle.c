@@ -38,6 +38,14 @@
  *   dg_t = sum_{t'>=t, same sequence} dG_t'
  *   dw   = sum over rows and heads of dn (.) xhat
  *
+ * Gate given as logits (gate_logits != 0): the argument g holds raw logits
+ * x, and the forget gate is g = logsigmoid(x), so the per-token factor is
+ * exp(g_u) = sigmoid(x_u) = 1 / (1 + exp(-x_u)) and the reported gradient is
+ * the one with respect to x: dx_t = dg_t * dg_t/dx_t = dg_t * sigmoid(-x_t).
+ * (The pages fix g as a log-space gate shaped like v; logsigmoid of
+ * unconstrained logits is the plainest way to produce one, and it is how
+ * every benchmark workload builds g.)
+ *
  * Layout: every tensor is token-major and packed, [Ttot, H, D] row-major
  * (a dense [B, T, H, D] batch is Ttot = B*T with sequence b at offset b*T).
  * Inputs arrive as fp64 holding exactly the values the GPU receives (bf16
@@ -68,12 +76,12 @@ typedef struct {
   const int64_t *cu;
   int64_t Hq, Hkv, G, dk, dv;
   double scale, eps;
-  int o_norm;
+  int o_norm, gate_logits;
   const double *q, *k, *v, *g, *w, *z;
   const double *m_in;
   const unsigned char *mask;
   int64_t window;
-  double *a; /* exp(g), [Ttot, Hkv, dv] */
+  double *a; /* exp(g) (or sigmoid(x) for logits), [Ttot, Hkv, dv] */
 } octx;
 
 typedef struct {
@@ -142,19 +150,19 @@ static double row_rstd(const octx *c, const double *x) {
 }
 
 static int setup(octx *c, int64_t nseq, const int64_t *cu, int64_t Hq, int64_t Hkv, int64_t dk,
-                 int64_t dv, double scale, double eps, int o_norm, const double *q, const double *k,
+                 int64_t dv, double scale, double eps, int o_norm, int gate_logits, const double *q, const double *k,
                  const double *v, const double *g, const double *w, const double *z, const double *m_in,
                  const unsigned char *mask, int64_t window) {
   if (nseq < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || dk <= 0 || dv <= 0) return 1;
   c->nseq = nseq; c->cu = cu; c->Hq = Hq; c->Hkv = Hkv; c->G = Hq / Hkv;
-  c->dk = dk; c->dv = dv; c->scale = scale; c->eps = eps; c->o_norm = o_norm;
+  c->dk = dk; c->dv = dv; c->scale = scale; c->eps = eps; c->o_norm = o_norm; c->gate_logits = gate_logits;
   c->q = q; c->k = k; c->v = v; c->g = g; c->w = w; c->z = z; c->m_in = m_in;
   c->mask = mask; c->window = window;
   int64_t Ttot = cu[nseq];
   c->a = (double *)malloc(sizeof(double) * (size_t)(Ttot > 0 ? Ttot : 1) * Hkv * dv);
   if (!c->a) return 2;
 #pragma omp parallel for schedule(static)
-  for (int64_t e = 0; e < Ttot * Hkv * dv; ++e) c->a[e] = exp(g[e]);
+  for (int64_t e = 0; e < Ttot * Hkv * dv; ++e) c->a[e] = gate_logits ? 1.0 / (1.0 + exp(-g[e])) : exp(g[e]);
   return 0;
 }
 
@@ -181,12 +189,12 @@ static int64_t max_len(const octx *c) {
 }
 
 int fix_oracle_fwd(int64_t nseq, const int64_t *cu, int64_t Hq, int64_t Hkv, int64_t dk, int64_t dv,
-                   double scale, double eps, int o_norm, const double *q, const double *k,
+                   double scale, double eps, int o_norm, int gate_logits, const double *q, const double *k,
                    const double *v, const double *g, const double *w, const double *z,
                    const double *m_in, const unsigned char *unit_mask, int64_t window, double *o,
                    double *x_out, double *m_out, double *rstd_out) {
   octx c;
-  int st = setup(&c, nseq, cu, Hq, Hkv, dk, dv, scale, eps, o_norm, q, k, v, g, w, z, m_in,
+  int st = setup(&c, nseq, cu, Hq, Hkv, dk, dv, scale, eps, o_norm, gate_logits, q, k, v, g, w, z, m_in,
                  unit_mask, window);
   if (st) return st;
   int64_t n;
@@ -222,13 +230,13 @@ int fix_oracle_fwd(int64_t nseq, const int64_t *cu, int64_t Hq, int64_t Hkv, int
 }
 
 int fix_oracle_bwd(int64_t nseq, const int64_t *cu, int64_t Hq, int64_t Hkv, int64_t dk, int64_t dv,
-                   double scale, double eps, int o_norm, const double *q, const double *k,
+                   double scale, double eps, int o_norm, int gate_logits, const double *q, const double *k,
                    const double *v, const double *g, const double *w, const double *z,
                    const double *dO, const double *m_in, const unsigned char *unit_mask,
                    int64_t window, double *dq, double *dk_out, double *dv_out, double *dg,
                    double *dw, double *dz) {
   octx c;
-  int st = setup(&c, nseq, cu, Hq, Hkv, dk, dv, scale, eps, o_norm, q, k, v, g, w, z, m_in,
+  int st = setup(&c, nseq, cu, Hq, Hkv, dk, dv, scale, eps, o_norm, gate_logits, q, k, v, g, w, z, m_in,
                  unit_mask, window);
   if (st) return st;
   int64_t Ttot = cu[nseq];
@@ -400,7 +408,8 @@ int fix_oracle_bwd(int64_t nseq, const int64_t *cu, int64_t Hq, int64_t Hkv, int
           size_t ko = (size_t)((base + t) * Hkv + kh);
           dG -= v[ko * dv + d] * dv_out[ko * dv + d];
           run += dG;
-          dg[ko * dv + d] = run;
+          /* logits: chain rule through g = logsigmoid(x) */
+          dg[ko * dv + d] = c.gate_logits ? run / (1.0 + exp(g[ko * dv + d])) : run;
         }
       }
     }

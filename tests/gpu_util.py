@@ -31,6 +31,7 @@ def device_inputs(x: dict):
     dt = torch.bfloat16 if wl.in_dtype == "bf16" else torch.float32
     d = {n: to_dev(x[n], dt) for n in ("q", "k", "v", "w", "z", "dO")}
     d["g"] = to_dev(x["g"], torch.float32)
+    d["g_logits"] = to_dev(x["g_logits"], torch.float32)
     d["cu_seqlens"] = None if x["cu_seqlens"] is None else torch.from_numpy(x["cu_seqlens"]).cuda()
     d["dtype"] = dt
     return d
@@ -60,15 +61,18 @@ def bf16_ulp(a):
     return np.exp2(e - 7)
 
 
-def oracle_fwd_for(x: dict, *, o_norm=True, eps=1e-5, unit_mask=None, window=0):
-    wl = x["workload"]
-    return O.oracle_fwd(x["q"], x["k"], x["v"], x["g"], x["cu_seqlens"], eps=eps, o_norm=o_norm,
-                        w=x["w"] if o_norm else None, z=x["z"], unit_mask=unit_mask, window=window)
+def oracle_fwd_for(x: dict, *, o_norm=True, eps=1e-5, unit_mask=None, window=0, gate_logits=False):
+    g = x["g_logits"] if gate_logits else x["g"]
+    return O.oracle_fwd(x["q"], x["k"], x["v"], g, x["cu_seqlens"], eps=eps, o_norm=o_norm,
+                        w=x["w"] if o_norm else None, z=x["z"], unit_mask=unit_mask, window=window,
+                        gate_logits=gate_logits)
 
 
-def oracle_bwd_for(x: dict, *, o_norm=True, eps=1e-5, unit_mask=None, window=0):
-    return O.oracle_bwd(x["q"], x["k"], x["v"], x["g"], x["dO"], x["cu_seqlens"], eps=eps, o_norm=o_norm,
-                        w=x["w"] if o_norm else None, z=x["z"], unit_mask=unit_mask, window=window)
+def oracle_bwd_for(x: dict, *, o_norm=True, eps=1e-5, unit_mask=None, window=0, gate_logits=False):
+    g = x["g_logits"] if gate_logits else x["g"]
+    return O.oracle_bwd(x["q"], x["k"], x["v"], g, x["dO"], x["cu_seqlens"], eps=eps, o_norm=o_norm,
+                        w=x["w"] if o_norm else None, z=x["z"], unit_mask=unit_mask, window=window,
+                        gate_logits=gate_logits)
 
 
 def custom_inputs(B, T, Hq, Hkv, dk, dv, *, in_dtype="bf16", gate=(3.0, 1.5), lengths=(), o_gate=False,

@@ -347,6 +347,51 @@ def pin_prefix_window(lib, rng):
     return worst
 
 
+def pin_logits_finite_differences(lib, rng):
+    """Gate given as raw logits x (gate = logsigmoid(x)): every gradient, dg now with respect
+    to x, against central differences of sum(o * dO) at eps = 0."""
+    lengths = [3, 4]
+    q, k, v, _, cu = rand_case(rng, 1, 7, 2, 1, 3, 4, lengths=lengths)
+    x = rng.standard_normal((1, 7, 1, 4)) * 1.5 + 0.3  # both signs: both branches of the transform
+    dO = rng.standard_normal((1, 7, 2, 4))
+    grads = O.oracle_bwd(q, k, v, x, dO, cu, eps=0.0, gate_logits=True, lib=lib)
+    loss = lambda qq, kk, vv, xx: float(np.sum(O.oracle_fwd(qq, kk, vv, xx, cu, eps=0.0, gate_logits=True,
+                                                                lib=lib)["o"] * dO))
+    worst, h = 0.0, 1e-6
+    arrs = {"q": q, "k": k, "v": v, "x": x}
+    for name, gname in [("q", "dq"), ("k", "dk"), ("v", "dv"), ("x", "dg")]:
+        fd = np.zeros_like(arrs[name])
+        for idx in np.ndindex(arrs[name].shape):
+            vals = []
+            for sgn in (1, -1):
+                a2 = {kk: vv.copy() for kk, vv in arrs.items()}
+                a2[name][idx] += sgn * h
+                vals.append(loss(a2["q"], a2["k"], a2["v"], a2["x"]))
+            fd[idx] = (vals[0] - vals[1]) / (2 * h)
+        worst = max(worst, rel(grads[gname], fd))
+    return worst
+
+
+def pin_logits_match_logsigmoid(lib, rng):
+    """Logits x give what the log gate torch.nn.functional.logsigmoid(x) gives (forward and
+    dq, dk, dv), and dg with respect to x is the log-gate dg times torch.sigmoid(-x)."""
+    lengths = [11, 1, 20]
+    q, k, v, _, cu = rand_case(rng, 1, 32, 4, 2, 8, 8, lengths=lengths)
+    x = rng.standard_normal((1, 32, 2, 8)) * 2.0 + 1.0
+    dO = rng.standard_normal((1, 32, 4, 8))
+    tx = torch.from_numpy(x)
+    g = torch.nn.functional.logsigmoid(tx).numpy()
+    fa = O.oracle_fwd(q, k, v, x, cu, gate_logits=True, lib=lib)
+    fb = O.oracle_fwd(q, k, v, g, cu, lib=lib)
+    ba = O.oracle_bwd(q, k, v, x, dO, cu, gate_logits=True, lib=lib)
+    bb = O.oracle_bwd(q, k, v, g, dO, cu, lib=lib)
+    worst = rel(fa["o"], fb["o"])
+    for n in ("dq", "dk", "dv"):
+        worst = max(worst, rel(ba[n], bb[n]))
+    worst = max(worst, rel(ba["dg"], bb["dg"] * torch.sigmoid(-tx).numpy()))
+    return worst
+
+
 ALL_PINS = {
     "no_gate_softmax": (pin_no_gate_is_softmax_attention, 1e-12),
     "no_gate_unnormalised": (pin_no_gate_unnormalised, 1e-12),
@@ -364,4 +409,6 @@ ALL_PINS = {
     "dense_reference_unnormed": (lambda lib, rng: pin_dense_reference(lib, rng, False), 1e-10),
     "suffix_window": (pin_suffix_window, 0.0),
     "prefix_window": (pin_prefix_window, 0.0),
+    "logits_finite_diff": (pin_logits_finite_differences, 1e-6),
+    "logits_match_logsigmoid": (pin_logits_match_logsigmoid, 1e-12),
 }

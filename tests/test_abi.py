@@ -109,3 +109,21 @@ def test_event_trace_setting_is_host_only():
     lib.fix_attn_set_event_trace(None, 0)
     assert lib.fix_attn_event_trace_count() == 0
     assert lib.fix_attn_event_trace_label(1) is None
+
+
+def test_descriptor_layout_matches_header(tmp_path):
+    """sizeof and field offsets of fix_attn_desc in the C header equal the ctypes binding's."""
+    import ctypes
+    import subprocess
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    fields = [f[0] for f in F.fix_attn_desc._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "fixattn.h"\nint main(void) {\n'
+                   '  printf("%zu\\n", sizeof(fix_attn_desc));\n'
+                   + "".join(f'  printf("%zu\\n", offsetof(fix_attn_desc, {n}));\n' for n in fields)
+                   + "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(root, "include"), str(src), "-o", str(exe)], check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    want = [ctypes.sizeof(F.fix_attn_desc)] + [getattr(F.fix_attn_desc, n).offset for n in fields]
+    assert got == want

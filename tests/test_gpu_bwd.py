@@ -15,14 +15,16 @@ pytestmark = [pytest.mark.gpu, needs_gpu]
 TOL, TOL_DG = 1e-2, 5e-3
 
 
-def run_bwd(x, *, o_norm=True, eps=1e-5):
+def run_bwd(x, *, o_norm=True, eps=1e-5, gate_logits=False):
     d = device_inputs(x)
     w = d["w"] if o_norm else None
-    o, m, rstd, xx = F.forward(d["q"], d["k"], d["v"], d["g"], d["cu_seqlens"], o_norm=o_norm, o_norm_weight=w,
-                               o_gate=d["z"], eps=eps)
-    dq, dk, dv, dg, dw, dz = F.backward(d["q"], d["k"], d["v"], d["g"], m, rstd, xx, d["dO"], d["cu_seqlens"],
+    g = d["g_logits"] if gate_logits else d["g"]
+    o, m, rstd, xx = F.forward(d["q"], d["k"], d["v"], g, d["cu_seqlens"], o_norm=o_norm, o_norm_weight=w,
+                               o_gate=d["z"], eps=eps, gate_logits=gate_logits)
+    dq, dk, dv, dg, dw, dz = F.backward(d["q"], d["k"], d["v"], g, m, rstd, xx, d["dO"], d["cu_seqlens"],
                                         o_norm=o_norm, o_norm_weight=w, o_gate=d["z"], eps=eps,
-                                        out_dtype=torch.float32, need_dw=True, need_dz=True)
+                                        out_dtype=torch.float32, need_dw=True, need_dz=True,
+                                        gate_logits=gate_logits)
     torch.cuda.synchronize()
     cpu = lambda t: None if t is None else t.float().cpu().numpy()
     return {"dq": cpu(dq), "dk": cpu(dk), "dv": cpu(dv), "dg": cpu(dg), "dw": cpu(dw), "dz": cpu(dz)}
@@ -186,3 +188,18 @@ def test_bwd_full_size_first_keys():
     print("errors:", {k: f"{v:.2e}" for k, v in e.items()}, flush=True)
     for n, v in e.items():
         assert v <= TOL, f"{n}: {v:.3e}"
+
+
+# The gate given as raw logits: dg is the gradient with respect to the logits.
+LOGIT_CASES = [
+    (1, 640, 4, 2, 64, 64, {"lengths": (100, 300, 240), "o_gate": True, "gate": (3.0, 1.5)}),
+    (2, 300, 2, 2, 128, 128, {"gate": (0.0, 2.0)}),
+]
+
+
+@pytest.mark.parametrize("case", LOGIT_CASES, ids=lambda c: "B{}-T{}-H{}x{}-dk{}-dv{}".format(*c[:6]))
+def test_bwd_gate_logits(case):
+    B, T, Hq, Hkv, dk, dv, extra = case
+    announce(f"bwd gate logits {case}")
+    x = custom_inputs(B, T, Hq, Hkv, dk, dv, **extra)
+    check_bwd(run_bwd(x, gate_logits=True), oracle_bwd_for(x, gate_logits=True))

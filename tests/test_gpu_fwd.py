@@ -20,11 +20,12 @@ pytestmark = [pytest.mark.gpu, needs_gpu]
 TOL = 1e-2
 
 
-def run_fwd(x, *, o_norm=True, out_dtype=torch.float32, eps=1e-5):
+def run_fwd(x, *, o_norm=True, out_dtype=torch.float32, eps=1e-5, gate_logits=False):
     d = device_inputs(x)
-    o, m, rstd, xx = F.forward(d["q"], d["k"], d["v"], d["g"], d["cu_seqlens"], o_norm=o_norm,
+    g = d["g_logits"] if gate_logits else d["g"]
+    o, m, rstd, xx = F.forward(d["q"], d["k"], d["v"], g, d["cu_seqlens"], o_norm=o_norm,
                                o_norm_weight=d["w"] if o_norm else None, o_gate=d["z"], eps=eps,
-                               out_dtype=out_dtype)
+                               out_dtype=out_dtype, gate_logits=gate_logits)
     torch.cuda.synchronize()
     return {"o": o.float().cpu().numpy(), "m": m.cpu().numpy(), "rstd": rstd.cpu().numpy(),
             "x": xx.cpu().numpy()}
@@ -167,3 +168,18 @@ def test_fwd_full_size_sampled(name, units):
     got = run_fwd(x)
     ref = oracle_fwd_for(x, unit_mask=_unit_mask(x["workload"], units), window=256)
     check_fwd(got, ref)
+
+
+# The gate given as raw logits (the kernels apply logsigmoid themselves).
+LOGIT_CASES = [
+    (1, 640, 4, 2, 64, 64, {"lengths": (100, 300, 240), "o_gate": True, "gate": (3.0, 1.5)}),
+    (2, 300, 2, 2, 128, 128, {"gate": (0.0, 2.0)}),
+]
+
+
+@pytest.mark.parametrize("case", LOGIT_CASES, ids=lambda c: "B{}-T{}-H{}x{}-dk{}-dv{}".format(*c[:6]))
+def test_fwd_gate_logits(case):
+    B, T, Hq, Hkv, dk, dv, extra = case
+    announce(f"fwd gate logits {case}")
+    x = custom_inputs(B, T, Hq, Hkv, dk, dv, **extra)
+    check_fwd(run_fwd(x, gate_logits=True), oracle_fwd_for(x, gate_logits=True))

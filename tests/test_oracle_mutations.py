@@ -41,6 +41,10 @@ MUTATIONS = {
     "gate_weight_in_norm": [("if (o_norm) val = val * r * (w ? w[d] : 1.0);", "if (o_norm) val = val * r;")],
     "window_off_by_one": [("return L - c->window;", "return L - c->window + 1;")],
     "dkv_loop_skips_diagonal": [("for (int64_t i = j; i < L; ++i) {", "for (int64_t i = j + 1; i < L; ++i) {")],
+    # gate logits: sigmoid sign slip, and the chain-rule factor dropped or with the wrong sign
+    "logits_sigmoid_sign": [("1.0 / (1.0 + exp(-g[e]))", "1.0 / (1.0 + exp(g[e]))")],
+    "logits_chain_rule_dropped": [("run / (1.0 + exp(g[ko * dv + d]))", "run")],
+    "logits_chain_rule_sign": [("run / (1.0 + exp(g[ko * dv + d]))", "run / (1.0 + exp(-g[ko * dv + d]))")],
 }
 
 

@@ -93,10 +93,10 @@ struct BwdWs {
   fix::Plan plan;
   float *Gl2, *Gam;
   double *Lam;
-  _Float16 *Vr, *Qt, *Kt, *VE;
+  _Float16 *Vr, *Qt, *Kt, *VE, *Q16;
   __bf16 *VBH, *VBL;
   float *delta;
-  _Float16 *dh, *dht, *X16;
+  _Float16 *dh, *X16;
   __bf16 *XH, *XL, *XTH, *XTL;
   float *mb, *sig, *qside, *dG, *dq_i, *dk_i, *dv_i, *dw_part, *dg_tot, *dg_carry;
 };
@@ -110,10 +110,10 @@ size_t carve_bwd(Carve &cv, const fix_attn_desc *d, BwdWs &w) {
   w.Lam = cv.take<double>(ncb * Hkv * DV);
   w.Vr = cv.take<_Float16>(ncb * Hkv * fix::CB * DV);
   w.Qt = cv.take<_Float16>(ncb * Hq * DK * fix::CB);
+  w.Q16 = cv.take<_Float16>(T * Hq * DK);
   w.Kt = cv.take<_Float16>(ncb * Hkv * DK * fix::CB);
   w.delta = cv.take<float>(T * Hq * DV);
   w.dh = cv.take<_Float16>(T * Hq * DV);
-  w.dht = cv.take<_Float16>(ncb * Hq * DV * fix::CB);
   w.VE = cv.take<_Float16>(T * Hkv * DV);
   w.VBH = cv.take<__bf16>(T * Hkv * DV);
   w.VBL = cv.take<__bf16>(T * Hkv * DV);
@@ -263,6 +263,7 @@ fix_status fix_attn_bwd(const fix_attn_desc *d, const void *q, const void *k, co
   FIX_TRY(fix::launch_chunk_logprefix(DV, w.Gl2, w.plan, Hkv, w.Lam, st), "chunk_logprefix");
   FIX_TRY(fix::launch_tiles_t(DK, q, f32in, w.plan, Hq, ncb, w.Qt, st), "tiles_q");
   FIX_TRY(fix::launch_tiles_t(DK, k, f32in, w.plan, Hkv, ncb, w.Kt, st), "tiles_k");
+  FIX_TRY(fix::launch_to_f16(q, f32in, s.Ttot * Hq * DK, w.Q16, st), "q_f16");
   fix::PrepArgs pa;
   pa.x = x; pa.rstd = rstd; pa.m = m; pa.Gl2 = w.Gl2;
   pa.dO = d_o; pa.z = o_gate; pa.w = d->o_norm ? o_norm_weight : nullptr;
@@ -271,15 +272,15 @@ fix_status fix_attn_bwd(const fix_attn_desc *d, const void *q, const void *k, co
   pa.o_norm = d->o_norm ? 1 : 0;
   pa.out_f32 = d->out_dtype == FIX_F32;
   pa.in_f32 = f32in;
-  pa.delta = w.delta; pa.dh = w.dh; pa.dht = w.dht; pa.mb = w.mb; pa.sig = w.sig; pa.qside = w.qside;
+  pa.delta = w.delta; pa.dh = w.dh; pa.mb = w.mb; pa.sig = w.sig; pa.qside = w.qside;
   pa.dz = d_o_gate;
   pa.X16 = w.X16; pa.XH = w.XH; pa.XL = w.XL; pa.XTH = w.XTH; pa.XTL = w.XTL;
   pa.dw_part = want_dw ? w.dw_part : nullptr;
   FIX_TRY(fix::launch_bwd_prep(DV, pa, ncb, st), "bwd_prep");
   fix::BwdArgs a;
   a.q = q; a.k = k; a.v = v;
-  a.Gl2 = w.Gl2; a.Gam = w.Gam; a.Lam = w.Lam; a.Vr = w.Vr; a.Qt = w.Qt; a.Kt = w.Kt;
-  a.delta = w.delta; a.dh = w.dh; a.dht = w.dht; a.mb = w.mb; a.sig = w.sig; a.qside = w.qside;
+  a.Gl2 = w.Gl2; a.Gam = w.Gam; a.Lam = w.Lam; a.Vr = w.Vr; a.Qt = w.Qt; a.Kt = w.Kt; a.Q16 = w.Q16;
+  a.delta = w.delta; a.dh = w.dh; a.mb = w.mb; a.sig = w.sig; a.qside = w.qside;
   a.VE = w.VE; a.VBH = w.VBH; a.VBL = w.VBL; a.X16 = w.X16; a.XH = w.XH; a.XL = w.XL; a.XTH = w.XTH; a.XTL = w.XTL;
   a.dq_i = w.dq_i; a.dk_i = w.dk_i; a.dv_i = w.dv_i;
   a.dq = dq; a.dk = dk; a.dv = dv; a.dG = w.dG;

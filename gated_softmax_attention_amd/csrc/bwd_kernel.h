@@ -833,8 +833,10 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdArgs a) {
 // dk, dv from query chunks two or more after the key chunk.  Workgroup = the
 // 128 keys of one key chunk J and kv head (4 waves x 32 keys), visiting the
 // query chunks from the last to J + 2 and, within each, the G query heads of
-// the group, 32 query rows per step copied straight into LDS, three steps in
-// flight: Q rows, transposed Q, scaled dhat rows and transposed scaled dhat.
+// the group, 32 query rows per step copied straight into LDS: fp16 Q rows
+// and scaled dhat rows only.  The dV and dK products take those rows as their
+// k-major operands through the transposing LDS read (tr_frag), so no
+// transposed copy of either is stored or moved.
 // The decay product between the chunks, gamma_IJ = exp2(Lam[I-1] - Lam[J]),
 // enters both products through per-chunk operands: V (.) gamma_IJ (rebuilt
 // per query chunk from an LDS copy of the chunk's V rows) for dP, and the
@@ -850,25 +852,21 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
   constexpr int NBK = DKP / 32, NBV = DVP / 32;
   constexpr int NB = 2;             // LDS stages
   constexpr int DIST = NB - 1;      // steps copied ahead of the one computed
-  using QT = LdsTile<32, DK * 2>;   // Q rows of the step
-  using QTT = LdsTile<DKP, 64>;     // transposed Q (dk rows x 32 queries)
-  using QTTD = LdsTile<DK, 64>;
-  using DR = LdsTile<32, DV * 2>;   // scaled dhat rows
-  using DTT = LdsTile<DVP, 64>;     // scaled dhat, transposed
-  using DTTD = LdsTile<DV, 64>;
+  using QT = LdsTile<32, DK * 2>;   // Q rows of the step (fp16)
+  using DR = LdsTile<32, DV * 2>;   // scaled dhat rows (fp16)
   using VRT = LdsTile<CB, DV * 2>;  // the key chunk's V rows, scaled to the chunk end
   // Loads a step issues after its copies' predecessors: the copies themselves
   // (fixed per wave) and nothing else, so waiting for the next step's copies
   // is waiting until this many are left in flight.
-  constexpr int NCOPY = F32IN ? QTTD::NW + DR::NW + DTTD::NW + 1 : QT::NW + QTTD::NW + DR::NW + DTTD::NW + 1;
-  // One LDS object for every tile (see the forward kernel).
-  constexpr int O_Q = 0, O_QT = O_Q + NB * QT::BYTES, O_D = O_QT + NB * QTT::BYTES, O_DT = O_D + NB * DR::BYTES;
-  constexpr int O_V = O_DT + NB * DTT::BYTES, O_M = O_V + VRT::BYTES, O_G = O_M + NB * 256, O_GH = O_G + 2 * DVP * 4;
+  constexpr int NCOPY = QT::NW + DR::NW + 1;
+  // One LDS object for every tile (see the forward kernel).  The transposed
+  // operands of the dV and dK products are read from the row tiles with the
+  // transposing LDS load (tr_frag).
+  constexpr int O_Q = 0, O_D = O_Q + NB * QT::BYTES;
+  constexpr int O_V = O_D + NB * DR::BYTES, O_M = O_V + VRT::BYTES, O_G = O_M + NB * 256, O_GH = O_G + 2 * DVP * 4;
   __shared__ __align__(1024) char smem[O_GH + 2 * DVP * 2];
   auto Qs = [&](int b) { return smem + O_Q + b * QT::BYTES; };
-  auto Qts = [&](int b) { return smem + O_QT + b * QTT::BYTES; };
   auto Ds = [&](int b) { return smem + O_D + b * DR::BYTES; };
-  auto Dts = [&](int b) { return smem + O_DT + b * DTT::BYTES; };
   auto Ms = [&](int b) { return (float *)(smem + O_M + b * 256); };  // 64 floats, 32 used
   auto gam = [&](int b) { return (float *)(smem + O_G) + b * DVP; };
   auto gamh = [&](int b) { return (_Float16 *)(smem + O_GH) + b * DVP; };  // the same, fp16
@@ -898,15 +896,15 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
   const int I0 = J + 2, I1 = nch - 1;                  // query chunks visited: I1 down to I0
   const int ns1 = (L - I1 * CB + 31) / 32;              // slices of the last (possibly partial) chunk
   const int nsteps = I0 <= I1 ? G * ns1 + 4 * G * (I1 - I0) : 0;
-  kfrag kf[NS];
+  // The key as an fp16 operand: Q is staged as fp16 (q converted once, exact
+  // for |q| in [2^-14, 65504]), so the score product runs in fp16 and equals
+  // the bf16 one for such inputs.
+  f16x8 kf[NS];
 #pragma unroll
-  for (int i = 0; i < NS; ++i)
-    kf[i] = kv ? IF::load(a.k, ((st + key) * Hkv + c) * DK + 16 * i + 8 * hh) : IF::zero();
-  for (int b = 0; b < NB; ++b) {
-    if (DK < DKP)
-      for (int e = tid; e < (DKP - DK) * 64 / 4; e += 256) ((uint32_t *)(Qts(b) + DK * 64))[e] = 0u;
-    if (DV < DVP)
-      for (int e = tid; e < (DVP - DV) * 64 / 4; e += 256) ((uint32_t *)(Dts(b) + DV * 64))[e] = 0u;
+  for (int i = 0; i < NS; ++i) {
+    const kfrag kr = kv ? IF::load(a.k, ((st + key) * Hkv + c) * DK + 16 * i + 8 * hh) : IF::zero();
+#pragma unroll
+    for (int e = 0; e < 8; ++e) kf[i][e] = (_Float16)(float)kr[e];
   }
   f32x16 accK[NBK], accV[NBV];
 #pragma unroll
@@ -931,28 +929,16 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
   };
   // Rows past the end of the sequence read as zeros; their probabilities are
   // masked to zero when the step is computed.
-  uint32_t oq[QT::NW], oqt[QTTD::NW], od[DR::NW], odt[DTTD::NW];
+  uint32_t oq[QT::NW], od[DR::NW];
   QT::lane_offsets(Hq * DK * 2, wave, lane, oq);
-  QTTD::lane_offsets(CB * 2, wave, lane, oqt);
   DR::lane_offsets(Hq * DV * 2, wave, lane, od);
-  DTTD::lane_offsets(CB * 2, wave, lane, odt);
   auto stage_tile = [&](const Pos &p, int b) {
     const int h = c * G + p.gq;
     const int qt0 = p.I * CB + 32 * p.u;
     const int64_t qr = (st + qt0) * Hq + h;
     const int nrow = L - qt0;
-    if constexpr (!F32IN) {
-      QT::dma(Qs(b), make_rsrc((const uint16_t *)a.q + qr * DK, (int64_t)nrow * Hq * DK * 2), oq, wave);
-    } else {
-      for (int e = tid; e < QT::NCH; e += 256) {
-        const int r = e / QT::CPR, cc = e % QT::CPR;
-        *(f16x8 *)(Qs(b) + QT::off(r, cc)) = IF::load(a.q, ((st + min(qt0 + r, L - 1)) * Hq + h) * DK + 8 * cc);
-      }
-    }
-    const int64_t ch = (int64_t)(cbs + p.I) * Hq + h;
-    QTTD::dma(Qts(b), make_rsrc(a.Qt + ch * DK * CB + 32 * p.u, (int64_t)DK * CB * 2), oqt, wave);
+    QT::dma(Qs(b), make_rsrc(a.Q16 + qr * DK, (int64_t)nrow * Hq * DK * 2), oq, wave);
     DR::dma(Ds(b), make_rsrc(a.dh + qr * DV, (int64_t)nrow * Hq * DV * 2), od, wave);
-    DTTD::dma(Dts(b), make_rsrc(a.dht + ch * DV * CB + 32 * p.u, (int64_t)DV * CB * 2), odt, wave);
     // lane r fills Ms[r] (every wave, the same bytes)
     dma4(Ms(b), make_rsrc(a.mb + qr, (int64_t)nrow * Hq * 4), (uint32_t)lane * Hq * 4);
   };
@@ -1024,10 +1010,10 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
       // S[q][key] and dP[q][key]: lane = key, register j = query acc_row(hh, j).
       // Operands of a group of products are read from LDS in one batch (one
       // wait for all of them rather than one per product).
-      kfrag qa[NS];
+      f16x8 qa[NS];
       f16x8 da[NSV];
 #pragma unroll
-      for (int i = 0; i < NS; ++i) qa[i] = *(const kfrag *)(Qs(b) + QT::off(n, 2 * i + hh));
+      for (int i = 0; i < NS; ++i) qa[i] = *(const f16x8 *)(Qs(b) + QT::off(n, 2 * i + hh));
 #pragma unroll
       for (int i = 0; i < NSV; ++i) da[i] = *(const f16x8 *)(Ds(b) + DR::off(n, 2 * i + hh));
       __builtin_amdgcn_sched_barrier(0);
@@ -1040,23 +1026,28 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
       // (the last step again near the end, so that every step issues the
       // same copies; `ahead` is that step's position), the next chunk's Lam
       // row, the step's row offsets and the dV / dK operands.
-      stage_tile(ahead, (k + DIST) % NB);
-      if (k + DIST + 1 < nsteps) advance(ahead);
-      lamI = lam_of(nxt.I);
-      f16x8 ta[NBV][2], tq[NBK][2];
+      f16x8 ta[NBV][2], tq[NBK][2];  // dhat^T and Q^T operands (k = query, in the result tiles' order)
 #pragma unroll
       for (int bv = 0; bv < NBV; ++bv)
 #pragma unroll
-        for (int uu = 0; uu < 2; ++uu) ta[bv][uu] = *(const f16x8 *)(Dts(b) + DTT::off(32 * bv + n, 2 * uu + hh));
+        for (int uu = 0; uu < 2; ++uu) ta[bv][uu] = tr_frag<DR>(Ds(b), 16 * uu, 32 * bv, lane);
 #pragma unroll
       for (int bk = 0; bk < NBK; ++bk)
 #pragma unroll
-        for (int uu = 0; uu < 2; ++uu) tq[bk][uu] = *(const f16x8 *)(Qts(b) + QTT::off(32 * bk + n, 2 * uu + hh));
+        for (int uu = 0; uu < 2; ++uu) tq[bk][uu] = tr_frag<QT>(Qs(b), 16 * uu, 32 * bk, lane);
+      stage_tile(ahead, (k + DIST) % NB);
+      if (k + DIST + 1 < nsteps) advance(ahead);
+      lamI = lam_of(nxt.I);
+      constexpr int NTR = 4 * (NBV + NBK);
 #pragma unroll
-      for (int i = 0; i < NS + NSV; ++i) {
+      for (int i = 0; i < NS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one product
+        __builtin_amdgcn_sched_group_barrier(0x100, (NTR + NS - 1) / NS, 0);  // transposing LDS reads
+      }
+#pragma unroll
+      for (int i = 0; i < NSV; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one product
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one copy / global load
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
       }
       __builtin_amdgcn_sched_barrier(0);
       if (qt0 + 32 > L) {  // rows past the end of the sequence: probability exp2(-inf) = 0

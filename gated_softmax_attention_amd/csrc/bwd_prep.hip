@@ -207,9 +207,8 @@ __global__ void __launch_bounds__(256) k_bwd_prep(PrepArgs a) {
   constexpr int SEG = 32;            // tokens per tile segment
   constexpr int STR = SEG + 8;       // LDS tile row stride (elements; rows 16-byte aligned)
   constexpr int TILE = DV * STR * 2, RED = RPP * DV * 4;
-  __shared__ __align__(16) char smem[3 * TILE > RED ? 3 * TILE : RED];
-  _Float16 *tile = (_Float16 *)smem;
-  __bf16 *tileh = (__bf16 *)(smem + TILE), *tilel = (__bf16 *)(smem + 2 * TILE);
+  __shared__ __align__(16) char smem[2 * TILE > RED ? 2 * TILE : RED];
+  __bf16 *tileh = (__bf16 *)smem, *tilel = (__bf16 *)(smem + TILE);
   const int gc = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
   if (gc >= a.plan.counts[0]) return;
   const Plan &pl = a.plan;
@@ -303,7 +302,6 @@ __global__ void __launch_bounds__(256) k_bwd_prep(PrepArgs a) {
         const int pos = key_pos(r);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          tile[(d0 + i) * STR + pos] = valid ? hv[i] : (_Float16)0.f;
           tileh[(d0 + i) * STR + pos] = valid ? xh[i] : (__bf16)0.f;
           tilel[(d0 + i) * STR + pos] = valid ? xl[i] : (__bf16)0.f;
         }
@@ -332,7 +330,6 @@ __global__ void __launch_bounds__(256) k_bwd_prep(PrepArgs a) {
       for (int e = tid; e < DV * SEG / 8; e += 256) {
         const int d = e / (SEG / 8), p8 = e % (SEG / 8);
         const int64_t o = tb + (int64_t)d * CB + 8 * p8;
-        *(uint4 *)(a.dht + o) = *(const uint4 *)&tile[d * STR + 8 * p8];
         *(uint4 *)(a.XTH + o) = *(const uint4 *)&tileh[d * STR + 8 * p8];
         *(uint4 *)(a.XTL + o) = *(const uint4 *)&tilel[d * STR + 8 * p8];
       }
@@ -431,6 +428,36 @@ __global__ void __launch_bounds__(128) k_dg_final(const float *__restrict__ dG, 
       }
     }
   }
+}
+
+// fp16 copy of a bf16 or fp32 tensor, 8 elements per thread (n a multiple of 8).
+__global__ void __launch_bounds__(256) k_to_f16(const void *__restrict__ in, bool in_f32, int64_t n8,
+                                                _Float16 *__restrict__ out) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= n8) return;
+  float v[8];
+  if (in_f32) {
+    const float4 lo = ((const float4 *)in)[2 * e], hi = ((const float4 *)in)[2 * e + 1];
+    v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w; v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+  } else {
+    const uint4 r = ((const uint4 *)in)[e];
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  f16x8 h;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) h[i] = (_Float16)v[i];
+  ((f16x8 *)out)[e] = h;
+}
+
+hipError_t launch_to_f16(const void *in, bool in_f32, int64_t n, _Float16 *out, hipStream_t st) {
+  const int64_t n8 = n / 8;
+  if (n8 > 0) hipLaunchKernelGGL(k_to_f16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, in, in_f32, n8, out);
+  return hipGetLastError();
 }
 
 #define FIX_DV_SWITCH(dv, ...)                         \

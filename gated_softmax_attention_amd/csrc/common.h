@@ -140,9 +140,14 @@ __device__ inline uint16_t f32_to_bf16_rne(float f) {
 // resource's byte count read as zeros (rows past the end of a sequence).
 //
 // Tiles are unpadded, [ROWS][RB bytes], and the 16-byte chunk c of row r is
-// stored at chunk position c ^ swz(r): for the MFMA operand reads (32 lanes
-// reading the same chunk of 32 consecutive rows) every 16 lanes then hit 16
-// distinct 16-byte bank groups, with no padding.
+// stored at chunk position c ^ swz(r), with no padding.  swz is a bijection of
+// the row bits that select a chunk position within a 256-byte bank period, so
+// that the MFMA operand reads (32 lanes reading the same chunk of 32
+// consecutive rows) have every 16 lanes on 16 distinct 16-byte bank groups;
+// its bits are rotated so that the two lowest row bits (those that differ
+// among 4 consecutive rows) land on the top chunk bits, which keeps the
+// transposing reads (tr_frag: 4 consecutive rows times 4 consecutive chunks
+// per 32 lanes) free of conflicts as well.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 // Buffer resource over [base, base + bytes) (raw, stride 0).  Both are the
@@ -168,7 +173,12 @@ template <int ROWS, int RB> struct LdsTile {
   // everything.
   static constexpr int NI = NCH / 64;             // 1 KB wave copies per tile
   static constexpr int NW = NI < 4 ? 1 : (NI + 3) / 4;
-  __device__ static int swz(int r) { return (r / (16 / CPR)) % CPR; }
+  __device__ static int swz(int r) {
+    constexpr int LG = CPR == 16 ? 4 : CPR == 8 ? 3 : CPR == 4 ? 2 : 1;  // log2(CPR)
+    constexpr int K = CPR == 16 ? 2 : CPR == 8 ? 1 : 0;                 // row bits below 4 in u
+    const int u = (r / (16 / CPR)) % CPR;
+    return ((u >> K) | (u << (LG - K))) & (CPR - 1);
+  }
   __device__ static int off(int r, int c) { return r * RB + ((c ^ swz(r)) << 4); }
   __device__ static int piece(int t, int wave) { return NI < 4 ? wave % NI : min(wave + 4 * t, NI - 1); }
   // This lane's source offsets in a global tile whose rows are `stride` bytes apart.
@@ -187,6 +197,31 @@ template <int ROWS, int RB> struct LdsTile {
                                                16, o[t], 0, 0, 0);
   }
 };
+
+// B operand of a 32x32x16 MFMA whose k index runs over the rows of a row-major
+// fp16 LdsTile, read with gfx950's transposing LDS load (ds_read_b64_tr_b16).
+// Within each 16-lane group, lane i receives element i % 4 of the 8-byte words
+// that lanes 4e + i / 4 (e = 0..3) address, so lane j of a group addresses row
+// j / 4 of four rows and columns 4 (j % 4) .. + 3 of the group's sixteen.
+// Lane (n, hh) then holds column col0 + n of rows row0 + 8t + 4hh + e as
+// element 4t + e (t = 0, 1): the k order of a product's result tile when it is
+// the next product's A operand (see slab_key).  row0 is a multiple of 16.
+// (The result is reinterpreted as a whole vector: a bit cast of one element
+// of an ext_vector_type value reads element 0 with this compiler.)
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+template <class T> __device__ inline f16x8 tr_frag(const char *tile, int row0, int col0, int lane) {
+  const int j = lane & 15, hh = lane >> 5, col = col0 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+  auto *base = (__attribute__((address_space(3))) char *)tile;
+  f16x4 h[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int row = row0 + 8 * t + 4 * hh + (j >> 2);
+    auto *p = (__attribute__((address_space(3))) s16x4 *)(base + T::off(row, col >> 3) + 2 * (col & 7));
+    h[t] = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(p));
+  }
+  return __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7);
+}
 
 // One copy of 16 (or 4) bytes per lane from a buffer resource at byte offset
 // `o`; lane l's piece lands at lds + 16 l (lds + 4 l).  Wave-uniform control

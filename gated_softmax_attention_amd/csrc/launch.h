@@ -27,8 +27,9 @@ struct BwdArgs {
   const double *Lam;           // [chunk][Hkv][DV] prefix over chunks of the chunk log2 totals
   const _Float16 *Vr;          // [chunk][Hkv][CB][DV] V scaled to its chunk end
   const _Float16 *Qt, *Kt;     // [chunk][H][D][CB] transposed fp16 tiles (key_pos order)
+  const _Float16 *Q16;         // [T, Hq, DK] q as fp16 (exact for |q| in [2^-14, 65504])
   const float *delta;          // [T, Hq, DV] gradient reaching x
-  const _Float16 *dh, *dht;    // sigma * exp(Gl) * delta, rows and transposed tiles
+  const _Float16 *dh;          // [T, Hq, DV] sigma * exp(Gl) * delta
   const float *mb, *sig;       // [T, Hq] m log2e - e, sigma = 2^-e
   const float *qside;          // [T, Hkv, DV]
   // Operands of the pairs in the same or the adjacent chunk, relative to
@@ -55,7 +56,6 @@ struct PrepArgs {
   int o_norm, out_f32, in_f32;
   float *delta;        // [Ttot, Hq, DV] fp32
   _Float16 *dh;        // [Ttot, Hq, DV] fp16, sigma * exp(Gl) * delta
-  _Float16 *dht;       // [chunk][Hq][DV][CB] fp16, the same transposed (key_pos order)
   float *mb;           // [Ttot, Hq] m log2e - e
   float *sig;          // [Ttot, Hq] sigma = 2^-e
   float *qside;        // [Ttot, Hkv, DV] sum over the group of delta (.) x
@@ -88,6 +88,7 @@ hipError_t launch_gate_prep_rows(int dv, const float *g, bool logits, const void
                                  int Hkv, int ncb_ub, float *Gl2, float *Gam, _Float16 *Vr, _Float16 *VE, __bf16 *VBH,
                                  __bf16 *VBL, hipStream_t st);
 hipError_t launch_chunk_logprefix(int dv, const float *Gl2, const Plan &plan, int Hkv, double *Lam, hipStream_t st);
+hipError_t launch_to_f16(const void *in, bool in_f32, int64_t n, _Float16 *out, hipStream_t st);
 hipError_t launch_tiles_t(int D, const void *in, bool in_f32, const Plan &plan, int H, int ncb_ub, _Float16 *out,
                           hipStream_t st);
 hipError_t launch_bwd_prep(int dv, const PrepArgs &a, int ncb_ub, hipStream_t st);

@@ -927,8 +927,7 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
       }
     }
   };
-  // Rows past the end of the sequence read as zeros; their probabilities are
-  // masked to zero when the step is computed.
+  // Rows past the end of the sequence read as zeros (see the probabilities).
   uint32_t oq[QT::NW], od[DR::NW];
   QT::lane_offsets(Hq * DK * 2, wave, lane, oq);
   DR::lane_offsets(Hq * DV * 2, wave, lane, od);
@@ -1050,15 +1049,10 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one copy / global load
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (qt0 + 32 > L) {  // rows past the end of the sequence: probability exp2(-inf) = 0
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          if (qt0 + acc_row(hh, 4 * q4) >= L) mq[q4].x = __builtin_inff();
-          if (qt0 + acc_row(hh, 4 * q4 + 1) >= L) mq[q4].y = __builtin_inff();
-          if (qt0 + acc_row(hh, 4 * q4 + 2) >= L) mq[q4].z = __builtin_inff();
-          if (qt0 + acc_row(hh, 4 * q4 + 3) >= L) mq[q4].w = __builtin_inff();
-        }
-      }
+      // Rows past the end of the sequence need no mask: their Q, dhat and
+      // row-offset copies read as zeros, so their probability is exp2(0) = 1
+      // (finite), their dP and hence dS are 0, and the dV product meets it
+      // only against their zero dhat rows.
       f16x8 pf[2], dsf[2];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
@@ -1066,7 +1060,7 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int j = 4 * q4 + e;
-          const float pv = fast_exp2(sc[j] * sl2 - mv[e]);  // rows past the end: mv = inf
+          const float pv = fast_exp2(sc[j] * sl2 - mv[e]);
           pf[j >> 3][j & 7] = (_Float16)pv;
           dsf[j >> 3][j & 7] = (_Float16)(pv * dp[j]);
         }

@@ -149,6 +149,7 @@ __device__ inline uint16_t f32_to_bf16_rne(float f) {
 // transposing reads (tr_frag: 4 consecutive rows times 4 consecutive chunks
 // per 32 lanes) free of conflicts as well.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Buffer resource over [base, base + bytes) (raw, stride 0).  Both are the
 // same in every lane wherever it is used; that is asserted to the compiler
@@ -189,6 +190,8 @@ template <int ROWS, int RB> struct LdsTile {
       o[t] = (uint32_t)r * stride + (uint32_t)((pc ^ swz(r)) << 4);
     }
   }
+  // Copy t of the tile (t < NW), untracked (dma16_untracked, defined below).
+  __device__ static void dma_piece_untracked(char *lds, const u32x4 &src, const uint32_t (&o)[NW], int t, int wave);
   // Copy the tile.  `wave` must be wave-uniform (an SGPR value).
   __device__ static void dma(char *lds, rsrc_t src, const uint32_t (&o)[NW], int wave) {
 #pragma unroll
@@ -223,6 +226,43 @@ template <class T> __device__ inline f16x8 tr_frag(const char *tile, int row0, i
   return __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// The same copies issued from inline assembly, which the compiler's wait-count
+// pass does not see.  That pass makes any LDS read wait for every direct copy
+// in flight that it cannot prove to write elsewhere (with a buffer index that
+// is not a constant it never can), which stalls loops that keep copies in
+// flight across reads of other buffers.  The caller orders these copies with
+// explicit waits (wait_vm): loads complete in issue order, so the compiler's
+// own counts stay conservative when these are issued between its loads.  The
+// resource is given as its four descriptor words; m0 (the LDS base of the
+// copy) is saved and restored around it.
+// LDS byte address of a pointer into LDS.
+__device__ inline uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
+}
+__device__ inline u32x4 rsrc_words(const void *base, int64_t bytes) {
+  const int nrec = (int)(bytes < 0 ? 0 : bytes > 0x7fffffffLL ? 0x7fffffffLL : bytes);
+  const uint64_t b = (uint64_t)base;
+  return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b),
+               (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) & 0xffffu,
+               (uint32_t)__builtin_amdgcn_readfirstlane(nrec), 0x00020000u};
+}
+__device__ inline void dma16_untracked(void *lds, const u32x4 &src, uint32_t o) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "s"(lds_addr(lds)), "v"(o), "s"(src) : "memory");
+}
+__device__ inline void dma4_untracked(void *lds, const u32x4 &src, uint32_t o) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dword %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "s"(lds_addr(lds)), "v"(o), "s"(src) : "memory");
+}
+
+template <int ROWS, int RB>
+__device__ inline void LdsTile<ROWS, RB>::dma_piece_untracked(char *lds, const u32x4 &src, const uint32_t (&o)[NW], int t,
+                                                              int wave) {
+  dma16_untracked(lds + piece(t, wave) * 1024, src, o[t]);
+}
+
 // One copy of 16 (or 4) bytes per lane from a buffer resource at byte offset
 // `o`; lane l's piece lands at lds + 16 l (lds + 4 l).  Wave-uniform control
 // flow only.
@@ -241,10 +281,6 @@ template <int N> __device__ inline void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// LDS byte address of a pointer into LDS.
-__device__ inline uint32_t lds_addr(const void *p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
-}
 // Four 16-byte LDS reads the compiler does not track: it would otherwise
 // make them wait for every direct copy in flight into LDS (it cannot tell
 // that they touch other regions).  The block waits for its own reads before

@@ -134,6 +134,104 @@ def copy_probe(torch):
     print(json.dumps({"copy_probe_bytes": COPY_BYTES, "dispatches": 3}), flush=True)
 
 
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E bandwidth (AMD specification)
+
+
+def decode_bench(args, x, F, torch):
+    """Decode steps against a cache holding all T tokens of every sequence of the workload.
+
+    Algorithmic bytes per step: the cached keys and values in their stored fp16 form
+    (T * (dk + dv) * 2 per sequence and kv head) plus q and o; the cache's fp64 chunk
+    decay prefixes (dv * 8 per 64 tokens) are extra traffic, not counted."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import oracle as O
+    from gpu_util import err_rms
+    wl = x["workload"]
+    B, T, Hq, Hkv, dk, dv = wl.B, wl.T, wl.Hq, wl.Hkv, wl.dk, wl.dv
+    bf = torch.bfloat16
+    dev = lambda a, dt=bf: torch.from_numpy(np.ascontiguousarray(a)).to(dt).cuda()
+    cache = F.DecodeCache(B, T, Hq, Hkv, dk, dv, dtype=bf, out_dtype=bf, o_norm=True)
+    cache.append(dev(x["k"]), dev(x["v"]), dev(x["g"], torch.float32))
+    q = dev(x["q"][:, T - 1])
+    w = dev(x["w"])
+    torch.cuda.synchronize()
+    print(f"[bench] decode cache filled: B={B} T={T} Hq={Hq} Hkv={Hkv} dk={dk} dv={dv}", file=sys.stderr, flush=True)
+    # parity gate: every sequence and head, against the oracle's last row
+    cf = F.DecodeCache(B, T, Hq, Hkv, dk, dv, dtype=bf, out_dtype=torch.float32, o_norm=True)
+    cf.append(dev(x["k"]), dev(x["v"]), dev(x["g"], torch.float32))
+    o32, m32 = cf.step(q, w)
+    torch.cuda.synchronize()
+    ref = O.oracle_fwd(x["q"], x["k"], x["v"], x["g"], window=1, w=x["w"])
+    err = err_rms(o32.cpu().numpy(), ref["o"][:, T - 1])
+    print(f"[bench] decode parity gate: {'pass' if err <= 1e-2 else 'FAIL'} o err {err:.2e}", file=sys.stderr,
+          flush=True)
+    if err > 1e-2:
+        sys.exit(1)
+    del cf
+    for _ in range(args.warmup):
+        cache.step(q, w)
+    torch.cuda.synchronize()
+    h = hip()
+    lib = F.library()
+    lib.fix_attn_set_event_trace.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    lib.fix_attn_event_trace_count.restype = ctypes.c_int
+    lib.fix_attn_event_trace_label.restype = ctypes.c_char_p
+    lib.fix_attn_event_trace_label.argtypes = [ctypes.c_int]
+    cap = 4
+    evs = []
+    for _ in range(args.steps):
+        arr = (ctypes.c_void_p * cap)()
+        for i in range(cap):
+            e = ctypes.c_void_p()
+            assert h.hipEventCreate(ctypes.byref(e)) == 0
+            arr[i] = e
+        evs.append(arr)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        lib.fix_attn_set_event_trace(ctypes.cast(evs[k], ctypes.c_void_p), cap)
+        cache.step(q, w)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    n = lib.fix_attn_event_trace_count()
+    labels = [lib.fix_attn_event_trace_label(i).decode() for i in range(1, n)]
+    lib.fix_attn_set_event_trace(None, 0)
+    per = {}
+    for k in range(args.steps):
+        for i in range(1, n):
+            t = ctypes.c_float()
+            assert h.hipEventElapsedTime(ctypes.byref(t), evs[k][i - 1], evs[k][i]) == 0
+            per.setdefault(labels[i - 1], []).append(t.value)
+    avg = {k: sum(v) / len(v) for k, v in per.items()}
+    ms = (t1 - t0) * 1e3 / args.steps
+    kv_bytes = B * Hkv * T * (dk + dv) * 2
+    io_bytes = B * Hq * (dk + dv) * 2
+    alg = kv_bytes + io_bytes
+    ach = alg / (avg["decode_step"] * 1e-3) / 1e9
+    out = {
+        "metric": "FiX decode step HBM GB/s (cache of T=8192 tokens per sequence, d=128, bf16)",
+        "value": round(alg / (ms * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": f"decode: B={B} cache T={T} Hq={Hq} Hkv={Hkv} dk={dk} dv={dv}, one query per "
+                               f"sequence, o_norm, bf16 in/out, cache operands fp16",
+                   "alg_bytes": alg, "kernel_ms": {k: round(v, 4) for k, v in avg.items()}},
+        "roofline": {"bound": "hbm", "kernel": "decode_step", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                     "avg_launch_ms": round(avg["decode_step"], 4)},
+    }
+    if not args.no_cpu_baseline:
+        O.load()
+        c0 = time.perf_counter()
+        O.oracle_fwd(x["q"], x["k"], x["v"], x["g"], window=1, w=x["w"])
+        c1 = time.perf_counter()
+        cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        out["cpu_baseline"] = {"value": round(alg / (c1 - c0) / 1e9, 3), "unit": "GB/s", "cores": cores,
+                               "kind": "oracle",
+                               "sample": f"the whole step: the last row of every sequence and head, {c1 - c0:.2f} s"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -144,6 +242,8 @@ def main():
                     help="pass the gate as raw logits (logsigmoid applied inside the kernels)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (HBM counter calibration)")
+    ap.add_argument("--decode", action="store_true",
+                    help="time decode steps (fix_decode_step) against a cache holding the workload's T tokens")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build runs the kernel on one GPU's share and has no "
@@ -158,6 +258,9 @@ def main():
     from gated_softmax_attention_amd import synth
 
     x = synth.make_inputs(WORKLOAD)
+    if args.decode:
+        decode_bench(args, x, F, torch)
+        return
     wl = x["workload"]
     dev = lambda a, dt=torch.bfloat16: torch.from_numpy(np.ascontiguousarray(a)).to(dt).cuda()
     d = {n: dev(x[n]) for n in ("q", "k", "v", "dO")}

@@ -37,6 +37,18 @@ class fix_attn_desc(ctypes.Structure):
     ]
 
 
+class fix_decode_desc(ctypes.Structure):
+    """Mirror of the C struct fix_decode_desc (include/fixattn.h)."""
+    _fields_ = [
+        ("B", ctypes.c_int64), ("cap", ctypes.c_int64),
+        ("Hq", ctypes.c_int64), ("Hkv", ctypes.c_int64),
+        ("dk", ctypes.c_int64), ("dv", ctypes.c_int64),
+        ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
+        ("scale", ctypes.c_float), ("eps", ctypes.c_float),
+        ("o_norm", ctypes.c_int32), ("gate_logits", ctypes.c_int32),
+    ]
+
+
 _lib = None
 
 
@@ -58,6 +70,19 @@ def _load():
     lib.fix_attn_fwd.restype = ctypes.c_int
     lib.fix_attn_bwd.argtypes = [D] + [P] * 17 + [S, P]
     lib.fix_attn_bwd.restype = ctypes.c_int
+    DD = ctypes.POINTER(fix_decode_desc)
+    lib.fix_decode_validate.argtypes = [DD]
+    lib.fix_decode_validate.restype = ctypes.c_int
+    lib.fix_decode_cache_size.argtypes = [DD]
+    lib.fix_decode_cache_size.restype = S
+    lib.fix_decode_workspace_size.argtypes = [DD]
+    lib.fix_decode_workspace_size.restype = S
+    lib.fix_decode_reset.argtypes = [DD, P, P]
+    lib.fix_decode_reset.restype = ctypes.c_int
+    lib.fix_decode_append.argtypes = [DD, P, P, P, P, ctypes.c_int64, P, P]
+    lib.fix_decode_append.restype = ctypes.c_int
+    lib.fix_decode_step.argtypes = [DD, P, P, P, P, P, P, P, S, P]
+    lib.fix_decode_step.restype = ctypes.c_int
     lib.fix_attn_status_string.argtypes = [ctypes.c_int]
     lib.fix_attn_status_string.restype = ctypes.c_char_p
     lib.fix_attn_last_hip_error.argtypes = []
@@ -275,3 +300,68 @@ __all__ = [
     "fix_attn_bwd", "FixAttnError", "FIX_OK", "FIX_E_INVALID", "FIX_E_UNSUPPORTED", "FIX_E_WORKSPACE",
     "FIX_E_HIP", "FIX_BF16", "FIX_F32",
 ]
+
+
+class DecodeCache:
+    """A key/value/gate cache for one-token decode steps (fix_decode_* in
+    include/fixattn.h): the cache buffer and the step's scratch are torch
+    device tensors owned by this object.
+
+        c = DecodeCache(B, cap, Hq, Hkv, dk, dv, dtype=torch.bfloat16)
+        c.append(k, v, g)           # k [B,n,Hkv,dk], v/g [B,n,Hkv,dv]
+        o, m = c.step(q)            # q [B,Hq,dk] of the newest token
+    """
+
+    def __init__(self, B, cap, Hq, Hkv, dk, dv, *, dtype=None, out_dtype=None, scale=None, eps=1e-5,
+                 o_norm=False, gate_logits=False, device="cuda"):
+        import torch
+        dtype = torch.bfloat16 if dtype is None else dtype
+        dt = {torch.bfloat16: FIX_BF16, torch.float32: FIX_F32}
+        self.dtype, self.out_dtype = dtype, dtype if out_dtype is None else out_dtype
+        d = fix_decode_desc()
+        d.B, d.cap, d.Hq, d.Hkv, d.dk, d.dv = B, cap, Hq, Hkv, dk, dv
+        d.in_dtype, d.out_dtype = dt[dtype], dt[self.out_dtype]
+        d.scale = 0.0 if scale is None else float(scale)
+        d.eps = float(eps)
+        d.o_norm = 1 if o_norm else 0
+        d.gate_logits = 1 if gate_logits else 0
+        lib = _load()
+        _check("fix_decode_validate", lib.fix_decode_validate(ctypes.byref(d)))
+        self.desc = d
+        self.cache = torch.empty(lib.fix_decode_cache_size(ctypes.byref(d)), dtype=torch.uint8, device=device)
+        self.ws = torch.empty(lib.fix_decode_workspace_size(ctypes.byref(d)), dtype=torch.uint8, device=device)
+        self.reset()
+
+    def reset(self):
+        _check("fix_decode_reset", _load().fix_decode_reset(ctypes.byref(self.desc), _ptr(self.cache), _stream()))
+
+    def append(self, k, v, g, n_seq=None):
+        """Append n tokens per sequence (the first n_seq[b] of row b, n_seq an int32 device tensor)."""
+        d = self.desc
+        n = k.shape[1]
+        if (tuple(k.shape) != (d.B, n, d.Hkv, d.dk) or tuple(v.shape) != (d.B, n, d.Hkv, d.dv)
+                or tuple(g.shape) != (d.B, n, d.Hkv, d.dv)):
+            raise ValueError("k, v, g shapes do not match the cache")
+        import torch
+        if k.dtype != self.dtype or v.dtype != self.dtype or g.dtype != torch.float32:
+            raise ValueError("k, v must have the cache dtype and g float32")
+        for t in (k, v, g):
+            if not t.is_contiguous():
+                raise ValueError("tensors must be contiguous")
+        st = _load().fix_decode_append(ctypes.byref(d), _ptr(self.cache), _ptr(k), _ptr(v), _ptr(g), n,
+                                       _ptr(n_seq), _stream())
+        _check("fix_decode_append", st)
+
+    def step(self, q, o_norm_weight=None, o_gate=None):
+        """Output (o [B,Hq,dv], m [B,Hq]) of the newest cached token of every sequence."""
+        import torch
+        d = self.desc
+        if tuple(q.shape) != (d.B, d.Hq, d.dk) or q.dtype != self.dtype or not q.is_contiguous():
+            raise ValueError("q must be a contiguous [B, Hq, dk] tensor of the cache dtype")
+        o = torch.empty(d.B, d.Hq, d.dv, dtype=self.out_dtype, device=q.device)
+        m = torch.empty(d.B, d.Hq, dtype=torch.float32, device=q.device)
+        st = _load().fix_decode_step(ctypes.byref(d), _ptr(self.cache), _ptr(q),
+                                     _ptr(o_norm_weight) if d.o_norm else None, _ptr(o_gate), _ptr(o), _ptr(m),
+                                     _ptr(self.ws), self.ws.numel(), _stream())
+        _check("fix_decode_step", st)
+        return o, m

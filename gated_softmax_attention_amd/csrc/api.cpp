@@ -147,6 +147,33 @@ fix_status hip_fail(hipError_t e) {
 
 }  // namespace
 
+// ---- decode cache and workspace layout (see decode.hip) ----
+int decode_splits(const fix_decode_desc *d) {
+  const int64_t nch = d->cap / fix::CH, s = cdiv(nch, 16);
+  return (int)(s < 1 ? 1 : s > 64 ? 64 : s);
+}
+size_t carve_decode(Carve &cv, const fix_decode_desc *d, fix::DecodeCache &dc) {
+  const int64_t B = d->B, cap = d->cap, Hkv = d->Hkv, nch = cap / fix::CH;
+  dc.B = (int)B; dc.cap = (int)cap; dc.Hq = (int)d->Hq; dc.Hkv = (int)Hkv; dc.G = (int)(d->Hq / d->Hkv);
+  dc.dk = (int)d->dk; dc.dv = (int)d->dv;
+  dc.len = cv.take<int>(B);
+  dc.K = cv.take<_Float16>(B * cap * Hkv * d->dk);
+  dc.VT = cv.take<_Float16>(B * nch * Hkv * d->dv * fix::CH);
+  dc.Vo = cv.take<_Float16>(B * fix::CH * Hkv * d->dv);
+  dc.Go = cv.take<float>(B * fix::CH * Hkv * d->dv);
+  dc.Lam = cv.take<double>(B * (nch + 1) * Hkv * d->dv);
+  return cv.off;
+}
+struct DecodeWs {
+  float *part, *mpart;
+};
+size_t carve_decode_ws(Carve &cv, const fix_decode_desc *d, DecodeWs &w) {
+  const int64_t units = 4 * decode_splits(d), rows = d->B * d->Hkv * units * (d->Hq / d->Hkv);
+  w.part = cv.take<float>(rows * d->dv);
+  w.mpart = cv.take<float>(rows);
+  return cv.off;
+}
+
 extern "C" {
 
 fix_status fix_attn_validate(const fix_attn_desc *d) {
@@ -301,6 +328,92 @@ fix_status fix_attn_bwd(const fix_attn_desc *d, const void *q, const void *k, co
   }
 #undef FIX_TRY
   return FIX_OK;
+}
+
+fix_status fix_decode_validate(const fix_decode_desc *d) {
+  if (!d) return FIX_E_INVALID;
+  if (d->B < 1 || d->cap < 1 || d->Hq < 1 || d->Hkv < 1 || d->dk < 1 || d->dv < 1) return FIX_E_INVALID;
+  if (d->Hq % d->Hkv != 0 || d->cap % fix::CH != 0) return FIX_E_INVALID;
+  if (d->in_dtype != FIX_BF16 && d->in_dtype != FIX_F32) return FIX_E_INVALID;
+  if (d->out_dtype != FIX_BF16 && d->out_dtype != FIX_F32) return FIX_E_INVALID;
+  if (std::isnan(d->scale) || std::isnan(d->eps) || std::isinf(d->scale) || std::isinf(d->eps) || d->eps < 0)
+    return FIX_E_INVALID;
+  if (!head_dim_ok(d->dk) || !head_dim_ok(d->dv)) return FIX_E_UNSUPPORTED;
+  if (d->Hq / d->Hkv > 32) return FIX_E_UNSUPPORTED;
+  if (d->cap >= (int64_t(1) << 30) || d->B >= (int64_t(1) << 20) || d->B * d->Hq >= (int64_t(1) << 31))
+    return FIX_E_UNSUPPORTED;
+  const int64_t D = d->dk > d->dv ? d->dk : d->dv;
+  if ((double)d->B * (double)d->cap * (double)d->Hkv * (double)D >= (double)(int64_t(1) << 40))
+    return FIX_E_UNSUPPORTED;
+  return FIX_OK;
+}
+
+size_t fix_decode_cache_size(const fix_decode_desc *d) {
+  if (fix_decode_validate(d) != FIX_OK) return 0;
+  Carve cv(nullptr);
+  fix::DecodeCache dc;
+  return carve_decode(cv, d, dc);
+}
+
+size_t fix_decode_workspace_size(const fix_decode_desc *d) {
+  if (fix_decode_validate(d) != FIX_OK) return 0;
+  Carve cv(nullptr);
+  DecodeWs w;
+  return carve_decode_ws(cv, d, w);
+}
+
+fix_status fix_decode_reset(const fix_decode_desc *d, void *cache, void *hip_stream) {
+  fix_status stt = fix_decode_validate(d);
+  if (stt != FIX_OK) return stt;
+  if (!cache || ((uintptr_t)cache & 255)) return FIX_E_INVALID;
+  Carve cv(cache);
+  fix::DecodeCache dc;
+  carve_decode(cv, d, dc);
+  hipError_t e = fix::launch_decode_reset(dc, (hipStream_t)hip_stream);
+  return e == hipSuccess ? FIX_OK : hip_fail(e);
+}
+
+fix_status fix_decode_append(const fix_decode_desc *d, void *cache, const void *k, const void *v, const float *g,
+                             int64_t n, const int32_t *n_seq, void *hip_stream) {
+  fix_status stt = fix_decode_validate(d);
+  if (stt != FIX_OK) return stt;
+  if (!cache || ((uintptr_t)cache & 255) || !k || !v || !g || n < 1 || n > d->cap) return FIX_E_INVALID;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(g)) return FIX_E_INVALID;
+  Carve cv(cache);
+  fix::DecodeCache dc;
+  carve_decode(cv, d, dc);
+  hipError_t e = fix::launch_decode_append(dc, k, v, g, (int)n, n_seq, d->in_dtype == FIX_F32, d->gate_logits != 0,
+                                           (hipStream_t)hip_stream);
+  return e == hipSuccess ? FIX_OK : hip_fail(e);
+}
+
+fix_status fix_decode_step(const fix_decode_desc *d, const void *cache, const void *q, const void *o_norm_weight,
+                           const void *o_gate, void *o, float *m, void *ws, size_t ws_bytes, void *hip_stream) {
+  fix_status stt = fix_decode_validate(d);
+  if (stt != FIX_OK) return stt;
+  if (!cache || ((uintptr_t)cache & 255) || !q || !o) return FIX_E_INVALID;
+  if (!aligned16(q) || !aligned16(o) || (o_gate && !aligned16(o_gate))) return FIX_E_INVALID;
+  const size_t need = fix_decode_workspace_size(d);
+  if (ws_bytes < need || !ws) return FIX_E_WORKSPACE;
+  if (!aligned16(ws)) return FIX_E_INVALID;
+  hipStream_t st = (hipStream_t)hip_stream;
+  Carve cv((void *)cache);
+  fix::DecodeCache dc;
+  carve_decode(cv, d, dc);
+  Carve cw(ws);
+  DecodeWs w;
+  carve_decode_ws(cw, d, w);
+  const bool f32in = d->in_dtype == FIX_F32;
+  const float scale = d->scale > 0.f ? d->scale : 1.0f / std::sqrt((float)d->dk);
+  const int splits = decode_splits(d);
+  hipError_t e = trace_begin(st);
+  if (e == hipSuccess) e = fix::launch_decode_step(dc, q, f32in, scale * fix::LOG2E, splits, w.part, w.mpart, st);
+  if (e == hipSuccess) e = trace_mark(st, "decode_step");
+  if (e == hipSuccess)
+    e = fix::launch_decode_combine(dc, 4 * splits, w.part, w.mpart, d->o_norm ? o_norm_weight : nullptr, o_gate, f32in,
+                                   d->out_dtype == FIX_F32, d->o_norm != 0, d->eps, o, m, st);
+  if (e == hipSuccess) e = trace_mark(st, "decode_combine");
+  return e == hipSuccess ? FIX_OK : hip_fail(e);
 }
 
 const char *fix_attn_status_string(fix_status s) {

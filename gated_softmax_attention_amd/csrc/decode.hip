@@ -1,0 +1,323 @@
+// Decode: the FiX output of the newest token of each sequence against a cache
+// of the sequence's earlier keys, values and gates (FiX ICML 2026 poster page,
+// abstract: inference memory is one of the challenges the method addresses;
+// the operation is the one of the FiX README, "Quick Start").
+//
+// For the newest token t of a sequence and query head h (kv head c):
+//   x_t = sum_{j<=t} exp(s_tj - m_t) * exp(G_t - G_j) (.) v_j
+// with the per-channel decay exp(G_t - G_j) factored around chunks of
+// CH = 64 tokens, as in the forward: a closed chunk n holds its values scaled
+// to the chunk end, Vt_j = exp(G_end(n) - G_j) v_j (every factor <= 1 for a
+// forget gate), so that its contribution is exp(G_t - G_end(n)) (.) sum_j
+// p_tj Vt_j, the chunk factor taken from fp64 prefixes of the chunk totals.
+// The open (partial) chunk keeps raw values and its chunk-local prefix, and
+// its tokens are decayed one by one.
+//
+// Cache layout (one caller buffer, carved in this order, 256-byte aligned):
+//   len  [B]                      int32   tokens held per sequence
+//   K    [B, cap, Hkv, dk]        fp16    keys
+//   VT   [B, cap/64, Hkv, dv, 64] fp16    closed chunks: V scaled to the chunk
+//                                         end, transposed, keys in key_pos order
+//   Vo   [B, 64, Hkv, dv]         fp16    the open chunk's values (slot t % 64)
+//   Go   [B, 64, Hkv, dv]         fp32    its chunk-local inclusive prefix of
+//                                         g * log2(e)
+//   Lam  [B, cap/64 + 1, Hkv, dv] fp64    log2 decay prefix at each chunk start
+// fp16 operands assume |k|, |v| and |q| in [2^-14, 65504] like the backward.
+#include "common.h"
+#include "launch.h"
+
+namespace fix {
+
+// Appends up to n tokens to every sequence (row b appends the first n_seq[b]
+// rows of its [n, Hkv, d] block, or all n when n_seq is null).  Workgroup =
+// (sequence, kv head); thread i owns channel i of k and of v / g.  Tokens
+// past the capacity are dropped.
+__global__ void __launch_bounds__(128) k_decode_append(DecodeCache dc, const void *__restrict__ k,
+                                                       const void *__restrict__ v, const float *__restrict__ g,
+                                                       int n, const int *__restrict__ n_seq, bool in_f32,
+                                                       bool logits) {
+  const int b = blockIdx.x, c = blockIdx.y, i = threadIdx.x;
+  const int Hkv = dc.Hkv, dk = dc.dk, dv = dc.dv;
+  const int len0 = dc.len[b];
+  const int cnt = min(n_seq ? min(max(n_seq[b], 0), n) : n, dc.cap - len0);
+  const int nch = dc.cap / CH;
+  for (int u = 0; u < cnt; ++u) {
+    const int t = len0 + u, slot = t % CH;
+    const int64_t src = (((int64_t)b * n + u) * Hkv + c);
+    if (i < dk) dc.K[(((int64_t)b * dc.cap + t) * Hkv + c) * dk + i] = (_Float16)load_in(k, src * dk + i, in_f32);
+    if (i < dv) {
+      const int64_t o = (((int64_t)b * CH + slot) * Hkv + c) * dv + i;
+      float gv = g[src * dv + i];
+      if (logits) gv = log_sigmoid(gv);
+      const float prev = slot == 0 ? 0.f : dc.Go[o - (int64_t)Hkv * dv];
+      const float gl = prev + gv * LOG2E;
+      dc.Go[o] = gl;
+      dc.Vo[o] = (_Float16)load_in(v, src * dv + i, in_f32);
+      if (slot == CH - 1) {  // the chunk is full: seal it
+        const int n_ = t / CH;
+        _Float16 row[CH];
+        for (int j = 0; j < CH; ++j) {
+          const int64_t oj = (((int64_t)b * CH + j) * Hkv + c) * dv + i;
+          row[key_pos(j)] = (_Float16)(fast_exp2(gl - dc.Go[oj]) * (float)dc.Vo[oj]);
+        }
+        uint4 *dst = (uint4 *)(dc.VT + ((((int64_t)b * nch + n_) * Hkv + c) * dv + i) * CH);
+        for (int p = 0; p < CH / 8; ++p) dst[p] = *(const uint4 *)(row + 8 * p);
+        const int64_t l0 = (((int64_t)b * (nch + 1) + n_) * Hkv + c) * dv + i;
+        dc.Lam[l0 + (int64_t)Hkv * dv] = dc.Lam[l0] + (double)gl;
+      }
+    }
+  }
+}
+
+// New lengths, after every workgroup of the append has read the old ones.
+__global__ void k_decode_len(DecodeCache dc, int n, const int *__restrict__ n_seq) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < dc.B) dc.len[b] = min(dc.cap, dc.len[b] + (n_seq ? min(max(n_seq[b], 0), n) : n));
+}
+
+// Empties every sequence: lengths 0 and a zero decay prefix at chunk 0.
+__global__ void k_decode_reset(DecodeCache dc) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per = (int64_t)dc.Hkv * dc.dv, nch1 = dc.cap / CH + 1;
+  if (e < (int64_t)dc.B * per) dc.Lam[(e / per) * nch1 * per + e % per] = 0.0;
+  if (e < dc.B) dc.len[e] = 0;
+}
+
+// One decode step, split over the cached chunks.  Grid (split, sequence *
+// kv head), 4 waves; unit = 4 * split + wave takes chunks unit, unit + U, ...
+// (U = 4 * splits), the open chunk being the one numbered nclosed.  A wave
+// holds the G query rows of the group padded to 32 (rows >= G are zero) and
+// computes S^T = K Q^T per 32-key half (lane = query, registers = keys), so
+// the row max is a reduction within a lane; P then is the A operand of the
+// P V product with the transposed chunk tile as B (the forward's layout).
+// The wave keeps an online row max: on a new maximum its accumulator rows are
+// rescaled.  It writes its partial (row max and x over dv) to the workspace.
+template <int DK, int DV>
+__global__ void __launch_bounds__(256) k_decode_step(DecodeCache dc, const void *__restrict__ q, bool in_f32, float sl2,
+                                                     int units, float *__restrict__ part, float *__restrict__ mpart) {
+  constexpr int NS = DK / 16, NBV = (DV < 32 ? 32 : DV) / 32;
+  const int Hkv = dc.Hkv, G = dc.G, nch = dc.cap / CH;
+  const int bc = blockIdx.y, b = bc / Hkv, c = bc % Hkv;
+  const int lane = threadIdx.x & 63, hh = lane >> 5, n = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int unit = 4 * blockIdx.x + wave;
+  const int len = uniform(dc.len[b]);
+  const int t = len - 1, nclosed = len / CH, open = len % CH;
+  const int nwork = nclosed + (open ? 1 : 0);
+
+  // query of the lane's row n (zero past the group)
+  f16x8 qf[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const int64_t o = ((int64_t)b * dc.Hq + c * G + min(n, G - 1)) * DK + 16 * i + 8 * hh;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qf[i][e] = n < G ? (_Float16)load_in(q, o + e, in_f32) : (_Float16)0.f;
+  }
+  // log2 decay prefix of the newest token, per output column of the lane
+  double lam_t[NBV];
+#pragma unroll
+  for (int bv = 0; bv < NBV; ++bv) {
+    const int d = min(32 * bv + n, DV - 1);
+    const int64_t l = (((int64_t)b * (nch + 1) + nclosed) * Hkv + c) * DV + d;
+    lam_t[bv] = len > 0 ? dc.Lam[l] : 0.0;
+    if (open) lam_t[bv] += (double)dc.Go[(((int64_t)b * CH + t % CH) * Hkv + c) * DV + d];
+  }
+  float gl_t[NBV];  // the newest token's chunk-local prefix (open chunk)
+#pragma unroll
+  for (int bv = 0; bv < NBV; ++bv)
+    gl_t[bv] = open ? dc.Go[(((int64_t)b * CH + t % CH) * Hkv + c) * DV + min(32 * bv + n, DV - 1)] : 0.f;
+
+  f32x16 acc[NBV];
+#pragma unroll
+  for (int bv = 0; bv < NBV; ++bv) acc[bv] = zero16();
+  float mrun = -INFINITY;  // row max (log2 units) of the lane's query row n
+  for (int w = unit; w < nwork; w += units) {
+    const bool is_open = w == nclosed;
+    const int t0 = w * CH;
+    // S^T[key][row]: lane = row n, register j = key acc_row(hh, j) of the half.
+    f32x16 sc[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int key = t0 + 32 * h + n;
+      const _Float16 *kr = dc.K + (((int64_t)b * dc.cap + min(key, t)) * Hkv + c) * DK;
+      sc[h] = zero16();
+#pragma unroll
+      for (int i = 0; i < NS; ++i) sc[h] = mma32(*(const f16x8 *)(kr + 16 * i + 8 * hh), qf[i], sc[h]);
+    }
+    float mc = -INFINITY;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int key = t0 + 32 * h + acc_row(hh, j);
+        sc[h][j] = key <= t ? sc[h][j] * sl2 : -INFINITY;
+        mc = fmaxf(mc, sc[h][j]);
+      }
+    mc = fmaxf(mc, __shfl_xor(mc, 32));
+    const float mnew = fmaxf(mrun, mc);
+    if (__any(mnew > mrun)) {
+      // rescale accumulator rows: register j holds row acc_row(hh, j)
+      const float r = mrun == -INFINITY ? 0.f : fast_exp2(mrun - mnew);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float rj = __shfl(r, acc_row(hh, j));
+#pragma unroll
+        for (int bv = 0; bv < NBV; ++bv) acc[bv][j] *= rj;
+      }
+    }
+    mrun = mnew;
+    // P^T as the A operand: fragment (h, u) = registers 8u .. 8u + 7 of half h
+    f16x8 pf[2][2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) pf[h][j >> 3][j & 7] = (_Float16)fast_exp2(sc[h][j] - mnew);
+    // B operand: column d = 32 bv + n, keys of positions 32 h + 16 u + 8 hh ..
+#pragma unroll
+    for (int bv = 0; bv < NBV; ++bv) {
+      const int d = min(32 * bv + n, DV - 1);
+      f32x16 part_c = zero16();
+      if (!is_open) {
+        const _Float16 *vt = dc.VT + ((((int64_t)b * nch + w) * Hkv + c) * DV + d) * CH;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+            part_c = mma32(pf[h][u], *(const f16x8 *)(vt + 32 * h + 16 * u + 8 * hh), part_c);
+        // chunk factor exp2(G_t - G_end(w)) of column d (<= 1)
+        const double lend = dc.Lam[(((int64_t)b * (nch + 1) + w + 1) * Hkv + c) * DV + d];
+        const float f = 32 * bv + n < DV ? fast_exp2((float)(lam_t[bv] - lend)) : 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[bv][j] += f * part_c[j];
+      } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            f16x8 vb;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int j = slab_key(u, hh, e) + 32 * h;  // key within the chunk
+              const int64_t o = (((int64_t)b * CH + j) * Hkv + c) * DV + d;
+              vb[e] = (t0 + j <= t && 32 * bv + n < DV) ? (_Float16)(fast_exp2(gl_t[bv] - dc.Go[o]) * (float)dc.Vo[o])
+                                                         : (_Float16)0.f;
+            }
+            part_c = mma32(pf[h][u], vb, part_c);
+          }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[bv][j] += part_c[j];
+      }
+    }
+  }
+  // partial of this unit: rows r < G, columns d
+  const int64_t pbase = ((int64_t)bc * units + unit) * G;
+  if (hh == 0 && n < G) mpart[pbase + n] = mrun;
+#pragma unroll
+  for (int bv = 0; bv < NBV; ++bv) {
+    const int d = 32 * bv + n;
+    if (d < DV)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int r = acc_row(hh, j);
+        if (r < G) part[(pbase + r) * DV + d] = acc[bv][j];
+      }
+  }
+}
+
+// Combines the units of one (sequence, query head) and applies the output
+// transform.  Block = max(DV, 64) threads (thread d: channel d).
+template <int DV>
+__global__ void __launch_bounds__(128) k_decode_combine(DecodeCache dc, int units, const float *__restrict__ part,
+                                                        const float *__restrict__ mpart, const void *__restrict__ w,
+                                                        const void *__restrict__ z, bool in_f32, bool out_f32,
+                                                        bool o_norm, float eps, void *__restrict__ o,
+                                                        float *__restrict__ m_out) {
+  const int bh = blockIdx.x, b = bh / dc.Hq, h = bh % dc.Hq, G = dc.G, c = h / G, r = h % G;
+  const int dd = threadIdx.x, d = min(dd, DV - 1);  // at least 64 threads: lanes >= DV add nothing
+  const int64_t bc = (int64_t)b * dc.Hkv + c;
+  float m = -INFINITY;
+  for (int u = 0; u < units; ++u) m = fmaxf(m, mpart[(bc * units + u) * G + r]);
+  float x = 0.f;
+  for (int u = 0; u < units; ++u) {
+    const float mu = mpart[(bc * units + u) * G + r];
+    if (mu != -INFINITY) x += fast_exp2(mu - m) * part[((bc * units + u) * G + r) * DV + d];
+  }
+  // RMSNorm over the DV channels (one wave per 64 channels, LDS across waves)
+  __shared__ float red[2];
+  float ss = dd < DV ? x * x : 0.f;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+  if (DV > 64) {
+    if ((dd & 63) == 0) red[dd >> 6] = ss;
+    __syncthreads();
+    ss = red[0] + red[1];
+  }
+  if (dd >= DV) return;
+  const float rs = rsqrtf(ss / DV + eps);
+  float y = x;
+  if (o_norm) y = x * rs * (w ? load_in(w, d, in_f32) : 1.f);
+  if (z) y *= load_in(z, (int64_t)bh * DV + d, in_f32);
+  store_out(o, (int64_t)bh * DV + d, y, out_f32);
+  if (m_out && d == 0) m_out[bh] = dc.len[b] > 0 ? m / LOG2E : 0.f;
+}
+
+hipError_t launch_decode_reset(const DecodeCache &dc, hipStream_t st) {
+  const int64_t nthr = (int64_t)dc.B * dc.Hkv * dc.dv;
+  hipLaunchKernelGGL(k_decode_reset, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, st, dc);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_append(const DecodeCache &dc, const void *k, const void *v, const float *g, int n,
+                                const int *n_seq, bool in_f32, bool logits, hipStream_t st) {
+  hipLaunchKernelGGL(k_decode_append, dim3(dc.B, dc.Hkv), dim3(128), 0, st, dc, k, v, g, n, n_seq, in_f32, logits);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_decode_len, dim3((dc.B + 63) / 64), dim3(64), 0, st, dc, n, n_seq);
+  return hipGetLastError();
+}
+
+template <int DK, int DV>
+static void step_dv(const DecodeCache &dc, const void *q, bool in_f32, float sl2, int splits, float *part, float *mpart,
+                    hipStream_t st) {
+  hipLaunchKernelGGL((k_decode_step<DK, DV>), dim3(splits, dc.B * dc.Hkv), dim3(256), 0, st, dc, q, in_f32, sl2,
+                     4 * splits, part, mpart);
+}
+template <int DK>
+static hipError_t step_dk(const DecodeCache &dc, const void *q, bool in_f32, float sl2, int splits, float *part,
+                          float *mpart, hipStream_t st) {
+  switch (dc.dv) {
+    case 16: step_dv<DK, 16>(dc, q, in_f32, sl2, splits, part, mpart, st); break;
+    case 32: step_dv<DK, 32>(dc, q, in_f32, sl2, splits, part, mpart, st); break;
+    case 64: step_dv<DK, 64>(dc, q, in_f32, sl2, splits, part, mpart, st); break;
+    case 128: step_dv<DK, 128>(dc, q, in_f32, sl2, splits, part, mpart, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_step(const DecodeCache &dc, const void *q, bool in_f32, float sl2, int splits, float *part,
+                              float *mpart, hipStream_t st) {
+  switch (dc.dk) {
+    case 16: return step_dk<16>(dc, q, in_f32, sl2, splits, part, mpart, st);
+    case 32: return step_dk<32>(dc, q, in_f32, sl2, splits, part, mpart, st);
+    case 64: return step_dk<64>(dc, q, in_f32, sl2, splits, part, mpart, st);
+    case 128: return step_dk<128>(dc, q, in_f32, sl2, splits, part, mpart, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_combine(const DecodeCache &dc, int units, const float *part, const float *mpart,
+                                 const void *w, const void *z, bool in_f32, bool out_f32, bool o_norm, float eps,
+                                 void *o, float *m, hipStream_t st) {
+  const dim3 grid(dc.B * dc.Hq);
+  switch (dc.dv) {
+    case 16: hipLaunchKernelGGL((k_decode_combine<16>), grid, dim3(64), 0, st, dc, units, part, mpart, w, z, in_f32, out_f32, o_norm, eps, o, m); break;
+    case 32: hipLaunchKernelGGL((k_decode_combine<32>), grid, dim3(64), 0, st, dc, units, part, mpart, w, z, in_f32, out_f32, o_norm, eps, o, m); break;
+    case 64: hipLaunchKernelGGL((k_decode_combine<64>), grid, dim3(64), 0, st, dc, units, part, mpart, w, z, in_f32, out_f32, o_norm, eps, o, m); break;
+    case 128: hipLaunchKernelGGL((k_decode_combine<128>), grid, dim3(128), 0, st, dc, units, part, mpart, w, z, in_f32, out_f32, o_norm, eps, o, m); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fix

@@ -88,6 +88,23 @@ hipError_t launch_gate_prep_rows(int dv, const float *g, bool logits, const void
                                  int Hkv, int ncb_ub, float *Gl2, float *Gam, _Float16 *Vr, _Float16 *VE, __bf16 *VBH,
                                  __bf16 *VBL, hipStream_t st);
 hipError_t launch_chunk_logprefix(int dv, const float *Gl2, const Plan &plan, int Hkv, double *Lam, hipStream_t st);
+// Decode cache (layout in decode.hip): device pointers carved from one
+// caller buffer, and the shape they were carved for.
+struct DecodeCache {
+  int B, cap, Hq, Hkv, G, dk, dv;
+  int *len;
+  _Float16 *K, *VT, *Vo;
+  float *Go;
+  double *Lam;
+};
+hipError_t launch_decode_reset(const DecodeCache &dc, hipStream_t st);
+hipError_t launch_decode_append(const DecodeCache &dc, const void *k, const void *v, const float *g, int n,
+                                const int *n_seq, bool in_f32, bool logits, hipStream_t st);
+hipError_t launch_decode_step(const DecodeCache &dc, const void *q, bool in_f32, float sl2, int splits, float *part,
+                              float *mpart, hipStream_t st);
+hipError_t launch_decode_combine(const DecodeCache &dc, int units, const float *part, const float *mpart,
+                                 const void *w, const void *z, bool in_f32, bool out_f32, bool o_norm, float eps,
+                                 void *o, float *m, hipStream_t st);
 hipError_t launch_to_f16(const void *in, bool in_f32, int64_t n, _Float16 *out, hipStream_t st);
 hipError_t launch_tiles_t(int D, const void *in, bool in_f32, const Plan &plan, int H, int ncb_ub, _Float16 *out,
                           hipStream_t st);

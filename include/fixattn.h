@@ -131,9 +131,72 @@ fix_status fix_attn_bwd(const fix_attn_desc *d, const void *q, const void *k, co
                         void *dq, void *dk, void *dv, float *dg, float *d_o_norm_weight,
                         void *d_o_gate, void *ws, size_t ws_bytes, void *hip_stream);
 
+/* ---- Decode: the newest token of each sequence against a cache ----
+ * Inference runs the operation above one token at a time (FiX ICML 2026
+ * poster page, abstract: the method's inference memory).  For the newest
+ * token t of sequence b and query head h, fix_decode_step computes o_t (and
+ * m_t) exactly as fix_attn_fwd would for row t of the whole sequence held in
+ * the cache.  The cache is one caller-owned device buffer of
+ * fix_decode_cache_size bytes (256-byte aligned), laid out by the library:
+ * keys (fp16), closed 64-token chunks of values scaled to their chunk end
+ * (fp16, transposed), the open chunk's values (fp16) and chunk-local gate
+ * prefix (fp32), fp64 decay prefixes at chunk starts, and per-sequence
+ * lengths.  It holds up to cap tokens per sequence; its contents are only
+ * meaningful to these entry points.  fp16 storage assumes |k|, |v|, |q| in
+ * [2^-14, 65504] (smaller magnitudes keep an absolute error below 2^-25).
+ * Calls on one cache are ordered by their stream; calls that overlap on one
+ * cache race. */
+typedef struct {
+  int64_t B;           /* sequences held by the cache */
+  int64_t cap;         /* tokens per sequence, a positive multiple of 64 */
+  int64_t Hq, Hkv;     /* query heads and key/value heads, Hq % Hkv == 0, Hq / Hkv <= 32 */
+  int64_t dk, dv;      /* head dims, each in {16, 32, 64, 128} */
+  fix_dtype in_dtype;  /* q, k, v, o_norm_weight and o_gate */
+  fix_dtype out_dtype; /* o */
+  float scale;         /* logit scale; <= 0 selects dk^-1/2 */
+  float eps;           /* RMSNorm epsilon (used when o_norm != 0) */
+  int32_t o_norm;      /* nonzero: apply RMSNorm and o_norm_weight */
+  int32_t gate_logits; /* nonzero: g holds logits x and the gate is logsigmoid(x) */
+} fix_decode_desc;
+
+/* Host-only check of a decode descriptor (no HIP call).
+ * FIX_E_INVALID: B, cap, Hq, Hkv, dk or dv < 1; cap % 64 != 0; Hq % Hkv != 0;
+ *   unknown dtype; negative eps; NaN or infinite scale or eps.
+ * FIX_E_UNSUPPORTED: dk or dv not in {16, 32, 64, 128}; Hq / Hkv > 32;
+ *   cap >= 2^30; B >= 2^20; B * Hq >= 2^31; B * cap * Hkv * max(dk, dv) >= 2^40. */
+fix_status fix_decode_validate(const fix_decode_desc *d);
+
+/* Bytes of the cache buffer, and of the scratch fix_decode_step needs (0
+ * when the descriptor does not validate). */
+size_t fix_decode_cache_size(const fix_decode_desc *d);
+size_t fix_decode_workspace_size(const fix_decode_desc *d);
+
+/* Empties every sequence of the cache (lengths 0). */
+fix_status fix_decode_reset(const fix_decode_desc *d, void *cache, void *hip_stream);
+
+/* Appends tokens to every sequence: row b of
+ *   k [B,n,Hkv,dk], v [B,n,Hkv,dv]   in_dtype
+ *   g [B,n,Hkv,dv]                   fp32 log-space gate (or logits)
+ * contributes its first n_seq[b] tokens (n_seq: device int32 [B] with
+ * 0 <= n_seq[b] <= n, or NULL for all n).  1 <= n <= cap is checked on the
+ * host; tokens that would take a sequence past cap are dropped (a device
+ * condition the host cannot see). */
+fix_status fix_decode_append(const fix_decode_desc *d, void *cache, const void *k, const void *v, const float *g,
+                             int64_t n, const int32_t *n_seq, void *hip_stream);
+
+/* One decode step: the output for the newest cached token of every sequence.
+ *   q [B,Hq,dk] in_dtype: the query of that token
+ *   o_norm_weight [dv] in_dtype or NULL (ones); read only when o_norm
+ *   o_gate [B,Hq,dv] in_dtype or NULL
+ * Outputs: o [B,Hq,dv] out_dtype (required); m [B,Hq] fp32 or NULL.  A
+ * sequence with no tokens gets o = 0 and m = 0.  ws: at least
+ * fix_decode_workspace_size bytes. */
+fix_status fix_decode_step(const fix_decode_desc *d, const void *cache, const void *q, const void *o_norm_weight,
+                           const void *o_gate, void *o, float *m, void *ws, size_t ws_bytes, void *hip_stream);
+
 /* Opt-in launch timing for benchmarks (host side, per calling thread).
  * With events non-NULL and capacity > 0, every later fix_attn_fwd /
- * fix_attn_bwd call on this thread records events[0] on its stream before
+ * fix_attn_bwd / fix_decode_step call on this thread records events[0] on its stream before
  * its first kernel and events[i] after its i-th launch, at most capacity
  * events; the events are hipEvent_t created by the caller and stay the
  * caller's.  fix_attn_event_trace_count() gives the number recorded by the

@@ -149,6 +149,8 @@ fix_status hip_fail(hipError_t e) {
 
 // ---- decode cache and workspace layout (see decode.hip) ----
 int decode_splits(const fix_decode_desc *d) {
+  // 16 chunks per split: measured best at T = 8192 (fewer add per-workgroup
+  // cost, more leave too few workgroups)
   const int64_t nch = d->cap / fix::CH, s = cdiv(nch, 16);
   return (int)(s < 1 ? 1 : s > 64 ? 64 : s);
 }
@@ -166,11 +168,13 @@ size_t carve_decode(Carve &cv, const fix_decode_desc *d, fix::DecodeCache &dc) {
 }
 struct DecodeWs {
   float *part, *mpart;
+  _Float16 *vto;  // the open chunk of every (sequence, kv head), decayed to the newest token
 };
 size_t carve_decode_ws(Carve &cv, const fix_decode_desc *d, DecodeWs &w) {
   const int64_t units = 4 * decode_splits(d), rows = d->B * d->Hkv * units * (d->Hq / d->Hkv);
   w.part = cv.take<float>(rows * d->dv);
   w.mpart = cv.take<float>(rows);
+  w.vto = cv.take<_Float16>(d->B * d->Hkv * d->dv * fix::CH);
   return cv.off;
 }
 
@@ -407,7 +411,9 @@ fix_status fix_decode_step(const fix_decode_desc *d, const void *cache, const vo
   const float scale = d->scale > 0.f ? d->scale : 1.0f / std::sqrt((float)d->dk);
   const int splits = decode_splits(d);
   hipError_t e = trace_begin(st);
-  if (e == hipSuccess) e = fix::launch_decode_step(dc, q, f32in, scale * fix::LOG2E, splits, w.part, w.mpart, st);
+  if (e == hipSuccess) e = fix::launch_decode_open(dc, w.vto, st);
+  if (e == hipSuccess) e = trace_mark(st, "decode_open");
+  if (e == hipSuccess) e = fix::launch_decode_step(dc, q, f32in, scale * fix::LOG2E, splits, w.vto, w.part, w.mpart, st);
   if (e == hipSuccess) e = trace_mark(st, "decode_step");
   if (e == hipSuccess)
     e = fix::launch_decode_combine(dc, 4 * splits, w.part, w.mpart, d->o_norm ? o_norm_weight : nullptr, o_gate, f32in,

@@ -83,6 +83,25 @@ __global__ void k_decode_reset(DecodeCache dc) {
   if (e < dc.B) dc.len[e] = 0;
 }
 
+// The open chunk of every (sequence, kv head) as a tile of the closed-chunk
+// layout, its values decayed to the newest token: exp2(Gl_t - Gl_j) v_j (zero
+// past t), so that the step treats it like a closed chunk with factor 1.
+// Block = dv threads (channel d).
+__global__ void __launch_bounds__(128) k_decode_open(DecodeCache dc, _Float16 *__restrict__ vto) {
+  const int b = blockIdx.x, c = blockIdx.y, d = threadIdx.x, Hkv = dc.Hkv, dv = dc.dv;
+  if (d >= dv) return;
+  const int len = dc.len[b], open = len % CH, last = (len - 1) % CH;
+  _Float16 row[CH];
+  const float glt = open ? dc.Go[(((int64_t)b * CH + last) * Hkv + c) * dv + d] : 0.f;
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    const int64_t o = (((int64_t)b * CH + j) * Hkv + c) * dv + d;
+    row[key_pos(j)] = j < open ? (_Float16)(fast_exp2(glt - dc.Go[o]) * (float)dc.Vo[o]) : (_Float16)0.f;
+  }
+  uint4 *dst = (uint4 *)(vto + (((int64_t)b * Hkv + c) * dv + d) * CH);
+  for (int p = 0; p < CH / 8; ++p) dst[p] = *(const uint4 *)(row + 8 * p);
+}
+
 // One decode step, split over the cached chunks.  Grid (split, sequence *
 // kv head), 4 waves; unit = 4 * split + wave takes chunks unit, unit + U, ...
 // (U = 4 * splits), the open chunk being the one numbered nclosed.  A wave
@@ -92,9 +111,11 @@ __global__ void k_decode_reset(DecodeCache dc) {
 // P V product with the transposed chunk tile as B (the forward's layout).
 // The wave keeps an online row max: on a new maximum its accumulator rows are
 // rescaled.  It writes its partial (row max and x over dv) to the workspace.
+// The open chunk comes from k_decode_open's tile.
 template <int DK, int DV>
-__global__ void __launch_bounds__(256) k_decode_step(DecodeCache dc, const void *__restrict__ q, bool in_f32, float sl2,
-                                                     int units, float *__restrict__ part, float *__restrict__ mpart) {
+__global__ void __launch_bounds__(256, 2) k_decode_step(DecodeCache dc, const void *__restrict__ q, bool in_f32, float sl2,
+                                                     int units, const _Float16 *__restrict__ vto,
+                                                     float *__restrict__ part, float *__restrict__ mpart) {
   constexpr int NS = DK / 16, NBV = (DV < 32 ? 32 : DV) / 32;
   const int Hkv = dc.Hkv, G = dc.G, nch = dc.cap / CH;
   const int bc = blockIdx.y, b = bc / Hkv, c = bc % Hkv;
@@ -122,10 +143,6 @@ __global__ void __launch_bounds__(256) k_decode_step(DecodeCache dc, const void 
     lam_t[bv] = len > 0 ? dc.Lam[l] : 0.0;
     if (open) lam_t[bv] += (double)dc.Go[(((int64_t)b * CH + t % CH) * Hkv + c) * DV + d];
   }
-  float gl_t[NBV];  // the newest token's chunk-local prefix (open chunk)
-#pragma unroll
-  for (int bv = 0; bv < NBV; ++bv)
-    gl_t[bv] = open ? dc.Go[(((int64_t)b * CH + t % CH) * Hkv + c) * DV + min(32 * bv + n, DV - 1)] : 0.f;
 
   f32x16 acc[NBV];
 #pragma unroll
@@ -173,40 +190,23 @@ __global__ void __launch_bounds__(256) k_decode_step(DecodeCache dc, const void 
 #pragma unroll
       for (int j = 0; j < 16; ++j) pf[h][j >> 3][j & 7] = (_Float16)fast_exp2(sc[h][j] - mnew);
     // B operand: column d = 32 bv + n, keys of positions 32 h + 16 u + 8 hh ..
+    // of the chunk's transposed tile (the open chunk: its decayed copy, factor 1)
 #pragma unroll
     for (int bv = 0; bv < NBV; ++bv) {
       const int d = min(32 * bv + n, DV - 1);
+      const _Float16 *vt = is_open ? vto + (((int64_t)b * Hkv + c) * DV + d) * CH
+                                   : dc.VT + ((((int64_t)b * nch + w) * Hkv + c) * DV + d) * CH;
       f32x16 part_c = zero16();
-      if (!is_open) {
-        const _Float16 *vt = dc.VT + ((((int64_t)b * nch + w) * Hkv + c) * DV + d) * CH;
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int u = 0; u < 2; ++u)
-            part_c = mma32(pf[h][u], *(const f16x8 *)(vt + 32 * h + 16 * u + 8 * hh), part_c);
-        // chunk factor exp2(G_t - G_end(w)) of column d (<= 1)
-        const double lend = dc.Lam[(((int64_t)b * (nch + 1) + w + 1) * Hkv + c) * DV + d];
-        const float f = 32 * bv + n < DV ? fast_exp2((float)(lam_t[bv] - lend)) : 0.f;
+        for (int u = 0; u < 2; ++u) part_c = mma32(pf[h][u], *(const f16x8 *)(vt + 32 * h + 16 * u + 8 * hh), part_c);
+      // chunk factor exp2(G_t - G_end(w)) of column d (<= 1; 1 for the open chunk)
+      float f = 1.f;
+      if (!is_open) f = fast_exp2((float)(lam_t[bv] - dc.Lam[(((int64_t)b * (nch + 1) + w + 1) * Hkv + c) * DV + d]));
+      if (32 * bv + n >= DV) f = 0.f;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) acc[bv][j] += f * part_c[j];
-      } else {
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            f16x8 vb;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int j = slab_key(u, hh, e) + 32 * h;  // key within the chunk
-              const int64_t o = (((int64_t)b * CH + j) * Hkv + c) * DV + d;
-              vb[e] = (t0 + j <= t && 32 * bv + n < DV) ? (_Float16)(fast_exp2(gl_t[bv] - dc.Go[o]) * (float)dc.Vo[o])
-                                                         : (_Float16)0.f;
-            }
-            part_c = mma32(pf[h][u], vb, part_c);
-          }
-#pragma unroll
-        for (int j = 0; j < 16; ++j) acc[bv][j] += part_c[j];
-      }
+      for (int j = 0; j < 16; ++j) acc[bv][j] += f * part_c[j];
     }
   }
   // partial of this unit: rows r < G, columns d
@@ -235,15 +235,34 @@ __global__ void __launch_bounds__(128) k_decode_combine(DecodeCache dc, int unit
   const int bh = blockIdx.x, b = bh / dc.Hq, h = bh % dc.Hq, G = dc.G, c = h / G, r = h % G;
   const int dd = threadIdx.x, d = min(dd, DV - 1);  // at least 64 threads: lanes >= DV add nothing
   const int64_t bc = (int64_t)b * dc.Hkv + c;
+  // the units' row maxima into LDS (units <= 256), their maximum by shuffles
+  __shared__ float mu_s[256];
+  __shared__ float red[2];
+  const int nthr = blockDim.x;
   float m = -INFINITY;
-  for (int u = 0; u < units; ++u) m = fmaxf(m, mpart[(bc * units + u) * G + r]);
-  float x = 0.f;
-  for (int u = 0; u < units; ++u) {
+  for (int u = dd; u < units; u += nthr) {
     const float mu = mpart[(bc * units + u) * G + r];
-    if (mu != -INFINITY) x += fast_exp2(mu - m) * part[((bc * units + u) * G + r) * DV + d];
+    mu_s[u] = mu;
+    m = fmaxf(m, mu);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if (nthr > 64) {
+    if ((dd & 63) == 0) red[dd >> 6] = m;
+    __syncthreads();
+    m = fmaxf(red[0], red[1]);
+    __syncthreads();
+  } else {
+    __syncthreads();
+  }
+  float x = 0.f;
+#pragma unroll 8
+  for (int u = 0; u < units; ++u) {
+    const float mu = mu_s[u];
+    const float pv = part[((bc * units + u) * G + r) * DV + d];
+    if (mu != -INFINITY) x += fast_exp2(mu - m) * pv;
   }
   // RMSNorm over the DV channels (one wave per 64 channels, LDS across waves)
-  __shared__ float red[2];
   float ss = dd < DV ? x * x : 0.f;
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
@@ -277,31 +296,36 @@ hipError_t launch_decode_append(const DecodeCache &dc, const void *k, const void
 }
 
 template <int DK, int DV>
-static void step_dv(const DecodeCache &dc, const void *q, bool in_f32, float sl2, int splits, float *part, float *mpart,
-                    hipStream_t st) {
+static void step_dv(const DecodeCache &dc, const void *q, bool in_f32, float sl2, int splits, const _Float16 *vto,
+                    float *part, float *mpart, hipStream_t st) {
   hipLaunchKernelGGL((k_decode_step<DK, DV>), dim3(splits, dc.B * dc.Hkv), dim3(256), 0, st, dc, q, in_f32, sl2,
-                     4 * splits, part, mpart);
+                     4 * splits, vto, part, mpart);
 }
 template <int DK>
-static hipError_t step_dk(const DecodeCache &dc, const void *q, bool in_f32, float sl2, int splits, float *part,
-                          float *mpart, hipStream_t st) {
+static hipError_t step_dk(const DecodeCache &dc, const void *q, bool in_f32, float sl2, int splits,
+                          const _Float16 *vto, float *part, float *mpart, hipStream_t st) {
   switch (dc.dv) {
-    case 16: step_dv<DK, 16>(dc, q, in_f32, sl2, splits, part, mpart, st); break;
-    case 32: step_dv<DK, 32>(dc, q, in_f32, sl2, splits, part, mpart, st); break;
-    case 64: step_dv<DK, 64>(dc, q, in_f32, sl2, splits, part, mpart, st); break;
-    case 128: step_dv<DK, 128>(dc, q, in_f32, sl2, splits, part, mpart, st); break;
+    case 16: step_dv<DK, 16>(dc, q, in_f32, sl2, splits, vto, part, mpart, st); break;
+    case 32: step_dv<DK, 32>(dc, q, in_f32, sl2, splits, vto, part, mpart, st); break;
+    case 64: step_dv<DK, 64>(dc, q, in_f32, sl2, splits, vto, part, mpart, st); break;
+    case 128: step_dv<DK, 128>(dc, q, in_f32, sl2, splits, vto, part, mpart, st); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_decode_step(const DecodeCache &dc, const void *q, bool in_f32, float sl2, int splits, float *part,
-                              float *mpart, hipStream_t st) {
+hipError_t launch_decode_open(const DecodeCache &dc, _Float16 *vto, hipStream_t st) {
+  hipLaunchKernelGGL(k_decode_open, dim3(dc.B, dc.Hkv), dim3(dc.dv), 0, st, dc, vto);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_step(const DecodeCache &dc, const void *q, bool in_f32, float sl2, int splits,
+                              const _Float16 *vto, float *part, float *mpart, hipStream_t st) {
   switch (dc.dk) {
-    case 16: return step_dk<16>(dc, q, in_f32, sl2, splits, part, mpart, st);
-    case 32: return step_dk<32>(dc, q, in_f32, sl2, splits, part, mpart, st);
-    case 64: return step_dk<64>(dc, q, in_f32, sl2, splits, part, mpart, st);
-    case 128: return step_dk<128>(dc, q, in_f32, sl2, splits, part, mpart, st);
+    case 16: return step_dk<16>(dc, q, in_f32, sl2, splits, vto, part, mpart, st);
+    case 32: return step_dk<32>(dc, q, in_f32, sl2, splits, vto, part, mpart, st);
+    case 64: return step_dk<64>(dc, q, in_f32, sl2, splits, vto, part, mpart, st);
+    case 128: return step_dk<128>(dc, q, in_f32, sl2, splits, vto, part, mpart, st);
   }
   return hipErrorInvalidValue;
 }

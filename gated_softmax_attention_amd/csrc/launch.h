@@ -100,8 +100,9 @@ struct DecodeCache {
 hipError_t launch_decode_reset(const DecodeCache &dc, hipStream_t st);
 hipError_t launch_decode_append(const DecodeCache &dc, const void *k, const void *v, const float *g, int n,
                                 const int *n_seq, bool in_f32, bool logits, hipStream_t st);
-hipError_t launch_decode_step(const DecodeCache &dc, const void *q, bool in_f32, float sl2, int splits, float *part,
-                              float *mpart, hipStream_t st);
+hipError_t launch_decode_open(const DecodeCache &dc, _Float16 *vto, hipStream_t st);
+hipError_t launch_decode_step(const DecodeCache &dc, const void *q, bool in_f32, float sl2, int splits,
+                              const _Float16 *vto, float *part, float *mpart, hipStream_t st);
 hipError_t launch_decode_combine(const DecodeCache &dc, int units, const float *part, const float *mpart,
                                  const void *w, const void *z, bool in_f32, bool out_f32, bool o_norm, float eps,
                                  void *o, float *m, hipStream_t st);

@@ -127,3 +127,64 @@ def test_descriptor_layout_matches_header(tmp_path):
     got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
     want = [ctypes.sizeof(F.fix_attn_desc)] + [getattr(F.fix_attn_desc, n).offset for n in fields]
     assert got == want
+
+
+def ddesc(**kw):
+    d = F.fix_decode_desc()
+    d.B, d.cap, d.Hq, d.Hkv, d.dk, d.dv = 2, 256, 4, 2, 64, 64
+    d.in_dtype, d.out_dtype, d.eps = F.FIX_BF16, F.FIX_F32, 1e-5
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({}, F.FIX_OK),
+    ({"cap": 100}, F.FIX_E_INVALID),           # not a multiple of 64
+    ({"cap": 0}, F.FIX_E_INVALID),
+    ({"Hq": 3}, F.FIX_E_INVALID),              # Hq % Hkv
+    ({"eps": -1.0}, F.FIX_E_INVALID),
+    ({"in_dtype": 7}, F.FIX_E_INVALID),
+    ({"dk": 48}, F.FIX_E_UNSUPPORTED),
+    ({"Hq": 66, "Hkv": 2}, F.FIX_E_UNSUPPORTED),  # group of 33 query heads
+    ({"Hq": 64, "Hkv": 2}, F.FIX_OK),              # group of 32
+    ({"cap": 1 << 30}, F.FIX_E_UNSUPPORTED),
+])
+def test_decode_validate(kw, status):
+    lib = F.library()
+    assert lib.fix_decode_validate(ctypes.byref(ddesc(**kw))) == status
+
+
+def test_decode_sizes_and_host_rejections():
+    lib = F.library()
+    d = ddesc()
+    cs, ws = lib.fix_decode_cache_size(ctypes.byref(d)), lib.fix_decode_workspace_size(ctypes.byref(d))
+    # the cache holds at least the fp16 keys and chunk-end values of every token
+    assert cs >= 2 * 256 * 2 * (64 + 64) * 2 and ws > 0
+    assert lib.fix_decode_cache_size(ctypes.byref(ddesc(cap=512))) > cs
+    assert lib.fix_decode_cache_size(ctypes.byref(ddesc(cap=100))) == 0
+    fake = 0x10000
+    # null or misaligned cache, bad counts, missing workspace: rejected before any launch
+    assert lib.fix_decode_reset(ctypes.byref(d), None, None) == F.FIX_E_INVALID
+    assert lib.fix_decode_reset(ctypes.byref(d), fake + 16, None) == F.FIX_E_INVALID
+    assert lib.fix_decode_append(ctypes.byref(d), fake, fake, fake, fake, 0, None, None) == F.FIX_E_INVALID
+    assert lib.fix_decode_append(ctypes.byref(d), fake, fake, fake, fake, 257, None, None) == F.FIX_E_INVALID
+    assert lib.fix_decode_step(ctypes.byref(d), fake, fake, None, None, fake, None, fake, 16, None) == F.FIX_E_WORKSPACE
+    assert lib.fix_decode_step(ctypes.byref(d), fake, None, None, None, fake, None, fake, ws, None) == F.FIX_E_INVALID
+
+
+def test_decode_descriptor_layout_matches_header(tmp_path):
+    """sizeof and field offsets of fix_decode_desc in the C header equal the ctypes binding's."""
+    import subprocess
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    fields = [f[0] for f in F.fix_decode_desc._fields_]
+    src = tmp_path / "dlayout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "fixattn.h"\nint main(void) {\n'
+                   '  printf("%zu\\n", sizeof(fix_decode_desc));\n'
+                   + "".join(f'  printf("%zu\\n", offsetof(fix_decode_desc, {n}));\n' for n in fields)
+                   + "  return 0;\n}\n")
+    exe = tmp_path / "dlayout"
+    subprocess.run(["gcc", "-I", os.path.join(root, "include"), str(src), "-o", str(exe)], check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    want = [ctypes.sizeof(F.fix_decode_desc)] + [getattr(F.fix_decode_desc, n).offset for n in fields]
+    assert got == want

@@ -31,11 +31,16 @@ PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16/fp16 MFMA peak (AMD specification
 # a plain-copy calibration (x2.0 reads, x1.0 writes); valid only for the sources they were
 # taken on (sha256 prefix over the files listed, the build flags included).  Reported as roofline.traffic, else null.
 TRAFFIC = {
-    "bwd_dkv": {"bytes": 2 * 1456097 * 1024 + 531942 * 1024, "sha": "ad2f8ceef7091e66",
+    "bwd_dkv": {"bytes": 2 * 1033264 * 1024 + 528967 * 1024, "sha": "42cb408e491c313f",
                 "files": ["gated_softmax_attention_amd/csrc/bwd_kernel.h",
                           "gated_softmax_attention_amd/csrc/common.h",
                           "gated_softmax_attention_amd/csrc/launch.h",
                           "gated_softmax_attention_amd/build.py"]},
+    "decode_step": {"bytes": int(2 * 135728.5625 * 1024) + 1040 * 1024, "sha": "012d1d595ccc3a70",
+                    "files": ["gated_softmax_attention_amd/csrc/decode.hip",
+                              "gated_softmax_attention_amd/csrc/common.h",
+                              "gated_softmax_attention_amd/csrc/launch.h",
+                              "gated_softmax_attention_amd/build.py"]},
 }
 
 
@@ -217,7 +222,7 @@ def decode_bench(args, x, F, torch):
                                f"sequence, o_norm, bf16 in/out, cache operands fp16",
                    "alg_bytes": alg, "kernel_ms": {k: round(v, 4) for k, v in avg.items()}},
         "roofline": {"bound": "hbm", "kernel": "decode_step", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": measured_traffic("decode_step"),
                      "avg_launch_ms": round(avg["decode_step"], 4)},
     }
     if not args.no_cpu_baseline:

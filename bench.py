@@ -247,6 +247,9 @@ def main():
                     help="pass the gate as raw logits (logsigmoid applied inside the kernels)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (HBM counter calibration)")
+    ap.add_argument("--scalar-gate", action="store_true",
+                    help="one gate value per token and kv head (channel 0 of the workload's gate): the "
+                         "logit-bias forward and the broadcast backward")
     ap.add_argument("--decode", action="store_true",
                     help="time decode steps (fix_decode_step) against a cache holding the workload's T tokens")
     args = ap.parse_args()
@@ -263,6 +266,10 @@ def main():
     from gated_softmax_attention_amd import synth
 
     x = synth.make_inputs(WORKLOAD)
+    if args.scalar_gate:
+        x = dict(x)
+        x["g"] = np.ascontiguousarray(x["g"][..., 0])
+        x["g_logits"] = np.ascontiguousarray(x["g_logits"][..., 0])
     if args.decode:
         decode_bench(args, x, F, torch)
         return
@@ -287,7 +294,8 @@ def main():
     xx = torch.empty(B, T, Hq, dv, device="cuda")
     dq, dkk, dvv = torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"])
     dg = torch.empty_like(d["g"])
-    desc = F.make_desc(d["q"], d["k"], d["v"], o_norm=True, gate_logits=args.gate_logits)
+    desc = F.make_desc(d["q"], d["k"], d["v"], o_norm=True, gate_logits=args.gate_logits,
+                       gate_scalar=args.scalar_gate)
     wf, wb = F.fix_attn_fwd_workspace_size(desc), F.fix_attn_bwd_workspace_size(desc)
     ws_f = torch.empty(wf, dtype=torch.uint8, device="cuda")
     ws_b = torch.empty(wb, dtype=torch.uint8, device="cuda")
@@ -357,6 +365,7 @@ def main():
     # Algorithmic flops of each kernel: its share of the 2 forward and 5 backward products.
     alg = {
         "fix_fwd": fwd_flops,
+        "fox_fwd": fwd_flops,
         "bwd_dq": 2 * (2 * dk + dv) * pc["inter"] * heads,        # S, dP, dQ on pairs in different chunks
         "bwd_dkv": 2 * (dk + dv) * pc["far"] * heads,             # dV, dK on pairs two or more chunks apart
         "bwd_intra_dq": 2 * (2 * dk + dv) * pc["same"] * heads,
@@ -375,7 +384,8 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{WORKLOAD}: B={B} T={T} Hq={Hq} Hkv={Hkv} dk={dk} dv={dv} bf16 in/out, "
                                f"g=logsigmoid(N({wl.gate_mu},{wl.gate_sd}))"
-                               f"{' passed as logits (logsigmoid in the kernels)' if args.gate_logits else ''}, "
+                               f"{' passed as logits (logsigmoid in the kernels)' if args.gate_logits else ''}"
+                               f"{', scalar per token and head (channel 0)' if args.scalar_gate else ''}, "
                                f"o_norm, fwd+bwd",
                    "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
                    "fwd_flops": fwd_flops, "bwd_flops": bwd_flops,

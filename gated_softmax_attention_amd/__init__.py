@@ -34,6 +34,7 @@ class fix_attn_desc(ctypes.Structure):
         ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
         ("scale", ctypes.c_float), ("eps", ctypes.c_float),
         ("o_norm", ctypes.c_int32), ("gate_logits", ctypes.c_int32),
+        ("gate_scalar", ctypes.c_int32),
     ]
 
 
@@ -156,7 +157,7 @@ def fix_attn_bwd(desc, q, k, v, g, o_norm_weight, o_gate, m, rstd, x, d_o, dq, d
 
 
 def make_desc(q, k, v, cu_seqlens=None, *, o_norm=False, scale=None, eps=1e-5, out_dtype=None,
-              gate_logits=False) -> fix_attn_desc:
+              gate_logits=False, gate_scalar=False) -> fix_attn_desc:
     """Descriptor for torch tensors q [B,T,Hq,dk], k [B,T,Hkv,dk], v [B,T,Hkv,dv]."""
     import torch
     B, T, Hq, dk = q.shape
@@ -176,6 +177,7 @@ def make_desc(q, k, v, cu_seqlens=None, *, o_norm=False, scale=None, eps=1e-5, o
     d.eps = float(eps)
     d.o_norm = 1 if o_norm else 0
     d.gate_logits = 1 if gate_logits else 0
+    d.gate_scalar = 1 if gate_scalar else 0
     return d
 
 
@@ -186,15 +188,18 @@ def _stream():
 
 def _check_inputs(q, k, v, g, cu_seqlens, o_norm_weight, o_gate):
     import torch
-    for name, t in (("q", q), ("k", k), ("v", v), ("g", g)):
+    for name, t in (("q", q), ("k", k), ("v", v)):
         if not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
             raise ValueError(f"{name} must be a contiguous 4-D CUDA tensor")
+    if not g.is_cuda or not g.is_contiguous() or g.dim() not in (3, 4):
+        raise ValueError("g must be a contiguous CUDA tensor, [B,T,Hkv,dv] or [B,T,Hkv] (scalar gate)")
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k and v must share one dtype")
     if g.dtype != torch.float32:
         raise ValueError("the forget gate g must be float32")
     B, T, Hq, dk = q.shape
-    if k.shape[:2] != (B, T) or v.shape[:3] != k.shape[:3] or g.shape != v.shape or k.shape[3] != dk:
+    if (k.shape[:2] != (B, T) or v.shape[:3] != k.shape[:3] or k.shape[3] != dk
+            or tuple(g.shape) not in (tuple(v.shape), tuple(v.shape[:3]))):
         raise ValueError("shape mismatch among q, k, v, g")
     if cu_seqlens is not None and (cu_seqlens.dtype != torch.int64 or not cu_seqlens.is_cuda or B != 1):
         raise ValueError("cu_seqlens must be an int64 CUDA tensor and requires B == 1")
@@ -211,7 +216,7 @@ def forward(q, k, v, g, cu_seqlens=None, *, o_norm=False, o_norm_weight=None, o_
     import torch
     _check_inputs(q, k, v, g, cu_seqlens, o_norm_weight, o_gate)
     desc = make_desc(q, k, v, cu_seqlens, o_norm=o_norm, scale=scale, eps=eps, out_dtype=out_dtype,
-                     gate_logits=gate_logits)
+                     gate_logits=gate_logits, gate_scalar=g.dim() == 3)
     B, T, Hq, _ = q.shape
     dv = v.shape[3]
     od = q.dtype if out_dtype is None else out_dtype
@@ -234,7 +239,7 @@ def backward(q, k, v, g, m, rstd, x, d_o, cu_seqlens=None, *, o_norm=False, o_no
     import torch
     _check_inputs(q, k, v, g, cu_seqlens, o_norm_weight, o_gate)
     desc = make_desc(q, k, v, cu_seqlens, o_norm=o_norm, scale=scale, eps=eps, out_dtype=out_dtype,
-                     gate_logits=gate_logits)
+                     gate_logits=gate_logits, gate_scalar=g.dim() == 3)
     od = q.dtype if out_dtype is None else out_dtype
     d_o = d_o.contiguous().to(q.dtype)
     dq = torch.empty(q.shape, dtype=od, device=q.device)

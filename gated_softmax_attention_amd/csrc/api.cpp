@@ -67,8 +67,12 @@ struct Carve {
 
 struct FwdWs {
   fix::Plan plan;
-  float *Gl2, *Gam;
-  _Float16 *VtT;
+  float *Gl2 = nullptr, *Gam = nullptr;
+  _Float16 *VtT = nullptr;
+  // scalar gate: v as fp16, the gate's block-local prefix and block references
+  _Float16 *V16 = nullptr;
+  float *loc = nullptr;
+  double *ref = nullptr;
 };
 
 void carve_plan(Carve &cv, const fix_attn_desc *d, const Shape &s, fix::Plan &p) {
@@ -83,6 +87,12 @@ void carve_plan(Carve &cv, const fix_attn_desc *d, const Shape &s, fix::Plan &p)
 size_t carve_fwd(Carve &cv, const fix_attn_desc *d, FwdWs &w) {
   Shape s = shape_of(d);
   carve_plan(cv, d, s, w.plan);
+  if (d->gate_scalar) {
+    w.V16 = cv.take<_Float16>(s.Ttot * d->Hkv * d->dv);
+    w.loc = cv.take<float>(s.Ttot * d->Hkv);
+    w.ref = cv.take<double>(s.nch_ub * d->Hkv);
+    return cv.off;
+  }
   w.Gl2 = cv.take<float>(s.Ttot * d->Hkv * d->dv);
   w.Gam = cv.take<float>(s.nch_ub * d->Hkv * d->dv);
   w.VtT = cv.take<_Float16>(s.nch_ub * d->Hkv * d->dv * fix::CH);
@@ -99,6 +109,7 @@ struct BwdWs {
   _Float16 *dh, *X16;
   __bf16 *XH, *XL, *XTH, *XTL;
   float *mb, *sig, *qside, *dG, *dq_i, *dk_i, *dv_i, *dw_part, *dg_tot, *dg_carry;
+  float *gb = nullptr, *dgb = nullptr;  // scalar gate: per-channel copy of g and the per-channel dg
 };
 
 size_t carve_bwd(Carve &cv, const fix_attn_desc *d, BwdWs &w) {
@@ -132,6 +143,10 @@ size_t carve_bwd(Carve &cv, const fix_attn_desc *d, BwdWs &w) {
   w.dw_part = cv.take<float>(ncb * Hkv * DV);
   w.dg_tot = cv.take<float>(ncb * Hkv * DV);
   w.dg_carry = cv.take<float>(ncb * Hkv * DV);
+  if (d->gate_scalar) {
+    w.gb = cv.take<float>(T * Hkv * DV);
+    w.dgb = cv.take<float>(T * Hkv * DV);
+  }
   return cv.off;
 }
 
@@ -189,6 +204,7 @@ fix_status fix_attn_validate(const fix_attn_desc *d) {
   if (std::isnan(d->scale) || std::isnan(d->eps) || std::isinf(d->scale) || std::isinf(d->eps) || d->eps < 0)
     return FIX_E_INVALID;
   if (d->cu_seqlens && (d->B != 1 || d->num_seqs < 1)) return FIX_E_INVALID;
+  if (d->gate_scalar != 0 && d->gate_scalar != 1) return FIX_E_INVALID;
   if (!head_dim_ok(d->dk) || !head_dim_ok(d->dv)) return FIX_E_UNSUPPORTED;
   const int64_t Ttot = d->B * d->T;
   if (d->T >= (int64_t(1) << 31) || Ttot >= (int64_t(1) << 31)) return FIX_E_UNSUPPORTED;
@@ -229,6 +245,27 @@ fix_status fix_attn_fwd(const fix_attn_desc *d, const void *q, const void *k, co
   e = fix::launch_plan(d->cu_seqlens, (int)s.nseq, (int)d->T, s.Ttot, w.plan, st);
   if (e == hipSuccess) e = trace_mark(st, "plan");
   if (e != hipSuccess) return hip_fail(e);
+  if (d->gate_scalar) {  // decay as a logit bias: no value scaling
+    const float scale = d->scale > 0.f ? d->scale : 1.f / std::sqrt((float)d->dk);
+    e = fix::launch_fox_prefix(g, d->gate_logits != 0, w.plan, (int)s.nseq, (int)d->Hkv, w.loc, w.ref, st);
+    if (e == hipSuccess) e = trace_mark(st, "fox_prefix");
+    if (e == hipSuccess) e = fix::launch_to_f16(v, f32in, s.Ttot * d->Hkv * d->dv, w.V16, st);
+    if (e == hipSuccess) e = trace_mark(st, "v_f16");
+    if (e != hipSuccess) return hip_fail(e);
+    fix::FoxArgs fa;
+    fa.q = q; fa.k = k; fa.V16 = w.V16; fa.loc = w.loc; fa.ref = w.ref;
+    fa.w = o_norm_weight; fa.z = o_gate;
+    fa.o = o; fa.m = m; fa.rstd = rstd; fa.x = x;
+    fa.plan = w.plan;
+    fa.Hq = (int)d->Hq; fa.Hkv = (int)d->Hkv;
+    fa.sl2 = scale * fix::LOG2E;
+    fa.eps = d->eps;
+    fa.o_norm = d->o_norm ? 1 : 0;
+    fa.out_f32 = d->out_dtype == FIX_F32;
+    e = fix::launch_fox_fwd((int)d->dk, (int)d->dv, f32in, fa, (int)round8(s.nqb_ub * d->Hq), st);
+    if (e == hipSuccess) e = trace_mark(st, "fox_fwd");
+    return e == hipSuccess ? FIX_OK : hip_fail(e);
+  }
   e = fix::launch_gate_prep((int)d->dv, g, d->gate_logits != 0, v, f32in, w.plan, (int)d->Hkv, (int)s.nch_ub, w.Gl2,
                             w.Gam, w.VtT, st);
   if (e == hipSuccess) e = trace_mark(st, "gate_prep");
@@ -288,7 +325,16 @@ fix_status fix_attn_bwd(const fix_attn_desc *d, const void *q, const void *k, co
   e = trace_begin(st);
   if (e != hipSuccess) return hip_fail(e);
   FIX_TRY(fix::launch_plan(d->cu_seqlens, (int)s.nseq, (int)d->T, s.Ttot, w.plan, st), "plan");
-  FIX_TRY(fix::launch_gate_prep_rows(DV, g, d->gate_logits != 0, v, f32in, w.plan, Hkv, ncb, w.Gl2, w.Gam, w.Vr,
+  // A scalar gate goes through the per-channel path as a broadcast copy; its
+  // gradient is the per-channel one summed over the channels.
+  const float *gch = g;
+  float *dgch = dg;
+  if (d->gate_scalar) {
+    FIX_TRY(fix::launch_gate_broadcast(g, s.Ttot * Hkv, DV, w.gb, st), "gate_broadcast");
+    gch = w.gb;
+    dgch = w.dgb;
+  }
+  FIX_TRY(fix::launch_gate_prep_rows(DV, gch, d->gate_logits != 0, v, f32in, w.plan, Hkv, ncb, w.Gl2, w.Gam, w.Vr,
                                      w.VE, w.VBH, w.VBL, st),
           "gate_prep_rows");
   FIX_TRY(fix::launch_chunk_logprefix(DV, w.Gl2, w.plan, Hkv, w.Lam, st), "chunk_logprefix");
@@ -325,8 +371,10 @@ fix_status fix_attn_bwd(const fix_attn_desc *d, const void *q, const void *k, co
   FIX_TRY(fix::launch_bwd(fix::BK_INTRA_DKV, DK, DV, f32in, a, dim3(ncb, Hkv), st), "bwd_intra_dkv");
   FIX_TRY(fix::launch_bwd(fix::BK_DQ, DK, DV, f32in, a, dim3(round8(ncb * Hq)), st), "bwd_dq");
   FIX_TRY(fix::launch_bwd(fix::BK_DKV, DK, DV, f32in, a, dim3(round8(ncb * Hkv)), st), "bwd_dkv");
-  FIX_TRY(fix::launch_dg_scan(DV, w.dG, d->gate_logits ? g : nullptr, w.plan, Hkv, ncb, w.dg_tot, w.dg_carry, dg, st),
+  FIX_TRY(fix::launch_dg_scan(DV, w.dG, d->gate_logits ? gch : nullptr, w.plan, Hkv, ncb, w.dg_tot, w.dg_carry, dgch,
+                              st),
           "dg_scan");
+  if (d->gate_scalar) FIX_TRY(fix::launch_gate_reduce(dgch, s.Ttot * Hkv, DV, dg, st), "gate_reduce");
   if (want_dw) {
     FIX_TRY(fix::launch_dw_reduce(w.dw_part, w.plan.counts, Hkv, DV, d_o_norm_weight, st), "dw_reduce");
   }

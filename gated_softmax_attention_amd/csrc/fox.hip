@@ -1,0 +1,318 @@
+// Scalar-gate fast path: the FiX operation when the forget gate is one value
+// per token and kv head (the forgetting-attention case, "Forgetting
+// Transformer" page, abstract: a forget gate that down-weights the
+// unnormalised attention scores).  With g_t a scalar, the decay
+// exp(G_i - G_j) is the same for every channel and enters as a bias on the
+// logits:
+//   x_i = sum_{j<=i} exp(s_ij - m_i + G_i - G_j) v_j,   m_i = max_{j<=i} s_ij
+// so no value vector is scaled: the kernel is a causal attention pass with
+// an additive bias, an exact online row max and no softmax denominator,
+// followed by the same output transform as the per-channel path.
+//
+// The gate prefix is kept as an fp64 value at the start of every 64-token
+// block of a sequence plus an fp32 prefix local to the block, so that
+// G_i - G_j is exact to fp32 rounding of block-sized terms however long the
+// sequence is.
+#include "common.h"
+#include "launch.h"
+
+namespace fix {
+
+// Gate prefix per (sequence, kv head): for 64-token block n of the sequence
+// (global index chunk_base[s] + n), ref[n] = log2-prefix of g before the
+// block (fp64) and loc[t] = log2-prefix of g from the block start to t,
+// inclusive (fp32).  Block = 256 threads, a thread per 64-token block; the
+// block totals are scanned through LDS, 256 blocks at a time.
+template <bool LOGITS>
+__global__ void __launch_bounds__(256) k_fox_prefix(const float *__restrict__ g, Plan plan, int Hkv,
+                                                    float *__restrict__ loc, double *__restrict__ ref) {
+  const int s = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
+  if (s >= plan.nseq) return;
+  const int64_t st = plan.seq_start[s];
+  const int L = plan.seq_len[s], cb = plan.chunk_base[s];
+  __shared__ double tot[256];
+  double carry = 0.0;
+  for (int b0 = 0; b0 * CH < L; b0 += 256) {
+    const int blk = b0 + tid, t0 = blk * CH;
+    double sum = 0.0;
+    float acc = 0.f;
+    if (t0 < L) {
+      const int n = min(CH, L - t0);
+      for (int j = 0; j < n; ++j) {
+        float gv = g[(st + t0 + j) * Hkv + c];
+        if (LOGITS) gv = log_sigmoid(gv);
+        acc += gv * LOG2E;
+        loc[(st + t0 + j) * Hkv + c] = acc;
+      }
+      sum = (double)acc;
+    }
+    tot[tid] = sum;
+    __syncthreads();
+    // exclusive prefix of the block totals (simple: thread tid sums those before it)
+    double before = carry;
+    for (int u = 0; u < tid; ++u) before += tot[u];
+    if (t0 < L) ref[(int64_t)(cb + blk) * Hkv + c] = before;
+    double all = 0.0;
+    for (int u = 0; u < 256; ++u) all += tot[u];
+    carry += all;
+    __syncthreads();
+  }
+}
+
+// Forward.  Workgroup = 128 query rows (4 waves x 32) of one q head, keys
+// visited in 64-token blocks from the first, K and V tiles staged in LDS
+// (double buffered, shared by the waves; V as fp16 rows).  A wave computes
+// S^T = K Q^T (lane = query row, registers = keys), so the exact online row
+// max is a reduction within a lane; P = exp2(s sl2 - m + bias) (<= 1 for a
+// forget gate) is the A operand of P V, whose B operand is read from the V
+// rows with the transposing LDS load.
+template <int DK, int DV, bool F32IN>
+__global__ void __launch_bounds__(256, 2) k_fox_fwd(FoxArgs a) {
+  using IF = InFrag<F32IN>;
+  using kfrag = typename IF::type;
+  constexpr int DVP = DV < 32 ? 32 : DV;
+  constexpr int NB = DVP / 32, NS = DK / 16;
+  using KT = LdsTile<CH, DK * 2>;  // K rows of a key block (bf16, or fp16 for fp32 inputs)
+  using VT = LdsTile<CH, DV * 2>;  // V rows of a key block (fp16)
+  constexpr int O_K = 0, O_V = O_K + 2 * KT::BYTES, O_G = O_V + 2 * VT::BYTES, O_R = O_G + 2 * 256;
+  __shared__ __align__(1024) char smem[O_R + 2 * 256];
+  auto Ks = [&](int b) { return smem + O_K + b * KT::BYTES; };
+  auto Vs = [&](int b) { return smem + O_V + b * VT::BYTES; };
+  auto Gk = [&](int b) { return (float *)(smem + O_G + b * 256); };  // the block's local prefixes
+  auto Rf = [&](int b) { return (double *)(smem + O_R + b * 256); };  // [0]: the block's reference
+
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, n = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const Plan &pl = a.plan;
+  const int Hq = a.Hq, Hkv = a.Hkv, G = Hq / Hkv;
+  const int nblk = pl.counts[0];
+  const int idx = xcd_item(nblk * Hq);
+  if (idx < 0) return;
+  const int c = uniform(idx / (nblk * G)), rem = uniform(idx % (nblk * G));
+  const int bi = rem / G, gq = rem % G;
+  const int s = seq_of_chunk(pl.cb128, pl.nseq, bi);
+  const int64_t st = uniform((int64_t)pl.seq_start[s]);
+  const int L = uniform(pl.seq_len[s]);
+  const int cb = uniform(pl.chunk_base[s]);
+  const int qb = (L + QB - 1) / QB - 1 - (bi - uniform(pl.cb128[s]));  // longest first within the sequence
+  const int hq = c * G + gq;
+  const int q0 = qb * QB;
+  const int nrows = min(QB, L - q0);
+  const int rbase = q0 + 32 * wave;       // the wave's first row
+  const int row = rbase + n;              // the lane's query row
+  const bool active = 32 * wave < nrows;
+  const int nJ = (q0 + nrows + CH - 1) / CH;  // key blocks the workgroup needs
+  const float sl2 = a.sl2;
+
+  kfrag qf[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i)
+    qf[i] = (active && row < L) ? IF::load(a.q, ((st + row) * Hq + hq) * DK + 16 * i + 8 * hh) : IF::zero();
+  // the row's gate prefix (fp64): block reference + block-local part
+  const int rr = min(row, L - 1);
+  const double grow = a.ref[(int64_t)(cb + rr / CH) * Hkv + c] + (double)a.loc[(st + rr) * Hkv + c];
+
+  uint32_t ok[KT::NW], ov[VT::NW];
+  KT::lane_offsets(Hkv * DK * 2, wave, lane, ok);
+  VT::lane_offsets(Hkv * DV * 2, wave, lane, ov);
+  // Copies of key block J (untracked: the loop reads the other buffer while
+  // they are in flight, ordered by the explicit waits below).
+  auto stage = [&](int J, int b) {
+    const int64_t kr = (st + J * CH) * Hkv + c;
+    const int64_t nrow = (int64_t)(L - J * CH) * Hkv;  // rows past the sequence read as zeros
+    if constexpr (!F32IN) {
+      const u32x4 sk = rsrc_words((const uint16_t *)a.k + kr * DK, nrow * DK * 2);
+#pragma unroll
+      for (int t = 0; t < KT::NW; ++t) KT::dma_piece_untracked(Ks(b), sk, ok, t, wave);
+    } else {
+      for (int p = tid; p < KT::NCH; p += 256) {
+        const int r = p / KT::CPR, cc = p % KT::CPR;
+        *(f16x8 *)(Ks(b) + KT::off(r, cc)) = IF::load(a.k, ((st + min(J * CH + r, L - 1)) * Hkv + c) * DK + 8 * cc);
+      }
+    }
+    const u32x4 sv = rsrc_words(a.V16 + kr * DV, nrow * DV * 2);
+#pragma unroll
+    for (int t = 0; t < VT::NW; ++t) VT::dma_piece_untracked(Vs(b), sv, ov, t, wave);
+    // the block's local gate prefixes (lane l: token l) and its fp64 reference
+    // (lanes 0 and 1), in every wave (the same bytes)
+    dma4_untracked(Gk(b), rsrc_words(a.loc + kr, nrow * 4), (uint32_t)lane * Hkv * 4);
+    dma4_untracked(Rf(b), rsrc_words(a.ref + (int64_t)(cb + J) * Hkv + c, 8), (uint32_t)lane * 4);
+  };
+
+  f32x16 acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b] = zero16();
+  float m = -INFINITY;  // exact running row max of the lane's row (log2 units)
+
+  if (nJ > 0) stage(0, 0);
+  for (int J = 0; J < nJ; ++J) {
+    const int b = J & 1;
+    wait_all();
+    __syncthreads();  // block J landed in every wave's copy; block J - 1's readers are done
+    if (J + 1 < nJ) stage(J + 1, b ^ 1);
+    const int k0 = J * CH;
+    if (!active || k0 > rbase + 31) continue;  // keys all after the wave's rows
+    // S^T per 32-key half: lane = row n, register j = key k0 + 32 h + acc_row(hh, j)
+    f32x16 sc[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      sc[h] = zero16();
+#pragma unroll
+      for (int i = 0; i < NS; ++i)
+        sc[h] = mma32(*(const kfrag *)(Ks(b) + KT::off(32 * h + n, 2 * i + hh)), qf[i], sc[h]);
+    }
+    // bias G_row - G_key = (G_row - ref_J) - loc_key
+    const float gq = (float)(grow - Rf(b)[0]);
+    float mb = -INFINITY;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int key = k0 + 32 * h + acc_row(hh, j);
+        sc[h][j] = (key <= row && key < L) ? sc[h][j] * sl2 : -INFINITY;
+        mb = fmaxf(mb, sc[h][j]);
+      }
+    mb = fmaxf(mb, __shfl_xor(mb, 32));
+    const float mn = fmaxf(m, mb);
+    if (__any(mn > m)) {
+      const float r = m == -INFINITY ? 0.f : fast_exp2(m - mn);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float rj = __shfl(r, acc_row(hh, j));
+#pragma unroll
+        for (int bv = 0; bv < NB; ++bv) acc[bv][j] *= rj;
+      }
+    }
+    m = mn;
+    f16x8 pf[2][2];
+    const float *gk = Gk(b);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        pf[h][j >> 3][j & 7] = (_Float16)fast_exp2(sc[h][j] - m + gq - gk[32 * h + acc_row(hh, j)]);
+#pragma unroll
+    for (int bv = 0; bv < NB; ++bv)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          acc[bv] = mma32(pf[h][u], tr_frag<VT>(Vs(b), 32 * h + 16 * u, 32 * bv, lane), acc[bv]);
+  }
+
+  // epilogue: RMSNorm over the row, weight, output gate; x, m, rstd (for dv
+  // < 32 the columns past dv hold values read past the narrow V rows: left out)
+  float ss[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    float t = 0.f;
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb)
+      if (32 * bb + n < DV) t += acc[bb][j] * acc[bb][j];
+    ss[j] = t;
+  }
+#pragma unroll
+  for (int off = 1; off < 32; off <<= 1)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) ss[j] += __shfl_xor(ss[j], off);
+  if (!active) return;
+  float wv[NB];
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb) {
+    const int d = 32 * bb + n;
+    wv[bb] = (a.o_norm && a.w && d < DV) ? load_in(a.w, d, F32IN) : 1.f;
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int r = rbase + acc_row(hh, j);
+    if (r >= L) continue;
+    const float rs = 1.f / sqrtf(ss[j] * (1.f / DV) + a.eps);
+    const int64_t rb = ((st + r) * Hq + hq) * DV;
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+      const int d = 32 * bb + n;
+      if (d >= DV) continue;
+      const float xv = acc[bb][j];
+      if (a.x) a.x[rb + d] = xv;
+      float ov = a.o_norm ? xv * rs * wv[bb] : xv;
+      if (a.z) ov *= load_in(a.z, rb + d, F32IN);
+      store_out(a.o, rb + d, ov, a.out_f32);
+    }
+    if (n == j) a.rstd[(st + r) * Hq + hq] = rs;
+  }
+  if (hh == 0 && row < L) a.m[(st + row) * Hq + hq] = m * LN2;
+}
+
+hipError_t launch_fox_prefix(const float *g, bool logits, const Plan &plan, int nseq, int Hkv, float *loc,
+                             double *ref, hipStream_t st) {
+  if (logits) hipLaunchKernelGGL(k_fox_prefix<true>, dim3(nseq, Hkv), dim3(256), 0, st, g, plan, Hkv, loc, ref);
+  else hipLaunchKernelGGL(k_fox_prefix<false>, dim3(nseq, Hkv), dim3(256), 0, st, g, plan, Hkv, loc, ref);
+  return hipGetLastError();
+}
+
+template <int DK, int DV>
+static hipError_t fox_dv(bool f32in, const FoxArgs &a, int grid, hipStream_t st) {
+  if (f32in) hipLaunchKernelGGL((k_fox_fwd<DK, DV, true>), dim3(grid), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((k_fox_fwd<DK, DV, false>), dim3(grid), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+template <int DK>
+static hipError_t fox_dk(int dv, bool f32in, const FoxArgs &a, int grid, hipStream_t st) {
+  switch (dv) {
+    case 16: return fox_dv<DK, 16>(f32in, a, grid, st);
+    case 32: return fox_dv<DK, 32>(f32in, a, grid, st);
+    case 64: return fox_dv<DK, 64>(f32in, a, grid, st);
+    case 128: return fox_dv<DK, 128>(f32in, a, grid, st);
+  }
+  return hipErrorInvalidValue;
+}
+hipError_t launch_fox_fwd(int dk, int dv, bool f32in, const FoxArgs &a, int grid, hipStream_t st) {
+  switch (dk) {
+    case 16: return fox_dk<16>(dv, f32in, a, grid, st);
+    case 32: return fox_dk<32>(dv, f32in, a, grid, st);
+    case 64: return fox_dk<64>(dv, f32in, a, grid, st);
+    case 128: return fox_dk<128>(dv, f32in, a, grid, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+// Per-channel copy of a scalar gate ([T, Hkv] -> [T, Hkv, dv]) for the
+// backward, and the sum over channels of a per-channel gate gradient.  Both
+// move one float4 per lane (dv is a multiple of 4); in the sum, the dv/4
+// lanes of one row (an aligned group inside the wave) add their partial sums
+// with cross-lane shuffles, so each wave reads contiguous memory.
+__global__ void k_gate_broadcast(const float *__restrict__ g, int64_t n, int q, float4 *__restrict__ gb) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e < n * q) {
+    const float v = g[e / q];
+    gb[e] = make_float4(v, v, v, v);
+  }
+}
+__global__ void __launch_bounds__(256) k_gate_reduce(const float4 *__restrict__ dgb, int64_t n, int q,
+                                                     float *__restrict__ dg) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const bool in = e < n * q;
+  float s = 0.f;
+  if (in) {
+    const float4 v = dgb[e];
+    s = (v.x + v.y) + (v.z + v.w);
+  }
+  for (int off = 1; off < q; off <<= 1) s += __shfl_xor(s, off);
+  if (in && e % q == 0) dg[e / q] = s;
+}
+hipError_t launch_gate_broadcast(const float *g, int64_t n, int dv, float *gb, hipStream_t st) {
+  if (dv % 4 || 64 % (dv / 4)) return hipErrorInvalidValue;
+  const int64_t tot = n * (dv / 4);
+  hipLaunchKernelGGL(k_gate_broadcast, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, g, n, dv / 4,
+                     (float4 *)gb);
+  return hipGetLastError();
+}
+hipError_t launch_gate_reduce(const float *dgb, int64_t n, int dv, float *dg, hipStream_t st) {
+  if (dv % 4 || 64 % (dv / 4)) return hipErrorInvalidValue;
+  const int64_t tot = n * (dv / 4);
+  hipLaunchKernelGGL(k_gate_reduce, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, (const float4 *)dgb,
+                     n, dv / 4, dg);
+  return hipGetLastError();
+}
+
+}  // namespace fix

@@ -21,6 +21,26 @@ struct FwdArgs {
   int out_f32;
 };
 
+// Scalar-gate (forgetting-attention) forward, fox.hip.
+struct FoxArgs {
+  const void *q, *k;
+  const _Float16 *V16;  // [T, Hkv, DV] v as fp16
+  const float *loc;     // [T, Hkv] log2 gate prefix local to the token's 64-token block
+  const double *ref;    // [64-block][Hkv] log2 gate prefix before each block
+  const void *w, *z;
+  void *o;
+  float *m, *rstd, *x;
+  Plan plan;
+  int Hq, Hkv;
+  float sl2, eps;
+  int o_norm, out_f32;
+};
+hipError_t launch_fox_prefix(const float *g, bool logits, const Plan &plan, int nseq, int Hkv, float *loc,
+                             double *ref, hipStream_t st);
+hipError_t launch_fox_fwd(int dk, int dv, bool f32in, const FoxArgs &a, int grid, hipStream_t st);
+hipError_t launch_gate_broadcast(const float *g, int64_t n, int dv, float *gb, hipStream_t st);
+hipError_t launch_gate_reduce(const float *dgb, int64_t n, int dv, float *dg, hipStream_t st);
+
 struct BwdArgs {
   const void *q, *k, *v;
   const float *Gl2, *Gam;      // 128-chunk local prefix sums of g (log2 units), chunk decays

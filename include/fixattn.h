@@ -43,6 +43,14 @@
  *    gradient with respect to x (dg/dx = sigmoid(-x)).  The pages fix g as a
  *    log-space gate shaped like v (FiX README, "Quick Start"); logsigmoid of
  *    unconstrained logits is the usual way to produce one.
+ *  - Scalar gate: with gate_scalar = 1, g (and dg) hold one value per token
+ *    and kv head, [B,T,Hkv] fp32, the decay being the same for every channel
+ *    (the forgetting-attention case, "Forgetting Transformer" page,
+ *    abstract).  The forward then applies it as a bias on the logits,
+ *    exp(s_ij - m_i + G_i - G_j), with no value scaling (its own kernel);
+ *    the backward runs the per-channel path on a broadcast copy of g and
+ *    sums dg over the channels.  Results equal those of the per-channel
+ *    call with g broadcast over dv.
  *  - Preconditions not checked (they would need a device scan): g <= 0
  *    (a forget gate; results for positive g are only as accurate as fp32
  *    range allows), cu_seqlens non-decreasing with cu[0] = 0 and
@@ -83,11 +91,13 @@ typedef struct {
   float eps;           /* RMSNorm epsilon (used when o_norm != 0) */
   int32_t o_norm;      /* nonzero: apply RMSNorm and o_norm_weight to the output */
   int32_t gate_logits; /* nonzero: g holds logits x, the gate is logsigmoid(x), dg is d/dx */
+  int32_t gate_scalar; /* 1: one gate value per token and kv head, g and dg [B,T,Hkv] (see below); 0: [B,T,Hkv,dv] */
 } fix_attn_desc;
 
 /* Checks a descriptor on the host; makes no HIP call (usable without a GPU).
  * FIX_E_INVALID: B, T, Hq, Hkv, dk or dv < 1; Hq % Hkv != 0; cu_seqlens with
- *   B != 1 or num_seqs < 1; unknown dtype; negative eps; NaN scale or eps.
+ *   B != 1 or num_seqs < 1; unknown dtype; negative eps; NaN scale or eps;
+ *   gate_scalar not 0 or 1.
  * FIX_E_UNSUPPORTED: dk or dv not in {16, 32, 64, 128}; B*T*max(Hq, Hkv) *
  *   max(dk, dv) >= 2^40 or B*T >= 2^31 (index ranges of the kernels). */
 fix_status fix_attn_validate(const fix_attn_desc *d);
@@ -100,7 +110,7 @@ size_t fix_attn_bwd_workspace_size(const fix_attn_desc *d);
 
 /* Forward pass.
  *   q [B,T,Hq,dk], k [B,T,Hkv,dk], v [B,T,Hkv,dv]       in_dtype
- *   g [B,T,Hkv,dv]                                      fp32, log-space forget gate (or its logits)
+ *   g [B,T,Hkv,dv] ([B,T,Hkv] with gate_scalar)          fp32, log-space forget gate (or its logits)
  *   o_norm_weight [dv] in_dtype or NULL (ones); read only when o_norm
  *   o_gate [B,T,Hq,dv] in_dtype or NULL (no output gate)
  * Outputs (all required except x):
@@ -122,7 +132,8 @@ fix_status fix_attn_fwd(const fix_attn_desc *d, const void *q, const void *k, co
  *   d_o [B,T,Hq,dv] in_dtype: gradient of the loss with respect to o
  * Outputs:
  *   dq [B,T,Hq,dk], dk [B,T,Hkv,dk], dv [B,T,Hkv,dv]   out_dtype (required)
- *   dg [B,T,Hkv,dv] fp32 (required): gradient with respect to g (to the logits with gate_logits)
+ *   dg [B,T,Hkv,dv] fp32 (required; [B,T,Hkv] with gate_scalar): gradient with respect to g
+ *      (to the logits with gate_logits)
  *   d_o_norm_weight [dv] fp32, or NULL to skip (written only when o_norm)
  *   d_o_gate [B,T,Hq,dv] out_dtype, or NULL to skip (needs o_gate) */
 fix_status fix_attn_bwd(const fix_attn_desc *d, const void *q, const void *k, const void *v,

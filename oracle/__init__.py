@@ -71,6 +71,15 @@ def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
+def _gate_per_channel(g, dv):
+    """A scalar gate [B,T,Hkv] as the per-channel gate it stands for ([B,T,Hkv,dv], every
+    channel the same value); a per-channel gate unchanged.  Marshalling only."""
+    g = np.asarray(g)
+    if g.ndim == 3:
+        return np.ascontiguousarray(np.broadcast_to(g[..., None], g.shape + (dv,))), True
+    return g, False
+
+
 def _layout(q, k, v, g, cu_seqlens):
     B, T, Hq, dk = q.shape
     Hkv, dv = k.shape[2], v.shape[3]
@@ -92,6 +101,7 @@ def oracle_fwd(q, k, v, g, cu_seqlens=None, *, scale=None, eps=1e-5, o_norm=True
     Returns dict o, x [B,T,Hq,dv], m, rstd [B,T,Hq] (float64; NaN where not computed).
     """
     lib = lib or load()
+    g, _ = _gate_per_channel(g, np.asarray(v).shape[3])
     q, k, v, g, w, z = map(_f64, (q, k, v, g, w, z))
     B, T, Hq, Hkv, dk, dv, cu = _layout(q, k, v, g, cu_seqlens)
     scale = dk ** -0.5 if scale is None else float(scale)
@@ -120,8 +130,11 @@ def oracle_bwd(q, k, v, g, dO, cu_seqlens=None, *, scale=None, eps=1e-5, o_norm=
     window > 0: the last `window` rows and keys of every selected unit; window < 0: dq of the
     first -window rows and dk, dv of the first -window keys (dg not computed).
     Returns dict dq, dk, dv, dg, dw ([dv]; zeros without o_norm), dz (NaN where not computed).
+    A scalar gate g [B,T,Hkv] stands for the same value in every channel; its dg is the
+    gradient of the loss through every copy, the sum over the channels of the per-channel dg.
     """
     lib = lib or load()
+    g, scalar = _gate_per_channel(g, np.asarray(v).shape[3])
     q, k, v, g, w, z, dO = map(_f64, (q, k, v, g, w, z, dO))
     B, T, Hq, Hkv, dk, dv, cu = _layout(q, k, v, g, cu_seqlens)
     scale = dk ** -0.5 if scale is None else float(scale)
@@ -140,4 +153,6 @@ def oracle_bwd(q, k, v, g, dO, cu_seqlens=None, *, scale=None, eps=1e-5, o_norm=
                             _ptr(dz))
     if st != 0:
         raise RuntimeError(f"fix_oracle_bwd failed with status {st}")
+    if scalar:
+        dg = dg.sum(axis=-1)
     return {"dq": dq, "dk": dkk, "dv": dvv, "dg": dg, "dw": dw, "dz": dz}

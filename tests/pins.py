@@ -392,6 +392,32 @@ def pin_logits_match_logsigmoid(lib, rng):
     return worst
 
 
+def pin_scalar_gate_finite_differences(lib, rng):
+    """A scalar gate (one value per token and kv head, [B,T,Hkv]), plain and as logits: its
+    dg against central differences of sum(o * dO) at eps = 0."""
+    lengths = [3, 5]
+    q, k, v, _, cu = rand_case(rng, 1, 8, 2, 1, 3, 4, lengths=lengths)
+    dO = rng.standard_normal((1, 8, 2, 4))
+    worst, h = 0.0, 1e-6
+    for logits in (False, True):
+        x = rng.standard_normal((1, 8, 1)) * 1.5 + (0.3 if logits else -1.0)
+        if not logits:
+            x = -np.abs(x)  # a forget gate
+        dg = O.oracle_bwd(q, k, v, x, dO, cu, eps=0.0, gate_logits=logits, lib=lib)["dg"]
+        assert dg.shape == x.shape
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            vals = []
+            for sgn in (1, -1):
+                x2 = x.copy()
+                x2[idx] += sgn * h
+                vals.append(float(np.sum(O.oracle_fwd(q, k, v, x2, cu, eps=0.0, gate_logits=logits, lib=lib)["o"]
+                                         * dO)))
+            fd[idx] = (vals[0] - vals[1]) / (2 * h)
+        worst = max(worst, rel(dg, fd))
+    return worst
+
+
 ALL_PINS = {
     "no_gate_softmax": (pin_no_gate_is_softmax_attention, 1e-12),
     "no_gate_unnormalised": (pin_no_gate_unnormalised, 1e-12),
@@ -411,4 +437,5 @@ ALL_PINS = {
     "prefix_window": (pin_prefix_window, 0.0),
     "logits_finite_diff": (pin_logits_finite_differences, 1e-6),
     "logits_match_logsigmoid": (pin_logits_match_logsigmoid, 1e-12),
+    "scalar_gate_finite_diff": (pin_scalar_gate_finite_differences, 1e-6),
 }

@@ -833,10 +833,14 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdArgs a) {
 // dk, dv from query chunks two or more after the key chunk.  Workgroup = the
 // 128 keys of one key chunk J and kv head (4 waves x 32 keys), visiting the
 // query chunks from the last to J + 2 and, within each, the G query heads of
-// the group, 32 query rows per step copied straight into LDS: fp16 Q rows
-// and scaled dhat rows only.  The dV and dK products take those rows as their
-// k-major operands through the transposing LDS read (tr_frag), so no
-// transposed copy of either is stored or moved.
+// the group, 64 query rows per step copied straight into LDS (fp16 Q rows and
+// scaled dhat rows only) and computed as two 32-row halves.  With one wave
+// per SIMD every instruction of the step's bookkeeping (positions, copy
+// addresses, the barrier and the wait for the copies) is issue time the
+// products do not hide, so a step spans as many rows as the LDS stages allow.
+// The dV and dK products take those rows as their k-major operands through
+// the transposing LDS read (tr_frag), so no transposed copy of either is
+// stored or moved.
 // The decay product between the chunks, gamma_IJ = exp2(Lam[I-1] - Lam[J]),
 // enters both products through per-chunk operands: V (.) gamma_IJ (rebuilt
 // per query chunk from an LDS copy of the chunk's V rows) for dP, and the
@@ -852,8 +856,9 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
   constexpr int NBK = DKP / 32, NBV = DVP / 32;
   constexpr int NB = 2;             // LDS stages
   constexpr int DIST = NB - 1;      // steps copied ahead of the one computed
-  using QT = LdsTile<32, DK * 2>;   // Q rows of the step (fp16)
-  using DR = LdsTile<32, DV * 2>;   // scaled dhat rows (fp16)
+  constexpr int RS = 64;            // query rows per step (two halves of 32)
+  using QT = LdsTile<RS, DK * 2>;   // Q rows of the step (fp16)
+  using DR = LdsTile<RS, DV * 2>;   // scaled dhat rows (fp16)
   using VRT = LdsTile<CB, DV * 2>;  // the key chunk's V rows, scaled to the chunk end
   // Loads a step issues after its copies' predecessors: the copies themselves
   // (fixed per wave) and nothing else, so waiting for the next step's copies
@@ -894,8 +899,8 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
 
   const int nch = (L + CB - 1) / CB;
   const int I0 = J + 2, I1 = nch - 1;                  // query chunks visited: I1 down to I0
-  const int ns1 = (L - I1 * CB + 31) / 32;              // slices of the last (possibly partial) chunk
-  const int nsteps = I0 <= I1 ? G * ns1 + 4 * G * (I1 - I0) : 0;
+  const int ns1 = (L - I1 * CB + RS - 1) / RS;          // slices of the last (possibly partial) chunk
+  const int nsteps = I0 <= I1 ? G * ns1 + (CB / RS) * G * (I1 - I0) : 0;
   // The key as an fp16 operand: Q is staged as fp16 (q converted once, exact
   // for |q| in [2^-14, 65504]), so the score product runs in fp16 and equals
   // the bf16 one for such inputs.
@@ -918,7 +923,7 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
     int I, gq, u, ord;
   };
   auto advance = [&](Pos &p) {
-    if (++p.u == (p.I == I1 ? ns1 : 4)) {
+    if (++p.u == (p.I == I1 ? ns1 : CB / RS)) {
       p.u = 0;
       if (++p.gq == G) {
         p.gq = 0;
@@ -933,7 +938,7 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
   DR::lane_offsets(Hq * DV * 2, wave, lane, od);
   auto stage_tile = [&](const Pos &p, int b) {
     const int h = c * G + p.gq;
-    const int qt0 = p.I * CB + 32 * p.u;
+    const int qt0 = p.I * CB + RS * p.u;
     const int64_t qr = (st + qt0) * Hq + h;
     const int nrow = L - qt0;
     QT::dma(Qs(b), make_rsrc(a.Q16 + qr * DK, (int64_t)nrow * Hq * DK * 2), oq, wave);
@@ -971,7 +976,7 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
   int prev_ord = -1;
   for (int k = 0; k < nsteps; ++k) {
     const int b = k % NB;
-    const int I = cur.I, qt0 = I * CB + 32 * cur.u;
+    const int I = cur.I, qt0 = I * CB + RS * cur.u;
     if (cur.ord != prev_ord) {  // first step of a query chunk
       prev_ord = cur.ord;
       const float *gm = gam(cur.ord & 1);
@@ -998,82 +1003,93 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
     Pos nxt = cur;
     if (k + 1 < nsteps) advance(nxt);
     const bool next_chunk = nxt.ord != cur.ord;
-    double lamI;
-    // Exponent offsets of the step's rows: read before the step's copies are
-    // issued (an LDS read after them can make the compiler wait for them) and
-    // used only after the products.
-    float4 mq[4];
+    double lamI = 0.0;
+    // Two 32-row halves in turn, kept as a loop (unrolled, the compiler
+    // interleaves the halves' live ranges and spends vector instructions moving
+    // values between register files); the second half is skipped when it lies
+    // past the sequence end.
+#pragma unroll 1
+    for (int h2 = 0; h2 < 2; ++h2) {
+      if (h2 == 1 && qt0 + 32 >= L) break;
+      // Exponent offsets of the step's rows: read before the step's copies are
+      // issued (an LDS read after them can make the compiler wait for them) and
+      // used only after the products.
+      float4 mq[4];
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) mq[q4] = *(const float4 *)&Ms(b)[8 * q4 + 4 * hh];
-    {
-      // S[q][key] and dP[q][key]: lane = key, register j = query acc_row(hh, j).
-      // Operands of a group of products are read from LDS in one batch (one
-      // wait for all of them rather than one per product).
-      f16x8 qa[NS];
-      f16x8 da[NSV];
+      for (int q4 = 0; q4 < 4; ++q4) mq[q4] = *(const float4 *)&Ms(b)[32 * h2 + 8 * q4 + 4 * hh];
+      {
+        // S[q][key] and dP[q][key]: lane = key, register j = query acc_row(hh, j).
+        // Operands of a group of products are read from LDS in one batch (one
+        // wait for all of them rather than one per product).
+        f16x8 qa[NS];
+        f16x8 da[NSV];
 #pragma unroll
-      for (int i = 0; i < NS; ++i) qa[i] = *(const f16x8 *)(Qs(b) + QT::off(n, 2 * i + hh));
+        for (int i = 0; i < NS; ++i) qa[i] = *(const f16x8 *)(Qs(b) + QT::off(32 * h2 + n, 2 * i + hh));
 #pragma unroll
-      for (int i = 0; i < NSV; ++i) da[i] = *(const f16x8 *)(Ds(b) + DR::off(n, 2 * i + hh));
-      __builtin_amdgcn_sched_barrier(0);
-      f32x16 sc = zero16(), dp = zero16();
+        for (int i = 0; i < NSV; ++i) da[i] = *(const f16x8 *)(Ds(b) + DR::off(32 * h2 + n, 2 * i + hh));
+        __builtin_amdgcn_sched_barrier(0);
+        f32x16 sc = zero16(), dp = zero16();
 #pragma unroll
-      for (int i = 0; i < NS; ++i) sc = mma32(qa[i], kf[i], sc);
+        for (int i = 0; i < NS; ++i) sc = mma32(qa[i], kf[i], sc);
 #pragma unroll
-      for (int i = 0; i < NSV; ++i) dp = mma32(da[i], vf[i], dp);
-      // While the products run, between them: the copies of step k + DIST
-      // (the last step again near the end, so that every step issues the
-      // same copies; `ahead` is that step's position), the next chunk's Lam
-      // row, the step's row offsets and the dV / dK operands.
-      f16x8 ta[NBV][2], tq[NBK][2];  // dhat^T and Q^T operands (k = query, in the result tiles' order)
+        for (int i = 0; i < NSV; ++i) dp = mma32(da[i], vf[i], dp);
+        // While the products run, between them: the copies of step k + DIST
+        // (the last step again near the end, so that every step issues the
+        // same copies; `ahead` is that step's position), the next chunk's Lam
+        // row, the step's row offsets and the dV / dK operands.
+        f16x8 ta[NBV][2], tq[NBK][2];  // dhat^T and Q^T operands (k = query, in the result tiles' order)
 #pragma unroll
-      for (int bv = 0; bv < NBV; ++bv)
+        for (int bv = 0; bv < NBV; ++bv)
 #pragma unroll
-        for (int uu = 0; uu < 2; ++uu) ta[bv][uu] = tr_frag<DR>(Ds(b), 16 * uu, 32 * bv, lane);
+          for (int uu = 0; uu < 2; ++uu) ta[bv][uu] = tr_frag<DR>(Ds(b), 32 * h2 + 16 * uu, 32 * bv, lane);
 #pragma unroll
-      for (int bk = 0; bk < NBK; ++bk)
+        for (int bk = 0; bk < NBK; ++bk)
 #pragma unroll
-        for (int uu = 0; uu < 2; ++uu) tq[bk][uu] = tr_frag<QT>(Qs(b), 16 * uu, 32 * bk, lane);
-      stage_tile(ahead, (k + DIST) % NB);
-      if (k + DIST + 1 < nsteps) advance(ahead);
-      lamI = lam_of(nxt.I);
-      constexpr int NTR = 4 * (NBV + NBK);
-#pragma unroll
-      for (int i = 0; i < NS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one product
-        __builtin_amdgcn_sched_group_barrier(0x100, (NTR + NS - 1) / NS, 0);  // transposing LDS reads
-      }
-#pragma unroll
-      for (int i = 0; i < NSV; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one product
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one copy / global load
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      // Rows past the end of the sequence need no mask: their Q, dhat and
-      // row-offset copies read as zeros, so their probability is exp2(0) = 1
-      // (finite), their dP and hence dS are 0, and the dV product meets it
-      // only against their zero dhat rows.
-      f16x8 pf[2], dsf[2];
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const float mv[4] = {mq[q4].x, mq[q4].y, mq[q4].z, mq[q4].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = 4 * q4 + e;
-          const float pv = fast_exp2(sc[j] * sl2 - mv[e]);
-          pf[j >> 3][j & 7] = (_Float16)pv;
-          dsf[j >> 3][j & 7] = (_Float16)(pv * dp[j]);
+          for (int uu = 0; uu < 2; ++uu) tq[bk][uu] = tr_frag<QT>(Qs(b), 32 * h2 + 16 * uu, 32 * bk, lane);
+        if (h2 == 0) {
+          stage_tile(ahead, (k + DIST) % NB);
+          if (k + DIST + 1 < nsteps) advance(ahead);
+          lamI = lam_of(nxt.I);
         }
+        constexpr int NTR = 4 * (NBV + NBK);
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one product
+          __builtin_amdgcn_sched_group_barrier(0x100, (NTR + NS - 1) / NS, 0);  // transposing LDS reads
+        }
+#pragma unroll
+        for (int i = 0; i < NSV; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one product
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one copy / global load
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // Rows past the end of the sequence need no mask: their Q, dhat and
+        // row-offset copies read as zeros, so their probability is exp2(0) = 1
+        // (finite), their dP and hence dS are 0, and the dV product meets it
+        // only against their zero dhat rows.
+        f16x8 pf[2], dsf[2];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float mv[4] = {mq[q4].x, mq[q4].y, mq[q4].z, mq[q4].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int j = 4 * q4 + e;
+            const float pv = fast_exp2(sc[j] * sl2 - mv[e]);
+            pf[j >> 3][j & 7] = (_Float16)pv;
+            dsf[j >> 3][j & 7] = (_Float16)(pv * dp[j]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int bv = 0; bv < NBV; ++bv)
+#pragma unroll
+          for (int uu = 0; uu < 2; ++uu) accV[bv] = mma32(pf[uu], ta[bv][uu] * gh[bv], accV[bv]);
+#pragma unroll
+        for (int bk = 0; bk < NBK; ++bk)
+#pragma unroll
+          for (int uu = 0; uu < 2; ++uu) accK[bk] = mma32(dsf[uu], tq[bk][uu], accK[bk]);
       }
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int bv = 0; bv < NBV; ++bv)
-#pragma unroll
-        for (int uu = 0; uu < 2; ++uu) accV[bv] = mma32(pf[uu], ta[bv][uu] * gh[bv], accV[bv]);
-#pragma unroll
-      for (int bk = 0; bk < NBK; ++bk)
-#pragma unroll
-        for (int uu = 0; uu < 2; ++uu) accK[bk] = mma32(dsf[uu], tq[bk][uu], accK[bk]);
     }
     // gamma of the next chunk, into the other buffer (its last readers passed
     // the barrier that ended the first step of the previous chunk).

@@ -36,7 +36,7 @@ TRAFFIC = {
                           "gated_softmax_attention_amd/csrc/common.h",
                           "gated_softmax_attention_amd/csrc/launch.h",
                           "gated_softmax_attention_amd/build.py"]},
-    "decode_step": {"bytes": int(2 * 135728.5625 * 1024) + 1040 * 1024, "sha": "012d1d595ccc3a70",
+    "decode_step": {"bytes": int(2 * 135701.125 * 1024) + 1040 * 1024, "sha": "e1c557aecbc74ebd",
                     "files": ["gated_softmax_attention_amd/csrc/decode.hip",
                               "gated_softmax_attention_amd/csrc/common.h",
                               "gated_softmax_attention_amd/csrc/launch.h",

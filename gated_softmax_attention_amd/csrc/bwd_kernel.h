@@ -304,8 +304,8 @@ __global__ void __launch_bounds__(256, 1) k_bwd_intra_dkv(BwdArgs a) {
   // One LDS object for every tile (see the forward kernel).
   constexpr int O_Q = 0, O_QT = O_Q + 2 * QT::BYTES, O_X = O_QT + 2 * QTT::BYTES;
   constexpr int O_TH = O_X + 2 * XR::BYTES, O_TL = O_TH + 2 * XTT::BYTES;
-  constexpr int O_M = O_TL + 2 * XTT::BYTES, O_E = O_M + 2 * 256;
-  __shared__ __align__(1024) char smem[O_E + 9 * DV * 4];
+  constexpr int O_M = O_TL + 2 * XTT::BYTES, O_E = O_M + 2 * 256, O_GW = O_E + 9 * DV * 4;
+  __shared__ __align__(1024) char smem[O_GW + 4 * DV * 4];
   auto Qs = [&](int b) { return smem + O_Q + b * QT::BYTES; };
   auto Qts = [&](int b) { return smem + O_QT + b * QTT::BYTES; };
   auto Xs = [&](int b) { return smem + O_X + b * XR::BYTES; };
@@ -313,6 +313,7 @@ __global__ void __launch_bounds__(256, 1) k_bwd_intra_dkv(BwdArgs a) {
   auto Tls = [&](int b) { return smem + O_TL + b * XTT::BYTES; };
   auto Ms = [&](int b) { return (float *)(smem + O_M + b * 256); };  // 64 floats, 32 used
   float(*BE)[DV] = (float(*)[DV])(smem + O_E);  // BE[b + 1] = E(b), b = -1..7
+  float *gw = (float *)(smem + O_GW) + (threadIdx.x >> 6) * DV;  // this wave's gamma of the step, per channel
 
   const Plan &pl = a.plan;
   const int gc = blockIdx.x, c = blockIdx.y;
@@ -387,7 +388,9 @@ __global__ void __launch_bounds__(256, 1) k_bwd_intra_dkv(BwdArgs a) {
     const int64_t qr = (st + q0) * Hq + h;
     const int nrow = L - q0;
     if constexpr (!F32IN) {
-      QT::dma(Qs(buf), make_rsrc((const uint16_t *)a.q + qr * DK, (int64_t)nrow * Hq * DK * 2), oq, wave);
+      const u32x4 rq = rsrc_words((const uint16_t *)a.q + qr * DK, (int64_t)nrow * Hq * DK * 2);
+#pragma unroll
+      for (int t = 0; t < QT::NW; ++t) QT::dma_piece_untracked(Qs(buf), rq, oq, t, wave);
     } else {
       for (int p = tid; p < QT::NCH; p += 256) {
         const int r = p / QT::CPR, cc = p % QT::CPR;
@@ -395,12 +398,21 @@ __global__ void __launch_bounds__(256, 1) k_bwd_intra_dkv(BwdArgs a) {
       }
     }
     const int64_t ch = (int64_t)(gc + (qa >> 2)) * Hq + h;
-    QTTD::dma(Qts(buf), make_rsrc(a.Qt + ch * DK * CB + 32 * (qa & 3), (int64_t)DK * CB * 2), oqt, wave);
-    XR::dma(Xs(buf), make_rsrc(a.X16 + qr * DV, (int64_t)nrow * Hq * DV * 2), ox, wave);
-    XTTD::dma(Ths(buf), make_rsrc(a.XTH + ch * DV * CB + 32 * (qa & 3), (int64_t)DV * CB * 2), oxt, wave);
-    XTTD::dma(Tls(buf), make_rsrc(a.XTL + ch * DV * CB + 32 * (qa & 3), (int64_t)DV * CB * 2), oxt, wave);
+    const u32x4 rqt = rsrc_words(a.Qt + ch * DK * CB + 32 * (qa & 3), (int64_t)DK * CB * 2);
+#pragma unroll
+    for (int t = 0; t < QTTD::NW; ++t) QTTD::dma_piece_untracked(Qts(buf), rqt, oqt, t, wave);
+    const u32x4 rx = rsrc_words(a.X16 + qr * DV, (int64_t)nrow * Hq * DV * 2);
+#pragma unroll
+    for (int t = 0; t < XR::NW; ++t) XR::dma_piece_untracked(Xs(buf), rx, ox, t, wave);
+    const u32x4 rth = rsrc_words(a.XTH + ch * DV * CB + 32 * (qa & 3), (int64_t)DV * CB * 2);
+    const u32x4 rtl = rsrc_words(a.XTL + ch * DV * CB + 32 * (qa & 3), (int64_t)DV * CB * 2);
+#pragma unroll
+    for (int t = 0; t < XTTD::NW; ++t) {
+      XTTD::dma_piece_untracked(Ths(buf), rth, oxt, t, wave);
+      XTTD::dma_piece_untracked(Tls(buf), rtl, oxt, t, wave);
+    }
     // lane r fills Ms[r] (every wave, the same bytes)
-    dma4(Ms(buf), make_rsrc(a.mb + qr, (int64_t)nrow * Hq * 4), (uint32_t)lane * Hq * 4);
+    dma4_untracked(Ms(buf), rsrc_words(a.mb + qr, (int64_t)nrow * Hq * 4), (uint32_t)lane * Hq * 4);
   };
 
   if (nsteps > 0) stage_tile(0, 0);
@@ -411,29 +423,34 @@ __global__ void __launch_bounds__(256, 1) k_bwd_intra_dkv(BwdArgs a) {
     const int qa = 1 + k % nqo;
     const int q0 = c0 + 32 * qa;
     const bool act = active && qa > wave;
-    // LDS tables are read, and gamma applied, before the next copies are
-    // issued (LDS reads that follow a copy issue in the same step can make
-    // the compiler wait for it).
+    // The next step's copies first: they are issued from inline assembly that
+    // the compiler's wait counts do not see, so the LDS reads below do not
+    // wait for them, and they have the whole step to land.
+    stage_tile(min(k + 1, nsteps - 1), buf ^ 1);
     float4 mq[4];
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) mq[q4] = *(const float4 *)&Ms(buf)[8 * q4 + 4 * hh];
     float gcol[NBV];  // gamma of the lane's dV output columns
     f16x8 kop[NSV];   // V to block end (.) gamma, B operand of dP
     if (act) {
+      // gamma[d] = exp2(E(qa - 1) - E(wave)) depends on the channel only: each
+      // lane evaluates two channels into the wave's table, then every lane
+      // reads the channels it needs (a wave's LDS accesses complete in order).
 #pragma unroll
-      for (int bv = 0; bv < NBV; ++bv) {
-        const int d = min(32 * bv + n, DV - 1);
-        gcol[bv] = fast_exp2(BE[qa][d] - BE[wave + 1][d]);
+      for (int t = 0; t < (DV + 63) / 64; ++t) {
+        const int d = lane + 64 * t;
+        if (d < DV) gw[d] = fast_exp2(BE[qa][d] - BE[wave + 1][d]);
       }
 #pragma unroll
-      for (int i = 0; i < NSV; ++i)
+      for (int bv = 0; bv < NBV; ++bv) gcol[bv] = gw[min(32 * bv + n, DV - 1)];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int d = 16 * i + 8 * hh + e;
-          kop[i][e] = (_Float16)((float)ve[i][e] * fast_exp2(BE[qa][d] - BE[wave + 1][d]));
-        }
+      for (int i = 0; i < NSV; ++i) {
+        const float4 g0 = *(const float4 *)(gw + 16 * i + 8 * hh), g1 = *(const float4 *)(gw + 16 * i + 8 * hh + 4);
+        const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kop[i][e] = (_Float16)((float)ve[i][e] * gv[e]);
+      }
     }
-    stage_tile(min(k + 1, nsteps - 1), buf ^ 1);
     if (act) {
       // S[q][key] and dP[q][key]: lane = key, register j = query acc_row(hh, j)
       f32x16 sc = zero16(), dp = zero16();

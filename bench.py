@@ -31,7 +31,7 @@ PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16/fp16 MFMA peak (AMD specification
 # a plain-copy calibration (x2.0 reads, x1.0 writes); valid only for the sources they were
 # taken on (sha256 prefix over the files listed, the build flags included).  Reported as roofline.traffic, else null.
 TRAFFIC = {
-    "bwd_dkv": {"bytes": 2 * 1021253 * 1024 + 532007 * 1024, "sha": "59da17ffa466d677",
+    "bwd_dkv": {"bytes": 2 * 1021253 * 1024 + 532007 * 1024, "sha": "58c7e69df0654a08",
                 "files": ["gated_softmax_attention_amd/csrc/bwd_kernel.h",
                           "gated_softmax_attention_amd/csrc/common.h",
                           "gated_softmax_attention_amd/csrc/launch.h",

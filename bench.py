@@ -31,12 +31,12 @@ PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16/fp16 MFMA peak (AMD specification
 # a plain-copy calibration (x2.0 reads, x1.0 writes); valid only for the sources they were
 # taken on (sha256 prefix over the files listed, the build flags included).  Reported as roofline.traffic, else null.
 TRAFFIC = {
-    "bwd_dkv": {"bytes": 2 * 1021253 * 1024 + 532007 * 1024, "sha": "58c7e69df0654a08",
+    "bwd_dkv": {"bytes": 2 * 1021253 * 1024 + 532007 * 1024, "sha": "c04255e680d0994e",
                 "files": ["gated_softmax_attention_amd/csrc/bwd_kernel.h",
                           "gated_softmax_attention_amd/csrc/common.h",
                           "gated_softmax_attention_amd/csrc/launch.h",
                           "gated_softmax_attention_amd/build.py"]},
-    "decode_step": {"bytes": int(2 * 135701.125 * 1024) + 1040 * 1024, "sha": "e1c557aecbc74ebd",
+    "decode_step": {"bytes": int(2 * 135701.125 * 1024) + 1040 * 1024, "sha": "4c7ae8d84ece29e7",
                     "files": ["gated_softmax_attention_amd/csrc/decode.hip",
                               "gated_softmax_attention_amd/csrc/common.h",
                               "gated_softmax_attention_amd/csrc/launch.h",

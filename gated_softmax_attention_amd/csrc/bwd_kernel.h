@@ -669,12 +669,14 @@ __global__ void __launch_bounds__(256, 1) k_bwd_intra_dkv(BwdArgs a) {
 // one q head (4 waves x 32 rows); key chunks are visited from the first on
 // (so the workgroups of a head, started together, read the same key chunk at
 // the same time and share it in L2), 32 keys per step copied straight into
-// LDS (double buffered): K rows
-// (bf16) for S^T, transposed K (fp16) for dS.K, and V scaled to its chunk
-// end (fp16) for dP^T.  The decay product between the chunks, gamma_IJ =
-// exp2(Lam[I-1] - Lam[J]), multiplies the query-side operand (the scaled
-// dhat rows), rebuilt once per key chunk; gamma_IJ itself is computed into
-// LDS during the step before the chunk starts, from a Lam row loaded then.
+// LDS, two steps ahead through three stages: K rows (bf16) for S^T,
+// transposed K (fp16) for dS.K, and V scaled to its chunk end (fp16) for
+// dP^T.  Many copies come from HBM (the L2 holds only part of a head's key
+// chunks), so a step's copies get two steps to land.  The decay product
+// between the chunks, gamma_IJ = exp2(Lam[I-1] - Lam[J]), multiplies the
+// query-side operand (the scaled dhat rows, kept in registers), rebuilt once
+// per key chunk; gamma_IJ itself is computed into LDS at the end of the step
+// before the chunk starts, from the Lam row copied with that step's tiles.
 // ---------------------------------------------------------------------------
 template <int DK, int DV, bool F32IN>
 __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdArgs a) {
@@ -685,12 +687,17 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdArgs a) {
   using TT = LdsTile<DKP, 64>;     // transposed K (dk rows x 32 keys), rows padded to DKP
   using TTD = LdsTile<DK, 64>;
   using VT = LdsTile<32, DV * 2>;  // V rows of the step (scaled to their chunk end)
-  // One LDS object for every tile (see the forward kernel).
-  constexpr int O_K = 0, O_T = O_K + 2 * KT::BYTES, O_V = O_T + 2 * TT::BYTES, O_G = O_V + 2 * VT::BYTES;
+  // One LDS object for every tile (see the forward kernel).  Three stages:
+  // a step's copies are issued two steps ahead.  Each stage also holds the
+  // Lam row of the key chunk after the step's (DV doubles, 1 KB reserved).
+  constexpr int NBQ = 3;
+  constexpr int O_K = 0, O_T = O_K + NBQ * KT::BYTES, O_V = O_T + NBQ * TT::BYTES, O_L = O_V + NBQ * VT::BYTES;
+  constexpr int O_G = O_L + NBQ * 1024;
   __shared__ __align__(1024) char smem[O_G + 2 * DV * 4];
   auto Ks = [&](int b) { return smem + O_K + b * KT::BYTES; };
   auto Kts = [&](int b) { return smem + O_T + b * TT::BYTES; };
   auto Vs = [&](int b) { return smem + O_V + b * VT::BYTES; };
+  auto Ls = [&](int b) { return smem + O_L + b * 1024; };
   auto gam = [&](int b) { return (float *)(smem + O_G) + b * DV; };
 
   const Plan &pl = a.plan;
@@ -727,10 +734,8 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdArgs a) {
   const _Float16 *dhrow = a.dh + ((st + min(row, L - 1)) * Hq + hq) * DV;
   f16x8 dhf[NSV];
   if (DK < DKP)
-    for (int e = tid; e < (DKP - DK) * 64 / 4; e += 256) {
-      ((uint32_t *)(Kts(0) + DK * 64))[e] = 0u;
-      ((uint32_t *)(Kts(1) + DK * 64))[e] = 0u;
-    }
+    for (int e = tid; e < (DKP - DK) * 64 / 4; e += 256)
+      for (int b = 0; b < NBQ; ++b) ((uint32_t *)(Kts(b) + DK * 64))[e] = 0u;
   f32x16 acc[NBK];
 #pragma unroll
   for (int b = 0; b < NBK; ++b) acc[b] = zero16();
@@ -749,9 +754,11 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdArgs a) {
   auto stage_tile = [&](int k, int b) {
     const int J = k >> 2, u = k & 3;
     const int kt0 = J * CB + 32 * u;
+    b = uniform(b);
     if constexpr (!F32IN) {
-      KT::dma(Ks(b), make_rsrc((const uint16_t *)a.k + ((st + kt0) * Hkv + c) * DK, (int64_t)32 * Hkv * DK * 2), ok,
-              wave);
+      const u32x4 rk = rsrc_words((const uint16_t *)a.k + ((st + kt0) * Hkv + c) * DK, (int64_t)32 * Hkv * DK * 2);
+#pragma unroll
+      for (int t = 0; t < KT::NW; ++t) KT::dma_piece_untracked(Ks(b), rk, ok, t, wave);
     } else {
       for (int p = tid; p < KT::NCH; p += 256) {
         const int r = p / KT::CPR, cc = p % KT::CPR;
@@ -759,25 +766,39 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdArgs a) {
       }
     }
     const int64_t ch = (int64_t)(cbs + J) * Hkv + c;
-    TTD::dma(Kts(b), make_rsrc(a.Kt + ch * DK * CB + 32 * u, (int64_t)DK * CB * 2), ot, wave);
-    VT::dma(Vs(b), make_rsrc(a.Vr + (ch * CB + 32 * u) * DV, 32 * DV * 2), ov, wave);
+    const u32x4 rt = rsrc_words(a.Kt + ch * DK * CB + 32 * u, (int64_t)DK * CB * 2);
+#pragma unroll
+    for (int t = 0; t < TTD::NW; ++t) TTD::dma_piece_untracked(Kts(b), rt, ot, t, wave);
+    const u32x4 rv = rsrc_words(a.Vr + (ch * CB + 32 * u) * DV, 32 * DV * 2);
+#pragma unroll
+    for (int t = 0; t < VT::NW; ++t) VT::dma_piece_untracked(Vs(b), rv, ov, t, wave);
+    // Lam row of key chunk J + 1 (clamped): wave w copies bytes 256 w .. +255
+    // (zeros past DV doubles)
+    const double *lrow = a.Lam + ((int64_t)(cbs + min(J + 1, I - 1)) * Hkv + c) * DV;
+    dma4_untracked(Ls(b) + 256 * wave, rsrc_words(lrow, (int64_t)DV * 8), (uint32_t)(256 * wave + 4 * lane));
   };
+  // Copies a step issues from inline assembly (the compiler's wait counts do
+  // not see them); with fp32 inputs the K rows are stored by the threads
+  // instead, and the compiler's own wait for those loads covers every earlier
+  // copy.
+  constexpr int NCOPYQ = (F32IN ? 0 : KT::NW) + TTD::NW + VT::NW + 1;
 
-  // The unscaled dhat rows are loaded at the end of the step before each key
-  // chunk (so their wait is the step's final wait) and scaled at the top of
-  // the chunk's first step, before that step issues any copy: LDS reads that
-  // follow a copy issue in the same step can make the compiler wait for it.
+  // The unscaled dhat rows stay in registers; they are scaled by gamma_IJ at
+  // the top of each key chunk's first step.  Every load of the kernel's own
+  // is complete before the first copy is issued, and the loop makes none.
   f16x8 raw[NSV];
+#pragma unroll
+  for (int i = 0; i < NSV; ++i) raw[i] = *(const f16x8 *)(dhrow + 16 * i + 8 * hh);
+  if (nsteps > 0 && tid < DV) gam(0)[tid] = fast_exp2((float)(lamI - lam_of(0)));
+  wait_all();
   if (nsteps > 0) {
     stage_tile(0, 0);
-    if (tid < DV) gam(0)[tid] = fast_exp2((float)(lamI - lam_of(0)));
-#pragma unroll
-    for (int i = 0; i < NSV; ++i) raw[i] = *(const f16x8 *)(dhrow + 16 * i + 8 * hh);
+    stage_tile(min(1, nsteps - 1), 1);
   }
-  wait_all();
-  __syncthreads();
+  wait_vm<NCOPYQ>();  // step 0 has landed
+  lds_barrier();
   for (int k = 0; k < nsteps; ++k) {
-    const int b = k & 1;
+    const int b = uniform(k % NBQ);
     const bool next_chunk = (k & 3) == 3 && k + 1 < nsteps;
     if ((k & 3) == 0) {  // entered key chunk J: dhat operand times gamma_IJ
       const float *gm = gam((k >> 2) & 1);
@@ -789,10 +810,10 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdArgs a) {
         for (int e = 0; e < 8; ++e) dhf[i][e] = (_Float16)((float)raw[i][e] * gv[e]);
       }
     }
-    // Same copies and loads on every step (the last step re-copies its own
-    // tile into the idle buffer; the Lam row index is kept valid).
-    stage_tile(min(k + 1, nsteps - 1), b ^ 1);
-    const double lamJ = lam_of(min((k >> 2) + 1, I - 1));
+    // Same copies on every step (past the last step, the last step's tile
+    // again, into a stage nobody reads); step k + 2's stage was last read in
+    // step k - 1.
+    stage_tile(min(k + 2, nsteps - 1), uniform((k + 2) % NBQ));
     {
       // (Operands are read from LDS per product: batching them needs more
       // registers than this kernel has at two workgroups per CU.)
@@ -817,14 +838,12 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdArgs a) {
     }
     // gamma of the next chunk, into the other buffer (its last readers passed
     // the barrier that began this chunk).
-    if (next_chunk) {
-      if (tid < DV) gam(((k >> 2) + 1) & 1)[tid] = fast_exp2((float)(lamI - lamJ));
-#pragma unroll
-      for (int i = 0; i < NSV; ++i) raw[i] = *(const f16x8 *)(dhrow + 16 * i + 8 * hh);
-    }
-    wait_all();
-    __syncthreads();
+    if (next_chunk && tid < DV)
+      gam(((k >> 2) + 1) & 1)[tid] = fast_exp2((float)(lamI - ((const double *)Ls(b))[tid]));
+    wait_vm<NCOPYQ>();  // step k + 1 has landed (step k + 2's copies stay in flight)
+    lds_barrier();
   }
+  wait_all();  // copies issued past the last step
   // The block's inputs are loaded before any of its stores (the compiler
   // cannot tell dq and dq_i apart, so interleaving would serialize them).
 #pragma unroll

@@ -234,7 +234,9 @@ template <class T> __device__ inline f16x8 tr_frag(const char *tile, int row0, i
 // explicit waits (wait_vm): loads complete in issue order, so the compiler's
 // own counts stay conservative when these are issued between its loads.  The
 // resource is given as its four descriptor words; m0 (the LDS base of the
-// copy) is saved and restored around it.
+// copy, which must be the same in every lane: it is taken from the first
+// active lane, since the compiler cannot always prove it uniform) is saved
+// and restored around it.
 // LDS byte address of a pointer into LDS.
 __device__ inline uint32_t lds_addr(const void *p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
@@ -249,12 +251,12 @@ __device__ inline u32x4 rsrc_words(const void *base, int64_t bytes) {
 __device__ inline void dma16_untracked(void *lds, const u32x4 &src, uint32_t o) {
   uint32_t saved;
   asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
-               : "=&s"(saved) : "s"(lds_addr(lds)), "v"(o), "s"(src) : "memory");
+               : "=&s"(saved) : "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds))), "v"(o), "s"(src) : "memory");
 }
 __device__ inline void dma4_untracked(void *lds, const u32x4 &src, uint32_t o) {
   uint32_t saved;
   asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dword %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
-               : "=&s"(saved) : "s"(lds_addr(lds)), "v"(o), "s"(src) : "memory");
+               : "=&s"(saved) : "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds))), "v"(o), "s"(src) : "memory");
 }
 
 template <int ROWS, int RB>

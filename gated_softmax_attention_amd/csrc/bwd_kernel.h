@@ -286,8 +286,10 @@ __global__ void __launch_bounds__(256, 1) k_bwd_intra_dq(BwdArgs a) {
 // the first factor is in the staged dhat, the middle one gamma multiplies
 // the wave's V-to-block-end operand (dP) and each dV step's result per
 // channel, and the last one scales dV in the epilogue.  The diagonal block
-// uses gamma = exp2(E(w-1) - E(w)) >= 1 and V from the token before the
-// block, as in the dq kernel; past 2^BGUARD its pairs are evaluated directly.
+// (the step whose query block is the wave's own) uses gamma =
+// exp2(E(w-1) - E(w)) >= 1 and V from the token before the block, as in the
+// dq kernel, from tiles staged with that step; past 2^BGUARD its pairs are
+// evaluated directly after the loop.
 // ---------------------------------------------------------------------------
 template <int DK, int DV, bool F32IN>
 __global__ void __launch_bounds__(256, 1) k_bwd_intra_dkv(BwdArgs a) {
@@ -305,7 +307,15 @@ __global__ void __launch_bounds__(256, 1) k_bwd_intra_dkv(BwdArgs a) {
   constexpr int O_Q = 0, O_QT = O_Q + 2 * QT::BYTES, O_X = O_QT + 2 * QTT::BYTES;
   constexpr int O_TH = O_X + 2 * XR::BYTES, O_TL = O_TH + 2 * XTT::BYTES;
   constexpr int O_M = O_TL + 2 * XTT::BYTES, O_E = O_M + 2 * 256, O_GW = O_E + 9 * DV * 4;
-  __shared__ __align__(1024) char smem[O_GW + 4 * DV * 4];
+  // Diagonal steps also stage the query block's dhat as bf16 hi / lo rows and
+  // the key block's V relative to the token before it (bf16 hi / lo rows).
+  constexpr int O_XH = O_GW + 4 * DV * 4, O_XL = O_XH + 2 * XR::BYTES, O_BH = O_XL + 2 * XR::BYTES;
+  constexpr int O_BL = O_BH + 2 * XR::BYTES;
+  __shared__ __align__(1024) char smem[O_BL + 2 * XR::BYTES];
+  auto XHs = [&](int b) { return smem + O_XH + b * XR::BYTES; };
+  auto XLs = [&](int b) { return smem + O_XL + b * XR::BYTES; };
+  auto BHs = [&](int b) { return smem + O_BH + b * XR::BYTES; };
+  auto BLs = [&](int b) { return smem + O_BL + b * XR::BYTES; };
   auto Qs = [&](int b) { return smem + O_Q + b * QT::BYTES; };
   auto Qts = [&](int b) { return smem + O_QT + b * QTT::BYTES; };
   auto Xs = [&](int b) { return smem + O_X + b * XR::BYTES; };
@@ -370,19 +380,22 @@ __global__ void __launch_bounds__(256, 1) k_bwd_intra_dkv(BwdArgs a) {
 #pragma unroll
   for (int b = 0; b < NBV; ++b) accV[b] = zero16();
 
-  // Off-diagonal query blocks qa = 1 .. nqb - 1 of every head through LDS
-  // (block 0 is only ever diagonal); the diagonal blocks follow per wave.
-  const int nqo = nqb - 1;
+  // Query blocks qa = 0 .. nqb - 1 of every head through LDS.  Wave w takes
+  // the blocks after its own (qa > w) and, at qa = w, its diagonal block,
+  // unless the block's gate range needs exact per-pair decays (then that
+  // block is done afterwards, from global memory).
+  const int nqo = nqb;
   const int nsteps = G * nqo;
   // Rows past the end of the sequence read as zeros; their probabilities are
   // masked to zero when the step is computed.
-  uint32_t oq[QT::NW], oqt[QTTD::NW], ox[XR::NW], oxt[XTTD::NW];
+  uint32_t oq[QT::NW], oqt[QTTD::NW], ox[XR::NW], oxt[XTTD::NW], ob[XR::NW];
+  XR::lane_offsets(Hkv * DV * 2, wave, lane, ob);
   QT::lane_offsets(Hq * DK * 2, wave, lane, oq);
   QTTD::lane_offsets(CB * 2, wave, lane, oqt);
   XR::lane_offsets(Hq * DV * 2, wave, lane, ox);
   XTTD::lane_offsets(CB * 2, wave, lane, oxt);
   auto stage_tile = [&](int k, int buf) {
-    const int gq = k / nqo, qa = 1 + k % nqo;
+    const int gq = k / nqo, qa = k % nqo;
     const int h = c * G + gq;
     const int q0 = c0 + 32 * qa;
     const int64_t qr = (st + q0) * Hq + h;
@@ -413,16 +426,45 @@ __global__ void __launch_bounds__(256, 1) k_bwd_intra_dkv(BwdArgs a) {
     }
     // lane r fills Ms[r] (every wave, the same bytes)
     dma4_untracked(Ms(buf), rsrc_words(a.mb + qr, (int64_t)nrow * Hq * 4), (uint32_t)lane * Hq * 4);
+    if (qa < 4) {  // the diagonal block of wave qa
+      const u32x4 rxh = rsrc_words(a.XH + qr * DV, (int64_t)nrow * Hq * DV * 2);
+      const u32x4 rxl = rsrc_words(a.XL + qr * DV, (int64_t)nrow * Hq * DV * 2);
+      const int64_t kr = (st + q0) * Hkv + c;  // the key block is the query block
+      const u32x4 rbh = rsrc_words(a.VBH + kr * DV, (int64_t)nrow * Hkv * DV * 2);
+      const u32x4 rbl = rsrc_words(a.VBL + kr * DV, (int64_t)nrow * Hkv * DV * 2);
+#pragma unroll
+      for (int t = 0; t < XR::NW; ++t) {
+        XR::dma_piece_untracked(XHs(buf), rxh, ox, t, wave);
+        XR::dma_piece_untracked(XLs(buf), rxl, ox, t, wave);
+        XR::dma_piece_untracked(BHs(buf), rbh, ob, t, wave);
+        XR::dma_piece_untracked(BLs(buf), rbl, ob, t, wave);
+      }
+    }
+  };
+  // Whether this wave's diagonal block needs exact per-pair decays (gate
+  // range of the block beyond 2^BGUARD; BE is complete after the barrier below).
+  auto exact_diag = [&]() {
+    float rng = 0.f;
+#pragma unroll
+    for (int i = 0; i < NSV; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int d = 16 * i + 8 * hh + e;
+        rng = fmaxf(rng, BE[wave][d] - BE[wave + 1][d]);
+      }
+    return __any(rng > BGUARD);
   };
 
   if (nsteps > 0) stage_tile(0, 0);
   wait_all();
   __syncthreads();
+  const bool direct = exact_diag();
   for (int k = 0; k < nsteps; ++k) {
     const int buf = k & 1;
-    const int qa = 1 + k % nqo;
+    const int qa = k % nqo;
     const int q0 = c0 + 32 * qa;
-    const bool act = active && qa > wave;
+    const bool diag = qa == wave;
+    const bool act = active && (qa > wave || (diag && !direct));
     // The next step's copies first: they are issued from inline assembly that
     // the compiler's wait counts do not see, so the LDS reads below do not
     // wait for them, and they have the whole step to land.
@@ -443,21 +485,36 @@ __global__ void __launch_bounds__(256, 1) k_bwd_intra_dkv(BwdArgs a) {
       }
 #pragma unroll
       for (int bv = 0; bv < NBV; ++bv) gcol[bv] = gw[min(32 * bv + n, DV - 1)];
+      if (!diag)
 #pragma unroll
-      for (int i = 0; i < NSV; ++i) {
-        const float4 g0 = *(const float4 *)(gw + 16 * i + 8 * hh), g1 = *(const float4 *)(gw + 16 * i + 8 * hh + 4);
-        const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+        for (int i = 0; i < NSV; ++i) {
+          const float4 g0 = *(const float4 *)(gw + 16 * i + 8 * hh), g1 = *(const float4 *)(gw + 16 * i + 8 * hh + 4);
+          const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) kop[i][e] = (_Float16)((float)ve[i][e] * gv[e]);
-      }
+          for (int e = 0; e < 8; ++e) kop[i][e] = (_Float16)((float)ve[i][e] * gv[e]);
+        }
     }
     if (act) {
       // S[q][key] and dP[q][key]: lane = key, register j = query acc_row(hh, j)
       f32x16 sc = zero16(), dp = zero16();
 #pragma unroll
       for (int i = 0; i < NS; ++i) sc = mma32(*(const kfrag *)(Qs(buf) + QT::off(n, 2 * i + hh)), kf[i], sc);
+      if (diag) {
+        // split at the token before the block: dhat and V as bf16 hi / lo (bf16x3)
 #pragma unroll
-      for (int i = 0; i < NSV; ++i) dp = mma32(*(const f16x8 *)(Xs(buf) + XR::off(n, 2 * i + hh)), kop[i], dp);
+        for (int i = 0; i < NSV; ++i) {
+          const bf16x8 xh = *(const bf16x8 *)(XHs(buf) + XR::off(n, 2 * i + hh));
+          const bf16x8 xl = *(const bf16x8 *)(XLs(buf) + XR::off(n, 2 * i + hh));
+          const bf16x8 vh = *(const bf16x8 *)(BHs(buf) + XR::off(n, 2 * i + hh));
+          const bf16x8 vl = *(const bf16x8 *)(BLs(buf) + XR::off(n, 2 * i + hh));
+          dp = mma32(xh, vh, dp);
+          dp = mma32(xl, vh, dp);
+          dp = mma32(xh, vl, dp);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < NSV; ++i) dp = mma32(*(const f16x8 *)(Xs(buf) + XR::off(n, 2 * i + hh)), kop[i], dp);
+      }
       f16x8 dsf[2];
       bf16x8 ph[2], plo[2];
 #pragma unroll
@@ -466,7 +523,8 @@ __global__ void __launch_bounds__(256, 1) k_bwd_intra_dkv(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int j = 4 * q4 + e;
-          const float pv = q0 + acc_row(hh, j) < L ? fast_exp2(sc[j] * sl2 - mv[e]) : 0.f;
+          const int r = acc_row(hh, j);
+          const float pv = q0 + r < L && (!diag || r >= n) ? fast_exp2(sc[j] * sl2 - mv[e]) : 0.f;
           dsf[j >> 3][j & 7] = (_Float16)(pv * dp[j]);
           split_bf16(pv, ph[j >> 3], plo[j >> 3], j & 7);
         }
@@ -498,9 +556,10 @@ __global__ void __launch_bounds__(256, 1) k_bwd_intra_dkv(BwdArgs a) {
   }
   if (!active) return;
 
-  // Diagonal block (queries of the wave's own block), per head, from global
-  // memory (L2): the split is at the token before the block, gamma =
-  // exp2(E(w-1) - E(w)) >= 1, V from the token before the block as bf16x3.
+  // Diagonal block with exact per-pair decays (gate range beyond 2^BGUARD),
+  // per head from global memory.  (Otherwise the staged loop did it: split at
+  // the token before the block, gamma = exp2(E(w-1) - E(w)) >= 1, V from the
+  // token before the block as bf16x3.)
   bool dflag = false;  // exact diagonal contributions written to dv_i
   {
     float rng = 0.f, gd[NBV];
@@ -517,19 +576,13 @@ __global__ void __launch_bounds__(256, 1) k_bwd_intra_dkv(BwdArgs a) {
       gd[bv] = fast_exp2(BE[wave][d] - BE[wave + 1][d]);
     }
     const bool direct = __any(rng > BGUARD);
-    bf16x8 vh[NSV], vl[NSV];  // the key's V relative to the token before the block, bf16 hi / lo
-    if (!direct) {
-      const int64_t kr = ((st + min(key, L - 1)) * Hkv + c) * DV;
-      const bf16x8 zero = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+    // (the staged loop computed this block unless it needs the exact decays)
+    bf16x8 vh[NSV], vl[NSV];
 #pragma unroll
-      for (int i = 0; i < NSV; ++i) {
-        vh[i] = kv ? *(const bf16x8 *)(a.VBH + kr + 16 * i + 8 * hh) : zero;
-        vl[i] = kv ? *(const bf16x8 *)(a.VBL + kr + 16 * i + 8 * hh) : zero;
-      }
-    }
+    for (int i = 0; i < NSV; ++i) vh[i] = vl[i] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
     const int q0 = kb;
     const int qrow = min(q0 + n, L - 1);  // A-operand row of this lane
-    for (int gq = 0; gq < G; ++gq) {
+    for (int gq = 0; direct && gq < G; ++gq) {
       const int h = c * G + gq;
       f32x16 sc = zero16(), dp = zero16();
 #pragma unroll

@@ -69,8 +69,11 @@ __device__ __noinline__ void direct_dp(const float *delta, const float *sig, con
 // ---------------------------------------------------------------------------
 // Within-chunk contributions to dq.  Workgroup = one 128-chunk of one q head;
 // wave w owns query rows c0 + 32w .. +31 (query block w).  Key blocks b are
-// copied into LDS one per step (double buffered): K rows, transposed K, and
-// V scaled to the end of its block (VE).  With E(b) the chunk-local log2
+// copied into LDS one per step (double buffered): K rows, transposed K, V
+// scaled to the end of its block (VE), and for the diagonal block of wave b
+// its V relative to the token before it and query block b's dhat (bf16 hi /
+// lo each), so every wave's diagonal block is computed in the step of its
+// own key block.  With E(b) the chunk-local log2
 // gate prefix at the end of block b (E(-1) = 0), the decay of a pair in
 // query block a > b splits as
 //     exp2(Gl_i - E(a-1)) * exp2(E(a-1) - E(b)) * exp2(E(b) - Gl_j),
@@ -92,7 +95,16 @@ __global__ void __launch_bounds__(256, 1) k_bwd_intra_dq(BwdArgs a) {
   using VT = LdsTile<32, DV * 2>;  // VE rows of the key block
   // One LDS object for every tile (see the forward kernel).
   constexpr int O_K = 0, O_T = O_K + 2 * KT::BYTES, O_V = O_T + 2 * TT::BYTES, O_E = O_V + 2 * VT::BYTES;
-  __shared__ __align__(1024) char smem[O_E + 5 * DV * 4];
+  // Per stage also, for the diagonal block of the wave whose block it is, the
+  // key block's V relative to the token before it and the same block's
+  // block-relative dhat rows (bf16 hi, lo each).
+  constexpr int O_BH = O_E + 5 * DV * 4, O_BL = O_BH + 2 * VT::BYTES, O_XH = O_BL + 2 * VT::BYTES;
+  constexpr int O_XL = O_XH + 2 * VT::BYTES;
+  __shared__ __align__(1024) char smem[O_XL + 2 * VT::BYTES];
+  auto BHs = [&](int b) { return smem + O_BH + b * VT::BYTES; };
+  auto BLs = [&](int b) { return smem + O_BL + b * VT::BYTES; };
+  auto XHs = [&](int b) { return smem + O_XH + b * VT::BYTES; };
+  auto XLs = [&](int b) { return smem + O_XL + b * VT::BYTES; };
   auto Ks = [&](int b) { return smem + O_K + b * KT::BYTES; };
   auto Kts = [&](int b) { return smem + O_T + b * TT::BYTES; };
   auto Vs = [&](int b) { return smem + O_V + b * VT::BYTES; };
@@ -139,40 +151,76 @@ __global__ void __launch_bounds__(256, 1) k_bwd_intra_dq(BwdArgs a) {
 #pragma unroll
   for (int b = 0; b < NBK; ++b) acc[b] = zero16();
 
-  // Off-diagonal key blocks lie wholly before a valid query row: every key is valid.
-  uint32_t ok[KT::NW], ot[TTD::NW], ov[VT::NW];
+  // Key block b is staged with the rows before the sequence end only (the
+  // rest read as zeros): off the diagonal every key is valid, on the diagonal
+  // the keys past the end meet only masked pairs.
+  uint32_t ok[KT::NW], ot[TTD::NW], ov[VT::NW], oxq[VT::NW];
+  VT::lane_offsets(Hq * DV * 2, wave, lane, oxq);
   KT::lane_offsets(Hkv * DK * 2, wave, lane, ok);
   TTD::lane_offsets(CB * 2, wave, lane, ot);
   VT::lane_offsets(Hkv * DV * 2, wave, lane, ov);
   auto stage_tile = [&](int b, int buf) {
     const int kb = c0 + 32 * b;
     const int64_t kr = (st + kb) * Hkv + c;
+    const int nrow = min(32, L - kb);
     if constexpr (!F32IN) {
-      KT::dma(Ks(buf), make_rsrc((const uint16_t *)a.k + kr * DK, (int64_t)32 * Hkv * DK * 2), ok, wave);
+      const u32x4 rk = rsrc_words((const uint16_t *)a.k + kr * DK, (int64_t)nrow * Hkv * DK * 2);
+#pragma unroll
+      for (int t = 0; t < KT::NW; ++t) KT::dma_piece_untracked(Ks(buf), rk, ok, t, wave);
     } else {
       for (int p = tid; p < KT::NCH; p += 256) {
         const int r = p / KT::CPR, cc = p % KT::CPR;
-        *(f16x8 *)(Ks(buf) + KT::off(r, cc)) = IF::load(a.k, ((st + kb + r) * Hkv + c) * DK + 8 * cc);
+        *(f16x8 *)(Ks(buf) + KT::off(r, cc)) = IF::load(a.k, ((st + min(kb + r, L - 1)) * Hkv + c) * DK + 8 * cc);
       }
     }
-    TTD::dma(Kts(buf), make_rsrc(a.Kt + ((int64_t)gc * Hkv + c) * DK * CB + 32 * b, (int64_t)DK * CB * 2), ot, wave);
-    VT::dma(Vs(buf), make_rsrc(a.VE + kr * DV, (int64_t)32 * Hkv * DV * 2), ov, wave);
+    const u32x4 rt = rsrc_words(a.Kt + ((int64_t)gc * Hkv + c) * DK * CB + 32 * b, (int64_t)DK * CB * 2);
+#pragma unroll
+    for (int t = 0; t < TTD::NW; ++t) TTD::dma_piece_untracked(Kts(buf), rt, ot, t, wave);
+    const u32x4 rv = rsrc_words(a.VE + kr * DV, (int64_t)nrow * Hkv * DV * 2);
+    const u32x4 rbh = rsrc_words(a.VBH + kr * DV, (int64_t)nrow * Hkv * DV * 2);
+    const u32x4 rbl = rsrc_words(a.VBL + kr * DV, (int64_t)nrow * Hkv * DV * 2);
+    const int64_t xq = ((st + kb) * Hq + hq) * DV;  // query block b = key block b
+    const u32x4 rxh = rsrc_words(a.XH + xq, (int64_t)nrow * Hq * DV * 2);
+    const u32x4 rxl = rsrc_words(a.XL + xq, (int64_t)nrow * Hq * DV * 2);
+#pragma unroll
+    for (int t = 0; t < VT::NW; ++t) {
+      VT::dma_piece_untracked(Vs(buf), rv, ov, t, wave);
+      VT::dma_piece_untracked(BHs(buf), rbh, ov, t, wave);
+      VT::dma_piece_untracked(BLs(buf), rbl, ov, t, wave);
+      VT::dma_piece_untracked(XHs(buf), rxh, oxq, t, wave);
+      VT::dma_piece_untracked(XLs(buf), rxl, oxq, t, wave);
+    }
   };
 
-  // Off-diagonal key blocks b < wave through LDS; block nblk - 1 is only
-  // ever diagonal, so it is not staged.
-  const int nsteps = nblk - 1;
+  // Key blocks b <= wave through LDS: the blocks before the wave's own, then
+  // (at b = wave) its diagonal block, unless that block's gate range needs
+  // exact per-pair decays (then it is done afterwards from global memory).
+  const int nsteps = nblk;
+  wait_all();  // every load above is complete before the first untracked copy
   if (nsteps > 0) stage_tile(0, 0);
   wait_all();
   __syncthreads();
+  bool direct;
+  {
+    float rng = 0.f;
+#pragma unroll
+    for (int i = 0; i < NSV; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int d = 16 * i + 8 * hh + e;
+        rng = fmaxf(rng, BE[wave][d] - BE[wave + 1][d]);
+      }
+    direct = __any(rng > BGUARD);
+  }
   for (int b = 0; b < nsteps; ++b) {
     const int buf = b & 1;
-    const bool act = active && wave > b;
+    const bool diag = wave == b;
+    const bool act = active && (wave > b || (diag && !direct));
     // gamma_ab (an LDS table) is applied before the next copies are issued:
     // LDS reads that follow a copy issue in the same step can make the
     // compiler wait for it.
     f16x8 xg[NSV];
-    if (act) {
+    if (act && !diag) {
 #pragma unroll
       for (int i = 0; i < NSV; ++i)
 #pragma unroll
@@ -187,13 +235,34 @@ __global__ void __launch_bounds__(256, 1) k_bwd_intra_dq(BwdArgs a) {
       f32x16 sc = zero16(), dp = zero16();
 #pragma unroll
       for (int i = 0; i < NS; ++i) sc = mma32(*(const kfrag *)(Ks(buf) + KT::off(n, 2 * i + hh)), qf[i], sc);
-#pragma unroll
-      for (int i = 0; i < NSV; ++i) dp = mma32(*(const f16x8 *)(Vs(buf) + VT::off(n, 2 * i + hh)), xg[i], dp);
       f16x8 dsf[2];
+      if (diag) {
+        // split at the token before the block: V and dhat as bf16 hi / lo (bf16x3)
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+        for (int i = 0; i < NSV; ++i) {
+          const bf16x8 vh = *(const bf16x8 *)(BHs(buf) + VT::off(n, 2 * i + hh));
+          const bf16x8 vl = *(const bf16x8 *)(BLs(buf) + VT::off(n, 2 * i + hh));
+          const bf16x8 xh = *(const bf16x8 *)(XHs(buf) + VT::off(n, 2 * i + hh));
+          const bf16x8 xl = *(const bf16x8 *)(XLs(buf) + VT::off(n, 2 * i + hh));
+          dp = mma32(vh, xh, dp);
+          dp = mma32(vh, xl, dp);
+          dp = mma32(vl, xh, dp);
+        }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) dsf[u][i] = (_Float16)(fast_exp2(sc[8 * u + i] * sl2 - mbn) * dp[8 * u + i]);
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int j = 8 * u + i;
+            dsf[u][i] = (_Float16)(acc_row(hh, j) > n ? 0.f : fast_exp2(sc[j] * sl2 - mbn) * dp[j]);
+          }
+      } else {
+#pragma unroll
+        for (int i = 0; i < NSV; ++i) dp = mma32(*(const f16x8 *)(Vs(buf) + VT::off(n, 2 * i + hh)), xg[i], dp);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) dsf[u][i] = (_Float16)(fast_exp2(sc[8 * u + i] * sl2 - mbn) * dp[8 * u + i]);
+      }
 #pragma unroll
       for (int bk = 0; bk < NBK; ++bk)
 #pragma unroll
@@ -204,9 +273,9 @@ __global__ void __launch_bounds__(256, 1) k_bwd_intra_dq(BwdArgs a) {
     __syncthreads();
   }
   if (!active) return;
-  // Diagonal block, per wave from global memory (L2): keys kb .. kb + 31 of
-  // the wave's own block, split at the token before it (bf16x3).
-  {
+  // Diagonal block with exact per-pair decays (gate range beyond 2^BGUARD),
+  // per wave from global memory; the staged loop did the others.
+  if (direct) {
     const int kb = r0;
     const int key = min(kb + n, L - 1);
     float rng = 0.f;

@@ -22,6 +22,11 @@
 
 namespace fix {
 
+// Two 16-bit values packed into one 32-bit word (element 0 in the low half).
+template <class T> __device__ inline uint32_t pack2(const T (&x)[2]) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, x[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, x[1]) << 16);
+}
+
 // Gl2 (log2 units, 128-chunk local), Gam per 128-chunk, row-major fp16 V
 // scaled to its chunk end, Vr[chunk][kvh][t][d] = exp(Gl_end - Gl_t) v_t, V
 // scaled to the end of its 32-token block, VE[t][kvh][d] (the block end
@@ -29,16 +34,18 @@ namespace fix {
 // 32-token block, VB = exp(Gl_blockstart-1 - Gl_t) v_t (>= |v_t|, fp32 range)
 // as bf16 hi / lo parts, the key operand of the diagonal blocks.
 template <int DV, bool LOGITS>
-__global__ void __launch_bounds__(8 * DV) k_gate_prep_rows(const float *__restrict__ g, const void *__restrict__ v,
+__global__ void __launch_bounds__(4 * DV) k_gate_prep_rows(const float *__restrict__ g, const void *__restrict__ v,
                                                            bool in_f32, Plan plan, int Hkv, float *__restrict__ Gl2,
                                                            float *__restrict__ Gam, _Float16 *__restrict__ Vr,
                                                            _Float16 *__restrict__ VE, __bf16 *__restrict__ VBH,
                                                            __bf16 *__restrict__ VBL) {
-  // Thread (blk, d): channel d of the chunk's 16-token piece blk.  Each piece's
-  // local prefix sums, then the totals of the pieces before it (through LDS).
-  constexpr int NP = CB / 16;
+  // Thread (blk, d): channels d, d + 1 of the chunk's 16-token piece blk (two
+  // channels per thread: every load and store moves 8 or 4 bytes per lane).
+  // Each piece's local prefix sums, then the totals of the pieces before it
+  // (through LDS).
+  constexpr int NP = CB / 16, TPP = DV / 2;
   __shared__ float tot[NP][DV];
-  const int gc = blockIdx.x, c = blockIdx.y, d = threadIdx.x % DV, blk = threadIdx.x / DV;
+  const int gc = blockIdx.x, c = blockIdx.y, d = 2 * (threadIdx.x % TPP), blk = threadIdx.x / TPP;
   if (gc >= plan.counts[0]) return;
   const int s = seq_of_chunk(plan.cb128, plan.nseq, gc);
   const int t0 = (gc - plan.cb128[s]) * CB;
@@ -46,55 +53,85 @@ __global__ void __launch_bounds__(8 * DV) k_gate_prep_rows(const float *__restri
   const int64_t tok0 = (int64_t)plan.seq_start[s] + t0;
   const int j0 = 16 * blk;
   // every load of the piece first (rows past the end repeat the last row, unused)
-  float gl[16], vv[16];
+  float gl[16][2], vv[16][2];
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const int64_t idx = ((tok0 + min(j0 + j, n - 1)) * Hkv + c) * DV + d;
-    gl[j] = g[idx];
-    vv[j] = load_in(v, idx, in_f32);
+    const float2 g2 = *(const float2 *)(g + idx);
+    gl[j][0] = g2.x;
+    gl[j][1] = g2.y;
+    if (in_f32) {
+      const float2 v2 = *(const float2 *)((const float *)v + idx);
+      vv[j][0] = v2.x;
+      vv[j][1] = v2.y;
+    } else {
+      const uint32_t w = *(const uint32_t *)((const uint16_t *)v + idx);
+      vv[j][0] = __uint_as_float(w << 16);
+      vv[j][1] = __uint_as_float(w & 0xffff0000u);
+    }
   }
   if constexpr (LOGITS)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) gl[j] = log_sigmoid(gl[j]);
-  float acc = 0.f;
+    for (int j = 0; j < 16; ++j)
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    if (j0 + j < n) acc += gl[j] * LOG2E;
-    gl[j] = acc;  // past the end the prefix stops growing
-  }
-  tot[blk][d] = acc;
+      for (int e = 0; e < 2; ++e) gl[j][e] = log_sigmoid(gl[j][e]);
+  float acc[2] = {0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      if (j0 + j < n) acc[e] += gl[j][e] * LOG2E;
+      gl[j][e] = acc[e];  // past the end the prefix stops growing
+    }
+  tot[blk][d] = acc[0];
+  tot[blk][d + 1] = acc[1];
   __syncthreads();
   // totals of the pieces before this one, and of the pieces of this one's
   // 32-token block (for the block end) and of the whole chunk
-  float before = 0.f, all = 0.f, blkend = 0.f, blkstart = 0.f;
+  float before[2], all[2], gbe[2], gbs[2];
 #pragma unroll
-  for (int q = 0; q < NP; ++q) {
-    const float tq = tot[q][d];
-    before += q < blk ? tq : 0.f;
-    blkend += q <= (blk | 1) ? tq : 0.f;
-    blkstart += q < (blk & ~1) ? tq : 0.f;
-    all += tq;
+  for (int e = 0; e < 2; ++e) {
+    float bf = 0.f, al = 0.f, be = 0.f, bs = 0.f;
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
+      const float tq = tot[q][d + e];
+      bf += q < blk ? tq : 0.f;
+      be += q <= (blk | 1) ? tq : 0.f;
+      bs += q < (blk & ~1) ? tq : 0.f;
+      al += tq;
+    }
+    before[e] = bf;
+    all[e] = al;
+    gbe[e] = be - bf;  // 32-token block end (clamped to the sequence end), piece-local
+    gbs[e] = bs - bf;  // the token before the 32-token block, piece-local
   }
   const int64_t cidx = ((int64_t)gc * Hkv + c);
-  if (blk == 0) Gam[cidx * DV + d] = fast_exp2(all);
+  if (blk == 0) *(float2 *)(Gam + cidx * DV + d) = make_float2(fast_exp2(all[0]), fast_exp2(all[1]));
   _Float16 *dst = Vr + cidx * CB * DV + d;
-  const float gbe = blkend - before;  // 32-token block end (clamped to the sequence end), piece-local
-  const float gbs = blkstart - before;  // the token before the 32-token block, piece-local
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const int t = j0 + j;
-    float val = 0.f;
+    _Float16 vr[2] = {(_Float16)0.f, (_Float16)0.f};
     if (t < n) {
       const int64_t idx = ((tok0 + t) * Hkv + c) * DV + d;
-      Gl2[idx] = before + gl[j];
-      val = fast_exp2(all - before - gl[j]) * vv[j];
-      VE[idx] = (_Float16)(fast_exp2(gbe - gl[j]) * vv[j]);
-      const float vb = fast_exp2(gbs - gl[j]) * vv[j];
-      const __bf16 vbh = (__bf16)vb;
-      VBH[idx] = vbh;
-      VBL[idx] = (__bf16)(vb - (float)vbh);
+      float gv[2];
+      _Float16 ve[2];
+      __bf16 bh[2], bl[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        gv[e] = before[e] + gl[j][e];
+        vr[e] = (_Float16)(fast_exp2(all[e] - before[e] - gl[j][e]) * vv[j][e]);
+        ve[e] = (_Float16)(fast_exp2(gbe[e] - gl[j][e]) * vv[j][e]);
+        const float vb = fast_exp2(gbs[e] - gl[j][e]) * vv[j][e];
+        bh[e] = (__bf16)vb;
+        bl[e] = (__bf16)(vb - (float)bh[e]);
+      }
+      *(float2 *)(Gl2 + idx) = make_float2(gv[0], gv[1]);
+      *(uint32_t *)(VE + idx) = pack2(ve);
+      *(uint32_t *)(VBH + idx) = pack2(bh);
+      *(uint32_t *)(VBL + idx) = pack2(bl);
     }
-    dst[(int64_t)t * DV] = (_Float16)val;
+    *(uint32_t *)(dst + (int64_t)t * DV) = pack2(vr);
   }
 }
 
@@ -474,10 +511,10 @@ hipError_t launch_gate_prep_rows(int dv, const float *g, bool logits, const void
                                  __bf16 *VBL, hipStream_t st) {
   dim3 grid(ncb_ub, Hkv);
   if (logits)
-    FIX_DV_SWITCH(dv, hipLaunchKernelGGL((k_gate_prep_rows<DVC, true>), grid, dim3(8 * DVC), 0, st, g, v, in_f32,
+    FIX_DV_SWITCH(dv, hipLaunchKernelGGL((k_gate_prep_rows<DVC, true>), grid, dim3(4 * DVC), 0, st, g, v, in_f32,
                                          plan, Hkv, Gl2, Gam, Vr, VE, VBH, VBL))
   else
-    FIX_DV_SWITCH(dv, hipLaunchKernelGGL((k_gate_prep_rows<DVC, false>), grid, dim3(8 * DVC), 0, st, g, v, in_f32,
+    FIX_DV_SWITCH(dv, hipLaunchKernelGGL((k_gate_prep_rows<DVC, false>), grid, dim3(4 * DVC), 0, st, g, v, in_f32,
                                          plan, Hkv, Gl2, Gam, Vr, VE, VBH, VBL));
   return hipGetLastError();
 }

@@ -159,8 +159,12 @@ __global__ void __launch_bounds__(128) k_chunk_logprefix(const float *__restrict
 template <int D>
 __global__ void __launch_bounds__(256) k_tiles_t(const void *__restrict__ in, bool in_f32, Plan plan, int H,
                                                  _Float16 *__restrict__ out) {
-  constexpr int STR = CB + 8;
-  __shared__ _Float16 tile[D * STR];
+  // LDS tile [d][CB] with the 16-byte chunk index of row d XORed with
+  // (d / 8) % 16: the eight channels one thread stores (rows d8 .. d8 + 7,
+  // one column) and the rows of the threads beside it (d8 + 8, ...) land in
+  // different banks, and the copy-out still reads whole 16-byte chunks.
+  __shared__ __align__(16) _Float16 tile[D * CB];
+  auto at = [](int d, int col) { return d * CB + ((((col >> 3) ^ (d >> 3)) & 15) << 3) + (col & 7); };
   const int gc = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   if (gc >= plan.counts[0]) return;
   const int s = seq_of_chunk(plan.cb128, plan.nseq, gc);
@@ -185,13 +189,13 @@ __global__ void __launch_bounds__(256) k_tiles_t(const void *__restrict__ in, bo
       }
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) tile[(d8 + i) * STR + key_pos(t)] = (_Float16)(t < n ? val[i] : 0.f);
+    for (int i = 0; i < 8; ++i) tile[at(d8 + i, key_pos(t))] = (_Float16)(t < n ? val[i] : 0.f);
   }
   __syncthreads();
   uint4 *dst = (uint4 *)(out + ((int64_t)gc * H + h) * D * CB);
   for (int e = tid; e < D * CB / 8; e += 256) {
     int d = e / (CB / 8), p8 = e % (CB / 8);
-    dst[e] = *(const uint4 *)&tile[d * STR + 8 * p8];
+    dst[e] = *(const uint4 *)&tile[at(d, 8 * p8)];
   }
 }
 

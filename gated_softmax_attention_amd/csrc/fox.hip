@@ -164,14 +164,26 @@ __global__ void __launch_bounds__(256, 2) k_fox_fwd(FoxArgs a) {
     // bias G_row - G_key = (G_row - ref_J) - loc_key
     const float gq = (float)(grow - Rf(b)[0]);
     float mb = -INFINITY;
+    // Only a block that reaches past the wave's first row or the sequence end
+    // needs the causal mask.
+    if (k0 + CH - 1 <= rbase && k0 + CH <= L) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int key = k0 + 32 * h + acc_row(hh, j);
-        sc[h][j] = (key <= row && key < L) ? sc[h][j] * sl2 : -INFINITY;
-        mb = fmaxf(mb, sc[h][j]);
-      }
+        for (int j = 0; j < 16; ++j) {
+          sc[h][j] *= sl2;
+          mb = fmaxf(mb, sc[h][j]);
+        }
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int key = k0 + 32 * h + acc_row(hh, j);
+          sc[h][j] = (key <= row && key < L) ? sc[h][j] * sl2 : -INFINITY;
+          mb = fmaxf(mb, sc[h][j]);
+        }
+    }
     mb = fmaxf(mb, __shfl_xor(mb, 32));
     const float mn = fmaxf(m, mb);
     if (__any(mn > m)) {

@@ -31,7 +31,7 @@ PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16/fp16 MFMA peak (AMD specification
 # a plain-copy calibration (x2.0 reads, x1.0 writes); valid only for the sources they were
 # taken on (sha256 prefix over the files listed, the build flags included).  Reported as roofline.traffic, else null.
 TRAFFIC = {
-    "bwd_dkv": {"bytes": 2 * 1026502 * 1024 + 532313 * 1024, "sha": "73ac43155d216708",
+    "bwd_dkv": {"bytes": 2 * 1024168 * 1024 + 532034 * 1024, "sha": "73ac43155d216708",
                 "files": ["gated_softmax_attention_amd/csrc/bwd_kernel.h",
                           "gated_softmax_attention_amd/csrc/common.h",
                           "gated_softmax_attention_amd/csrc/launch.h",

@@ -36,7 +36,7 @@ TRAFFIC = {
                           "gated_softmax_attention_amd/csrc/common.h",
                           "gated_softmax_attention_amd/csrc/launch.h",
                           "gated_softmax_attention_amd/build.py"]},
-    "decode_step": {"bytes": int(2 * 135701.125 * 1024) + 1040 * 1024, "sha": "4c7ae8d84ece29e7",
+    "decode_step": {"bytes": int(2 * 135696.875 * 1024) + 1040 * 1024, "sha": "4302847cdeed07c0",
                     "files": ["gated_softmax_attention_amd/csrc/decode.hip",
                               "gated_softmax_attention_amd/csrc/common.h",
                               "gated_softmax_attention_amd/csrc/launch.h",

@@ -29,42 +29,101 @@
 namespace fix {
 
 // Appends up to n tokens to every sequence (row b appends the first n_seq[b]
-// rows of its [n, Hkv, d] block, or all n when n_seq is null).  Workgroup =
-// (sequence, kv head); thread i owns channel i of k and of v / g.  Tokens
-// past the capacity are dropped.
+// rows of its [n, Hkv, d] block, or all n when n_seq is null); tokens past
+// the capacity are dropped.  The chunk-local prefix restarts at every chunk,
+// so the chunks an append touches are independent: workgroup (sequence * Hkv
+// + kv head, w) takes the w-th of them, thread i channel i of k and of v / g,
+// its tokens in order.  The chunk's prefixes and values stay in LDS (the ring
+// only holds the chunk left open); a chunk that fills is sealed (its
+// transposed tile, and its total in the Lam slot after it, which
+// k_decode_finish turns into the running prefix).  The ring is written here
+// only when the chunk left open is the first one touched (the same workgroup
+// read its earlier tokens); otherwise k_decode_finish writes it, after every
+// reader of the old ring is done.
 __global__ void __launch_bounds__(128) k_decode_append(DecodeCache dc, const void *__restrict__ k,
                                                        const void *__restrict__ v, const float *__restrict__ g,
                                                        int n, const int *__restrict__ n_seq, bool in_f32,
-                                                       bool logits) {
-  const int b = blockIdx.x, c = blockIdx.y, i = threadIdx.x;
+                                                       bool logits, int nw) {
+  __shared__ float sg[CH][128];      // chunk-local prefixes, [slot][channel]
+  __shared__ _Float16 sv[CH][128];   // values
   const int Hkv = dc.Hkv, dk = dc.dk, dv = dc.dv;
+  const int b = blockIdx.x / Hkv, c = blockIdx.x % Hkv, i = threadIdx.x;
   const int len0 = dc.len[b];
   const int cnt = min(n_seq ? min(max(n_seq[b], 0), n) : n, dc.cap - len0);
   const int nch = dc.cap / CH;
-  for (int u = 0; u < cnt; ++u) {
-    const int t = len0 + u, slot = t % CH;
-    const int64_t src = (((int64_t)b * n + u) * Hkv + c);
-    if (i < dk) dc.K[(((int64_t)b * dc.cap + t) * Hkv + c) * dk + i] = (_Float16)load_in(k, src * dk + i, in_f32);
-    if (i < dv) {
-      const int64_t o = (((int64_t)b * CH + slot) * Hkv + c) * dv + i;
+  for (int w = blockIdx.y; w < nw; w += gridDim.y) {  // each thread only touches its own channel's LDS column
+    const int ch = len0 / CH + w, c0 = ch * CH;
+    const int ta = max(len0, c0), tb = min(len0 + cnt, c0 + CH);  // tokens of this chunk appended now
+    if (ta >= tb) continue;
+    // the chunk's earlier tokens (an open chunk from an earlier append) from the ring
+    float glp = 0.f;
+    if (i < dv)
+      for (int t = c0; t < ta; ++t) {
+        const int64_t o = (((int64_t)b * CH + t % CH) * Hkv + c) * dv + i;
+        glp = dc.Go[o];
+        sg[t % CH][i] = glp;
+        sv[t % CH][i] = dc.Vo[o];
+      }
+    for (int t = ta; t < tb; ++t) {
+      const int slot = t % CH;
+      const int64_t src = (((int64_t)b * n + (t - len0)) * Hkv + c);
+      if (i < dk) dc.K[(((int64_t)b * dc.cap + t) * Hkv + c) * dk + i] = (_Float16)load_in(k, src * dk + i, in_f32);
+      if (i < dv) {
+        float gv = g[src * dv + i];
+        if (logits) gv = log_sigmoid(gv);
+        glp += gv * LOG2E;
+        sg[slot][i] = glp;
+        sv[slot][i] = (_Float16)load_in(v, src * dv + i, in_f32);
+      }
+    }
+    if (i >= dv) continue;
+    if (tb == c0 + CH) {  // the chunk is full: seal it
+      _Float16 row[CH];
+      for (int j = 0; j < CH; ++j) row[key_pos(j)] = (_Float16)(fast_exp2(glp - sg[j][i]) * (float)sv[j][i]);
+      uint4 *dst = (uint4 *)(dc.VT + ((((int64_t)b * nch + ch) * Hkv + c) * dv + i) * CH);
+      for (int p = 0; p < CH / 8; ++p) dst[p] = *(const uint4 *)(row + 8 * p);
+      dc.Lam[(((int64_t)b * (nch + 1) + ch + 1) * Hkv + c) * dv + i] = (double)glp;  // the chunk total, for now
+    } else if (w == 0) {  // it stays open: its new tokens go to the ring
+      for (int t = ta; t < tb; ++t) {
+        const int64_t o = (((int64_t)b * CH + t % CH) * Hkv + c) * dv + i;
+        dc.Go[o] = sg[t % CH][i];
+        dc.Vo[o] = sv[t % CH][i];
+      }
+    }
+  }
+}
+
+// After k_decode_append: Lam after every chunk it sealed (the slot holds the
+// chunk total, added to the prefix before it, chunk after chunk, fp64), and
+// the ring of a chunk left open that started in this append (its prefixes
+// recomputed from the inputs, as the append computes them).  Before the new
+// lengths are written (it reads the old ones).
+__global__ void __launch_bounds__(128) k_decode_finish(DecodeCache dc, const void *__restrict__ v,
+                                                       const float *__restrict__ g, int n,
+                                                       const int *__restrict__ n_seq, bool in_f32, bool logits) {
+  const int Hkv = dc.Hkv, dv = dc.dv, nch = dc.cap / CH;
+  const int b = blockIdx.x / Hkv, c = blockIdx.x % Hkv, i = threadIdx.x;
+  if (i >= dv) return;
+  const int len0 = dc.len[b];
+  const int cnt = min(n_seq ? min(max(n_seq[b], 0), n) : n, dc.cap - len0);
+  double run = 0.0;
+  for (int ch = len0 / CH; ch < (len0 + cnt) / CH; ++ch) {
+    const int64_t l = (((int64_t)b * (nch + 1) + ch) * Hkv + c) * dv + i;
+    if (ch == len0 / CH) run = dc.Lam[l];
+    run += dc.Lam[l + (int64_t)Hkv * dv];
+    dc.Lam[l + (int64_t)Hkv * dv] = run;
+  }
+  const int end = len0 + cnt, c0 = end / CH * CH;
+  if (end % CH != 0 && c0 > len0) {
+    float glp = 0.f;
+    for (int t = c0; t < end; ++t) {
+      const int64_t src = (((int64_t)b * n + (t - len0)) * Hkv + c);
       float gv = g[src * dv + i];
       if (logits) gv = log_sigmoid(gv);
-      const float prev = slot == 0 ? 0.f : dc.Go[o - (int64_t)Hkv * dv];
-      const float gl = prev + gv * LOG2E;
-      dc.Go[o] = gl;
+      glp += gv * LOG2E;
+      const int64_t o = (((int64_t)b * CH + t % CH) * Hkv + c) * dv + i;
+      dc.Go[o] = glp;
       dc.Vo[o] = (_Float16)load_in(v, src * dv + i, in_f32);
-      if (slot == CH - 1) {  // the chunk is full: seal it
-        const int n_ = t / CH;
-        _Float16 row[CH];
-        for (int j = 0; j < CH; ++j) {
-          const int64_t oj = (((int64_t)b * CH + j) * Hkv + c) * dv + i;
-          row[key_pos(j)] = (_Float16)(fast_exp2(gl - dc.Go[oj]) * (float)dc.Vo[oj]);
-        }
-        uint4 *dst = (uint4 *)(dc.VT + ((((int64_t)b * nch + n_) * Hkv + c) * dv + i) * CH);
-        for (int p = 0; p < CH / 8; ++p) dst[p] = *(const uint4 *)(row + 8 * p);
-        const int64_t l0 = (((int64_t)b * (nch + 1) + n_) * Hkv + c) * dv + i;
-        dc.Lam[l0 + (int64_t)Hkv * dv] = dc.Lam[l0] + (double)gl;
-      }
     }
   }
 }
@@ -288,8 +347,15 @@ hipError_t launch_decode_reset(const DecodeCache &dc, hipStream_t st) {
 
 hipError_t launch_decode_append(const DecodeCache &dc, const void *k, const void *v, const float *g, int n,
                                 const int *n_seq, bool in_f32, bool logits, hipStream_t st) {
-  hipLaunchKernelGGL(k_decode_append, dim3(dc.B, dc.Hkv), dim3(128), 0, st, dc, k, v, g, n, n_seq, in_f32, logits);
+  if (n <= 0) return hipSuccess;
+  // chunks an append of up to n tokens can touch: an open chunk, then n more tokens
+  const int nw = (CH - 1 + n + CH - 1) / CH;
+  hipLaunchKernelGGL(k_decode_append, dim3(dc.B * dc.Hkv, min(nw, 65535)), dim3(128), 0, st, dc, k, v, g, n, n_seq,
+                     in_f32, logits, nw);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_decode_finish, dim3(dc.B * dc.Hkv), dim3(128), 0, st, dc, v, g, n, n_seq, in_f32, logits);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_decode_len, dim3((dc.B + 63) / 64), dim3(64), 0, st, dc, n, n_seq);
   return hipGetLastError();

@@ -240,13 +240,15 @@ template <class T> __device__ inline void store8h(T *p, int64_t idx, const T (&v
 // in turn.  A thread owns eight consecutive channels of a token row (16-byte
 // loads and stores; DV / 8 threads per row, row reductions by lane shuffles
 // inside that group).  The transposed tiles are built in LDS one 32-token
-// segment at a time and written out as 16-byte row pieces.
+// segment at a time and written out as 16-byte row pieces.  All of a thread's
+// rows of a segment are loaded before the first of them is computed.
 template <int DV>
 __global__ void __launch_bounds__(256) k_bwd_prep(PrepArgs a) {
   constexpr int TPR = DV / 8;        // threads per token row
   constexpr int RPP = 256 / TPR;     // rows per pass of the workgroup
   constexpr int SEG = 32;            // tokens per tile segment
   constexpr int STR = SEG + 8;       // LDS tile row stride (elements; rows 16-byte aligned)
+  constexpr int NR = SEG / RPP > 0 ? SEG / RPP : 1;  // rows of a segment per thread
   constexpr int TILE = DV * STR * 2, RED = RPP * DV * 4;
   __shared__ __align__(16) char smem[2 * TILE > RED ? 2 * TILE : RED];
   __bf16 *tileh = (__bf16 *)smem, *tilel = (__bf16 *)(smem + TILE);
@@ -272,96 +274,103 @@ __global__ void __launch_bounds__(256) k_bwd_prep(PrepArgs a) {
   for (int gq = 0; gq < G; ++gq) {
     const int h = c * G + gq;
     for (int hf = 0; hf < CB / SEG; ++hf) {
-#pragma unroll 1
-      for (int r = rr; r < SEG; r += RPP) {
-        const int t = SEG * hf + r;  // token within the chunk
-        const int tc = min(t, n - 1);  // rows past the end repeat the last (nothing stored)
-        const int64_t tok = tok0 + tc;
-        const int64_t rb = (tok * Hq + h) * DV + d0, gi = (tok * Hkv + c) * DV + d0;
-        // every input of the row first (see the note on stores below)
-        float xv[8], go[8], zz[8], gl[8], gbs[8], qo[8];
-        load8f(a.x, rb, xv);
-        load8(a.dO, rb, in_f32, go);
-        if (a.z) load8(a.z, rb, in_f32, zz);
-        load8f(a.Gl2, gi, gl);
-        if (tc & ~31) load8f(a.Gl2, ((tok0 + (tc & ~31) - 1) * Hkv + c) * DV + d0, gbs);
-        if (gq > 0) load8f(a.qside, gi, qo);
-        const float rs = a.rstd[tok * Hq + h], mrow = a.m[tok * Hq + h];
-        if (!a.z)
+      if (rr < SEG) {
+        // every input of the thread's rows first, then each row's arithmetic and
+        // outputs (the compiler cannot tell the buffers apart, so a load placed
+        // after a store would wait for it)
+        float xv[NR][8], go[NR][8], zz[NR][8], gl[NR][8], gbs[NR][8], qo[NR][8], rs[NR], mrow[NR];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) zz[i] = 1.f;
-        if (!(tc & ~31))
+        for (int k = 0; k < NR; ++k) {
+          const int tc = min(SEG * hf + rr + k * RPP, n - 1);  // rows past the end repeat the last (nothing stored)
+          const int64_t tok = tok0 + tc;
+          const int64_t rb = (tok * Hq + h) * DV + d0, gi = (tok * Hkv + c) * DV + d0;
+          load8f(a.x, rb, xv[k]);
+          load8(a.dO, rb, in_f32, go[k]);
+          if (a.z) load8(a.z, rb, in_f32, zz[k]);
+          else
 #pragma unroll
-          for (int i = 0; i < 8; ++i) gbs[i] = 0.f;
-        if (gq == 0)
+            for (int i = 0; i < 8; ++i) zz[k][i] = 1.f;
+          load8f(a.Gl2, gi, gl[k]);
+          if (tc & ~31) load8f(a.Gl2, ((tok0 + (tc & ~31) - 1) * Hkv + c) * DV + d0, gbs[k]);
+          else
 #pragma unroll
-          for (int i = 0; i < 8; ++i) qo[i] = 0.f;
-
-        float dn[8], nval[8], proj = 0.f;
+            for (int i = 0; i < 8; ++i) gbs[k][i] = 0.f;
+          if (gq > 0) load8f(a.qside, gi, qo[k]);
+          else
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          dn[i] = go[i] * zz[i];
-          nval[i] = o_norm ? xv[i] * rs * wv[i] : xv[i];
-          proj += dn[i] * wv[i] * xv[i] * rs;
-        }
-        if (o_norm) {
-#pragma unroll
-          for (int off = TPR / 2; off > 0; off >>= 1) proj += __shfl_xor(proj, off);
-          proj *= 1.f / DV;
-        }
-        // sigma = 2^-e scales the row so that max |sigma delta| is about 1; every
-        // fp16 operand built from the row (exp(Gl) sigma delta, within a block
-        // exp(Gl_i - Gl_ref) sigma delta, all factors <= 1) stays in range
-        float del[8], amax = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          del[i] = o_norm ? rs * (dn[i] * wv[i] - xv[i] * rs * proj) : dn[i];
-          amax = fmaxf(amax, fabsf(del[i]));
+            for (int i = 0; i < 8; ++i) qo[k][i] = 0.f;
+          rs[k] = a.rstd[tok * Hq + h];
+          mrow[k] = a.m[tok * Hq + h];
         }
 #pragma unroll
-        for (int off = TPR / 2; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-        int e = 0;
-        if (amax > 0.f) e = min(15, max(-15, (int)ceilf(__log2f(amax))));
-        const float sg = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e
-        _Float16 hv[8], x16[8];
-        __bf16 xh[8], xl[8];
-        float qs[8], dzv[8];
+        for (int k = 0; k < NR; ++k) {
+          const int r = rr + k * RPP, t = SEG * hf + r;  // token within the chunk
+          const int64_t tok = tok0 + min(t, n - 1);
+          const int64_t rb = (tok * Hq + h) * DV + d0, gi = (tok * Hkv + c) * DV + d0;
+          float dn[8], nval[8], proj = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          // query side of dG, summed over the group ((token, channel) is owned by
-          // this thread for every head of the group)
-          qs[i] = qo[i] + del[i] * xv[i];
-          dzv[i] = go[i] * nval[i];
-          hv[i] = (_Float16)(fast_exp2(gl[i]) * del[i] * sg);
-          // relative to the token before the row's 32-token block (<= 1)
-          const float xb = fast_exp2(gl[i] - gbs[i]) * del[i] * sg;
-          x16[i] = (_Float16)xb;
-          xh[i] = (__bf16)xb;
-          xl[i] = (__bf16)(xb - (float)xh[i]);
-        }
-        const bool valid = t < n;
-        const int pos = key_pos(r);
+          for (int i = 0; i < 8; ++i) {
+            dn[i] = go[k][i] * zz[k][i];
+            nval[i] = o_norm ? xv[k][i] * rs[k] * wv[i] : xv[k][i];
+            proj += dn[i] * wv[i] * xv[k][i] * rs[k];
+          }
+          if (o_norm) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          tileh[(d0 + i) * STR + pos] = valid ? xh[i] : (__bf16)0.f;
-          tilel[(d0 + i) * STR + pos] = valid ? xl[i] : (__bf16)0.f;
-        }
-        if (valid) {
-          if (o_norm)
+            for (int off = TPR / 2; off > 0; off >>= 1) proj += __shfl_xor(proj, off);
+            proj *= 1.f / DV;
+          }
+          // sigma = 2^-e scales the row so that max |sigma delta| is about 1; every
+          // fp16 operand built from the row (exp(Gl) sigma delta, within a block
+          // exp(Gl_i - Gl_ref) sigma delta, all factors <= 1) stays in range
+          float del[8], amax = 0.f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) dwacc[i] += dn[i] * xv[i] * rs;
-          // The row's outputs after all of its inputs: the compiler cannot tell
-          // the buffers apart, so a load placed after a store would wait for it.
-          if (a.dz) store8(a.dz, rb, dzv, a.out_f32);
-          store8f(a.delta, rb, del);
-          store8f(a.qside, gi, qs);
-          store8h(a.dh, rb, hv);
-          store8h(a.X16, rb, x16);
-          store8h(a.XH, rb, xh);
-          store8h(a.XL, rb, xl);
-          if (sub == 0) {
-            a.mb[tok * Hq + h] = mrow * LOG2E - (float)e;
-            a.sig[tok * Hq + h] = sg;
+          for (int i = 0; i < 8; ++i) {
+            del[i] = o_norm ? rs[k] * (dn[i] * wv[i] - xv[k][i] * rs[k] * proj) : dn[i];
+            amax = fmaxf(amax, fabsf(del[i]));
+          }
+#pragma unroll
+          for (int off = TPR / 2; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+          int e = 0;
+          if (amax > 0.f) e = min(15, max(-15, (int)ceilf(__log2f(amax))));
+          const float sg = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e
+          _Float16 hv[8], x16[8];
+          __bf16 xh[8], xl[8];
+          float qs[8], dzv[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            // query side of dG, summed over the group ((token, channel) is owned by
+            // this thread for every head of the group)
+            qs[i] = qo[k][i] + del[i] * xv[k][i];
+            dzv[i] = go[k][i] * nval[i];
+            hv[i] = (_Float16)(fast_exp2(gl[k][i]) * del[i] * sg);
+            // relative to the token before the row's 32-token block (<= 1)
+            const float xb = fast_exp2(gl[k][i] - gbs[k][i]) * del[i] * sg;
+            x16[i] = (_Float16)xb;
+            xh[i] = (__bf16)xb;
+            xl[i] = (__bf16)(xb - (float)xh[i]);
+          }
+          const bool valid = t < n;
+          const int pos = key_pos(r);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            tileh[(d0 + i) * STR + pos] = valid ? xh[i] : (__bf16)0.f;
+            tilel[(d0 + i) * STR + pos] = valid ? xl[i] : (__bf16)0.f;
+          }
+          if (valid) {
+            if (o_norm)
+#pragma unroll
+              for (int i = 0; i < 8; ++i) dwacc[i] += dn[i] * xv[k][i] * rs[k];
+            if (a.dz) store8(a.dz, rb, dzv, a.out_f32);
+            store8f(a.delta, rb, del);
+            store8f(a.qside, gi, qs);
+            store8h(a.dh, rb, hv);
+            store8h(a.X16, rb, x16);
+            store8h(a.XH, rb, xh);
+            store8h(a.XL, rb, xl);
+            if (sub == 0) {
+              a.mb[tok * Hq + h] = mrow[k] * LOG2E - (float)e;
+              a.sig[tok * Hq + h] = sg;
+            }
           }
         }
       }

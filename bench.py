@@ -31,12 +31,12 @@ PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16/fp16 MFMA peak (AMD specification
 # a plain-copy calibration (x2.0 reads, x1.0 writes); valid only for the sources they were
 # taken on (sha256 prefix over the files listed, the build flags included).  Reported as roofline.traffic, else null.
 TRAFFIC = {
-    "bwd_dkv": {"bytes": 2 * 1024168 * 1024 + 532034 * 1024, "sha": "73ac43155d216708",
+    "bwd_dkv": {"bytes": 2 * 1023348 * 1024 + 531964 * 1024, "sha": "73ac43155d216708",
                 "files": ["gated_softmax_attention_amd/csrc/bwd_kernel.h",
                           "gated_softmax_attention_amd/csrc/common.h",
                           "gated_softmax_attention_amd/csrc/launch.h",
                           "gated_softmax_attention_amd/build.py"]},
-    "decode_step": {"bytes": int(2 * 135696.875 * 1024) + 1040 * 1024, "sha": "4302847cdeed07c0",
+    "decode_step": {"bytes": int(2 * 135786.8125 * 1024) + 1040 * 1024, "sha": "57a171f043b4aa06",
                     "files": ["gated_softmax_attention_amd/csrc/decode.hip",
                               "gated_softmax_attention_amd/csrc/common.h",
                               "gated_softmax_attention_amd/csrc/launch.h",

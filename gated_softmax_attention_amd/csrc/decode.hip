@@ -15,7 +15,7 @@
 //
 // Cache layout (one caller buffer, carved in this order, 256-byte aligned):
 //   len  [B]                      int32   tokens held per sequence
-//   K    [B, cap, Hkv, dk]        fp16    keys
+//   K    [B, Hkv, cap, dk]        fp16    keys (a chunk's keys of one head contiguous)
 //   VT   [B, cap/64, Hkv, dv, 64] fp16    closed chunks: V scaled to the chunk
 //                                         end, transposed, keys in key_pos order
 //   Vo   [B, 64, Hkv, dv]         fp16    the open chunk's values (slot t % 64)
@@ -67,7 +67,7 @@ __global__ void __launch_bounds__(128) k_decode_append(DecodeCache dc, const voi
     for (int t = ta; t < tb; ++t) {
       const int slot = t % CH;
       const int64_t src = (((int64_t)b * n + (t - len0)) * Hkv + c);
-      if (i < dk) dc.K[(((int64_t)b * dc.cap + t) * Hkv + c) * dk + i] = (_Float16)load_in(k, src * dk + i, in_f32);
+      if (i < dk) dc.K[(((int64_t)b * Hkv + c) * dc.cap + t) * dk + i] = (_Float16)load_in(k, src * dk + i, in_f32);
       if (i < dv) {
         float gv = g[src * dv + i];
         if (logits) gv = log_sigmoid(gv);
@@ -215,7 +215,7 @@ __global__ void __launch_bounds__(256, 2) k_decode_step(DecodeCache dc, const vo
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int key = t0 + 32 * h + n;
-      const _Float16 *kr = dc.K + (((int64_t)b * dc.cap + min(key, t)) * Hkv + c) * DK;
+      const _Float16 *kr = dc.K + (((int64_t)b * Hkv + c) * dc.cap + min(key, t)) * DK;
       sc[h] = zero16();
 #pragma unroll
       for (int i = 0; i < NS; ++i) sc[h] = mma32(*(const f16x8 *)(kr + 16 * i + 8 * hh), qf[i], sc[h]);

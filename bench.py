@@ -36,7 +36,7 @@ TRAFFIC = {
                           "gated_softmax_attention_amd/csrc/common.h",
                           "gated_softmax_attention_amd/csrc/launch.h",
                           "gated_softmax_attention_amd/build.py"]},
-    "decode_step": {"bytes": int(2 * 135786.8125 * 1024) + 1040 * 1024, "sha": "57a171f043b4aa06",
+    "decode_step": {"bytes": int(2 * 135774.125 * 1024) + 1040 * 1024, "sha": "ca18dcf888947a22",
                     "files": ["gated_softmax_attention_amd/csrc/decode.hip",
                               "gated_softmax_attention_amd/csrc/common.h",
                               "gated_softmax_attention_amd/csrc/launch.h",

@@ -284,53 +284,58 @@ __global__ void __launch_bounds__(256, 2) k_decode_step(DecodeCache dc, const vo
 }
 
 // Combines the units of one (sequence, query head) and applies the output
-// transform.  Block = max(DV, 64) threads (thread d: channel d).
+// transform.  Block = 4 groups of max(DV, 64) threads (thread d of a group:
+// channel d); group j sums units j, j + 4, ..., and the four sums are added
+// in LDS in a fixed order.
 template <int DV>
-__global__ void __launch_bounds__(128) k_decode_combine(DecodeCache dc, int units, const float *__restrict__ part,
+__global__ void __launch_bounds__(512) k_decode_combine(DecodeCache dc, int units, const float *__restrict__ part,
                                                         const float *__restrict__ mpart, const void *__restrict__ w,
                                                         const void *__restrict__ z, bool in_f32, bool out_f32,
                                                         bool o_norm, float eps, void *__restrict__ o,
                                                         float *__restrict__ m_out) {
+  constexpr int DW = DV < 64 ? 64 : DV, NG = 4, NT = NG * DW, NW = NT / 64;
   const int bh = blockIdx.x, b = bh / dc.Hq, h = bh % dc.Hq, G = dc.G, c = h / G, r = h % G;
-  const int dd = threadIdx.x, d = min(dd, DV - 1);  // at least 64 threads: lanes >= DV add nothing
+  const int tid = threadIdx.x, gq = tid / DW, dd = tid % DW, d = min(dd, DV - 1);  // lanes dd >= DV add nothing
   const int64_t bc = (int64_t)b * dc.Hkv + c;
-  // the units' row maxima into LDS (units <= 256), their maximum by shuffles
+  // the units' row maxima into LDS (units <= 256), their maximum over the block
   __shared__ float mu_s[256];
-  __shared__ float red[2];
-  const int nthr = blockDim.x;
+  __shared__ float red[NW];
+  __shared__ float xs[NG][DW];
   float m = -INFINITY;
-  for (int u = dd; u < units; u += nthr) {
+  for (int u = tid; u < units; u += NT) {
     const float mu = mpart[(bc * units + u) * G + r];
     mu_s[u] = mu;
     m = fmaxf(m, mu);
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  if (nthr > 64) {
-    if ((dd & 63) == 0) red[dd >> 6] = m;
-    __syncthreads();
-    m = fmaxf(red[0], red[1]);
-    __syncthreads();
-  } else {
-    __syncthreads();
-  }
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  m = red[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) m = fmaxf(m, red[i]);
+  __syncthreads();  // red is reused below
   float x = 0.f;
 #pragma unroll 8
-  for (int u = 0; u < units; ++u) {
+  for (int u = gq; u < units; u += NG) {
     const float mu = mu_s[u];
     const float pv = part[((bc * units + u) * G + r) * DV + d];
     if (mu != -INFINITY) x += fast_exp2(mu - m) * pv;
   }
-  // RMSNorm over the DV channels (one wave per 64 channels, LDS across waves)
-  float ss = dd < DV ? x * x : 0.f;
+  xs[gq][dd] = x;
+  __syncthreads();
+  x = ((xs[0][dd] + xs[1][dd]) + xs[2][dd]) + xs[3][dd];
+  // RMSNorm over the DV channels of group 0 (every thread takes part in the
+  // reductions and barriers; only group 0 writes)
+  float ss = gq == 0 && dd < DV ? x * x : 0.f;
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
-  if (DV > 64) {
-    if ((dd & 63) == 0) red[dd >> 6] = ss;
-    __syncthreads();
-    ss = red[0] + red[1];
-  }
-  if (dd >= DV) return;
+  if ((tid & 63) == 0) red[tid >> 6] = ss;
+  __syncthreads();
+  ss = red[0];
+#pragma unroll
+  for (int i = 1; i < DW / 64; ++i) ss += red[i];
+  if (gq != 0 || dd >= DV) return;
   const float rs = rsqrtf(ss / DV + eps);
   float y = x;
   if (o_norm) y = x * rs * (w ? load_in(w, d, in_f32) : 1.f);
@@ -401,10 +406,10 @@ hipError_t launch_decode_combine(const DecodeCache &dc, int units, const float *
                                  void *o, float *m, hipStream_t st) {
   const dim3 grid(dc.B * dc.Hq);
   switch (dc.dv) {
-    case 16: hipLaunchKernelGGL((k_decode_combine<16>), grid, dim3(64), 0, st, dc, units, part, mpart, w, z, in_f32, out_f32, o_norm, eps, o, m); break;
-    case 32: hipLaunchKernelGGL((k_decode_combine<32>), grid, dim3(64), 0, st, dc, units, part, mpart, w, z, in_f32, out_f32, o_norm, eps, o, m); break;
-    case 64: hipLaunchKernelGGL((k_decode_combine<64>), grid, dim3(64), 0, st, dc, units, part, mpart, w, z, in_f32, out_f32, o_norm, eps, o, m); break;
-    case 128: hipLaunchKernelGGL((k_decode_combine<128>), grid, dim3(128), 0, st, dc, units, part, mpart, w, z, in_f32, out_f32, o_norm, eps, o, m); break;
+    case 16: hipLaunchKernelGGL((k_decode_combine<16>), grid, dim3(256), 0, st, dc, units, part, mpart, w, z, in_f32, out_f32, o_norm, eps, o, m); break;
+    case 32: hipLaunchKernelGGL((k_decode_combine<32>), grid, dim3(256), 0, st, dc, units, part, mpart, w, z, in_f32, out_f32, o_norm, eps, o, m); break;
+    case 64: hipLaunchKernelGGL((k_decode_combine<64>), grid, dim3(256), 0, st, dc, units, part, mpart, w, z, in_f32, out_f32, o_norm, eps, o, m); break;
+    case 128: hipLaunchKernelGGL((k_decode_combine<128>), grid, dim3(512), 0, st, dc, units, part, mpart, w, z, in_f32, out_f32, o_norm, eps, o, m); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -249,7 +249,7 @@ def main():
                     help="only run a plain 1 GiB device-to-device copy 3 times (HBM counter calibration)")
     ap.add_argument("--scalar-gate", action="store_true",
                     help="one gate value per token and kv head (channel 0 of the workload's gate): the "
-                         "logit-bias forward and the broadcast backward")
+                         "logit-bias forward and backward")
     ap.add_argument("--decode", action="store_true",
                     help="time decode steps (fix_decode_step) against a cache holding the workload's T tokens")
     args = ap.parse_args()
@@ -370,6 +370,8 @@ def main():
         "bwd_dkv": 2 * (dk + dv) * pc["far"] * heads,             # dV, dK on pairs two or more chunks apart
         "bwd_intra_dq": 2 * (2 * dk + dv) * pc["same"] * heads,
         "bwd_intra_dkv": 2 * (dk + dv) * (pc["same"] + pc["adj"]) * heads,
+        "fox_bwd_dq": 2 * (2 * dk + dv) * pc["all"] * heads,      # S, dP, dQ on every pair
+        "fox_bwd_dkv": 2 * (dk + dv) * pc["all"] * heads,         # dV, dK on every pair
     }
     dom = max(avg, key=avg.get)
     roof = None

@@ -109,8 +109,35 @@ struct BwdWs {
   _Float16 *dh, *X16;
   __bf16 *XH, *XL, *XTH, *XTL;
   float *mb, *sig, *qside, *dG, *dq_i, *dk_i, *dv_i, *dw_part, *dg_tot, *dg_carry;
-  float *gb = nullptr, *dgb = nullptr;  // scalar gate: per-channel copy of g and the per-channel dg
 };
+
+// Scalar-gate backward workspace (logit-bias form; fox_bwd.h).
+struct FoxBwdWs {
+  fix::Plan plan;
+  float *loc;
+  double *ref;
+  _Float16 *Q16, *K16, *V16, *D16;
+  float *mb, *rsum, *csum, *dw_part;
+};
+
+int64_t pad32(int64_t d) { return d < 32 ? 32 : d; }
+
+size_t carve_fox_bwd(Carve &cv, const fix_attn_desc *d, FoxBwdWs &w) {
+  Shape s = shape_of(d);
+  carve_plan(cv, d, s, w.plan);
+  const int64_t T = s.Ttot, Hq = d->Hq, Hkv = d->Hkv;
+  w.loc = cv.take<float>(T * Hkv);
+  w.ref = cv.take<double>(s.nch_ub * Hkv);
+  w.Q16 = cv.take<_Float16>(T * Hq * pad32(d->dk));
+  w.K16 = cv.take<_Float16>(T * Hkv * pad32(d->dk));
+  w.V16 = cv.take<_Float16>(T * Hkv * d->dv);
+  w.D16 = cv.take<_Float16>(T * Hq * pad32(d->dv));
+  w.mb = cv.take<float>(T * Hq);
+  w.rsum = cv.take<float>(T * Hq);
+  w.csum = cv.take<float>(T * Hkv);
+  w.dw_part = cv.take<float>(s.nqb_ub * Hkv * d->dv);
+  return cv.off;
+}
 
 size_t carve_bwd(Carve &cv, const fix_attn_desc *d, BwdWs &w) {
   Shape s = shape_of(d);
@@ -143,10 +170,6 @@ size_t carve_bwd(Carve &cv, const fix_attn_desc *d, BwdWs &w) {
   w.dw_part = cv.take<float>(ncb * Hkv * DV);
   w.dg_tot = cv.take<float>(ncb * Hkv * DV);
   w.dg_carry = cv.take<float>(ncb * Hkv * DV);
-  if (d->gate_scalar) {
-    w.gb = cv.take<float>(T * Hkv * DV);
-    w.dgb = cv.take<float>(T * Hkv * DV);
-  }
   return cv.off;
 }
 
@@ -291,6 +314,10 @@ fix_status fix_attn_fwd(const fix_attn_desc *d, const void *q, const void *k, co
 size_t fix_attn_bwd_workspace_size(const fix_attn_desc *d) {
   if (fix_attn_validate(d) != FIX_OK) return 0;
   Carve cv(nullptr);
+  if (d->gate_scalar) {
+    FoxBwdWs w;
+    return carve_fox_bwd(cv, d, w);
+  }
   BwdWs w;
   return carve_bwd(cv, d, w);
 }
@@ -311,30 +338,63 @@ fix_status fix_attn_bwd(const fix_attn_desc *d, const void *q, const void *k, co
   if (!aligned16(ws)) return FIX_E_INVALID;
   hipStream_t st = (hipStream_t)hip_stream;
   Shape s = shape_of(d);
-  Carve cv(ws);
-  BwdWs w;
-  carve_bwd(cv, d, w);
   const bool f32in = d->in_dtype == FIX_F32;
   const int Hq = (int)d->Hq, Hkv = (int)d->Hkv, DK = (int)d->dk, DV = (int)d->dv, ncb = (int)s.nqb_ub;
   const bool want_dw = d->o_norm && d_o_norm_weight;
+  const float scale = d->scale > 0.f ? d->scale : 1.f / std::sqrt((float)d->dk);
   hipError_t e;
-#define FIX_TRY(call, label)          \
-  e = (call);                         \
-  if (e == hipSuccess) e = trace_mark(st, label); \
-  if (e != hipSuccess) return hip_fail(e);
+#define FIX_TRY(call, label)                        \
+  do {                                              \
+    e = (call);                                     \
+    if (e == hipSuccess) e = trace_mark(st, label); \
+    if (e != hipSuccess) return hip_fail(e);        \
+  } while (0)
   e = trace_begin(st);
   if (e != hipSuccess) return hip_fail(e);
-  FIX_TRY(fix::launch_plan(d->cu_seqlens, (int)s.nseq, (int)d->T, s.Ttot, w.plan, st), "plan");
-  // A scalar gate goes through the per-channel path as a broadcast copy; its
-  // gradient is the per-channel one summed over the channels.
-  const float *gch = g;
-  float *dgch = dg;
   if (d->gate_scalar) {
-    FIX_TRY(fix::launch_gate_broadcast(g, s.Ttot * Hkv, DV, w.gb, st), "gate_broadcast");
-    gch = w.gb;
-    dgch = w.dgb;
+    // The decay as a logit bias (fox_bwd.h): dq with the row sums of dS, dk and
+    // dv with its column sums, and dg as the suffix sum of their difference.
+    Carve cv(ws);
+    FoxBwdWs w;
+    carve_fox_bwd(cv, d, w);
+    const int DKP = (int)pad32(DK), DVP = (int)pad32(DV);
+    FIX_TRY(fix::launch_plan(d->cu_seqlens, (int)s.nseq, (int)d->T, s.Ttot, w.plan, st), "plan");
+    FIX_TRY(fix::launch_fox_prefix(g, d->gate_logits != 0, w.plan, (int)s.nseq, Hkv, w.loc, w.ref, st), "fox_prefix");
+    FIX_TRY(fix::launch_to_f16_pad(q, f32in, s.Ttot * Hq, DK, DKP, w.Q16, st), "q_f16");
+    FIX_TRY(fix::launch_to_f16_pad(k, f32in, s.Ttot * Hkv, DK, DKP, w.K16, st), "k_f16");
+    FIX_TRY(fix::launch_to_f16(v, f32in, s.Ttot * Hkv * DV, w.V16, st), "v_f16");
+    fix::FoxPrepArgs pa;
+    pa.x = x; pa.rstd = rstd; pa.m = m;
+    pa.dO = d_o; pa.z = o_gate; pa.w = d->o_norm ? o_norm_weight : nullptr;
+    pa.plan = w.plan;
+    pa.Hq = Hq; pa.Hkv = Hkv;
+    pa.o_norm = d->o_norm ? 1 : 0;
+    pa.out_f32 = d->out_dtype == FIX_F32;
+    pa.in_f32 = f32in;
+    pa.D16 = w.D16; pa.mb = w.mb; pa.dz = d_o_gate;
+    pa.dw_part = want_dw ? w.dw_part : nullptr;
+    FIX_TRY(fix::launch_fox_bwd_prep(DV, pa, ncb, st), "fox_bwd_prep");
+    fix::FoxBwdArgs fa;
+    fa.Q16 = w.Q16; fa.K16 = w.K16; fa.V16 = w.V16; fa.D16 = w.D16;
+    fa.mb = w.mb; fa.loc = w.loc; fa.ref = w.ref; fa.rsum = w.rsum; fa.csum = w.csum;
+    fa.dq = dq; fa.dk = dk; fa.dv = dv;
+    fa.plan = w.plan;
+    fa.Hq = Hq; fa.Hkv = Hkv;
+    fa.sl2 = scale * fix::LOG2E;
+    fa.scale = scale;
+    fa.out_f32 = d->out_dtype == FIX_F32;
+    FIX_TRY(fix::launch_fox_bwd(fix::FK_DQ, DK, DV, fa, (int)round8(s.nqb_ub * Hq), st), "fox_bwd_dq");
+    FIX_TRY(fix::launch_fox_bwd(fix::FK_DKV, DK, DV, fa, (int)round8(s.nqb_ub * Hkv), st), "fox_bwd_dkv");
+    FIX_TRY(fix::launch_fox_dg_scan(w.rsum, w.csum, d->gate_logits ? g : nullptr, w.plan, (int)s.nseq, Hq, Hkv, dg, st),
+            "fox_dg_scan");
+    if (want_dw) FIX_TRY(fix::launch_dw_reduce(w.dw_part, w.plan.counts, Hkv, DV, d_o_norm_weight, st), "dw_reduce");
+    return FIX_OK;
   }
-  FIX_TRY(fix::launch_gate_prep_rows(DV, gch, d->gate_logits != 0, v, f32in, w.plan, Hkv, ncb, w.Gl2, w.Gam, w.Vr,
+  Carve cv(ws);
+  BwdWs w;
+  carve_bwd(cv, d, w);
+  FIX_TRY(fix::launch_plan(d->cu_seqlens, (int)s.nseq, (int)d->T, s.Ttot, w.plan, st), "plan");
+  FIX_TRY(fix::launch_gate_prep_rows(DV, g, d->gate_logits != 0, v, f32in, w.plan, Hkv, ncb, w.Gl2, w.Gam, w.Vr,
                                      w.VE, w.VBH, w.VBL, st),
           "gate_prep_rows");
   FIX_TRY(fix::launch_chunk_logprefix(DV, w.Gl2, w.plan, Hkv, w.Lam, st), "chunk_logprefix");
@@ -363,7 +423,6 @@ fix_status fix_attn_bwd(const fix_attn_desc *d, const void *q, const void *k, co
   a.dq = dq; a.dk = dk; a.dv = dv; a.dG = w.dG;
   a.plan = w.plan;
   a.Hq = Hq; a.Hkv = Hkv;
-  const float scale = d->scale > 0.f ? d->scale : 1.f / std::sqrt((float)d->dk);
   a.sl2 = scale * fix::LOG2E;
   a.scale = scale;
   a.out_f32 = d->out_dtype == FIX_F32;
@@ -371,10 +430,9 @@ fix_status fix_attn_bwd(const fix_attn_desc *d, const void *q, const void *k, co
   FIX_TRY(fix::launch_bwd(fix::BK_INTRA_DKV, DK, DV, f32in, a, dim3(ncb, Hkv), st), "bwd_intra_dkv");
   FIX_TRY(fix::launch_bwd(fix::BK_DQ, DK, DV, f32in, a, dim3(round8(ncb * Hq)), st), "bwd_dq");
   FIX_TRY(fix::launch_bwd(fix::BK_DKV, DK, DV, f32in, a, dim3(round8(ncb * Hkv)), st), "bwd_dkv");
-  FIX_TRY(fix::launch_dg_scan(DV, w.dG, d->gate_logits ? gch : nullptr, w.plan, Hkv, ncb, w.dg_tot, w.dg_carry, dgch,
+  FIX_TRY(fix::launch_dg_scan(DV, w.dG, d->gate_logits ? g : nullptr, w.plan, Hkv, ncb, w.dg_tot, w.dg_carry, dg,
                               st),
           "dg_scan");
-  if (d->gate_scalar) FIX_TRY(fix::launch_gate_reduce(dgch, s.Ttot * Hkv, DV, dg, st), "gate_reduce");
   if (want_dw) {
     FIX_TRY(fix::launch_dw_reduce(w.dw_part, w.plan.counts, Hkv, DV, d_o_norm_weight, st), "dw_reduce");
   }

@@ -288,42 +288,179 @@ hipError_t launch_fox_fwd(int dk, int dv, bool f32in, const FoxArgs &a, int grid
   return hipErrorInvalidValue;
 }
 
-// Per-channel copy of a scalar gate ([T, Hkv] -> [T, Hkv, dv]) for the
-// backward, and the sum over channels of a per-channel gate gradient.  Both
-// move one float4 per lane (dv is a multiple of 4); in the sum, the dv/4
-// lanes of one row (an aligned group inside the wave) add their partial sums
-// with cross-lane shuffles, so each wave reads contiguous memory.
-__global__ void k_gate_broadcast(const float *__restrict__ g, int64_t n, int q, float4 *__restrict__ gb) {
-  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e < n * q) {
-    const float v = g[e / q];
-    gb[e] = make_float4(v, v, v, v);
+// Backward preprocessing of the scalar-gate path: the output-side backward
+// (as for the per-channel gate: with r = rstd and xh = x r,
+//   dz = dO (.) n (n = xh (.) w under the norm, x without it), dn = dO (.) z,
+//   dw = sum over rows of dn (.) xh,
+//   delta = r (dn (.) w - xh mean_d(dn (.) w (.) xh))   (dn without the norm))
+// and the fp16 operand sigma delta with sigma = 2^-e, max_d |sigma delta|
+// about 1, plus the row offset mb = m log2e - e.  One workgroup per 128-chunk
+// and kv head, every q head of the group in turn; a thread owns eight
+// consecutive channels of a row (DV / 8 threads per row, row reductions by
+// shuffles inside that group).
+template <int DV>
+__global__ void __launch_bounds__(256) k_fox_bwd_prep(FoxPrepArgs a) {
+  constexpr int TPR = DV / 8, RPP = 256 / TPR, DVP = DV < 32 ? 32 : DV;
+  __shared__ float red[RPP * DV];
+  const int gc = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
+  if (gc >= a.plan.counts[0]) return;
+  const Plan &pl = a.plan;
+  const int s = seq_of_chunk(pl.cb128, pl.nseq, gc);
+  const int t0 = (gc - pl.cb128[s]) * CB;
+  const int n = min(CB, pl.seq_len[s] - t0);
+  const int64_t tok0 = (int64_t)pl.seq_start[s] + t0;
+  const int Hq = a.Hq, G = Hq / a.Hkv;
+  const bool in_f32 = a.in_f32, o_norm = a.o_norm;
+  const int sub = tid % TPR, d0 = 8 * sub, rr = tid / TPR;
+  float wv[8], dwacc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    wv[i] = (o_norm && a.w) ? load_in(a.w, d0 + i, in_f32) : 1.f;
+    dwacc[i] = 0.f;
+  }
+  for (int gq = 0; gq < G; ++gq) {
+    const int h = c * G + gq;
+    for (int r = rr; r < n; r += RPP) {
+      const int64_t tok = tok0 + r;
+      const int64_t rb = (tok * Hq + h) * DV + d0;
+      float xv[8], go[8], zz[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        xv[i] = a.x[rb + i];
+        go[i] = load_in(a.dO, rb + i, in_f32);
+        zz[i] = a.z ? load_in(a.z, rb + i, in_f32) : 1.f;
+      }
+      const float rs = a.rstd[tok * Hq + h], mrow = a.m[tok * Hq + h];
+      float dn[8], proj = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        dn[i] = go[i] * zz[i];
+        proj += dn[i] * wv[i] * xv[i] * rs;
+      }
+      if (o_norm) {
+#pragma unroll
+        for (int off = TPR / 2; off > 0; off >>= 1) proj += __shfl_xor(proj, off);
+        proj *= 1.f / DV;
+      }
+      float del[8], amax = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        del[i] = o_norm ? rs * (dn[i] * wv[i] - xv[i] * rs * proj) : dn[i];
+        amax = fmaxf(amax, fabsf(del[i]));
+      }
+#pragma unroll
+      for (int off = TPR / 2; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+      int e = 0;
+      if (amax > 0.f) e = min(15, max(-15, (int)ceilf(__log2f(amax))));
+      const float sg = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e
+      f16x8 hv;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) hv[i] = (_Float16)(del[i] * sg);
+      _Float16 *drow = a.D16 + (tok * Hq + h) * DVP;
+      *(f16x8 *)(drow + d0) = hv;
+      if (DV < DVP) *(f16x8 *)(drow + DV + d0) = __builtin_bit_cast(f16x8, make_uint4(0, 0, 0, 0));
+      if (a.dz)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) store_out(a.dz, rb + i, go[i] * (o_norm ? xv[i] * rs * wv[i] : xv[i]), a.out_f32);
+      if (o_norm)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dwacc[i] += dn[i] * xv[i] * rs;
+      if (sub == 0) a.mb[tok * Hq + h] = mrow * LOG2E - (float)e;
+    }
+  }
+  if (a.dw_part) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) red[rr * DV + d0 + i] = dwacc[i];
+    __syncthreads();
+    for (int d = tid; d < DV; d += 256) {
+      float acc = 0.f;
+      for (int q = 0; q < RPP; ++q) acc += red[q * DV + d];
+      a.dw_part[((int64_t)gc * a.Hkv + c) * DV + d] = acc;
+    }
   }
 }
-__global__ void __launch_bounds__(256) k_gate_reduce(const float4 *__restrict__ dgb, int64_t n, int q,
-                                                     float *__restrict__ dg) {
-  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const bool in = e < n * q;
-  float s = 0.f;
-  if (in) {
-    const float4 v = dgb[e];
-    s = (v.x + v.y) + (v.z + v.w);
+
+hipError_t launch_fox_bwd_prep(int dv, const FoxPrepArgs &a, int ncb_ub, hipStream_t st) {
+  dim3 grid(ncb_ub, a.Hkv);
+  switch (dv) {
+    case 16: hipLaunchKernelGGL(k_fox_bwd_prep<16>, grid, dim3(256), 0, st, a); break;
+    case 32: hipLaunchKernelGGL(k_fox_bwd_prep<32>, grid, dim3(256), 0, st, a); break;
+    case 64: hipLaunchKernelGGL(k_fox_bwd_prep<64>, grid, dim3(256), 0, st, a); break;
+    case 128: hipLaunchKernelGGL(k_fox_bwd_prep<128>, grid, dim3(256), 0, st, a); break;
+    default: return hipErrorInvalidValue;
   }
-  for (int off = 1; off < q; off <<= 1) s += __shfl_xor(s, off);
-  if (in && e % q == 0) dg[e / q] = s;
-}
-hipError_t launch_gate_broadcast(const float *g, int64_t n, int dv, float *gb, hipStream_t st) {
-  if (dv % 4 || 64 % (dv / 4)) return hipErrorInvalidValue;
-  const int64_t tot = n * (dv / 4);
-  hipLaunchKernelGGL(k_gate_broadcast, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, g, n, dv / 4,
-                     (float4 *)gb);
   return hipGetLastError();
 }
-hipError_t launch_gate_reduce(const float *dgb, int64_t n, int dv, float *dg, hipStream_t st) {
-  if (dv % 4 || 64 % (dv / 4)) return hipErrorInvalidValue;
-  const int64_t tot = n * (dv / 4);
-  hipLaunchKernelGGL(k_gate_reduce, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, (const float4 *)dgb,
-                     n, dv / 4, dg);
+
+// The gate gradient: dL/dG_t = sum over the group of rsum_t,h - csum_t; dg_t is
+// its suffix sum over the sequence (fp64 accumulation), times sigmoid(-x_t)
+// when the gate was given as logits x.  One workgroup per (sequence, kv head);
+// thread u owns a contiguous run of tokens, the runs' totals are combined
+// through LDS.
+template <bool LOGITS>
+__global__ void __launch_bounds__(256) k_fox_dg_scan(const float *__restrict__ rsum, const float *__restrict__ csum,
+                                                     const float *__restrict__ logits, Plan plan, int Hq, int Hkv,
+                                                     float *__restrict__ dg) {
+  const int s = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
+  if (s >= plan.nseq) return;
+  const int L = plan.seq_len[s];
+  const int64_t st = plan.seq_start[s];
+  const int G = Hq / Hkv;
+  const int per = (L + 255) / 256, t0 = min(L, tid * per), t1 = min(L, t0 + per);
+  auto dF = [&](int t) {
+    const int64_t tok = st + t;
+    float r = 0.f;
+    for (int gq = 0; gq < G; ++gq) r += rsum[tok * Hq + c * G + gq];
+    return (double)r - (double)csum[tok * Hkv + c];
+  };
+  __shared__ double tot[256];
+  double sum = 0.0;
+  for (int t = t0; t < t1; ++t) sum += dF(t);
+  tot[tid] = sum;
+  __syncthreads();
+  double run = 0.0;
+  for (int u = tid + 1; u < 256; ++u) run += tot[u];
+  for (int t = t1 - 1; t >= t0; --t) {
+    run += dF(t);
+    const int64_t i = (st + t) * Hkv + c;
+    dg[i] = LOGITS ? (float)run * sigmoid_neg(logits[i]) : (float)run;
+  }
+}
+
+hipError_t launch_fox_dg_scan(const float *rsum, const float *csum, const float *logits, const Plan &plan, int nseq,
+                              int Hq, int Hkv, float *dg, hipStream_t st) {
+  dim3 grid(nseq, Hkv);
+  if (logits) hipLaunchKernelGGL(k_fox_dg_scan<true>, grid, dim3(256), 0, st, rsum, csum, logits, plan, Hq, Hkv, dg);
+  else hipLaunchKernelGGL(k_fox_dg_scan<false>, grid, dim3(256), 0, st, rsum, csum, logits, plan, Hq, Hkv, dg);
+  return hipGetLastError();
+}
+
+// fp16 copy of a [rows, D] tensor into rows of DP >= D elements (zeros past D),
+// eight elements per thread.
+__global__ void __launch_bounds__(256) k_to_f16_pad(const void *__restrict__ in, bool in_f32, int64_t rows, int D,
+                                                    int DP, _Float16 *__restrict__ out) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int per = DP / 8;
+  if (e >= rows * per) return;
+  const int64_t r = e / per;
+  const int c8 = 8 * (int)(e % per);
+  f16x8 h;
+  if (c8 < D) {
+    const int64_t src = r * D + c8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = (_Float16)load_in(in, src + i, in_f32);
+  } else {
+    h = __builtin_bit_cast(f16x8, make_uint4(0, 0, 0, 0));
+  }
+  *(f16x8 *)(out + r * DP + c8) = h;
+}
+
+hipError_t launch_to_f16_pad(const void *in, bool in_f32, int64_t rows, int D, int DP, _Float16 *out, hipStream_t st) {
+  if (D % 8 || DP % 8 || DP < D) return hipErrorInvalidValue;
+  const int64_t tot = rows * (DP / 8);
+  if (tot > 0)
+    hipLaunchKernelGGL(k_to_f16_pad, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, in, in_f32, rows, D, DP,
+                       out);
   return hipGetLastError();
 }
 

@@ -38,8 +38,58 @@ struct FoxArgs {
 hipError_t launch_fox_prefix(const float *g, bool logits, const Plan &plan, int nseq, int Hkv, float *loc,
                              double *ref, hipStream_t st);
 hipError_t launch_fox_fwd(int dk, int dv, bool f32in, const FoxArgs &a, int grid, hipStream_t st);
-hipError_t launch_gate_broadcast(const float *g, int64_t n, int dv, float *gb, hipStream_t st);
-hipError_t launch_gate_reduce(const float *dgb, int64_t n, int dv, float *dg, hipStream_t st);
+
+// Scalar-gate backward (fox_bwd.h): the logit-bias form of the gradients.
+// Operands are fp16 copies, rows padded to 32 columns where a product reads
+// them column-wise (head dims below 32).
+struct FoxBwdArgs {
+  const _Float16 *Q16;  // [T, Hq, DKP]
+  const _Float16 *K16;  // [T, Hkv, DKP]
+  const _Float16 *V16;  // [T, Hkv, DV]
+  const _Float16 *D16;  // [T, Hq, DVP] sigma * delta (delta: the gradient reaching x)
+  const float *mb;      // [T, Hq] m log2e - e (sigma = 2^-e)
+  const float *loc;     // [T, Hkv] log2 gate prefix local to the token's 64-token block
+  const double *ref;    // [64-block][Hkv] log2 gate prefix before each block
+  float *rsum;          // [T, Hq] row sums of dS (written by the dq kernel)
+  float *csum;          // [T, Hkv] column sums of dS over the head group (dk/dv kernel)
+  void *dq, *dk, *dv;
+  Plan plan;
+  int Hq, Hkv;
+  float sl2, scale;
+  int out_f32;
+};
+struct FoxPrepArgs {
+  const float *x, *rstd, *m;
+  const void *dO, *z, *w;
+  Plan plan;
+  int Hq, Hkv;
+  int o_norm, out_f32, in_f32;
+  _Float16 *D16;   // [T, Hq, DVP]
+  float *mb;       // [T, Hq]
+  void *dz;        // [T, Hq, DV] or null
+  float *dw_part;  // [128-chunks * Hkv][DV] or null
+};
+enum FoxBwdKernel { FK_DQ = 0, FK_DKV = 1 };
+hipError_t launch_fox_bwd_prep(int dv, const FoxPrepArgs &a, int ncb_ub, hipStream_t st);
+hipError_t launch_fox_bwd_d16(FoxBwdKernel kind, int dv, const FoxBwdArgs &a, int grid, hipStream_t st);
+hipError_t launch_fox_bwd_d32(FoxBwdKernel kind, int dv, const FoxBwdArgs &a, int grid, hipStream_t st);
+hipError_t launch_fox_bwd_d64(FoxBwdKernel kind, int dv, const FoxBwdArgs &a, int grid, hipStream_t st);
+hipError_t launch_fox_bwd_d128(FoxBwdKernel kind, int dv, const FoxBwdArgs &a, int grid, hipStream_t st);
+inline hipError_t launch_fox_bwd(FoxBwdKernel kind, int dk, int dv, const FoxBwdArgs &a, int grid, hipStream_t st) {
+  switch (dk) {
+    case 16: return launch_fox_bwd_d16(kind, dv, a, grid, st);
+    case 32: return launch_fox_bwd_d32(kind, dv, a, grid, st);
+    case 64: return launch_fox_bwd_d64(kind, dv, a, grid, st);
+    case 128: return launch_fox_bwd_d128(kind, dv, a, grid, st);
+  }
+  return hipErrorInvalidValue;
+}
+// dg_t = sum over t' >= t of the sequence of (sum over the group of rsum - csum)
+// (times sigmoid(-x) when the gate was given as logits x).
+hipError_t launch_fox_dg_scan(const float *rsum, const float *csum, const float *logits, const Plan &plan, int nseq,
+                              int Hq, int Hkv, float *dg, hipStream_t st);
+// fp16 copy of a [rows, D] bf16 or fp32 tensor into [rows, DP] (DP >= D, zero columns past D).
+hipError_t launch_to_f16_pad(const void *in, bool in_f32, int64_t rows, int D, int DP, _Float16 *out, hipStream_t st);
 
 struct BwdArgs {
   const void *q, *k, *v;

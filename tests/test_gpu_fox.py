@@ -1,18 +1,14 @@
 """Parity of the scalar-gate path (gate_scalar: one gate value per token and kv head).
 
-The forward has its own kernel (the decay as a logit bias); the backward runs
-the per-channel kernels on a broadcast copy and sums dg over the channels.
-The reference is the fp64 oracle with the same scalar gate (the oracle treats
-it as the same value in every channel).  Bars: max |gpu - oracle| /
-rms(oracle) <= 1e-2 on o, x, dq, dk, dv, dw, dz and on dg; m within
-1e-4 * max|m| (bf16 inputs) or 2^-9 * max|m| (fp32 inputs staged as fp16);
-rstd within 1e-2 relative.  The dg of a scalar gate is the sum over the dv
-channels of per-channel terms dG = sum_h delta (.) x - v (.) dv that nearly
-cancel; each is held to 5e-3 of its own scale in the per-channel tests, and
-their sum, measured against its own (smaller) rms, to the general 1e-2.
-A single token (exact dq = dk = dg = 0, no relative error defined) is
-checked on the forward only; its backward is the per-channel one, tested
-with floors in the per-channel backward tests.
+Forward and backward have their own kernels (the decay as a logit bias); the
+gate gradient is the suffix sum of row sums minus column sums of dS.  The
+reference is the fp64 oracle with the same scalar gate (the oracle treats it
+as the same value in every channel and sums its per-channel dg).  Bars: max
+|gpu - oracle| / rms(oracle) <= 1e-2 on o, x, dq, dk, dv, dw, dz and 5e-3 on
+dg; m within 1e-4 * max|m| (bf16 inputs) or 2^-9 * max|m| (fp32 inputs
+staged as fp16); rstd within 1e-2 relative.  A single token (exact dq, dk
+and dg vanish at eps = 0, so no relative error is defined) is checked on the
+forward only; packed cases hold one-token and empty sequences.
 """
 import numpy as np
 import pytest
@@ -23,6 +19,7 @@ from gpu_util import announce, custom_inputs, device_inputs, err_rms, needs_gpu,
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 TOL = 1e-2
+TOL_DG = 5e-3
 
 
 def scalar_inputs(*args, **kw):
@@ -70,7 +67,7 @@ def check(got, rf, rb, *, o_norm=True, f32_inputs=False):
             e["dw"] = err_rms(got["dw"], rb["dw"])
     print("errors:", {k: f"{v:.2e}" for k, v in e.items()}, f"m {m_err:.2e}", flush=True)
     for n, v in e.items():
-        assert v <= TOL, f"{n}: {v:.3e}"
+        assert v <= (TOL_DG if n == "dg" else TOL), f"{n}: {v:.3e}"
     m_tol = 2.0 ** -9 if f32_inputs else 1e-4
     assert m_err <= m_tol * max(1.0, float(np.nanmax(np.abs(rf["m"]))))
 
@@ -114,12 +111,34 @@ def test_scalar_gate_logits_no_norm():
 
 
 def test_scalar_gate_full_size_sampled():
-    """The training shape (B=4, T=8192, Hq=Hkv=16, d=128) with a scalar gate: forward on the
-    last 256 rows of two (sequence, kv head) units, from the full sequences."""
+    """The training shape (B=4, T=8192, Hq=Hkv=16, d=128) with a scalar gate, as the benchmark
+    runs it: o and dq on the last 256 rows, dk, dv and dg on the last 256 keys of two
+    (sequence, kv head) units, from the full sequences."""
     announce("scalar gate full size")
-    x = scalar_inputs(4, 8192, 16, 16, 128, 128, gate=(4.0, 2.0), seed=5, backward=False)
-    got = run(x, backward=False)
+    x = scalar_inputs(4, 8192, 16, 16, 128, 128, gate=(4.0, 2.0), seed=5)
+    got = run(x)
     mask = np.zeros((4, 16), np.uint8)
     mask[0, 0] = mask[3, 15] = 1
     rf = oracle_fwd_for(x, unit_mask=mask, window=256)
-    check(got, rf, None)
+    rb = oracle_bwd_for(x, unit_mask=mask, window=256)
+    e = {"o": err_rms(got["o"], rf["o"])}
+    for n in ("dq", "dk", "dv", "dg"):
+        e[n] = err_rms(got[n], rb[n])
+    print("errors:", {k: f"{v:.2e}" for k, v in e.items()}, flush=True)
+    for n, v in e.items():
+        assert v <= (TOL_DG if n == "dg" else TOL), f"{n}: {v:.3e}"
+
+
+def test_scalar_gate_full_size_first_keys():
+    """Training shape, scalar gate: dq of the first 256 rows and dk, dv of the first 256 keys
+    of one unit, whose gradients gather every later query of the sequence."""
+    announce("scalar gate full size, first keys")
+    x = scalar_inputs(4, 8192, 16, 16, 128, 128, gate=(4.0, 2.0), seed=5)
+    got = run(x)
+    mask = np.zeros((4, 16), np.uint8)
+    mask[2, 7] = 1
+    rb = oracle_bwd_for(x, unit_mask=mask, window=-256)
+    e = {n: err_rms(got[n], rb[n]) for n in ("dq", "dk", "dv")}
+    print("errors:", {k: f"{v:.2e}" for k, v in e.items()}, flush=True)
+    for n, v in e.items():
+        assert v <= TOL, f"{n}: {v:.3e}"

@@ -20,7 +20,9 @@
  *     o_i *= z_i                                      if an output gate is given
  *
  * The decay is evaluated as a running product of per-token gate factors,
- * never as an exponential of a difference of prefix sums.  The readings
+ * never as an exponential of a difference of prefix sums.  A walk along the
+ * keys (or queries) stops once that product is exactly zero in every channel:
+ * every later term is then an exact zero, so no result changes.  The readings
  * taken where the pages are silent (inclusive gate product, m_i the row max
  * of the scaled undecayed logits, contiguous GQA head groups, m held
  * constant in the backward, literal product with the output gate after the
@@ -110,6 +112,15 @@ static const double *K(const octx *c, int64_t t, int64_t kh) { return c->k + (t 
 static const double *V(const octx *c, int64_t t, int64_t kh) { return c->v + (t * c->Hkv + kh) * c->dv; }
 static const double *A(const octx *c, int64_t t, int64_t kh) { return c->a + (t * c->Hkv + kh) * c->dv; }
 
+/* 1 when every channel of a running decay product is exactly zero: from then on
+ * every later term of the walk is an exact zero (a product of finite factors with
+ * 0), so the walk can stop without changing any result. */
+static int all_zero(const double *D, int64_t n) {
+  for (int64_t d = 0; d < n; ++d)
+    if (D[d] != 0.0) return 0;
+  return 1;
+}
+
 static double dot(const double *x, const double *y, int64_t n) {
   double acc = 0.0;
   for (int64_t e = 0; e < n; ++e) acc += x[e] * y[e];
@@ -140,6 +151,7 @@ static void row_x(const octx *c, int64_t s, int64_t h, int64_t i, const double *
     const double *aj = A(c, base + j, kh);
     for (int64_t d = 0; d < dv; ++d) x[d] += p * D[d] * vj[d];
     for (int64_t d = 0; d < dv; ++d) D[d] *= aj[d];
+    if (all_zero(D, dv)) break;
   }
 }
 
@@ -332,6 +344,7 @@ int fix_oracle_bwd(int64_t nseq, const int64_t *cu, int64_t Hq, int64_t Hkv, int
         const double *kj = K(&c, base + j, kh);
         for (int64_t e2 = 0; e2 < dk; ++e2) acc[e2] += dS * kj[e2];
         for (int64_t d = 0; d < dv; ++d) D[d] *= aj[d];
+        if (all_zero(D, dv)) break;
       }
       for (int64_t e2 = 0; e2 < dk; ++e2) dq[ro * dk + e2] = scale * acc[e2];
     }
@@ -369,6 +382,7 @@ int fix_oracle_bwd(int64_t nseq, const int64_t *cu, int64_t Hq, int64_t Hkv, int
           if (i > j) {
             const double *ai = A(&c, base + i, kh);
             for (int64_t d = 0; d < dv; ++d) D[d] *= ai[d];
+            if (all_zero(D, dv)) break;
           }
           size_t ro = (size_t)((base + i) * Hq + h);
           const double *qi = Q(&c, base + i, h);

@@ -300,6 +300,30 @@ def pin_dense_reference(lib, rng, o_norm=True):
     return worst
 
 
+def pin_dense_reference_vanishing_decay(lib, rng):
+    """Oracle vs the dense autograd reference under gates so strong (logsigmoid of N(-30, 2), and
+    -1e4 in half the channels) that the running decay product reaches exactly zero in every
+    channel within a few tokens, where the oracle's walks stop, and with zeros in only some
+    channels, where they must not: the shortcut must leave every output unchanged."""
+    lengths = [60, 3, 61]
+    q, k, v, g, cu = rand_case(rng, 1, 124, 4, 2, 16, 8, gate=(-30.0, 2.0), lengths=lengths)
+    # half the channels cut off at once everywhere; in the last sequence the other half
+    # forgets slowly, so the product is zero in some channels only and the walk must go on
+    g[..., :4] = -1e4
+    g[0, 63:, :, 4:] = -np.logaddexp(0.0, -(rng.standard_normal((61, 2, 4)) + 2.0))
+    dO = rng.standard_normal((1, 124, 4, 8))
+    ref = dense_reference(q, k, v, g, dO, cu, eps=1e-5)
+    f = O.oracle_fwd(q, k, v, g, cu, eps=1e-5, lib=lib)
+    b = O.oracle_bwd(q, k, v, g, dO, cu, eps=1e-5, lib=lib)
+    worst = rel(f["o"], ref["o"])
+    for n in ("dq", "dk", "dv"):
+        worst = max(worst, rel(b[n], ref[n]))
+    # dg is a difference of nearly equal terms here (x_t is almost v_t, dv_t almost delta_t):
+    # measured against the scale of the cancelling terms, as fp64 cancellation leaves it
+    scale = np.sqrt(np.mean((v * ref["dv"]) ** 2))
+    return max(worst, float(np.max(np.abs(b["dg"] - ref["dg"])) / scale))
+
+
 def pin_suffix_window(lib, rng):
     """The sampled (unit mask + suffix window) mode reproduces the full results there."""
     lengths = [30, 45]
@@ -433,6 +457,7 @@ ALL_PINS = {
     "value_scale": (pin_value_scale, 1e-12),
     "dense_reference": (pin_dense_reference, 1e-10),
     "dense_reference_unnormed": (lambda lib, rng: pin_dense_reference(lib, rng, False), 1e-10),
+    "dense_reference_vanishing_decay": (pin_dense_reference_vanishing_decay, 1e-10),
     "suffix_window": (pin_suffix_window, 0.0),
     "prefix_window": (pin_prefix_window, 0.0),
     "logits_finite_diff": (pin_logits_finite_differences, 1e-6),

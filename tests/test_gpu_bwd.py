@@ -176,18 +176,48 @@ def test_bwd_full_size_sampled(name, units):
     check_bwd(got, ref, check_dw=False)
 
 
-def test_bwd_full_size_first_keys():
-    """Training shape as the benchmark runs it: dq of the first 256 rows and dk, dv of the first
-    256 keys of two units, whose gradients gather every later query (the inter-chunk kernels'
-    work); the oracle computes the units' whole forward for them."""
-    announce("bwd full-size train, first keys")
-    x = synth.make_inputs("train")
+FIRST_KEYS = [
+    ("train", [(0, 5), (2, 11)]),
+    ("long_d16", [(0, 3)]),
+    ("long_d32", [(0, 0)]),
+    ("long_d64", [(0, 5)]),
+    ("long_d128", [(0, 7)]),
+]
+
+
+@pytest.mark.parametrize("name,units", FIRST_KEYS)
+def test_bwd_full_size_first_keys(name, units):
+    """Full-size workloads as the benchmark runs them: dq of the first 256 rows and dk, dv of
+    the first 256 keys of the selected units, whose gradients gather every later query (the
+    inter-chunk kernels' work); the oracle computes the units' whole forward for them."""
+    announce(f"bwd full-size {name}, first keys")
+    x = synth.make_inputs(name)
     got = run_bwd(x)
-    ref = oracle_bwd_for(x, unit_mask=_unit_mask(x["workload"], [(0, 5), (2, 11)]), window=-256)
+    ref = oracle_bwd_for(x, unit_mask=_unit_mask(x["workload"], units), window=-256)
     e = {n: err_rms(got[n], ref[n]) for n in ("dq", "dk", "dv")}
     print("errors:", {k: f"{v:.2e}" for k, v in e.items()}, flush=True)
     for n, v in e.items():
         assert v <= TOL, f"{n}: {v:.3e}"
+
+
+def test_bwd_full_size_dw():
+    """Training shape: d(o_norm_weight) is a sum over every row of every head.  With dO zero
+    outside the last 256 rows of two units (the gradient is linear in dO), only those rows
+    contribute, and the oracle computes exactly them; dq, dk, dv, dg of the units are checked
+    on the same input."""
+    announce("bwd full-size train, dw")
+    x = dict(synth.make_inputs("train"))
+    wl = x["workload"]
+    units = [(1, 4), (3, 9)]
+    G = wl.Hq // wl.Hkv
+    keep = np.zeros(x["dO"].shape, bool)
+    for s_, c in units:
+        keep[s_, wl.T - 256:, c * G:(c + 1) * G] = True
+    x["dO"] = np.where(keep, x["dO"], 0.0).astype(x["dO"].dtype)
+    x["w"] = synth.make_inputs("quick")["w"][:wl.dv].copy()  # a weight that is not all ones
+    got = run_bwd(x)
+    ref = oracle_bwd_for(x, unit_mask=_unit_mask(wl, units), window=256)
+    check_bwd(got, ref, check_dw=True)
 
 
 # The gate given as raw logits: dg is the gradient with respect to the logits.

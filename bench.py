@@ -1,15 +1,18 @@
 """Benchmark of the FiX attention hot path (forward + backward) on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
-One step = fix_attn_fwd + fix_attn_bwd over the training-shape workload
-(B=4, T=8192, Hq=Hkv=16, dk=dv=128, bf16 inputs and outputs, gates
-logsigmoid(N(4, 2))), with inputs, outputs and workspaces resident in HBM
-before the timed region.  Before anything is timed the same inputs pass a
-parity check against the fp64 oracle on a sampled set of rows.  Prints one
-JSON line.  Throughput counts algorithmic flops (FlashAttention convention,
-causal pairs only): forward 2*(dk+dv) per pair and head, backward
-2*(3*dk+2*dv).
+One step = fix_attn_fwd + fix_attn_bwd over one workload (default: the
+training shape, B=4, T=8192, Hq=Hkv=16, dk=dv=128, bf16 inputs and outputs,
+gates logsigmoid(N(4, 2))), with inputs, outputs and workspaces resident in
+HBM before the timed region; the backward returns d(o_norm_weight) (and
+d(o_gate) where the workload has an output gate).  Before anything is timed
+the same inputs pass a parity check against the fp64 oracle on a sampled set
+of rows.  Prints one JSON line.  Throughput counts algorithmic flops
+(FlashAttention convention, causal pairs only): forward 2*(dk+dv) per pair and
+head, backward 2*(3*dk+2*dv).  --workload picks any of the synthetic
+workloads (tiny, quick, varlen, train, long_d16 .. long_d128); tiny is
+forward only.
 """
 from __future__ import annotations
 
@@ -80,49 +83,82 @@ def hip():
     return lib
 
 
+def sample_units(wl, nseq):
+    """(sequence, kv head) units checked by the parity gate: the first and the last."""
+    mask = np.zeros((nseq, wl.Hkv), np.uint8)
+    mask[0, 0] = mask[nseq - 1, wl.Hkv - 1] = 1
+    return mask
+
+
 def parity_gate(x, d, F, torch, logits=False):
-    """Sampled parity against the oracle (last 64 rows of two (sequence, kv head) units)."""
+    """Sampled parity against the oracle: the last 64 rows (and keys) of two (sequence, kv head)
+    units, or every row of a workload the oracle runs in seconds (the forward-only one)."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     import oracle as O
     from gpu_util import err_rms
-    o, m, rstd, xx = F.forward(d["q"], d["k"], d["v"], d["g"], o_norm=True, out_dtype=torch.float32,
-                               gate_logits=logits)
-    dq, dk, dv, dg, _, _ = F.backward(d["q"], d["k"], d["v"], d["g"], m, rstd, xx, d["dO"], o_norm=True,
-                                      out_dtype=torch.float32, gate_logits=logits)
-    torch.cuda.synchronize()
     wl = x["workload"]
-    mask = np.zeros((wl.B, wl.Hkv), np.uint8)
-    mask[0, 0] = mask[wl.B - 1, wl.Hkv - 1] = 1
+    cu = x["cu_seqlens"]
+    nseq = wl.B if cu is None else len(cu) - 1
+    full = not wl.backward
+    mask = None if full else sample_units(wl, nseq)
+    win = 0 if full else 64
     g = x["g_logits"] if logits else x["g"]
-    rf = O.oracle_fwd(x["q"], x["k"], x["v"], g, unit_mask=mask, window=64, gate_logits=logits)
-    rb = O.oracle_bwd(x["q"], x["k"], x["v"], g, x["dO"], unit_mask=mask, window=64, gate_logits=logits)
+    o, m, rstd, xx = F.forward(d["q"], d["k"], d["v"], d["g"], d["cu"], o_norm=True, o_norm_weight=d["w"],
+                               o_gate=d["z"], out_dtype=torch.float32, gate_logits=logits)
+    torch.cuda.synchronize()
+    rf = O.oracle_fwd(x["q"], x["k"], x["v"], g, cu, w=x["w"], z=x["z"], unit_mask=mask, window=win,
+                      gate_logits=logits)
     errs = {"o": err_rms(o.cpu().numpy(), rf["o"])}
-    for n, t in (("dq", dq), ("dk", dk), ("dv", dv), ("dg", dg)):
-        errs[n] = err_rms(t.cpu().numpy(), rb[n])
+    if wl.backward:
+        dq, dk, dv, dg, _, _ = F.backward(d["q"], d["k"], d["v"], d["g"], m, rstd, xx, d["dO"], d["cu"],
+                                          o_norm=True, o_norm_weight=d["w"], o_gate=d["z"],
+                                          out_dtype=torch.float32, gate_logits=logits)
+        torch.cuda.synchronize()
+        rb = O.oracle_bwd(x["q"], x["k"], x["v"], g, x["dO"], cu, w=x["w"], z=x["z"], unit_mask=mask,
+                          window=win, gate_logits=logits)
+        for n, t in (("dq", dq), ("dk", dk), ("dv", dv), ("dg", dg)):
+            errs[n] = err_rms(t.cpu().numpy(), rb[n])
     ok = all(v <= (5e-3 if n == "dg" else 1e-2) for n, v in errs.items())
     return ok, errs
 
 
 def cpu_baseline(x, logits=False):
-    """The fp64 oracle, fwd + bwd, on four heads of one batch row of the same workload, full length."""
+    """The fp64 oracle, forward (+ backward), on a bounded slice of the same workload: whole
+    sequences of the first batch row (or packed sequence), a few heads of one kv group."""
     import oracle as O
-    NH = 4
-    sl = lambda a: np.ascontiguousarray(a[:1, :, :NH])
-    q, k, v, g, dO = (sl(x[n]) for n in ("q", "k", "v", "g_logits" if logits else "g", "dO"))
+    wl = x["workload"]
+    cu = x["cu_seqlens"]
+    G = wl.Hq // wl.Hkv
+    if wl.name == "train":
+        nh, nk = 4, 4          # four heads of batch row 0 (about 15 s on 16 threads)
+    else:
+        nh, nk = min(G, 4), 1  # the first kv head and up to four of its q heads
+        if wl.T >= 32768:
+            nh = 1             # one head of the 32k-token sequence
+    if cu is not None:
+        L0 = int(cu[1])
+        sl = lambda a, h: np.ascontiguousarray(a[:, :L0, :h])
+        lengths = [L0]
+    else:
+        sl = lambda a, h: np.ascontiguousarray(a[:1, :, :h])
+        lengths = [wl.T]
+    q = sl(x["q"], nh)
+    k, v, g = (sl(x[n], nk) for n in ("k", "v", "g_logits" if logits else "g"))
+    z = None if x["z"] is None else sl(x["z"], nh)
     O.load()
     t0 = time.perf_counter()
-    O.oracle_fwd(q, k, v, g, gate_logits=logits)
+    O.oracle_fwd(q, k, v, g, w=x["w"], z=z, gate_logits=logits)
     t1 = time.perf_counter()
-    O.oracle_bwd(q, k, v, g, dO, gate_logits=logits)
+    if wl.backward:
+        O.oracle_bwd(q, k, v, g, sl(x["dO"], nh), w=x["w"], z=z, gate_logits=logits)
     t2 = time.perf_counter()
-    wl = x["workload"]
-    pairs = wl.T * (wl.T + 1) // 2 * NH
-    flops = (2 * (wl.dk + wl.dv) + 2 * (3 * wl.dk + 2 * wl.dv)) * pairs
+    pairs = sum(L * (L + 1) // 2 for L in lengths) * nh
+    flops = 2 * (wl.dk + wl.dv) * pairs + (2 * (3 * wl.dk + 2 * wl.dv) * pairs if wl.backward else 0)
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": flops / (t2 - t0) / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"heads 0-{NH - 1} of batch row 0 of the workload: B=1 T={wl.T} H={NH} d={wl.dk}, "
-                      f"fwd {t1 - t0:.1f} s + "
-                      f"bwd {t2 - t1:.1f} s (the backward recomputes the forward)"}
+            "sample": f"{nh} q head(s) of the first sequence (L={lengths[0]}, dk={wl.dk}, dv={wl.dv}): "
+                      f"fwd {t1 - t0:.1f} s" + (f" + bwd {t2 - t1:.1f} s (the backward recomputes the forward)"
+                                                 if wl.backward else "")}
 
 
 COPY_BYTES = 1 << 30
@@ -237,14 +273,61 @@ def decode_bench(args, x, F, torch):
     print(json.dumps(out), flush=True)
 
 
+PEAK_EXP_GEXPS = 1024 * 64 / 8 * 2.4  # v_exp_f32: 8 cycles per wave64 instruction
+
+
+def peak_probe(torch):
+    """Measured peaks: independent 32x32x16 bf16 products on every SIMD, independent v_exp_f32
+    chains, and a 16-byte-per-lane copy of 1 GiB (libfixprobe.so, separate from the library)."""
+    lib = ctypes.CDLL(os.path.join(ROOT, "gated_softmax_attention_amd", "libfixprobe.so"))
+    lib.fix_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.fix_probe_exp.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.fix_probe_copy.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    st = torch.cuda.current_stream().cuda_stream
+    blocks = 256 * 4
+    out = torch.empty(blocks * 256, device="cuda")
+
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        best = None
+        for _ in range(reps):
+            e0.record()
+            assert fn() == 0
+            e1.record()
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) * 1e-3
+            best = t if best is None else min(best, t)
+        return best
+
+    it_m, it_e = 2000, 100000
+    t_m = timed(lambda: lib.fix_probe_mfma(blocks, it_m, out.data_ptr(), st))
+    t_e = timed(lambda: lib.fix_probe_exp(blocks, it_e, out.data_ptr(), st))
+    src = torch.ones(COPY_BYTES // 4, device="cuda")
+    dst = torch.empty_like(src)
+    t_c = timed(lambda: lib.fix_probe_copy(256 * 8, src.data_ptr(), dst.data_ptr(), COPY_BYTES, st))
+    mfma = blocks * 4 * it_m * 4 * 32768 / t_m / 1e12
+    exps = blocks * 256 * it_e * 8 / t_e / 1e9
+    copy = 2 * COPY_BYTES / t_c / 1e9
+    print(json.dumps({"mfma_bf16_tflops": round(mfma, 1), "mfma_frac_of_spec": round(mfma / PEAK_BF16_TFLOPS, 4),
+                      "exp_gexps": round(exps, 1), "exp_frac_of_model": round(exps / PEAK_EXP_GEXPS, 4),
+                      "copy_gbs": round(copy, 1), "copy_frac_of_spec": round(copy / PEAK_HBM_GBS, 4),
+                      "mfma_s": t_m, "exp_s": t_e, "copy_s": t_c}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=WORKLOAD,
+                    help="tiny, quick, varlen, train (default), long_d16, long_d32, long_d64, long_d128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--gate-logits", action="store_true",
                     help="pass the gate as raw logits (logsigmoid applied inside the kernels)")
+    ap.add_argument("--peak-probe", action="store_true",
+                    help="only measure the matrix-product, exponential and copy peaks (libfixprobe.so)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (HBM counter calibration)")
     ap.add_argument("--scalar-gate", action="store_true",
@@ -262,10 +345,13 @@ def main():
     if args.copy_probe:
         copy_probe(torch)
         return
+    if args.peak_probe:
+        peak_probe(torch)
+        return
     import gated_softmax_attention_amd as F
     from gated_softmax_attention_amd import synth
 
-    x = synth.make_inputs(WORKLOAD)
+    x = synth.make_inputs(args.workload)
     if args.scalar_gate:
         x = dict(x)
         x["g"] = np.ascontiguousarray(x["g"][..., 0])
@@ -274,9 +360,11 @@ def main():
         decode_bench(args, x, F, torch)
         return
     wl = x["workload"]
-    dev = lambda a, dt=torch.bfloat16: torch.from_numpy(np.ascontiguousarray(a)).to(dt).cuda()
-    d = {n: dev(x[n]) for n in ("q", "k", "v", "dO")}
+    dt = torch.bfloat16 if wl.in_dtype == "bf16" else torch.float32
+    dev = lambda a, t=dt: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(t).cuda()
+    d = {n: dev(x[n]) for n in ("q", "k", "v", "dO", "w", "z")}
     d["g"] = dev(x["g_logits"] if args.gate_logits else x["g"], torch.float32)
+    d["cu"] = None if x["cu_seqlens"] is None else torch.from_numpy(x["cu_seqlens"]).cuda()
     print(f"[bench] inputs resident: {wl}{' (gate as logits)' if args.gate_logits else ''}", file=sys.stderr,
           flush=True)
 
@@ -287,40 +375,43 @@ def main():
 
     B, T, Hq, dk = d["q"].shape
     Hkv, dv = d["k"].shape[2], d["v"].shape[3]
-    bf = torch.bfloat16
-    o = torch.empty(B, T, Hq, dv, dtype=bf, device="cuda")
+    o = torch.empty(B, T, Hq, dv, dtype=dt, device="cuda")
     m = torch.empty(B, T, Hq, device="cuda")
     rstd = torch.empty(B, T, Hq, device="cuda")
     xx = torch.empty(B, T, Hq, dv, device="cuda")
-    dq, dkk, dvv = torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"])
-    dg = torch.empty_like(d["g"])
-    desc = F.make_desc(d["q"], d["k"], d["v"], o_norm=True, gate_logits=args.gate_logits,
+    if wl.backward:
+        dq, dkk, dvv = torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"])
+        dg = torch.empty_like(d["g"])
+        dw = torch.empty(dv, device="cuda")
+        dz = None if d["z"] is None else torch.empty_like(d["z"])
+    desc = F.make_desc(d["q"], d["k"], d["v"], d["cu"], o_norm=True, gate_logits=args.gate_logits,
                        gate_scalar=args.scalar_gate)
     wf, wb = F.fix_attn_fwd_workspace_size(desc), F.fix_attn_bwd_workspace_size(desc)
     ws_f = torch.empty(wf, dtype=torch.uint8, device="cuda")
-    ws_b = torch.empty(wb, dtype=torch.uint8, device="cuda")
+    ws_b = torch.empty(wb if wl.backward else 1, dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
     lib = F.library()
-    lib.fix_attn_set_event_trace.argtypes = [ctypes.c_void_p, ctypes.c_int]
-    lib.fix_attn_event_trace_count.restype = ctypes.c_int
-    lib.fix_attn_event_trace_label.restype = ctypes.c_char_p
-    lib.fix_attn_event_trace_label.argtypes = [ctypes.c_int]
 
-    def step():
-        F.fix_attn_fwd(desc, d["q"], d["k"], d["v"], d["g"], None, None, o, m, rstd, xx, ws_f, wf, stream)
-        F.fix_attn_bwd(desc, d["q"], d["k"], d["v"], d["g"], None, None, m, rstd, xx, d["dO"], dq, dkk, dvv, dg,
-                       None, None, ws_b, wb, stream)
+    def fwd():
+        F.fix_attn_fwd(desc, d["q"], d["k"], d["v"], d["g"], d["w"], d["z"], o, m, rstd,
+                       xx if wl.backward else None, ws_f, wf, stream)
+
+    def bwd():
+        F.fix_attn_bwd(desc, d["q"], d["k"], d["v"], d["g"], d["w"], d["z"], m, rstd, xx, d["dO"], dq, dkk, dvv, dg,
+                       dw, dz, ws_b, wb, stream)
 
     for _ in range(args.warmup):
-        step()
+        fwd()
+        if wl.backward:
+            bwd()
     torch.cuda.synchronize()
 
     # Per-kernel events recorded by the library on its stream during the timed steps.
     h = hip()
-    cap = 16
+    cap = 24
     ev = [[(ctypes.c_void_p * cap)() for _ in range(2)] for _ in range(args.steps)]
-    for s in ev:
-        for arr in s:
+    for s_ in ev:
+        for arr in s_:
             for i in range(cap):
                 e = ctypes.c_void_p()
                 assert h.hipEventCreate(ctypes.byref(e)) == 0
@@ -332,68 +423,99 @@ def main():
     t0 = time.perf_counter()
     for k in range(args.steps):
         lib.fix_attn_set_event_trace(ctypes.cast(ev[k][0], ctypes.c_void_p), cap)
-        F.fix_attn_fwd(desc, d["q"], d["k"], d["v"], d["g"], None, None, o, m, rstd, xx, ws_f, wf, stream)
+        fwd()
         counts[0] = lib.fix_attn_event_trace_count()
         if labels[0] is None:
             labels[0] = [lib.fix_attn_event_trace_label(i).decode() for i in range(1, counts[0])]
-        lib.fix_attn_set_event_trace(ctypes.cast(ev[k][1], ctypes.c_void_p), cap)
-        F.fix_attn_bwd(desc, d["q"], d["k"], d["v"], d["g"], None, None, m, rstd, xx, d["dO"], dq, dkk, dvv, dg,
-                       None, None, ws_b, wb, stream)
-        counts[1] = lib.fix_attn_event_trace_count()
-        if labels[1] is None:
-            labels[1] = [lib.fix_attn_event_trace_label(i).decode() for i in range(1, counts[1])]
+        if wl.backward:
+            lib.fix_attn_set_event_trace(ctypes.cast(ev[k][1], ctypes.c_void_p), cap)
+            bwd()
+            counts[1] = lib.fix_attn_event_trace_count()
+            if labels[1] is None:
+                labels[1] = [lib.fix_attn_event_trace_label(i).decode() for i in range(1, counts[1])]
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     lib.fix_attn_set_event_trace(None, 0)
     ms_step = (t1 - t0) * 1e3 / args.steps
 
     per_kernel = {}
+    side_ms = [[], []]
     for k in range(args.steps):
-        for side in (0, 1):
+        for side in (0, 1) if wl.backward else (0,):
+            tot = 0.0
             for i in range(1, counts[side]):
                 t = ctypes.c_float()
                 assert h.hipEventElapsedTime(ctypes.byref(t), ev[k][side][i - 1], ev[k][side][i]) == 0
                 per_kernel.setdefault(labels[side][i - 1], []).append(t.value)
+                tot += t.value
+            side_ms[side].append(tot)
     avg = {n: sum(v) / len(v) for n, v in per_kernel.items()}
 
-    pc = pair_counts([T] * B)
+    cu = x["cu_seqlens"]
+    lengths = [T] * B if cu is None else [int(cu[i + 1] - cu[i]) for i in range(len(cu) - 1)]
+    pc = pair_counts(lengths)
     heads = Hq
     fwd_flops = 2 * (dk + dv) * pc["all"] * heads
-    bwd_flops = 2 * (3 * dk + 2 * dv) * pc["all"] * heads
+    bwd_flops = 2 * (3 * dk + 2 * dv) * pc["all"] * heads if wl.backward else 0
     total = fwd_flops + bwd_flops
     tflops = total / (ms_step * 1e-3) / 1e12
-    # Algorithmic flops of each kernel: its share of the 2 forward and 5 backward products.
+    # Algorithmic flops per head of each kernel (its share of the 2 forward and 5 backward products)
+    # and the exponentials it must evaluate (one per pair for every kernel that forms P).
     alg = {
-        "fix_fwd": fwd_flops,
-        "fox_fwd": fwd_flops,
-        "bwd_dq": 2 * (2 * dk + dv) * pc["inter"] * heads,        # S, dP, dQ on pairs in different chunks
-        "bwd_dkv": 2 * (dk + dv) * pc["far"] * heads,             # dV, dK on pairs two or more chunks apart
-        "bwd_intra_dq": 2 * (2 * dk + dv) * pc["same"] * heads,
-        "bwd_intra_dkv": 2 * (dk + dv) * (pc["same"] + pc["adj"]) * heads,
-        "fox_bwd_dq": 2 * (2 * dk + dv) * pc["all"] * heads,      # S, dP, dQ on every pair
-        "fox_bwd_dkv": 2 * (dk + dv) * pc["all"] * heads,         # dV, dK on every pair
+        "fix_fwd": (2 * (dk + dv) * pc["all"], pc["all"]),
+        "fox_fwd": (2 * (dk + dv) * pc["all"], pc["all"]),
+        "bwd_dq": (2 * (2 * dk + dv) * pc["inter"], pc["inter"]),      # S, dP, dQ on pairs in different chunks
+        "bwd_dkv": (2 * (dk + dv) * pc["far"], pc["far"]),             # dV, dK on pairs two or more chunks apart
+        "bwd_intra_dq": (2 * (2 * dk + dv) * pc["same"], pc["same"]),
+        "bwd_intra_dkv": (2 * (dk + dv) * (pc["same"] + pc["adj"]), pc["same"] + pc["adj"]),
+        "fox_bwd_dq": (2 * (2 * dk + dv) * pc["all"], pc["all"]),      # S, dP, dQ on every pair
+        "fox_bwd_dkv": (2 * (dk + dv) * pc["all"], pc["all"]),         # dV, dK on every pair
     }
     dom = max(avg, key=avg.get)
     roof = None
     if dom in alg:
-        ach = alg[dom] / (avg[dom] * 1e-3) / 1e12
-        roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(dom),
-                "avg_launch_ms": round(avg[dom], 4)}
+        fl, npair = alg[dom]
+        fl, nexp = fl * heads, npair * heads
+        sec = avg[dom] * 1e-3
+        t_mfma = fl / (PEAK_BF16_TFLOPS * 1e12)
+        t_exp = nexp / (PEAK_EXP_GEXPS * 1e9)
+        if t_exp > t_mfma:   # the exponentials, not the products, bound this kernel at its head dims
+            ach = nexp / sec / 1e9
+            roof = {"bound": "alu", "kernel": dom, "achieved": round(ach, 1), "peak": round(PEAK_EXP_GEXPS, 1),
+                    "unit": "Gexp/s", "frac": round(ach / PEAK_EXP_GEXPS, 4),
+                    "mfma_frac": round(fl / sec / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        else:
+            ach = fl / sec / 1e12
+            roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
+        roof["traffic"] = measured_traffic(dom)
+        roof["avg_launch_ms"] = round(avg[dom], 4)
+    fwd_ms = sum(side_ms[0]) / len(side_ms[0])
+    bwd_ms = sum(side_ms[1]) / len(side_ms[1]) if wl.backward else None
+    desc_w = (f"{wl.name}: B={B} T={T}" + (f" packed {len(lengths)} seqs" if cu is not None else "")
+              + f" Hq={Hq} Hkv={Hkv} dk={dk} dv={dv} {wl.in_dtype} in/{wl.in_dtype} out, "
+              f"g=logsigmoid(N({wl.gate_mu},{wl.gate_sd}))"
+              + (" passed as logits (logsigmoid in the kernels)" if args.gate_logits else "")
+              + (", scalar per token and head (channel 0)" if args.scalar_gate else "")
+              + ", o_norm" + (" with d(o_norm_weight)" if wl.backward else "")
+              + (", o_gate" + (" with d(o_gate)" if wl.backward else "") if d["z"] is not None else "")
+              + (", fwd+bwd" if wl.backward else ", fwd only"))
+    metric = METRIC if wl.name == WORKLOAD and wl.backward else (
+        f"FiX attn {'fwd+bwd' if wl.backward else 'fwd'} TFLOP/s (and % MFMA peak), workload {wl.name}, 1 GPU")
     out = {
-        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "metric": metric, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": f"{WORKLOAD}: B={B} T={T} Hq={Hq} Hkv={Hkv} dk={dk} dv={dv} bf16 in/out, "
-                               f"g=logsigmoid(N({wl.gate_mu},{wl.gate_sd}))"
-                               f"{' passed as logits (logsigmoid in the kernels)' if args.gate_logits else ''}"
-                               f"{', scalar per token and head (channel 0)' if args.scalar_gate else ''}, "
-                               f"o_norm, fwd+bwd",
+        "vs_baseline": None, "dtype": "bf16" if wl.in_dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": desc_w,
                    "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
                    "fwd_flops": fwd_flops, "bwd_flops": bwd_flops,
+                   "fwd_ms": round(fwd_ms, 4), "bwd_ms": None if bwd_ms is None else round(bwd_ms, 4),
+                   "fwd_tflops": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 2),
                    "kernel_ms": {n: round(v, 4) for n, v in sorted(avg.items(), key=lambda kv: -kv[1])}},
         "roofline": roof,
     }
+    if cu is not None:
+        out["config"]["cu_seqlens"] = [int(c) for c in cu]
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host ...", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(x, logits=args.gate_logits)

@@ -80,7 +80,26 @@ def build(force: bool = True, jobs: int | None = None, verbose: bool = True) -> 
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
+    build_probe(verbose=verbose)
     return LIB
+
+
+PROBE_SRC = os.path.join(HERE, "probe", "peak_probe.hip")
+PROBE_LIB = os.path.join(HERE, "libfixprobe.so")
+
+
+def build_probe(verbose: bool = True) -> str:
+    """The peak-probe library (matrix-product, exponential and copy loops) that
+    `bench.py --peak-probe` times; separate from the attention library."""
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [HIPCC, "-x", "hip", *COMMON_FLAGS, "-shared", PROBE_SRC, "-o", tmp, "-Wl,-rpath,/opt/rocm/lib"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {PROBE_SRC}:\n{res.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    if verbose:
+        print(f"built {PROBE_LIB}")
+    return PROBE_LIB
 
 
 if __name__ == "__main__":

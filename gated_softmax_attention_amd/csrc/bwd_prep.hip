@@ -401,15 +401,29 @@ __global__ void __launch_bounds__(256) k_bwd_prep(PrepArgs a) {
   }
 }
 
-// dw[d] = sum over blocks of the partials, in a fixed order.
-__global__ void __launch_bounds__(256) k_dw_reduce(const float *__restrict__ part, const int *__restrict__ counts,
-                                                   int Hkv, int dv, float *__restrict__ dw) {
-  const int d = blockIdx.x * 256 + threadIdx.x;
-  if (d >= dv) return;
+// dw[d] = sum over blocks of the partials, in a fixed order.  One workgroup of
+// 1024 threads: thread t owns channel t % dv of partial rows t / dv, t / dv +
+// 1024 / dv, ... (each wave reads whole rows of consecutive channels, eight
+// independent sums per thread), then the 1024 / dv groups meet in LDS in
+// group order.
+__global__ void __launch_bounds__(1024) k_dw_reduce(const float *__restrict__ part, const int *__restrict__ counts,
+                                                    int Hkv, int dv, float *__restrict__ dw) {
+  __shared__ float red[1024];
+  const int t = threadIdx.x, d = t % dv, grp = t / dv, ng = 1024 / dv;
   const int nb = counts[0] * Hkv;
-  float acc = 0.f;
-  for (int b = 0; b < nb; ++b) acc += part[(int64_t)b * dv + d];
-  dw[d] = acc;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int b = grp;
+  for (; b + 7 * ng < nb; b += 8 * ng)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] += part[(int64_t)(b + u * ng) * dv + d];
+  for (int u = 0; b < nb; b += ng, ++u) acc[u & 7] += part[(int64_t)b * dv + d];
+  red[t] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+  __syncthreads();
+  if (grp == 0) {
+    float s = 0.f;
+    for (int q = 0; q < ng; ++q) s += red[q * dv + d];
+    dw[d] = s;
+  }
 }
 
 // dg_t = sum over t' >= t of the same sequence of dG_t' (the gate enters
@@ -570,7 +584,8 @@ hipError_t launch_dg_scan(int dv, const float *dG, const float *logits, const Pl
 }
 
 hipError_t launch_dw_reduce(const float *part, const int *counts, int Hkv, int dv, float *dw, hipStream_t st) {
-  hipLaunchKernelGGL(k_dw_reduce, dim3((dv + 255) / 256), dim3(256), 0, st, part, counts, Hkv, dv, dw);
+  if (dv < 1 || dv > 1024 || 1024 % dv) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_dw_reduce, dim3(1), dim3(1024), 0, st, part, counts, Hkv, dv, dw);
   return hipGetLastError();
 }
 

@@ -1,0 +1,65 @@
+// Measured peaks of MI355X (gfx950) for the roofline denominators the
+// benchmark reports beside the published ones: a loop of independent
+// 32x32x16 bf16 matrix products, a loop of independent v_exp_f32 chains, and
+// a plain 16-byte-per-lane device copy.  Not part of the attention library:
+// only `bench.py --peak-probe` loads this.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Four independent accumulator chains per wave, iters products each.
+__global__ void __launch_bounds__(256) k_probe_mfma(int iters, float *out) {
+  const int t = threadIdx.x;
+  bf16x8 a, b;
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(1.0f + 1e-3f * (float)((t + i) & 7));
+    b[i] = (__bf16)(1e-3f * (float)((t * 3 + i) & 7));
+  }
+  f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (int i = 0; i < iters; ++i) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+  }
+  float s = 0.f;
+  for (int j = 0; j < 16; ++j) s += c0[j] + c1[j] + c2[j] + c3[j];
+  out[(int64_t)blockIdx.x * 256 + t] = s;
+}
+
+// Eight independent chains x <- exp2(-x) per lane (values stay in (0.5, 1]).
+__global__ void __launch_bounds__(256) k_probe_exp(int iters, float *out) {
+  const int t = threadIdx.x;
+  float x[8];
+  for (int j = 0; j < 8; ++j) x[j] = 1e-3f * (float)((t + j) & 63);
+  for (int i = 0; i < iters; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = __builtin_amdgcn_exp2f(-x[j]);
+  float s = 0.f;
+  for (int j = 0; j < 8; ++j) s += x[j];
+  out[(int64_t)blockIdx.x * 256 + t] = s;
+}
+
+__global__ void __launch_bounds__(256) k_probe_copy(const uint4 *__restrict__ src, uint4 *__restrict__ dst,
+                                                    int64_t n16) {
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n16; e += (int64_t)gridDim.x * 256) dst[e] = src[e];
+}
+
+extern "C" {
+// Grid sizes: enough workgroups for several waves per SIMD on every CU.
+int fix_probe_mfma(int blocks, int iters, float *out, void *stream) {
+  hipLaunchKernelGGL(k_probe_mfma, dim3(blocks), dim3(256), 0, (hipStream_t)stream, iters, out);
+  return (int)hipGetLastError();
+}
+int fix_probe_exp(int blocks, int iters, float *out, void *stream) {
+  hipLaunchKernelGGL(k_probe_exp, dim3(blocks), dim3(256), 0, (hipStream_t)stream, iters, out);
+  return (int)hipGetLastError();
+}
+int fix_probe_copy(int blocks, const void *src, void *dst, int64_t bytes, void *stream) {
+  hipLaunchKernelGGL(k_probe_copy, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const uint4 *)src, (uint4 *)dst,
+                     bytes / 16);
+  return (int)hipGetLastError();
+}
+}

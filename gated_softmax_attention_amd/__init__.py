@@ -84,6 +84,8 @@ def _load():
     lib.fix_decode_append.restype = ctypes.c_int
     lib.fix_decode_step.argtypes = [DD, P, P, P, P, P, P, P, S, P]
     lib.fix_decode_step.restype = ctypes.c_int
+    lib.fix_decode_step_noalloc.argtypes = [DD, P, P, P, P, P, P, P]
+    lib.fix_decode_step_noalloc.restype = ctypes.c_int
     lib.fix_attn_status_string.argtypes = [ctypes.c_int]
     lib.fix_attn_status_string.restype = ctypes.c_char_p
     lib.fix_attn_last_hip_error.argtypes = []
@@ -370,3 +372,16 @@ class DecodeCache:
                                      _ptr(self.ws), self.ws.numel(), _stream())
         _check("fix_decode_step", st)
         return o, m
+
+    def step_noalloc(self, q, o, m, o_norm_weight=None, o_gate=None):
+        """fix_decode_step_noalloc into caller-given o [B,Hq,dv] and m [B,Hq] (or None): the same
+        step with the library's own scratch, so no device memory is allocated."""
+        d = self.desc
+        if tuple(q.shape) != (d.B, d.Hq, d.dk) or q.dtype != self.dtype or not q.is_contiguous():
+            raise ValueError("q must be a contiguous [B, Hq, dk] tensor of the cache dtype")
+        if tuple(o.shape) != (d.B, d.Hq, d.dv) or o.dtype != self.out_dtype or not o.is_contiguous():
+            raise ValueError("o must be a contiguous [B, Hq, dv] tensor of the output dtype")
+        st = _load().fix_decode_step_noalloc(ctypes.byref(d), _ptr(self.cache), _ptr(q),
+                                             _ptr(o_norm_weight) if d.o_norm else None, _ptr(o_gate), _ptr(o),
+                                             _ptr(m), _stream())
+        _check("fix_decode_step_noalloc", st)

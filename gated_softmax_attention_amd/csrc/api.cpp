@@ -7,6 +7,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "common.h"
 #include "launch.h"
@@ -215,6 +216,35 @@ size_t carve_decode_ws(Carve &cv, const fix_decode_desc *d, DecodeWs &w) {
   w.vto = cv.take<_Float16>(d->B * d->Hkv * d->dv * fix::CH);
   return cv.off;
 }
+
+// ---- scratch of the allocation-free decode step ----
+// One copy of this array lives on every GPU the library runs on; host code
+// must never pass its name to a kernel (that is a host-side stand-in): the
+// device address of each GPU's copy is resolved once per device and kept.
+static __device__ __align__(256) char scratch[FIX_DECODE_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_addr[kMaxDevices] = {};
+
+// Device address of the current device's copy of the scratch array.
+hipError_t decode_scratch(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return hipSuccess;
+}
+}  // namespace
 
 extern "C" {
 
@@ -526,6 +556,19 @@ fix_status fix_decode_step(const fix_decode_desc *d, const void *cache, const vo
                                    d->out_dtype == FIX_F32, d->o_norm != 0, d->eps, o, m, st);
   if (e == hipSuccess) e = trace_mark(st, "decode_combine");
   return e == hipSuccess ? FIX_OK : hip_fail(e);
+}
+
+fix_status fix_decode_step_noalloc(const fix_decode_desc *d, const void *cache, const void *q,
+                                   const void *o_norm_weight, const void *o_gate, void *o, float *m,
+                                   void *hip_stream) {
+  fix_status stt = fix_decode_validate(d);
+  if (stt != FIX_OK) return stt;
+  if (fix_decode_workspace_size(d) > FIX_DECODE_SCRATCH_BYTES) return FIX_E_WORKSPACE;
+  void *ws = nullptr;
+  hipError_t e = decode_scratch(&ws);
+  if (e != hipSuccess) return hip_fail(e);
+  // every byte of the step's scratch is written before it is read: nothing to clear
+  return fix_decode_step(d, cache, q, o_norm_weight, o_gate, o, m, ws, FIX_DECODE_SCRATCH_BYTES, hip_stream);
 }
 
 const char *fix_attn_status_string(fix_status s) {

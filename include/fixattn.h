@@ -205,6 +205,24 @@ fix_status fix_decode_append(const fix_decode_desc *d, void *cache, const void *
 fix_status fix_decode_step(const fix_decode_desc *d, const void *cache, const void *q, const void *o_norm_weight,
                            const void *o_gate, void *o, float *m, void *ws, size_t ws_bytes, void *hip_stream);
 
+/* fix_decode_step for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The same kernels and results as fix_decode_step, with the step's scratch
+ * taken from a device array inside the library (FIX_DECODE_SCRATCH_BYTES per
+ * GPU, held by each GPU the library runs on until the process ends) instead
+ * of a caller buffer.  No allocation is made.  The first call on a device
+ * resolves that device's copy of the array (a runtime query, best made
+ * before any graph capture); every later call on the device reuses it.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (different streams without ordering) race and give undefined results.
+ * FIX_E_WORKSPACE: fix_decode_workspace_size(d) > FIX_DECODE_SCRATCH_BYTES.
+ * FIX_E_HIP: the current device or the array's address could not be
+ * queried. */
+#define FIX_DECODE_SCRATCH_BYTES ((size_t)32 << 20)
+fix_status fix_decode_step_noalloc(const fix_decode_desc *d, const void *cache, const void *q,
+                                   const void *o_norm_weight, const void *o_gate, void *o, float *m,
+                                   void *hip_stream);
+
 /* Opt-in launch timing for benchmarks (host side, per calling thread).
  * With events non-NULL and capacity > 0, every later fix_attn_fwd /
  * fix_attn_bwd / fix_decode_step call on this thread records events[0] on its stream before

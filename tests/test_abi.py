@@ -14,7 +14,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def declared_functions():
     src = open(os.path.join(ROOT, "include", "fixattn.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(fix_attn_\w+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(fix_(?:attn|decode)_\w+)\s*\(", src)))
 
 
 def test_library_exports_every_declared_function():
@@ -188,3 +188,16 @@ def test_decode_descriptor_layout_matches_header(tmp_path):
     got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
     want = [ctypes.sizeof(F.fix_decode_desc)] + [getattr(F.fix_decode_desc, n).offset for n in fields]
     assert got == want
+
+
+def test_decode_step_noalloc_rejects_oversize():
+    """The allocation-free decode step refuses, before anything runs, a shape whose scratch
+    exceeds the library's per-GPU array (FIX_DECODE_SCRATCH_BYTES = 32 MiB)."""
+    lib = F.library()
+    d = F.fix_decode_desc()
+    d.B, d.cap, d.Hq, d.Hkv, d.dk, d.dv = 256, 4096, 64, 64, 128, 128
+    d.in_dtype, d.out_dtype, d.eps = F.FIX_BF16, F.FIX_F32, 1e-5
+    assert lib.fix_decode_validate(ctypes.byref(d)) == F.FIX_OK
+    assert lib.fix_decode_workspace_size(ctypes.byref(d)) > (32 << 20)
+    st = lib.fix_decode_step_noalloc(ctypes.byref(d), None, None, None, None, None, None, None)
+    assert st == F.FIX_E_WORKSPACE

@@ -192,6 +192,19 @@ template <int ROWS, int RB> struct LdsTile {
   }
   // Copy t of the tile (t < NW), untracked (dma16_untracked, defined below).
   __device__ static void dma_piece_untracked(char *lds, const u32x4 &src, const uint32_t (&o)[NW], int t, int wave);
+  // The same split over the W waves of a larger workgroup (NWW copies per wave).
+  template <int W> struct Waves {
+    static constexpr int NWW = NI < W ? 1 : (NI + W - 1) / W;
+    __device__ static int piece(int t, int wave) { return NI < W ? wave % NI : min(wave + W * t, NI - 1); }
+    __device__ static void lane_offsets(uint32_t stride, int wave, int lane, uint32_t (&o)[NWW]) {
+#pragma unroll
+      for (int t = 0; t < NWW; ++t) {
+        const int p = piece(t, wave) * 64 + lane, r = p / CPR, pc = p % CPR;
+        o[t] = (uint32_t)r * stride + (uint32_t)((pc ^ swz(r)) << 4);
+      }
+    }
+    __device__ static void dma_untracked(char *lds, const u32x4 &src, const uint32_t (&o)[NWW], int wave);
+  };
   // Copy the tile.  `wave` must be wave-uniform (an SGPR value).
   __device__ static void dma(char *lds, rsrc_t src, const uint32_t (&o)[NW], int wave) {
 #pragma unroll
@@ -224,6 +237,37 @@ template <class T> __device__ inline f16x8 tr_frag(const char *tile, int row0, i
     h[t] = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(p));
   }
   return __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// LDS reads from a precomputed per-lane byte address (plus a constant), so a
+// loop body with a fixed buffer needs no address arithmetic: a 16-byte row
+// fragment, and one 8-byte transposing read (ds_read_b64_tr_b16; tr_frag's
+// layout, one of its two halves).
+typedef __attribute__((address_space(3))) char lds_char;
+__device__ inline const lds_char *lds_at(uint32_t a) { return (const lds_char *)(uintptr_t)a; }
+__device__ inline f16x8 lds_row16(uint32_t a) { return *(const __attribute__((address_space(3))) f16x8 *)lds_at(a); }
+__device__ inline f16x4 lds_tr8(uint32_t a) {
+  return __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                       (__attribute__((address_space(3))) s16x4 *)(uintptr_t)a));
+}
+// A value the compiler must treat as changed here: keeps it from hoisting
+// base + constant address sums out of a loop as registers of their own (the
+// constant then folds into each instruction's offset field).
+__device__ inline uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// Byte offsets within a tile T of the two 8-byte pieces tr_frag reads for
+// (row0 = 0, col0): the pieces for another row0 (a multiple of 16) are
+// row0 * RB further on.
+template <class T> __device__ inline void tr_offsets(int col0, int lane, uint32_t (&o)[2]) {
+  const int j = lane & 15, hh = lane >> 5, col = col0 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int row = 8 * t + 4 * hh + (j >> 2);
+    o[t] = (uint32_t)(T::off(row, col >> 3) + 2 * (col & 7));
+  }
 }
 
 // The same copies issued from inline assembly, which the compiler's wait-count
@@ -263,6 +307,13 @@ template <int ROWS, int RB>
 __device__ inline void LdsTile<ROWS, RB>::dma_piece_untracked(char *lds, const u32x4 &src, const uint32_t (&o)[NW], int t,
                                                               int wave) {
   dma16_untracked(lds + piece(t, wave) * 1024, src, o[t]);
+}
+template <int ROWS, int RB>
+template <int W>
+__device__ inline void LdsTile<ROWS, RB>::Waves<W>::dma_untracked(char *lds, const u32x4 &src,
+                                                                  const uint32_t (&o)[NWW], int wave) {
+#pragma unroll
+  for (int t = 0; t < NWW; ++t) dma16_untracked(lds + piece(t, wave) * 1024, src, o[t]);
 }
 
 // One copy of 16 (or 4) bytes per lane from a buffer resource at byte offset

@@ -21,6 +21,8 @@
 // probabilities come out as P / sigma with sigma = 2^-e the row scale of
 // delta, so every product with the scaled delta rows is unchanged.
 #pragma once
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -174,27 +176,35 @@ __global__ void __launch_bounds__(256, 2) k_fox_bwd_dq(FoxBwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // dk, dv and the column sums of dS (over the head group).  Workgroup = 128
-// keys (4 waves x 32) of one kv head; for each q head of the group, the query
-// rows from the key chunk's first on in 64-row steps, Q rows and scaled delta
-// rows (fp16) double buffered in LDS.  A wave forms S = Q K^T and dP = delta
-// V^T (lane = key, registers = query rows), so P and dS are the A operands of
-// dV = P^T delta and dK = dS^T Q, whose B operands are the same LDS rows read
-// with the transposing load; the column sum is a sum within a lane.
+// keys of one kv head and 8 waves: the 32 keys of pair p are shared by wave
+// p (A) and wave p + 4 (B), which the hardware places on the same SIMD.  The
+// query rows from the key chunk's first on go in 64-row steps (from the
+// sequence end down, every q head of the group per slice), Q rows and scaled
+// delta rows (fp16) double buffered in LDS.  Per step:
+//   A: S = Q K^T and P (lane = key, registers = query rows), P (fp32) to LDS;
+//   B: dP = delta V^T;
+//   -- barrier --
+//   A: dV += P^T delta;
+//   B: dS = P dP with A's P, the column sums, dK += dS^T Q.
+// The transposed operands are the LDS rows read with the transposing load.
+// Each wave holds one accumulator set and one key-side operand (about half
+// the registers of a wave doing all four products), so two waves share each
+// SIMD, and the matrix products of one overlap the exponentials, masks and
+// conversions of the other.
 // ---------------------------------------------------------------------------
 template <int DK, int DV>
-__global__ void __launch_bounds__(256, 1) k_fox_bwd_dkv(FoxBwdArgs a) {
+__global__ void __launch_bounds__(512, 1) k_fox_bwd_dkv(FoxBwdArgs a) {
   constexpr int NS = DK / 16, NSV = DV / 16, DKP = FoxPad<DK>::value, DVP = FoxPad<DV>::value;
   constexpr int NBK = DKP / 32, NBV = DVP / 32;
   constexpr int RS = 64;            // query rows per step (two halves of 32)
   using QT = LdsTile<RS, DKP * 2>;  // Q rows of the step (padded)
   using DT = LdsTile<RS, DVP * 2>;  // scaled delta rows of the step (padded)
+  using QW = typename QT::template Waves<8>;
+  using DW = typename DT::template Waves<8>;
   constexpr int O_Q = 0, O_D = O_Q + 2 * QT::BYTES, O_M = O_D + 2 * DT::BYTES, O_L = O_M + 2 * 256;
-  constexpr int O_R = O_L + 2 * 256, O_T = O_R + 2 * 256;
-  __shared__ __align__(1024) char smem[O_T + 4 * 256];
-  auto Qs = [&](int b) { return smem + O_Q + b * QT::BYTES; };
-  auto Ds = [&](int b) { return smem + O_D + b * DT::BYTES; };
-  auto Ms = [&](int b) { return (const float *)(smem + O_M + b * 256); };  // row offsets mb
-  auto Lc = [&](int b) { return (const float *)(smem + O_L + b * 256); };  // rows' local gate prefixes
+  constexpr int O_R = O_L + 2 * 256, O_T = O_R + 2 * 256, O_P = O_T + 4 * 256;
+  constexpr int PEX = 2 * 64 * 16 * 4;  // one pair's P of a step: two halves, 64 lanes x 16 floats
+  __shared__ __align__(1024) char smem[O_P + 4 * PEX];
   auto Rf = [&](int b) { return (const double *)(smem + O_R + b * 256); };  // [0]: the rows' block reference
 
   const Plan &pl = a.plan;
@@ -210,130 +220,225 @@ __global__ void __launch_bounds__(256, 1) k_fox_bwd_dkv(FoxBwdArgs a) {
   const int cb = uniform(pl.chunk_base[s]);
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, n = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  float *gqt = (float *)(smem + O_T + 256 * wave);  // the step's query-side exponent terms, per wave
-  const int kb = J * CB + 32 * wave;
+  const bool isA = wave < 4;
+  const int pr = wave & 3;
+  float *gqt = (float *)(smem + O_T + 256 * pr);  // the step's query-side exponent terms (A)
+  float *pex = (float *)(smem + O_P + PEX * pr);  // the pair's P of the step, [half][quad][lane][4]
+  const int kb = J * CB + 32 * pr;
   const int key = kb + n;
   const bool kv = key < L;
   const float sl2 = a.sl2;
   const int r00 = J * CB;
   const int nsl = (L - r00 + RS - 1) / RS;
-  const int nsteps = G * nsl;
 
-  f16x8 kf[NS], vf[NSV];
+  // Key-side operand: K for S (A), V for dP (B).
+  constexpr int NKS = NS > NSV ? NS : NSV;
+  f16x8 kf[NKS];
   const f16x8 zf = __builtin_bit_cast(f16x8, make_uint4(0, 0, 0, 0));
 #pragma unroll
-  for (int i = 0; i < NS; ++i) kf[i] = kv ? *(const f16x8 *)(a.K16 + ((st + key) * Hkv + c) * DKP + 16 * i + 8 * hh) : zf;
-#pragma unroll
-  for (int i = 0; i < NSV; ++i) vf[i] = kv ? *(const f16x8 *)(a.V16 + ((st + key) * Hkv + c) * DV + 16 * i + 8 * hh) : zf;
-  const float gk = kv ? a.loc[(st + key) * Hkv + c] : 0.f;
-  const double refk = kb < L ? a.ref[(int64_t)(cb + kb / CH) * Hkv + c] : 0.0;
+  for (int i = 0; i < NKS; ++i) {
+    if (isA) kf[i] = (kv && i < NS) ? *(const f16x8 *)(a.K16 + ((st + key) * Hkv + c) * DKP + 16 * i + 8 * hh) : zf;
+    else kf[i] = (kv && i < NSV) ? *(const f16x8 *)(a.V16 + ((st + key) * Hkv + c) * DV + 16 * i + 8 * hh) : zf;
+  }
+  const float gk = (isA && kv) ? a.loc[(st + key) * Hkv + c] : 0.f;
+  const double refk = (isA && kb < L) ? a.ref[(int64_t)(cb + kb / CH) * Hkv + c] : 0.0;
 
-  uint32_t oq[QT::NW], od[DT::NW];
-  QT::lane_offsets(Hq * DKP * 2, wave, lane, oq);
-  DT::lane_offsets(Hq * DVP * 2, wave, lane, od);
-  auto stage = [&](int k, int b) {
-    const int gq = k / nsl, sl = k % nsl;
+  // Per-lane LDS addresses in stage 0 (stage 1 is a constant further): the
+  // first product's row fragments, and the second's transposed pieces.
+  const uint32_t sbase = lds_addr(smem);
+  uint32_t a1[NKS], a2[NBK > NBV ? NBK : NBV][2];
+#pragma unroll
+  for (int i = 0; i < NKS; ++i)
+    a1[i] = sbase + (isA ? O_Q + QT::off(n, 2 * i + hh) : O_D + DT::off(n, 2 * i + hh));
+#pragma unroll
+  for (int bo = 0; bo < (NBK > NBV ? NBK : NBV); ++bo) {
+    uint32_t oq[2], od[2];
+    tr_offsets<QT>(32 * bo, lane, oq);
+    tr_offsets<DT>(32 * bo, lane, od);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) a2[bo][t] = sbase + (isA ? O_D + od[t] : O_Q + oq[t]);
+  }
+  const uint32_t apx = lds_addr(pex) + 16 * lane, agq = lds_addr(gqt) + 4 * (4 * hh);
+  const uint32_t ams = sbase + O_M + 4 * (4 * hh);
+
+  uint32_t oq[QW::NWW], od[DW::NWW];
+  QW::lane_offsets(Hq * DKP * 2, wave, lane, oq);
+  DW::lane_offsets(Hq * DVP * 2, wave, lane, od);
+  // Steps run over the query rows from the sequence end down, each 64-row
+  // slice for every q head of the group in turn, so the workgroups of one
+  // (sequence, kv head) read the same rows at the same time (and share them
+  // in L2); the ones with later keys finish first.
+  auto stage = [&](int sl, int gq, int b) {
     const int h = c * G + gq, r0 = r00 + RS * sl;
     const int64_t qr = (st + r0) * Hq + h;
     const int64_t nrow = L - r0;  // rows past the sequence read as zeros
-    const u32x4 sq = rsrc_words(a.Q16 + qr * DKP, nrow * Hq * DKP * 2);
-#pragma unroll
-    for (int t = 0; t < QT::NW; ++t) QT::dma_piece_untracked(Qs(b), sq, oq, t, wave);
-    const u32x4 sd = rsrc_words(a.D16 + qr * DVP, nrow * Hq * DVP * 2);
-#pragma unroll
-    for (int t = 0; t < DT::NW; ++t) DT::dma_piece_untracked(Ds(b), sd, od, t, wave);
-    dma4_untracked(smem + O_M + b * 256, rsrc_words(a.mb + qr, nrow * Hq * 4), (uint32_t)lane * Hq * 4);
-    dma4_untracked(smem + O_L + b * 256, rsrc_words(a.loc + (st + r0) * Hkv + c, nrow * Hkv * 4),
-                   (uint32_t)lane * Hkv * 4);
-    dma4_untracked(smem + O_R + b * 256, rsrc_words(a.ref + (int64_t)(cb + r0 / CH) * Hkv + c, 8), (uint32_t)lane * 4);
+    QW::dma_untracked(smem + O_Q + b * QT::BYTES, rsrc_words(a.Q16 + qr * DKP, nrow * Hq * DKP * 2), oq, wave);
+    DW::dma_untracked(smem + O_D + b * DT::BYTES, rsrc_words(a.D16 + qr * DVP, nrow * Hq * DVP * 2), od, wave);
+    if (wave == 0) {
+      dma4_untracked(smem + O_M + b * 256, rsrc_words(a.mb + qr, nrow * Hq * 4), (uint32_t)lane * Hq * 4);
+      dma4_untracked(smem + O_L + b * 256, rsrc_words(a.loc + (st + r0) * Hkv + c, nrow * Hkv * 4),
+                     (uint32_t)lane * Hkv * 4);
+      dma4_untracked(smem + O_R + b * 256, rsrc_words(a.ref + (int64_t)(cb + r0 / CH) * Hkv + c, 8),
+                     (uint32_t)lane * 4);
+    }
   };
 
-  f32x16 accK[NBK], accV[NBV];
+  // A accumulates dV, B dK (NBV or NBK blocks).
+  constexpr int NBA = NBK > NBV ? NBK : NBV;
+  f32x16 acc[NBA];
 #pragma unroll
-  for (int b = 0; b < NBK; ++b) accK[b] = zero16();
-#pragma unroll
-  for (int b = 0; b < NBV; ++b) accV[b] = zero16();
+  for (int b = 0; b < NBA; ++b) acc[b] = zero16();
   float csum = 0.f;
+  const int n1 = isA ? NS : NSV;     // k slabs of the first product
+  const int n2 = isA ? NBV : NBK;    // output blocks of the second
 
-  if (nsteps > 0) stage(0, 0);
-  for (int k = 0; k < nsteps; ++k) {
-    const int b = k & 1;
-    wait_all();
-    __syncthreads();
-    if (k + 1 < nsteps) stage(k + 1, b ^ 1);
-    const int r0 = r00 + RS * (k % nsl);
-    if (kb >= L || r0 + RS - 1 < kb) continue;  // no key of the wave, or every row before them
-    // query-side term of each row (lane r: row r0 + r), as the dq kernel forms it
-    gqt[lane] = (float)((Rf(b)[0] + (double)Lc(b)[lane]) - refk);
+  // One step on stage B (a constant, so every LDS offset below is one).  The
+  // products run on every step: rows before the pair's keys, past the
+  // sequence end or in a slice the pair does not reach get P = 0, so they add
+  // nothing (their operand rows are zeros or finite), and the accumulators
+  // never sit behind a branch.  The masks, and the waves' different scalar
+  // work, branch once per block.
+  constexpr bool SAME = NS == NSV;
+  auto body = [&](auto bc, int r0) {
+    constexpr int B = decltype(bc)::value;
+    const uint32_t so1 = B * (isA ? QT::BYTES : DT::BYTES);  // stage offset of the first product's tile
+    const uint32_t so2 = B * (isA ? DT::BYTES : QT::BYTES);
+    const uint32_t rb1 = isA ? 2 * DKP : 2 * DVP, rb2 = isA ? 2 * DVP : 2 * DKP;  // row bytes
+    const uint32_t ams_ = opaque(ams), agq_ = opaque(agq), apx_ = opaque(apx);
     const bool mask = r0 < kb + 31 || r0 + RS > L;
+    // First product, the same shape for both waves: A forms S = Q K^T, B dP =
+    // delta V^T (lane = key, register j = query row r0 + 32 h2 + acc_row(hh, j)).
+    f32x16 xr[2];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
-      const int rb2 = r0 + 32 * h2;
-      if (rb2 + 31 < kb) continue;  // the half lies before every key of the wave
-      if (rb2 >= L) break;
-      float4 mq[4], gv[4];
+      f16x8 fr[NKS];
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        mq[q4] = *(const float4 *)(Ms(b) + 32 * h2 + 8 * q4 + 4 * hh);
-        gv[q4] = *(const float4 *)(gqt + 32 * h2 + 8 * q4 + 4 * hh);
-      }
-      f32x16 sc = zero16(), dp = zero16();
+      for (int i = 0; i < NKS; ++i)
+        if (SAME || i < n1) fr[i] = lds_row16(a1[i] + so1 + 32 * h2 * rb1);
+      xr[h2] = zero16();
 #pragma unroll
-      for (int i = 0; i < NS; ++i) sc = mma32(*(const f16x8 *)(Qs(b) + QT::off(32 * h2 + n, 2 * i + hh)), kf[i], sc);
+      for (int i = 0; i < NKS; ++i)
+        if (SAME || i < n1) xr[h2] = mma32(fr[i], kf[i], xr[h2]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (isA) {
+      // P (fp32) of both halves into the pair's exchange buffer
+      gqt[lane] = (float)((Rf(B)[0] + (double)((const float *)(smem + O_L + B * 256))[lane]) - refk);
+      auto probs = [&](auto mc) {
+        constexpr bool MASK = decltype(mc)::value;
 #pragma unroll
-      for (int i = 0; i < NSV; ++i) dp = mma32(*(const f16x8 *)(Ds(b) + DT::off(32 * h2 + n, 2 * i + hh)), vf[i], dp);
-      f16x8 pf[2], dsf[2];
+        for (int h2 = 0; h2 < 2; ++h2) {
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const float mv[4] = {mq[q4].x, mq[q4].y, mq[q4].z, mq[q4].w};
-        const float gr[4] = {gv[q4].x, gv[q4].y, gv[q4].z, gv[q4].w};
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4 mq = *(const __attribute__((address_space(3))) f32x4 *)lds_at(
+                ams_ + B * 256 + 4 * (32 * h2 + 8 * q4));
+            const f32x4 gv = *(const __attribute__((address_space(3))) f32x4 *)lds_at(agq_ + 4 * (32 * h2 + 8 * q4));
+            f32x4 p4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = 4 * q4 + e;
-          float p = fox_pair_exp(sc[j], sl2, mv[e], gr[e], gk);
-          if (mask) {
-            const int r = rb2 + acc_row(hh, j);
-            p = (key <= r && r < L) ? p : 0.f;
+            for (int e = 0; e < 4; ++e) {
+              const int j = 4 * q4 + e;
+              float p = fox_pair_exp(xr[h2][j], sl2, mq[e], gv[e], gk);
+              if (MASK) {
+                const int r = r0 + 32 * h2 + acc_row(hh, j);
+                p = (key <= r && r < L) ? p : 0.f;
+              }
+              p4[e] = p;
+            }
+            *(__attribute__((address_space(3))) f32x4 *)lds_at(apx_ + 16 * 64 * (h2 * 4 + q4)) = p4;
           }
-          const float ds = p * dp[j];
-          csum += ds;
-          pf[j >> 3][j & 7] = (_Float16)p;
-          dsf[j >> 3][j & 7] = (_Float16)ds;
+        }
+      };
+      if (mask) probs(std::true_type());
+      else probs(std::false_type());
+    }
+    lds_barrier();  // A's P is in LDS
+    // Second product: A dV += P^T delta, B dK += dS^T Q (dS = P dP), both with
+    // P read back from the exchange buffer.
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      f16x8 of[2];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 p4 = *(const __attribute__((address_space(3))) f32x4 *)lds_at(apx_ + 16 * 64 * (h2 * 4 + q4));
+        if (!isA) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int j = 4 * q4 + e;
+            const float ds = p4[e] * xr[h2][j];  // dS, exactly as the dq kernel forms it
+            csum += ds;
+            of[j >> 3][j & 7] = (_Float16)ds;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) of[q4 >> 1][4 * (q4 & 1) + e] = (_Float16)p4[e];
         }
       }
+      // two output blocks at a time: their transposed pieces, then their products
 #pragma unroll
-      for (int bv = 0; bv < NBV; ++bv)
+      for (int b0 = 0; b0 < NBA; b0 += 2) {
+        f16x4 tp[2][2][2];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) accV[bv] = mma32(pf[u], tr_frag<DT>(Ds(b), 32 * h2 + 16 * u, 32 * bv, lane), accV[bv]);
+        for (int db = 0; db < 2; ++db)
+          if (b0 + db < NBA && (SAME || b0 + db < n2))
 #pragma unroll
-      for (int bk = 0; bk < NBK; ++bk)
+            for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int u = 0; u < 2; ++u) accK[bk] = mma32(dsf[u], tr_frag<QT>(Qs(b), 32 * h2 + 16 * u, 32 * bk, lane), accK[bk]);
+              for (int t = 0; t < 2; ++t) tp[db][u][t] = lds_tr8(a2[b0 + db][t] + so2 + (32 * h2 + 16 * u) * rb2);
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+          if (b0 + db < NBA && (SAME || b0 + db < n2))
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+              acc[b0 + db] = mma32(of[u], __builtin_shufflevector(tp[db][u][0], tp[db][u][1], 0, 1, 2, 3, 4, 5, 6, 7),
+                                   acc[b0 + db]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
+
+  // Steps: slices from the sequence end down, the group's q heads per slice.
+  int sl = nsl - 1, gq = 0, k = 0;
+  if (nsl > 0) stage(sl, gq, 0);
+  while (sl >= 0) {
+    const int b = k & 1;
+    int nsl_ = sl, ngq = gq + 1;
+    if (ngq == G) { ngq = 0; --nsl_; }
+    wait_all();
+    __syncthreads();  // step k landed; every read of step k - 1 (P included) is done
+    if (nsl_ >= 0) stage(nsl_, ngq, b ^ 1);
+    const int r0 = r00 + RS * sl;
+    if (b == 0) body(std::integral_constant<int, 0>(), r0);
+    else body(std::integral_constant<int, 1>(), r0);
+    sl = nsl_;
+    gq = ngq;
+    ++k;
   }
   csum += __shfl_xor(csum, 32);
   if (kb >= L) return;
+  if (isA) {
 #pragma unroll
-  for (int bk = 0; bk < NBK; ++bk) {
-    const int col = 32 * bk + n;
-    if (col >= DK) continue;
+    for (int bv = 0; bv < NBV; ++bv) {
+      const int col = 32 * bv + n;
+      if (col >= DV) continue;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int kj = kb + acc_row(hh, j);
-      if (kj < L) store_out(a.dk, ((st + kj) * Hkv + c) * DK + col, a.scale * accK[bk][j], a.out_f32);
+      for (int j = 0; j < 16; ++j) {
+        const int kj = kb + acc_row(hh, j);
+        if (kj < L) store_out(a.dv, ((st + kj) * Hkv + c) * DV + col, acc[bv][j], a.out_f32);
+      }
     }
-  }
+  } else {
 #pragma unroll
-  for (int bv = 0; bv < NBV; ++bv) {
-    const int col = 32 * bv + n;
-    if (col >= DV) continue;
+    for (int bk = 0; bk < NBK; ++bk) {
+      const int col = 32 * bk + n;
+      if (col >= DK) continue;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int kj = kb + acc_row(hh, j);
-      if (kj < L) store_out(a.dv, ((st + kj) * Hkv + c) * DV + col, accV[bv][j], a.out_f32);
+      for (int j = 0; j < 16; ++j) {
+        const int kj = kb + acc_row(hh, j);
+        if (kj < L) store_out(a.dk, ((st + kj) * Hkv + c) * DK + col, a.scale * acc[bk][j], a.out_f32);
+      }
     }
+    if (hh == 0 && kv) a.csum[(st + key) * Hkv + c] = csum;
   }
-  if (hh == 0 && kv) a.csum[(st + key) * Hkv + c] = csum;
 }
 
 template <int DK>
@@ -341,7 +446,7 @@ hipError_t launch_fox_bwd_dk(FoxBwdKernel kind, int dv, const FoxBwdArgs &a, int
 #define FIX_FOX_BWD(DVC)                                                                              \
   case DVC:                                                                                           \
     if (kind == FK_DQ) hipLaunchKernelGGL((k_fox_bwd_dq<DK, DVC>), dim3(grid), dim3(256), 0, st, a);  \
-    else hipLaunchKernelGGL((k_fox_bwd_dkv<DK, DVC>), dim3(grid), dim3(256), 0, st, a);               \
+    else hipLaunchKernelGGL((k_fox_bwd_dkv<DK, DVC>), dim3(grid), dim3(512), 0, st, a);               \
     break;
   switch (dv) {
     FIX_FOX_BWD(16)

@@ -57,7 +57,14 @@ __global__ void __launch_bounds__(256, 2) k_fix_fwd(FwdArgs a) {
 
   // One LDS object for every tile: with a single object the compiler does not
   // make LDS reads wait for copies in flight into the other buffer.
-  constexpr int O_K = 0, O_V = O_K + 2 * KT::BYTES, O_G = O_V + 2 * VT::BYTES, O_A = O_G + 2 * 1024;
+  // The nearest-key phase after the far loop reuses the same memory (below).
+  using KB = LdsTile<32, DK * 2>;    // K rows of a 32-key block (bf16, or fp16 for fp32 inputs)
+  using OT = LdsTile<32, DVP * 2>;   // built operand tiles [key][channel], padded columns zero
+  constexpr int VRB = DV * (F32IN ? 4 : 2), GRB = DV * 4;  // raw v and gate row bytes (plain layout)
+  constexpr int N_NK = 0, N_NV = N_NK + KB::BYTES, N_NG = N_NV + 32 * VRB, N_O = N_NG + 32 * GRB;
+  constexpr int N_E = N_O + 4 * OT::BYTES, N_END = N_E + 4 * DVP * 4;
+  constexpr int O_K = 0, O_V = O_K + 2 * KT::BYTES, O_G = O_V + 2 * VT::BYTES, O_FAR = O_G + 2 * 1024;
+  constexpr int O_A = O_FAR > N_END ? O_FAR : N_END;
   __shared__ __align__(1024) char smem[O_A + 4 * 32 * 4];
   auto Ks = [&](int b) { return smem + O_K + b * KT::BYTES; };
   auto Vs = [&](int b) { return smem + O_V + b * VT::BYTES; };
@@ -188,13 +195,18 @@ __global__ void __launch_bounds__(256, 2) k_fix_fwd(FwdArgs a) {
     if (comp) {
 #pragma unroll
       for (int be = 0; be < 2; ++be) {
-        kfrag ka[NS];
-#pragma unroll
-        for (int i = 0; i < NS; ++i) ka[i] = *(const kfrag *)(Ks(b) + KT::off(32 * be + n, 2 * i + hh));
-        __builtin_amdgcn_sched_barrier(0);
+        // the key fragments in groups of (at most) four
+        constexpr int NG = NS < 4 ? NS : 4;
         sc[be] = zero16();
 #pragma unroll
-        for (int i = 0; i < NS; ++i) sc[be] = mma32(ka[i], qf[i], sc[be]);
+        for (int i0 = 0; i0 < NS; i0 += NG) {
+          kfrag ka[NG];
+#pragma unroll
+          for (int i = 0; i < NG; ++i) ka[i] = *(const kfrag *)(Ks(b) + KT::off(32 * be + n, 2 * (i0 + i) + hh));
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int i = 0; i < NG; ++i) sc[be] = mma32(ka[i], qf[i0 + i], sc[be]);
+        }
         if (be == 0) {
           stage_tile(min(J + 1, nJ - 1), b ^ 1);
 #pragma unroll
@@ -236,157 +248,197 @@ __global__ void __launch_bounds__(256, 2) k_fix_fwd(FwdArgs a) {
     wait_all();
     __syncthreads();
   }
-  if (!active) return;
+  // ---------------- nearest keys: the previous chunk and the own chunk ----------------
+  // Key blocks of 32 from the first block of the chunk before the workgroup's
+  // first chunk up to the block of its last rows, one per step.  Per block the
+  // workgroup stages K, v and the chunk-local log2 gate prefix rows in LDS and
+  // builds two operand tiles from them, each as bf16 hi and lo parts (fp32
+  // range, about 16 significant bits):
+  //   VE_j = exp2(E_b - Gl_j) v_j      (<= |v_j|)   V to the block end E_b
+  //   VB_j = exp2(E_p - Gl_j) v_j      (>= |v_j|)   V to the token before the
+  //                                                  block (E_p = E_{b-1}, 0 at
+  //                                                  a chunk start)
+  // A wave whose rows lie after block b takes it as one more factored step,
+  // A <- A (.) exp2(E_b - E_p) + P VE; the block of its own rows takes P VB
+  // (causal mask) and then scales row i by exp2(Gl_i - E_p) <= 1.  P and the
+  // operands are multiplied as bf16x3 (hi*hi + hi*lo + lo*hi): these nearest
+  // keys carry the largest decay weights.  A diagonal block whose gate range
+  // exceeds 2^GUARD is finished after the loop with exact per-pair decays.
+  // (LDS: K rows, raw v and gate rows, the four operand tiles, then E_p, E_b,
+  // exp2(E_b - E_p) and the previous block's E_b, DVP floats each.)
+  char *nk = smem + N_NK, *nv = smem + N_NV, *ng = smem + N_NG;
+  char *tEH = smem + N_O, *tEL = tEH + OT::BYTES, *tBH = tEL + OT::BYTES, *tBL = tBH + OT::BYTES;
+  float *Ep = (float *)(smem + N_E), *Eb = Ep + DVP, *Gb = Eb + DVP, *Eprev = Gb + DVP;
 
-  // ---------------- own chunk ----------------
-  const int wp = wave & 1;
-  const int c0 = Iw * CH;      // first token of the chunk (sequence relative)
-  const int kb = c0 + 32 * wp;  // first key of the diagonal block
+  const int a0 = q0 / 32;                      // the workgroup's first row block
+  const int aw = a0 + wave;                    // this wave's row block
+  const int bmin_w = max(0, 2 * (aw / 2) - 2);  // its nearest key blocks: bmin_w .. aw
+  const int nb_lo = max(0, a0 - 2);
+  const int nb_hi = (q0 + nrows - 1) / 32;
+  uint32_t okn[KB::NW];
+  KB::lane_offsets(Hkv * DK * 2, wave, lane, okn);
+  // plain row-major copy of a [32][RB] tile whose global rows are `stride` bytes apart
+  auto copy_plain = [&](char *dst, const void *src, int64_t bytes, int RB, int stride) {
+    const rsrc_t r = make_rsrc(src, bytes);
+    const int npieces = 32 * RB / 16, cpr = RB / 16;
+    for (int p0 = wave * 64; p0 < npieces; p0 += 256) {
+      const int p = p0 + lane, rr = p / cpr, pc = p % cpr;
+      dma16(dst + p0 * 16, r, (uint32_t)(rr * stride + pc * 16));
+    }
+  };
+  bool direct = false;
+
+  for (int bk = nb_lo; bk <= nb_hi; ++bk) {
+    const int kb0 = bk * 32;
+    const int64_t kr = (st + kb0) * Hkv + c;
+    const int64_t nrow = (int64_t)(L - kb0) * Hkv;  // rows past the sequence read as zeros
+    // stage K, v and Gl rows of the block
+    if constexpr (!F32IN) {
+      KB::dma(nk, make_rsrc((const uint16_t *)a.k + kr * DK, nrow * DK * 2), okn, wave);
+    } else {
+      for (int p = tid; p < KB::NCH; p += 256) {
+        const int r = p / KB::CPR, cc = p % KB::CPR;
+        *(f16x8 *)(nk + KB::off(r, cc)) = kb0 + r < L ? IF::load(a.k, ((st + kb0 + r) * Hkv + c) * DK + 8 * cc) : IF::zero();
+      }
+    }
+    copy_plain(nv, (const char *)a.v + kr * DV * (F32IN ? 4 : 2), nrow * VRB, VRB, Hkv * VRB);
+    copy_plain(ng, a.Gl2 + kr * DV, nrow * GRB, GRB, Hkv * GRB);
+    wait_all();
+    __syncthreads();
+    // block end and the factor between the block ends (E_p = 0 at a chunk start)
+    for (int d = tid; d < DVP; d += 256) {
+      const float ep = (bk & 1) ? Eprev[d] : 0.f;
+      const float eb = d < DV ? ((const float *)ng)[31 * DV + d] : 0.f;
+      Ep[d] = ep;
+      Eb[d] = eb;
+      Gb[d] = fast_exp2(eb - ep);
+    }
+    __syncthreads();
+    // operand tiles: thread item (key r, 8 channels)
+    for (int it = tid; it < 32 * (DVP / 8); it += 256) {
+      const int r = it / (DVP / 8), c8 = 8 * (it % (DVP / 8));
+      bf16x8 eh, el, bh, bl;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int d = c8 + e;
+        float ve = 0.f, vb = 0.f;
+        if (d < DV) {
+          const float gl = ((const float *)ng)[r * DV + d];
+          const float vv = F32IN ? ((const float *)nv)[r * DV + d] : bf16_to_f32(((const uint16_t *)nv)[r * DV + d]);
+          ve = fast_exp2(Eb[d] - gl) * vv;
+          vb = fast_exp2(Ep[d] - gl) * vv;
+        }
+        split_bf16(ve, eh, el, e);
+        split_bf16(vb, bh, bl, e);
+      }
+      *(bf16x8 *)(tEH + OT::off(r, c8 / 8)) = eh;
+      *(bf16x8 *)(tEL + OT::off(r, c8 / 8)) = el;
+      *(bf16x8 *)(tBH + OT::off(r, c8 / 8)) = bh;
+      *(bf16x8 *)(tBL + OT::off(r, c8 / 8)) = bl;
+    }
+    __syncthreads();
+    if (active && bk >= bmin_w && bk <= aw) {
+      const bool diag = bk == aw;
+      // S^T of the block: lane = the wave's row n, register j = key kb0 + acc_row(hh, j)
+      f32x16 s1 = zero16();
+      {
+        kfrag ka[NS];
+#pragma unroll
+        for (int i = 0; i < NS; ++i) ka[i] = *(const kfrag *)(nk + KB::off(n, 2 * i + hh));
+#pragma unroll
+        for (int i = 0; i < NS; ++i) s1 = mma32(ka[i], qf[i], s1);
+      }
+      if (diag)
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (acc_row(hh, j) > n) s1[j] = -INFINITY;
+      update_max(max_across_halves(row_max(s1)) * sl2);
+      float pv[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) pv[j] = fast_exp2(s1[j] * sl2 - m_used);
+      if (!diag) {
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) {
+          const float gb = Gb[32 * bb + n];
+#pragma unroll
+          for (int j = 0; j < 16; ++j) acc[bb][j] *= gb;
+        }
+      } else {
+        // gate range of the block: E_p - Gl at its last key
+        const int kl = min(31, L - 1 - kb0);
+        float range = 0.f;
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) {
+          const int d = 32 * bb + n;
+          if (d < DV) range = fmaxf(range, Ep[d] - ((const float *)ng)[kl * DV + d]);
+        }
+        direct = __any(range > GUARD);
+      }
+      if (!direct) {
+        bf16x8 ph[2], plo[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) split_bf16(pv[8 * u + i], ph[u], plo[u], i);
+        const char *th = diag ? tBH : tEH, *tl = diag ? tBL : tEL;
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) {
+          bf16x8 vh[2], vl[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            vh[u] = __builtin_bit_cast(bf16x8, tr_frag<OT>(th, 16 * u, 32 * bb, lane));
+            vl[u] = __builtin_bit_cast(bf16x8, tr_frag<OT>(tl, 16 * u, 32 * bb, lane));
+          }
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            acc[bb] = mma32(ph[u], vh[u], acc[bb]);
+            acc[bb] = mma32(ph[u], vl[u], acc[bb]);
+            acc[bb] = mma32(plo[u], vh[u], acc[bb]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if (diag) {
+        // row i: exp2(Gl_i - E_p) <= 1 (rows of the block are the wave's rows)
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) {
+          const int d = 32 * bb + n;
+          const float ep = Ep[d];
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int r = acc_row(hh, j);
+            const float gi = (kb0 + r < L && d < DV) ? ((const float *)ng)[r * DV + d] : ep;
+            acc[bb][j] *= fast_exp2(gi - ep);
+          }
+        }
+      }
+    }
+    // keep this block's end for the next (odd) block, once every wave is done with the tiles
+    __syncthreads();
+    for (int d = tid; d < DVP; d += 256) Eprev[d] = Eb[d];
+  }
+  if (!active) return;
+  const int kb = aw * 32;  // the diagonal block of the wave
   const float *Gl2 = a.Gl2;
   auto gl_at = [&](int tok, int d) { return Gl2[((st + tok) * Hkv + c) * DV + d]; };
   auto v_at = [&](int tok, int d) { return load_in(a.v, ((st + tok) * Hkv + c) * DV + d, F32IN); };
-  float glref[NB];
-#pragma unroll
-  for (int bb = 0; bb < NB; ++bb) {
-    int d = 32 * bb + n;
-    glref[bb] = (wp == 1 && d < DV) ? gl_at(c0 + 31, d) : 0.f;
-  }
-  // 32 keys kb0 .. kb0+31 that precede every row of the wave, with the decay
-  // taken to the token whose chunk-local log2 prefix sum is gref (>= every
-  // key's, so each factor is <= 1).  P and V are multiplied as bf16x3: these
-  // nearest keys carry the largest decay weights.
-  auto near_block = [&](int kb0, const float *gref) {
-    f32x16 s1 = zero16();
-#pragma unroll
-    for (int i = 0; i < NS; ++i)
-      s1 = mma32(IF::load(a.k, ((st + kb0 + n) * Hkv + c) * DK + 16 * i + 8 * hh), qf[i], s1);
-    update_max(max_across_halves(row_max(s1)) * sl2);
-    bf16x8 ph[2], plo[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) split_bf16(fast_exp2(s1[8 * u + i] * sl2 - m_used), ph[u], plo[u], i);
-#pragma unroll
-    for (int bb = 0; bb < NB; ++bb) {
-      const int d = 32 * bb + n;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        bf16x8 vh, vl;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int tok = kb0 + slab_key(u, hh, i);
-          const float val = (d < DV) ? fast_exp2(gref[bb] - gl_at(tok, d)) * v_at(tok, d) : 0.f;
-          split_bf16(val, vh, vl, i);
-        }
-        acc[bb] = mma32(ph[u], vh, acc[bb]);
-        acc[bb] = mma32(ph[u], vl, acc[bb]);
-        acc[bb] = mma32(plo[u], vh, acc[bb]);
-      }
-    }
-  };
-  if (Iw >= 1) {
-    // previous chunk: A <- A (.) Gam + P V~ with V~ to the chunk end
-    const int jc = (Iw - 1) * CH;
-    float gend[NB];
-#pragma unroll
-    for (int bb = 0; bb < NB; ++bb) {
-      const int d = 32 * bb + n;
-      gend[bb] = d < DV ? gl_at(jc + CH - 1, d) : 0.f;
-      const float gam = fast_exp2(gend[bb]);
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc[bb][j] *= gam;
-    }
-    near_block(jc, gend);
-    near_block(jc + 32, gend);
-  }
-  if (wp == 1) {
-    // keys c0 .. c0+31 precede every row of this wave: decay to key 31 of the chunk
-#pragma unroll
-    for (int bb = 0; bb < NB; ++bb) {
-      const float gam = fast_exp2(glref[bb]);
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc[bb][j] *= gam;
-    }
-    near_block(c0, glref);
-  }
-
-  // Diagonal 32x32 block: keys kb .. kb+31 against rows kb .. kb+31.
-  f32x16 s2;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) s2[j] = 0.f;
-  {
-    const bool kval = kb + n < L;
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      kfrag kf = kval ? IF::load(a.k, ((st + kb + n) * Hkv + c) * DK + 16 * i + 8 * hh) : IF::zero();
-      s2 = mma32(kf, qf[i], s2);
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < 16; ++j)
-    if (acc_row(hh, j) > n) s2[j] = -INFINITY;
-  {
-    float mx = row_max(s2);
-    mx = max_across_halves(mx) * sl2;
-    update_max(mx);
-  }
-  float p2[16];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) p2[j] = fast_exp2(s2[j] * sl2 - m_used);
-
-  const int klast = min(kb + 31, L - 1);
-  float range = 0.f;
-#pragma unroll
-  for (int bb = 0; bb < NB; ++bb) {
-    int d = 32 * bb + n;
-    if (d < DV) range = fmaxf(range, glref[bb] - gl_at(klast, d));
-  }
-  const bool direct = __any(range > GUARD);
-  if (!direct) {
-    bf16x8 ph[2], plo[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float pv = p2[8 * u + i];
-        __bf16 hi = (__bf16)pv;
-        ph[u][i] = hi;
-        plo[u][i] = (__bf16)(pv - (float)hi);
-      }
-#pragma unroll
-    for (int bb = 0; bb < NB; ++bb) {
-      const int d = 32 * bb + n;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        bf16x8 vh, vl;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          int tok = kb + slab_key(u, hh, i);
-          float val = (tok < L && d < DV) ? fast_exp2(glref[bb] - gl_at(tok, d)) * v_at(tok, d) : 0.f;
-          __bf16 hi = (__bf16)val;
-          vh[i] = hi;
-          vl[i] = (__bf16)(val - (float)hi);
-        }
-        acc[bb] = mma32(ph[u], vh, acc[bb]);
-        acc[bb] = mma32(ph[u], vl, acc[bb]);
-        acc[bb] = mma32(plo[u], vh, acc[bb]);
-      }
-    }
-  }
-  // Query-side factor exp(Gl_i - Gl_ref) <= 1 for every row of the wave.
   const int rbase = q0 + wave * 32;
-#pragma unroll
-  for (int bb = 0; bb < NB; ++bb) {
-    const int d = 32 * bb + n;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      int row = rbase + acc_row(hh, j);
-      float gi = (row < L && d < DV) ? gl_at(row, d) : glref[bb];
-      acc[bb][j] *= fast_exp2(gi - glref[bb]);
-    }
-  }
   if (direct) {
-    // Rare path (gate range of the block beyond 2^GUARD): exact per-pair decays.
+    // Rare path (gate range of the block beyond 2^GUARD): exact per-pair decays,
+    // with the block's probabilities formed again (m_used is final: the
+    // diagonal block is the wave's last).
+    float p2[16];
+    {
+      f32x16 s2 = zero16();
+      const bool kval = kb + n < L;
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        kfrag kf = kval ? IF::load(a.k, ((st + kb + n) * Hkv + c) * DK + 16 * i + 8 * hh) : IF::zero();
+        s2 = mma32(kf, qf[i], s2);
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) p2[j] = acc_row(hh, j) > n ? 0.f : fast_exp2(s2[j] * sl2 - m_used);
+    }
 #pragma unroll
     for (int key = 0; key < 32; ++key) {
       const int jsrc = (key >> 3) * 4 + (key & 3), hsrc = (key >> 2) & 1;

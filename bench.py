@@ -278,7 +278,8 @@ PEAK_EXP_GEXPS = 1024 * 64 / 8 * 2.4  # v_exp_f32: 8 cycles per wave64 instructi
 
 def peak_probe(torch):
     """Measured peaks: independent 32x32x16 bf16 products on every SIMD, independent v_exp_f32
-    chains, and a 16-byte-per-lane copy of 1 GiB (libfixprobe.so, separate from the library)."""
+    chains, a 16-byte-per-lane copy of 1 GiB, and the fp32 atomic dq traffic a key-stationary
+    fused backward would make at the training shape (libfixprobe.so, separate from the library)."""
     lib = ctypes.CDLL(os.path.join(ROOT, "gated_softmax_attention_amd", "libfixprobe.so"))
     lib.fix_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     lib.fix_probe_exp.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
@@ -307,12 +308,25 @@ def peak_probe(torch):
     src = torch.ones(COPY_BYTES // 4, device="cuda")
     dst = torch.empty_like(src)
     t_c = timed(lambda: lib.fix_probe_copy(256 * 8, src.data_ptr(), dst.data_ptr(), COPY_BYTES, st))
+    # dq accumulation of a key-stationary fused backward at the training shape (B=4, T=8192,
+    # H=16, dk=128): every (key chunk, 64-row slice) pair adds a 64 x 128 fp32 tile atomically
+    lib.fix_probe_atomic_dq.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_void_p]
+    Bq, Tq, Hq = 4, 8192, 16
+    dqa = torch.zeros(Bq * Tq * Hq * 128, device="cuda")
+    t_a = timed(lambda: lib.fix_probe_atomic_dq(dqa.data_ptr(), Bq, Tq, Hq, 0, st), reps=3)
+    t_as = timed(lambda: lib.fix_probe_atomic_dq(dqa.data_ptr(), Bq, Tq, Hq, 1, st), reps=3)
+    nsl = Tq // 64
+    adds = Bq * Hq * sum(max(0, nsl - 2 * J) for J in range(Tq // 128)) * 64 * 128
     mfma = blocks * 4 * it_m * 4 * 32768 / t_m / 1e12
     exps = blocks * 256 * it_e * 8 / t_e / 1e9
     copy = 2 * COPY_BYTES / t_c / 1e9
     print(json.dumps({"mfma_bf16_tflops": round(mfma, 1), "mfma_frac_of_spec": round(mfma / PEAK_BF16_TFLOPS, 4),
                       "exp_gexps": round(exps, 1), "exp_frac_of_model": round(exps / PEAK_EXP_GEXPS, 4),
                       "copy_gbs": round(copy, 1), "copy_frac_of_spec": round(copy / PEAK_HBM_GBS, 4),
+                      "fused_dq_atomics_ms": round(t_a * 1e3, 3), "fused_dq_atomic_bytes": adds * 4,
+                      "fused_dq_atomic_gbs": round(adds * 4 / t_a / 1e9, 1),
+                      "fused_dq_atomics_staggered_ms": round(t_as * 1e3, 3),
                       "mfma_s": t_m, "exp_s": t_e, "copy_s": t_c}), flush=True)
 
 

@@ -47,7 +47,33 @@ __global__ void __launch_bounds__(256) k_probe_copy(const uint4 *__restrict__ sr
   for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n16; e += (int64_t)gridDim.x * 256) dst[e] = src[e];
 }
 
+// The dq traffic of a key-stationary fused backward at the training shape
+// (B sequences of T tokens, H heads, dk = 128, 128-key workgroups): workgroup
+// (head, sequence, key chunk J) adds a 64-row x 128-column fp32 tile into
+// dq[b, rows, h, :] for every 64-row slice of the sequence from its end down
+// to row 128 J, with hardware fp32 atomics (no return); workgroups of one
+// (sequence, head) are contiguous in launch order.  Values are 1.0.
+// stagger != 0: workgroup J walks its slices starting at a rotated position,
+// so that concurrent workgroups of one (sequence, head) add to different rows.
+__global__ void __launch_bounds__(256) k_probe_atomic_dq(float *__restrict__ dq, int B, int T, int H, int nchunk,
+                                                         int stagger) {
+  const int item = blockIdx.x, J = item % nchunk, bh = item / nchunk, h = bh % H, b = bh / H;
+  const int t = threadIdx.x, col = t & 127, r0 = t >> 7;  // a wave adds 64 consecutive floats of a row
+  const int first = 2 * J, n = T / 64 - first;            // slices first .. T/64 - 1
+  for (int i = 0; i < n; ++i) {
+    const int s0 = 64 * (first + (stagger ? (i + 7 * J) % n : n - 1 - i));
+#pragma unroll 8
+    for (int r = r0; r < 64; r += 2) unsafeAtomicAdd(dq + (((int64_t)b * T + s0 + r) * H + h) * 128 + col, 1.0f);
+  }
+}
+
 extern "C" {
+int fix_probe_atomic_dq(float *dq, int B, int T, int H, int stagger, void *stream) {
+  const int nchunk = T / 128;
+  hipLaunchKernelGGL(k_probe_atomic_dq, dim3(B * H * nchunk), dim3(256), 0, (hipStream_t)stream, dq, B, T, H, nchunk,
+                     stagger);
+  return (int)hipGetLastError();
+}
 // Grid sizes: enough workgroups for several waves per SIMD on every CU.
 int fix_probe_mfma(int blocks, int iters, float *out, void *stream) {
   hipLaunchKernelGGL(k_probe_mfma, dim3(blocks), dim3(256), 0, (hipStream_t)stream, iters, out);

@@ -316,6 +316,12 @@ def peak_probe(torch):
     dqa = torch.zeros(Bq * Tq * Hq * 128, device="cuda")
     t_a = timed(lambda: lib.fix_probe_atomic_dq(dqa.data_ptr(), Bq, Tq, Hq, 0, st), reps=3)
     t_as = timed(lambda: lib.fix_probe_atomic_dq(dqa.data_ptr(), Bq, Tq, Hq, 1, st), reps=3)
+    # LDS read bandwidth: 16-byte reads and 8-byte transposing reads, 8 waves per workgroup
+    lib.fix_probe_lds.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lblocks, it_l = 256 * 4, 4000
+    lout = torch.empty(lblocks * 512, dtype=torch.int32, device="cuda")
+    t_l = [timed(lambda m=m: lib.fix_probe_lds(m, lblocks, it_l, lout.data_ptr(), st)) for m in (0, 1)]
+    lds_bytes = [lblocks * 512 * it_l * 8 * w for w in (16, 8)]
     nsl = Tq // 64
     adds = Bq * Hq * sum(max(0, nsl - 2 * J) for J in range(Tq // 128)) * 64 * 128
     mfma = blocks * 4 * it_m * 4 * 32768 / t_m / 1e12
@@ -327,6 +333,8 @@ def peak_probe(torch):
                       "fused_dq_atomics_ms": round(t_a * 1e3, 3), "fused_dq_atomic_bytes": adds * 4,
                       "fused_dq_atomic_gbs": round(adds * 4 / t_a / 1e9, 1),
                       "fused_dq_atomics_staggered_ms": round(t_as * 1e3, 3),
+                      "lds_b128_bytes_per_clk_cu": round(lds_bytes[0] / t_l[0] / 256 / 2.4e9, 1),
+                      "lds_tr_b64_bytes_per_clk_cu": round(lds_bytes[1] / t_l[1] / 256 / 2.4e9, 1),
                       "mfma_s": t_m, "exp_s": t_e, "copy_s": t_c}), flush=True)
 
 

@@ -30,10 +30,11 @@ namespace fix {
 
 template <int D> struct FoxPad { static constexpr int value = D < 32 ? 32 : D; };
 
-// The exponent of a pair, shared by both kernels: s sl2 - mb + (G_i - ref_J) - loc_j
-// with the query-side term rounded from fp64 once per (row, 64-key block).
-__device__ inline float fox_pair_exp(float s, float sl2, float mb, float gq, float gk) {
-  return fast_exp2((__builtin_fmaf(s, sl2, -mb) + gq) - gk);
+// The probability of a pair, shared by both kernels: exp2 of s sl2 + tq - loc_j,
+// where tq = (G_i - ref_J) - mb_i is the query-side term (rounded from fp64
+// once per row and 64-key block) minus the row's maximum, formed in fp32.
+__device__ inline float fox_pair_exp(float s, float sl2, float tq, float gk) {
+  return fast_exp2(__builtin_fmaf(s, sl2, tq) - gk);
 }
 
 // ---------------------------------------------------------------------------
@@ -125,7 +126,7 @@ __global__ void __launch_bounds__(256, 2) k_fox_bwd_dq(FoxBwdArgs a) {
     if (J + 1 < nJ) stage(J + 1, b ^ 1);
     const int k0 = J * CH;
     if (!active || k0 > rbase + 31) continue;
-    const float gqr = (float)(grow - Rf(b)[0]);
+    const float tqr = (float)(grow - Rf(b)[0]) - mbr;
     const bool mask = !(k0 + CH - 1 <= rbase && k0 + CH <= L);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -143,7 +144,7 @@ __global__ void __launch_bounds__(256, 2) k_fox_bwd_dq(FoxBwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int j = 4 * q4 + e;
-          float p = fox_pair_exp(sc[j], sl2, mbr, gqr, gk[e]);
+          float p = fox_pair_exp(sc[j], sl2, tqr, gk[e]);
           if (mask) {
             const int key = k0 + 32 * h + acc_row(hh, j);
             p = (key <= row && key < L) ? p : 0.f;
@@ -179,29 +180,32 @@ __global__ void __launch_bounds__(256, 2) k_fox_bwd_dq(FoxBwdArgs a) {
 // keys of one kv head and 8 waves: the 32 keys of pair p are shared by wave
 // p (A) and wave p + 4 (B), which the hardware places on the same SIMD.  The
 // query rows from the key chunk's first on go in 64-row steps (from the
-// sequence end down, every q head of the group per slice), Q rows and scaled
-// delta rows (fp16) double buffered in LDS.  Per step:
-//   A: S = Q K^T and P (lane = key, registers = query rows), P (fp32) to LDS;
-//   B: dP = delta V^T;
-//   -- barrier --
-//   A: dV += P^T delta;
-//   B: dS = P dP with A's P, the column sums, dK += dS^T Q.
-// The transposed operands are the LDS rows read with the transposing load.
-// Each wave holds one accumulator set and one key-side operand (about half
-// the registers of a wave doing all four products), so two waves share each
-// SIMD, and the matrix products of one overlap the exponentials, masks and
-// conversions of the other.
+// sequence end down, every q head of the group per slice), Q rows (three
+// stages) and scaled delta rows (two stages, fp16) in LDS.  Step k runs as
+// two phases, split by a barrier:
+//   phase 1  A: S_k = Q K^T, P_k (fp32) into LDS
+//            B: the copies of step k + 1, dK += dS_{k-1}^T Q_{k-1} with the
+//               dS it formed in step k - 1, then dP_k = delta V^T
+//   phase 2  A: dV += P_k^T delta_k
+//            B: dS_k = P_k dP_k (kept in registers for the next step) and
+//               its column sums
+// so that each wave's vector work (A's exponentials, B's products of P and
+// dP) runs while the other wave's matrix products fill the SIMD.  Each wave
+// holds one accumulator set and one key-side operand (about half the
+// registers of a wave doing all four products), so two waves share each
+// SIMD.  The transposed operands are the LDS rows read with the transposing
+// load.
 // ---------------------------------------------------------------------------
 template <int DK, int DV>
 __global__ void __launch_bounds__(512, 1) k_fox_bwd_dkv(FoxBwdArgs a) {
   constexpr int NS = DK / 16, NSV = DV / 16, DKP = FoxPad<DK>::value, DVP = FoxPad<DV>::value;
   constexpr int NBK = DKP / 32, NBV = DVP / 32;
   constexpr int RS = 64;            // query rows per step (two halves of 32)
-  using QT = LdsTile<RS, DKP * 2>;  // Q rows of the step (padded)
-  using DT = LdsTile<RS, DVP * 2>;  // scaled delta rows of the step (padded)
-  using QW = typename QT::template Waves<8>;
-  using DW = typename DT::template Waves<8>;
-  constexpr int O_Q = 0, O_D = O_Q + 2 * QT::BYTES, O_M = O_D + 2 * DT::BYTES, O_L = O_M + 2 * 256;
+  using QT = LdsTile<RS, DKP * 2>;  // Q rows of a step (padded)
+  using DT = LdsTile<RS, DVP * 2>;  // scaled delta rows of a step (padded)
+  using QW = typename QT::template Waves<4>;  // copies issued by the four B waves
+  using DW = typename DT::template Waves<4>;
+  constexpr int O_Q = 0, O_D = O_Q + 3 * QT::BYTES, O_M = O_D + 2 * DT::BYTES, O_L = O_M + 2 * 256;
   constexpr int O_R = O_L + 2 * 256, O_T = O_R + 2 * 256, O_P = O_T + 4 * 256;
   constexpr int PEX = 2 * 64 * 16 * 4;  // one pair's P of a step: two halves, 64 lanes x 16 floats
   __shared__ __align__(1024) char smem[O_P + 4 * PEX];
@@ -230,6 +234,7 @@ __global__ void __launch_bounds__(512, 1) k_fox_bwd_dkv(FoxBwdArgs a) {
   const float sl2 = a.sl2;
   const int r00 = J * CB;
   const int nsl = (L - r00 + RS - 1) / RS;
+  const int nsteps = nsl * G;
 
   // Key-side operand: K for S (A), V for dP (B).
   constexpr int NKS = NS > NSV ? NS : NSV;
@@ -243,15 +248,17 @@ __global__ void __launch_bounds__(512, 1) k_fox_bwd_dkv(FoxBwdArgs a) {
   const float gk = (isA && kv) ? a.loc[(st + key) * Hkv + c] : 0.f;
   const double refk = (isA && kb < L) ? a.ref[(int64_t)(cb + kb / CH) * Hkv + c] : 0.0;
 
-  // Per-lane LDS addresses in stage 0 (stage 1 is a constant further): the
-  // first product's row fragments, and the second's transposed pieces.
+  // Per-lane LDS addresses in stage 0: the first product's row fragments (Q
+  // for A, delta for B) and the second's transposed pieces (delta for A, Q
+  // for B); a step adds its stage's offset.
   const uint32_t sbase = lds_addr(smem);
-  uint32_t a1[NKS], a2[NBK > NBV ? NBK : NBV][2];
+  constexpr int NBA = NBK > NBV ? NBK : NBV;
+  uint32_t a1[NKS], a2[NBA][2];
 #pragma unroll
   for (int i = 0; i < NKS; ++i)
     a1[i] = sbase + (isA ? O_Q + QT::off(n, 2 * i + hh) : O_D + DT::off(n, 2 * i + hh));
 #pragma unroll
-  for (int bo = 0; bo < (NBK > NBV ? NBK : NBV); ++bo) {
+  for (int bo = 0; bo < NBA; ++bo) {
     uint32_t oq[2], od[2];
     tr_offsets<QT>(32 * bo, lane, oq);
     tr_offsets<DT>(32 * bo, lane, od);
@@ -259,90 +266,136 @@ __global__ void __launch_bounds__(512, 1) k_fox_bwd_dkv(FoxBwdArgs a) {
     for (int t = 0; t < 2; ++t) a2[bo][t] = sbase + (isA ? O_D + od[t] : O_Q + oq[t]);
   }
   const uint32_t apx = lds_addr(pex) + 16 * lane, agq = lds_addr(gqt) + 4 * (4 * hh);
-  const uint32_t ams = sbase + O_M + 4 * (4 * hh);
+  const uint32_t rb1 = isA ? 2 * DKP : 2 * DVP, rb2 = isA ? 2 * DVP : 2 * DKP;  // row bytes of the two tiles
 
   uint32_t oq[QW::NWW], od[DW::NWW];
-  QW::lane_offsets(Hq * DKP * 2, wave, lane, oq);
-  DW::lane_offsets(Hq * DVP * 2, wave, lane, od);
-  // Steps run over the query rows from the sequence end down, each 64-row
-  // slice for every q head of the group in turn, so the workgroups of one
-  // (sequence, kv head) read the same rows at the same time (and share them
-  // in L2); the ones with later keys finish first.
-  auto stage = [&](int sl, int gq, int b) {
+  const int wb = wave & 3;
+  QW::lane_offsets(Hq * DKP * 2, wb, lane, oq);
+  DW::lane_offsets(Hq * DVP * 2, wb, lane, od);
+  // Copies of the step at (slice sl, q head gq) into Q stage qs and stage ds
+  // (B waves only).
+  auto stage = [&](int sl, int gq, int qs, int ds) {
     const int h = c * G + gq, r0 = r00 + RS * sl;
     const int64_t qr = (st + r0) * Hq + h;
     const int64_t nrow = L - r0;  // rows past the sequence read as zeros
-    QW::dma_untracked(smem + O_Q + b * QT::BYTES, rsrc_words(a.Q16 + qr * DKP, nrow * Hq * DKP * 2), oq, wave);
-    DW::dma_untracked(smem + O_D + b * DT::BYTES, rsrc_words(a.D16 + qr * DVP, nrow * Hq * DVP * 2), od, wave);
-    if (wave == 0) {
-      dma4_untracked(smem + O_M + b * 256, rsrc_words(a.mb + qr, nrow * Hq * 4), (uint32_t)lane * Hq * 4);
-      dma4_untracked(smem + O_L + b * 256, rsrc_words(a.loc + (st + r0) * Hkv + c, nrow * Hkv * 4),
+    QW::dma_untracked(smem + O_Q + qs * QT::BYTES, rsrc_words(a.Q16 + qr * DKP, nrow * Hq * DKP * 2), oq, wb);
+    DW::dma_untracked(smem + O_D + ds * DT::BYTES, rsrc_words(a.D16 + qr * DVP, nrow * Hq * DVP * 2), od, wb);
+    if (wb == 0) {
+      dma4_untracked(smem + O_M + ds * 256, rsrc_words(a.mb + qr, nrow * Hq * 4), (uint32_t)lane * Hq * 4);
+      dma4_untracked(smem + O_L + ds * 256, rsrc_words(a.loc + (st + r0) * Hkv + c, nrow * Hkv * 4),
                      (uint32_t)lane * Hkv * 4);
-      dma4_untracked(smem + O_R + b * 256, rsrc_words(a.ref + (int64_t)(cb + r0 / CH) * Hkv + c, 8),
+      dma4_untracked(smem + O_R + ds * 256, rsrc_words(a.ref + (int64_t)(cb + r0 / CH) * Hkv + c, 8),
                      (uint32_t)lane * 4);
     }
   };
 
-  // A accumulates dV, B dK (NBV or NBK blocks).
-  constexpr int NBA = NBK > NBV ? NBK : NBV;
-  f32x16 acc[NBA];
+  f32x16 acc[NBA];  // A: dV, B: dK
 #pragma unroll
   for (int b = 0; b < NBA; ++b) acc[b] = zero16();
   float csum = 0.f;
+  constexpr bool SAME = NS == NSV;
   const int n1 = isA ? NS : NSV;     // k slabs of the first product
   const int n2 = isA ? NBV : NBK;    // output blocks of the second
 
-  // One step on stage B (a constant, so every LDS offset below is one).  The
-  // products run on every step: rows before the pair's keys, past the
-  // sequence end or in a slice the pair does not reach get P = 0, so they add
-  // nothing (their operand rows are zeros or finite), and the accumulators
-  // never sit behind a branch.  The masks, and the waves' different scalar
-  // work, branch once per block.
-  constexpr bool SAME = NS == NSV;
-  auto body = [&](auto bc, int r0) {
-    constexpr int B = decltype(bc)::value;
-    const uint32_t so1 = B * (isA ? QT::BYTES : DT::BYTES);  // stage offset of the first product's tile
-    const uint32_t so2 = B * (isA ? DT::BYTES : QT::BYTES);
-    const uint32_t rb1 = isA ? 2 * DKP : 2 * DVP, rb2 = isA ? 2 * DVP : 2 * DKP;  // row bytes
-    const uint32_t ams_ = opaque(ams), agq_ = opaque(agq), apx_ = opaque(apx);
-    const bool mask = r0 < kb + 31 || r0 + RS > L;
-    // First product, the same shape for both waves: A forms S = Q K^T, B dP =
-    // delta V^T (lane = key, register j = query row r0 + 32 h2 + acc_row(hh, j)).
-    f32x16 xr[2];
+  // Second product, both halves: acc[b] += of[h2][u]^T (tile rows 32 h2 + 16 u,
+  // read transposed at base + off).  The MFMAs go output block fastest (four
+  // independent chains); the reads run LA products ahead of them.
+  auto second = [&](const f16x8 (&of)[2][2], uint32_t off) {
+    constexpr int NM = 4 * NBA, LA = 4;
+    f16x4 tp[NM][2];
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      f16x8 fr[NKS];
+    for (int m = 0; m < NM; ++m) {
+      const int hu = m / NBA, b = m % NBA;
+      if (SAME || b < n2)
 #pragma unroll
-      for (int i = 0; i < NKS; ++i)
-        if (SAME || i < n1) fr[i] = lds_row16(a1[i] + so1 + 32 * h2 * rb1);
-      xr[h2] = zero16();
-#pragma unroll
-      for (int i = 0; i < NKS; ++i)
-        if (SAME || i < n1) xr[h2] = mma32(fr[i], kf[i], xr[h2]);
-      __builtin_amdgcn_sched_barrier(0);
+        for (int t = 0; t < 2; ++t) tp[m][t] = lds_tr8(a2[b][t] + off + 16 * hu * rb2);
     }
-    if (isA) {
-      // P (fp32) of both halves into the pair's exchange buffer
-      gqt[lane] = (float)((Rf(B)[0] + (double)((const float *)(smem + O_L + B * 256))[lane]) - refk);
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const int hu = m / NBA, b = m % NBA;
+      if (SAME || b < n2)
+        acc[b] = mma32(of[hu >> 1][hu & 1], __builtin_shufflevector(tp[m][0], tp[m][1], 0, 1, 2, 3, 4, 5, 6, 7), acc[b]);
+    }
+    if (SAME) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * LA, 0);
+#pragma unroll
+      for (int m = 0; m < NM - LA; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Phase 1's first product, the same shape for both waves (A: S = Q K^T, B:
+  // dP = delta V^T); lane = key, register j = row r0 + 32 h2 + acc_row(hh, j).
+  // The two halves' chains alternate and the reads run four products ahead.
+  auto first = [&](uint32_t so1, f32x16 (&xr)[2]) {
+    f16x8 fr[NKS][2];
+#pragma unroll
+    for (int i = 0; i < NKS; ++i)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+        if (SAME || i < n1) fr[i][h2] = lds_row16(a1[i] + so1 + 32 * h2 * rb1);
+    xr[0] = xr[1] = zero16();
+#pragma unroll
+    for (int i = 0; i < NKS; ++i)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+        if (SAME || i < n1) xr[h2] = mma32(fr[i][h2], kf[i], xr[h2]);
+    if (SAME) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int m = 0; m < 2 * NKS - 4; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // The two waves of a pair run separate loops with the same barriers, so
+  // each keeps only its own values live.
+  if (isA) {
+    const uint32_t agq_ = opaque(agq), apx_ = opaque(apx);
+    int sl = nsl - 1, gq = 0;
+    for (int k = 0; k < nsteps; ++k) {
+      const int qs = k % 3, ds = k & 1;
+      wait_all();
+      __syncthreads();  // step k landed; every read of step k - 1 is done
+      const int r0 = r00 + RS * sl;
+      const bool mask = r0 < kb + 31 || r0 + RS > L;
+      // the step's query-side exponent terms minus the row maxima
+      const float gv = (float)((Rf(ds)[0] + (double)((const float *)(smem + O_L + ds * 256))[lane]) - refk);
+      gqt[lane] = gv - ((const float *)(smem + O_M + ds * 256))[lane];
+      f32x16 xr[2];
+      first(qs * QT::BYTES, xr);
+      // P (fp32) of both halves into the pair's exchange buffer; P (fp16)
+      // kept as the A operand of dV
+      f16x8 pf[2][2];
       auto probs = [&](auto mc) {
         constexpr bool MASK = decltype(mc)::value;
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
+          f32x4 tv[4];
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4)
+            tv[q4] = *(const __attribute__((address_space(3))) f32x4 *)lds_at(agq_ + 4 * (32 * h2 + 8 * q4));
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
-            const f32x4 mq = *(const __attribute__((address_space(3))) f32x4 *)lds_at(
-                ams_ + B * 256 + 4 * (32 * h2 + 8 * q4));
-            const f32x4 gv = *(const __attribute__((address_space(3))) f32x4 *)lds_at(agq_ + 4 * (32 * h2 + 8 * q4));
             f32x4 p4;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int j = 4 * q4 + e;
-              float p = fox_pair_exp(xr[h2][j], sl2, mq[e], gv[e], gk);
+              float p = fox_pair_exp(xr[h2][j], sl2, tv[q4][e], gk);
               if (MASK) {
                 const int r = r0 + 32 * h2 + acc_row(hh, j);
                 p = (key <= r && r < L) ? p : 0.f;
               }
               p4[e] = p;
+              pf[h2][j >> 3][j & 7] = (_Float16)p;
             }
             *(__attribute__((address_space(3))) f32x4 *)lds_at(apx_ + 16 * 64 * (h2 * 4 + q4)) = p4;
           }
@@ -350,68 +403,44 @@ __global__ void __launch_bounds__(512, 1) k_fox_bwd_dkv(FoxBwdArgs a) {
       };
       if (mask) probs(std::true_type());
       else probs(std::false_type());
+      lds_barrier();  // P is in LDS
+      second(pf, ds * DT::BYTES);  // dV += P^T delta
+      if (++gq == G) { gq = 0; --sl; }
     }
-    lds_barrier();  // A's P is in LDS
-    // Second product: A dV += P^T delta, B dK += dS^T Q (dS = P dP), both with
-    // P read back from the exchange buffer.
+  } else {
+    const uint32_t apx_ = opaque(apx);
+    f16x8 dsp[2][2];  // dS of the previous step (both halves), the A operand of its dK product
+    int sl = nsl - 1, gq = 0;
+    if (nsteps > 0) stage(sl, gq, 0, 0);
+    for (int k = 0; k < nsteps; ++k) {
+      const int ds = k & 1;
+      int nsl_ = sl, ngq = gq + 1;
+      if (ngq == G) { ngq = 0; --nsl_; }
+      wait_all();
+      __syncthreads();  // step k landed; every read of step k - 1 is done
+      if (k + 1 < nsteps) stage(nsl_, ngq, (k + 1) % 3, ds ^ 1);
+      if (k > 0) second(dsp, ((k + 2) % 3) * QT::BYTES);  // dK of the previous step
+      f32x16 xr[2];
+      first(ds * DT::BYTES, xr);
+      lds_barrier();  // A's P is in LDS
+      f32x4 p4[2][4];
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      f16x8 of[2];
+      for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 p4 = *(const __attribute__((address_space(3))) f32x4 *)lds_at(apx_ + 16 * 64 * (h2 * 4 + q4));
-        if (!isA) {
+        for (int q4 = 0; q4 < 4; ++q4)
+          p4[h2][q4] = *(const __attribute__((address_space(3))) f32x4 *)lds_at(apx_ + 16 * 64 * (h2 * 4 + q4));
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int j = 4 * q4 + e;
-            const float ds = p4[e] * xr[h2][j];  // dS, exactly as the dq kernel forms it
-            csum += ds;
-            of[j >> 3][j & 7] = (_Float16)ds;
-          }
-        } else {
+      for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) of[q4 >> 1][4 * (q4 & 1) + e] = (_Float16)p4[e];
+        for (int j = 0; j < 16; ++j) {
+          const float d = p4[h2][j >> 2][j & 3] * xr[h2][j];  // dS, exactly as the dq kernel forms it
+          csum += d;
+          dsp[h2][j >> 3][j & 7] = (_Float16)d;
         }
-      }
-      // two output blocks at a time: their transposed pieces, then their products
-#pragma unroll
-      for (int b0 = 0; b0 < NBA; b0 += 2) {
-        f16x4 tp[2][2][2];
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
-          if (b0 + db < NBA && (SAME || b0 + db < n2))
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-              for (int t = 0; t < 2; ++t) tp[db][u][t] = lds_tr8(a2[b0 + db][t] + so2 + (32 * h2 + 16 * u) * rb2);
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
-          if (b0 + db < NBA && (SAME || b0 + db < n2))
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-              acc[b0 + db] = mma32(of[u], __builtin_shufflevector(tp[db][u][0], tp[db][u][1], 0, 1, 2, 3, 4, 5, 6, 7),
-                                   acc[b0 + db]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      sl = nsl_;
+      gq = ngq;
     }
-  };
-
-  // Steps: slices from the sequence end down, the group's q heads per slice.
-  int sl = nsl - 1, gq = 0, k = 0;
-  if (nsl > 0) stage(sl, gq, 0);
-  while (sl >= 0) {
-    const int b = k & 1;
-    int nsl_ = sl, ngq = gq + 1;
-    if (ngq == G) { ngq = 0; --nsl_; }
-    wait_all();
-    __syncthreads();  // step k landed; every read of step k - 1 (P included) is done
-    if (nsl_ >= 0) stage(nsl_, ngq, b ^ 1);
-    const int r0 = r00 + RS * sl;
-    if (b == 0) body(std::integral_constant<int, 0>(), r0);
-    else body(std::integral_constant<int, 1>(), r0);
-    sl = nsl_;
-    gq = ngq;
-    ++k;
+    if (nsteps > 0) second(dsp, ((nsteps - 1) % 3) * QT::BYTES);  // dK of the last step
   }
   csum += __shfl_xor(csum, 32);
   if (kb >= L) return;

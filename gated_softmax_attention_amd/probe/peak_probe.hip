@@ -1,13 +1,16 @@
 // Measured peaks of MI355X (gfx950) for the roofline denominators the
 // benchmark reports beside the published ones: a loop of independent
 // 32x32x16 bf16 matrix products, a loop of independent v_exp_f32 chains, and
-// a plain 16-byte-per-lane device copy.  Not part of the attention library:
+// a plain 16-byte-per-lane device copy, and LDS read bandwidth (16-byte row
+// reads and the 8-byte transposing reads the matrix-product kernels use).  Not part of the attention library:
 // only `bench.py --peak-probe` loads this.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 // Four independent accumulator chains per wave, iters products each.
 __global__ void __launch_bounds__(256) k_probe_mfma(int iters, float *out) {
@@ -67,7 +70,43 @@ __global__ void __launch_bounds__(256) k_probe_atomic_dq(float *__restrict__ dq,
   }
 }
 
+// LDS reads: 8 waves per workgroup, 64 KiB of LDS, every lane 8 independent
+// reads per iteration at conflict-free addresses (consecutive lanes on
+// consecutive 16- or 8-byte words).  MODE 0: 16-byte reads; MODE 1: 8-byte
+// transposing reads (ds_read_b64_tr_b16).  The empty asm makes the address
+// look changed on every iteration so the loads stay in the loop.
+template <int MODE>
+__global__ void __launch_bounds__(512) k_probe_lds(int iters, unsigned *out) {
+  __shared__ __align__(16) unsigned lds[16384];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  for (int i = t; i < 16384; i += 512) lds[i] = (unsigned)i * 2654435761u;
+  __syncthreads();
+  constexpr uint32_t W = MODE == 0 ? 16 : 8;
+  uint32_t a = (uint32_t)(uintptr_t)lds + W * lane + 1024 * wave;
+  unsigned x = 0;
+  for (int i = 0; i < iters; ++i) {
+    asm volatile("" : "+v"(a));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t aj = a + 8192 * j;  // eight 8 KiB windows: every address stays inside the 64 KiB array
+      if (MODE == 0) {
+        const u32x4 v = *(const __attribute__((address_space(3))) u32x4 *)(uintptr_t)aj;
+        x ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+      } else {
+        const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(uintptr_t)aj);
+        x ^= (unsigned)(v[0] ^ v[1] ^ v[2] ^ v[3]);
+      }
+    }
+  }
+  out[(int64_t)blockIdx.x * 512 + t] = x;
+}
+
 extern "C" {
+int fix_probe_lds(int mode, int blocks, int iters, unsigned *out, void *stream) {
+  if (mode == 0) hipLaunchKernelGGL(k_probe_lds<0>, dim3(blocks), dim3(512), 0, (hipStream_t)stream, iters, out);
+  else hipLaunchKernelGGL(k_probe_lds<1>, dim3(blocks), dim3(512), 0, (hipStream_t)stream, iters, out);
+  return (int)hipGetLastError();
+}
 int fix_probe_atomic_dq(float *dq, int B, int T, int H, int stagger, void *stream) {
   const int nchunk = T / 128;
   hipLaunchKernelGGL(k_probe_atomic_dq, dim3(B * H * nchunk), dim3(256), 0, (hipStream_t)stream, dq, B, T, H, nchunk,

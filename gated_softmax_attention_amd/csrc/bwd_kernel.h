@@ -989,50 +989,49 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // dk, dv from query chunks two or more after the key chunk.  Workgroup = the
-// 128 keys of one key chunk J and kv head (4 waves x 32 keys), visiting the
-// query chunks from the last to J + 2 and, within each, the G query heads of
-// the group, 64 query rows per step copied straight into LDS (fp16 Q rows and
-// scaled dhat rows only) and computed as two 32-row halves.  With one wave
-// per SIMD every instruction of the step's bookkeeping (positions, copy
-// addresses, the barrier and the wait for the copies) is issue time the
-// products do not hide, so a step spans as many rows as the LDS stages allow.
-// The dV and dK products take those rows as their k-major operands through
-// the transposing LDS read (tr_frag), so no transposed copy of either is
-// stored or moved.
+// 128 keys of one key chunk J and kv head, 8 waves: the 32 keys of pair p are
+// shared by wave p (A) and wave p + 4 (B), which the hardware places on the
+// same SIMD.  Query chunks go from the last to J + 2 and, within each, the G
+// query heads of the group, 64 query rows per step (Q rows in three LDS
+// stages, the scaled dhat rows in two).  Step k runs as two phases split by
+// a barrier:
+//   phase 1  A: S_k = Q K^T, P_k into LDS (fp32) and registers (fp16)
+//            B: the copies of step k + 1, dK += dS_{k-1}^T Q_{k-1} with the
+//               dS it formed in step k - 1, then dP_k = dhat (V (.) gamma)^T
+//   phase 2  A: dV += P_k^T dhat_k
+//            B: dS_k = P_k dP_k, kept in registers for the next step
+// so that A's exponentials run beside B's products and each wave holds one
+// accumulator set and one key-side operand.  All query rows lie at least a
+// chunk after the keys, so no pair is masked; rows past the sequence end read
+// as zeros (their dP, dS and dhat are zero).
 // The decay product between the chunks, gamma_IJ = exp2(Lam[I-1] - Lam[J]),
-// enters both products through per-chunk operands: V (.) gamma_IJ (rebuilt
-// per query chunk from an LDS copy of the chunk's V rows) for dP, and the
-// transposed dhat times gamma_IJ[d] (a per-lane factor, d being the lane's
-// output column) for dV, so the accumulators are only ever touched by MFMAs.
-// gamma_IJ is computed into LDS during the step before its chunk.
+// enters dP through V (.) gamma_IJ (B rebuilds it per query chunk from an LDS
+// copy of the chunk's V rows) and dV through the accumulator: A accumulates
+// dV relative to the current chunk's gamma and, entering the next (nearer)
+// chunk, multiplies it by gamma_I / gamma_{I-1} = exp2(Lam[I-1] - Lam[I-2]) <= 1
+// per column; the epilogue applies gamma_{J+2,J}.  The dV and dK products
+// read their transposed operands from the row tiles with the transposing LDS
+// load; LDS reads run a few products ahead of their MFMAs.
 // ---------------------------------------------------------------------------
 template <int DK, int DV, bool F32IN>
-__global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
+__global__ void __launch_bounds__(512, 1) k_bwd_dkv(BwdArgs a) {
   using IF = InFrag<F32IN>;
   using kfrag = typename IF::type;
   constexpr int NS = DK / 16, NSV = DV / 16, DKP = Pad32<DK>::value, DVP = Pad32<DV>::value;
   constexpr int NBK = DKP / 32, NBV = DVP / 32;
-  constexpr int NB = 2;             // LDS stages
-  constexpr int DIST = NB - 1;      // steps copied ahead of the one computed
   constexpr int RS = 64;            // query rows per step (two halves of 32)
-  using QT = LdsTile<RS, DK * 2>;   // Q rows of the step (fp16)
-  using DR = LdsTile<RS, DV * 2>;   // scaled dhat rows (fp16)
+  using QT = LdsTile<RS, DK * 2>;   // Q rows of a step (fp16)
+  using DR = LdsTile<RS, DV * 2>;   // scaled dhat rows of a step (fp16)
   using VRT = LdsTile<CB, DV * 2>;  // the key chunk's V rows, scaled to the chunk end
-  // Loads a step issues after its copies' predecessors: the copies themselves
-  // (fixed per wave) and nothing else, so waiting for the next step's copies
-  // is waiting until this many are left in flight.
-  constexpr int NCOPY = QT::NW + DR::NW + 1;
-  // One LDS object for every tile (see the forward kernel).  The transposed
-  // operands of the dV and dK products are read from the row tiles with the
-  // transposing LDS load (tr_frag).
-  constexpr int O_Q = 0, O_D = O_Q + NB * QT::BYTES;
-  constexpr int O_V = O_D + NB * DR::BYTES, O_M = O_V + VRT::BYTES, O_G = O_M + NB * 256, O_GH = O_G + 2 * DVP * 4;
-  __shared__ __align__(1024) char smem[O_GH + 2 * DVP * 2];
-  auto Qs = [&](int b) { return smem + O_Q + b * QT::BYTES; };
-  auto Ds = [&](int b) { return smem + O_D + b * DR::BYTES; };
-  auto Ms = [&](int b) { return (float *)(smem + O_M + b * 256); };  // 64 floats, 32 used
-  auto gam = [&](int b) { return (float *)(smem + O_G) + b * DVP; };
-  auto gamh = [&](int b) { return (_Float16 *)(smem + O_GH) + b * DVP; };  // the same, fp16
+  using QW = typename QT::template Waves<4>;  // copies issued by the four B waves
+  using DW = typename DR::template Waves<4>;
+  using VW = typename VRT::template Waves<4>;
+  constexpr int PEX = 2 * 64 * 16 * 4;  // one pair's P of a step: two halves, 64 lanes x 16 floats
+  constexpr int O_Q = 0, O_D = O_Q + 3 * QT::BYTES, O_V = O_D + 2 * DR::BYTES, O_M = O_V + VRT::BYTES;
+  constexpr int O_G = O_M + 2 * 256, O_GH = O_G + 2 * DVP * 4, O_P = O_GH + 2 * DVP * 2;
+  __shared__ __align__(1024) char smem[O_P + 4 * PEX];
+  auto rat = [&](int b) { return (float *)(smem + O_G) + b * DVP; };        // gamma_I / gamma_{I-1} per column
+  auto gamh = [&](int b) { return (_Float16 *)(smem + O_GH) + b * DVP; };  // gamma_IJ (fp16)
 
   const Plan &pl = a.plan;
   const int Hq = a.Hq, Hkv = a.Hkv, G = Hq / Hkv;
@@ -1050,7 +1049,9 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
   const int L = uniform(pl.seq_len[s]);
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, n = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kb = J * CB + 32 * wave;
+  const bool isA = wave < 4;
+  const int pr = wave & 3;
+  const int kb = J * CB + 32 * pr;
   const int key = kb + n;
   const bool kv = key < L;
   const float sl2 = a.sl2;
@@ -1059,23 +1060,7 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
   const int I0 = J + 2, I1 = nch - 1;                  // query chunks visited: I1 down to I0
   const int ns1 = (L - I1 * CB + RS - 1) / RS;          // slices of the last (possibly partial) chunk
   const int nsteps = I0 <= I1 ? G * ns1 + (CB / RS) * G * (I1 - I0) : 0;
-  // The key as an fp16 operand: Q is staged as fp16 (q converted once, exact
-  // for |q| in [2^-14, 65504]), so the score product runs in fp16 and equals
-  // the bf16 one for such inputs.
-  f16x8 kf[NS];
-#pragma unroll
-  for (int i = 0; i < NS; ++i) {
-    const kfrag kr = kv ? IF::load(a.k, ((st + key) * Hkv + c) * DK + 16 * i + 8 * hh) : IF::zero();
-#pragma unroll
-    for (int e = 0; e < 8; ++e) kf[i][e] = (_Float16)(float)kr[e];
-  }
-  f32x16 accK[NBK], accV[NBV];
-#pragma unroll
-  for (int b = 0; b < NBK; ++b) accK[b] = zero16();
-#pragma unroll
-  for (int b = 0; b < NBV; ++b) accV[b] = zero16();
-
-  // Step position: query chunk I, query head of the group gq, 32-row slice
+  // Step position: query chunk I, query head of the group gq, 64-row slice
   // u, and the ordinal of the chunk among the visited ones (0 for I1).
   struct Pos {
     int I, gq, u, ord;
@@ -1090,241 +1075,325 @@ __global__ void __launch_bounds__(256, 1) k_bwd_dkv(BwdArgs a) {
       }
     }
   };
-  // Rows past the end of the sequence read as zeros (see the probabilities).
-  uint32_t oq[QT::NW], od[DR::NW];
-  QT::lane_offsets(Hq * DK * 2, wave, lane, oq);
-  DR::lane_offsets(Hq * DV * 2, wave, lane, od);
-  auto stage_tile = [&](const Pos &p, int b) {
-    const int h = c * G + p.gq;
-    const int qt0 = p.I * CB + RS * p.u;
+
+  // Key-side operand: K for S (A), V (.) gamma for dP (B, rebuilt per chunk).
+  constexpr int NKS = NS > NSV ? NS : NSV;
+  f16x8 kf[NKS];
+  const f16x8 zf = __builtin_bit_cast(f16x8, make_uint4(0, 0, 0, 0));
+#pragma unroll
+  for (int i = 0; i < NKS; ++i) kf[i] = zf;
+  if (isA) {
+    // The key as an fp16 operand: Q is staged as fp16 (q converted once,
+    // exact for |q| in [2^-14, 65504]), so the score product runs in fp16 and
+    // equals the bf16 one for such inputs.
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const kfrag kr = kv ? IF::load(a.k, ((st + key) * Hkv + c) * DK + 16 * i + 8 * hh) : IF::zero();
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kf[i][e] = (_Float16)(float)kr[e];
+    }
+  }
+
+  // Per-lane LDS addresses in stage 0: the first product's row fragments (Q
+  // for A, dhat for B) and the second's transposed pieces (dhat for A, Q for
+  // B); a step adds its stage's offset.
+  const uint32_t sbase = lds_addr(smem);
+  constexpr int NBA = NBK > NBV ? NBK : NBV;
+  uint32_t a1[NKS], a2[NBA][2];
+#pragma unroll
+  for (int i = 0; i < NKS; ++i)
+    a1[i] = sbase + (isA ? O_Q + QT::off(n, min(2 * i + hh, QT::CPR - 1)) : O_D + DR::off(n, min(2 * i + hh, DR::CPR - 1)));
+#pragma unroll
+  for (int bo = 0; bo < NBA; ++bo) {
+    uint32_t oq[2], od[2];
+    tr_offsets<QT>(32 * bo, lane, oq);
+    tr_offsets<DR>(32 * bo, lane, od);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) a2[bo][t] = sbase + (isA ? O_D + od[t] : O_Q + oq[t]);
+  }
+  float *pex = (float *)(smem + O_P + PEX * pr);  // the pair's P of the step, [half][quad][lane][4]
+  const uint32_t apx = lds_addr(pex) + 16 * lane, ams = sbase + O_M + 4 * (4 * hh);
+  const uint32_t rb1 = isA ? 2 * DK : 2 * DV, rb2 = isA ? 2 * DV : 2 * DK;  // row bytes of the two tiles
+
+  uint32_t oq[QW::NWW], od[DW::NWW];
+  const int wb = wave & 3;
+  QW::lane_offsets(Hq * DK * 2, wb, lane, oq);
+  DW::lane_offsets(Hq * DV * 2, wb, lane, od);
+  // Copies of the step at p into Q stage qs and stage ds (B waves only).
+  auto stage = [&](const Pos &p, int qs, int ds) {
+    const int h = c * G + p.gq, qt0 = p.I * CB + RS * p.u;
     const int64_t qr = (st + qt0) * Hq + h;
-    const int nrow = L - qt0;
-    QT::dma(Qs(b), make_rsrc(a.Q16 + qr * DK, (int64_t)nrow * Hq * DK * 2), oq, wave);
-    DR::dma(Ds(b), make_rsrc(a.dh + qr * DV, (int64_t)nrow * Hq * DV * 2), od, wave);
-    // lane r fills Ms[r] (every wave, the same bytes)
-    dma4(Ms(b), make_rsrc(a.mb + qr, (int64_t)nrow * Hq * 4), (uint32_t)lane * Hq * 4);
+    const int64_t nrow = L - qt0;  // rows past the sequence read as zeros
+    QW::dma_untracked(smem + O_Q + qs * QT::BYTES, rsrc_words(a.Q16 + qr * DK, nrow * Hq * DK * 2), oq, wb);
+    DW::dma_untracked(smem + O_D + ds * DR::BYTES, rsrc_words(a.dh + qr * DV, nrow * Hq * DV * 2), od, wb);
+    if (wb == 0) dma4_untracked(smem + O_M + ds * 256, rsrc_words(a.mb + qr, nrow * Hq * 4), (uint32_t)lane * Hq * 4);
   };
 
-  // gamma_IJ[d] for d = tid (threads tid < DV).
-  const int dt = min(tid, DV - 1);
-  const double lamJ = a.Lam[((int64_t)(cbs + J) * Hkv + c) * DV + dt];
-  auto lam_of = [&](int I) { return a.Lam[((int64_t)(cbs + I - 1) * Hkv + c) * DV + dt]; };
+  // gamma per column d = tid - 256 (B threads below DV): gamma_IJ (fp16, for
+  // V (.) gamma) and the ratio to the next chunk's, into buffer ord & 1.
+  const int dt = min(max(tid - 256, 0), DV - 1);
+  const bool gthread = !isA && tid - 256 < DV;
+  const double lamJ = gthread ? a.Lam[((int64_t)(cbs + J) * Hkv + c) * DV + dt] : 0.0;
+  auto lam_of = [&](int I) { return a.Lam[((int64_t)(cbs + I - 1) * Hkv + c) * DV + dt]; };  // Lam[I-1]
 
-  Pos cur{I1, 0, 0, 0}, ahead{I1, 0, 0, 0};  // the step computed, the step being copied
-  if (nsteps > 0) {
-    uint32_t ovr[VRT::NW];
-    VRT::lane_offsets(DV * 2, wave, lane, ovr);
-    VRT::dma(smem + O_V, make_rsrc(a.Vr + ((int64_t)(cbs + J) * Hkv + c) * CB * DV, (int64_t)CB * DV * 2), ovr, wave);
-    if (tid < DV) {
-      const float g0 = fast_exp2((float)(lam_of(I1) - lamJ));
-      gam(0)[tid] = g0;
-      gamh(0)[tid] = (_Float16)g0;
-    }
-    for (int k = 0; k < DIST; ++k) {  // steps 0 .. DIST - 1 (the last step again past the end)
-      stage_tile(ahead, k);
-      if (k + 1 < nsteps) advance(ahead);
-    }
-    // `ahead` is now step DIST (or the last step)
-  }
-  wait_all();
-  __syncthreads();
-
-  f16x8 vf[NSV];        // key-side dP operand V (.) gamma_IJ, rebuilt per query chunk
-  _Float16 gh[NBV];     // gamma_IJ of the lane's dV output columns
-  int prev_ord = -1;
-  for (int k = 0; k < nsteps; ++k) {
-    const int b = k % NB;
-    const int I = cur.I, qt0 = I * CB + RS * cur.u;
-    if (cur.ord != prev_ord) {  // first step of a query chunk
-      prev_ord = cur.ord;
-      const float *gm = gam(cur.ord & 1);
-      const _Float16 *gmh = gamh(cur.ord & 1);
-      // every read of the rebuild first (no copies are in flight here: the
-      // previous step waited for all of them)
-      f16x8 r[NSV], gv[NSV];
-      float gcol[NBV];
+  f32x16 acc[NBA];  // A: dV (relative to the current chunk's gamma), B: dK
 #pragma unroll
-      for (int i = 0; i < NSV; ++i) {
-        r[i] = *(const f16x8 *)(smem + O_V + VRT::off(32 * wave + n, 2 * i + hh));
-        gv[i] = *(const f16x8 *)(gmh + 16 * i + 8 * hh);
+  for (int b = 0; b < NBA; ++b) acc[b] = zero16();
+  constexpr bool SAME = NS == NSV;
+  const int n1 = isA ? NS : NSV;     // k slabs of the first product
+  const int n2 = isA ? NBV : NBK;    // output blocks of the second
+
+  // Second product, both halves: acc[b] += of[h2][u]^T (tile rows 32 h2 + 16 u,
+  // read transposed at base + off); output block fastest, reads LA products ahead.
+  auto second = [&](const f16x8 (&of)[2][2], uint32_t off) {
+    constexpr int NM = 4 * NBA, LA = NM < 4 ? NM : 4;
+    f16x4 tp[NM][2];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const int hu = m / NBA, b = m % NBA;
+      if (SAME || b < n2)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) tp[m][t] = lds_tr8(a2[b][t] + off + 16 * hu * rb2);
+    }
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const int hu = m / NBA, b = m % NBA;
+      if (SAME || b < n2)
+        acc[b] = mma32(of[hu >> 1][hu & 1], __builtin_shufflevector(tp[m][0], tp[m][1], 0, 1, 2, 3, 4, 5, 6, 7), acc[b]);
+    }
+    if (SAME) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * LA, 0);
+#pragma unroll
+      for (int m = 0; m < NM - LA; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
-#pragma unroll
-      for (int i = 0; i < NBV; ++i) gcol[i] = gm[min(32 * i + n, DV - 1)];
-#pragma unroll
-      for (int i = 0; i < NSV; ++i) vf[i] = r[i] * gv[i];
-      // gamma of the lane's dV column 32 bv + n
-#pragma unroll
-      for (int i = 0; i < NBV; ++i) gh[i] = 32 * i + n < DV ? (_Float16)gcol[i] : (_Float16)0.f;
+      __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);
     }
-    // The position after this step: its chunk's gamma is due at the end of
-    // this step if the chunk changes.
-    Pos nxt = cur;
-    if (k + 1 < nsteps) advance(nxt);
-    const bool next_chunk = nxt.ord != cur.ord;
-    double lamI = 0.0;
-    // Two 32-row halves in turn, kept as a loop (unrolled, the compiler
-    // interleaves the halves' live ranges and spends vector instructions moving
-    // values between register files); the second half is skipped when it lies
-    // past the sequence end.
-#pragma unroll 1
-    for (int h2 = 0; h2 < 2; ++h2) {
-      if (h2 == 1 && qt0 + 32 >= L) break;
-      // Exponent offsets of the step's rows: read before the step's copies are
-      // issued (an LDS read after them can make the compiler wait for them) and
-      // used only after the products.
-      float4 mq[4];
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // First product (A: S = Q K^T, B: dP = dhat (V (.) gamma)^T); lane = key,
+  // register j = row r0 + 32 h2 + acc_row(hh, j).  The halves' chains
+  // alternate, reads run four products ahead.
+  auto first = [&](uint32_t so1, f32x16 (&xr)[2]) {
+    f16x8 fr[NKS][2];
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) mq[q4] = *(const float4 *)&Ms(b)[32 * h2 + 8 * q4 + 4 * hh];
-      {
-        // S[q][key] and dP[q][key]: lane = key, register j = query acc_row(hh, j).
-        // Operands of a group of products are read from LDS in one batch (one
-        // wait for all of them rather than one per product).
-        f16x8 qa[NS];
-        f16x8 da[NSV];
+    for (int i = 0; i < NKS; ++i)
 #pragma unroll
-        for (int i = 0; i < NS; ++i) qa[i] = *(const f16x8 *)(Qs(b) + QT::off(32 * h2 + n, 2 * i + hh));
+      for (int h2 = 0; h2 < 2; ++h2)
+        if (SAME || i < n1) fr[i][h2] = lds_row16(a1[i] + so1 + 32 * h2 * rb1);
+    xr[0] = xr[1] = zero16();
 #pragma unroll
-        for (int i = 0; i < NSV; ++i) da[i] = *(const f16x8 *)(Ds(b) + DR::off(32 * h2 + n, 2 * i + hh));
-        __builtin_amdgcn_sched_barrier(0);
-        f32x16 sc = zero16(), dp = zero16();
+    for (int i = 0; i < NKS; ++i)
 #pragma unroll
-        for (int i = 0; i < NS; ++i) sc = mma32(qa[i], kf[i], sc);
+      for (int h2 = 0; h2 < 2; ++h2)
+        if (SAME || i < n1) xr[h2] = mma32(fr[i][h2], kf[i], xr[h2]);
+    if (SAME && NKS >= 2) {
+      constexpr int LA = 2 * NKS < 4 ? 2 * NKS : 4;
+      __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);
 #pragma unroll
-        for (int i = 0; i < NSV; ++i) dp = mma32(da[i], vf[i], dp);
-        // While the products run, between them: the copies of step k + DIST
-        // (the last step again near the end, so that every step issues the
-        // same copies; `ahead` is that step's position), the next chunk's Lam
-        // row, the step's row offsets and the dV / dK operands.
-        f16x8 ta[NBV][2], tq[NBK][2];  // dhat^T and Q^T operands (k = query, in the result tiles' order)
+      for (int m = 0; m < 2 * NKS - LA; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  if (nsteps > 0 && !isA) {
+    uint32_t ovr[VW::NWW];
+    VW::lane_offsets(DV * 2, wb, lane, ovr);
+    VW::dma_untracked(smem + O_V, rsrc_words(a.Vr + ((int64_t)(cbs + J) * Hkv + c) * CB * DV, (int64_t)CB * DV * 2),
+                      ovr, wb);
+    if (gthread) gamh(0)[tid - 256] = (_Float16)fast_exp2((float)(lam_of(I1) - lamJ));
+  }
+
+  // The two waves of a pair run separate loops with the same barriers, so
+  // each keeps only its own values live.
+  if (isA) {
+    const uint32_t apx_ = opaque(apx), ams_ = opaque(ams);
+    Pos cur{I1, 0, 0, 0};
+    int prev_ord = 0;
+    for (int k = 0; k < nsteps; ++k) {
+      const int qs = k % 3, ds = k & 1;
+      wait_all();
+      __syncthreads();  // step k landed; every read of step k - 1 is done
+      f32x16 xr[2];
+      first(qs * QT::BYTES, xr);
+      // P of both halves: fp32 into the pair's exchange buffer, fp16 kept as
+      // the A operand of dV
+      f16x8 pf[2][2];
 #pragma unroll
-        for (int bv = 0; bv < NBV; ++bv)
+      for (int h2 = 0; h2 < 2; ++h2) {
+        f32x4 mq[4];
 #pragma unroll
-          for (int uu = 0; uu < 2; ++uu) ta[bv][uu] = tr_frag<DR>(Ds(b), 32 * h2 + 16 * uu, 32 * bv, lane);
-#pragma unroll
-        for (int bk = 0; bk < NBK; ++bk)
-#pragma unroll
-          for (int uu = 0; uu < 2; ++uu) tq[bk][uu] = tr_frag<QT>(Qs(b), 32 * h2 + 16 * uu, 32 * bk, lane);
-        if (h2 == 0) {
-          stage_tile(ahead, (k + DIST) % NB);
-          if (k + DIST + 1 < nsteps) advance(ahead);
-          lamI = lam_of(nxt.I);
-        }
-        constexpr int NTR = 4 * (NBV + NBK);
-#pragma unroll
-        for (int i = 0; i < NS; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one product
-          __builtin_amdgcn_sched_group_barrier(0x100, (NTR + NS - 1) / NS, 0);  // transposing LDS reads
-        }
-#pragma unroll
-        for (int i = 0; i < NSV; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one product
-          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one copy / global load
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        // Rows past the end of the sequence need no mask: their Q, dhat and
-        // row-offset copies read as zeros, so their probability is exp2(0) = 1
-        // (finite), their dP and hence dS are 0, and the dV product meets it
-        // only against their zero dhat rows.
-        f16x8 pf[2], dsf[2];
+        for (int q4 = 0; q4 < 4; ++q4)
+          mq[q4] = *(const __attribute__((address_space(3))) f32x4 *)lds_at(ams_ + ds * 256 + 4 * (32 * h2 + 8 * q4));
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const float mv[4] = {mq[q4].x, mq[q4].y, mq[q4].z, mq[q4].w};
+          f32x4 p4;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int j = 4 * q4 + e;
-            const float pv = fast_exp2(sc[j] * sl2 - mv[e]);
-            pf[j >> 3][j & 7] = (_Float16)pv;
-            dsf[j >> 3][j & 7] = (_Float16)(pv * dp[j]);
+            const float p = fast_exp2(xr[h2][j] * sl2 - mq[q4][e]);
+            p4[e] = p;
+            pf[h2][j >> 3][j & 7] = (_Float16)p;
           }
+          *(__attribute__((address_space(3))) f32x4 *)lds_at(apx_ + 16 * 64 * (h2 * 4 + q4)) = p4;
         }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int bv = 0; bv < NBV; ++bv)
-#pragma unroll
-          for (int uu = 0; uu < 2; ++uu) accV[bv] = mma32(pf[uu], ta[bv][uu] * gh[bv], accV[bv]);
-#pragma unroll
-        for (int bk = 0; bk < NBK; ++bk)
-#pragma unroll
-          for (int uu = 0; uu < 2; ++uu) accK[bk] = mma32(dsf[uu], tq[bk][uu], accK[bk]);
       }
-      __builtin_amdgcn_sched_barrier(0);
+      lds_barrier();  // P is in LDS
+      if (cur.ord != prev_ord) {  // entered a nearer chunk: dV so far times gamma_I / gamma_{I-1}
+        prev_ord = cur.ord;
+        const float *rt = rat(cur.ord & 1);
+#pragma unroll
+        for (int bv = 0; bv < NBV; ++bv) {
+          const float r = rt[min(32 * bv + n, DVP - 1)];
+#pragma unroll
+          for (int j = 0; j < 16; ++j) acc[bv][j] *= r;
+        }
+      }
+      second(pf, ds * DR::BYTES);  // dV += P^T dhat
+      if (k + 1 < nsteps) advance(cur);
     }
-    // gamma of the next chunk, into the other buffer (its last readers passed
-    // the barrier that ended the first step of the previous chunk).
-    if (next_chunk && tid < DV) {
-      const float gn = fast_exp2((float)(lamI - lamJ));
-      gam(nxt.ord & 1)[tid] = gn;
-      gamh(nxt.ord & 1)[tid] = (_Float16)gn;
+  } else {
+    const uint32_t apx_ = opaque(apx);
+    f16x8 dsp[2][2];  // dS of the previous step (both halves), the A operand of its dK product
+    Pos cur{I1, 0, 0, 0}, nxt = cur;
+    if (nsteps > 0) stage(cur, 0, 0);
+    int prev_ord = -1;
+    double lamI = gthread ? lam_of(I1) : 0.0, lamN = 0.0;
+    for (int k = 0; k < nsteps; ++k) {
+      const int ds = k & 1;
+      if (k + 1 < nsteps) advance(nxt);
+      const bool last_of_chunk = k + 1 < nsteps && nxt.ord != cur.ord;
+      if (last_of_chunk && gthread) lamN = lam_of(nxt.I);  // used at the end of the step
+      wait_all();
+      __syncthreads();  // step k landed; every read of step k - 1 is done
+      if (k + 1 < nsteps) stage(nxt, (k + 1) % 3, ds ^ 1);
+      if (k > 0) second(dsp, ((k + 2) % 3) * QT::BYTES);  // dK of the previous step
+      if (cur.ord != prev_ord) {  // first step of a query chunk: V (.) gamma_IJ
+        prev_ord = cur.ord;
+        const _Float16 *gmh = gamh(cur.ord & 1);
+        f16x8 r[NSV], gv[NSV];
+#pragma unroll
+        for (int i = 0; i < NSV; ++i) {
+          r[i] = *(const f16x8 *)(smem + O_V + VRT::off(32 * pr + n, 2 * i + hh));
+          gv[i] = *(const f16x8 *)(gmh + 16 * i + 8 * hh);
+        }
+#pragma unroll
+        for (int i = 0; i < NSV; ++i) kf[i] = r[i] * gv[i];
+      }
+      f32x16 xr[2];
+      first(ds * DR::BYTES, xr);
+      lds_barrier();  // A's P is in LDS
+      f32x4 p4[2][4];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          p4[h2][q4] = *(const __attribute__((address_space(3))) f32x4 *)lds_at(apx_ + 16 * 64 * (h2 * 4 + q4));
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) dsp[h2][j >> 3][j & 7] = (_Float16)(p4[h2][j >> 2][j & 3] * xr[h2][j]);
+      if (last_of_chunk && gthread) {
+        // the next chunk's gamma and the ratio A applies on entering it (the
+        // buffer's last readers passed the barrier that began this chunk)
+        gamh(nxt.ord & 1)[tid - 256] = (_Float16)fast_exp2((float)(lamN - lamJ));
+        rat(nxt.ord & 1)[tid - 256] = fast_exp2((float)(lamI - lamN));
+        lamI = lamN;
+      }
+      cur = nxt;
     }
-    cur = nxt;
-    wait_vm<(DIST - 1) * NCOPY>();  // the copies of step k + 1 have landed
-    lds_barrier();
+    if (nsteps > 0) second(dsp, ((nsteps - 1) % 3) * QT::BYTES);  // dK of the last step
   }
   if (kb >= L) return;
-  // epilogue: dk, dv (inter part scaled to the key: exp(Gl_end(J) - Gl_key)), dG = qside - v (.) dv.
-  // The compiler cannot tell the output and input buffers apart, so a load
-  // placed after a store waits for it: each block's inputs are loaded one
-  // block ahead, before the previous block's stores.
+  // epilogue: dk (B), dv (A; inter part scaled to the key: exp(Gl_end(J) -
+  // Gl_key) and by gamma_{J+2,J}), dG = qside - v (.) dv.  Addresses are the
+  // workgroup's first key row (uniform) plus 32-bit offsets.  The compiler
+  // cannot tell the output and input buffers apart, so a load placed after a
+  // store waits for it: inputs are loaded one half block ahead, before the
+  // previous half block's stores.
   const int tend = min((J + 1) * CB, L) - 1;
-  auto kidx = [&](int j) { return min(kb + acc_row(hh, j), L - 1); };
-  float pk[2][16];
-  auto load_dk = [&](int bk, float (&part)[16]) {
-    const int col = min(32 * bk + n, DK - 1);
+  // element offset of register j's key row from the workgroup's first key row
+  auto krow = [&](int j) { return (uint32_t)min(acc_row(hh, j), L - 1 - kb) * (uint32_t)Hkv; };
+  const int64_t row0 = (st + kb) * Hkv + c;
+  const int64_t nk = (int64_t)min(32, L - kb) * Hkv;  // rows covered by the resources below
+  if (!isA) {
+    const rsrc_t rki = make_rsrc(a.dk_i + row0 * DK, nk * DK * 4);
+    const rsrc_t rk = make_rsrc((const char *)a.dk + row0 * DK * (a.out_f32 ? 4 : 2), nk * DK * (a.out_f32 ? 4 : 2));
+    float pk[2][16];
+    auto load_dk = [&](int bk, float (&part)[16]) {
+      const uint32_t col = min(32 * bk + n, DK - 1);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) part[j] = a.dk_i[((st + kidx(j)) * Hkv + c) * DK + col];
-  };
-  load_dk(0, pk[0]);
+      for (int j = 0; j < 16; ++j) part[j] = buf_ld_f32(rki, 4 * (krow(j) * DK + col));
+    };
+    load_dk(0, pk[0]);
 #pragma unroll
-  for (int bk = 0; bk < NBK; ++bk) {
-    if (bk + 1 < NBK) load_dk(bk + 1, pk[(bk + 1) & 1]);
-    const int col = 32 * bk + n;
-    if (col < DK)
+    for (int bk = 0; bk < NBK; ++bk) {
+      if (bk + 1 < NBK) load_dk(bk + 1, pk[(bk + 1) & 1]);
+      const int col = 32 * bk + n;
+      if (col < DK)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int kj = kb + acc_row(hh, j);
-        if (kj < L) store_out(a.dk, ((st + kj) * Hkv + c) * DK + col, a.scale * accK[bk][j] + pk[bk & 1][j], a.out_f32);
-      }
+        for (int j = 0; j < 16; ++j)
+          if (kb + acc_row(hh, j) < L) buf_st_out(rk, krow(j) * DK + col, a.scale * acc[bk][j] + pk[bk & 1][j], a.out_f32);
+    }
+    return;
   }
-  float in[2][4][16];  // [slot][prefix sum, partial, qside, v][row]
+  const int64_t nb = nk * DV * 4;
+  const rsrc_t rgl = make_rsrc(a.Gl2 + row0 * DV, nb), rdi = make_rsrc(a.dv_i + row0 * DV, nb);
+  const rsrc_t rqs = make_rsrc(a.qside + row0 * DV, nb), rdg = make_rsrc(a.dG + row0 * DV, nb);
+  const rsrc_t rv = make_rsrc((const char *)a.v + row0 * DV * (F32IN ? 4 : 2), nk * DV * (F32IN ? 4 : 2));
+  const rsrc_t rdv = make_rsrc((const char *)a.dv + row0 * DV * (a.out_f32 ? 4 : 2), nk * DV * (a.out_f32 ? 4 : 2));
   float gend[NBV];
 #pragma unroll
-  for (int bv = 0; bv < NBV; ++bv) gend[bv] = a.Gl2[((st + tend) * Hkv + c) * DV + min(32 * bv + n, DV - 1)];
-  auto load_dv = [&](int bv, float (&x)[4][16]) {
+  for (int bv = 0; bv < NBV; ++bv) {
     const int col = min(32 * bv + n, DV - 1);
+    gend[bv] = a.Gl2[((st + tend) * Hkv + c) * DV + col];
+    if (nsteps > 0) {  // gamma_{J+2,J} = exp2(Lam[J+1] - Lam[J]) joins the key-side factor
+      const double l1 = a.Lam[((int64_t)(cbs + J + 1) * Hkv + c) * DV + col];
+      const double l0 = a.Lam[((int64_t)(cbs + J) * Hkv + c) * DV + col];
+      gend[bv] += (float)(l1 - l0);
+    }
+  }
+  // half blocks (8 rows of one column block)
+  float in[2][4][8];  // [slot][prefix sum, partial, qside, v][row]
+  auto load_dv = [&](int u, float (&x)[4][8]) {
+    const uint32_t col = min(32 * (u >> 1) + n, DV - 1), h8 = 8 * (u & 1);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int64_t idx = ((st + kidx(j)) * Hkv + c) * DV + col;
-      x[0][j] = a.Gl2[idx];
-      x[1][j] = a.dv_i[idx];
-      x[2][j] = a.qside[idx];
-      x[3][j] = load_in(a.v, idx, F32IN);
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t o = krow(h8 + j) * DV + col;
+      x[0][j] = buf_ld_f32(rgl, 4 * o);
+      x[1][j] = buf_ld_f32(rdi, 4 * o);
+      x[2][j] = buf_ld_f32(rqs, 4 * o);
+      x[3][j] = buf_ld_in(rv, o, F32IN);
     }
   };
   load_dv(0, in[0]);
 #pragma unroll
-  for (int bv = 0; bv < NBV; ++bv) {
-    if (bv + 1 < NBV) load_dv(bv + 1, in[(bv + 1) & 1]);
-    const int col = 32 * bv + n;
+  for (int u = 0; u < 2 * NBV; ++u) {
+    if (u + 1 < 2 * NBV) load_dv(u + 1, in[(u + 1) & 1]);
+    const int bv = u >> 1, h8 = 8 * (u & 1), col = 32 * bv + n;
     if (col < DV)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int kj = kb + acc_row(hh, j);
-        if (kj < L) {
-          const int64_t idx = ((st + kj) * Hkv + c) * DV + col;
-          const float(&x)[4][16] = in[bv & 1];
-          const float dvv = fast_exp2(gend[bv] - x[0][j]) * accV[bv][j] + x[1][j];
-          store_out(a.dv, idx, dvv, a.out_f32);
-          a.dG[idx] = x[2][j] - x[3][j] * dvv;
+      for (int j = 0; j < 8; ++j)
+        if (kb + acc_row(hh, h8 + j) < L) {
+          const uint32_t o = krow(h8 + j) * DV + col;
+          const float(&x)[4][8] = in[u & 1];
+          const float dvv = fast_exp2(gend[bv] - x[0][j]) * acc[bv][h8 + j] + x[1][j];
+          buf_st_out(rdv, o, dvv, a.out_f32);
+          buf_st_f32(rdg, 4 * o, x[2][j] - x[3][j] * dvv);
         }
-      }
   }
 }
 
 template <int DK, int DV>
 hipError_t launch_bwd_dk_dv(BwdKernel kind, bool f32in, const BwdArgs &a, dim3 grid, hipStream_t st) {
 #define FIX_BWD_LAUNCH(KERN)                                                                  \
-  if (f32in) hipLaunchKernelGGL((KERN<DK, DV, true>), grid, dim3(256), 0, st, a);             \
-  else hipLaunchKernelGGL((KERN<DK, DV, false>), grid, dim3(256), 0, st, a);
+  if (f32in) hipLaunchKernelGGL((KERN<DK, DV, true>), grid, dim3(kind == BK_DKV ? 512 : 256), 0, st, a); \
+  else hipLaunchKernelGGL((KERN<DK, DV, false>), grid, dim3(kind == BK_DKV ? 512 : 256), 0, st, a);
   switch (kind) {
     case BK_INTRA_DQ: FIX_BWD_LAUNCH(k_bwd_intra_dq); break;
     case BK_INTRA_DKV: FIX_BWD_LAUNCH(k_bwd_intra_dkv); break;

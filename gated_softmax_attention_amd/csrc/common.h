@@ -380,6 +380,22 @@ __device__ inline void lds_barrier() {
 // Wait for every outstanding memory operation of the wave (direct LDS copies included).
 __device__ inline void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
 
+// Scalar loads and stores through a buffer resource at a 32-bit byte offset
+// (a read past the resource's end returns 0, a write there is dropped).
+__device__ inline float buf_ld_f32(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ inline float buf_ld_in(rsrc_t r, uint32_t idx, bool is_f32) {
+  return is_f32 ? buf_ld_f32(r, 4 * idx) : bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, 2 * idx, 0, 0));
+}
+__device__ inline void buf_st_f32(rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
+}
+__device__ inline void buf_st_out(rsrc_t r, uint32_t idx, float v, bool is_f32) {
+  if (is_f32) buf_st_f32(r, 4 * idx, v);
+  else __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(v), r, 2 * idx, 0, 0);
+}
+
 // Load one scalar of an input tensor stored as bf16 (is_f32 = false) or fp32.
 __device__ inline float load_in(const void *p, int64_t idx, bool is_f32) {
   return is_f32 ? ((const float *)p)[idx] : bf16_to_f32(((const uint16_t *)p)[idx]);

@@ -117,6 +117,21 @@ __global__ void __launch_bounds__(256, 2) k_fox_bwd_dq(FoxBwdArgs a) {
 #pragma unroll
   for (int b = 0; b < NBK; ++b) acc[b] = zero16();
   float rsum = 0.f;
+  // Per-lane LDS addresses in buffer 0: the K and V row fragments, the
+  // transposed K pieces and the key-side exponent terms.
+  uint32_t ak[NS], av[NSV], at[NBK][2];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) ak[i] = lds_addr(Ks(0)) + KT::off(n, 2 * i + hh);
+#pragma unroll
+  for (int i = 0; i < NSV; ++i) av[i] = lds_addr(Vs(0)) + VT::off(n, 2 * i + hh);
+#pragma unroll
+  for (int bk = 0; bk < NBK; ++bk) {
+    uint32_t o[2];
+    tr_offsets<KT>(32 * bk, lane, o);
+    at[bk][0] = lds_addr(Ks(0)) + o[0];
+    at[bk][1] = lds_addr(Ks(0)) + o[1];
+  }
+  const uint32_t ag = lds_addr(smem + O_G) + 4 * (4 * hh);
 
   if (nJ > 0) stage(0, 0);
   for (int J = 0; J < nJ; ++J) {
@@ -128,36 +143,85 @@ __global__ void __launch_bounds__(256, 2) k_fox_bwd_dq(FoxBwdArgs a) {
     if (!active || k0 > rbase + 31) continue;
     const float tqr = (float)(grow - Rf(b)[0]) - mbr;
     const bool mask = !(k0 + CH - 1 <= rbase && k0 + CH <= L);
+    const uint32_t bo = opaque(b * KT::BYTES), bv = opaque(b * VT::BYTES), bg = opaque(b * 256);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       if (k0 + 32 * h > rbase + 31) break;  // the half lies after every row of the wave
+      // S^T and dP^T, their chains alternating, operand reads four products
+      // ahead; the half's key-side exponent terms read first
+      f32x4 g4[4];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        g4[q4] = *(const __attribute__((address_space(3))) f32x4 *)lds_at(ag + bg + 4 * (32 * h + 8 * q4));
       f32x16 sc = zero16(), dp = zero16();
+      {
+        constexpr int NM = NS > NSV ? NS : NSV;
+        f16x8 fk[NM], fv[NM];
 #pragma unroll
-      for (int i = 0; i < NS; ++i) sc = mma32(*(const f16x8 *)(Ks(b) + KT::off(32 * h + n, 2 * i + hh)), qf[i], sc);
-#pragma unroll
-      for (int i = 0; i < NSV; ++i) dp = mma32(*(const f16x8 *)(Vs(b) + VT::off(32 * h + n, 2 * i + hh)), df[i], dp);
-      f16x8 dsf[2];
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 g4 = *(const float4 *)(Gk(b) + 32 * h + 8 * q4 + 4 * hh);
-        const float gk[4] = {g4.x, g4.y, g4.z, g4.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = 4 * q4 + e;
-          float p = fox_pair_exp(sc[j], sl2, tqr, gk[e]);
-          if (mask) {
-            const int key = k0 + 32 * h + acc_row(hh, j);
-            p = (key <= row && key < L) ? p : 0.f;
-          }
-          const float ds = p * dp[j];
-          rsum += ds;
-          dsf[j >> 3][j & 7] = (_Float16)ds;
+        for (int i = 0; i < NM; ++i) {
+          if (i < NS) fk[i] = lds_row16(ak[i] + bo + 32 * h * (DKP * 2));
+          if (i < NSV) fv[i] = lds_row16(av[i] + bv + 32 * h * (DV * 2));
         }
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+          if (i < NS) sc = mma32(fk[i], qf[i], sc);
+          if (i < NSV) dp = mma32(fv[i], df[i], dp);
+        }
+        constexpr int NP = NS + NSV, LA = NP < 4 ? NP : 4;
+        __builtin_amdgcn_sched_group_barrier(0x100, LA + 4, 0);
+#pragma unroll
+        for (int m = 0; m < NP - LA; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      f16x8 dsf[2];
+      auto probs = [&](auto mc) {
+        constexpr bool MASK = decltype(mc)::value;
 #pragma unroll
-      for (int bk = 0; bk < NBK; ++bk)
+        for (int q4 = 0; q4 < 4; ++q4) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) acc[bk] = mma32(dsf[u], tr_frag<KT>(Ks(b), 32 * h + 16 * u, 32 * bk, lane), acc[bk]);
+          for (int e = 0; e < 4; ++e) {
+            const int j = 4 * q4 + e;
+            float p = fox_pair_exp(sc[j], sl2, tqr, g4[q4][e]);
+            if (MASK) {
+              const int key = k0 + 32 * h + acc_row(hh, j);
+              p = (key <= row && key < L) ? p : 0.f;
+            }
+            const float ds = p * dp[j];
+            rsum += ds;
+            dsf[j >> 3][j & 7] = (_Float16)ds;
+          }
+        }
+      };
+      if (mask) probs(std::true_type());
+      else probs(std::false_type());
+      // dQ += dS K, K read transposed, reads two products ahead
+      {
+        f16x4 tp[NBK][2][2];
+#pragma unroll
+        for (int bk = 0; bk < NBK; ++bk)
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) tp[bk][u][t] = lds_tr8(at[bk][t] + bo + (32 * h + 16 * u) * (DKP * 2));
+#pragma unroll
+        for (int bk = 0; bk < NBK; ++bk)
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+            acc[bk] = mma32(dsf[u], __builtin_shufflevector(tp[bk][u][0], tp[bk][u][1], 0, 1, 2, 3, 4, 5, 6, 7), acc[bk]);
+        constexpr int NP = 2 * NBK, LA = 2;
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * LA, 0);
+#pragma unroll
+        for (int m = 0; m < NP - LA; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
   rsum += __shfl_xor(rsum, 32);

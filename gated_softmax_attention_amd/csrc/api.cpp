@@ -107,7 +107,7 @@ struct BwdWs {
   _Float16 *Vr, *Qt, *Kt, *VE, *Q16;
   __bf16 *VBH, *VBL;
   float *delta;
-  _Float16 *dh, *X16;
+  _Float16 *dh, *dhT, *X16;
   __bf16 *XH, *XL, *XTH, *XTL;
   float *mb, *sig, *qside, *dG, *dq_i, *dk_i, *dv_i, *dw_part, *dg_tot, *dg_carry;
 };
@@ -153,6 +153,7 @@ size_t carve_bwd(Carve &cv, const fix_attn_desc *d, BwdWs &w) {
   w.Kt = cv.take<_Float16>(ncb * Hkv * DK * fix::CB);
   w.delta = cv.take<float>(T * Hq * DV);
   w.dh = cv.take<_Float16>(T * Hq * DV);
+  w.dhT = cv.take<_Float16>(ncb * Hq * DV * fix::CB);
   w.VE = cv.take<_Float16>(T * Hkv * DV);
   w.VBH = cv.take<__bf16>(T * Hkv * DV);
   w.VBL = cv.take<__bf16>(T * Hkv * DV);
@@ -444,10 +445,11 @@ fix_status fix_attn_bwd(const fix_attn_desc *d, const void *q, const void *k, co
   pa.X16 = w.X16; pa.XH = w.XH; pa.XL = w.XL; pa.XTH = w.XTH; pa.XTL = w.XTL;
   pa.dw_part = want_dw ? w.dw_part : nullptr;
   FIX_TRY(fix::launch_bwd_prep(DV, pa, ncb, st), "bwd_prep");
+  FIX_TRY(fix::launch_tiles_t(DV, w.dh, 2, w.plan, Hq, ncb, w.dhT, st), "tiles_dh");
   fix::BwdArgs a;
   a.q = q; a.k = k; a.v = v;
   a.Gl2 = w.Gl2; a.Gam = w.Gam; a.Lam = w.Lam; a.Vr = w.Vr; a.Qt = w.Qt; a.Kt = w.Kt; a.Q16 = w.Q16;
-  a.delta = w.delta; a.dh = w.dh; a.mb = w.mb; a.sig = w.sig; a.qside = w.qside;
+  a.delta = w.delta; a.dh = w.dh; a.dhT = w.dhT; a.mb = w.mb; a.sig = w.sig; a.qside = w.qside;
   a.VE = w.VE; a.VBH = w.VBH; a.VBL = w.VBL; a.X16 = w.X16; a.XH = w.XH; a.XL = w.XL; a.XTH = w.XTH; a.XTL = w.XTL;
   a.dq_i = w.dq_i; a.dk_i = w.dk_i; a.dv_i = w.dv_i;
   a.dq = dq; a.dk = dk; a.dv = dv; a.dG = w.dG;

@@ -815,12 +815,12 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdArgs a) {
   constexpr int NBQ = 3;
   constexpr int O_K = 0, O_T = O_K + NBQ * KT::BYTES, O_V = O_T + NBQ * TT::BYTES, O_L = O_V + NBQ * VT::BYTES;
   constexpr int O_G = O_L + NBQ * 1024;
-  __shared__ __align__(1024) char smem[O_G + 2 * DV * 4];
+  __shared__ __align__(1024) char smem[O_G + 2 * DV * 2];
   auto Ks = [&](int b) { return smem + O_K + b * KT::BYTES; };
   auto Kts = [&](int b) { return smem + O_T + b * TT::BYTES; };
   auto Vs = [&](int b) { return smem + O_V + b * VT::BYTES; };
   auto Ls = [&](int b) { return smem + O_L + b * 1024; };
-  auto gam = [&](int b) { return (float *)(smem + O_G) + b * DV; };
+  auto gam = [&](int b) { return (_Float16 *)(smem + O_G) + b * DV; };  // gamma_IJ (fp16)
 
   const Plan &pl = a.plan;
   const int Hq = a.Hq, Hkv = a.Hkv, G = Hq / Hkv;
@@ -905,13 +905,25 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdArgs a) {
   // copy.
   constexpr int NCOPYQ = (F32IN ? 0 : KT::NW) + TTD::NW + VT::NW + 1;
 
-  // The unscaled dhat rows stay in registers; they are scaled by gamma_IJ at
-  // the top of each key chunk's first step.  Every load of the kernel's own
-  // is complete before the first copy is issued, and the loop makes none.
-  f16x8 raw[NSV];
+  // The dhat rows stay in registers; gamma_IJ multiplies the V operand as it
+  // is read (a per-lane fp16 vector per k slab, read from LDS each step).
+  // Every load of the kernel's own is complete before the first copy is
+  // issued, and the loop makes none.
 #pragma unroll
-  for (int i = 0; i < NSV; ++i) raw[i] = *(const f16x8 *)(dhrow + 16 * i + 8 * hh);
-  if (nsteps > 0 && tid < DV) gam(0)[tid] = fast_exp2((float)(lamI - lam_of(0)));
+  for (int i = 0; i < NSV; ++i) dhf[i] = *(const f16x8 *)(dhrow + 16 * i + 8 * hh);
+  if (nsteps > 0 && tid < DV) gam(0)[tid] = (_Float16)fast_exp2((float)(lamI - lam_of(0)));
+  // Per-lane LDS addresses in stage 0: K and V row fragments, transposed K
+  // rows, and the gamma vectors.
+  uint32_t ak[NS], av[NSV], at[NBK][2];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) ak[i] = lds_addr(Ks(0)) + KT::off(n, 2 * i + hh);
+#pragma unroll
+  for (int i = 0; i < NSV; ++i) av[i] = lds_addr(Vs(0)) + VT::off(n, 2 * i + hh);
+#pragma unroll
+  for (int bk = 0; bk < NBK; ++bk)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) at[bk][u] = lds_addr(Kts(0)) + TT::off(32 * bk + n, 2 * u + hh);
+  const uint32_t ag = lds_addr(gam(0)) + 2 * (8 * hh);
   wait_all();
   if (nsteps > 0) {
     stage_tile(0, 0);
@@ -922,28 +934,43 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdArgs a) {
   for (int k = 0; k < nsteps; ++k) {
     const int b = uniform(k % NBQ);
     const bool next_chunk = (k & 3) == 3 && k + 1 < nsteps;
-    if ((k & 3) == 0) {  // entered key chunk J: dhat operand times gamma_IJ
-      const float *gm = gam((k >> 2) & 1);
-#pragma unroll
-      for (int i = 0; i < NSV; ++i) {
-        const float4 g0 = *(const float4 *)(gm + 16 * i + 8 * hh), g1 = *(const float4 *)(gm + 16 * i + 8 * hh + 4);
-        const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) dhf[i][e] = (_Float16)((float)raw[i][e] * gv[e]);
-      }
-    }
     // Same copies on every step (past the last step, the last step's tile
     // again, into a stage nobody reads); step k + 2's stage was last read in
     // step k - 1.
     stage_tile(min(k + 2, nsteps - 1), uniform((k + 2) % NBQ));
     {
-      // (Operands are read from LDS per product: batching them needs more
-      // registers than this kernel has at two workgroups per CU.)
+      const uint32_t ko = opaque(b * KT::BYTES), vo = opaque(b * VT::BYTES), to = opaque(b * TT::BYTES);
+      const uint32_t go = opaque(((k >> 2) & 1) * DV * 2);
+      // S^T and dP^T, their chains alternating, operand reads four products
+      // ahead (the chunk's gamma vectors first)
+      f16x8 gv[NSV];
+#pragma unroll
+      for (int i = 0; i < NSV; ++i) gv[i] = lds_row16(ag + go + 2 * 16 * i);
       f32x16 sc = zero16(), dp = zero16();
+      constexpr int NM = NS > NSV ? NS : NSV;
+      kfrag fk[NM];
+      f16x8 fv[NM];
 #pragma unroll
-      for (int i = 0; i < NS; ++i) sc = mma32(*(const kfrag *)(Ks(b) + KT::off(n, 2 * i + hh)), qf[i], sc);
+      for (int i = 0; i < NM; ++i) {
+        if (i < NS) fk[i] = *(const __attribute__((address_space(3))) kfrag *)lds_at(ak[i] + ko);
+        if (i < NSV) fv[i] = lds_row16(av[i] + vo);
+      }
 #pragma unroll
-      for (int i = 0; i < NSV; ++i) dp = mma32(*(const f16x8 *)(Vs(b) + VT::off(n, 2 * i + hh)), dhf[i], dp);
+      for (int i = 0; i < NM; ++i) {
+        if (i < NS) sc = mma32(fk[i], qf[i], sc);
+        if (i < NSV) dp = mma32(fv[i] * gv[i], dhf[i], dp);
+      }
+      {
+        constexpr int NP = NS + NSV, LA = NP < 4 ? NP : 4;
+        __builtin_amdgcn_sched_group_barrier(0x100, LA + NSV, 0);
+#pragma unroll
+        for (int m = 0; m < NP - LA; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       f16x8 dsf[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u)
@@ -952,16 +979,32 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdArgs a) {
           const int j = 8 * u + i;
           dsf[u][i] = (_Float16)(fast_exp2(sc[j] * sl2 - mbn) * dp[j]);
         }
+      // dQ += dS K with the transposed K rows, reads two products ahead
+      f16x8 tk[NBK][2];
 #pragma unroll
       for (int bk = 0; bk < NBK; ++bk)
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-          acc[bk] = mma32(dsf[u], *(const f16x8 *)(Kts(b) + TT::off(32 * bk + n, 2 * u + hh)), acc[bk]);
+        for (int u = 0; u < 2; ++u) tk[bk][u] = lds_row16(at[bk][u] + to);
+#pragma unroll
+      for (int bk = 0; bk < NBK; ++bk)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) acc[bk] = mma32(dsf[u], tk[bk][u], acc[bk]);
+      {
+        constexpr int NP = 2 * NBK, LA = 2;
+        __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);
+#pragma unroll
+        for (int m = 0; m < NP - LA; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     // gamma of the next chunk, into the other buffer (its last readers passed
     // the barrier that began this chunk).
     if (next_chunk && tid < DV)
-      gam(((k >> 2) + 1) & 1)[tid] = fast_exp2((float)(lamI - ((const double *)Ls(b))[tid]));
+      gam(((k >> 2) + 1) & 1)[tid] = (_Float16)fast_exp2((float)(lamI - ((const double *)Ls(b))[tid]));
     wait_vm<NCOPYQ>();  // step k + 1 has landed (step k + 2's copies stay in flight)
     lds_barrier();
   }
@@ -992,26 +1035,28 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdArgs a) {
 // 128 keys of one key chunk J and kv head, 8 waves: the 32 keys of pair p are
 // shared by wave p (A) and wave p + 4 (B), which the hardware places on the
 // same SIMD.  Query chunks go from the last to J + 2 and, within each, the G
-// query heads of the group, 64 query rows per step (Q rows in three LDS
-// stages, the scaled dhat rows in two).  Step k runs as two phases split by
-// a barrier:
-//   phase 1  A: S_k = Q K^T, P_k into LDS (fp32) and registers (fp16)
-//            B: the copies of step k + 1, dK += dS_{k-1}^T Q_{k-1} with the
-//               dS it formed in step k - 1, then dP_k = dhat (V (.) gamma)^T
+// query heads of the group, 64 query rows per step.  Step k runs as two
+// phases split by a barrier:
+//   phase 1  A: S_k = Q K^T, P_k (fp16) into LDS and registers, the copies
+//               of step k + 1's Q and dhat rows
+//            B: dK += dS_{k-1}^T Q_{k-1} with the dS it formed in step
+//               k - 1, then dP_k = dhat (V (.) gamma)^T
 //   phase 2  A: dV += P_k^T dhat_k
-//            B: dS_k = P_k dP_k, kept in registers for the next step
+//            B: dS_k = P_k dP_k, kept in registers for the next step, and the
+//               copies of step k + 1's transposed Q and dhat tiles
 // so that A's exponentials run beside B's products and each wave holds one
-// accumulator set and one key-side operand.  All query rows lie at least a
-// chunk after the keys, so no pair is masked; rows past the sequence end read
-// as zeros (their dP, dS and dhat are zero).
+// accumulator set and one key-side operand.  The first products read row
+// tiles, the second ones transposed tiles (the key_pos column order puts the
+// eight rows one lane needs side by side), all with 16-byte LDS reads run a
+// few products ahead of their MFMAs.  All query rows lie at least a chunk
+// after the keys, so no pair is masked; rows past the sequence end read as
+// zeros (their dP, dS and dhat are zero).
 // The decay product between the chunks, gamma_IJ = exp2(Lam[I-1] - Lam[J]),
-// enters dP through V (.) gamma_IJ (B rebuilds it per query chunk from an LDS
-// copy of the chunk's V rows) and dV through the accumulator: A accumulates
+// enters dP through V (.) gamma_IJ (B rebuilds it per query chunk from the V
+// rows it keeps in registers) and dV through the accumulator: A accumulates
 // dV relative to the current chunk's gamma and, entering the next (nearer)
 // chunk, multiplies it by gamma_I / gamma_{I-1} = exp2(Lam[I-1] - Lam[I-2]) <= 1
-// per column; the epilogue applies gamma_{J+2,J}.  The dV and dK products
-// read their transposed operands from the row tiles with the transposing LDS
-// load; LDS reads run a few products ahead of their MFMAs.
+// per column; the epilogue applies gamma_{J+2,J}.
 // ---------------------------------------------------------------------------
 template <int DK, int DV, bool F32IN>
 __global__ void __launch_bounds__(512, 1) k_bwd_dkv(BwdArgs a) {
@@ -1019,16 +1064,20 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkv(BwdArgs a) {
   using kfrag = typename IF::type;
   constexpr int NS = DK / 16, NSV = DV / 16, DKP = Pad32<DK>::value, DVP = Pad32<DV>::value;
   constexpr int NBK = DKP / 32, NBV = DVP / 32;
-  constexpr int RS = 64;            // query rows per step (two halves of 32)
-  using QT = LdsTile<RS, DK * 2>;   // Q rows of a step (fp16)
-  using DR = LdsTile<RS, DV * 2>;   // scaled dhat rows of a step (fp16)
-  using VRT = LdsTile<CB, DV * 2>;  // the key chunk's V rows, scaled to the chunk end
-  using QW = typename QT::template Waves<4>;  // copies issued by the four B waves
+  constexpr int RS = 64;             // query rows per step (two halves of 32)
+  using QT = LdsTile<RS, DK * 2>;    // Q rows of a step (fp16)
+  using DR = LdsTile<RS, DV * 2>;    // scaled dhat rows of a step (fp16)
+  using QX = LdsTile<DKP, RS * 2>;   // transposed Q of a step [d][row, key_pos order], rows padded to DKP
+  using QXD = LdsTile<DK, RS * 2>;   // the rows a copy fills
+  using DX = LdsTile<DVP, RS * 2>;   // transposed dhat of a step
+  using DXD = LdsTile<DV, RS * 2>;
+  using QW = typename QT::template Waves<4>;  // copies issued by the four A waves
   using DW = typename DR::template Waves<4>;
-  using VW = typename VRT::template Waves<4>;
-  constexpr int PEX = 2 * 64 * 16 * 4;  // one pair's P of a step: two halves, 64 lanes x 16 floats
-  constexpr int O_Q = 0, O_D = O_Q + 3 * QT::BYTES, O_V = O_D + 2 * DR::BYTES, O_M = O_V + VRT::BYTES;
-  constexpr int O_G = O_M + 2 * 256, O_GH = O_G + 2 * DVP * 4, O_P = O_GH + 2 * DVP * 2;
+  using QXW = typename QXD::template Waves<4>;  // copies issued by the four B waves
+  using DXW = typename DXD::template Waves<4>;
+  constexpr int PEX = 2 * 2 * 64 * 16;  // one pair's P of a step (fp16): [half][u][lane] 16 bytes
+  constexpr int O_Q = 0, O_D = O_Q + 2 * QT::BYTES, O_QX = O_D + 2 * DR::BYTES, O_DX = O_QX + 2 * QX::BYTES;
+  constexpr int O_M = O_DX + 2 * DX::BYTES, O_G = O_M + 2 * 256, O_GH = O_G + 2 * DVP * 4, O_P = O_GH + 2 * DVP * 2;
   __shared__ __align__(1024) char smem[O_P + 4 * PEX];
   auto rat = [&](int b) { return (float *)(smem + O_G) + b * DVP; };        // gamma_I / gamma_{I-1} per column
   auto gamh = [&](int b) { return (_Float16 *)(smem + O_GH) + b * DVP; };  // gamma_IJ (fp16)
@@ -1076,12 +1125,15 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkv(BwdArgs a) {
     }
   };
 
-  // Key-side operand: K for S (A), V (.) gamma for dP (B, rebuilt per chunk).
+  // Key-side operand: K for S (A), V (.) gamma for dP (B, rebuilt per chunk
+  // from its V rows, vr).
   constexpr int NKS = NS > NSV ? NS : NSV;
-  f16x8 kf[NKS];
+  f16x8 kf[NKS], vr[NSV];
   const f16x8 zf = __builtin_bit_cast(f16x8, make_uint4(0, 0, 0, 0));
 #pragma unroll
   for (int i = 0; i < NKS; ++i) kf[i] = zf;
+#pragma unroll
+  for (int i = 0; i < NSV; ++i) vr[i] = zf;
   if (isA) {
     // The key as an fp16 operand: Q is staged as fp16 (q converted once,
     // exact for |q| in [2^-14, 65504]), so the score product runs in fp16 and
@@ -1092,47 +1144,65 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkv(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) kf[i][e] = (_Float16)(float)kr[e];
     }
+  } else if (kv) {
+#pragma unroll
+    for (int i = 0; i < NSV; ++i)
+      vr[i] = *(const f16x8 *)(a.Vr + (((int64_t)(cbs + J) * Hkv + c) * CB + 32 * pr + n) * DV + 16 * i + 8 * hh);
   }
 
   // Per-lane LDS addresses in stage 0: the first product's row fragments (Q
-  // for A, dhat for B) and the second's transposed pieces (dhat for A, Q for
-  // B); a step adds its stage's offset.
+  // for A, dhat for B) and the second's transposed fragments (dhat for A, Q
+  // for B) per output block b and 16-row group g; a step adds its stage's offset.
   const uint32_t sbase = lds_addr(smem);
   constexpr int NBA = NBK > NBV ? NBK : NBV;
-  uint32_t a1[NKS], a2[NBA][2];
+  uint32_t a1[NKS], a2[NBA][4];
 #pragma unroll
   for (int i = 0; i < NKS; ++i)
     a1[i] = sbase + (isA ? O_Q + QT::off(n, min(2 * i + hh, QT::CPR - 1)) : O_D + DR::off(n, min(2 * i + hh, DR::CPR - 1)));
 #pragma unroll
-  for (int bo = 0; bo < NBA; ++bo) {
-    uint32_t oq[2], od[2];
-    tr_offsets<QT>(32 * bo, lane, oq);
-    tr_offsets<DR>(32 * bo, lane, od);
+  for (int b = 0; b < NBA; ++b)
 #pragma unroll
-    for (int t = 0; t < 2; ++t) a2[bo][t] = sbase + (isA ? O_D + od[t] : O_Q + oq[t]);
-  }
-  float *pex = (float *)(smem + O_P + PEX * pr);  // the pair's P of the step, [half][quad][lane][4]
+    for (int g = 0; g < 4; ++g)
+      a2[b][g] = sbase + (isA ? O_DX + DX::off(min(32 * b + n, DVP - 1), 2 * g + hh)
+                              : O_QX + QX::off(min(32 * b + n, DKP - 1), 2 * g + hh));
+  _Float16 *pex = (_Float16 *)(smem + O_P + PEX * pr);  // the pair's P of the step
   const uint32_t apx = lds_addr(pex) + 16 * lane, ams = sbase + O_M + 4 * (4 * hh);
-  const uint32_t rb1 = isA ? 2 * DK : 2 * DV, rb2 = isA ? 2 * DV : 2 * DK;  // row bytes of the two tiles
+  const uint32_t rb1 = isA ? 2 * DK : 2 * DV;  // row bytes of the first product's tile
 
-  uint32_t oq[QW::NWW], od[DW::NWW];
+  // Copies: A the row tiles and row maxima of a step, B its transposed tiles.
   const int wb = wave & 3;
+  uint32_t oq[QW::NWW], od[DW::NWW], oqx[QXW::NWW], odx[DXW::NWW];
   QW::lane_offsets(Hq * DK * 2, wb, lane, oq);
   DW::lane_offsets(Hq * DV * 2, wb, lane, od);
-  // Copies of the step at p into Q stage qs and stage ds (B waves only).
-  auto stage = [&](const Pos &p, int qs, int ds) {
+  QXW::lane_offsets(CB * 2, wb, lane, oqx);
+  DXW::lane_offsets(CB * 2, wb, lane, odx);
+  auto stage_rows = [&](const Pos &p, int b) {
     const int h = c * G + p.gq, qt0 = p.I * CB + RS * p.u;
     const int64_t qr = (st + qt0) * Hq + h;
     const int64_t nrow = L - qt0;  // rows past the sequence read as zeros
-    QW::dma_untracked(smem + O_Q + qs * QT::BYTES, rsrc_words(a.Q16 + qr * DK, nrow * Hq * DK * 2), oq, wb);
-    DW::dma_untracked(smem + O_D + ds * DR::BYTES, rsrc_words(a.dh + qr * DV, nrow * Hq * DV * 2), od, wb);
-    if (wb == 0) dma4_untracked(smem + O_M + ds * 256, rsrc_words(a.mb + qr, nrow * Hq * 4), (uint32_t)lane * Hq * 4);
+    QW::dma_untracked(smem + O_Q + b * QT::BYTES, rsrc_words(a.Q16 + qr * DK, nrow * Hq * DK * 2), oq, wb);
+    DW::dma_untracked(smem + O_D + b * DR::BYTES, rsrc_words(a.dh + qr * DV, nrow * Hq * DV * 2), od, wb);
+    if (wb == 0) dma4_untracked(smem + O_M + b * 256, rsrc_words(a.mb + qr, nrow * Hq * 4), (uint32_t)lane * Hq * 4);
   };
+  auto stage_cols = [&](const Pos &p, int b) {
+    const int64_t ch = (int64_t)(cbs + p.I) * Hq + c * G + p.gq;
+    QXW::dma_untracked(smem + O_QX + b * QX::BYTES, rsrc_words(a.Qt + ch * DK * CB + RS * p.u, (int64_t)DK * CB * 2),
+                       oqx, wb);
+    DXW::dma_untracked(smem + O_DX + b * DX::BYTES, rsrc_words(a.dhT + ch * DV * CB + RS * p.u, (int64_t)DV * CB * 2),
+                       odx, wb);
+  };
+  // zero rows of the narrow transposed tiles (never copied)
+  if (DK < DKP)
+    for (int e = tid; e < (DKP - DK) * RS * 2 / 4; e += 512)
+      for (int b = 0; b < 2; ++b) ((uint32_t *)(smem + O_QX + b * QX::BYTES + DK * RS * 2))[e] = 0u;
+  if (DV < DVP)
+    for (int e = tid; e < (DVP - DV) * RS * 2 / 4; e += 512)
+      for (int b = 0; b < 2; ++b) ((uint32_t *)(smem + O_DX + b * DX::BYTES + DV * RS * 2))[e] = 0u;
 
-  // gamma per column d = tid - 256 (B threads below DV): gamma_IJ (fp16, for
+  // gamma per column d = tid (A threads below DV): gamma_IJ (fp16, for
   // V (.) gamma) and the ratio to the next chunk's, into buffer ord & 1.
-  const int dt = min(max(tid - 256, 0), DV - 1);
-  const bool gthread = !isA && tid - 256 < DV;
+  const int dt = min(tid, DV - 1);
+  const bool gthread = isA && tid < DV;
   const double lamJ = gthread ? a.Lam[((int64_t)(cbs + J) * Hkv + c) * DV + dt] : 0.0;
   auto lam_of = [&](int I) { return a.Lam[((int64_t)(cbs + I - 1) * Hkv + c) * DV + dt]; };  // Lam[I-1]
 
@@ -1143,30 +1213,28 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkv(BwdArgs a) {
   const int n1 = isA ? NS : NSV;     // k slabs of the first product
   const int n2 = isA ? NBV : NBK;    // output blocks of the second
 
-  // Second product, both halves: acc[b] += of[h2][u]^T (tile rows 32 h2 + 16 u,
-  // read transposed at base + off); output block fastest, reads LA products ahead.
+  // Second product, both halves: acc[b] += of[h2][u]^T (16-row group g =
+  // 2 h2 + u of the transposed tile at stage offset off); output block
+  // fastest, reads LA products ahead.
   auto second = [&](const f16x8 (&of)[2][2], uint32_t off) {
     constexpr int NM = 4 * NBA, LA = NM < 4 ? NM : 4;
-    f16x4 tp[NM][2];
+    f16x8 tf[NM];
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
-      const int hu = m / NBA, b = m % NBA;
-      if (SAME || b < n2)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) tp[m][t] = lds_tr8(a2[b][t] + off + 16 * hu * rb2);
+      const int g = m / NBA, b = m % NBA;
+      if (SAME || b < n2) tf[m] = lds_row16(a2[b][g] + off);
     }
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
-      const int hu = m / NBA, b = m % NBA;
-      if (SAME || b < n2)
-        acc[b] = mma32(of[hu >> 1][hu & 1], __builtin_shufflevector(tp[m][0], tp[m][1], 0, 1, 2, 3, 4, 5, 6, 7), acc[b]);
+      const int g = m / NBA, b = m % NBA;
+      if (SAME || b < n2) acc[b] = mma32(of[g >> 1][g & 1], tf[m], acc[b]);
     }
     if (SAME) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * LA, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);
 #pragma unroll
       for (int m = 0; m < NM - LA; ++m) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);
     }
@@ -1201,49 +1269,49 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkv(BwdArgs a) {
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  if (nsteps > 0 && !isA) {
-    uint32_t ovr[VW::NWW];
-    VW::lane_offsets(DV * 2, wb, lane, ovr);
-    VW::dma_untracked(smem + O_V, rsrc_words(a.Vr + ((int64_t)(cbs + J) * Hkv + c) * CB * DV, (int64_t)CB * DV * 2),
-                      ovr, wb);
-    if (gthread) gamh(0)[tid - 256] = (_Float16)fast_exp2((float)(lam_of(I1) - lamJ));
+  Pos cur{I1, 0, 0, 0}, nxt = cur;
+  if (nsteps > 0) {
+    if (isA) stage_rows(cur, 0);
+    else stage_cols(cur, 0);
+    if (gthread) gamh(0)[tid] = (_Float16)fast_exp2((float)(lam_of(I1) - lamJ));
   }
 
   // The two waves of a pair run separate loops with the same barriers, so
   // each keeps only its own values live.
   if (isA) {
     const uint32_t apx_ = opaque(apx), ams_ = opaque(ams);
-    Pos cur{I1, 0, 0, 0};
     int prev_ord = 0;
+    double lamI = gthread ? lam_of(I1) : 0.0, lamN = 0.0;
     for (int k = 0; k < nsteps; ++k) {
-      const int qs = k % 3, ds = k & 1;
+      const int b = k & 1;
+      if (k + 1 < nsteps) advance(nxt);
+      const bool first_of_chunk = k == 0 || cur.ord != prev_ord;
+      const bool last_of_chunk = k + 1 < nsteps && nxt.ord != cur.ord;
       wait_all();
-      __syncthreads();  // step k landed; every read of step k - 1 is done
+      __syncthreads();  // step k's rows landed; every read of step k - 1 is done
+      // the next chunk's Lam row (used at this chunk's last step; the wait at
+      // the top of the next step covers it)
+      if (first_of_chunk && gthread && cur.I - 1 >= I0) lamN = lam_of(cur.I - 1);
       f32x16 xr[2];
-      first(qs * QT::BYTES, xr);
-      // P of both halves: fp32 into the pair's exchange buffer, fp16 kept as
-      // the A operand of dV
+      first(b * QT::BYTES, xr);
+      // P of both halves: fp16 into the pair's exchange buffer, kept as the A
+      // operand of dV
       f16x8 pf[2][2];
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         f32x4 mq[4];
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
-          mq[q4] = *(const __attribute__((address_space(3))) f32x4 *)lds_at(ams_ + ds * 256 + 4 * (32 * h2 + 8 * q4));
+          mq[q4] = *(const __attribute__((address_space(3))) f32x4 *)lds_at(ams_ + b * 256 + 4 * (32 * h2 + 8 * q4));
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          f32x4 p4;
+        for (int j = 0; j < 16; ++j) pf[h2][j >> 3][j & 7] = (_Float16)fast_exp2(xr[h2][j] * sl2 - mq[j >> 2][j & 3]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int j = 4 * q4 + e;
-            const float p = fast_exp2(xr[h2][j] * sl2 - mq[q4][e]);
-            p4[e] = p;
-            pf[h2][j >> 3][j & 7] = (_Float16)p;
-          }
-          *(__attribute__((address_space(3))) f32x4 *)lds_at(apx_ + 16 * 64 * (h2 * 4 + q4)) = p4;
-        }
+        for (int u = 0; u < 2; ++u)
+          *(__attribute__((address_space(3))) f16x8 *)lds_at(apx_ + 16 * 64 * (2 * h2 + u)) = pf[h2][u];
       }
-      lds_barrier();  // P is in LDS
+      // the row copies of the next step (their stages were last read in step k - 1)
+      if (k + 1 < nsteps) stage_rows(nxt, b ^ 1);
+      lds_barrier();  // P is in LDS, step k's transposed tiles landed
       if (cur.ord != prev_ord) {  // entered a nearer chunk: dV so far times gamma_I / gamma_{I-1}
         prev_ord = cur.ord;
         const float *rt = rat(cur.ord & 1);
@@ -1254,60 +1322,49 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkv(BwdArgs a) {
           for (int j = 0; j < 16; ++j) acc[bv][j] *= r;
         }
       }
-      second(pf, ds * DR::BYTES);  // dV += P^T dhat
-      if (k + 1 < nsteps) advance(cur);
-    }
-  } else {
-    const uint32_t apx_ = opaque(apx);
-    f16x8 dsp[2][2];  // dS of the previous step (both halves), the A operand of its dK product
-    Pos cur{I1, 0, 0, 0}, nxt = cur;
-    if (nsteps > 0) stage(cur, 0, 0);
-    int prev_ord = -1;
-    double lamI = gthread ? lam_of(I1) : 0.0, lamN = 0.0;
-    for (int k = 0; k < nsteps; ++k) {
-      const int ds = k & 1;
-      if (k + 1 < nsteps) advance(nxt);
-      const bool last_of_chunk = k + 1 < nsteps && nxt.ord != cur.ord;
-      if (last_of_chunk && gthread) lamN = lam_of(nxt.I);  // used at the end of the step
-      wait_all();
-      __syncthreads();  // step k landed; every read of step k - 1 is done
-      if (k + 1 < nsteps) stage(nxt, (k + 1) % 3, ds ^ 1);
-      if (k > 0) second(dsp, ((k + 2) % 3) * QT::BYTES);  // dK of the previous step
-      if (cur.ord != prev_ord) {  // first step of a query chunk: V (.) gamma_IJ
-        prev_ord = cur.ord;
-        const _Float16 *gmh = gamh(cur.ord & 1);
-        f16x8 r[NSV], gv[NSV];
-#pragma unroll
-        for (int i = 0; i < NSV; ++i) {
-          r[i] = *(const f16x8 *)(smem + O_V + VRT::off(32 * pr + n, 2 * i + hh));
-          gv[i] = *(const f16x8 *)(gmh + 16 * i + 8 * hh);
-        }
-#pragma unroll
-        for (int i = 0; i < NSV; ++i) kf[i] = r[i] * gv[i];
-      }
-      f32x16 xr[2];
-      first(ds * DR::BYTES, xr);
-      lds_barrier();  // A's P is in LDS
-      f32x4 p4[2][4];
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          p4[h2][q4] = *(const __attribute__((address_space(3))) f32x4 *)lds_at(apx_ + 16 * 64 * (h2 * 4 + q4));
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) dsp[h2][j >> 3][j & 7] = (_Float16)(p4[h2][j >> 2][j & 3] * xr[h2][j]);
+      second(pf, b * DX::BYTES);  // dV += P^T dhat
       if (last_of_chunk && gthread) {
-        // the next chunk's gamma and the ratio A applies on entering it (the
+        // the next chunk's gamma and the ratio applied on entering it (the
         // buffer's last readers passed the barrier that began this chunk)
-        gamh(nxt.ord & 1)[tid - 256] = (_Float16)fast_exp2((float)(lamN - lamJ));
-        rat(nxt.ord & 1)[tid - 256] = fast_exp2((float)(lamI - lamN));
+        gamh(nxt.ord & 1)[tid] = (_Float16)fast_exp2((float)(lamN - lamJ));
+        rat(nxt.ord & 1)[tid] = fast_exp2((float)(lamI - lamN));
         lamI = lamN;
       }
       cur = nxt;
     }
-    if (nsteps > 0) second(dsp, ((nsteps - 1) % 3) * QT::BYTES);  // dK of the last step
+  } else {
+    const uint32_t apx_ = opaque(apx);
+    f16x8 dsp[2][2];  // dS of the previous step (both halves), the A operand of its dK product
+    int prev_ord = -1;
+    for (int k = 0; k < nsteps; ++k) {
+      const int b = k & 1;
+      if (k + 1 < nsteps) advance(nxt);
+      lds_barrier();  // step k's rows landed (A waited for them); every read of step k - 1 is done
+      if (k > 0) second(dsp, (b ^ 1) * QX::BYTES);  // dK of the previous step
+      if (cur.ord != prev_ord) {  // first step of a query chunk: V (.) gamma_IJ
+        prev_ord = cur.ord;
+        const _Float16 *gmh = gamh(cur.ord & 1);
+#pragma unroll
+        for (int i = 0; i < NSV; ++i) kf[i] = vr[i] * *(const f16x8 *)(gmh + 16 * i + 8 * hh);
+      }
+      f32x16 xr[2];
+      first(b * DR::BYTES, xr);
+      wait_all();     // this wave's transposed copies of step k landed
+      lds_barrier();  // A's P is in LDS
+      f16x8 p16[2][2];
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        p16[g >> 1][g & 1] = *(const __attribute__((address_space(3))) f16x8 *)lds_at(apx_ + 16 * 64 * g);
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) dsp[h2][j >> 3][j & 7] = (_Float16)((float)p16[h2][j >> 3][j & 7] * xr[h2][j]);
+      // the transposed copies of the next step (their stages were last read
+      // by this step's dK and the previous step's dV)
+      if (k + 1 < nsteps) stage_cols(nxt, b ^ 1);
+      cur = nxt;
+    }
+    if (nsteps > 0) second(dsp, ((nsteps - 1) & 1) * QX::BYTES);  // dK of the last step
   }
   if (kb >= L) return;
   // epilogue: dk (B), dv (A; inter part scaled to the key: exp(Gl_end(J) -

@@ -156,8 +156,9 @@ __global__ void __launch_bounds__(128) k_chunk_logprefix(const float *__restrict
 
 // Transposed fp16 tiles of a [Ttot, H, D] input: out[chunk][h][d][key_pos(t)]
 // for the CB tokens of each 128-chunk (zero past the end of the sequence).
+// in_kind: 0 bf16, 1 fp32, 2 fp16.
 template <int D>
-__global__ void __launch_bounds__(256) k_tiles_t(const void *__restrict__ in, bool in_f32, Plan plan, int H,
+__global__ void __launch_bounds__(256) k_tiles_t(const void *__restrict__ in, int in_kind, Plan plan, int H,
                                                  _Float16 *__restrict__ out) {
   // LDS tile [d][CB] with the 16-byte chunk index of row d XORed with
   // (d / 8) % 16: the eight channels one thread stores (rows d8 .. d8 + 7,
@@ -176,7 +177,11 @@ __global__ void __launch_bounds__(256) k_tiles_t(const void *__restrict__ in, bo
     const int t = e / (D / 8), d8 = 8 * (e % (D / 8));
     const int64_t base = ((tok0 + min(t, n - 1)) * H + h) * D + d8;
     float val[8];
-    if (in_f32) {
+    if (in_kind == 2) {
+      const f16x8 r = *(const f16x8 *)((const _Float16 *)in + base);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) val[i] = (float)r[i];
+    } else if (in_kind == 1) {
       const float4 lo = *(const float4 *)((const float *)in + base), hi = *(const float4 *)((const float *)in + base + 4);
       val[0] = lo.x; val[1] = lo.y; val[2] = lo.z; val[3] = lo.w; val[4] = hi.x; val[5] = hi.y; val[6] = hi.z; val[7] = hi.w;
     } else {
@@ -552,10 +557,10 @@ hipError_t launch_chunk_logprefix(int dv, const float *Gl2, const Plan &plan, in
   return hipGetLastError();
 }
 
-hipError_t launch_tiles_t(int D, const void *in, bool in_f32, const Plan &plan, int H, int ncb_ub, _Float16 *out,
+hipError_t launch_tiles_t(int D, const void *in, int in_kind, const Plan &plan, int H, int ncb_ub, _Float16 *out,
                           hipStream_t st) {
   dim3 grid(ncb_ub, H);
-  FIX_DV_SWITCH(D, hipLaunchKernelGGL(k_tiles_t<DVC>, grid, dim3(256), 0, st, in, in_f32, plan, H, out));
+  FIX_DV_SWITCH(D, hipLaunchKernelGGL(k_tiles_t<DVC>, grid, dim3(256), 0, st, in, in_kind, plan, H, out));
   return hipGetLastError();
 }
 

@@ -100,6 +100,7 @@ struct BwdArgs {
   const _Float16 *Q16;         // [T, Hq, DK] q as fp16 (exact for |q| in [2^-14, 65504])
   const float *delta;          // [T, Hq, DV] gradient reaching x
   const _Float16 *dh;          // [T, Hq, DV] sigma * exp(Gl) * delta
+  const _Float16 *dhT;         // [chunk][Hq][DV][CB] the same as transposed tiles (key_pos order)
   const float *mb, *sig;       // [T, Hq] m log2e - e, sigma = 2^-e
   const float *qside;          // [T, Hkv, DV]
   // Operands of the pairs in the same or the adjacent chunk, relative to
@@ -177,7 +178,7 @@ hipError_t launch_decode_combine(const DecodeCache &dc, int units, const float *
                                  const void *w, const void *z, bool in_f32, bool out_f32, bool o_norm, float eps,
                                  void *o, float *m, hipStream_t st);
 hipError_t launch_to_f16(const void *in, bool in_f32, int64_t n, _Float16 *out, hipStream_t st);
-hipError_t launch_tiles_t(int D, const void *in, bool in_f32, const Plan &plan, int H, int ncb_ub, _Float16 *out,
+hipError_t launch_tiles_t(int D, const void *in, int in_kind, const Plan &plan, int H, int ncb_ub, _Float16 *out,
                           hipStream_t st);
 hipError_t launch_bwd_prep(int dv, const PrepArgs &a, int ncb_ub, hipStream_t st);
 hipError_t launch_dw_reduce(const float *part, const int *counts, int Hkv, int dv, float *dw, hipStream_t st);

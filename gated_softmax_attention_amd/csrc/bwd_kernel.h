@@ -1035,22 +1035,20 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdArgs a) {
 // 128 keys of one key chunk J and kv head, 8 waves: the 32 keys of pair p are
 // shared by wave p (A) and wave p + 4 (B), which the hardware places on the
 // same SIMD.  Query chunks go from the last to J + 2 and, within each, the G
-// query heads of the group, 64 query rows per step.  Step k runs as two
-// phases split by a barrier:
-//   phase 1  A: S_k = Q K^T, P_k (fp16) into LDS and registers, the copies
-//               of step k + 1's Q and dhat rows
-//            B: dK += dS_{k-1}^T Q_{k-1} with the dS it formed in step
-//               k - 1, then dP_k = dhat (V (.) gamma)^T
-//   phase 2  A: dV += P_k^T dhat_k
-//            B: dS_k = P_k dP_k, kept in registers for the next step, and the
-//               copies of step k + 1's transposed Q and dhat tiles
-// so that A's exponentials run beside B's products and each wave holds one
-// accumulator set and one key-side operand.  The first products read row
-// tiles, the second ones transposed tiles (the key_pos column order puts the
-// eight rows one lane needs side by side), all with 16-byte LDS reads run a
-// few products ahead of their MFMAs.  All query rows lie at least a chunk
-// after the keys, so no pair is masked; rows past the sequence end read as
-// zeros (their dP, dS and dhat are zero).
+// query heads of the group, 64 query rows per step, one barrier per step:
+//   A: S_k = Q K^T, P_k (fp16, into LDS and kept), dV += P_k^T dhat_k, and
+//      the copies of step k + 1's Q and dhat rows and row maxima
+//   B: dS_{k-1} = P_{k-1} (from LDS) times the dP_{k-1} it kept, dK +=
+//      dS_{k-1}^T Q_{k-1}, dP_k = dhat_k (V (.) gamma)^T, and the copy of
+//      step k + 1's transposed dhat tile
+// so that the waves of a pair never wait for each other within a step and
+// A's exponentials run beside B's products.  S and dP read row tiles, dV the
+// transposed dhat tile (key_pos column order: the eight rows a lane needs
+// are side by side) and dK the Q rows through the transposing LDS read; all
+// reads run a few products ahead of their MFMAs.  Q rows are kept three
+// steps (dK uses the previous step's), the other tiles two.  All query rows
+// lie at least a chunk after the keys, so no pair is masked; rows past the
+// sequence end read as zeros (their dP, dS and dhat are zero).
 // The decay product between the chunks, gamma_IJ = exp2(Lam[I-1] - Lam[J]),
 // enters dP through V (.) gamma_IJ (B rebuilds it per query chunk from the V
 // rows it keeps in registers) and dV through the accumulator: A accumulates
@@ -1067,18 +1065,15 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkv(BwdArgs a) {
   constexpr int RS = 64;             // query rows per step (two halves of 32)
   using QT = LdsTile<RS, DK * 2>;    // Q rows of a step (fp16)
   using DR = LdsTile<RS, DV * 2>;    // scaled dhat rows of a step (fp16)
-  using QX = LdsTile<DKP, RS * 2>;   // transposed Q of a step [d][row, key_pos order], rows padded to DKP
-  using QXD = LdsTile<DK, RS * 2>;   // the rows a copy fills
-  using DX = LdsTile<DVP, RS * 2>;   // transposed dhat of a step
-  using DXD = LdsTile<DV, RS * 2>;
+  using DX = LdsTile<DVP, RS * 2>;   // transposed dhat of a step [channel][row, key_pos order], rows padded to DVP
+  using DXD = LdsTile<DV, RS * 2>;   // the rows a copy fills
   using QW = typename QT::template Waves<4>;  // copies issued by the four A waves
   using DW = typename DR::template Waves<4>;
-  using QXW = typename QXD::template Waves<4>;  // copies issued by the four B waves
-  using DXW = typename DXD::template Waves<4>;
+  using DXW = typename DXD::template Waves<4>;  // copies issued by the four B waves
   constexpr int PEX = 2 * 2 * 64 * 16;  // one pair's P of a step (fp16): [half][u][lane] 16 bytes
-  constexpr int O_Q = 0, O_D = O_Q + 2 * QT::BYTES, O_QX = O_D + 2 * DR::BYTES, O_DX = O_QX + 2 * QX::BYTES;
-  constexpr int O_M = O_DX + 2 * DX::BYTES, O_G = O_M + 2 * 256, O_GH = O_G + 2 * DVP * 4, O_P = O_GH + 2 * DVP * 2;
-  __shared__ __align__(1024) char smem[O_P + 4 * PEX];
+  constexpr int O_Q = 0, O_D = O_Q + 3 * QT::BYTES, O_DX = O_D + 2 * DR::BYTES, O_P = O_DX + 2 * DX::BYTES;
+  constexpr int O_M = O_P + 2 * 4 * PEX, O_G = O_M + 2 * 256, O_GH = O_G + 2 * DVP * 4;
+  __shared__ __align__(1024) char smem[O_GH + 2 * DVP * 2];
   auto rat = [&](int b) { return (float *)(smem + O_G) + b * DVP; };        // gamma_I / gamma_{I-1} per column
   auto gamh = [&](int b) { return (_Float16 *)(smem + O_GH) + b * DVP; };  // gamma_IJ (fp16)
 
@@ -1151,50 +1146,48 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkv(BwdArgs a) {
   }
 
   // Per-lane LDS addresses in stage 0: the first product's row fragments (Q
-  // for A, dhat for B) and the second's transposed fragments (dhat for A, Q
-  // for B) per output block b and 16-row group g; a step adds its stage's offset.
+  // for A, dhat for B) and the second's fragments (transposed dhat for A per
+  // output block and 16-row group; the two transposing-read pieces of the Q
+  // rows for B per output block); a step adds its stage's offset.
   const uint32_t sbase = lds_addr(smem);
   constexpr int NBA = NBK > NBV ? NBK : NBV;
   uint32_t a1[NKS], a2[NBA][4];
+  auto addresses = [&]() {  // computed in each wave's own loop branch
 #pragma unroll
-  for (int i = 0; i < NKS; ++i)
-    a1[i] = sbase + (isA ? O_Q + QT::off(n, min(2 * i + hh, QT::CPR - 1)) : O_D + DR::off(n, min(2 * i + hh, DR::CPR - 1)));
+    for (int i = 0; i < NKS; ++i)
+      a1[i] = sbase + (isA ? O_Q + QT::off(n, min(2 * i + hh, QT::CPR - 1)) : O_D + DR::off(n, min(2 * i + hh, DR::CPR - 1)));
 #pragma unroll
-  for (int b = 0; b < NBA; ++b)
+    for (int b = 0; b < NBA; ++b) {
+      uint32_t oq[2];
+      tr_offsets<QT>(32 * b, lane, oq);
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
-      a2[b][g] = sbase + (isA ? O_DX + DX::off(min(32 * b + n, DVP - 1), 2 * g + hh)
-                              : O_QX + QX::off(min(32 * b + n, DKP - 1), 2 * g + hh));
-  _Float16 *pex = (_Float16 *)(smem + O_P + PEX * pr);  // the pair's P of the step
-  const uint32_t apx = lds_addr(pex) + 16 * lane, ams = sbase + O_M + 4 * (4 * hh);
+      for (int g = 0; g < 4; ++g)
+        a2[b][g] = isA ? sbase + O_DX + DX::off(min(32 * b + n, DVP - 1), 2 * g + hh) : sbase + O_Q + (g < 2 ? oq[g] : 0);
+    }
+  };
+  const uint32_t apx = sbase + O_P + PEX * pr + 16 * lane, ams = sbase + O_M + 4 * (4 * hh);
   const uint32_t rb1 = isA ? 2 * DK : 2 * DV;  // row bytes of the first product's tile
 
-  // Copies: A the row tiles and row maxima of a step, B its transposed tiles.
+  // Copies: A the row tiles and row maxima of a step, B its transposed dhat tile.
   const int wb = wave & 3;
-  uint32_t oq[QW::NWW], od[DW::NWW], oqx[QXW::NWW], odx[DXW::NWW];
+  uint32_t oq[QW::NWW], od[DW::NWW], odx[DXW::NWW];
   QW::lane_offsets(Hq * DK * 2, wb, lane, oq);
   DW::lane_offsets(Hq * DV * 2, wb, lane, od);
-  QXW::lane_offsets(CB * 2, wb, lane, oqx);
   DXW::lane_offsets(CB * 2, wb, lane, odx);
-  auto stage_rows = [&](const Pos &p, int b) {
+  auto stage_rows = [&](const Pos &p, int qs, int b) {
     const int h = c * G + p.gq, qt0 = p.I * CB + RS * p.u;
     const int64_t qr = (st + qt0) * Hq + h;
     const int64_t nrow = L - qt0;  // rows past the sequence read as zeros
-    QW::dma_untracked(smem + O_Q + b * QT::BYTES, rsrc_words(a.Q16 + qr * DK, nrow * Hq * DK * 2), oq, wb);
+    QW::dma_untracked(smem + O_Q + qs * QT::BYTES, rsrc_words(a.Q16 + qr * DK, nrow * Hq * DK * 2), oq, wb);
     DW::dma_untracked(smem + O_D + b * DR::BYTES, rsrc_words(a.dh + qr * DV, nrow * Hq * DV * 2), od, wb);
     if (wb == 0) dma4_untracked(smem + O_M + b * 256, rsrc_words(a.mb + qr, nrow * Hq * 4), (uint32_t)lane * Hq * 4);
   };
   auto stage_cols = [&](const Pos &p, int b) {
     const int64_t ch = (int64_t)(cbs + p.I) * Hq + c * G + p.gq;
-    QXW::dma_untracked(smem + O_QX + b * QX::BYTES, rsrc_words(a.Qt + ch * DK * CB + RS * p.u, (int64_t)DK * CB * 2),
-                       oqx, wb);
     DXW::dma_untracked(smem + O_DX + b * DX::BYTES, rsrc_words(a.dhT + ch * DV * CB + RS * p.u, (int64_t)DV * CB * 2),
                        odx, wb);
   };
   // zero rows of the narrow transposed tiles (never copied)
-  if (DK < DKP)
-    for (int e = tid; e < (DKP - DK) * RS * 2 / 4; e += 512)
-      for (int b = 0; b < 2; ++b) ((uint32_t *)(smem + O_QX + b * QX::BYTES + DK * RS * 2))[e] = 0u;
   if (DV < DVP)
     for (int e = tid; e < (DVP - DV) * RS * 2 / 4; e += 512)
       for (int b = 0; b < 2; ++b) ((uint32_t *)(smem + O_DX + b * DX::BYTES + DV * RS * 2))[e] = 0u;
@@ -1213,33 +1206,6 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkv(BwdArgs a) {
   const int n1 = isA ? NS : NSV;     // k slabs of the first product
   const int n2 = isA ? NBV : NBK;    // output blocks of the second
 
-  // Second product, both halves: acc[b] += of[h2][u]^T (16-row group g =
-  // 2 h2 + u of the transposed tile at stage offset off); output block
-  // fastest, reads LA products ahead.
-  auto second = [&](const f16x8 (&of)[2][2], uint32_t off) {
-    constexpr int NM = 4 * NBA, LA = NM < 4 ? NM : 4;
-    f16x8 tf[NM];
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      const int g = m / NBA, b = m % NBA;
-      if (SAME || b < n2) tf[m] = lds_row16(a2[b][g] + off);
-    }
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      const int g = m / NBA, b = m % NBA;
-      if (SAME || b < n2) acc[b] = mma32(of[g >> 1][g & 1], tf[m], acc[b]);
-    }
-    if (SAME) {
-      __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);
-#pragma unroll
-      for (int m = 0; m < NM - LA; ++m) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  };
   // First product (A: S = Q K^T, B: dP = dhat (V (.) gamma)^T); lane = key,
   // register j = row r0 + 32 h2 + acc_row(hh, j).  The halves' chains
   // alternate, reads run four products ahead.
@@ -1271,7 +1237,7 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkv(BwdArgs a) {
 
   Pos cur{I1, 0, 0, 0}, nxt = cur;
   if (nsteps > 0) {
-    if (isA) stage_rows(cur, 0);
+    if (isA) stage_rows(cur, 0, 0);
     else stage_cols(cur, 0);
     if (gthread) gamh(0)[tid] = (_Float16)fast_exp2((float)(lam_of(I1) - lamJ));
   }
@@ -1279,6 +1245,7 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkv(BwdArgs a) {
   // The two waves of a pair run separate loops with the same barriers, so
   // each keeps only its own values live.
   if (isA) {
+    addresses();
     const uint32_t apx_ = opaque(apx), ams_ = opaque(ams);
     int prev_ord = 0;
     double lamI = gthread ? lam_of(I1) : 0.0, lamN = 0.0;
@@ -1288,14 +1255,14 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkv(BwdArgs a) {
       const bool first_of_chunk = k == 0 || cur.ord != prev_ord;
       const bool last_of_chunk = k + 1 < nsteps && nxt.ord != cur.ord;
       wait_all();
-      __syncthreads();  // step k's rows landed; every read of step k - 1 is done
+      __syncthreads();  // step k's tiles landed; step k - 1's readers are done
       // the next chunk's Lam row (used at this chunk's last step; the wait at
       // the top of the next step covers it)
       if (first_of_chunk && gthread && cur.I - 1 >= I0) lamN = lam_of(cur.I - 1);
       f32x16 xr[2];
-      first(b * QT::BYTES, xr);
-      // P of both halves: fp16 into the pair's exchange buffer, kept as the A
-      // operand of dV
+      first((k % 3) * QT::BYTES, xr);
+      // P of both halves: fp16, into the exchange buffer of the step's parity
+      // and kept as the A operand of dV
       f16x8 pf[2][2];
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
@@ -1307,11 +1274,10 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkv(BwdArgs a) {
         for (int j = 0; j < 16; ++j) pf[h2][j >> 3][j & 7] = (_Float16)fast_exp2(xr[h2][j] * sl2 - mq[j >> 2][j & 3]);
 #pragma unroll
         for (int u = 0; u < 2; ++u)
-          *(__attribute__((address_space(3))) f16x8 *)lds_at(apx_ + 16 * 64 * (2 * h2 + u)) = pf[h2][u];
+          *(__attribute__((address_space(3))) f16x8 *)lds_at(apx_ + b * 4 * PEX + 16 * 64 * (2 * h2 + u)) = pf[h2][u];
       }
       // the row copies of the next step (their stages were last read in step k - 1)
-      if (k + 1 < nsteps) stage_rows(nxt, b ^ 1);
-      lds_barrier();  // P is in LDS, step k's transposed tiles landed
+      if (k + 1 < nsteps) stage_rows(nxt, (k + 1) % 3, b ^ 1);
       if (cur.ord != prev_ord) {  // entered a nearer chunk: dV so far times gamma_I / gamma_{I-1}
         prev_ord = cur.ord;
         const float *rt = rat(cur.ord & 1);
@@ -1322,7 +1288,27 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkv(BwdArgs a) {
           for (int j = 0; j < 16; ++j) acc[bv][j] *= r;
         }
       }
-      second(pf, b * DX::BYTES);  // dV += P^T dhat
+      // dV += P^T dhat: output block fastest, reads four products ahead
+      {
+        constexpr int NM = 4 * NBV, LA = NM < 4 ? NM : 4;
+        const uint32_t off = b * DX::BYTES;
+        f16x8 tf[NM];
+#pragma unroll
+        for (int m = 0; m < NM; ++m) tf[m] = lds_row16(a2[m % NBV][m / NBV] + off);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          const int g = m / NBV;
+          acc[m % NBV] = mma32(pf[g >> 1][g & 1], tf[m], acc[m % NBV]);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);
+#pragma unroll
+        for (int m = 0; m < NM - LA; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       if (last_of_chunk && gthread) {
         // the next chunk's gamma and the ratio applied on entering it (the
         // buffer's last readers passed the barrier that began this chunk)
@@ -1332,39 +1318,65 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkv(BwdArgs a) {
       }
       cur = nxt;
     }
+    wait_all();
+    __syncthreads();  // the barrier B's last dK step waits at
   } else {
+    addresses();
     const uint32_t apx_ = opaque(apx);
-    f16x8 dsp[2][2];  // dS of the previous step (both halves), the A operand of its dK product
     int prev_ord = -1;
+    f32x16 dpk[2];  // dP of the previous step
+    // dS of step k - 1 from A's P (LDS, exchange buffer pb) and the kept dP,
+    // then dK += dS^T Q_{k-1} with Q read transposed from its row stage qs
+    auto dk_step = [&](int pb, int qs) {
+      f16x8 dsp[2][2];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f16x8 p = *(const __attribute__((address_space(3))) f16x8 *)lds_at(apx_ + pb * 4 * PEX + 16 * 64 * g);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dsp[g >> 1][g & 1][i] = (_Float16)((float)p[i] * dpk[g >> 1][8 * (g & 1) + i]);
+      }
+      constexpr int NM = 4 * NBK, LA = NM < 4 ? NM : 4;
+      const uint32_t off = qs * QT::BYTES;
+      f16x4 tp[NM][2];
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) tp[m][t] = lds_tr8(a2[m % NBK][t] + off + 16 * (m / NBK) * (2 * DK));
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        const int g = m / NBK;
+        acc[m % NBK] = mma32(dsp[g >> 1][g & 1], __builtin_shufflevector(tp[m][0], tp[m][1], 0, 1, 2, 3, 4, 5, 6, 7),
+                             acc[m % NBK]);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * LA, 0);
+#pragma unroll
+      for (int m = 0; m < NM - LA; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    };
     for (int k = 0; k < nsteps; ++k) {
       const int b = k & 1;
       if (k + 1 < nsteps) advance(nxt);
-      lds_barrier();  // step k's rows landed (A waited for them); every read of step k - 1 is done
-      if (k > 0) second(dsp, (b ^ 1) * QX::BYTES);  // dK of the previous step
+      wait_all();
+      __syncthreads();  // step k's tiles landed; step k - 1's readers are done
+      // the transposed dhat copy of the next step (its stage was last read in step k - 1)
+      if (k + 1 < nsteps) stage_cols(nxt, b ^ 1);
+      if (k > 0) dk_step(b ^ 1, (k + 2) % 3);
       if (cur.ord != prev_ord) {  // first step of a query chunk: V (.) gamma_IJ
         prev_ord = cur.ord;
         const _Float16 *gmh = gamh(cur.ord & 1);
 #pragma unroll
         for (int i = 0; i < NSV; ++i) kf[i] = vr[i] * *(const f16x8 *)(gmh + 16 * i + 8 * hh);
       }
-      f32x16 xr[2];
-      first(b * DR::BYTES, xr);
-      wait_all();     // this wave's transposed copies of step k landed
-      lds_barrier();  // A's P is in LDS
-      f16x8 p16[2][2];
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        p16[g >> 1][g & 1] = *(const __attribute__((address_space(3))) f16x8 *)lds_at(apx_ + 16 * 64 * g);
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) dsp[h2][j >> 3][j & 7] = (_Float16)((float)p16[h2][j >> 3][j & 7] * xr[h2][j]);
-      // the transposed copies of the next step (their stages were last read
-      // by this step's dK and the previous step's dV)
-      if (k + 1 < nsteps) stage_cols(nxt, b ^ 1);
+      first(b * DR::BYTES, dpk);
       cur = nxt;
     }
-    if (nsteps > 0) second(dsp, ((nsteps - 1) & 1) * QX::BYTES);  // dK of the last step
+    wait_all();
+    __syncthreads();  // A's last P is in LDS
+    if (nsteps > 0) dk_step((nsteps - 1) & 1, (nsteps - 1) % 3);
   }
   if (kb >= L) return;
   // epilogue: dk (B), dv (A; inter part scaled to the key: exp(Gl_end(J) -
@@ -1373,9 +1385,12 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkv(BwdArgs a) {
   // cannot tell the output and input buffers apart, so a load placed after a
   // store waits for it: inputs are loaded one half block ahead, before the
   // previous half block's stores.
+  // (lane indices taken afresh: values kept from before the loops would stay
+  // live across them)
+  const int le = (int)(opaque((uint32_t)threadIdx.x) & 63), hhe = le >> 5, ne = le & 31;
   const int tend = min((J + 1) * CB, L) - 1;
   // element offset of register j's key row from the workgroup's first key row
-  auto krow = [&](int j) { return (uint32_t)min(acc_row(hh, j), L - 1 - kb) * (uint32_t)Hkv; };
+  auto krow = [&](int j) { return (uint32_t)min(acc_row(hhe, j), L - 1 - kb) * (uint32_t)Hkv; };
   const int64_t row0 = (st + kb) * Hkv + c;
   const int64_t nk = (int64_t)min(32, L - kb) * Hkv;  // rows covered by the resources below
   if (!isA) {
@@ -1383,7 +1398,7 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkv(BwdArgs a) {
     const rsrc_t rk = make_rsrc((const char *)a.dk + row0 * DK * (a.out_f32 ? 4 : 2), nk * DK * (a.out_f32 ? 4 : 2));
     float pk[2][16];
     auto load_dk = [&](int bk, float (&part)[16]) {
-      const uint32_t col = min(32 * bk + n, DK - 1);
+      const uint32_t col = min(32 * bk + ne, DK - 1);
 #pragma unroll
       for (int j = 0; j < 16; ++j) part[j] = buf_ld_f32(rki, 4 * (krow(j) * DK + col));
     };
@@ -1391,11 +1406,11 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkv(BwdArgs a) {
 #pragma unroll
     for (int bk = 0; bk < NBK; ++bk) {
       if (bk + 1 < NBK) load_dk(bk + 1, pk[(bk + 1) & 1]);
-      const int col = 32 * bk + n;
+      const int col = 32 * bk + ne;
       if (col < DK)
 #pragma unroll
         for (int j = 0; j < 16; ++j)
-          if (kb + acc_row(hh, j) < L) buf_st_out(rk, krow(j) * DK + col, a.scale * acc[bk][j] + pk[bk & 1][j], a.out_f32);
+          if (kb + acc_row(hhe, j) < L) buf_st_out(rk, krow(j) * DK + col, a.scale * acc[bk][j] + pk[bk & 1][j], a.out_f32);
     }
     return;
   }
@@ -1407,7 +1422,7 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkv(BwdArgs a) {
   float gend[NBV];
 #pragma unroll
   for (int bv = 0; bv < NBV; ++bv) {
-    const int col = min(32 * bv + n, DV - 1);
+    const int col = min(32 * bv + ne, DV - 1);
     gend[bv] = a.Gl2[((st + tend) * Hkv + c) * DV + col];
     if (nsteps > 0) {  // gamma_{J+2,J} = exp2(Lam[J+1] - Lam[J]) joins the key-side factor
       const double l1 = a.Lam[((int64_t)(cbs + J + 1) * Hkv + c) * DV + col];
@@ -1418,7 +1433,7 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkv(BwdArgs a) {
   // half blocks (8 rows of one column block)
   float in[2][4][8];  // [slot][prefix sum, partial, qside, v][row]
   auto load_dv = [&](int u, float (&x)[4][8]) {
-    const uint32_t col = min(32 * (u >> 1) + n, DV - 1), h8 = 8 * (u & 1);
+    const uint32_t col = min(32 * (u >> 1) + ne, DV - 1), h8 = 8 * (u & 1);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const uint32_t o = krow(h8 + j) * DV + col;
@@ -1432,11 +1447,11 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkv(BwdArgs a) {
 #pragma unroll
   for (int u = 0; u < 2 * NBV; ++u) {
     if (u + 1 < 2 * NBV) load_dv(u + 1, in[(u + 1) & 1]);
-    const int bv = u >> 1, h8 = 8 * (u & 1), col = 32 * bv + n;
+    const int bv = u >> 1, h8 = 8 * (u & 1), col = 32 * bv + ne;
     if (col < DV)
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        if (kb + acc_row(hh, h8 + j) < L) {
+        if (kb + acc_row(hhe, h8 + j) < L) {
           const uint32_t o = krow(h8 + j) * DV + col;
           const float(&x)[4][8] = in[u & 1];
           const float dvv = fast_exp2(gend[bv] - x[0][j]) * acc[bv][h8 + j] + x[1][j];

@@ -20,7 +20,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfixattn.so")
 
-FIX_OK, FIX_E_INVALID, FIX_E_UNSUPPORTED, FIX_E_WORKSPACE, FIX_E_HIP = range(5)
+FIX_OK, FIX_E_INVALID, FIX_E_UNSUPPORTED, FIX_E_WORKSPACE, FIX_E_HIP, FIX_E_RANGE = range(6)
 FIX_BF16, FIX_F32 = 0, 1
 
 
@@ -86,6 +86,8 @@ def _load():
     lib.fix_decode_step.restype = ctypes.c_int
     lib.fix_decode_step_noalloc.argtypes = [DD, P, P, P, P, P, P, P]
     lib.fix_decode_step_noalloc.restype = ctypes.c_int
+    lib.fix_attn_check_inputs.argtypes = [D, P, P, P, S, P]
+    lib.fix_attn_check_inputs.restype = ctypes.c_int
     lib.fix_attn_status_string.argtypes = [ctypes.c_int]
     lib.fix_attn_status_string.restype = ctypes.c_char_p
     lib.fix_attn_last_hip_error.argtypes = []
@@ -156,6 +158,19 @@ def fix_attn_bwd(desc, q, k, v, g, o_norm_weight, o_gate, m, rstd, x, d_o, dq, d
                               _ptr(dv), _ptr(dg), _ptr(d_o_norm_weight), _ptr(d_o_gate), _ptr(ws), ws_bytes,
                               stream)
     _check("fix_attn_bwd", st)
+
+
+def fix_attn_check_inputs(desc, q, k, ws, ws_bytes, stream) -> int:
+    """Status of the q/k range check (FIX_OK or FIX_E_RANGE; other codes as the C call)."""
+    return _load().fix_attn_check_inputs(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(ws), ws_bytes, stream)
+
+
+def check_inputs(q, k, v, cu_seqlens=None) -> int:
+    """fix_attn_check_inputs on torch tensors (synchronizes the current stream)."""
+    import torch
+    desc = make_desc(q, k, v, cu_seqlens)
+    ws = torch.empty(64, dtype=torch.uint8, device=q.device)
+    return fix_attn_check_inputs(desc, q, k, ws, ws.numel(), torch.cuda.current_stream().cuda_stream)
 
 
 def make_desc(q, k, v, cu_seqlens=None, *, o_norm=False, scale=None, eps=1e-5, out_dtype=None,
@@ -305,7 +320,7 @@ __all__ = [
     "parallel_fix_attn", "forward", "backward", "make_desc", "library", "fix_attn_desc",
     "fix_attn_validate", "fix_attn_fwd_workspace_size", "fix_attn_bwd_workspace_size", "fix_attn_fwd",
     "fix_attn_bwd", "FixAttnError", "FIX_OK", "FIX_E_INVALID", "FIX_E_UNSUPPORTED", "FIX_E_WORKSPACE",
-    "FIX_E_HIP", "FIX_BF16", "FIX_F32",
+    "FIX_E_HIP", "FIX_E_RANGE", "FIX_BF16", "FIX_F32", "fix_attn_check_inputs",
 ]
 
 

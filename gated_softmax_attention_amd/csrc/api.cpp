@@ -573,6 +573,27 @@ fix_status fix_decode_step_noalloc(const fix_decode_desc *d, const void *cache, 
   return fix_decode_step(d, cache, q, o_norm_weight, o_gate, o, m, ws, FIX_DECODE_SCRATCH_BYTES, hip_stream);
 }
 
+fix_status fix_attn_check_inputs(const fix_attn_desc *d, const void *q, const void *k, void *ws, size_t ws_bytes,
+                                 void *hip_stream) {
+  const fix_status v = fix_attn_validate(d);
+  if (v != FIX_OK) return v;
+  if (!q || !k || !ws) return FIX_E_INVALID;
+  if (ws_bytes < 8) return FIX_E_WORKSPACE;
+  const hipStream_t st = (hipStream_t)hip_stream;
+  const bool f32in = d->in_dtype == FIX_F32;
+  const int64_t nt = d->cu_seqlens ? d->T : d->B * d->T;
+  unsigned *mx = (unsigned *)ws;
+  hipError_t e = hipMemsetAsync(mx, 0, 8, st);
+  if (e == hipSuccess) e = fix::launch_absmax(q, f32in, nt * d->Hq * d->dk, mx, st);
+  if (e == hipSuccess) e = fix::launch_absmax(k, f32in, nt * d->Hkv * d->dk, mx + 1, st);
+  unsigned h[2] = {0, 0};
+  if (e == hipSuccess) e = hipMemcpyAsync(h, mx, 8, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e);
+  const unsigned lim = 0x477FE000u;  // 65504.0f, the largest finite fp16
+  return (h[0] > lim || h[1] > lim) ? FIX_E_RANGE : FIX_OK;
+}
+
 const char *fix_attn_status_string(fix_status s) {
   switch (s) {
     case FIX_OK: return "ok";
@@ -580,6 +601,7 @@ const char *fix_attn_status_string(fix_status s) {
     case FIX_E_UNSUPPORTED: return "unsupported shape or head dimension (head dims must be 16, 32, 64 or 128)";
     case FIX_E_WORKSPACE: return "workspace too small";
     case FIX_E_HIP: return "HIP launch failed";
+    case FIX_E_RANGE: return "q or k holds a value the fp16 operands cannot hold (|x| > 65504, inf or NaN)";
   }
   return "unknown status";
 }

@@ -523,6 +523,27 @@ __global__ void __launch_bounds__(256) k_to_f16(const void *__restrict__ in, boo
   ((f16x8 *)out)[e] = h;
 }
 
+// Largest |x| over n elements (bf16 or fp32), as the bit pattern of a
+// non-negative float (whose integer order is the float order; a NaN sorts
+// above +inf), folded into *out with an atomic max.
+__global__ void __launch_bounds__(256) k_absmax(const void *__restrict__ in, bool in_f32, int64_t n,
+                                                unsigned *__restrict__ out) {
+  unsigned mx = 0;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
+    const float v = in_f32 ? ((const float *)in)[e] : __uint_as_float((uint32_t)((const uint16_t *)in)[e] << 16);
+    mx = max(mx, __float_as_uint(fabsf(v)));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = max(mx, (unsigned)__shfl_xor((int)mx, o));
+  if ((threadIdx.x & 63) == 0 && mx) atomicMax(out, mx);
+}
+
+hipError_t launch_absmax(const void *in, bool in_f32, int64_t n, unsigned *out, hipStream_t st) {
+  const int64_t blocks = min((int64_t)2048, (n + 255) / 256);
+  if (blocks > 0) hipLaunchKernelGGL(k_absmax, dim3((unsigned)blocks), dim3(256), 0, st, in, in_f32, n, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_to_f16(const void *in, bool in_f32, int64_t n, _Float16 *out, hipStream_t st) {
   const int64_t n8 = n / 8;
   if (n8 > 0) hipLaunchKernelGGL(k_to_f16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, in, in_f32, n8, out);

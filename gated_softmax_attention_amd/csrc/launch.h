@@ -178,6 +178,7 @@ hipError_t launch_decode_combine(const DecodeCache &dc, int units, const float *
                                  const void *w, const void *z, bool in_f32, bool out_f32, bool o_norm, float eps,
                                  void *o, float *m, hipStream_t st);
 hipError_t launch_to_f16(const void *in, bool in_f32, int64_t n, _Float16 *out, hipStream_t st);
+hipError_t launch_absmax(const void *in, bool in_f32, int64_t n, unsigned *out, hipStream_t st);
 hipError_t launch_tiles_t(int D, const void *in, int in_kind, const Plan &plan, int H, int ncb_ub, _Float16 *out,
                           hipStream_t st);
 hipError_t launch_bwd_prep(int dv, const PrepArgs &a, int ncb_ub, hipStream_t st);

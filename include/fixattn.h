@@ -46,11 +46,15 @@
  *  - Scalar gate: with gate_scalar = 1, g (and dg) hold one value per token
  *    and kv head, [B,T,Hkv] fp32, the decay being the same for every channel
  *    (the forgetting-attention case, "Forgetting Transformer" page,
- *    abstract).  The forward then applies it as a bias on the logits,
- *    exp(s_ij - m_i + G_i - G_j), with no value scaling (its own kernel);
- *    the backward runs the per-channel path on a broadcast copy of g and
- *    sums dg over the channels.  Results equal those of the per-channel
- *    call with g broadcast over dv.
+ *    abstract).  Forward and backward then apply it as a bias on the
+ *    logits, exp(s_ij - m_i + G_i - G_j), with no value scaling (kernels of
+ *    their own); dg is the suffix sum over tokens of the row sums minus the
+ *    column sums of dS.  Results equal those of the per-channel call with g
+ *    broadcast over dv (dg summed over the channels).
+ *  - Range: the backward (and the forward with fp32 inputs) runs some
+ *    products on q and k rounded to fp16, so |q| and |k| must not exceed
+ *    65504 (fix_attn_check_inputs reports whether they do).  Elements below
+ *    2^-14 become fp16 subnormals: each keeps an absolute error below 2^-25.
  *  - Preconditions not checked (they would need a device scan): g <= 0
  *    (a forget gate; results for positive g are only as accurate as fp32
  *    range allows), cu_seqlens non-decreasing with cu[0] = 0 and
@@ -71,7 +75,8 @@ typedef enum {
   FIX_E_INVALID = 1,     /* malformed descriptor or a required NULL pointer */
   FIX_E_UNSUPPORTED = 2, /* well formed but outside what the kernels handle */
   FIX_E_WORKSPACE = 3,   /* workspace smaller than required */
-  FIX_E_HIP = 4          /* a HIP launch failed */
+  FIX_E_HIP = 4,         /* a HIP launch failed */
+  FIX_E_RANGE = 5        /* fix_attn_check_inputs: q or k outside the fp16 range */
 } fix_status;
 
 typedef enum {
@@ -141,6 +146,18 @@ fix_status fix_attn_bwd(const fix_attn_desc *d, const void *q, const void *k, co
                         const float *m, const float *rstd, const float *x, const void *d_o,
                         void *dq, void *dk, void *dv, float *dg, float *d_o_norm_weight,
                         void *d_o_gate, void *ws, size_t ws_bytes, void *hip_stream);
+
+/* Input range check for callers that cannot bound q and k: max |q| and
+ * max |k| over the whole descriptor (every row of B x T) on the device.
+ * Unlike the other entry points it synchronizes hip_stream (the result is
+ * read back).  ws: at least 8 bytes of device scratch (the start of the
+ * forward or backward workspace will do; contents overwritten).
+ * Returns FIX_OK when every |q|, |k| <= 65504 (finite fp16), FIX_E_RANGE
+ * when one is larger, infinite or NaN; FIX_E_INVALID / FIX_E_UNSUPPORTED as
+ * fix_attn_validate, or for a NULL pointer; FIX_E_WORKSPACE when ws_bytes < 8;
+ * FIX_E_HIP when a launch, copy or the synchronization fails. */
+fix_status fix_attn_check_inputs(const fix_attn_desc *d, const void *q, const void *k, void *ws, size_t ws_bytes,
+                                 void *hip_stream);
 
 /* ---- Decode: the newest token of each sequence against a cache ----
  * Inference runs the operation above one token at a time (FiX ICML 2026

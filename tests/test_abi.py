@@ -96,9 +96,19 @@ def test_entry_points_reject_before_launching():
     assert st == F.FIX_E_INVALID
 
 
+def test_check_inputs_rejects_before_launching():
+    lib = F.library()
+    fake = 0x10000
+    assert F.fix_attn_check_inputs(desc(dk=48), fake, fake, fake, 64, None) == F.FIX_E_UNSUPPORTED
+    assert F.fix_attn_check_inputs(desc(), None, fake, fake, 64, None) == F.FIX_E_INVALID
+    assert F.fix_attn_check_inputs(desc(), fake, fake, None, 64, None) == F.FIX_E_INVALID
+    assert F.fix_attn_check_inputs(desc(), fake, fake, fake, 4, None) == F.FIX_E_WORKSPACE
+    assert b"65504" in lib.fix_attn_status_string(F.FIX_E_RANGE)
+
+
 def test_status_strings():
     lib = F.library()
-    for s in range(5):
+    for s in range(6):
         assert lib.fix_attn_status_string(s)
     assert b"head dim" in lib.fix_attn_status_string(F.FIX_E_UNSUPPORTED)
     assert lib.fix_attn_last_hip_error() == 0

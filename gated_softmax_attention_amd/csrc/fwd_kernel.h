@@ -65,7 +65,7 @@ __global__ void __launch_bounds__(256, 2) k_fix_fwd(FwdArgs a) {
   constexpr int N_E = N_O + 4 * OT::BYTES, N_END = N_E + 4 * DVP * 4;
   constexpr int O_K = 0, O_V = O_K + 2 * KT::BYTES, O_G = O_V + 2 * VT::BYTES, O_FAR = O_G + 2 * 1024;
   constexpr int O_A = O_FAR > N_END ? O_FAR : N_END;
-  __shared__ __align__(1024) char smem[O_A + 4 * 32 * 4];
+  __shared__ __align__(1024) char smem[O_A + 2 * 4 * 32 * 4];
   auto Ks = [&](int b) { return smem + O_K + b * KT::BYTES; };
   auto Vs = [&](int b) { return smem + O_V + b * VT::BYTES; };
   auto Gs = [&](int b) { return (float *)(smem + O_G + b * 1024); };  // 256 floats, DV used
@@ -140,7 +140,25 @@ __global__ void __launch_bounds__(256, 2) k_fix_fwd(FwdArgs a) {
   for (int b = 0; b < NB; ++b)
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc[b][j] = 0.f;
-  float m_used = -INFINITY, m_true = -INFINITY;  // per row n, log2 units
+  float m_used = -INFINITY;  // per row n, log2 units
+  // The exact row max lives in LDS (this wave's slot of row n; lanes n and
+  // n + 32 hold the same value): as a register it was spilled, and the
+  // reload's wait for vector memory also waited for the tile copies in flight.
+  // The slot address is formed where it is used, from the lane id, so that
+  // it is not a register kept (and spilled) across the loops either.
+  const uint32_t mt_base = uniform((int)lds_addr(smem + O_A + 4 * 32 * 4)) + 128 * wave;
+  auto mt_addr = [&]() {
+    uint32_t z = 0;
+    asm volatile("" : "+s"(z));
+    return mt_base + 4 * (__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, z)) & 31);
+  };
+  auto mt_write = [&](float v) { asm volatile("ds_write_b32 %0, %1" ::"v"(mt_addr()), "v"(v) : "memory"); };
+  auto mt_read = [&]() {
+    float v;
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(mt_addr()) : "memory");
+    return v;
+  };
+  mt_write(-INFINITY);
 
   // Multiply accumulator row r by the row factor held in lane r of this half-wave pair.
   auto row_scale = [&](float f) {
@@ -164,7 +182,7 @@ __global__ void __launch_bounds__(256, 2) k_fix_fwd(FwdArgs a) {
   };
   // Fold a new row max (log2 units, identical in lanes n and n+32) into the running state.
   auto update_max = [&](float mx) {
-    m_true = fmaxf(m_true, mx);
+    mt_write(fmaxf(mt_read(), mx));
     if (__any(mx > m_used + TAU)) {
       float m_new = fmaxf(m_used, mx);
       float alpha = fast_exp2(m_used - m_new);
@@ -460,6 +478,7 @@ __global__ void __launch_bounds__(256, 2) k_fix_fwd(FwdArgs a) {
       }
     }
   }
+  const float m_true = mt_read();
   if (__any(m_used != m_true)) {
     float alpha = fast_exp2(m_used - m_true);
     m_used = m_true;

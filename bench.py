@@ -30,15 +30,22 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16/fp16 MFMA peak (AMD specification)
 
-# HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs of this workload, scaled by
-# a plain-copy calibration (x2.0 reads, x1.0 writes); valid only for the sources they were
+# HBM bytes per launch (the last dispatch of the run: a timed step) from rocprofv3 FETCH_SIZE /
+# WRITE_SIZE runs of the training workload, scaled by a plain-copy calibration (x2.0 reads,
+# x1.0 writes); valid only for the sources they were
 # taken on (sha256 prefix over the files listed, the build flags included).  Reported as roofline.traffic, else null.
 TRAFFIC = {
-    "bwd_dkv": {"bytes": 2 * 1023348 * 1024 + 531964 * 1024, "sha": "73ac43155d216708",
+    "bwd_dkv": {"bytes": int(2 * 1213948.75 * 1024 + 542059.1875 * 1024), "sha": "240a83862f925743",
                 "files": ["gated_softmax_attention_amd/csrc/bwd_kernel.h",
                           "gated_softmax_attention_amd/csrc/common.h",
                           "gated_softmax_attention_amd/csrc/launch.h",
                           "gated_softmax_attention_amd/build.py"]},
+    "fox_bwd_dkv": {"bytes": int(2 * 380865.0 * 1024 + 278529.1875 * 1024), "sha": "ae05bac3911e9914",
+                    "files": ["gated_softmax_attention_amd/csrc/fox_bwd.h",
+                              "gated_softmax_attention_amd/csrc/fox_bwd_d128.hip",
+                              "gated_softmax_attention_amd/csrc/common.h",
+                              "gated_softmax_attention_amd/csrc/launch.h",
+                              "gated_softmax_attention_amd/build.py"]},
     "decode_step": {"bytes": int(2 * 135774.125 * 1024) + 1040 * 1024, "sha": "ca18dcf888947a22",
                     "files": ["gated_softmax_attention_amd/csrc/decode.hip",
                               "gated_softmax_attention_amd/csrc/common.h",
@@ -510,7 +517,8 @@ def main():
             ach = fl / sec / 1e12
             roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
-        roof["traffic"] = measured_traffic(dom)
+        # the stored counts were taken on the training workload (per-channel or scalar gate as run)
+        roof["traffic"] = measured_traffic(dom) if wl.name == "train" and not args.gate_logits else None
         roof["avg_launch_ms"] = round(avg[dom], 4)
     fwd_ms = sum(side_ms[0]) / len(side_ms[0])
     bwd_ms = sum(side_ms[1]) / len(side_ms[1]) if wl.backward else None

@@ -1,9 +1,9 @@
 // Measured peaks of MI355X (gfx950) for the roofline denominators the
 // benchmark reports beside the published ones: a loop of independent
-// 32x32x16 bf16 matrix products, a loop of independent v_exp_f32 chains, and
-// a plain 16-byte-per-lane device copy, and LDS read bandwidth (16-byte row
-// reads and the 8-byte transposing reads the matrix-product kernels use).  Not part of the attention library:
-// only `bench.py --peak-probe` loads this.
+// 32x32x16 bf16 matrix products, a loop of independent v_exp_f32 chains, a
+// plain 16-byte-per-lane device copy, and LDS read bandwidth (16-byte row
+// reads and the 8-byte transposing reads the matrix-product kernels use).
+// Not part of the attention library: only `bench.py --peak-probe` loads this.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

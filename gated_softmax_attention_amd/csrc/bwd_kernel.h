@@ -345,10 +345,11 @@ __global__ void __launch_bounds__(256, 1) k_bwd_intra_dq(BwdArgs a) {
 // wave w owns keys c0 + 32w .. +31 (key block w), against the query blocks
 // qa = 0..7 of chunk J and of the next chunk (the pairs with the largest
 // decay weights), summed over the head group.  Each step copies one query
-// block into LDS (double buffered): Q rows, transposed Q, the block-relative
-// dhat as fp16 rows (dP off the diagonal), bf16 hi/lo rows (dP on the
-// diagonal) and bf16 hi/lo transposed (dV, always bf16x3: dv feeds the gate
-// gradient, whose suffix sums accumulate the rounding of every token).  With
+// block into LDS (double buffered), as row tiles only: Q (fp16; read
+// transposed for dK), the block-relative dhat as fp16 (dP off the diagonal)
+// and as bf16 hi / lo (dP on the diagonal; read transposed for dV, which is
+// always bf16x3: dv feeds the gate gradient, whose suffix sums accumulate the
+// rounding of every token).  With
 // E(b) the log2 gate prefix at the end of block b, continued into the next
 // chunk, the decay of a pair in query block qa > w splits as
 //     exp2(Gl_i - E(qa-1)) * exp2(E(qa-1) - E(w)) * exp2(E(w) - Gl_j):
@@ -366,30 +367,22 @@ __global__ void __launch_bounds__(256, 1) k_bwd_intra_dkv(BwdArgs a) {
   using kfrag = typename IF::type;
   constexpr int NS = DK / 16, NSV = DV / 16, DKP = Pad32<DK>::value, DVP = Pad32<DV>::value;
   constexpr int NBK = DKP / 32, NBV = DVP / 32;
-  using QT = LdsTile<32, DK * 2>;   // Q rows of the step
-  using QTT = LdsTile<DKP, 64>;     // transposed Q (dk rows x 32 queries)
-  using QTTD = LdsTile<DK, 64>;
-  using XR = LdsTile<32, DV * 2>;   // block-relative dhat rows (fp16)
-  using XTT = LdsTile<DVP, 64>;     // the same transposed (bf16 hi, lo), rows padded to DVP
-  using XTTD = LdsTile<DV, 64>;
-  // One LDS object for every tile (see the forward kernel).
-  constexpr int O_Q = 0, O_QT = O_Q + 2 * QT::BYTES, O_X = O_QT + 2 * QTT::BYTES;
-  constexpr int O_TH = O_X + 2 * XR::BYTES, O_TL = O_TH + 2 * XTT::BYTES;
-  constexpr int O_M = O_TL + 2 * XTT::BYTES, O_E = O_M + 2 * 256, O_GW = O_E + 9 * DV * 4;
-  // Diagonal steps also stage the query block's dhat as bf16 hi / lo rows and
-  // the key block's V relative to the token before it (bf16 hi / lo rows).
-  constexpr int O_XH = O_GW + 4 * DV * 4, O_XL = O_XH + 2 * XR::BYTES, O_BH = O_XL + 2 * XR::BYTES;
-  constexpr int O_BL = O_BH + 2 * XR::BYTES;
-  __shared__ __align__(1024) char smem[O_BL + 2 * XR::BYTES];
+  // Row tiles of the step's 32 queries.  The products whose k index runs over
+  // the queries (dK, dV) read them with transposing LDS loads (tr_frag).
+  using QT = LdsTile<32, DK * 2>;   // Q rows (fp16)
+  using XR = LdsTile<32, DV * 2>;   // block-relative dhat rows: fp16, and bf16 hi / lo
+  // One LDS object for every tile (see the forward kernel).  Diagonal steps
+  // also stage the key block's V relative to the token before it (bf16 hi / lo).
+  constexpr int O_Q = 0, O_X = O_Q + 2 * QT::BYTES, O_XH = O_X + 2 * XR::BYTES, O_XL = O_XH + 2 * XR::BYTES;
+  constexpr int O_BH = O_XL + 2 * XR::BYTES, O_BL = O_BH + 2 * XR::BYTES;
+  constexpr int O_M = O_BL + 2 * XR::BYTES, O_E = O_M + 2 * 256, O_GW = O_E + 9 * DV * 4;
+  __shared__ __align__(1024) char smem[O_GW + 4 * DV * 4];
   auto XHs = [&](int b) { return smem + O_XH + b * XR::BYTES; };
   auto XLs = [&](int b) { return smem + O_XL + b * XR::BYTES; };
   auto BHs = [&](int b) { return smem + O_BH + b * XR::BYTES; };
   auto BLs = [&](int b) { return smem + O_BL + b * XR::BYTES; };
   auto Qs = [&](int b) { return smem + O_Q + b * QT::BYTES; };
-  auto Qts = [&](int b) { return smem + O_QT + b * QTT::BYTES; };
   auto Xs = [&](int b) { return smem + O_X + b * XR::BYTES; };
-  auto Ths = [&](int b) { return smem + O_TH + b * XTT::BYTES; };
-  auto Tls = [&](int b) { return smem + O_TL + b * XTT::BYTES; };
   auto Ms = [&](int b) { return (float *)(smem + O_M + b * 256); };  // 64 floats, 32 used
   float(*BE)[DV] = (float(*)[DV])(smem + O_E);  // BE[b + 1] = E(b), b = -1..7
   float *gw = (float *)(smem + O_GW) + (threadIdx.x >> 6) * DV;  // this wave's gamma of the step, per channel
@@ -412,37 +405,6 @@ __global__ void __launch_bounds__(256, 1) k_bwd_intra_dkv(BwdArgs a) {
   const int nqb = min(8, (L - c0 + 31) / 32);  // query blocks in this chunk and the next
   auto gl_at = [&](int tok, int d) { return a.Gl2[((st + tok) * Hkv + c) * DV + d]; };
 
-  for (int e = tid; e < 9 * DV; e += 256) {
-    const int b = e / DV - 1, d = e % DV;
-    float v = 0.f;
-    if (b >= 0 && b < 4) v = gl_at(min(c0 + 32 * b + 31, L - 1), d);
-    if (b >= 4) {
-      v = gl_at(min(c0 + CB - 1, L - 1), d);
-      if (c0 + CB < L) v += gl_at(min(c0 + CB + 32 * (b - 4) + 31, L - 1), d);
-    }
-    BE[b + 1][d] = v;
-  }
-  if (DK < DKP)
-    for (int e = tid; e < (DKP - DK) * 64 / 4; e += 256) {
-      ((uint32_t *)(Qts(0) + DK * 64))[e] = 0u;
-      ((uint32_t *)(Qts(1) + DK * 64))[e] = 0u;
-    }
-  if (DV < DVP)
-    for (int e = tid; e < (DVP - DV) * 64 / 4; e += 256) {
-      ((uint32_t *)(Ths(0) + DV * 64))[e] = 0u;
-      ((uint32_t *)(Ths(1) + DV * 64))[e] = 0u;
-      ((uint32_t *)(Tls(0) + DV * 64))[e] = 0u;
-      ((uint32_t *)(Tls(1) + DV * 64))[e] = 0u;
-    }
-  kfrag kf[NS];
-  f16x8 ve[NSV];  // the key's V to the end of its block, B operand of dP (k = channel)
-#pragma unroll
-  for (int i = 0; i < NS; ++i)
-    kf[i] = kv ? IF::load(a.k, ((st + key) * Hkv + c) * DK + 16 * i + 8 * hh) : IF::zero();
-#pragma unroll
-  for (int i = 0; i < NSV; ++i)
-    ve[i] = kv ? *(const f16x8 *)(a.VE + ((st + key) * Hkv + c) * DV + 16 * i + 8 * hh)
-               : __builtin_bit_cast(f16x8, make_uint4(0, 0, 0, 0));
   f32x16 accK[NBK], accV[NBV];
 #pragma unroll
   for (int b = 0; b < NBK; ++b) accK[b] = zero16();
@@ -457,54 +419,36 @@ __global__ void __launch_bounds__(256, 1) k_bwd_intra_dkv(BwdArgs a) {
   const int nsteps = G * nqo;
   // Rows past the end of the sequence read as zeros; their probabilities are
   // masked to zero when the step is computed.
-  uint32_t oq[QT::NW], oqt[QTTD::NW], ox[XR::NW], oxt[XTTD::NW], ob[XR::NW];
+  uint32_t oq[QT::NW], ox[XR::NW], ob[XR::NW];
   XR::lane_offsets(Hkv * DV * 2, wave, lane, ob);
   QT::lane_offsets(Hq * DK * 2, wave, lane, oq);
-  QTTD::lane_offsets(CB * 2, wave, lane, oqt);
   XR::lane_offsets(Hq * DV * 2, wave, lane, ox);
-  XTTD::lane_offsets(CB * 2, wave, lane, oxt);
   auto stage_tile = [&](int k, int buf) {
     const int gq = k / nqo, qa = k % nqo;
     const int h = c * G + gq;
     const int q0 = c0 + 32 * qa;
     const int64_t qr = (st + q0) * Hq + h;
     const int nrow = L - q0;
-    if constexpr (!F32IN) {
-      const u32x4 rq = rsrc_words((const uint16_t *)a.q + qr * DK, (int64_t)nrow * Hq * DK * 2);
+    const u32x4 rq = rsrc_words(a.Q16 + qr * DK, (int64_t)nrow * Hq * DK * 2);
 #pragma unroll
-      for (int t = 0; t < QT::NW; ++t) QT::dma_piece_untracked(Qs(buf), rq, oq, t, wave);
-    } else {
-      for (int p = tid; p < QT::NCH; p += 256) {
-        const int r = p / QT::CPR, cc = p % QT::CPR;
-        *(f16x8 *)(Qs(buf) + QT::off(r, cc)) = IF::load(a.q, ((st + min(q0 + r, L - 1)) * Hq + h) * DK + 8 * cc);
-      }
-    }
-    const int64_t ch = (int64_t)(gc + (qa >> 2)) * Hq + h;
-    const u32x4 rqt = rsrc_words(a.Qt + ch * DK * CB + 32 * (qa & 3), (int64_t)DK * CB * 2);
-#pragma unroll
-    for (int t = 0; t < QTTD::NW; ++t) QTTD::dma_piece_untracked(Qts(buf), rqt, oqt, t, wave);
+    for (int t = 0; t < QT::NW; ++t) QT::dma_piece_untracked(Qs(buf), rq, oq, t, wave);
     const u32x4 rx = rsrc_words(a.X16 + qr * DV, (int64_t)nrow * Hq * DV * 2);
+    const u32x4 rxh = rsrc_words(a.XH + qr * DV, (int64_t)nrow * Hq * DV * 2);
+    const u32x4 rxl = rsrc_words(a.XL + qr * DV, (int64_t)nrow * Hq * DV * 2);
 #pragma unroll
-    for (int t = 0; t < XR::NW; ++t) XR::dma_piece_untracked(Xs(buf), rx, ox, t, wave);
-    const u32x4 rth = rsrc_words(a.XTH + ch * DV * CB + 32 * (qa & 3), (int64_t)DV * CB * 2);
-    const u32x4 rtl = rsrc_words(a.XTL + ch * DV * CB + 32 * (qa & 3), (int64_t)DV * CB * 2);
-#pragma unroll
-    for (int t = 0; t < XTTD::NW; ++t) {
-      XTTD::dma_piece_untracked(Ths(buf), rth, oxt, t, wave);
-      XTTD::dma_piece_untracked(Tls(buf), rtl, oxt, t, wave);
+    for (int t = 0; t < XR::NW; ++t) {
+      XR::dma_piece_untracked(Xs(buf), rx, ox, t, wave);
+      XR::dma_piece_untracked(XHs(buf), rxh, ox, t, wave);
+      XR::dma_piece_untracked(XLs(buf), rxl, ox, t, wave);
     }
     // lane r fills Ms[r] (every wave, the same bytes)
     dma4_untracked(Ms(buf), rsrc_words(a.mb + qr, (int64_t)nrow * Hq * 4), (uint32_t)lane * Hq * 4);
-    if (qa < 4) {  // the diagonal block of wave qa
-      const u32x4 rxh = rsrc_words(a.XH + qr * DV, (int64_t)nrow * Hq * DV * 2);
-      const u32x4 rxl = rsrc_words(a.XL + qr * DV, (int64_t)nrow * Hq * DV * 2);
-      const int64_t kr = (st + q0) * Hkv + c;  // the key block is the query block
+    if (qa < 4) {  // the diagonal block of wave qa: its key block is the query block
+      const int64_t kr = (st + q0) * Hkv + c;
       const u32x4 rbh = rsrc_words(a.VBH + kr * DV, (int64_t)nrow * Hkv * DV * 2);
       const u32x4 rbl = rsrc_words(a.VBL + kr * DV, (int64_t)nrow * Hkv * DV * 2);
 #pragma unroll
       for (int t = 0; t < XR::NW; ++t) {
-        XR::dma_piece_untracked(XHs(buf), rxh, ox, t, wave);
-        XR::dma_piece_untracked(XLs(buf), rxl, ox, t, wave);
         XR::dma_piece_untracked(BHs(buf), rbh, ob, t, wave);
         XR::dma_piece_untracked(BLs(buf), rbl, ob, t, wave);
       }
@@ -524,10 +468,57 @@ __global__ void __launch_bounds__(256, 1) k_bwd_intra_dkv(BwdArgs a) {
     return __any(rng > BGUARD);
   };
 
+  // The prologue's loads and the first step's copies are all issued before
+  // one wait: the block-end gate values (E), then this wave's K and VE rows.
+  constexpr int NBE = (9 * DV + 255) / 256;
+  float be0[NBE], be1[NBE];
+#pragma unroll
+  for (int t = 0; t < NBE; ++t) {
+    const int e = tid + 256 * t, b = e / DV - 1, d = e % DV;
+    be0[t] = be1[t] = 0.f;
+    if (e < 9 * DV && b >= 0) {
+      if (b < 4) {
+        be0[t] = gl_at(min(c0 + 32 * b + 31, L - 1), d);
+      } else {
+        be0[t] = gl_at(min(c0 + CB - 1, L - 1), d);
+        if (c0 + CB < L) be1[t] = gl_at(min(c0 + CB + 32 * (b - 4) + 31, L - 1), d);
+      }
+    }
+  }
+  // The key as an fp16 operand: Q is staged as fp16 (as in k_bwd_dkv).
+  kfrag kr[NS];
+  f16x8 kf[NS], ve[NSV];  // ve: the key's V to the end of its block, B operand of dP (k = channel)
+#pragma unroll
+  for (int i = 0; i < NS; ++i)
+    kr[i] = kv ? IF::load(a.k, ((st + key) * Hkv + c) * DK + 16 * i + 8 * hh) : IF::zero();
+#pragma unroll
+  for (int i = 0; i < NSV; ++i)
+    ve[i] = kv ? *(const f16x8 *)(a.VE + ((st + key) * Hkv + c) * DV + 16 * i + 8 * hh)
+               : __builtin_bit_cast(f16x8, make_uint4(0, 0, 0, 0));
   if (nsteps > 0) stage_tile(0, 0);
   wait_all();
+#pragma unroll
+  for (int i = 0; i < NS; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) kf[i][e] = (_Float16)(float)kr[i][e];
+#pragma unroll
+  for (int t = 0; t < NBE; ++t) {
+    const int e = tid + 256 * t, b = e / DV - 1, d = e % DV;
+    if (e < 9 * DV) BE[b + 1][d] = be0[t] + be1[t];
+  }
   __syncthreads();
   const bool direct = exact_diag();
+  // The gate values of the wave's keys, for the dv epilogue: loaded during
+  // the last step (the step's own wait completes them).
+  float gl[NBV][16];
+  auto load_gl = [&]() {
+#pragma unroll
+    for (int bv = 0; bv < NBV; ++bv) {
+      const int col = min(32 * bv + n, DV - 1);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) gl[bv][j] = gl_at(min(kb + acc_row(hh, j), L - 1), col);
+    }
+  };
   for (int k = 0; k < nsteps; ++k) {
     const int buf = k & 1;
     const int qa = k % nqo;
@@ -538,6 +529,7 @@ __global__ void __launch_bounds__(256, 1) k_bwd_intra_dkv(BwdArgs a) {
     // the compiler's wait counts do not see, so the LDS reads below do not
     // wait for them, and they have the whole step to land.
     stage_tile(min(k + 1, nsteps - 1), buf ^ 1);
+    if (k == nsteps - 1) load_gl();
     float4 mq[4];
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) mq[q4] = *(const float4 *)&Ms(buf)[8 * q4 + 4 * hh];
@@ -567,7 +559,7 @@ __global__ void __launch_bounds__(256, 1) k_bwd_intra_dkv(BwdArgs a) {
       // S[q][key] and dP[q][key]: lane = key, register j = query acc_row(hh, j)
       f32x16 sc = zero16(), dp = zero16();
 #pragma unroll
-      for (int i = 0; i < NS; ++i) sc = mma32(*(const kfrag *)(Qs(buf) + QT::off(n, 2 * i + hh)), kf[i], sc);
+      for (int i = 0; i < NS; ++i) sc = mma32(*(const f16x8 *)(Qs(buf) + QT::off(n, 2 * i + hh)), kf[i], sc);
       if (diag) {
         // split at the token before the block: dhat and V as bf16 hi / lo (bf16x3)
 #pragma unroll
@@ -604,8 +596,8 @@ __global__ void __launch_bounds__(256, 1) k_bwd_intra_dkv(BwdArgs a) {
         f32x16 tmp = zero16();
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const bf16x8 th = *(const bf16x8 *)(Ths(buf) + XTT::off(32 * bv + n, 2 * u + hh));
-          const bf16x8 tl = *(const bf16x8 *)(Tls(buf) + XTT::off(32 * bv + n, 2 * u + hh));
+          const bf16x8 th = __builtin_bit_cast(bf16x8, tr_frag<XR>(XHs(buf), 16 * u, 32 * bv, lane));
+          const bf16x8 tl = __builtin_bit_cast(bf16x8, tr_frag<XR>(XLs(buf), 16 * u, 32 * bv, lane));
           tmp = mma32(ph[u], th, tmp);
           tmp = mma32(ph[u], tl, tmp);
           tmp = mma32(plo[u], th, tmp);
@@ -618,7 +610,7 @@ __global__ void __launch_bounds__(256, 1) k_bwd_intra_dkv(BwdArgs a) {
       for (int bk = 0; bk < NBK; ++bk)
 #pragma unroll
         for (int u = 0; u < 2; ++u)
-          accK[bk] = mma32(dsf[u], *(const f16x8 *)(Qts(buf) + QTT::off(32 * bk + n, 2 * u + hh)), accK[bk]);
+          accK[bk] = mma32(dsf[u], tr_frag<QT>(Qs(buf), 16 * u, 32 * bk, lane), accK[bk]);
     }
     wait_all();
     __syncthreads();
@@ -630,147 +622,104 @@ __global__ void __launch_bounds__(256, 1) k_bwd_intra_dkv(BwdArgs a) {
   // the token before the block, gamma = exp2(E(w-1) - E(w)) >= 1, V from the
   // token before the block as bf16x3.)
   bool dflag = false;  // exact diagonal contributions written to dv_i
-  {
-    float rng = 0.f, gd[NBV];
-#pragma unroll
-    for (int i = 0; i < NSV; ++i)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = 16 * i + 8 * hh + e;
-        rng = fmaxf(rng, BE[wave][d] - BE[wave + 1][d]);
-      }
-#pragma unroll
-    for (int bv = 0; bv < NBV; ++bv) {
-      const int d = min(32 * bv + n, DV - 1);
-      gd[bv] = fast_exp2(BE[wave][d] - BE[wave + 1][d]);
-    }
-    const bool direct = __any(rng > BGUARD);
-    // (the staged loop computed this block unless it needs the exact decays)
-    bf16x8 vh[NSV], vl[NSV];
-#pragma unroll
-    for (int i = 0; i < NSV; ++i) vh[i] = vl[i] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+  if (direct) {
     const int q0 = kb;
     const int qrow = min(q0 + n, L - 1);  // A-operand row of this lane
-    for (int gq = 0; direct && gq < G; ++gq) {
+    for (int gq = 0; gq < G; ++gq) {
       const int h = c * G + gq;
       f32x16 sc = zero16(), dp = zero16();
 #pragma unroll
       for (int i = 0; i < NS; ++i)
-        sc = mma32(IF::load(a.q, ((st + qrow) * Hq + h) * DK + 16 * i + 8 * hh), kf[i], sc);
+        sc = mma32(*(const f16x8 *)(a.Q16 + ((st + qrow) * Hq + h) * DK + 16 * i + 8 * hh), kf[i], sc);
       float p[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int r = acc_row(hh, j);
         p[j] = (q0 + r < L && r >= n) ? fast_exp2(sc[j] * sl2 - a.mb[(st + q0 + r) * Hq + h]) : 0.f;
       }
-      if (!direct) {
-        const int64_t xrw = ((st + qrow) * Hq + h) * DV;
-#pragma unroll
-        for (int i = 0; i < NSV; ++i) {
-          const bf16x8 xh = *(const bf16x8 *)(a.XH + xrw + 16 * i + 8 * hh);
-          const bf16x8 xl = *(const bf16x8 *)(a.XL + xrw + 16 * i + 8 * hh);
-          dp = mma32(xh, vh[i], dp);
-          dp = mma32(xl, vh[i], dp);
-          dp = mma32(xh, vl[i], dp);
-        }
-      } else {
+      {
         float t[16];
         direct_dp<DV, F32IN, false>(a.delta, a.sig, a.Gl2, a.v, Hq, Hkv, st, c, h, L, q0, kb, hh, n, t);
 #pragma unroll
         for (int j = 0; j < 16; ++j) dp[j] = t[j];
       }
       f16x8 dsf[2];
-      bf16x8 ph[2], plo[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          dsf[u][i] = (_Float16)(p[8 * u + i] * dp[8 * u + i]);
-          split_bf16(p[8 * u + i], ph[u], plo[u], i);
-        }
-      const int64_t qtb = ((int64_t)gc * Hq + h) * DK * CB + 32 * wave;
-      const int64_t xtb = ((int64_t)gc * Hq + h) * DV * CB + 32 * wave;
-      if (!direct) {
+        for (int i = 0; i < 8; ++i) dsf[u][i] = (_Float16)(p[8 * u + i] * dp[8 * u + i]);
+      // exact per-pair decays, written straight to the within-chunk partial
+      // (this wave owns these keys): P[q][kj] lives in lane kj, register of q
 #pragma unroll
-        for (int bv = 0; bv < NBV; ++bv) {
-          const int col = min(32 * bv + n, DV - 1);  // padded columns are never stored
-          f32x16 tmp = zero16();
+      for (int bv = 0; bv < NBV; ++bv) {
+        const int col = 32 * bv + n;
+        float t[16];
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const bf16x8 th = *(const bf16x8 *)(a.XTH + xtb + (int64_t)col * CB + 16 * u + 8 * hh);
-            const bf16x8 tl = *(const bf16x8 *)(a.XTL + xtb + (int64_t)col * CB + 16 * u + 8 * hh);
-            tmp = mma32(ph[u], th, tmp);
-            tmp = mma32(ph[u], tl, tmp);
-            tmp = mma32(plo[u], th, tmp);
-          }
-#pragma unroll
-          for (int j = 0; j < 16; ++j) accV[bv][j] += gd[bv] * tmp[j];
-        }
-      } else {
-        // exact per-pair decays, written straight to the within-chunk partial
-        // (this wave owns these keys): P[q][kj] lives in lane kj, register of q
-#pragma unroll
-        for (int bv = 0; bv < NBV; ++bv) {
-          const int col = 32 * bv + n;
-          float t[16];
-#pragma unroll
-          for (int j = 0; j < 16; ++j) t[j] = 0.f;
+        for (int j = 0; j < 16; ++j) t[j] = 0.f;
 #pragma unroll 1
-          for (int qq = 0; qq < 32; ++qq) {
-            const int qk = q0 + qq;
-            const int jsrc = (qq >> 3) * 4 + (qq & 3), hsrc = (qq >> 2) & 1;
-            float pj = 0.f;
+        for (int qq = 0; qq < 32; ++qq) {
+          const int qk = q0 + qq;
+          const int jsrc = (qq >> 3) * 4 + (qq & 3), hsrc = (qq >> 2) & 1;
+          float pj = 0.f;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) pj = (j == jsrc) ? p[j] : pj;
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-              const int kl = acc_row(hh, j);
-              const float pv = __shfl(pj, kl + 32 * hsrc);
-              const int kj = kb + kl;
-              if (col < DV && qk < L && kj <= qk)
-                t[j] += pv * fast_exp2(gl_at(qk, col) - gl_at(kj, col)) * a.delta[((st + qk) * Hq + h) * DV + col] *
-                        a.sig[(st + qk) * Hq + h];
-            }
-          }
+          for (int j = 0; j < 16; ++j) pj = (j == jsrc) ? p[j] : pj;
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
-            const int kj = kb + acc_row(hh, j);
-            if (col < DV && kj < L) {
-              const int64_t idx = ((st + kj) * Hkv + c) * DV + col;
-              a.dv_i[idx] = (dflag ? a.dv_i[idx] : 0.f) + t[j];
-            }
+            const int kl = acc_row(hh, j);
+            const float pv = __shfl(pj, kl + 32 * hsrc);
+            const int kj = kb + kl;
+            if (col < DV && qk < L && kj <= qk)
+              t[j] += pv * fast_exp2(gl_at(qk, col) - gl_at(kj, col)) * a.delta[((st + qk) * Hq + h) * DV + col] *
+                      a.sig[(st + qk) * Hq + h];
           }
         }
-        dflag = true;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int kj = kb + acc_row(hh, j);
+          if (col < DV && kj < L) {
+            const int64_t idx = ((st + kj) * Hkv + c) * DV + col;
+            a.dv_i[idx] = (dflag ? a.dv_i[idx] : 0.f) + t[j];
+          }
+        }
       }
+      dflag = true;
+      // dK[key][dk] += dS[q][key] Q[q][dk]: element i of lane (hh, n) of the
+      // B operand is Q[q0 + 16u + acc_row(hh, i)][32bk + n], the k order of dsf
 #pragma unroll
       for (int bk = 0; bk < NBK; ++bk) {
         const int col = min(32 * bk + n, DK - 1);
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-          accK[bk] = mma32(dsf[u], *(const f16x8 *)(a.Qt + qtb + (int64_t)col * CB + 16 * u + 8 * hh), accK[bk]);
+        for (int u = 0; u < 2; ++u) {
+          f16x8 qb;
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            qb[i] = a.Q16[((st + min(q0 + 16 * u + acc_row(hh, i), L - 1)) * Hq + h) * DK + col];
+          accK[bk] = mma32(dsf[u], qb, accK[bk]);
+        }
       }
     }
   }
-  // dv relative to the end of the key's block: exp2(E(w) - Gl_j).  Each
-  // block's inputs are loaded before any of its stores (the compiler cannot
-  // tell the buffers apart, so a load after a store would wait for it).
+  // dv relative to the end of the key's block: exp2(E(w) - Gl_j).  Every
+  // input of the epilogue is loaded before its first store (the compiler
+  // cannot tell the buffers apart, so a load after a store would wait for it).
+  if (nsteps == 0) load_gl();
+  float part[NBV][16];
+#pragma unroll
+  for (int bv = 0; bv < NBV; ++bv) {
+    const int col = min(32 * bv + n, DV - 1);
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      part[bv][j] = dflag ? a.dv_i[((st + min(kb + acc_row(hh, j), L - 1)) * Hkv + c) * DV + col] : 0.f;
+  }
 #pragma unroll
   for (int bv = 0; bv < NBV; ++bv) {
     const int col = 32 * bv + n;
     if (col >= DV) continue;
     const float ew = BE[wave + 1][col];
-    float gl[16], part[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int64_t idx = ((st + min(kb + acc_row(hh, j), L - 1)) * Hkv + c) * DV + col;
-      gl[j] = a.Gl2[idx];
-      part[j] = dflag ? a.dv_i[idx] : 0.f;
-    }
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int kj = kb + acc_row(hh, j);
-      if (kj < L) a.dv_i[((st + kj) * Hkv + c) * DV + col] = fast_exp2(ew - gl[j]) * accV[bv][j] + part[j];
+      if (kj < L) a.dv_i[((st + kj) * Hkv + c) * DV + col] = fast_exp2(ew - gl[bv][j]) * accV[bv][j] + part[bv][j];
     }
   }
   // dk after dv: the dv block loads then wait for no earlier stores

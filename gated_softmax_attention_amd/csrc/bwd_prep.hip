@@ -244,19 +244,15 @@ template <class T> __device__ inline void store8h(T *p, int64_t idx, const T (&v
 // One workgroup per 128-token chunk and kv head, each query head of the group
 // in turn.  A thread owns eight consecutive channels of a token row (16-byte
 // loads and stores; DV / 8 threads per row, row reductions by lane shuffles
-// inside that group).  The transposed tiles are built in LDS one 32-token
-// segment at a time and written out as 16-byte row pieces.  All of a thread's
-// rows of a segment are loaded before the first of them is computed.
+// inside that group).  Rows are taken 32 tokens at a time; all of a thread's
+// rows of such a segment are loaded before the first of them is computed.
 template <int DV>
 __global__ void __launch_bounds__(256) k_bwd_prep(PrepArgs a) {
   constexpr int TPR = DV / 8;        // threads per token row
   constexpr int RPP = 256 / TPR;     // rows per pass of the workgroup
-  constexpr int SEG = 32;            // tokens per tile segment
-  constexpr int STR = SEG + 8;       // LDS tile row stride (elements; rows 16-byte aligned)
+  constexpr int SEG = 32;            // tokens per segment
   constexpr int NR = SEG / RPP > 0 ? SEG / RPP : 1;  // rows of a segment per thread
-  constexpr int TILE = DV * STR * 2, RED = RPP * DV * 4;
-  __shared__ __align__(16) char smem[2 * TILE > RED ? 2 * TILE : RED];
-  __bf16 *tileh = (__bf16 *)smem, *tilel = (__bf16 *)(smem + TILE);
+  __shared__ __align__(16) char smem[RPP * DV * 4];
   const int gc = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
   if (gc >= a.plan.counts[0]) return;
   const Plan &pl = a.plan;
@@ -354,14 +350,7 @@ __global__ void __launch_bounds__(256) k_bwd_prep(PrepArgs a) {
             xh[i] = (__bf16)xb;
             xl[i] = (__bf16)(xb - (float)xh[i]);
           }
-          const bool valid = t < n;
-          const int pos = key_pos(r);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            tileh[(d0 + i) * STR + pos] = valid ? xh[i] : (__bf16)0.f;
-            tilel[(d0 + i) * STR + pos] = valid ? xl[i] : (__bf16)0.f;
-          }
-          if (valid) {
+          if (t < n) {
             if (o_norm)
 #pragma unroll
               for (int i = 0; i < 8; ++i) dwacc[i] += dn[i] * xv[k][i] * rs[k];
@@ -379,21 +368,11 @@ __global__ void __launch_bounds__(256) k_bwd_prep(PrepArgs a) {
           }
         }
       }
-      __syncthreads();
-      // the segment's tile rows: DV rows of SEG keys, 16-byte pieces
-      const int64_t tb = ((int64_t)gc * Hq + h) * DV * CB + SEG * hf;
-      for (int e = tid; e < DV * SEG / 8; e += 256) {
-        const int d = e / (SEG / 8), p8 = e % (SEG / 8);
-        const int64_t o = tb + (int64_t)d * CB + 8 * p8;
-        *(uint4 *)(a.XTH + o) = *(const uint4 *)&tileh[d * STR + 8 * p8];
-        *(uint4 *)(a.XTL + o) = *(const uint4 *)&tilel[d * STR + 8 * p8];
-      }
-      __syncthreads();
     }
   }
   if (a.dw_part) {
-    // per-block partials: the rows of the block's threads summed in LDS (the
-    // tile memory, free after the last barrier), then one row per block
+    // per-block partials: the rows of the block's threads summed in LDS,
+    // then one row per block
     float *red = (float *)smem;  // [RPP][DV]
 #pragma unroll
     for (int i = 0; i < 8; ++i) red[rr * DV + d0 + i] = dwacc[i];

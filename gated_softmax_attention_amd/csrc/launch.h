@@ -96,7 +96,7 @@ struct BwdArgs {
   const float *Gl2, *Gam;      // 128-chunk local prefix sums of g (log2 units), chunk decays
   const double *Lam;           // [chunk][Hkv][DV] prefix over chunks of the chunk log2 totals
   const _Float16 *Vr;          // [chunk][Hkv][CB][DV] V scaled to its chunk end
-  const _Float16 *Qt, *Kt;     // [chunk][H][D][CB] transposed fp16 tiles (key_pos order)
+  const _Float16 *Kt;          // [chunk][Hkv][DK][CB] transposed fp16 K tiles (key_pos order)
   const _Float16 *Q16;         // [T, Hq, DK] q as fp16 (exact for |q| in [2^-14, 65504])
   const float *delta;          // [T, Hq, DV] gradient reaching x
   const _Float16 *dh;          // [T, Hq, DV] sigma * exp(Gl) * delta
@@ -109,7 +109,6 @@ struct BwdArgs {
   const __bf16 *VBH, *VBL;     // [T, Hkv, DV] exp(Gl_blockstart-1 - Gl_j) v_j (>= |v_j|), bf16 hi / lo
   const _Float16 *X16;         // [T, Hq, DV] exp(Gl_i - Gl_blockstart-1) sigma delta_i
   const __bf16 *XH, *XL;       // the same, bf16 hi and lo parts
-  const __bf16 *XTH, *XTL;     // [chunk][Hq][DV][CB] transposed hi / lo tiles (key_pos order)
   float *dq_i, *dk_i, *dv_i;   // within-chunk contributions (fp32)
   void *dq, *dk, *dv;          // outputs (out dtype)
   float *dG;                   // [T, Hkv, DV] gradient with respect to the prefix sums of g
@@ -134,7 +133,6 @@ struct PrepArgs {
   float *dw_part;      // [chunks * Hkv][DV] per-block partial sums of dn (.) xh, or null
   _Float16 *X16;       // [Ttot, Hq, DV] sigma * exp(Gl - Gl at the token before the 32-block) * delta
   __bf16 *XH, *XL;     // the same as bf16 hi / lo parts
-  __bf16 *XTH, *XTL;   // [chunk][Hq][DV][CB] hi / lo transposed (key_pos order)
 };
 
 hipError_t launch_plan(const int64_t *cu, int nseq, int T, int64_t Ttot, const Plan &plan, hipStream_t st);

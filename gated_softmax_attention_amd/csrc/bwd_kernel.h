@@ -340,141 +340,232 @@ __global__ void __launch_bounds__(256, 1) k_bwd_intra_dq(BwdArgs a) {
   }
 }
 
+// The diagonal block of key block kb with exact per-pair decays (its gate
+// range beyond 2^BGUARD; rare), for one wave, from global memory, after the
+// wave has stored its dk rows: dK is added to the stored rows (the same
+// lanes wrote them), dV goes straight into the within-chunk partial.  A
+// function of its own so that the kernel's loops keep their registers.
+template <int DK, int DV, bool F32IN>
+__device__ __noinline__ void near_exact_diag(const float *delta, const float *sig, const float *Gl2, const void *v,
+                                             const void *kp, const _Float16 *Q16, const float *mb, float *dv_i,
+                                             float *dk_i, float scale, float sl2, int Hq, int Hkv, int G, int64_t st,
+                                             int c, int L, int kb) {
+  using IF = InFrag<F32IN>;
+  using kfrag = typename IF::type;
+  constexpr int NS = DK / 16, NBK = Pad32<DK>::value / 32, NBV = Pad32<DV>::value / 32;
+  const int lane = threadIdx.x & 63, hh = lane >> 5, n = lane & 31;
+  const int key = kb + n;
+  const bool kv = key < L;
+  auto gl_at = [&](int tok, int d) { return Gl2[((st + tok) * Hkv + c) * DV + d]; };
+  const int q0 = kb;
+  const int qrow = min(q0 + n, L - 1);  // A-operand row of this lane
+  for (int gq = 0; gq < G; ++gq) {
+    const int h = c * G + gq;
+    float dpe[16];
+    direct_dp<DV, F32IN, false>(delta, sig, Gl2, v, Hq, Hkv, st, c, h, L, q0, kb, hh, n, dpe);
+    f32x16 sc = zero16();
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const kfrag k8 = kv ? IF::load(kp, ((st + key) * Hkv + c) * DK + 16 * i + 8 * hh) : IF::zero();
+      f16x8 kf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kf[e] = (_Float16)(float)k8[e];
+      sc = mma32(*(const f16x8 *)(Q16 + ((st + qrow) * Hq + h) * DK + 16 * i + 8 * hh), kf, sc);
+    }
+    float pe[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int r = acc_row(hh, j);
+      pe[j] = (q0 + r < L && r >= n) ? fast_exp2(sc[j] * sl2 - mb[(st + q0 + r) * Hq + h]) : 0.f;
+    }
+    f16x8 dsf[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dsf[u][i] = (_Float16)(pe[8 * u + i] * dpe[8 * u + i]);
+    // exact per-pair decays: P[q][kj] lives in lane kj, register of q
+#pragma unroll 1
+    for (int bv = 0; bv < NBV; ++bv) {
+      const int col = 32 * bv + n;
+      float t[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) t[j] = 0.f;
+#pragma unroll 1
+      for (int qq = 0; qq < 32; ++qq) {
+        const int qk = q0 + qq;
+        const int jsrc = (qq >> 3) * 4 + (qq & 3), hsrc = (qq >> 2) & 1;
+        float pj = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) pj = (j == jsrc) ? pe[j] : pj;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int kl = acc_row(hh, j);
+          const float pvv = __shfl(pj, kl + 32 * hsrc);
+          const int kj = kb + kl;
+          if (col < DV && qk < L && kj <= qk)
+            t[j] += pvv * fast_exp2(gl_at(qk, col) - gl_at(kj, col)) * delta[((st + qk) * Hq + h) * DV + col] *
+                    sig[(st + qk) * Hq + h];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int kj = kb + acc_row(hh, j);
+        if (col < DV && kj < L) {
+          const int64_t idx = ((st + kj) * Hkv + c) * DV + col;
+          dv_i[idx] = (gq > 0 ? dv_i[idx] : 0.f) + t[j];
+        }
+      }
+    }
+    // dK[key][dk] += dS[q][key] Q[q][dk]: element i of lane (hh, n) of the
+    // B operand is Q[q0 + 16u + acc_row(hh, i)][32bk + n], the k order of dsf
+#pragma unroll 1
+    for (int bk = 0; bk < NBK; ++bk) {
+      const int col = min(32 * bk + n, DK - 1);
+      f32x16 dacc = zero16();
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        f16x8 qb;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          qb[i] = Q16[((st + min(q0 + 16 * u + acc_row(hh, i), L - 1)) * Hq + h) * DK + col];
+        dacc = mma32(dsf[u], qb, dacc);
+      }
+      if (32 * bk + n < DK)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int kj = kb + acc_row(hh, j);
+          if (kj < L) dk_i[((st + kj) * Hkv + c) * DK + col] += scale * dacc[j];
+        }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Near contributions to dk, dv: workgroup = one 128-chunk J of one kv head;
-// wave w owns keys c0 + 32w .. +31 (key block w), against the query blocks
-// qa = 0..7 of chunk J and of the next chunk (the pairs with the largest
-// decay weights), summed over the head group.  Each step copies one query
-// block into LDS (double buffered), as row tiles only: Q (fp16; read
-// transposed for dK), the block-relative dhat as fp16 (dP off the diagonal)
-// and as bf16 hi / lo (dP on the diagonal; read transposed for dV, which is
-// always bf16x3: dv feeds the gate gradient, whose suffix sums accumulate the
-// rounding of every token).  With
-// E(b) the log2 gate prefix at the end of block b, continued into the next
-// chunk, the decay of a pair in query block qa > w splits as
-//     exp2(Gl_i - E(qa-1)) * exp2(E(qa-1) - E(w)) * exp2(E(w) - Gl_j):
+// key block p (keys c0 + 32p .. +31) is shared by wave p (A) and wave p + 4
+// (B), which the hardware places on the same SIMD.  Steps run over the query
+// blocks qa = 0..7 of chunk J and of the next chunk (the pairs with the
+// largest decay weights), each head of the group in turn.  Each step copies
+// one query block into LDS as row tiles: Q (fp16, three stages: B reads it
+// one step late, transposed, for dK), the block-relative dhat as fp16 (dP off
+// the diagonal) and as bf16 hi / lo (dP on the diagonal; read transposed for
+// dV, which is always bf16x3: dv feeds the gate gradient, whose suffix sums
+// accumulate the rounding of every token).  With E(b) the log2 gate prefix
+// at the end of block b, continued into the next chunk, the decay of a pair
+// in query block qa > p splits as
+//     exp2(Gl_i - E(qa-1)) * exp2(E(qa-1) - E(p)) * exp2(E(p) - Gl_j):
 // the first factor is in the staged dhat, the middle one gamma multiplies
-// the wave's V-to-block-end operand (dP) and each dV step's result per
+// B's V-to-block-end operand (dP) and each of A's dV step results per
 // channel, and the last one scales dV in the epilogue.  The diagonal block
-// (the step whose query block is the wave's own) uses gamma =
-// exp2(E(w-1) - E(w)) >= 1 and V from the token before the block, as in the
-// dq kernel, from tiles staged with that step; past 2^BGUARD its pairs are
-// evaluated directly after the loop.
+// (the step whose query block is the pair's own) uses gamma =
+// exp2(E(p-1) - E(p)) >= 1 and V from the token before the block (bf16x3,
+// tiles staged with that step); past 2^BGUARD its pairs are evaluated
+// directly after the loop.
+//   A, step k: S_k = Q K^T, P_k = exp2(S sl2 - m) (fp32 into LDS), dV +=
+//              gamma (.) (P_k^T dhat_k); the copies of step k+1's Q and fp16
+//              dhat rows and row offsets.
+//   B, step k: dS_{k-1} = P_{k-1} (LDS) (.) the dP_{k-1} it kept, dK +=
+//              dS_{k-1}^T Q_{k-1}; dP_k = dhat_k (V (.) gamma)^T; the copies
+//              of step k+1's bf16 hi / lo rows.
+// One barrier per step; every wave waits for its own copies before it.
 // ---------------------------------------------------------------------------
 template <int DK, int DV, bool F32IN>
-__global__ void __launch_bounds__(256, 1) k_bwd_intra_dkv(BwdArgs a) {
+__global__ void __launch_bounds__(512, 1) k_bwd_intra_dkv(BwdArgs a) {
   using IF = InFrag<F32IN>;
   using kfrag = typename IF::type;
   constexpr int NS = DK / 16, NSV = DV / 16, DKP = Pad32<DK>::value, DVP = Pad32<DV>::value;
   constexpr int NBK = DKP / 32, NBV = DVP / 32;
-  // Row tiles of the step's 32 queries.  The products whose k index runs over
-  // the queries (dK, dV) read them with transposing LDS loads (tr_frag).
-  using QT = LdsTile<32, DK * 2>;   // Q rows (fp16)
-  using XR = LdsTile<32, DV * 2>;   // block-relative dhat rows: fp16, and bf16 hi / lo
-  // One LDS object for every tile (see the forward kernel).  Diagonal steps
-  // also stage the key block's V relative to the token before it (bf16 hi / lo).
-  constexpr int O_Q = 0, O_X = O_Q + 2 * QT::BYTES, O_XH = O_X + 2 * XR::BYTES, O_XL = O_XH + 2 * XR::BYTES;
-  constexpr int O_BH = O_XL + 2 * XR::BYTES, O_BL = O_BH + 2 * XR::BYTES;
-  constexpr int O_M = O_BL + 2 * XR::BYTES, O_E = O_M + 2 * 256, O_GW = O_E + 9 * DV * 4;
+  using QT = LdsTile<32, DK * 2>;  // Q rows (fp16)
+  using XR = LdsTile<32, DV * 2>;  // block-relative dhat rows (fp16, bf16 hi, bf16 lo); V rows of the diagonal
+  constexpr int PX = 4 * 64 * 16;  // one pair's P of a step: [j / 4][lane] float4
+  // One LDS object for every tile (see the forward kernel).
+  constexpr int O_Q = 0, O_X = O_Q + 3 * QT::BYTES, O_XH = O_X + 2 * XR::BYTES, O_XL = O_XH + 2 * XR::BYTES;
+  constexpr int O_BH = O_XL + 2 * XR::BYTES, O_BL = O_BH + 2 * XR::BYTES, O_P = O_BL + 2 * XR::BYTES;
+  constexpr int O_M = O_P + 2 * 4 * PX, O_E = O_M + 2 * 256, O_GW = O_E + 9 * DV * 4;
   __shared__ __align__(1024) char smem[O_GW + 4 * DV * 4];
+  auto Qs = [&](int b) { return smem + O_Q + b * QT::BYTES; };
+  auto Xs = [&](int b) { return smem + O_X + b * XR::BYTES; };
   auto XHs = [&](int b) { return smem + O_XH + b * XR::BYTES; };
   auto XLs = [&](int b) { return smem + O_XL + b * XR::BYTES; };
   auto BHs = [&](int b) { return smem + O_BH + b * XR::BYTES; };
   auto BLs = [&](int b) { return smem + O_BL + b * XR::BYTES; };
-  auto Qs = [&](int b) { return smem + O_Q + b * QT::BYTES; };
-  auto Xs = [&](int b) { return smem + O_X + b * XR::BYTES; };
   auto Ms = [&](int b) { return (float *)(smem + O_M + b * 256); };  // 64 floats, 32 used
   float(*BE)[DV] = (float(*)[DV])(smem + O_E);  // BE[b + 1] = E(b), b = -1..7
-  float *gw = (float *)(smem + O_GW) + (threadIdx.x >> 6) * DV;  // this wave's gamma of the step, per channel
 
   const Plan &pl = a.plan;
   const int gc = blockIdx.x, c = blockIdx.y;
   if (gc >= pl.counts[0]) return;
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, n = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool isA = wave < 4;
+  const int p = wave & 3;
+  float *gw = (float *)(smem + O_GW) + p * DV;  // B's gamma of the step, per channel
   const int s = seq_of_chunk(pl.cb128, pl.nseq, gc);
   const int c0 = uniform((gc - pl.cb128[s]) * CB);
   const int L = uniform(pl.seq_len[s]);
   const int64_t st = uniform((int64_t)pl.seq_start[s]);
   const int Hq = a.Hq, Hkv = a.Hkv, G = Hq / Hkv;
-  const int kb = c0 + 32 * wave;
+  const int kb = c0 + 32 * p;
   const bool active = kb < L;
   const int key = kb + n;
   const bool kv = key < L;
   const float sl2 = a.sl2;
-  const int nqb = min(8, (L - c0 + 31) / 32);  // query blocks in this chunk and the next
+  const int nqo = min(8, (L - c0 + 31) / 32);  // query blocks in this chunk and the next
+  const int nsteps = G * nqo;
+  // Step k: query block nqo - 1 - k / G (the farthest first), head k % G.
+  auto qa_of = [&](int k) { return nqo - 1 - k / G; };
   auto gl_at = [&](int tok, int d) { return a.Gl2[((st + tok) * Hkv + c) * DV + d]; };
 
-  f32x16 accK[NBK], accV[NBV];
-#pragma unroll
-  for (int b = 0; b < NBK; ++b) accK[b] = zero16();
-#pragma unroll
-  for (int b = 0; b < NBV; ++b) accV[b] = zero16();
-
-  // Query blocks qa = 0 .. nqb - 1 of every head through LDS.  Wave w takes
-  // the blocks after its own (qa > w) and, at qa = w, its diagonal block,
-  // unless the block's gate range needs exact per-pair decays (then that
-  // block is done afterwards, from global memory).
-  const int nqo = nqb;
-  const int nsteps = G * nqo;
-  // Rows past the end of the sequence read as zeros; their probabilities are
-  // masked to zero when the step is computed.
+  // Copies.  Rows past the end of the sequence read as zeros; their
+  // probabilities are masked to zero when the step is computed.
   uint32_t oq[QT::NW], ox[XR::NW], ob[XR::NW];
-  XR::lane_offsets(Hkv * DV * 2, wave, lane, ob);
-  QT::lane_offsets(Hq * DK * 2, wave, lane, oq);
-  XR::lane_offsets(Hq * DV * 2, wave, lane, ox);
-  auto stage_tile = [&](int k, int buf) {
-    const int gq = k / nqo, qa = k % nqo;
-    const int h = c * G + gq;
-    const int q0 = c0 + 32 * qa;
+  QT::lane_offsets(Hq * DK * 2, p, lane, oq);
+  XR::lane_offsets(Hq * DV * 2, p, lane, ox);
+  XR::lane_offsets(Hkv * DV * 2, p, lane, ob);
+  auto stage_tile = [&](int k) {
+    const int gq = k % G, qa = qa_of(k);
+    const int h = c * G + gq, q0 = c0 + 32 * qa;
     const int64_t qr = (st + q0) * Hq + h;
     const int nrow = L - q0;
-    const u32x4 rq = rsrc_words(a.Q16 + qr * DK, (int64_t)nrow * Hq * DK * 2);
+    if (isA) {
+      const u32x4 rq = rsrc_words(a.Q16 + qr * DK, (int64_t)nrow * Hq * DK * 2);
+      const u32x4 rx = rsrc_words(a.X16 + qr * DV, (int64_t)nrow * Hq * DV * 2);
 #pragma unroll
-    for (int t = 0; t < QT::NW; ++t) QT::dma_piece_untracked(Qs(buf), rq, oq, t, wave);
-    const u32x4 rx = rsrc_words(a.X16 + qr * DV, (int64_t)nrow * Hq * DV * 2);
-    const u32x4 rxh = rsrc_words(a.XH + qr * DV, (int64_t)nrow * Hq * DV * 2);
-    const u32x4 rxl = rsrc_words(a.XL + qr * DV, (int64_t)nrow * Hq * DV * 2);
+      for (int t = 0; t < QT::NW; ++t) QT::dma_piece_untracked(Qs(k % 3), rq, oq, t, p);
 #pragma unroll
-    for (int t = 0; t < XR::NW; ++t) {
-      XR::dma_piece_untracked(Xs(buf), rx, ox, t, wave);
-      XR::dma_piece_untracked(XHs(buf), rxh, ox, t, wave);
-      XR::dma_piece_untracked(XLs(buf), rxl, ox, t, wave);
-    }
-    // lane r fills Ms[r] (every wave, the same bytes)
-    dma4_untracked(Ms(buf), rsrc_words(a.mb + qr, (int64_t)nrow * Hq * 4), (uint32_t)lane * Hq * 4);
-    if (qa < 4) {  // the diagonal block of wave qa: its key block is the query block
-      const int64_t kr = (st + q0) * Hkv + c;
-      const u32x4 rbh = rsrc_words(a.VBH + kr * DV, (int64_t)nrow * Hkv * DV * 2);
-      const u32x4 rbl = rsrc_words(a.VBL + kr * DV, (int64_t)nrow * Hkv * DV * 2);
+      for (int t = 0; t < XR::NW; ++t) XR::dma_piece_untracked(Xs(k & 1), rx, ox, t, p);
+      // lane r fills Ms[r] (every A wave, the same bytes)
+      dma4_untracked(Ms(k & 1), rsrc_words(a.mb + qr, (int64_t)nrow * Hq * 4), (uint32_t)lane * Hq * 4);
+    } else {
+      const u32x4 rxh = rsrc_words(a.XH + qr * DV, (int64_t)nrow * Hq * DV * 2);
+      const u32x4 rxl = rsrc_words(a.XL + qr * DV, (int64_t)nrow * Hq * DV * 2);
 #pragma unroll
       for (int t = 0; t < XR::NW; ++t) {
-        XR::dma_piece_untracked(BHs(buf), rbh, ob, t, wave);
-        XR::dma_piece_untracked(BLs(buf), rbl, ob, t, wave);
+        XR::dma_piece_untracked(XHs(k & 1), rxh, ox, t, p);
+        XR::dma_piece_untracked(XLs(k & 1), rxl, ox, t, p);
+      }
+      if (qa < 4) {  // the diagonal block of pair qa: its key block is the query block
+        const int64_t kr = (st + q0) * Hkv + c;
+        const u32x4 rbh = rsrc_words(a.VBH + kr * DV, (int64_t)nrow * Hkv * DV * 2);
+        const u32x4 rbl = rsrc_words(a.VBL + kr * DV, (int64_t)nrow * Hkv * DV * 2);
+#pragma unroll
+        for (int t = 0; t < XR::NW; ++t) {
+          XR::dma_piece_untracked(BHs(k & 1), rbh, ob, t, p);
+          XR::dma_piece_untracked(BLs(k & 1), rbl, ob, t, p);
+        }
       }
     }
   };
-  // Whether this wave's diagonal block needs exact per-pair decays (gate
-  // range of the block beyond 2^BGUARD; BE is complete after the barrier below).
-  auto exact_diag = [&]() {
-    float rng = 0.f;
-#pragma unroll
-    for (int i = 0; i < NSV; ++i)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = 16 * i + 8 * hh + e;
-        rng = fmaxf(rng, BE[wave][d] - BE[wave + 1][d]);
-      }
-    return __any(rng > BGUARD);
-  };
 
-  // The prologue's loads and the first step's copies are all issued before
-  // one wait: the block-end gate values (E), then this wave's K and VE rows.
-  constexpr int NBE = (9 * DV + 255) / 256;
+  // Prologue: the block-end gate values (E), the key-side operand of the
+  // wave's role (A: K as fp16, exact for |k| in [2^-14, 65504], since Q is
+  // staged as fp16; B: V to the end of its block) and the first step's
+  // copies, all issued before one wait.
+  constexpr int NBE = (9 * DV + 511) / 512;
   float be0[NBE], be1[NBE];
 #pragma unroll
   for (int t = 0; t < NBE; ++t) {
-    const int e = tid + 256 * t, b = e / DV - 1, d = e % DV;
+    const int e = tid + 512 * t, b = e / DV - 1, d = e % DV;
     be0[t] = be1[t] = 0.f;
     if (e < 9 * DV && b >= 0) {
       if (b < 4) {
@@ -485,252 +576,313 @@ __global__ void __launch_bounds__(256, 1) k_bwd_intra_dkv(BwdArgs a) {
       }
     }
   }
-  // The key as an fp16 operand: Q is staged as fp16 (as in k_bwd_dkv).
+  constexpr int NKS = NS > NSV ? NS : NSV;
+  const f16x8 zf = __builtin_bit_cast(f16x8, make_uint4(0, 0, 0, 0));
   kfrag kr[NS];
-  f16x8 kf[NS], ve[NSV];  // ve: the key's V to the end of its block, B operand of dP (k = channel)
+  f16x8 kop[NKS];  // A: K (fp16); B: V to the end of its block
 #pragma unroll
-  for (int i = 0; i < NS; ++i)
-    kr[i] = kv ? IF::load(a.k, ((st + key) * Hkv + c) * DK + 16 * i + 8 * hh) : IF::zero();
+  for (int i = 0; i < NKS; ++i) kop[i] = zf;
+  if (isA) {
 #pragma unroll
-  for (int i = 0; i < NSV; ++i)
-    ve[i] = kv ? *(const f16x8 *)(a.VE + ((st + key) * Hkv + c) * DV + 16 * i + 8 * hh)
-               : __builtin_bit_cast(f16x8, make_uint4(0, 0, 0, 0));
-  if (nsteps > 0) stage_tile(0, 0);
+    for (int i = 0; i < NS; ++i)
+      kr[i] = kv ? IF::load(a.k, ((st + key) * Hkv + c) * DK + 16 * i + 8 * hh) : IF::zero();
+  } else if (kv) {
+#pragma unroll
+    for (int i = 0; i < NSV; ++i) kop[i] = *(const f16x8 *)(a.VE + ((st + key) * Hkv + c) * DV + 16 * i + 8 * hh);
+  }
+  if (nsteps > 0) stage_tile(0);
   wait_all();
+  if (isA)
 #pragma unroll
-  for (int i = 0; i < NS; ++i)
+    for (int i = 0; i < NS; ++i)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) kf[i][e] = (_Float16)(float)kr[i][e];
+      for (int e = 0; e < 8; ++e) kop[i][e] = (_Float16)(float)kr[i][e];
 #pragma unroll
   for (int t = 0; t < NBE; ++t) {
-    const int e = tid + 256 * t, b = e / DV - 1, d = e % DV;
+    const int e = tid + 512 * t, b = e / DV - 1, d = e % DV;
     if (e < 9 * DV) BE[b + 1][d] = be0[t] + be1[t];
   }
   __syncthreads();
-  const bool direct = exact_diag();
-  // The gate values of the wave's keys, for the dv epilogue: loaded during
-  // the last step (the step's own wait completes them).
-  float gl[NBV][16];
-  auto load_gl = [&]() {
+  // Whether a key block's diagonal needs exact per-pair decays (its gate
+  // range beyond 2^BGUARD): this pair's, and whether any pair's does.
+  bool direct = false, direct_any = false;
+#pragma unroll 1
+  for (int pb = 0; pb < 4; ++pb) {
+    float rng = 0.f;
+#pragma unroll
+    for (int i = 0; i < NSV; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int d = 16 * i + 8 * hh + e;
+        rng = fmaxf(rng, BE[pb][d] - BE[pb + 1][d]);
+      }
+    const bool x = __any(rng > BGUARD);
+    direct_any |= x;
+    if (pb == p) direct = x;
+  }
+  auto act_of = [&](int qa) { return active && (qa > p || (qa == p && !direct)); };
+  const uint32_t sbase = lds_addr(smem);
+  const uint32_t apx = sbase + O_P + p * PX + 16 * lane;  // this lane's P exchange slot
+  constexpr uint32_t RQ = 2 * DK, RX = 2 * DV;  // row bytes of the Q and dhat tiles
+
+  f32x16 acc[NBK > NBV ? NBK : NBV];  // A: dV (relative to gamma of the current query block); B: dK
+#pragma unroll
+  for (int b = 0; b < (NBK > NBV ? NBK : NBV); ++b) acc[b] = zero16();
+  // A: the query block whose gamma acc is relative to (its last one, after
+  // the loop); dv then carries exp2(E(qlast - 1) - Gl_j) per key and channel
+  int qlast = p + 1;
+  if (isA) {
+    // per-lane LDS addresses in stage 0: Q row fragments (S) and the two
+    // transposing-read pieces of the dhat hi rows per output block (dV)
+    uint32_t aq[NS], adv[NBV][2];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) aq[i] = sbase + O_Q + QT::off(n, min(2 * i + hh, QT::CPR - 1));
 #pragma unroll
     for (int bv = 0; bv < NBV; ++bv) {
-      const int col = min(32 * bv + n, DV - 1);
-#pragma unroll
-      for (int j = 0; j < 16; ++j) gl[bv][j] = gl_at(min(kb + acc_row(hh, j), L - 1), col);
+      uint32_t o[2];
+      tr_offsets<XR>(32 * bv, lane, o);
+      adv[bv][0] = sbase + O_XH + o[0];
+      adv[bv][1] = sbase + O_XH + o[1];
     }
-  };
-  for (int k = 0; k < nsteps; ++k) {
-    const int buf = k & 1;
-    const int qa = k % nqo;
-    const int q0 = c0 + 32 * qa;
-    const bool diag = qa == wave;
-    const bool act = active && (qa > wave || (diag && !direct));
-    // The next step's copies first: they are issued from inline assembly that
-    // the compiler's wait counts do not see, so the LDS reads below do not
-    // wait for them, and they have the whole step to land.
-    stage_tile(min(k + 1, nsteps - 1), buf ^ 1);
-    if (k == nsteps - 1) load_gl();
-    float4 mq[4];
+    const uint32_t apx_ = opaque(apx);
+    int qcur = -1;
+    for (int k = 0; k < nsteps; ++k) {
+      const int qa = qa_of(k);
+      const bool diag = qa == p;
+      wait_all();
+      __syncthreads();  // step k's tiles landed; step k - 1's readers are done
+      if (k + 1 < nsteps) stage_tile(k + 1);
+      if (!act_of(qa)) continue;
+      const int q0 = c0 + 32 * qa;
+      f32x4 mq[4];
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) mq[q4] = *(const float4 *)&Ms(buf)[8 * q4 + 4 * hh];
-    float gcol[NBV];  // gamma of the lane's dV output columns
-    f16x8 kop[NSV];   // V to block end (.) gamma, B operand of dP
-    if (act) {
-      // gamma[d] = exp2(E(qa - 1) - E(wave)) depends on the channel only: each
-      // lane evaluates two channels into the wave's table, then every lane
-      // reads the channels it needs (a wave's LDS accesses complete in order).
+      for (int q4 = 0; q4 < 4; ++q4)
+        mq[q4] = *(const __attribute__((address_space(3))) f32x4 *)lds_at(sbase + O_M + (k & 1) * 256 + 4 * (8 * q4 + 4 * hh));
+      // S[q][key]: lane = key, register j = query acc_row(hh, j)
+      f32x16 sc = zero16();
+      {
+        const uint32_t so = (k % 3) * QT::BYTES;
+        f16x8 fq[NS];
 #pragma unroll
-      for (int t = 0; t < (DV + 63) / 64; ++t) {
-        const int d = lane + 64 * t;
-        if (d < DV) gw[d] = fast_exp2(BE[qa][d] - BE[wave + 1][d]);
+        for (int i = 0; i < NS; ++i) fq[i] = lds_row16(opaque(aq[i]) + so);
+#pragma unroll
+        for (int i = 0; i < NS; ++i) sc = mma32(fq[i], kop[i], sc);
+      }
+      // entering a nearer query block: dV so far times gamma_old / gamma_new
+      // = exp2(E(qcur - 1) - E(qa - 1)) <= 1 (query blocks are visited last first)
+      if (qa != qcur) {
+        if (qcur >= 0)
+#pragma unroll
+          for (int bv = 0; bv < NBV; ++bv) {
+            const int d = min(32 * bv + n, DV - 1);
+            const float r = fast_exp2(BE[qcur][d] - BE[qa][d]);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) acc[bv][j] *= r;
+          }
+        qcur = qa;
+      }
+      float pv[16];
+      bf16x8 ph[2], plo[2];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int r = acc_row(hh, j);
+        pv[j] = q0 + r < L && (!diag || r >= n) ? fast_exp2(sc[j] * sl2 - mq[j >> 2][j & 3]) : 0.f;
+        split_bf16(pv[j], ph[j >> 3], plo[j >> 3], j & 7);
       }
 #pragma unroll
-      for (int bv = 0; bv < NBV; ++bv) gcol[bv] = gw[min(32 * bv + n, DV - 1)];
-      if (!diag)
+      for (int j4 = 0; j4 < 4; ++j4)
+        *(__attribute__((address_space(3))) f32x4 *)lds_at(apx_ + (k & 1) * 4 * PX + 1024 * j4) =
+            f32x4{pv[4 * j4], pv[4 * j4 + 1], pv[4 * j4 + 2], pv[4 * j4 + 3]};
+      // dV[key][d] += sum_q P[q][key] dhat[q][d] (bf16x3), output blocks
+      // interleaved; the transposing reads of a k slice run one slice ahead
+      {
+        const uint32_t so = (k & 1) * XR::BYTES;
+        f16x4 th[2][NBV][2], tl[2][NBV][2];
+        auto rd = [&](int u, int s2) {
 #pragma unroll
-        for (int i = 0; i < NSV; ++i) {
-          const float4 g0 = *(const float4 *)(gw + 16 * i + 8 * hh), g1 = *(const float4 *)(gw + 16 * i + 8 * hh + 4);
-          const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+          for (int bv = 0; bv < NBV; ++bv)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) kop[i][e] = (_Float16)((float)ve[i][e] * gv[e]);
+            for (int t = 0; t < 2; ++t) {
+              th[s2][bv][t] = lds_tr8(opaque(adv[bv][t]) + so + 16 * u * RX);
+              tl[s2][bv][t] = lds_tr8(opaque(adv[bv][t]) + so + 16 * u * RX + 2 * XR::BYTES);
+            }
+        };
+        rd(0, 0);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          if (u == 0) rd(1, 1);
+#pragma unroll
+          for (int bv = 0; bv < NBV; ++bv) {
+            const bf16x8 h8 = __builtin_bit_cast(bf16x8, __builtin_shufflevector(th[u][bv][0], th[u][bv][1], 0, 1, 2, 3, 4, 5, 6, 7));
+            acc[bv] = mma32(ph[u], h8, acc[bv]);
+          }
+#pragma unroll
+          for (int bv = 0; bv < NBV; ++bv) {
+            const bf16x8 l8 = __builtin_bit_cast(bf16x8, __builtin_shufflevector(tl[u][bv][0], tl[u][bv][1], 0, 1, 2, 3, 4, 5, 6, 7));
+            acc[bv] = mma32(ph[u], l8, acc[bv]);
+          }
+#pragma unroll
+          for (int bv = 0; bv < NBV; ++bv) {
+            const bf16x8 h8 = __builtin_bit_cast(bf16x8, __builtin_shufflevector(th[u][bv][0], th[u][bv][1], 0, 1, 2, 3, 4, 5, 6, 7));
+            acc[bv] = mma32(plo[u], h8, acc[bv]);
+          }
         }
+      }
     }
-    if (act) {
-      // S[q][key] and dP[q][key]: lane = key, register j = query acc_row(hh, j)
-      f32x16 sc = zero16(), dp = zero16();
+    wait_all();
+    __syncthreads();  // the barrier B's last dK step waits at
+    if (qcur >= 0) qlast = qcur;
+  } else {
+    // per-lane LDS addresses in stage 0: dhat row fragments (dP; the other
+    // row tiles lie at fixed distances) and the two transposing-read pieces
+    // of the Q rows per output block (dK)
+    uint32_t ax[NSV], aqt[NBK][2];
 #pragma unroll
-      for (int i = 0; i < NS; ++i) sc = mma32(*(const f16x8 *)(Qs(buf) + QT::off(n, 2 * i + hh)), kf[i], sc);
+    for (int i = 0; i < NSV; ++i) ax[i] = sbase + O_X + XR::off(n, min(2 * i + hh, XR::CPR - 1));
+#pragma unroll
+    for (int bk = 0; bk < NBK; ++bk) {
+      uint32_t o[2];
+      tr_offsets<QT>(32 * bk, lane, o);
+      aqt[bk][0] = sbase + O_Q + o[0];
+      aqt[bk][1] = sbase + O_Q + o[1];
+    }
+    const uint32_t apx_ = opaque(apx);
+    f32x16 dpk = zero16();  // dP of the previous step
+    f16x8 kg[NSV];          // V to the end of its block times gamma of the current query block
+#pragma unroll
+    for (int i = 0; i < NSV; ++i) kg[i] = zf;
+    int qcur = -1;
+    // dS of step kk from A's P (LDS) and the kept dP, then dK += dS^T Q_kk
+    // with Q read transposed from its row stage
+    auto dk_step = [&](int kk) {
+      f16x8 dsf[2];
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        const f32x4 pq = *(const __attribute__((address_space(3))) f32x4 *)lds_at(apx_ + (kk & 1) * 4 * PX + 1024 * j4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = 4 * j4 + e;
+          dsf[j >> 3][j & 7] = (_Float16)(pq[e] * dpk[j]);
+        }
+      }
+      const uint32_t so = (kk % 3) * QT::BYTES;
+      f16x4 tq[2][NBK][2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int bk = 0; bk < NBK; ++bk)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) tq[u][bk][t] = lds_tr8(opaque(aqt[bk][t]) + so + 16 * u * RQ);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int bk = 0; bk < NBK; ++bk)
+          acc[bk] = mma32(dsf[u], __builtin_shufflevector(tq[u][bk][0], tq[u][bk][1], 0, 1, 2, 3, 4, 5, 6, 7), acc[bk]);
+    };
+    for (int k = 0; k < nsteps; ++k) {
+      const int qa = qa_of(k);
+      const bool diag = qa == p;
+      wait_all();
+      __syncthreads();  // step k's tiles landed; step k - 1's readers are done
+      if (k + 1 < nsteps) stage_tile(k + 1);
+      if (k > 0 && act_of(qa_of(k - 1))) dk_step(k - 1);
+      if (!act_of(qa)) continue;
+      const uint32_t so = (k & 1) * XR::BYTES;
+      // dP[q][key] (lane = key, register j = query acc_row(hh, j))
+      f32x16 dp = zero16();
       if (diag) {
         // split at the token before the block: dhat and V as bf16 hi / lo (bf16x3)
 #pragma unroll
         for (int i = 0; i < NSV; ++i) {
-          const bf16x8 xh = *(const bf16x8 *)(XHs(buf) + XR::off(n, 2 * i + hh));
-          const bf16x8 xl = *(const bf16x8 *)(XLs(buf) + XR::off(n, 2 * i + hh));
-          const bf16x8 vh = *(const bf16x8 *)(BHs(buf) + XR::off(n, 2 * i + hh));
-          const bf16x8 vl = *(const bf16x8 *)(BLs(buf) + XR::off(n, 2 * i + hh));
+          const uint32_t ai = opaque(ax[i]) + so;
+          const bf16x8 xh = __builtin_bit_cast(bf16x8, lds_row16(ai + 2 * XR::BYTES));
+          const bf16x8 xl = __builtin_bit_cast(bf16x8, lds_row16(ai + 4 * XR::BYTES));
+          const bf16x8 vh = __builtin_bit_cast(bf16x8, lds_row16(ai + 6 * XR::BYTES));
+          const bf16x8 vl = __builtin_bit_cast(bf16x8, lds_row16(ai + 8 * XR::BYTES));
           dp = mma32(xh, vh, dp);
           dp = mma32(xl, vh, dp);
           dp = mma32(xh, vl, dp);
         }
       } else {
+        if (qa != qcur) {
+          // gamma[d] = exp2(E(qa - 1) - E(p)) depends on the channel only: each
+          // lane evaluates two channels into the wave's table, then every lane
+          // reads the channels it needs (a wave's LDS accesses complete in order)
 #pragma unroll
-        for (int i = 0; i < NSV; ++i) dp = mma32(*(const f16x8 *)(Xs(buf) + XR::off(n, 2 * i + hh)), kop[i], dp);
-      }
-      f16x8 dsf[2];
-      bf16x8 ph[2], plo[2];
+          for (int t = 0; t < (DV + 63) / 64; ++t) {
+            const int d = lane + 64 * t;
+            if (d < DV) gw[d] = fast_exp2(BE[qa][d] - BE[p + 1][d]);
+          }
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const float mv[4] = {mq[q4].x, mq[q4].y, mq[q4].z, mq[q4].w};
+          for (int i = 0; i < NSV; ++i) {
+            const float4 g0 = *(const float4 *)(gw + 16 * i + 8 * hh), g1 = *(const float4 *)(gw + 16 * i + 8 * hh + 4);
+            const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = 4 * q4 + e;
-          const int r = acc_row(hh, j);
-          const float pv = q0 + r < L && (!diag || r >= n) ? fast_exp2(sc[j] * sl2 - mv[e]) : 0.f;
-          dsf[j >> 3][j & 7] = (_Float16)(pv * dp[j]);
-          split_bf16(pv, ph[j >> 3], plo[j >> 3], j & 7);
+            for (int e = 0; e < 8; ++e) kg[i][e] = (_Float16)((float)kop[i][e] * gv[e]);
+          }
+          qcur = qa;
         }
+        f16x8 fx[NSV];
+#pragma unroll
+        for (int i = 0; i < NSV; ++i) fx[i] = lds_row16(opaque(ax[i]) + so);
+#pragma unroll
+        for (int i = 0; i < NSV; ++i) dp = mma32(fx[i], kg[i], dp);
       }
-      // dV[key][d] += gamma[d] * sum_q P[q][key] dhat[q][d]  (bf16x3)
-#pragma unroll
-      for (int bv = 0; bv < NBV; ++bv) {
-        f32x16 tmp = zero16();
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const bf16x8 th = __builtin_bit_cast(bf16x8, tr_frag<XR>(XHs(buf), 16 * u, 32 * bv, lane));
-          const bf16x8 tl = __builtin_bit_cast(bf16x8, tr_frag<XR>(XLs(buf), 16 * u, 32 * bv, lane));
-          tmp = mma32(ph[u], th, tmp);
-          tmp = mma32(ph[u], tl, tmp);
-          tmp = mma32(plo[u], th, tmp);
-        }
-#pragma unroll
-        for (int j = 0; j < 16; ++j) accV[bv][j] += gcol[bv] * tmp[j];
-      }
-      // dK[key][dk] += dS[q][key] Q[q][dk]
-#pragma unroll
-      for (int bk = 0; bk < NBK; ++bk)
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-          accK[bk] = mma32(dsf[u], tr_frag<QT>(Qs(buf), 16 * u, 32 * bk, lane), accK[bk]);
+      dpk = dp;
     }
     wait_all();
-    __syncthreads();
+    __syncthreads();  // A's last P is in LDS
+    if (nsteps > 0 && act_of(qa_of(nsteps - 1))) dk_step(nsteps - 1);
   }
-  if (!active) return;
 
-  // Diagonal block with exact per-pair decays (gate range beyond 2^BGUARD),
-  // per head from global memory.  (Otherwise the staged loop did it: split at
-  // the token before the block, gamma = exp2(E(w-1) - E(w)) >= 1, V from the
-  // token before the block as bf16x3.)
-  bool dflag = false;  // exact diagonal contributions written to dv_i
-  if (direct) {
-    const int q0 = kb;
-    const int qrow = min(q0 + n, L - 1);  // A-operand row of this lane
-    for (int gq = 0; gq < G; ++gq) {
-      const int h = c * G + gq;
-      f32x16 sc = zero16(), dp = zero16();
+  if (!isA && active) {
 #pragma unroll
-      for (int i = 0; i < NS; ++i)
-        sc = mma32(*(const f16x8 *)(a.Q16 + ((st + qrow) * Hq + h) * DK + 16 * i + 8 * hh), kf[i], sc);
-      float p[16];
+    for (int bk = 0; bk < NBK; ++bk) {
+      const int col = 32 * bk + n;
+      if (col >= DK) continue;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const int r = acc_row(hh, j);
-        p[j] = (q0 + r < L && r >= n) ? fast_exp2(sc[j] * sl2 - a.mb[(st + q0 + r) * Hq + h]) : 0.f;
-      }
-      {
-        float t[16];
-        direct_dp<DV, F32IN, false>(a.delta, a.sig, a.Gl2, a.v, Hq, Hkv, st, c, h, L, q0, kb, hh, n, t);
-#pragma unroll
-        for (int j = 0; j < 16; ++j) dp[j] = t[j];
-      }
-      f16x8 dsf[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) dsf[u][i] = (_Float16)(p[8 * u + i] * dp[8 * u + i]);
-      // exact per-pair decays, written straight to the within-chunk partial
-      // (this wave owns these keys): P[q][kj] lives in lane kj, register of q
-#pragma unroll
-      for (int bv = 0; bv < NBV; ++bv) {
-        const int col = 32 * bv + n;
-        float t[16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) t[j] = 0.f;
-#pragma unroll 1
-        for (int qq = 0; qq < 32; ++qq) {
-          const int qk = q0 + qq;
-          const int jsrc = (qq >> 3) * 4 + (qq & 3), hsrc = (qq >> 2) & 1;
-          float pj = 0.f;
-#pragma unroll
-          for (int j = 0; j < 16; ++j) pj = (j == jsrc) ? p[j] : pj;
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int kl = acc_row(hh, j);
-            const float pv = __shfl(pj, kl + 32 * hsrc);
-            const int kj = kb + kl;
-            if (col < DV && qk < L && kj <= qk)
-              t[j] += pv * fast_exp2(gl_at(qk, col) - gl_at(kj, col)) * a.delta[((st + qk) * Hq + h) * DV + col] *
-                      a.sig[(st + qk) * Hq + h];
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int kj = kb + acc_row(hh, j);
-          if (col < DV && kj < L) {
-            const int64_t idx = ((st + kj) * Hkv + c) * DV + col;
-            a.dv_i[idx] = (dflag ? a.dv_i[idx] : 0.f) + t[j];
-          }
-        }
-      }
-      dflag = true;
-      // dK[key][dk] += dS[q][key] Q[q][dk]: element i of lane (hh, n) of the
-      // B operand is Q[q0 + 16u + acc_row(hh, i)][32bk + n], the k order of dsf
-#pragma unroll
-      for (int bk = 0; bk < NBK; ++bk) {
-        const int col = min(32 * bk + n, DK - 1);
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          f16x8 qb;
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-            qb[i] = a.Q16[((st + min(q0 + 16 * u + acc_row(hh, i), L - 1)) * Hq + h) * DK + col];
-          accK[bk] = mma32(dsf[u], qb, accK[bk]);
-        }
+        const int kj = kb + acc_row(hh, j);
+        if (kj < L) a.dk_i[((st + kj) * Hkv + c) * DK + col] = a.scale * acc[bk][j];
       }
     }
   }
-  // dv relative to the end of the key's block: exp2(E(w) - Gl_j).  Every
-  // input of the epilogue is loaded before its first store (the compiler
-  // cannot tell the buffers apart, so a load after a store would wait for it).
-  if (nsteps == 0) load_gl();
-  float part[NBV][16];
-#pragma unroll
-  for (int bv = 0; bv < NBV; ++bv) {
+  // Diagonal block with exact per-pair decays (gate range beyond 2^BGUARD),
+  // by B after its dk store; A's epilogue reads its dV partials after the
+  // barrier below.  (Otherwise the staged loop did it: split at the token
+  // before the block, gamma = exp2(E(p-1) - E(p)) >= 1, V from the token
+  // before the block as bf16x3.)
+  if (!isA && direct && active)
+    near_exact_diag<DK, DV, F32IN>(a.delta, a.sig, a.Gl2, a.v, a.k, a.Q16, a.mb, a.dv_i, a.dk_i, a.scale, sl2, Hq, Hkv, G,
+                                   st, c, L, kb);
+  if (direct_any) __syncthreads();  // B's exact diagonal dV partials are written
+  if (!active || !isA) return;
+  // dv relative to the last query block's gamma: exp2(E(qlast - 1) - Gl_j).  Each
+  // column block's inputs are loaded one block ahead, before the previous
+  // block's stores (the compiler cannot tell the buffers apart, so a load
+  // after a store would wait for it).
+  float in[2][2][16];  // [slot][gate value, exact partial][row]
+  auto load_dv = [&](int bv, float (&x)[2][16]) {
     const int col = min(32 * bv + n, DV - 1);
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-      part[bv][j] = dflag ? a.dv_i[((st + min(kb + acc_row(hh, j), L - 1)) * Hkv + c) * DV + col] : 0.f;
-  }
+    for (int j = 0; j < 16; ++j) {
+      const int64_t idx = ((st + min(kb + acc_row(hh, j), L - 1)) * Hkv + c) * DV + col;
+      x[0][j] = a.Gl2[idx];
+      x[1][j] = direct ? a.dv_i[idx] : 0.f;
+    }
+  };
+  load_dv(0, in[0]);
 #pragma unroll
   for (int bv = 0; bv < NBV; ++bv) {
+    if (bv + 1 < NBV) load_dv(bv + 1, in[(bv + 1) & 1]);
     const int col = 32 * bv + n;
     if (col >= DV) continue;
-    const float ew = BE[wave + 1][col];
+    const float ew = BE[qlast][col];
+    const float(&x)[2][16] = in[bv & 1];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int kj = kb + acc_row(hh, j);
-      if (kj < L) a.dv_i[((st + kj) * Hkv + c) * DV + col] = fast_exp2(ew - gl[bv][j]) * accV[bv][j] + part[bv][j];
-    }
-  }
-  // dk after dv: the dv block loads then wait for no earlier stores
-#pragma unroll
-  for (int bk = 0; bk < NBK; ++bk) {
-    const int col = 32 * bk + n;
-    if (col >= DK) continue;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int kj = kb + acc_row(hh, j);
-      if (kj < L) a.dk_i[((st + kj) * Hkv + c) * DK + col] = a.scale * accK[bk][j];
+      if (kj < L) a.dv_i[((st + kj) * Hkv + c) * DV + col] = fast_exp2(ew - x[0][j]) * acc[bv][j] + x[1][j];
     }
   }
 }
@@ -1413,8 +1565,8 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkv(BwdArgs a) {
 template <int DK, int DV>
 hipError_t launch_bwd_dk_dv(BwdKernel kind, bool f32in, const BwdArgs &a, dim3 grid, hipStream_t st) {
 #define FIX_BWD_LAUNCH(KERN)                                                                  \
-  if (f32in) hipLaunchKernelGGL((KERN<DK, DV, true>), grid, dim3(kind == BK_DKV ? 512 : 256), 0, st, a); \
-  else hipLaunchKernelGGL((KERN<DK, DV, false>), grid, dim3(kind == BK_DKV ? 512 : 256), 0, st, a);
+  if (f32in) hipLaunchKernelGGL((KERN<DK, DV, true>), grid, dim3(kind == BK_DQ || kind == BK_INTRA_DQ ? 256 : 512), 0, st, a); \
+  else hipLaunchKernelGGL((KERN<DK, DV, false>), grid, dim3(kind == BK_DQ || kind == BK_INTRA_DQ ? 256 : 512), 0, st, a);
   switch (kind) {
     case BK_INTRA_DQ: FIX_BWD_LAUNCH(k_bwd_intra_dq); break;
     case BK_INTRA_DKV: FIX_BWD_LAUNCH(k_bwd_intra_dkv); break;

@@ -67,47 +67,95 @@ __device__ __noinline__ void direct_dp(const float *delta, const float *sig, con
 }
 
 // ---------------------------------------------------------------------------
-// Within-chunk contributions to dq.  Workgroup = one 128-chunk of one q head;
-// wave w owns query rows c0 + 32w .. +31 (query block w).  Key blocks b are
-// copied into LDS one per step (double buffered): K rows, transposed K, V
-// scaled to the end of its block (VE), and for the diagonal block of wave b
-// its V relative to the token before it and query block b's dhat (bf16 hi /
-// lo each), so every wave's diagonal block is computed in the step of its
-// own key block.  With E(b) the chunk-local log2
-// gate prefix at the end of block b (E(-1) = 0), the decay of a pair in
-// query block a > b splits as
+// Within-chunk contributions to dq.  Workgroup = one 128-chunk of one q
+// head; query block p (rows c0 + 32p .. +31) is shared by wave p (A) and wave
+// p + 4 (B), which the hardware places on the same SIMD.  Key blocks b are
+// copied into LDS one per step: K, V scaled to the end of its block
+// (VE), and for the diagonal block of pair b its V relative to the token
+// before it and query block b's dhat (bf16 hi / lo each).  K is staged twice:
+// as rows (bf16, fp16 for fp32 inputs) for S^T and as its transposed fp16
+// tile (three stages: B reads it one step late) for dQ.  With E(b) the
+// chunk-local log2 gate prefix at the end of block b (E(-1) = 0), the decay
+// of a pair in query block a > b splits as
 //     exp2(Gl_i - E(a-1)) * exp2(E(a-1) - E(b)) * exp2(E(b) - Gl_j),
 // all three <= 1: the first is the prepared block-relative dhat (X16), the
-// middle one gamma_ab multiplies the wave's dhat operand per channel, the
-// last is VE.  On the diagonal block the split is at the token before it:
-// the key side exp2(E(a-1) - Gl_j) >= 1 needs fp32 range and is multiplied
-// as bf16x3 (hi*hi + hi*lo + lo*hi); a block whose gate range exceeds
-// 2^BGUARD is evaluated with direct per-pair decays.
+// middle one gamma_ab multiplies B's dhat operand per channel, the last is
+// VE.  On the diagonal block the split is at the token before it: the key
+// side exp2(E(a-1) - Gl_j) >= 1 needs fp32 range and is multiplied as bf16x3
+// (hi*hi + hi*lo + lo*hi); a block whose gate range exceeds 2^BGUARD is
+// evaluated with direct per-pair decays.
+//   A, step b: S^T = K Q^T (lane = query row), P = exp2(S sl2 - m) (fp32
+//              into LDS); the copies of step b+1's K rows and tile.
+//   B, step b: dS_{b-1} = P_{b-1} (LDS) (.) the dP_{b-1} it kept, dQ +=
+//              dS_{b-1} K_{b-1}; dP_b^T = V (dhat (.) gamma)^T; the copies of
+//              step b+1's V rows and diagonal tiles.
 // ---------------------------------------------------------------------------
+// The diagonal block of query block r0 with exact per-pair decays (its gate
+// range beyond 2^BGUARD; rare), for one wave, from global memory, after the
+// wave has stored its dq rows: the block's dQ is added to them (the same
+// lanes wrote them).  A function of its own so that the kernel's loops keep
+// their registers.
 template <int DK, int DV, bool F32IN>
-__global__ void __launch_bounds__(256, 1) k_bwd_intra_dq(BwdArgs a) {
+__device__ __noinline__ void near_exact_diag_dq(const float *delta, const float *sig, const float *Gl2, const void *v,
+                                                const void *kp, const void *qp, const _Float16 *Kt, const float *mb,
+                                                float *dq_i, float scale, float sl2, int Hq, int Hkv, int64_t st, int c,
+                                                int hq, int L, int gc, int r0) {
+  using IF = InFrag<F32IN>;
+  constexpr int NS = DK / 16, NBK = Pad32<DK>::value / 32;
+  const int lane = threadIdx.x & 63, hh = lane >> 5, n = lane & 31;
+  const int row = r0 + n, kb = r0;
+  const int key = min(kb + n, L - 1), qrow = min(row, L - 1);
+  float t[16];
+  direct_dp<DV, F32IN, true>(delta, sig, Gl2, v, Hq, Hkv, st, c, hq, L, r0, kb, hh, n, t);
+  // S^T[key][row]: lane = row, register j = key acc_row(hh, j)
+  f32x16 sc = zero16();
+#pragma unroll
+  for (int i = 0; i < NS; ++i)
+    sc = mma32(IF::load(kp, ((st + key) * Hkv + c) * DK + 16 * i + 8 * hh),
+               IF::load(qp, ((st + qrow) * Hq + hq) * DK + 16 * i + 8 * hh), sc);
+  const float mbn = row < L ? mb[(st + row) * Hq + hq] : INFINITY;
+  f16x8 dsf[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int j = 8 * u + i;
+      dsf[u][i] = (_Float16)(acc_row(hh, j) > n ? 0.f : fast_exp2(sc[j] * sl2 - mbn) * t[j]);
+    }
+  // dQ[row][dk] += dS[row][key] K[key][dk], K from its transposed tile
+  const _Float16 *ktile = Kt + ((int64_t)gc * Hkv + c) * DK * CB + (r0 % CB);
+#pragma unroll 1
+  for (int bk = 0; bk < NBK; ++bk) {
+    const int col = min(32 * bk + n, DK - 1);  // padded columns are never stored
+    f32x16 dacc = zero16();
+#pragma unroll
+    for (int u = 0; u < 2; ++u) dacc = mma32(dsf[u], *(const f16x8 *)(ktile + (int64_t)col * CB + 16 * u + 8 * hh), dacc);
+    if (32 * bk + n < DK)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int r = r0 + acc_row(hh, j);
+        if (r < L) dq_i[((st + r) * Hq + hq) * DK + col] += scale * dacc[j];
+      }
+  }
+}
+
+template <int DK, int DV, bool F32IN>
+__global__ void __launch_bounds__(512, 1) k_bwd_intra_dq(BwdArgs a) {
   using IF = InFrag<F32IN>;
   using kfrag = typename IF::type;
   constexpr int NS = DK / 16, NSV = DV / 16, DKP = Pad32<DK>::value, NBK = DKP / 32;
-  using KT = LdsTile<32, DK * 2>;   // K rows of the key block
-  using TT = LdsTile<DKP, 64>;     // transposed K, rows padded to DKP
+  using KT = LdsTile<32, DK * 2>;  // K rows of the key block
+  using TT = LdsTile<DKP, 64>;     // transposed K (dk rows x 32 keys, key_pos order), rows padded to DKP
   using TTD = LdsTile<DK, 64>;
-  using VT = LdsTile<32, DV * 2>;  // VE rows of the key block
-  // One LDS object for every tile (see the forward kernel).
-  constexpr int O_K = 0, O_T = O_K + 2 * KT::BYTES, O_V = O_T + 2 * TT::BYTES, O_E = O_V + 2 * VT::BYTES;
-  // Per stage also, for the diagonal block of the wave whose block it is, the
-  // key block's V relative to the token before it and the same block's
-  // block-relative dhat rows (bf16 hi, lo each).
-  constexpr int O_BH = O_E + 5 * DV * 4, O_BL = O_BH + 2 * VT::BYTES, O_XH = O_BL + 2 * VT::BYTES;
-  constexpr int O_XL = O_XH + 2 * VT::BYTES;
-  __shared__ __align__(1024) char smem[O_XL + 2 * VT::BYTES];
-  auto BHs = [&](int b) { return smem + O_BH + b * VT::BYTES; };
-  auto BLs = [&](int b) { return smem + O_BL + b * VT::BYTES; };
-  auto XHs = [&](int b) { return smem + O_XH + b * VT::BYTES; };
-  auto XLs = [&](int b) { return smem + O_XL + b * VT::BYTES; };
-  auto Ks = [&](int b) { return smem + O_K + b * KT::BYTES; };
-  auto Kts = [&](int b) { return smem + O_T + b * TT::BYTES; };
-  auto Vs = [&](int b) { return smem + O_V + b * VT::BYTES; };
+  using VT = LdsTile<32, DV * 2>;  // VE rows of the key block; the diagonal's bf16 hi / lo rows
+  constexpr int PX = 4 * 64 * 16;  // one pair's P of a step: [j / 4][lane] float4
+  // One LDS object for every tile (see the forward kernel).  Per stage, for
+  // the diagonal block of the pair whose block it is: the key block's V
+  // relative to the token before it and the same block's block-relative
+  // dhat rows (bf16 hi, lo each), at fixed distances from the VE tile.
+  constexpr int O_K = 0, O_T = O_K + 2 * KT::BYTES, O_V = O_T + 3 * TT::BYTES, O_P = O_V + 10 * VT::BYTES;
+  constexpr int O_E = O_P + 2 * 4 * PX, O_GW = O_E + 5 * DV * 4;
+  __shared__ __align__(1024) char smem[O_GW + 4 * DV * 2];
   float(*BE)[DV] = (float(*)[DV])(smem + O_E);  // BE[b + 1] = E(b), BE[0] = 0
 
   const Plan &pl = a.plan;
@@ -115,91 +163,110 @@ __global__ void __launch_bounds__(256, 1) k_bwd_intra_dq(BwdArgs a) {
   if (gc >= pl.counts[0]) return;
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, n = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool isA = wave < 4;
+  const int p = wave & 3;
+  _Float16 *gw = (_Float16 *)(smem + O_GW) + p * DV;  // B's gamma of the step, per channel (fp16)
   const int s = seq_of_chunk(pl.cb128, pl.nseq, gc);
   const int c0 = uniform((gc - pl.cb128[s]) * CB);
   const int L = uniform(pl.seq_len[s]);
   const int64_t st = uniform((int64_t)pl.seq_start[s]);
   const int Hq = a.Hq, Hkv = a.Hkv, c = hq / (Hq / Hkv);
-  const int nblk = min(4, (L - c0 + 31) / 32);  // query (and key) blocks present in the chunk
-  const int r0 = c0 + 32 * wave;
+  const int nsteps = min(4, (L - c0 + 31) / 32);  // query (and key) blocks present in the chunk
+  const int r0 = c0 + 32 * p;
   const int row = r0 + n;
-  const bool active = wave < nblk;
+  const bool active = p < nsteps;
   const bool rv = active && row < L;
   const float sl2 = a.sl2;
   auto gl_at = [&](int tok, int d) { return a.Gl2[((st + tok) * Hkv + c) * DV + d]; };
+  const uint32_t sbase = lds_addr(smem);
 
-  for (int e = tid; e < 5 * DV; e += 256) {
-    const int b = e / DV - 1, d = e % DV;
-    BE[b + 1][d] = b < 0 ? 0.f : gl_at(min(c0 + 32 * b + 31, L - 1), d);
-  }
-  if (DK < DKP)
-    for (int e = tid; e < (DKP - DK) * 64 / 4; e += 256) {
-      ((uint32_t *)(Kts(0) + DK * 64))[e] = 0u;
-      ((uint32_t *)(Kts(1) + DK * 64))[e] = 0u;
-    }
-  kfrag qf[NS];
-  f16x8 xr[NSV];  // the row's block-relative dhat, B operand of dP^T (k = channel)
-#pragma unroll
-  for (int i = 0; i < NS; ++i)
-    qf[i] = rv ? IF::load(a.q, ((st + row) * Hq + hq) * DK + 16 * i + 8 * hh) : IF::zero();
-#pragma unroll
-  for (int i = 0; i < NSV; ++i)
-    xr[i] = rv ? *(const f16x8 *)(a.X16 + ((st + row) * Hq + hq) * DV + 16 * i + 8 * hh)
-               : __builtin_bit_cast(f16x8, make_uint4(0, 0, 0, 0));
-  const float mbn = rv ? a.mb[(st + row) * Hq + hq] : INFINITY;
-  f32x16 acc[NBK];
-#pragma unroll
-  for (int b = 0; b < NBK; ++b) acc[b] = zero16();
-
-  // Key block b is staged with the rows before the sequence end only (the
-  // rest read as zeros): off the diagonal every key is valid, on the diagonal
-  // the keys past the end meet only masked pairs.
+  // Copies of key block b.  Rows past the sequence end read as zeros: off
+  // the diagonal every key is valid, on the diagonal the keys past the end
+  // meet only masked pairs.
   uint32_t ok[KT::NW], ot[TTD::NW], ov[VT::NW], oxq[VT::NW];
-  VT::lane_offsets(Hq * DV * 2, wave, lane, oxq);
-  KT::lane_offsets(Hkv * DK * 2, wave, lane, ok);
-  TTD::lane_offsets(CB * 2, wave, lane, ot);
-  VT::lane_offsets(Hkv * DV * 2, wave, lane, ov);
-  auto stage_tile = [&](int b, int buf) {
+  KT::lane_offsets(Hkv * DK * 2, p, lane, ok);
+  TTD::lane_offsets(CB * 2, p, lane, ot);
+  VT::lane_offsets(Hkv * DV * 2, p, lane, ov);
+  VT::lane_offsets(Hq * DV * 2, p, lane, oxq);
+  auto stage_tile = [&](int b) {
     const int kb = c0 + 32 * b;
     const int64_t kr = (st + kb) * Hkv + c;
-    const int nrow = min(32, L - kb);
-    if constexpr (!F32IN) {
-      const u32x4 rk = rsrc_words((const uint16_t *)a.k + kr * DK, (int64_t)nrow * Hkv * DK * 2);
+    const int nrow = L - kb;
+    if (isA) {
+      char *ks = smem + O_K + (b & 1) * KT::BYTES;
+      if constexpr (!F32IN) {
+        const u32x4 rk = rsrc_words((const uint16_t *)a.k + kr * DK, (int64_t)nrow * Hkv * DK * 2);
 #pragma unroll
-      for (int t = 0; t < KT::NW; ++t) KT::dma_piece_untracked(Ks(buf), rk, ok, t, wave);
-    } else {
-      for (int p = tid; p < KT::NCH; p += 256) {
-        const int r = p / KT::CPR, cc = p % KT::CPR;
-        *(f16x8 *)(Ks(buf) + KT::off(r, cc)) = IF::load(a.k, ((st + min(kb + r, L - 1)) * Hkv + c) * DK + 8 * cc);
+        for (int t = 0; t < KT::NW; ++t) KT::dma_piece_untracked(ks, rk, ok, t, p);
+      } else {
+        for (int q = tid; q < KT::NCH; q += 256) {
+          const int r = q / KT::CPR, cc = q % KT::CPR;
+          *(f16x8 *)(ks + KT::off(r, cc)) = IF::load(a.k, ((st + min(kb + r, L - 1)) * Hkv + c) * DK + 8 * cc);
+        }
       }
-    }
-    const u32x4 rt = rsrc_words(a.Kt + ((int64_t)gc * Hkv + c) * DK * CB + 32 * b, (int64_t)DK * CB * 2);
+      const u32x4 rt = rsrc_words(a.Kt + ((int64_t)gc * Hkv + c) * DK * CB + 32 * b, (int64_t)DK * CB * 2);
 #pragma unroll
-    for (int t = 0; t < TTD::NW; ++t) TTD::dma_piece_untracked(Kts(buf), rt, ot, t, wave);
-    const u32x4 rv = rsrc_words(a.VE + kr * DV, (int64_t)nrow * Hkv * DV * 2);
-    const u32x4 rbh = rsrc_words(a.VBH + kr * DV, (int64_t)nrow * Hkv * DV * 2);
-    const u32x4 rbl = rsrc_words(a.VBL + kr * DV, (int64_t)nrow * Hkv * DV * 2);
-    const int64_t xq = ((st + kb) * Hq + hq) * DV;  // query block b = key block b
-    const u32x4 rxh = rsrc_words(a.XH + xq, (int64_t)nrow * Hq * DV * 2);
-    const u32x4 rxl = rsrc_words(a.XL + xq, (int64_t)nrow * Hq * DV * 2);
+      for (int t = 0; t < TTD::NW; ++t) TTD::dma_piece_untracked(smem + O_T + (b % 3) * TT::BYTES, rt, ot, t, p);
+    } else {
+      char *v0 = smem + O_V + (b & 1) * VT::BYTES;  // VE, BH, BL, XH, XL at 2 tiles' distance each
+      const int64_t xq = ((st + kb) * Hq + hq) * DV;  // query block b = key block b
+      const u32x4 rv = rsrc_words(a.VE + kr * DV, (int64_t)nrow * Hkv * DV * 2);
+      const u32x4 rbh = rsrc_words(a.VBH + kr * DV, (int64_t)nrow * Hkv * DV * 2);
+      const u32x4 rbl = rsrc_words(a.VBL + kr * DV, (int64_t)nrow * Hkv * DV * 2);
+      const u32x4 rxh = rsrc_words(a.XH + xq, (int64_t)nrow * Hq * DV * 2);
+      const u32x4 rxl = rsrc_words(a.XL + xq, (int64_t)nrow * Hq * DV * 2);
 #pragma unroll
-    for (int t = 0; t < VT::NW; ++t) {
-      VT::dma_piece_untracked(Vs(buf), rv, ov, t, wave);
-      VT::dma_piece_untracked(BHs(buf), rbh, ov, t, wave);
-      VT::dma_piece_untracked(BLs(buf), rbl, ov, t, wave);
-      VT::dma_piece_untracked(XHs(buf), rxh, oxq, t, wave);
-      VT::dma_piece_untracked(XLs(buf), rxl, oxq, t, wave);
+      for (int t = 0; t < VT::NW; ++t) {
+        VT::dma_piece_untracked(v0, rv, ov, t, p);
+        VT::dma_piece_untracked(v0 + 2 * VT::BYTES, rbh, ov, t, p);
+        VT::dma_piece_untracked(v0 + 4 * VT::BYTES, rbl, ov, t, p);
+        VT::dma_piece_untracked(v0 + 6 * VT::BYTES, rxh, oxq, t, p);
+        VT::dma_piece_untracked(v0 + 8 * VT::BYTES, rxl, oxq, t, p);
+      }
     }
   };
 
-  // Key blocks b <= wave through LDS: the blocks before the wave's own, then
-  // (at b = wave) its diagonal block, unless that block's gate range needs
-  // exact per-pair decays (then it is done afterwards from global memory).
-  const int nsteps = nblk;
-  wait_all();  // every load above is complete before the first untracked copy
-  if (nsteps > 0) stage_tile(0, 0);
+  // Prologue: the block-end gate values (E), the row operand of the wave's
+  // role (A: q as fp16 and the row offset; B: the block-relative dhat) and
+  // the first step's copies, all issued before one wait.
+  constexpr int NBE = (5 * DV + 511) / 512;
+  float be[NBE];
+#pragma unroll
+  for (int t = 0; t < NBE; ++t) {
+    const int e = tid + 512 * t, b = e / DV - 1, d = e % DV;
+    be[t] = e < 5 * DV && b >= 0 ? gl_at(min(c0 + 32 * b + 31, L - 1), d) : 0.f;
+  }
+  const f16x8 zf = __builtin_bit_cast(f16x8, make_uint4(0, 0, 0, 0));
+  if (DK < DKP)  // the transposed tiles' padding rows
+    for (int e = tid; e < (DKP - DK) * 64 / 4; e += 512)
+      for (int b = 0; b < 3; ++b) ((uint32_t *)(smem + O_T + b * TT::BYTES + DK * 64))[e] = 0u;
+  kfrag qf[NS];  // A: the row's q
+#pragma unroll
+  for (int i = 0; i < NS; ++i) qf[i] = IF::zero();
+  f16x8 rop[NSV];  // B: the row's block-relative dhat (k = channel)
+#pragma unroll
+  for (int i = 0; i < NSV; ++i) rop[i] = zf;
+  float mbn = INFINITY;
+  if (isA) {
+    if (rv) {
+#pragma unroll
+      for (int i = 0; i < NS; ++i) qf[i] = IF::load(a.q, ((st + row) * Hq + hq) * DK + 16 * i + 8 * hh);
+      mbn = a.mb[(st + row) * Hq + hq];
+    }
+  } else if (rv) {
+#pragma unroll
+    for (int i = 0; i < NSV; ++i) rop[i] = *(const f16x8 *)(a.X16 + ((st + row) * Hq + hq) * DV + 16 * i + 8 * hh);
+  }
+  if (nsteps > 0) stage_tile(0);
   wait_all();
+#pragma unroll
+  for (int t = 0; t < NBE; ++t) {
+    const int e = tid + 512 * t, b = e / DV - 1, d = e % DV;
+    if (e < 5 * DV) BE[b + 1][d] = be[t];
+  }
   __syncthreads();
+  // Whether a block's diagonal needs exact per-pair decays (its gate range
+  // beyond 2^BGUARD): this pair's.
   bool direct;
   {
     float rng = 0.f;
@@ -208,126 +275,130 @@ __global__ void __launch_bounds__(256, 1) k_bwd_intra_dq(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int d = 16 * i + 8 * hh + e;
-        rng = fmaxf(rng, BE[wave][d] - BE[wave + 1][d]);
+        rng = fmaxf(rng, BE[p][d] - BE[p + 1][d]);
       }
     direct = __any(rng > BGUARD);
   }
-  for (int b = 0; b < nsteps; ++b) {
-    const int buf = b & 1;
-    const bool diag = wave == b;
-    const bool act = active && (wave > b || (diag && !direct));
-    // gamma_ab (an LDS table) is applied before the next copies are issued:
-    // LDS reads that follow a copy issue in the same step can make the
-    // compiler wait for it.
-    f16x8 xg[NSV];
-    if (act && !diag) {
+  auto act_of = [&](int b) { return active && (b < p || (b == p && !direct)); };
+  const uint32_t apx = sbase + O_P + p * PX + 16 * lane;  // this lane's P exchange slot
+
+  if (isA) {
+    uint32_t ak[NS];
 #pragma unroll
-      for (int i = 0; i < NSV; ++i)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int d = 16 * i + 8 * hh + e;
-          xg[i][e] = (_Float16)((float)xr[i][e] * fast_exp2(BE[wave][d] - BE[b + 1][d]));
-        }
-    }
-    stage_tile(min(b + 1, nsteps - 1), buf ^ 1);
-    if (act) {
+    for (int i = 0; i < NS; ++i) ak[i] = sbase + O_K + KT::off(n, min(2 * i + hh, KT::CPR - 1));
+    const uint32_t apx_ = opaque(apx);
+    for (int b = 0; b < nsteps; ++b) {
+      wait_all();
+      __syncthreads();  // step b's tiles landed; step b - 1's readers are done
+      if (b + 1 < nsteps) stage_tile(b + 1);
+      if (!act_of(b)) continue;
       // S^T[key][row]: lane = row, register j = key acc_row(hh, j)
-      f32x16 sc = zero16(), dp = zero16();
+      f32x16 sc = zero16();
+      {
+        const uint32_t so = (b & 1) * KT::BYTES;
+        kfrag fk[NS];
 #pragma unroll
-      for (int i = 0; i < NS; ++i) sc = mma32(*(const kfrag *)(Ks(buf) + KT::off(n, 2 * i + hh)), qf[i], sc);
-      f16x8 dsf[2];
-      if (diag) {
-        // split at the token before the block: V and dhat as bf16 hi / lo (bf16x3)
+        for (int i = 0; i < NS; ++i) fk[i] = __builtin_bit_cast(kfrag, lds_row16(opaque(ak[i]) + so));
 #pragma unroll
-        for (int i = 0; i < NSV; ++i) {
-          const bf16x8 vh = *(const bf16x8 *)(BHs(buf) + VT::off(n, 2 * i + hh));
-          const bf16x8 vl = *(const bf16x8 *)(BLs(buf) + VT::off(n, 2 * i + hh));
-          const bf16x8 xh = *(const bf16x8 *)(XHs(buf) + VT::off(n, 2 * i + hh));
-          const bf16x8 xl = *(const bf16x8 *)(XLs(buf) + VT::off(n, 2 * i + hh));
-          dp = mma32(vh, xh, dp);
-          dp = mma32(vh, xl, dp);
-          dp = mma32(vl, xh, dp);
-        }
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int j = 8 * u + i;
-            dsf[u][i] = (_Float16)(acc_row(hh, j) > n ? 0.f : fast_exp2(sc[j] * sl2 - mbn) * dp[j]);
-          }
-      } else {
-#pragma unroll
-        for (int i = 0; i < NSV; ++i) dp = mma32(*(const f16x8 *)(Vs(buf) + VT::off(n, 2 * i + hh)), xg[i], dp);
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) dsf[u][i] = (_Float16)(fast_exp2(sc[8 * u + i] * sl2 - mbn) * dp[8 * u + i]);
+        for (int i = 0; i < NS; ++i) sc = mma32(fk[i], qf[i], sc);
       }
+      const bool diag = b == p;
+      float pv[16];
 #pragma unroll
-      for (int bk = 0; bk < NBK; ++bk)
+      for (int j = 0; j < 16; ++j) pv[j] = diag && acc_row(hh, j) > n ? 0.f : fast_exp2(sc[j] * sl2 - mbn);
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-          acc[bk] = mma32(dsf[u], *(const f16x8 *)(Kts(buf) + TT::off(32 * bk + n, 2 * u + hh)), acc[bk]);
+      for (int j4 = 0; j4 < 4; ++j4)
+        *(__attribute__((address_space(3))) f32x4 *)lds_at(apx_ + (b & 1) * 4 * PX + 1024 * j4) =
+            f32x4{pv[4 * j4], pv[4 * j4 + 1], pv[4 * j4 + 2], pv[4 * j4 + 3]};
     }
     wait_all();
-    __syncthreads();
+    __syncthreads();  // the barrier B's last dQ step waits at
+    return;
   }
-  if (!active) return;
-  // Diagonal block with exact per-pair decays (gate range beyond 2^BGUARD),
-  // per wave from global memory; the staged loop did the others.
-  if (direct) {
-    const int kb = r0;
-    const int key = min(kb + n, L - 1);
-    float rng = 0.f;
+
+  // B: per-lane LDS addresses in stage 0: V row fragments (dP^T; the
+  // diagonal's tiles lie at fixed distances) and the transposed K fragments
+  // per output block and k slice (dQ)
+  uint32_t av[NSV], akt[NBK][2];
 #pragma unroll
-    for (int i = 0; i < NSV; ++i)
+  for (int i = 0; i < NSV; ++i) av[i] = sbase + O_V + VT::off(n, min(2 * i + hh, VT::CPR - 1));
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = 16 * i + 8 * hh + e;
-        rng = fmaxf(rng, BE[wave][d] - BE[wave + 1][d]);
+  for (int bk = 0; bk < NBK; ++bk)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) akt[bk][u] = sbase + O_T + TT::off(32 * bk + n, 2 * u + hh);
+  const uint32_t apx_ = opaque(apx);
+  f32x16 acc[NBK];
+#pragma unroll
+  for (int bk = 0; bk < NBK; ++bk) acc[bk] = zero16();
+  f32x16 dpk = zero16();  // dP^T of the previous step
+  // dS of step bb from A's P (LDS) and the kept dP, then dQ += dS K_bb with
+  // K from its transposed tile
+  auto dq_step = [&](int bb) {
+    f16x8 dsf[2];
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
+      const f32x4 pq = *(const __attribute__((address_space(3))) f32x4 *)lds_at(apx_ + (bb & 1) * 4 * PX + 1024 * j4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = 4 * j4 + e;
+        dsf[j >> 3][j & 7] = (_Float16)(pq[e] * dpk[j]);
       }
-    const bool direct = __any(rng > BGUARD);
-    f32x16 sc = zero16(), dp = zero16();
+    }
+    const uint32_t so = (bb % 3) * TT::BYTES;
+    f16x8 tk[2][NBK];
 #pragma unroll
-    for (int i = 0; i < NS; ++i)
-      sc = mma32(IF::load(a.k, ((st + key) * Hkv + c) * DK + 16 * i + 8 * hh), qf[i], sc);
-    if (!direct) {
-      const int64_t kr = ((st + key) * Hkv + c) * DV, xrw = ((st + min(row, L - 1)) * Hq + hq) * DV;
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int bk = 0; bk < NBK; ++bk) tk[u][bk] = lds_row16(opaque(akt[bk][u]) + so);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int bk = 0; bk < NBK; ++bk) acc[bk] = mma32(dsf[u], tk[u][bk], acc[bk]);
+  };
+  for (int b = 0; b < nsteps; ++b) {
+    wait_all();
+    __syncthreads();  // step b's tiles landed; step b - 1's readers are done
+    if (b + 1 < nsteps) stage_tile(b + 1);
+    if (b > 0 && act_of(b - 1)) dq_step(b - 1);
+    if (!act_of(b)) continue;
+    const uint32_t so = (b & 1) * VT::BYTES;
+    // dP^T[key][row] (lane = row, register j = key acc_row(hh, j))
+    f32x16 dp = zero16();
+    if (b == p) {
+      // split at the token before the block: V and dhat as bf16 hi / lo (bf16x3)
 #pragma unroll
       for (int i = 0; i < NSV; ++i) {
-        // the key's V relative to the token before the block, bf16 hi / lo
-        const bf16x8 zero = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
-        const bf16x8 vh = kb + n < L ? *(const bf16x8 *)(a.VBH + kr + 16 * i + 8 * hh) : zero;
-        const bf16x8 vl = kb + n < L ? *(const bf16x8 *)(a.VBL + kr + 16 * i + 8 * hh) : zero;
-        const bf16x8 xh = *(const bf16x8 *)(a.XH + xrw + 16 * i + 8 * hh);
-        const bf16x8 xl = *(const bf16x8 *)(a.XL + xrw + 16 * i + 8 * hh);
+        const uint32_t ai = opaque(av[i]) + so;
+        const bf16x8 vh = __builtin_bit_cast(bf16x8, lds_row16(ai + 2 * VT::BYTES));
+        const bf16x8 vl = __builtin_bit_cast(bf16x8, lds_row16(ai + 4 * VT::BYTES));
+        const bf16x8 xh = __builtin_bit_cast(bf16x8, lds_row16(ai + 6 * VT::BYTES));
+        const bf16x8 xl = __builtin_bit_cast(bf16x8, lds_row16(ai + 8 * VT::BYTES));
         dp = mma32(vh, xh, dp);
         dp = mma32(vh, xl, dp);
         dp = mma32(vl, xh, dp);
       }
     } else {
-      float t[16];
-      direct_dp<DV, F32IN, true>(a.delta, a.sig, a.Gl2, a.v, Hq, Hkv, st, c, hq, L, r0, kb, hh, n, t);
+      // gamma_pb[d] = exp2(E(p - 1) - E(b)) <= 1 depends on the channel only:
+      // each lane evaluates two channels into the wave's table (fp16), then
+      // every lane reads the channels it needs (a wave's LDS accesses
+      // complete in order) and scales its dhat operand with packed products
 #pragma unroll
-      for (int j = 0; j < 16; ++j) dp[j] = t[j];
-    }
-    f16x8 dsf[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int j = 8 * u + i;
-        dsf[u][i] = (_Float16)(acc_row(hh, j) > n ? 0.f : fast_exp2(sc[j] * sl2 - mbn) * dp[j]);
+      for (int t = 0; t < (DV + 63) / 64; ++t) {
+        const int d = lane + 64 * t;
+        if (d < DV) gw[d] = (_Float16)fast_exp2(BE[p][d] - BE[b + 1][d]);
       }
-    const _Float16 *ktile = a.Kt + ((int64_t)gc * Hkv + c) * DK * CB + 32 * wave;
+      f16x8 fv[NSV];
 #pragma unroll
-    for (int bk = 0; bk < NBK; ++bk) {
-      const int col = min(32 * bk + n, DK - 1);  // padded columns are never stored
+      for (int i = 0; i < NSV; ++i) fv[i] = lds_row16(opaque(av[i]) + so);
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-        acc[bk] = mma32(dsf[u], *(const f16x8 *)(ktile + (int64_t)col * CB + 16 * u + 8 * hh), acc[bk]);
+      for (int i = 0; i < NSV; ++i) dp = mma32(fv[i], rop[i] * *(const f16x8 *)(gw + 16 * i + 8 * hh), dp);
     }
+    dpk = dp;
   }
+  wait_all();
+  __syncthreads();  // A's last P is in LDS
+  if (nsteps > 0 && act_of(nsteps - 1)) dq_step(nsteps - 1);
+  if (!active) return;
 #pragma unroll
   for (int bk = 0; bk < NBK; ++bk) {
     const int col = 32 * bk + n;
@@ -338,6 +409,11 @@ __global__ void __launch_bounds__(256, 1) k_bwd_intra_dq(BwdArgs a) {
       if (r < L) a.dq_i[((st + r) * Hq + hq) * DK + col] = a.scale * acc[bk][j];
     }
   }
+  // Diagonal block with exact per-pair decays (gate range beyond 2^BGUARD),
+  // added to the stored rows.  (Otherwise the staged loop did it.)
+  if (direct)
+    near_exact_diag_dq<DK, DV, F32IN>(a.delta, a.sig, a.Gl2, a.v, a.k, a.q, a.Kt, a.mb, a.dq_i, a.scale, sl2, Hq, Hkv,
+                                      st, c, hq, L, gc, r0);
 }
 
 // The diagonal block of key block kb with exact per-pair decays (its gate
@@ -1565,8 +1641,8 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkv(BwdArgs a) {
 template <int DK, int DV>
 hipError_t launch_bwd_dk_dv(BwdKernel kind, bool f32in, const BwdArgs &a, dim3 grid, hipStream_t st) {
 #define FIX_BWD_LAUNCH(KERN)                                                                  \
-  if (f32in) hipLaunchKernelGGL((KERN<DK, DV, true>), grid, dim3(kind == BK_DQ || kind == BK_INTRA_DQ ? 256 : 512), 0, st, a); \
-  else hipLaunchKernelGGL((KERN<DK, DV, false>), grid, dim3(kind == BK_DQ || kind == BK_INTRA_DQ ? 256 : 512), 0, st, a);
+  if (f32in) hipLaunchKernelGGL((KERN<DK, DV, true>), grid, dim3(kind == BK_DQ ? 256 : 512), 0, st, a); \
+  else hipLaunchKernelGGL((KERN<DK, DV, false>), grid, dim3(kind == BK_DQ ? 256 : 512), 0, st, a);
   switch (kind) {
     case BK_INTRA_DQ: FIX_BWD_LAUNCH(k_bwd_intra_dq); break;
     case BK_INTRA_DKV: FIX_BWD_LAUNCH(k_bwd_intra_dkv); break;

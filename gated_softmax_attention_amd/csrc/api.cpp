@@ -106,7 +106,7 @@ struct BwdWs {
   double *Lam;
   _Float16 *Vr, *Kt, *VE, *Q16;
   __bf16 *VBH, *VBL;
-  float *delta;
+  float *prj;
   _Float16 *dh, *dhT, *X16;
   __bf16 *XH, *XL;
   float *mb, *sig, *qside, *dG, *dq_i, *dk_i, *dv_i, *dw_part, *dg_tot, *dg_carry;
@@ -150,7 +150,7 @@ size_t carve_bwd(Carve &cv, const fix_attn_desc *d, BwdWs &w) {
   w.Vr = cv.take<_Float16>(ncb * Hkv * fix::CB * DV);
   w.Q16 = cv.take<_Float16>(T * Hq * DK);
   w.Kt = cv.take<_Float16>(ncb * Hkv * DK * fix::CB);
-  w.delta = cv.take<float>(T * Hq * DV);
+  w.prj = cv.take<float>(T * Hq);
   w.dh = cv.take<_Float16>(T * Hq * DV);
   w.dhT = cv.take<_Float16>(ncb * Hq * DV * fix::CB);
   w.VE = cv.take<_Float16>(T * Hkv * DV);
@@ -436,7 +436,7 @@ fix_status fix_attn_bwd(const fix_attn_desc *d, const void *q, const void *k, co
   pa.o_norm = d->o_norm ? 1 : 0;
   pa.out_f32 = d->out_dtype == FIX_F32;
   pa.in_f32 = f32in;
-  pa.delta = w.delta; pa.dh = w.dh; pa.mb = w.mb; pa.sig = w.sig; pa.qside = w.qside;
+  pa.prj = w.prj; pa.dh = w.dh; pa.mb = w.mb; pa.sig = w.sig; pa.qside = w.qside;
   pa.dz = d_o_gate;
   pa.X16 = w.X16; pa.XH = w.XH; pa.XL = w.XL;
   pa.dw_part = want_dw ? w.dw_part : nullptr;
@@ -445,7 +445,9 @@ fix_status fix_attn_bwd(const fix_attn_desc *d, const void *q, const void *k, co
   fix::BwdArgs a;
   a.q = q; a.k = k; a.v = v;
   a.Gl2 = w.Gl2; a.Gam = w.Gam; a.Lam = w.Lam; a.Vr = w.Vr; a.Kt = w.Kt; a.Q16 = w.Q16;
-  a.delta = w.delta; a.dh = w.dh; a.dhT = w.dhT; a.mb = w.mb; a.sig = w.sig; a.qside = w.qside;
+  a.x = x; a.rstd = rstd; a.prj = w.prj; a.dO = d_o; a.z = o_gate; a.w = d->o_norm ? o_norm_weight : nullptr;
+  a.o_norm = d->o_norm ? 1 : 0;
+  a.dh = w.dh; a.dhT = w.dhT; a.mb = w.mb; a.sig = w.sig; a.qside = w.qside;
   a.VE = w.VE; a.VBH = w.VBH; a.VBL = w.VBL; a.X16 = w.X16; a.XH = w.XH; a.XL = w.XL;
   a.dq_i = w.dq_i; a.dk_i = w.dk_i; a.dv_i = w.dv_i;
   a.dq = dq; a.dk = dk; a.dv = dv; a.dG = w.dG;

@@ -40,26 +40,45 @@ constexpr float BGUARD = 100.f;  // largest factored gate range of a 32-token bl
 
 template <int D> struct Pad32 { static constexpr int value = D < 32 ? 32 : D; };
 
+// The gradient reaching x (delta) of element (row, d), row = token * Hq +
+// head, recomputed as the preprocess forms it (see bwd_prep.hip): dn = dO (.)
+// z, and with the norm delta = rstd (dn w - x rstd prj), prj the row's
+// stored projection.  Only the exact-decay paths below need it.
+struct DeltaSrc {
+  const float *x, *rstd, *prj;
+  const void *dO, *z, *w;
+  int o_norm;
+};
+template <int DV, bool F32IN> __device__ inline float delta_at(const DeltaSrc &s, int64_t row, int d) {
+  const int64_t i = row * DV + d;
+  const float dn = load_in(s.dO, i, F32IN) * (s.z ? load_in(s.z, i, F32IN) : 1.f);
+  if (!s.o_norm) return dn;
+  const float rs = s.rstd[row], wv = s.w ? load_in(s.w, d, F32IN) : 1.f;
+  return rs * (dn * wv - s.x[i] * rs * s.prj[row]);
+}
+
 // Exact per-pair decays for a diagonal 32x32 block whose gate range exceeds
 // 2^BGUARD (rare): dP for the pairs held by this lane, evaluated directly.
 // Register j of lane (hh, n) holds the pair (row q0 + rowof(j, n), key k0 + keyof(j, n)).
 // (Arguments by value: passing the kernel's argument struct by reference
 // would force a stack copy of it in every kernel that can call this.)
 template <int DV, bool F32IN, bool ROW_IS_LANE>
-__device__ __noinline__ void direct_dp(const float *delta, const float *sig, const float *Gl2, const void *v, int Hq,
-                                       int Hkv, int64_t st, int c, int h, int L, int q0, int k0, int hh, int n,
-                                       float *dp) {
+__device__ __noinline__ void direct_dp(const float *x, const float *rstd, const float *prj, const void *dO,
+                                       const void *z, const void *w, int o_norm, const float *sig, const float *Gl2,
+                                       const void *v, int Hq, int Hkv, int64_t st, int c, int h, int L, int q0, int k0,
+                                       int hh, int n, float *dp) {
+  const DeltaSrc ds{x, rstd, prj, dO, z, w, o_norm};
   for (int j = 0; j < 16; ++j) {
     const int r = ROW_IS_LANE ? n : acc_row(hh, j);
     const int kk = ROW_IS_LANE ? acc_row(hh, j) : n;
     const int qi = q0 + r, kj = k0 + kk;
     float t = 0.f;
     if (qi < L && kj <= qi) {
-      const float *dr = delta + ((st + qi) * Hq + h) * DV;
-      const float sg = sig[(st + qi) * Hq + h];
+      const int64_t row = (st + qi) * Hq + h;
+      const float sg = sig[row];
       for (int d = 0; d < DV; ++d) {
         const float gq = Gl2[((st + qi) * Hkv + c) * DV + d], gk = Gl2[((st + kj) * Hkv + c) * DV + d];
-        t += dr[d] * sg * fast_exp2(gq - gk) * load_in(v, ((st + kj) * Hkv + c) * DV + d, F32IN);
+        t += delta_at<DV, F32IN>(ds, row, d) * sg * fast_exp2(gq - gk) * load_in(v, ((st + kj) * Hkv + c) * DV + d, F32IN);
       }
     }
     dp[j] = t;
@@ -96,17 +115,18 @@ __device__ __noinline__ void direct_dp(const float *delta, const float *sig, con
 // lanes wrote them).  A function of its own so that the kernel's loops keep
 // their registers.
 template <int DK, int DV, bool F32IN>
-__device__ __noinline__ void near_exact_diag_dq(const float *delta, const float *sig, const float *Gl2, const void *v,
-                                                const void *kp, const void *qp, const _Float16 *Kt, const float *mb,
-                                                float *dq_i, float scale, float sl2, int Hq, int Hkv, int64_t st, int c,
-                                                int hq, int L, int gc, int r0) {
+__device__ __noinline__ void near_exact_diag_dq(const float *x, const float *rstd, const float *prj, const void *dO,
+                                                const void *z, const void *w, int o_norm, const float *sig,
+                                                const float *Gl2, const void *v, const void *kp, const void *qp,
+                                                const _Float16 *Kt, const float *mb, float *dq_i, float scale, float sl2,
+                                                int Hq, int Hkv, int64_t st, int c, int hq, int L, int gc, int r0) {
   using IF = InFrag<F32IN>;
   constexpr int NS = DK / 16, NBK = Pad32<DK>::value / 32;
   const int lane = threadIdx.x & 63, hh = lane >> 5, n = lane & 31;
   const int row = r0 + n, kb = r0;
   const int key = min(kb + n, L - 1), qrow = min(row, L - 1);
   float t[16];
-  direct_dp<DV, F32IN, true>(delta, sig, Gl2, v, Hq, Hkv, st, c, hq, L, r0, kb, hh, n, t);
+  direct_dp<DV, F32IN, true>(x, rstd, prj, dO, z, w, o_norm, sig, Gl2, v, Hq, Hkv, st, c, hq, L, r0, kb, hh, n, t);
   // S^T[key][row]: lane = row, register j = key acc_row(hh, j)
   f32x16 sc = zero16();
 #pragma unroll
@@ -412,8 +432,8 @@ __global__ void __launch_bounds__(512, 1) k_bwd_intra_dq(BwdArgs a) {
   // Diagonal block with exact per-pair decays (gate range beyond 2^BGUARD),
   // added to the stored rows.  (Otherwise the staged loop did it.)
   if (direct)
-    near_exact_diag_dq<DK, DV, F32IN>(a.delta, a.sig, a.Gl2, a.v, a.k, a.q, a.Kt, a.mb, a.dq_i, a.scale, sl2, Hq, Hkv,
-                                      st, c, hq, L, gc, r0);
+    near_exact_diag_dq<DK, DV, F32IN>(a.x, a.rstd, a.prj, a.dO, a.z, a.w, a.o_norm, a.sig, a.Gl2, a.v, a.k, a.q, a.Kt,
+                                      a.mb, a.dq_i, a.scale, sl2, Hq, Hkv, st, c, hq, L, gc, r0);
 }
 
 // The diagonal block of key block kb with exact per-pair decays (its gate
@@ -422,10 +442,12 @@ __global__ void __launch_bounds__(512, 1) k_bwd_intra_dq(BwdArgs a) {
 // lanes wrote them), dV goes straight into the within-chunk partial.  A
 // function of its own so that the kernel's loops keep their registers.
 template <int DK, int DV, bool F32IN>
-__device__ __noinline__ void near_exact_diag(const float *delta, const float *sig, const float *Gl2, const void *v,
-                                             const void *kp, const _Float16 *Q16, const float *mb, float *dv_i,
-                                             float *dk_i, float scale, float sl2, int Hq, int Hkv, int G, int64_t st,
-                                             int c, int L, int kb) {
+__device__ __noinline__ void near_exact_diag(const float *x, const float *rstd, const float *prj, const void *dO,
+                                             const void *z, const void *w, int o_norm, const float *sig,
+                                             const float *Gl2, const void *v, const void *kp, const _Float16 *Q16,
+                                             const float *mb, float *dv_i, float *dk_i, float scale, float sl2, int Hq,
+                                             int Hkv, int G, int64_t st, int c, int L, int kb) {
+  const DeltaSrc ds{x, rstd, prj, dO, z, w, o_norm};
   using IF = InFrag<F32IN>;
   using kfrag = typename IF::type;
   constexpr int NS = DK / 16, NBK = Pad32<DK>::value / 32, NBV = Pad32<DV>::value / 32;
@@ -438,7 +460,7 @@ __device__ __noinline__ void near_exact_diag(const float *delta, const float *si
   for (int gq = 0; gq < G; ++gq) {
     const int h = c * G + gq;
     float dpe[16];
-    direct_dp<DV, F32IN, false>(delta, sig, Gl2, v, Hq, Hkv, st, c, h, L, q0, kb, hh, n, dpe);
+    direct_dp<DV, F32IN, false>(x, rstd, prj, dO, z, w, o_norm, sig, Gl2, v, Hq, Hkv, st, c, h, L, q0, kb, hh, n, dpe);
     f32x16 sc = zero16();
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
@@ -479,7 +501,7 @@ __device__ __noinline__ void near_exact_diag(const float *delta, const float *si
           const float pvv = __shfl(pj, kl + 32 * hsrc);
           const int kj = kb + kl;
           if (col < DV && qk < L && kj <= qk)
-            t[j] += pvv * fast_exp2(gl_at(qk, col) - gl_at(kj, col)) * delta[((st + qk) * Hq + h) * DV + col] *
+            t[j] += pvv * fast_exp2(gl_at(qk, col) - gl_at(kj, col)) * delta_at<DV, F32IN>(ds, (st + qk) * Hq + h, col) *
                     sig[(st + qk) * Hq + h];
         }
       }
@@ -929,8 +951,8 @@ __global__ void __launch_bounds__(512, 1) k_bwd_intra_dkv(BwdArgs a) {
   // before the block, gamma = exp2(E(p-1) - E(p)) >= 1, V from the token
   // before the block as bf16x3.)
   if (!isA && direct && active)
-    near_exact_diag<DK, DV, F32IN>(a.delta, a.sig, a.Gl2, a.v, a.k, a.Q16, a.mb, a.dv_i, a.dk_i, a.scale, sl2, Hq, Hkv, G,
-                                   st, c, L, kb);
+    near_exact_diag<DK, DV, F32IN>(a.x, a.rstd, a.prj, a.dO, a.z, a.w, a.o_norm, a.sig, a.Gl2, a.v, a.k, a.Q16, a.mb,
+                                   a.dv_i, a.dk_i, a.scale, sl2, Hq, Hkv, G, st, c, L, kb);
   if (direct_any) __syncthreads();  // B's exact diagonal dV partials are written
   if (!active || !isA) return;
   // dv relative to the last query block's gamma: exp2(E(qlast - 1) - Gl_j).  Each

@@ -16,7 +16,9 @@
 // exp2(s log2e - (m log2e - e_i)) = P_ij / sigma_i, so every product of a
 // probability with a scaled dhat is unchanged.  The gate's own gradient
 // needs, per kv head, sum over the group's q heads of delta (.) x (the query
-// side of dG).
+// side of dG).  delta itself is not stored: the rare exact-decay paths of the
+// backward recompute it from dO, z, w, x, r and the row's projection
+// mean_d(dn (.) w (.) xh), which is stored.
 #include "common.h"
 #include "launch.h"
 
@@ -355,7 +357,6 @@ __global__ void __launch_bounds__(256) k_bwd_prep(PrepArgs a) {
 #pragma unroll
               for (int i = 0; i < 8; ++i) dwacc[i] += dn[i] * xv[k][i] * rs[k];
             if (a.dz) store8(a.dz, rb, dzv, a.out_f32);
-            store8f(a.delta, rb, del);
             store8f(a.qside, gi, qs);
             store8h(a.dh, rb, hv);
             store8h(a.X16, rb, x16);
@@ -364,6 +365,7 @@ __global__ void __launch_bounds__(256) k_bwd_prep(PrepArgs a) {
             if (sub == 0) {
               a.mb[tok * Hq + h] = mrow[k] * LOG2E - (float)e;
               a.sig[tok * Hq + h] = sg;
+              if (o_norm) a.prj[tok * Hq + h] = proj;
             }
           }
         }

@@ -98,7 +98,12 @@ struct BwdArgs {
   const _Float16 *Vr;          // [chunk][Hkv][CB][DV] V scaled to its chunk end
   const _Float16 *Kt;          // [chunk][Hkv][DK][CB] transposed fp16 K tiles (key_pos order)
   const _Float16 *Q16;         // [T, Hq, DK] q as fp16 (exact for |q| in [2^-14, 65504])
-  const float *delta;          // [T, Hq, DV] gradient reaching x
+  // what the gradient reaching x (delta) is recomputed from, element by
+  // element, where the exact-decay paths need it (the preprocess keeps only
+  // its scaled fp16 forms): x, rstd, the row projection prj, dO, z, w
+  const float *x, *rstd, *prj;
+  const void *dO, *z, *w;
+  int o_norm;
   const _Float16 *dh;          // [T, Hq, DV] sigma * exp(Gl) * delta
   const _Float16 *dhT;         // [chunk][Hq][DV][CB] the same as transposed tiles (key_pos order)
   const float *mb, *sig;       // [T, Hq] m log2e - e, sigma = 2^-e
@@ -124,7 +129,7 @@ struct PrepArgs {
   Plan plan;
   int Hq, Hkv;
   int o_norm, out_f32, in_f32;
-  float *delta;        // [Ttot, Hq, DV] fp32
+  float *prj;          // [Ttot, Hq] the row projection of the norm's backward (o_norm only)
   _Float16 *dh;        // [Ttot, Hq, DV] fp16, sigma * exp(Gl) * delta
   float *mb;           // [Ttot, Hq] m log2e - e
   float *sig;          // [Ttot, Hq] sigma = 2^-e

@@ -167,7 +167,7 @@ size_t carve_bwd(Carve &cv, const fix_attn_desc *d, BwdWs &w) {
   w.dk_i = cv.take<float>(T * Hkv * DK);
   w.dv_i = cv.take<float>(T * Hkv * DV);
   w.dw_part = cv.take<float>(ncb * Hkv * DV);
-  w.dg_tot = cv.take<float>(ncb * Hkv * DV);
+  w.dg_tot = cv.take<float>(ncb * Hkv * 4 * DV);
   w.dg_carry = cv.take<float>(ncb * Hkv * DV);
   return cv.off;
 }
@@ -450,7 +450,7 @@ fix_status fix_attn_bwd(const fix_attn_desc *d, const void *q, const void *k, co
   a.dh = w.dh; a.dhT = w.dhT; a.mb = w.mb; a.sig = w.sig; a.qside = w.qside;
   a.VE = w.VE; a.VBH = w.VBH; a.VBL = w.VBL; a.X16 = w.X16; a.XH = w.XH; a.XL = w.XL;
   a.dq_i = w.dq_i; a.dk_i = w.dk_i; a.dv_i = w.dv_i;
-  a.dq = dq; a.dk = dk; a.dv = dv; a.dG = w.dG;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dG = w.dG; a.dg_tot = w.dg_tot;
   a.plan = w.plan;
   a.Hq = Hq; a.Hkv = Hkv;
   a.sl2 = scale * fix::LOG2E;

@@ -1577,6 +1577,11 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkv(BwdArgs a) {
     __syncthreads();  // A's last P is in LDS
     if (nsteps > 0) dk_step((nsteps - 1) & 1, (nsteps - 1) % 3);
   }
+  // A waves of key blocks past the end: zero partial sums of dG (below)
+  if (isA && kb >= L) {
+    for (int d = lane; d < DV; d += 64) a.dg_tot[(((int64_t)gci * Hkv + c) * 4 + pr) * DV + d] = 0.f;
+    return;
+  }
   if (kb >= L) return;
   // epilogue: dk (B), dv (A; inter part scaled to the key: exp(Gl_end(J) -
   // Gl_key) and by gamma_{J+2,J}), dG = qside - v (.) dv.  Addresses are the
@@ -1642,6 +1647,11 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkv(BwdArgs a) {
       x[3][j] = buf_ld_in(rv, o, F32IN);
     }
   };
+  // the key block's column sums of dG (its 32 keys, in a fixed order) go to
+  // the reverse scan that forms dg
+  float dgs[NBV];
+#pragma unroll
+  for (int bv = 0; bv < NBV; ++bv) dgs[bv] = 0.f;
   load_dv(0, in[0]);
 #pragma unroll
   for (int u = 0; u < 2 * NBV; ++u) {
@@ -1654,9 +1664,17 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkv(BwdArgs a) {
           const uint32_t o = krow(h8 + j) * DV + col;
           const float(&x)[4][8] = in[u & 1];
           const float dvv = fast_exp2(gend[bv] - x[0][j]) * acc[bv][h8 + j] + x[1][j];
+          const float dgv = x[2][j] - x[3][j] * dvv;
           buf_st_out(rdv, o, dvv, a.out_f32);
-          buf_st_f32(rdg, 4 * o, x[2][j] - x[3][j] * dvv);
+          buf_st_f32(rdg, 4 * o, dgv);
+          dgs[bv] += dgv;
         }
+  }
+#pragma unroll
+  for (int bv = 0; bv < NBV; ++bv) {
+    const float t = dgs[bv] + __shfl_xor(dgs[bv], 32);
+    const int col = 32 * bv + ne;
+    if (hhe == 0 && col < DV) a.dg_tot[(((int64_t)gci * Hkv + c) * 4 + pr) * DV + col] = t;
   }
 }
 

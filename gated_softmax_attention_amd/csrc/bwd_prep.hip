@@ -413,27 +413,10 @@ __global__ void __launch_bounds__(1024) k_dw_reduce(const float *__restrict__ pa
 }
 
 // dg_t = sum over t' >= t of the same sequence of dG_t' (the gate enters
-// through G_t = sum_{u<=t} g_u).  Three passes over 128-chunks: chunk
-// totals, exclusive suffix carries per sequence, then in-chunk suffix sums.
-template <int DV>
-__global__ void __launch_bounds__(128) k_dg_totals(const float *__restrict__ dG, Plan plan, int Hkv,
-                                                   float *__restrict__ tot) {
-  const int gc = blockIdx.x, c = blockIdx.y, d = threadIdx.x;
-  if (gc >= plan.counts[0] || d >= DV) return;
-  const int s = seq_of_chunk(plan.cb128, plan.nseq, gc);
-  const int t0 = (gc - plan.cb128[s]) * CB;
-  const int n = min(CB, plan.seq_len[s] - t0);
-  const int64_t tok0 = (int64_t)plan.seq_start[s] + t0;
-  // fixed trip count, masked, so that the loads are issued together
-  float acc = 0.f;
-#pragma unroll 32
-  for (int j = 0; j < CB; ++j) {
-    const float x = dG[((tok0 + min(j, n - 1)) * Hkv + c) * DV + d];
-    acc += j < n ? x : 0.f;
-  }
-  tot[((int64_t)gc * Hkv + c) * DV + d] = acc;
-}
-
+// through G_t = sum_{u<=t} g_u).  Two passes over 128-chunks: exclusive
+// suffix carries per sequence (from the chunk totals, which the dk/dv
+// kernel leaves as four 32-key partial sums per chunk, added here in a fixed
+// order), then in-chunk suffix sums.
 template <int DV>
 __global__ void __launch_bounds__(128) k_dg_carry(const float *__restrict__ tot, Plan plan, int Hkv,
                                                   float *__restrict__ carry) {
@@ -442,8 +425,9 @@ __global__ void __launch_bounds__(128) k_dg_carry(const float *__restrict__ tot,
   float run = 0.f;
   for (int gc = plan.cb128[s + 1] - 1; gc >= plan.cb128[s]; --gc) {
     const int64_t idx = ((int64_t)gc * Hkv + c) * DV + d;
+    const float *t4 = tot + ((int64_t)gc * Hkv + c) * 4 * DV + d;
     carry[idx] = run;
-    run += tot[idx];
+    run += ((t4[0] + t4[DV]) + t4[2 * DV]) + t4[3 * DV];
   }
 }
 
@@ -575,11 +559,8 @@ hipError_t launch_bwd_prep(int dv, const PrepArgs &a, int ncb_ub, hipStream_t st
 hipError_t launch_dg_scan(int dv, const float *dG, const float *logits, const Plan &plan, int Hkv, int ncb_ub,
                           float *tot, float *carry, float *dg, hipStream_t st) {
   dim3 grid(ncb_ub, Hkv), gs(plan.nseq, Hkv);
-  FIX_DV_SWITCH(dv, hipLaunchKernelGGL(k_dg_totals<DVC>, grid, dim3(128), 0, st, dG, plan, Hkv, tot));
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   FIX_DV_SWITCH(dv, hipLaunchKernelGGL(k_dg_carry<DVC>, gs, dim3(128), 0, st, tot, plan, Hkv, carry));
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (logits)
     FIX_DV_SWITCH(dv, hipLaunchKernelGGL((k_dg_final<DVC, true>), grid, dim3(128), 0, st, dG, carry, logits, plan,

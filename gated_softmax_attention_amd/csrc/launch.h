@@ -117,6 +117,7 @@ struct BwdArgs {
   float *dq_i, *dk_i, *dv_i;   // within-chunk contributions (fp32)
   void *dq, *dk, *dv;          // outputs (out dtype)
   float *dG;                   // [T, Hkv, DV] gradient with respect to the prefix sums of g
+  float *dg_tot;               // [chunk][Hkv][4][DV] dG summed over each 32-key block of the chunk
   Plan plan;
   int Hq, Hkv;
   float sl2, scale;

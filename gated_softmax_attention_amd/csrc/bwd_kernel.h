@@ -328,7 +328,7 @@ __global__ void __launch_bounds__(512, 1) k_bwd_intra_dq(BwdArgs a) {
       for (int j = 0; j < 16; ++j) pv[j] = diag && acc_row(hh, j) > n ? 0.f : fast_exp2(sc[j] * sl2 - mbn);
 #pragma unroll
       for (int j4 = 0; j4 < 4; ++j4)
-        *(__attribute__((address_space(3))) f32x4 *)lds_at(apx_ + (b & 1) * 4 * PX + 1024 * j4) =
+        *(__attribute__((address_space(3))) f32x4 *)(lds_at(apx_ + (b & 1) * 4 * PX) + 1024 * j4) =
             f32x4{pv[4 * j4], pv[4 * j4 + 1], pv[4 * j4 + 2], pv[4 * j4 + 3]};
     }
     wait_all();
@@ -357,7 +357,7 @@ __global__ void __launch_bounds__(512, 1) k_bwd_intra_dq(BwdArgs a) {
     f16x8 dsf[2];
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) {
-      const f32x4 pq = *(const __attribute__((address_space(3))) f32x4 *)lds_at(apx_ + (bb & 1) * 4 * PX + 1024 * j4);
+      const f32x4 pq = *(const __attribute__((address_space(3))) f32x4 *)(lds_at(apx_ + (bb & 1) * 4 * PX) + 1024 * j4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int j = 4 * j4 + e;
@@ -389,10 +389,10 @@ __global__ void __launch_bounds__(512, 1) k_bwd_intra_dq(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < NSV; ++i) {
         const uint32_t ai = opaque(av[i]) + so;
-        const bf16x8 vh = __builtin_bit_cast(bf16x8, lds_row16(ai + 2 * VT::BYTES));
-        const bf16x8 vl = __builtin_bit_cast(bf16x8, lds_row16(ai + 4 * VT::BYTES));
-        const bf16x8 xh = __builtin_bit_cast(bf16x8, lds_row16(ai + 6 * VT::BYTES));
-        const bf16x8 xl = __builtin_bit_cast(bf16x8, lds_row16(ai + 8 * VT::BYTES));
+        const bf16x8 vh = __builtin_bit_cast(bf16x8, lds_row16p(lds_at(ai) + 2 * VT::BYTES));
+        const bf16x8 vl = __builtin_bit_cast(bf16x8, lds_row16p(lds_at(ai) + 4 * VT::BYTES));
+        const bf16x8 xh = __builtin_bit_cast(bf16x8, lds_row16p(lds_at(ai) + 6 * VT::BYTES));
+        const bf16x8 xl = __builtin_bit_cast(bf16x8, lds_row16p(lds_at(ai) + 8 * VT::BYTES));
         dp = mma32(vh, xh, dp);
         dp = mma32(vh, xl, dp);
         dp = mma32(vl, xh, dp);
@@ -755,7 +755,7 @@ __global__ void __launch_bounds__(512, 1) k_bwd_intra_dkv(BwdArgs a) {
       f32x4 mq[4];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4)
-        mq[q4] = *(const __attribute__((address_space(3))) f32x4 *)lds_at(sbase + O_M + (k & 1) * 256 + 4 * (8 * q4 + 4 * hh));
+        mq[q4] = *(const __attribute__((address_space(3))) f32x4 *)(lds_at(sbase + O_M + 16 * hh + (k & 1) * 256) + 32 * q4);
       // S[q][key]: lane = key, register j = query acc_row(hh, j)
       f32x16 sc = zero16();
       {
@@ -789,7 +789,7 @@ __global__ void __launch_bounds__(512, 1) k_bwd_intra_dkv(BwdArgs a) {
       }
 #pragma unroll
       for (int j4 = 0; j4 < 4; ++j4)
-        *(__attribute__((address_space(3))) f32x4 *)lds_at(apx_ + (k & 1) * 4 * PX + 1024 * j4) =
+        *(__attribute__((address_space(3))) f32x4 *)(lds_at(apx_ + (k & 1) * 4 * PX) + 1024 * j4) =
             f32x4{pv[4 * j4], pv[4 * j4 + 1], pv[4 * j4 + 2], pv[4 * j4 + 3]};
       // dV[key][d] += sum_q P[q][key] dhat[q][d] (bf16x3), output blocks
       // interleaved; the transposing reads of a k slice run one slice ahead
@@ -801,8 +801,8 @@ __global__ void __launch_bounds__(512, 1) k_bwd_intra_dkv(BwdArgs a) {
           for (int bv = 0; bv < NBV; ++bv)
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-              th[s2][bv][t] = lds_tr8(opaque(adv[bv][t]) + so + 16 * u * RX);
-              tl[s2][bv][t] = lds_tr8(opaque(adv[bv][t]) + so + 16 * u * RX + 2 * XR::BYTES);
+              th[s2][bv][t] = lds_tr8p(lds_at(opaque(adv[bv][t]) + so) + 16 * u * RX);
+              tl[s2][bv][t] = lds_tr8p(lds_at(opaque(adv[bv][t]) + so) + 16 * u * RX + 2 * XR::BYTES);
             }
         };
         rd(0, 0);
@@ -870,7 +870,7 @@ __global__ void __launch_bounds__(512, 1) k_bwd_intra_dkv(BwdArgs a) {
 #pragma unroll
         for (int bk = 0; bk < NBK; ++bk)
 #pragma unroll
-          for (int t = 0; t < 2; ++t) tq[u][bk][t] = lds_tr8(opaque(aqt[bk][t]) + so + 16 * u * RQ);
+          for (int t = 0; t < 2; ++t) tq[u][bk][t] = lds_tr8p(lds_at(opaque(aqt[bk][t]) + so) + 16 * u * RQ);
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -893,10 +893,10 @@ __global__ void __launch_bounds__(512, 1) k_bwd_intra_dkv(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < NSV; ++i) {
           const uint32_t ai = opaque(ax[i]) + so;
-          const bf16x8 xh = __builtin_bit_cast(bf16x8, lds_row16(ai + 2 * XR::BYTES));
-          const bf16x8 xl = __builtin_bit_cast(bf16x8, lds_row16(ai + 4 * XR::BYTES));
-          const bf16x8 vh = __builtin_bit_cast(bf16x8, lds_row16(ai + 6 * XR::BYTES));
-          const bf16x8 vl = __builtin_bit_cast(bf16x8, lds_row16(ai + 8 * XR::BYTES));
+          const bf16x8 xh = __builtin_bit_cast(bf16x8, lds_row16p(lds_at(ai) + 2 * XR::BYTES));
+          const bf16x8 xl = __builtin_bit_cast(bf16x8, lds_row16p(lds_at(ai) + 4 * XR::BYTES));
+          const bf16x8 vh = __builtin_bit_cast(bf16x8, lds_row16p(lds_at(ai) + 6 * XR::BYTES));
+          const bf16x8 vl = __builtin_bit_cast(bf16x8, lds_row16p(lds_at(ai) + 8 * XR::BYTES));
           dp = mma32(xh, vh, dp);
           dp = mma32(xl, vh, dp);
           dp = mma32(xh, vl, dp);
@@ -1144,7 +1144,7 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdArgs a) {
       // ahead (the chunk's gamma vectors first)
       f16x8 gv[NSV];
 #pragma unroll
-      for (int i = 0; i < NSV; ++i) gv[i] = lds_row16(ag + go + 2 * 16 * i);
+      for (int i = 0; i < NSV; ++i) gv[i] = lds_row16p(lds_at(ag + go) + 2 * 16 * i);
       f32x16 sc = zero16(), dp = zero16();
       constexpr int NM = NS > NSV ? NS : NSV;
       kfrag fk[NM];
@@ -1414,7 +1414,7 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkv(BwdArgs a) {
     for (int i = 0; i < NKS; ++i)
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
-        if (SAME || i < n1) fr[i][h2] = lds_row16(a1[i] + so1 + 32 * h2 * rb1);
+        if (SAME || i < n1) fr[i][h2] = lds_row16p(lds_at(a1[i] + so1) + 32 * h2 * rb1);
     xr[0] = xr[1] = zero16();
 #pragma unroll
     for (int i = 0; i < NKS; ++i)
@@ -1468,12 +1468,12 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkv(BwdArgs a) {
         f32x4 mq[4];
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
-          mq[q4] = *(const __attribute__((address_space(3))) f32x4 *)lds_at(ams_ + b * 256 + 4 * (32 * h2 + 8 * q4));
+          mq[q4] = *(const __attribute__((address_space(3))) f32x4 *)(lds_at(ams_ + b * 256) + 4 * (32 * h2 + 8 * q4));
 #pragma unroll
         for (int j = 0; j < 16; ++j) pf[h2][j >> 3][j & 7] = (_Float16)fast_exp2(xr[h2][j] * sl2 - mq[j >> 2][j & 3]);
 #pragma unroll
         for (int u = 0; u < 2; ++u)
-          *(__attribute__((address_space(3))) f16x8 *)lds_at(apx_ + b * 4 * PEX + 16 * 64 * (2 * h2 + u)) = pf[h2][u];
+          *(__attribute__((address_space(3))) f16x8 *)(lds_at(apx_ + b * 4 * PEX) + 16 * 64 * (2 * h2 + u)) = pf[h2][u];
       }
       // the row copies of the next step (their stages were last read in step k - 1)
       if (k + 1 < nsteps) stage_rows(nxt, (k + 1) % 3, b ^ 1);
@@ -1530,7 +1530,7 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkv(BwdArgs a) {
       f16x8 dsp[2][2];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const f16x8 p = *(const __attribute__((address_space(3))) f16x8 *)lds_at(apx_ + pb * 4 * PEX + 16 * 64 * g);
+        const f16x8 p = *(const __attribute__((address_space(3))) f16x8 *)(lds_at(apx_ + pb * 4 * PEX) + 16 * 64 * g);
 #pragma unroll
         for (int i = 0; i < 8; ++i) dsp[g >> 1][g & 1][i] = (_Float16)((float)p[i] * dpk[g >> 1][8 * (g & 1) + i]);
       }
@@ -1540,7 +1540,7 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkv(BwdArgs a) {
 #pragma unroll
       for (int m = 0; m < NM; ++m)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) tp[m][t] = lds_tr8(a2[m % NBK][t] + off + 16 * (m / NBK) * (2 * DK));
+        for (int t = 0; t < 2; ++t) tp[m][t] = lds_tr8p(lds_at(a2[m % NBK][t] + off) + 16 * (m / NBK) * (2 * DK));
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
         const int g = m / NBK;

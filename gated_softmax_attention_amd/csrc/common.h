@@ -250,6 +250,13 @@ __device__ inline f16x4 lds_tr8(uint32_t a) {
   return __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                                        (__attribute__((address_space(3))) s16x4 *)(uintptr_t)a));
 }
+// The same from an LDS pointer: a constant added to the pointer (rather than
+// to the integer address) folds into the instruction's offset field, where
+// an integer sum costs a vector add per read.
+__device__ inline f16x8 lds_row16p(const lds_char *p) { return *(const __attribute__((address_space(3))) f16x8 *)p; }
+__device__ inline f16x4 lds_tr8p(const lds_char *p) {
+  return __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)p));
+}
 // A value the compiler must treat as changed here: keeps it from hoisting
 // base + constant address sums out of a loop as registers of their own (the
 // constant then folds into each instruction's offset field).

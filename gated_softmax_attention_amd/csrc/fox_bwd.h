@@ -372,7 +372,7 @@ __global__ void __launch_bounds__(512, 1) k_fox_bwd_dkv(FoxBwdArgs a) {
       const int hu = m / NBA, b = m % NBA;
       if (SAME || b < n2)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) tp[m][t] = lds_tr8(a2[b][t] + off + 16 * hu * rb2);
+        for (int t = 0; t < 2; ++t) tp[m][t] = lds_tr8p(lds_at(a2[b][t] + off) + 16 * hu * rb2);
     }
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
@@ -401,7 +401,7 @@ __global__ void __launch_bounds__(512, 1) k_fox_bwd_dkv(FoxBwdArgs a) {
     for (int i = 0; i < NKS; ++i)
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
-        if (SAME || i < n1) fr[i][h2] = lds_row16(a1[i] + so1 + 32 * h2 * rb1);
+        if (SAME || i < n1) fr[i][h2] = lds_row16p(lds_at(a1[i] + so1) + 32 * h2 * rb1);
     xr[0] = xr[1] = zero16();
 #pragma unroll
     for (int i = 0; i < NKS; ++i)
@@ -446,7 +446,7 @@ __global__ void __launch_bounds__(512, 1) k_fox_bwd_dkv(FoxBwdArgs a) {
           f32x4 tv[4];
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4)
-            tv[q4] = *(const __attribute__((address_space(3))) f32x4 *)lds_at(agq_ + 4 * (32 * h2 + 8 * q4));
+            tv[q4] = *(const __attribute__((address_space(3))) f32x4 *)(lds_at(agq_) + 4 * (32 * h2 + 8 * q4));
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
             f32x4 p4;
@@ -461,7 +461,7 @@ __global__ void __launch_bounds__(512, 1) k_fox_bwd_dkv(FoxBwdArgs a) {
               p4[e] = p;
               pf[h2][j >> 3][j & 7] = (_Float16)p;
             }
-            *(__attribute__((address_space(3))) f32x4 *)lds_at(apx_ + 16 * 64 * (h2 * 4 + q4)) = p4;
+            *(__attribute__((address_space(3))) f32x4 *)(lds_at(apx_) + 16 * 64 * (h2 * 4 + q4)) = p4;
           }
         }
       };
@@ -492,7 +492,7 @@ __global__ void __launch_bounds__(512, 1) k_fox_bwd_dkv(FoxBwdArgs a) {
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
-          p4[h2][q4] = *(const __attribute__((address_space(3))) f32x4 *)lds_at(apx_ + 16 * 64 * (h2 * 4 + q4));
+          p4[h2][q4] = *(const __attribute__((address_space(3))) f32x4 *)(lds_at(apx_) + 16 * 64 * (h2 * 4 + q4));
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll

@@ -39,6 +39,7 @@ namespace fix {
 constexpr float BGUARD = 100.f;  // largest factored gate range of a 32-token block (log2 units)
 
 template <int D> struct Pad32 { static constexpr int value = D < 32 ? 32 : D; };
+template <int V> struct IC { static constexpr int value = V; };  // a compile-time int argument
 
 // The gradient reaching x (delta) of element (row, d), row = token * Hq +
 // head, recomputed as the preprocess forms it (see bwd_prep.hip): dn = dO (.)
@@ -1130,18 +1131,21 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdArgs a) {
   }
   wait_vm<NCOPYQ>();  // step 0 has landed
   lds_barrier();
-  for (int k = 0; k < nsteps; ++k) {
-    const int b = uniform(k % NBQ);
+  // One step; its stage b = k % 3 is a compile-time constant (the loop
+  // below runs three steps per trip), so each LDS read's stage offset folds
+  // into the instruction's offset field.
+  auto step = [&](int k, auto bc) {
+    constexpr int b = decltype(bc)::value;
     const bool next_chunk = (k & 3) == 3 && k + 1 < nsteps;
     // Same copies on every step (past the last step, the last step's tile
     // again, into a stage nobody reads); step k + 2's stage was last read in
     // step k - 1.
-    stage_tile(min(k + 2, nsteps - 1), uniform((k + 2) % NBQ));
+    stage_tile(min(k + 2, nsteps - 1), (b + 2) % NBQ);
     {
-      const uint32_t ko = opaque(b * KT::BYTES), vo = opaque(b * VT::BYTES), to = opaque(b * TT::BYTES);
       const uint32_t go = opaque(((k >> 2) & 1) * DV * 2);
-      // S^T and dP^T, their chains alternating, operand reads four products
-      // ahead (the chunk's gamma vectors first)
+      // S^T and dP^T, their chains alternating, operand reads two products
+      // ahead (the chunk's gamma vectors first; four ahead made the
+      // three-step loop spill)
       f16x8 gv[NSV];
 #pragma unroll
       for (int i = 0; i < NSV; ++i) gv[i] = lds_row16p(lds_at(ag + go) + 2 * 16 * i);
@@ -1151,8 +1155,8 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdArgs a) {
       f16x8 fv[NM];
 #pragma unroll
       for (int i = 0; i < NM; ++i) {
-        if (i < NS) fk[i] = *(const __attribute__((address_space(3))) kfrag *)lds_at(ak[i] + ko);
-        if (i < NSV) fv[i] = lds_row16(av[i] + vo);
+        if (i < NS) fk[i] = *(const __attribute__((address_space(3))) kfrag *)(lds_at(ak[i]) + b * KT::BYTES);
+        if (i < NSV) fv[i] = lds_row16p(lds_at(av[i]) + b * VT::BYTES);
       }
 #pragma unroll
       for (int i = 0; i < NM; ++i) {
@@ -1160,7 +1164,7 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdArgs a) {
         if (i < NSV) dp = mma32(fv[i] * gv[i], dhf[i], dp);
       }
       {
-        constexpr int NP = NS + NSV, LA = NP < 4 ? NP : 4;
+        constexpr int NP = NS + NSV, LA = NP < 2 ? NP : 2;
         __builtin_amdgcn_sched_group_barrier(0x100, LA + NSV, 0);
 #pragma unroll
         for (int m = 0; m < NP - LA; ++m) {
@@ -1183,7 +1187,7 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdArgs a) {
 #pragma unroll
       for (int bk = 0; bk < NBK; ++bk)
 #pragma unroll
-        for (int u = 0; u < 2; ++u) tk[bk][u] = lds_row16(at[bk][u] + to);
+        for (int u = 0; u < 2; ++u) tk[bk][u] = lds_row16p(lds_at(at[bk][u]) + b * TT::BYTES);
 #pragma unroll
       for (int bk = 0; bk < NBK; ++bk)
 #pragma unroll
@@ -1206,6 +1210,11 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdArgs a) {
       gam(((k >> 2) + 1) & 1)[tid] = (_Float16)fast_exp2((float)(lamI - ((const double *)Ls(b))[tid]));
     wait_vm<NCOPYQ>();  // step k + 1 has landed (step k + 2's copies stay in flight)
     lds_barrier();
+  };
+  for (int k = 0; k < nsteps; k += NBQ) {
+    step(k, IC<0>{});
+    if (k + 1 < nsteps) step(k + 1, IC<1>{});
+    if (k + 2 < nsteps) step(k + 2, IC<2>{});
   }
   wait_all();  // copies issued past the last step
   // The block's inputs are loaded before any of its stores (the compiler

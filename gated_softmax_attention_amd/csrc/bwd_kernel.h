@@ -319,7 +319,7 @@ __global__ void __launch_bounds__(512, 1) k_bwd_intra_dq(BwdArgs a) {
         const uint32_t so = (b & 1) * KT::BYTES;
         kfrag fk[NS];
 #pragma unroll
-        for (int i = 0; i < NS; ++i) fk[i] = __builtin_bit_cast(kfrag, lds_row16(opaque(ak[i]) + so));
+        for (int i = 0; i < NS; ++i) fk[i] = __builtin_bit_cast(kfrag, lds_row16p(lds_at(ak[i]) + so));
 #pragma unroll
         for (int i = 0; i < NS; ++i) sc = mma32(fk[i], qf[i], sc);
       }
@@ -370,7 +370,7 @@ __global__ void __launch_bounds__(512, 1) k_bwd_intra_dq(BwdArgs a) {
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int bk = 0; bk < NBK; ++bk) tk[u][bk] = lds_row16(opaque(akt[bk][u]) + so);
+      for (int bk = 0; bk < NBK; ++bk) tk[u][bk] = lds_row16p(lds_at(akt[bk][u]) + so);
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -389,7 +389,7 @@ __global__ void __launch_bounds__(512, 1) k_bwd_intra_dq(BwdArgs a) {
       // split at the token before the block: V and dhat as bf16 hi / lo (bf16x3)
 #pragma unroll
       for (int i = 0; i < NSV; ++i) {
-        const uint32_t ai = opaque(av[i]) + so;
+        const uint32_t ai = av[i] + so;
         const bf16x8 vh = __builtin_bit_cast(bf16x8, lds_row16p(lds_at(ai) + 2 * VT::BYTES));
         const bf16x8 vl = __builtin_bit_cast(bf16x8, lds_row16p(lds_at(ai) + 4 * VT::BYTES));
         const bf16x8 xh = __builtin_bit_cast(bf16x8, lds_row16p(lds_at(ai) + 6 * VT::BYTES));
@@ -410,7 +410,7 @@ __global__ void __launch_bounds__(512, 1) k_bwd_intra_dq(BwdArgs a) {
       }
       f16x8 fv[NSV];
 #pragma unroll
-      for (int i = 0; i < NSV; ++i) fv[i] = lds_row16(opaque(av[i]) + so);
+      for (int i = 0; i < NSV; ++i) fv[i] = lds_row16p(lds_at(av[i]) + so);
 #pragma unroll
       for (int i = 0; i < NSV; ++i) dp = mma32(fv[i], rop[i] * *(const f16x8 *)(gw + 16 * i + 8 * hh), dp);
     }
@@ -763,7 +763,7 @@ __global__ void __launch_bounds__(512, 1) k_bwd_intra_dkv(BwdArgs a) {
         const uint32_t so = (k % 3) * QT::BYTES;
         f16x8 fq[NS];
 #pragma unroll
-        for (int i = 0; i < NS; ++i) fq[i] = lds_row16(opaque(aq[i]) + so);
+        for (int i = 0; i < NS; ++i) fq[i] = lds_row16p(lds_at(aq[i]) + so);
 #pragma unroll
         for (int i = 0; i < NS; ++i) sc = mma32(fq[i], kop[i], sc);
       }
@@ -802,8 +802,8 @@ __global__ void __launch_bounds__(512, 1) k_bwd_intra_dkv(BwdArgs a) {
           for (int bv = 0; bv < NBV; ++bv)
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-              th[s2][bv][t] = lds_tr8p(lds_at(opaque(adv[bv][t]) + so) + 16 * u * RX);
-              tl[s2][bv][t] = lds_tr8p(lds_at(opaque(adv[bv][t]) + so) + 16 * u * RX + 2 * XR::BYTES);
+              th[s2][bv][t] = lds_tr8p(lds_at(adv[bv][t]) + so + 16 * u * RX);
+              tl[s2][bv][t] = lds_tr8p(lds_at(adv[bv][t]) + so + 16 * u * RX + 2 * XR::BYTES);
             }
         };
         rd(0, 0);
@@ -871,7 +871,7 @@ __global__ void __launch_bounds__(512, 1) k_bwd_intra_dkv(BwdArgs a) {
 #pragma unroll
         for (int bk = 0; bk < NBK; ++bk)
 #pragma unroll
-          for (int t = 0; t < 2; ++t) tq[u][bk][t] = lds_tr8p(lds_at(opaque(aqt[bk][t]) + so) + 16 * u * RQ);
+          for (int t = 0; t < 2; ++t) tq[u][bk][t] = lds_tr8p(lds_at(aqt[bk][t]) + so + 16 * u * RQ);
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -893,7 +893,7 @@ __global__ void __launch_bounds__(512, 1) k_bwd_intra_dkv(BwdArgs a) {
         // split at the token before the block: dhat and V as bf16 hi / lo (bf16x3)
 #pragma unroll
         for (int i = 0; i < NSV; ++i) {
-          const uint32_t ai = opaque(ax[i]) + so;
+          const uint32_t ai = ax[i] + so;
           const bf16x8 xh = __builtin_bit_cast(bf16x8, lds_row16p(lds_at(ai) + 2 * XR::BYTES));
           const bf16x8 xl = __builtin_bit_cast(bf16x8, lds_row16p(lds_at(ai) + 4 * XR::BYTES));
           const bf16x8 vh = __builtin_bit_cast(bf16x8, lds_row16p(lds_at(ai) + 6 * XR::BYTES));
@@ -923,7 +923,7 @@ __global__ void __launch_bounds__(512, 1) k_bwd_intra_dkv(BwdArgs a) {
         }
         f16x8 fx[NSV];
 #pragma unroll
-        for (int i = 0; i < NSV; ++i) fx[i] = lds_row16(opaque(ax[i]) + so);
+        for (int i = 0; i < NSV; ++i) fx[i] = lds_row16p(lds_at(ax[i]) + so);
 #pragma unroll
         for (int i = 0; i < NSV; ++i) dp = mma32(fx[i], kg[i], dp);
       }

@@ -160,8 +160,14 @@ __device__ __noinline__ void near_exact_diag_dq(const float *x, const float *rst
   }
 }
 
+// Minimum waves per SIMD (HIP's second launch bound) of the 512-thread
+// kernels: at head dims up to 32 their LDS holds two workgroups per CU, i.e.
+// four waves per SIMD, which caps a wave at 128 VGPRs (a few registers more
+// leave one workgroup per CU); otherwise one.
+constexpr int small_head_waves(int dk, int dv) { return (dk <= 32 && dv <= 32) ? 4 : 1; }
+
 template <int DK, int DV, bool F32IN>
-__global__ void __launch_bounds__(512, 1) k_bwd_intra_dq(BwdArgs a) {
+__global__ void __launch_bounds__(512, small_head_waves(DK, DV)) k_bwd_intra_dq(BwdArgs a) {
   using IF = InFrag<F32IN>;
   using kfrag = typename IF::type;
   constexpr int NS = DK / 16, NSV = DV / 16, DKP = Pad32<DK>::value, NBK = DKP / 32;
@@ -1265,7 +1271,7 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dq(BwdArgs a) {
 // per column; the epilogue applies gamma_{J+2,J}.
 // ---------------------------------------------------------------------------
 template <int DK, int DV, bool F32IN>
-__global__ void __launch_bounds__(512, 1) k_bwd_dkv(BwdArgs a) {
+__global__ void __launch_bounds__(512, small_head_waves(DK, DV)) k_bwd_dkv(BwdArgs a) {
   using IF = InFrag<F32IN>;
   using kfrag = typename IF::type;
   constexpr int NS = DK / 16, NSV = DV / 16, DKP = Pad32<DK>::value, DVP = Pad32<DV>::value;

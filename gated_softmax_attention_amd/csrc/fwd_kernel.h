@@ -44,8 +44,13 @@ namespace fix {
 constexpr float TAU = 8.f;      // lazy max threshold (log2 units)
 constexpr float GUARD = 100.f;  // largest factored gate range of a diagonal block (log2 units)
 
+// Minimum waves per SIMD (HIP's second launch bound; one wave per SIMD per
+// workgroup here): three at head dim 64, whose LDS holds four workgroups per
+// CU (unbounded it took 179 VGPRs, two workgroups), two otherwise.
+constexpr int fwd_waves(int dk, int dv) { return (dk == 64 && dv == 64) ? 3 : 2; }
+
 template <int DK, int DV, bool F32IN>
-__global__ void __launch_bounds__(256, 2) k_fix_fwd(FwdArgs a) {
+__global__ void __launch_bounds__(256, fwd_waves(DK, DV)) k_fix_fwd(FwdArgs a) {
   using IF = InFrag<F32IN>;
   using kfrag = typename IF::type;
   constexpr int DVP = DV < 32 ? 32 : DV;  // output columns padded to whole 32-wide MFMA blocks

@@ -146,11 +146,12 @@ __global__ void __launch_bounds__(256, fwd_waves(DK, DV)) k_fix_fwd(FwdArgs a) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc[b][j] = 0.f;
   float m_used = -INFINITY;  // per row n, log2 units
-  // The exact row max lives in LDS (this wave's slot of row n; lanes n and
-  // n + 32 hold the same value): as a register it was spilled, and the
-  // reload's wait for vector memory also waited for the tile copies in flight.
-  // The slot address is formed where it is used, from the lane id, so that
-  // it is not a register kept (and spilled) across the loops either.
+  // The exact row max: a register through the far loop (m_far, one max per
+  // step), then an LDS slot through the nearest-key phase (this wave's slot of
+  // row n; lanes n and n + 32 hold the same value), where a register was
+  // spilled and the reload's wait for vector memory also waited for the copies
+  // in flight.  The slot address is formed where it is used, from the lane id,
+  // so that it is not a register kept (and spilled) across the loops either.
   const uint32_t mt_base = uniform((int)lds_addr(smem + O_A + 4 * 32 * 4)) + 128 * wave;
   auto mt_addr = [&]() {
     uint32_t z = 0;
@@ -163,7 +164,6 @@ __global__ void __launch_bounds__(256, fwd_waves(DK, DV)) k_fix_fwd(FwdArgs a) {
     asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(mt_addr()) : "memory");
     return v;
   };
-  mt_write(-INFINITY);
 
   // Multiply accumulator row r by the row factor held in lane r of this half-wave pair.
   auto row_scale = [&](float f) {
@@ -186,8 +186,8 @@ __global__ void __launch_bounds__(256, fwd_waves(DK, DV)) k_fix_fwd(FwdArgs a) {
     __builtin_amdgcn_wave_barrier();
   };
   // Fold a new row max (log2 units, identical in lanes n and n+32) into the running state.
-  auto update_max = [&](float mx) {
-    mt_write(fmaxf(mt_read(), mx));
+  // Lazy running max (the exact one is kept apart, see above).
+  auto raise_max = [&](float mx) {
     if (__any(mx > m_used + TAU)) {
       float m_new = fmaxf(m_used, mx);
       float alpha = fast_exp2(m_used - m_new);
@@ -203,6 +203,7 @@ __global__ void __launch_bounds__(256, fwd_waves(DK, DV)) k_fix_fwd(FwdArgs a) {
   };
 
   // ---------------- inter-chunk loop ----------------
+  float m_far = -INFINITY;
   if (nJ > 0) stage_tile(0, 0);
   wait_all();
   __syncthreads();
@@ -246,7 +247,8 @@ __global__ void __launch_bounds__(256, fwd_waves(DK, DV)) k_fix_fwd(FwdArgs a) {
     if (comp) {
       float mx = fmaxf(row_max(sc[0]), row_max(sc[1]));
       mx = max_across_halves(mx) * sl2;
-      update_max(mx);
+      m_far = fmaxf(m_far, mx);
+      raise_max(mx);
       f16x8 pf[4];
 #pragma unroll
       for (int be = 0; be < 2; ++be)
@@ -271,6 +273,7 @@ __global__ void __launch_bounds__(256, fwd_waves(DK, DV)) k_fix_fwd(FwdArgs a) {
     wait_all();
     __syncthreads();
   }
+  mt_write(m_far);
   // ---------------- nearest keys: the previous chunk and the own chunk ----------------
   // Key blocks of 32 from the first block of the chunk before the workgroup's
   // first chunk up to the block of its last rows, one per step.  Per block the
@@ -375,7 +378,9 @@ __global__ void __launch_bounds__(256, fwd_waves(DK, DV)) k_fix_fwd(FwdArgs a) {
 #pragma unroll
         for (int j = 0; j < 16; ++j)
           if (acc_row(hh, j) > n) s1[j] = -INFINITY;
-      update_max(max_across_halves(row_max(s1)) * sl2);
+      const float mx = max_across_halves(row_max(s1)) * sl2;
+      mt_write(fmaxf(mt_read(), mx));
+      raise_max(mx);
       float pv[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) pv[j] = fast_exp2(s1[j] * sl2 - m_used);

@@ -75,7 +75,8 @@ __global__ void __launch_bounds__(256, 2) k_fox_fwd(FoxArgs a) {
   using KT = LdsTile<CH, DK * 2>;  // K rows of a key block (bf16, or fp16 for fp32 inputs)
   using VT = LdsTile<CH, DV * 2>;  // V rows of a key block (fp16)
   constexpr int O_K = 0, O_V = O_K + 2 * KT::BYTES, O_G = O_V + 2 * VT::BYTES, O_R = O_G + 2 * 256;
-  __shared__ __align__(1024) char smem[O_R + 2 * 256];
+  constexpr int O_S = O_R + 2 * 256;  // per wave, the 32 row factors of a rescale
+  __shared__ __align__(1024) char smem[O_S + 4 * 32 * 4];
   auto Ks = [&](int b) { return smem + O_K + b * KT::BYTES; };
   auto Vs = [&](int b) { return smem + O_V + b * VT::BYTES; };
   auto Gk = [&](int b) { return (float *)(smem + O_G + b * 256); };  // the block's local prefixes
@@ -187,13 +188,27 @@ __global__ void __launch_bounds__(256, 2) k_fox_fwd(FoxArgs a) {
     mb = fmaxf(mb, __shfl_xor(mb, 32));
     const float mn = fmaxf(m, mb);
     if (__any(mn > m)) {
-      const float r = m == -INFINITY ? 0.f : fast_exp2(m - mn);
+      // row factors through LDS: lane n (hh = 0) writes its row's, every lane
+      // reads the four rows of each of its register groups as one float4 (one
+      // write and four reads where a shuffle per register took sixteen)
+      float *rs = (float *)(smem + O_S) + 32 * wave;
+      if (hh == 0) rs[n] = m == -INFINITY ? 0.f : fast_exp2(m - mn);
+      // a wave's LDS accesses complete in order: its own write is visible to
+      // its reads once it has completed
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_wave_barrier();
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float rj = __shfl(r, acc_row(hh, j));
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 r4 = *(const float4 *)(rs + 8 * q4 + 4 * hh);
 #pragma unroll
-        for (int bv = 0; bv < NB; ++bv) acc[bv][j] *= rj;
+        for (int bv = 0; bv < NB; ++bv) {
+          acc[bv][4 * q4 + 0] *= r4.x;
+          acc[bv][4 * q4 + 1] *= r4.y;
+          acc[bv][4 * q4 + 2] *= r4.z;
+          acc[bv][4 * q4 + 3] *= r4.w;
+        }
       }
+      __builtin_amdgcn_wave_barrier();
     }
     m = mn;
     f16x8 pf[2][2];

@@ -340,28 +340,41 @@ __global__ void __launch_bounds__(256, fwd_waves(DK, DV)) k_fix_fwd(FwdArgs a) {
       Gb[d] = fast_exp2(eb - ep);
     }
     __syncthreads();
-    // operand tiles: thread item (key r, 8 channels)
-    for (int it = tid; it < 32 * (DVP / 8); it += 256) {
-      const int r = it / (DVP / 8), c8 = 8 * (it % (DVP / 8));
-      bf16x8 eh, el, bh, bl;
+    // operand tiles: thread item (key r, 8 channels).  VE is read only by
+    // waves whose rows lie after the block (none after the last one), VB only
+    // on a wave's own block (the workgroup's blocks from a0 on); a tile no
+    // wave reads is not built.
+    const bool needE = bk < nb_hi, needB = bk >= a0;
+    auto build = [&](auto wantE, auto wantB) {
+      for (int it = tid; it < 32 * (DVP / 8); it += 256) {
+        const int r = it / (DVP / 8), c8 = 8 * (it % (DVP / 8));
+        bf16x8 eh, el, bh, bl;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = c8 + e;
-        float ve = 0.f, vb = 0.f;
-        if (d < DV) {
-          const float gl = ((const float *)ng)[r * DV + d];
-          const float vv = F32IN ? ((const float *)nv)[r * DV + d] : bf16_to_f32(((const uint16_t *)nv)[r * DV + d]);
-          ve = fast_exp2(Eb[d] - gl) * vv;
-          vb = fast_exp2(Ep[d] - gl) * vv;
+        for (int e = 0; e < 8; ++e) {
+          const int d = c8 + e;
+          float ve = 0.f, vb = 0.f;
+          if (d < DV) {
+            const float gl = ((const float *)ng)[r * DV + d];
+            const float vv = F32IN ? ((const float *)nv)[r * DV + d] : bf16_to_f32(((const uint16_t *)nv)[r * DV + d]);
+            if constexpr (decltype(wantE)::value) ve = fast_exp2(Eb[d] - gl) * vv;
+            if constexpr (decltype(wantB)::value) vb = fast_exp2(Ep[d] - gl) * vv;
+          }
+          if constexpr (decltype(wantE)::value) split_bf16(ve, eh, el, e);
+          if constexpr (decltype(wantB)::value) split_bf16(vb, bh, bl, e);
         }
-        split_bf16(ve, eh, el, e);
-        split_bf16(vb, bh, bl, e);
+        if constexpr (decltype(wantE)::value) {
+          *(bf16x8 *)(tEH + OT::off(r, c8 / 8)) = eh;
+          *(bf16x8 *)(tEL + OT::off(r, c8 / 8)) = el;
+        }
+        if constexpr (decltype(wantB)::value) {
+          *(bf16x8 *)(tBH + OT::off(r, c8 / 8)) = bh;
+          *(bf16x8 *)(tBL + OT::off(r, c8 / 8)) = bl;
+        }
       }
-      *(bf16x8 *)(tEH + OT::off(r, c8 / 8)) = eh;
-      *(bf16x8 *)(tEL + OT::off(r, c8 / 8)) = el;
-      *(bf16x8 *)(tBH + OT::off(r, c8 / 8)) = bh;
-      *(bf16x8 *)(tBL + OT::off(r, c8 / 8)) = bl;
-    }
+    };
+    if (needE && needB) build(std::true_type{}, std::true_type{});
+    else if (needE) build(std::true_type{}, std::false_type{});
+    else build(std::false_type{}, std::true_type{});
     __syncthreads();
     if (active && bk >= bmin_w && bk <= aw) {
       const bool diag = bk == aw;

@@ -286,12 +286,16 @@ template <class T> __device__ inline void tr_offsets(int col0, int lane, uint32_
 // own counts stay conservative when these are issued between its loads.  The
 // resource is given as its four descriptor words; m0 (the LDS base of the
 // copy, which must be the same in every lane: it is taken from the first
-// active lane, since the compiler cannot always prove it uniform) is saved
-// and restored around it.
+// active lane, since the compiler cannot always prove it uniform) is declared
+// clobbered, so the compiler keeps nothing there across the copy.
 // LDS byte address of a pointer into LDS.
 __device__ inline uint32_t lds_addr(const void *p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
 }
+// The same for a pointer known to be into LDS (never null): the low 32 bits of
+// its flat address, which is the LDS byte address (the generic-to-LDS cast
+// above adds only a null check, four scalar instructions per copy).
+__device__ inline uint32_t lds_low32(const void *p) { return (uint32_t)(uintptr_t)p; }
 __device__ inline u32x4 rsrc_words(const void *base, int64_t bytes) {
   const int nrec = (int)(bytes < 0 ? 0 : bytes > 0x7fffffffLL ? 0x7fffffffLL : bytes);
   const uint64_t b = (uint64_t)base;
@@ -300,14 +304,12 @@ __device__ inline u32x4 rsrc_words(const void *base, int64_t bytes) {
                (uint32_t)__builtin_amdgcn_readfirstlane(nrec), 0x00020000u};
 }
 __device__ inline void dma16_untracked(void *lds, const u32x4 &src, uint32_t o) {
-  uint32_t saved;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
-               : "=&s"(saved) : "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds))), "v"(o), "s"(src) : "memory");
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds_low32(lds))), "v"(o), "s"(src) : "memory", "m0");
 }
 __device__ inline void dma4_untracked(void *lds, const u32x4 &src, uint32_t o) {
-  uint32_t saved;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dword %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
-               : "=&s"(saved) : "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds))), "v"(o), "s"(src) : "memory");
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds_low32(lds))), "v"(o), "s"(src) : "memory", "m0");
 }
 
 template <int ROWS, int RB>

@@ -35,18 +35,18 @@ PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16/fp16 MFMA peak (AMD specification
 # x1.0 writes); valid only for the sources they were
 # taken on (sha256 prefix over the files listed, the build flags included).  Reported as roofline.traffic, else null.
 TRAFFIC = {
-    "bwd_dkv": {"bytes": int(2 * 1233130.19 * 1024 + 551048.50 * 1024), "sha": "9e33606e663e65f6",
+    "bwd_dkv": {"bytes": int(2 * 1221795.38 * 1024 + 551170.44 * 1024), "sha": "b116608af67edde9",
                 "files": ["gated_softmax_attention_amd/csrc/bwd_kernel.h",
                           "gated_softmax_attention_amd/csrc/common.h",
                           "gated_softmax_attention_amd/csrc/launch.h",
                           "gated_softmax_attention_amd/build.py"]},
-    "fox_bwd_dkv": {"bytes": int(2 * 380361.50 * 1024 + 278538.88 * 1024), "sha": "0413886d028214ac",
+    "fox_bwd_dkv": {"bytes": int(2 * 379854.00 * 1024 + 278535.75 * 1024), "sha": "80f8e6aa85e01e1a",
                     "files": ["gated_softmax_attention_amd/csrc/fox_bwd.h",
                               "gated_softmax_attention_amd/csrc/fox_bwd_d128.hip",
                               "gated_softmax_attention_amd/csrc/common.h",
                               "gated_softmax_attention_amd/csrc/launch.h",
                               "gated_softmax_attention_amd/build.py"]},
-    "decode_step": {"bytes": int(2 * 135826.0 * 1024) + 1040 * 1024, "sha": "3a37de33ddd7a9ca",
+    "decode_step": {"bytes": int(2 * 135838.875 * 1024) + 1040 * 1024, "sha": "2a43a0c324eddeff",
                     "files": ["gated_softmax_attention_amd/csrc/decode.hip",
                               "gated_softmax_attention_amd/csrc/common.h",
                               "gated_softmax_attention_amd/csrc/launch.h",

@@ -280,7 +280,9 @@ def decode_bench(args, x, F, torch):
     print(json.dumps(out), flush=True)
 
 
-PEAK_EXP_GEXPS = 1024 * 64 / 8 * 2.4  # v_exp_f32: 8 cycles per wave64 instruction
+# Exponential peak: 1024 SIMDs at 2.4 GHz, one v_exp_f32 per wave64 every 8 cycles (the
+# transcendental unit handles 8 lanes a cycle), in Gexp/s.
+PEAK_EXP_GEXPS = 1024 * 64 / 8 * 2.4
 
 
 def peak_probe(torch):

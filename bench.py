@@ -368,7 +368,7 @@ def main():
                     help="time decode steps (fix_decode_step) against a cache holding the workload's T tokens")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build runs the kernel on one GPU's share and has no "
+        print(f"bench.py measures one GPU only: the library runs the kernels on one GPU's share and has no "
               f"multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
 

@@ -7,6 +7,9 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <mutex>
 
 #include "common.h"
@@ -24,7 +27,19 @@ struct Trace {
 };
 thread_local Trace g_trace;
 
-hipError_t trace_begin(hipStream_t st) {
+// Opt-in launch log: with FIX_ATTN_LOG set in the environment (to anything
+// but "0"), each kernel an entry point enqueues writes one line to stderr.
+bool launch_log() {
+  static const bool on = [] {
+    const char *v = std::getenv("FIX_ATTN_LOG");
+    return v && *v && std::strcmp(v, "0") != 0;
+  }();
+  return on;
+}
+thread_local const char *g_entry = "";
+
+hipError_t trace_begin(hipStream_t st, const char *entry) {
+  g_entry = entry;
   g_trace.count = 0;
   if (!g_trace.events || g_trace.capacity < 1) return hipSuccess;
   g_trace.labels[0] = "begin";
@@ -32,6 +47,7 @@ hipError_t trace_begin(hipStream_t st) {
   return hipEventRecord(g_trace.events[0], st);
 }
 hipError_t trace_mark(hipStream_t st, const char *label) {
+  if (launch_log()) std::fprintf(stderr, "[fixattn] %s: %s enqueued on stream %p\n", g_entry, label, (void *)st);
   if (!g_trace.events || g_trace.count >= g_trace.capacity || g_trace.count >= 64) return hipSuccess;
   g_trace.labels[g_trace.count] = label;
   return hipEventRecord(g_trace.events[g_trace.count++], st);
@@ -291,7 +307,7 @@ fix_status fix_attn_fwd(const fix_attn_desc *d, const void *q, const void *k, co
   FwdWs w;
   carve_fwd(cv, d, w);
   const bool f32in = d->in_dtype == FIX_F32;
-  hipError_t e = trace_begin(st);
+  hipError_t e = trace_begin(st, "fix_attn_fwd");
   if (e != hipSuccess) return hip_fail(e);
   e = fix::launch_plan(d->cu_seqlens, (int)s.nseq, (int)d->T, s.Ttot, w.plan, st);
   if (e == hipSuccess) e = trace_mark(st, "plan");
@@ -377,7 +393,7 @@ fix_status fix_attn_bwd(const fix_attn_desc *d, const void *q, const void *k, co
     if (e == hipSuccess) e = trace_mark(st, label); \
     if (e != hipSuccess) return hip_fail(e);        \
   } while (0)
-  e = trace_begin(st);
+  e = trace_begin(st, "fix_attn_bwd");
   if (e != hipSuccess) return hip_fail(e);
   if (d->gate_scalar) {
     // The decay as a logit bias (fox_bwd.h): dq with the row sums of dS, dk and
@@ -546,7 +562,7 @@ fix_status fix_decode_step(const fix_decode_desc *d, const void *cache, const vo
   const bool f32in = d->in_dtype == FIX_F32;
   const float scale = d->scale > 0.f ? d->scale : 1.0f / std::sqrt((float)d->dk);
   const int splits = decode_splits(d);
-  hipError_t e = trace_begin(st);
+  hipError_t e = trace_begin(st, "fix_decode_step");
   if (e == hipSuccess) e = fix::launch_decode_open(dc, w.vto, st);
   if (e == hipSuccess) e = trace_mark(st, "decode_open");
   if (e == hipSuccess) e = fix::launch_decode_step(dc, q, f32in, scale * fix::LOG2E, splits, w.vto, w.part, w.mpart, st);

@@ -248,7 +248,13 @@ fix_status fix_decode_step_noalloc(const fix_decode_desc *d, const void *cache, 
  * caller's.  fix_attn_event_trace_count() gives the number recorded by the
  * last call, fix_attn_event_trace_label(i) (i >= 1) the name of the launch
  * that events[i] closes (NULL out of range).  events == NULL turns it off.
- * A failed hipEventRecord ends the call with FIX_E_HIP. */
+ * A failed hipEventRecord ends the call with FIX_E_HIP.
+ *
+ * Launch log: with the environment variable FIX_ATTN_LOG set (to anything but
+ * "0") when the library first needs it, fix_attn_fwd, fix_attn_bwd and
+ * fix_decode_step (and its allocation-free form) write one line to stderr
+ * per kernel they enqueue: "[fixattn] <entry point>: <kernel> enqueued on
+ * stream <hip_stream>", the kernel names being those of the event trace. */
 void fix_attn_set_event_trace(void **events, int capacity);
 int fix_attn_event_trace_count(void);
 const char *fix_attn_event_trace_label(int i);
